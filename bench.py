@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE dispatch / combine hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic tokens:
+  flat workloads   : ep_get_layout -> ep_dispatch -> ep_combine (identity expert:
+                     the combine gathers the dispatched rows back)
+  two-level (hier) : ep_get_layout -> ep_hierarchical_dispatch (both steps) ->
+                     ep_combine on the chunked scale-up rows
+Inputs are seeded and already resident in HBM when the timed region starts.
+W untimed warm-up steps, then exactly K timed steps between two device
+synchronisations. Prints one JSON line.
+
+Also reported: per-kernel average durations from HIP events recorded on the
+stream the kernels run on, the roofline of the dominant kernel (algorithmic
+bytes per launch / average duration, against 8 TB/s HBM), HBM traffic from the
+committed rocprofv3 counter summary when it matches the current kernel
+sources, and the CPU oracle timed on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="ep32",
+                   choices=["tiny", "ep32", "ep256", "zipf", "hier8x8"])
+    p.add_argument("--fp8", action="store_true", help="also move the FP8 payload + scales")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="time budget of the CPU-oracle baseline (0 = skip)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_get_layout_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None if there is none or it was taken from other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "cross-GPU step in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from combine_get_layout_amd import ep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ep.lib()
+    torch.cuda.set_device(0)
+    w = synth.workload(args.workload)
+    hier = w.G > 1
+    fp8 = bool(args.fp8)
+    inp = synth.make_inputs(w, with_fp8=fp8)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.uint16)
+        return torch.from_numpy(a).cuda()
+
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, w.G)
+    tokens = dict(x=dev(inp["x"]), topk_idx=dev(inp["topk_idx"]), topk_weights=dev(inp["topk_w"]))
+    if fp8:
+        tokens["x_fp8"] = dev(inp["x_fp8"])
+        tokens["x_scales"] = dev(inp["x_scales"])
+    L = ep.alloc_layout(shape, masks=True, groups=hier)
+    ws = ep.alloc_workspace(shape)
+    ep.ep_get_layout(shape, tokens["topk_idx"], L, ws)
+    torch.cuda.synchronize()
+    N = int(L["rank_offsets"][-1].item())
+    G_rows = int(L["group_offsets"][-1].item()) if hier else 0
+    out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
+    seg = ep.EP_SEG_BF16 | ((ep.EP_SEG_FP8 | ep.EP_SEG_SCALES) if fp8 else 0)
+    if hier:
+        stride = ep.ep_chunked_record_bytes(shape, seg)
+        group_buf = torch.empty((G_rows, stride), dtype=torch.uint8, device="cuda")
+        peer_buf = torch.empty((N, stride), dtype=torch.uint8, device="cuda")
+    else:
+        recv = ep.alloc_recv(shape, N, fp8=fp8, scales=fp8, meta=True)
+
+    epoch = [0]
+    stream = torch.cuda.current_stream()
+    names = ["layout", "hier" if hier else "dispatch", "combine"]
+    ev = {n: [] for n in names}
+
+    def timed(name, fn, record):
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev[name].append((a, b))
+        else:
+            fn()
+
+    def step(record):
+        epoch[0] += 1
+        timed("layout", lambda: ep.ep_get_layout(shape, tokens["topk_idx"], L, ws), record)
+        if hier:
+            timed("hier", lambda: ep.ep_hierarchical_dispatch(
+                shape, L, tokens, epoch[0], ep.EP_HIER_SCALEOUT | ep.EP_HIER_FORWARD,
+                group_buf, G_rows, peer_buf, N, ws), record)
+            timed("combine", lambda: ep.ep_combine(shape, L, peer_buf, N, stride, ep.EP_FMT_CHUNKED,
+                                                   epoch[0], tokens["topk_weights"], out, ws), record)
+        else:
+            timed("dispatch", lambda: ep.ep_dispatch(shape, L, tokens, recv, N, ws), record)
+            timed("combine", lambda: ep.ep_combine(shape, L, recv["x"], N, 2 * w.H, ep.EP_FMT_PLAIN,
+                                                   0, tokens["topk_weights"], out, ws), record)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    if ep.ep_check_errors(ws) != 0:
+        raise RuntimeError("device error bits set during warm-up")
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    avg_ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
+    if ep.ep_check_errors(ws) != 0:
+        raise RuntimeError("device error bits set during the timed steps")
+
+    # Algorithmic bytes per launch (what the method must move).
+    T, H, K, R = w.T, w.H, w.K, w.R
+    row = 2 * H + ((H + 4 * (H // 128)) if fp8 else 0)
+    meta = 4 + 8 * K
+    route = T * K * (8 + 4 + 4)  # topk_idx read, weights read, slots read
+    bytes_layout = T * K * 8 + T * K * 4 + T * R + (T * K * 4 + T * w.G if hier else 0)
+    if hier:
+        rec = ep.ep_chunked_record_bytes(shape, seg)
+        hid = 512 * ((2 * H + 479) // 480)
+        bytes_main = T * row + route + T * K * 4 + 2 * G_rows * rec + N * rec
+        bytes_combine = N * hid + T * 2 * H + T * K * 8
+    else:
+        bytes_main = T * row + route + N * (row + meta)
+        bytes_combine = N * 2 * H + T * 2 * H + T * K * 8
+    by = {"layout": bytes_layout, names[1]: bytes_main, "combine": bytes_combine}
+    step_bytes = sum(by.values())
+    kernel_of = {"layout": "layout_*", "dispatch": "dispatch_kernel",
+                 "hier": "scaleout_kernel+forward_kernel", "combine": "combine_kernel"}
+    dom = max(names[1:], key=lambda n: avg_ms[n])
+    achieved = by[dom] / (avg_ms[dom] * 1e-3) / 1e9
+    traffic = committed_traffic(w.name + ("_fp8" if fp8 else ""), kernel_of[dom])
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, inp, fp8, hier, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": T * args.steps / (ms_total * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "wall_s": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "payload_dtype": "bf16" + ("+fp8e4m3" if fp8 else ""),
+        "data": "synthetic (seeded; see synth/__init__.py)",
+        "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": w.E,
+                   "ranks": R, "groups": w.G, "topk": K, "routing": w.routing,
+                   "receive_rows": N, "fp8_payload": fp8, "parallelism": "single GPU"},
+        "hbm_gbs_step": step_bytes / (ms_step * 1e-3) / 1e9,
+        "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernel_ms": avg_ms,
+        "kernel_algorithmic_bytes": by,
+        "roofline": {"kernel": kernel_of[dom], "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, inp, fp8, hier, budget_s):
+    """The oracle as it stands, single-threaded, on repeated full passes of the
+    same batch until the time budget is spent (at least one pass)."""
+    import oracle
+
+    oracle.build(force=False)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        L = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+        if hier:
+            Hd = oracle.hier_dispatch(inp["topk_idx"], w.E, w.R, w.G, L["slot"], L["group_offsets"],
+                                      1, x=inp["x"], x_fp8=inp.get("x_fp8"),
+                                      x_scales=inp.get("x_scales"), topk_w=inp["topk_w"])
+            oracle.combine(L["slot"], inp["topk_w"], Hd["peer_buf"], w.H, chunked=True, epoch=1)
+        else:
+            D = oracle.dispatch(inp["topk_idx"], w.E, w.R, L["rank_offsets"], x=inp["x"],
+                                x_fp8=inp.get("x_fp8"), x_scales=inp.get("x_scales"),
+                                topk_w=inp["topk_w"])
+            oracle.combine(L["slot"], inp["topk_w"], D["recv_x"], w.H)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": w.T * passes / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} full pass(es) of layout+{'two-level dispatch' if hier else 'dispatch'}"
+                      f"+combine over the same {w.T}-token batch, {el:.1f} s, single thread",
+            "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
+
+
+if __name__ == "__main__":
+    main()

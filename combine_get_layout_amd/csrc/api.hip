@@ -1,0 +1,224 @@
+// api.hip -- the extern "C" boundary of libep.so: argument checks, workspace
+// and record sizing, and the kernel launches (declared in include/ep.h).
+#include <hip/hip_runtime.h>
+
+#include "ep.h"
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+WsLayout ws_layout(const ep_shape& s) {
+    WsLayout w;
+    w.nb = s.T > 0 ? (s.T + kLayoutTokens - 1) / kLayoutTokens : 1;
+    size_t off = 0;
+    w.err = off;
+    off += 256;
+    w.part_rank = off;
+    off += align256(sizeof(int32_t) * (size_t)w.nb * s.R);
+    w.part_group = off;
+    off += align256(sizeof(int32_t) * (size_t)w.nb * s.G);
+    w.part_expert = off;
+    off += align256(sizeof(int32_t) * (size_t)w.nb * s.E);
+    w.tot_rank = off;
+    off += align256(sizeof(int32_t) * (size_t)s.R);
+    w.tot_group = off;
+    off += align256(sizeof(int32_t) * (size_t)s.G);
+    w.tot_expert = off;
+    off += align256(sizeof(int32_t) * (size_t)s.E);
+    w.total = off;
+    return w;
+}
+
+static int pad16_vecs(int64_t bytes) { return (int)((bytes + 15) / 16); }
+
+RecordGeom record_geom(const ep_shape& s, int seg) {
+    RecordGeom g;
+    g.nv_x = (seg & EP_SEG_BF16) ? pad16_vecs(2 * (int64_t)s.H) : 0;
+    g.nv_fp8 = (seg & EP_SEG_FP8) ? pad16_vecs(s.H) : 0;
+    g.nv_scales = (seg & EP_SEG_SCALES) ? pad16_vecs(4 * (int64_t)(s.H / 128)) : 0;
+    g.nv_idx = pad16_vecs(4 * (int64_t)s.K);
+    g.nv_w = pad16_vecs(4 * (int64_t)s.K);
+    g.q_fp8 = g.nv_x;
+    g.q_scales = g.q_fp8 + g.nv_fp8;
+    g.q_idx = g.q_scales + g.nv_scales;
+    g.q_w = g.q_idx + g.nv_idx;
+    g.q_src = g.q_w + g.nv_w;
+    g.nv = g.q_src + 1;
+    g.bytes = 16 * (int64_t)g.nv;
+    g.nchunks = (int)((g.bytes + kChunkPayload - 1) / kChunkPayload);
+    g.stride = (int64_t)kChunkBytes * g.nchunks;
+    return g;
+}
+
+namespace {
+
+__global__ void clear_error_kernel(uint32_t* err) { *err = 0u; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape check shared by all entry points.
+int check_shape(const ep_shape* s) {
+    if (!s) return EP_ERR_ARG;
+    if (s->T < 0 || s->H <= 0 || s->K < 1 || s->E < 1 || s->R < 1 || s->G < 1) return EP_ERR_ARG;
+    if (s->E % s->R != 0 || s->R % s->G != 0 || s->H % 8 != 0) return EP_ERR_ARG;
+    if (s->K > EP_MAX_TOPK || s->R > EP_MAX_RANKS || s->G > EP_MAX_GROUPS || s->E > EP_MAX_EXPERTS)
+        return EP_ERR_UNSUPPORTED;
+    if ((int64_t)s->T * s->K > INT32_MAX || (int64_t)s->T * s->R > ((int64_t)1 << 40))
+        return EP_ERR_UNSUPPORTED;
+    return EP_OK;
+}
+
+int check_ws(const ep_shape* s, void* ws, size_t ws_bytes) {
+    if (!ws || !aligned(ws, 256)) return EP_ERR_ARG;
+    if (ws_bytes < ws_layout(*s).total) return EP_ERR_ARG;
+    return EP_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+}  // namespace
+}  // namespace ep
+
+using namespace ep;
+
+extern "C" {
+
+size_t ep_workspace_bytes(const ep_shape* shape) {
+    if (check_shape(shape) != EP_OK) return 0;
+    return ws_layout(*shape).total;
+}
+
+int64_t ep_record_bytes(const ep_shape* shape, int seg_flags) {
+    if (check_shape(shape) != EP_OK || (seg_flags & ~7)) return -1;
+    if ((seg_flags & EP_SEG_SCALES) && shape->H % 128 != 0) return -1;
+    if ((seg_flags & EP_SEG_FP8) && shape->H % 16 != 0) return -1;
+    return record_geom(*shape, seg_flags).bytes;
+}
+
+int64_t ep_chunked_record_bytes(const ep_shape* shape, int seg_flags) {
+    if (ep_record_bytes(shape, seg_flags) < 0) return -1;
+    return record_geom(*shape, seg_flags).stride;
+}
+
+int ep_get_layout(const ep_shape* shape, const int64_t* topk_idx, const ep_layout* layout,
+                  void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(shape);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_ws(shape, ws, ws_bytes)) != EP_OK) return rc;
+    if (!layout || (shape->T > 0 && !topk_idx) || !aligned(topk_idx, 8)) return EP_ERR_ARG;
+    const ep_layout& L = *layout;
+    if (!aligned(L.is_token_in_rank, 16) || !aligned(L.is_token_in_group, 16)) return EP_ERR_ARG;
+    const void* i32s[] = {L.tokens_per_expert, L.tokens_per_rank, L.tokens_per_group,
+                          L.expert_offsets, L.rank_offsets, L.group_offsets, L.slot,
+                          L.group_slot};
+    for (const void* p : i32s)
+        if (!aligned(p, 4)) return EP_ERR_ARG;
+    return hip_status(launch_layout(*shape, topk_idx, L, static_cast<char*>(ws),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch(const ep_shape* shape, const ep_layout* layout, const ep_tokens* tokens,
+                const ep_recv* recv, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(shape);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_ws(shape, ws, ws_bytes)) != EP_OK) return rc;
+    if (!layout || !tokens || !recv || recv->capacity < 0) return EP_ERR_ARG;
+    if (shape->T > 0 && (!layout->slot || !tokens->topk_idx)) return EP_ERR_ARG;
+    if ((recv->x && !tokens->x) || (recv->x_fp8 && !tokens->x_fp8) ||
+        (recv->x_scales && !tokens->x_scales) || (recv->topk_weights && !tokens->topk_weights))
+        return EP_ERR_ARG;
+    if ((tokens->x_fp8 || recv->x_fp8) && shape->H % 16 != 0) return EP_ERR_ARG;
+    if ((tokens->x_scales || recv->x_scales) && shape->H % 128 != 0) return EP_ERR_ARG;
+    if (!aligned(tokens->x, 16) || !aligned(tokens->x_fp8, 16) || !aligned(recv->x, 16) ||
+        !aligned(recv->x_fp8, 16) || !aligned(tokens->x_scales, 4) || !aligned(recv->x_scales, 4) ||
+        !aligned(tokens->topk_idx, 8) || !aligned(tokens->topk_weights, 4) ||
+        !aligned(recv->src_idx, 4) || !aligned(recv->topk_idx, 4) ||
+        !aligned(recv->topk_weights, 4) || !aligned(layout->slot, 4))
+        return EP_ERR_ARG;
+    return hip_status(launch_dispatch(*shape, *layout, *tokens, *recv, static_cast<char*>(ws),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int ep_hierarchical_dispatch(const ep_shape* shape, const ep_layout* layout,
+                             const ep_tokens* tokens, uint32_t epoch, int steps,
+                             void* group_buf, int64_t group_cap, void* peer_buf,
+                             int64_t peer_cap, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(shape);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_ws(shape, ws, ws_bytes)) != EP_OK) return rc;
+    if (!layout || !tokens || epoch == 0 || steps < 1 || steps > 3) return EP_ERR_ARG;
+    if (group_cap < 0 || peer_cap < 0) return EP_ERR_ARG;
+    if ((steps & EP_HIER_SCALEOUT) && shape->T > 0 &&
+        (!tokens->x || !tokens->topk_idx || !tokens->topk_weights || !layout->group_slot ||
+         (group_cap > 0 && !group_buf)))
+        return EP_ERR_ARG;
+    if ((steps & EP_HIER_FORWARD) &&
+        (!layout->group_offsets || !layout->slot || (group_cap > 0 && !group_buf) ||
+         (peer_cap > 0 && !peer_buf)))
+        return EP_ERR_ARG;
+    if (tokens->x_fp8 && shape->H % 16 != 0) return EP_ERR_ARG;
+    if (tokens->x_scales && shape->H % 128 != 0) return EP_ERR_ARG;
+    if (!aligned(tokens->x, 16) || !aligned(tokens->x_fp8, 16) || !aligned(tokens->x_scales, 4) ||
+        !aligned(tokens->topk_idx, 8) || !aligned(tokens->topk_weights, 4) ||
+        !aligned(group_buf, 16) || !aligned(peer_buf, 16))
+        return EP_ERR_ARG;
+    return hip_status(launch_hier(*shape, *layout, *tokens, epoch, steps, group_buf, group_cap,
+                                  peer_buf, peer_cap, static_cast<char*>(ws),
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine(const ep_shape* shape, const ep_layout* layout, const void* y, int64_t y_rows,
+               int64_t y_row_stride, int y_format, uint32_t epoch, const float* topk_weights,
+               uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(shape);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_ws(shape, ws, ws_bytes)) != EP_OK) return rc;
+    if (!layout || y_rows < 0) return EP_ERR_ARG;
+    if (y_format != EP_FMT_PLAIN && y_format != EP_FMT_CHUNKED) return EP_ERR_ARG;
+    if (shape->T > 0 && (!layout->slot || !topk_weights || !out || (y_rows > 0 && !y)))
+        return EP_ERR_ARG;
+    if (y_format == EP_FMT_PLAIN && (y_row_stride % 16 != 0 || y_row_stride < 2 * (int64_t)shape->H))
+        return EP_ERR_ARG;
+    if (y_format == EP_FMT_CHUNKED) {
+        const int64_t hidden_blocks = (2 * (int64_t)shape->H + kChunkPayload - 1) / kChunkPayload;
+        if (epoch == 0 || y_row_stride % kChunkBytes != 0 || y_row_stride < hidden_blocks * kChunkBytes)
+            return EP_ERR_ARG;
+    }
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) || !aligned(layout->slot, 4))
+        return EP_ERR_ARG;
+    return hip_status(launch_combine(*shape, *layout, y, y_rows, y_row_stride, y_format, epoch,
+                                     topk_weights, out, static_cast<char*>(ws),
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int ep_clear_errors(void* ws, void* stream) {
+    if (!ws || !aligned(ws, 256)) return EP_ERR_ARG;
+    hipLaunchKernelGGL(clear_error_kernel, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream),
+                       reinterpret_cast<uint32_t*>(ws));
+    return hip_status(hipGetLastError());
+}
+
+int ep_check_errors(void* ws, void* stream, uint32_t* bits) {
+    if (!ws || !bits || !aligned(ws, 256)) return EP_ERR_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t v = 0;
+    if (hipMemcpyAsync(&v, ws, sizeof v, hipMemcpyDeviceToHost, st) != hipSuccess) return EP_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return EP_ERR_HIP;
+    *bits = v;
+    return EP_OK;
+}
+
+const char* ep_status_string(int status) {
+    switch (status) {
+        case EP_OK: return "ok";
+        case EP_ERR_ARG: return "invalid argument (null or misaligned pointer, bad shape or size)";
+        case EP_ERR_UNSUPPORTED: return "shape outside the supported limits";
+        case EP_ERR_HIP: return "HIP runtime or launch error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

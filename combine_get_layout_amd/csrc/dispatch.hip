@@ -1,0 +1,161 @@
+// dispatch.hip -- ep_dispatch on gfx950: read each token once, write its record
+// to every destination rank's receive row.
+//
+// What is computed follows "DeepEP V2 深度深潜：统一接口、SM 估算本质与 TopK
+// 复制机制", §3.3 阶段2 (dispatch warps: load the hidden row, load top-k ids and
+// weights, one destination per distinct rank) and §3.5 (recv_x,
+// recv_topk_idx, recv_topk_weights), with the record fields of "07: DeepEP
+// Intra/Inter-node 协调 — NVLink Scale-up + RDMA Scale-out 三阶段流水线的代码实证"
+// (hidden, scales, source index, top-k ids and weights; NVL receivers write
+// recv_x[row] and recv_x_scales[row * H/128]).
+//
+// Mapping on CDNA4: one wave64 per source token, four tokens per workgroup.
+// The wave loads up to 16 16-byte vectors per lane of the row (16 KiB in
+// flight per wave) into VGPRs, then streams them to each destination row with
+// non-temporal 16-byte stores: one HBM read, D writes, no LDS round trip.
+// Destinations are the lanes k whose slot differs from every earlier lane's
+// (the rank deduplication), found with one ballot.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+struct DispatchArgs {
+    int T, H, K, E;
+    const int32_t* slot;
+    const int64_t* topk;
+    const float* topk_w;
+    const uint8_t* x;       // bf16 rows as bytes
+    const uint8_t* x_fp8;
+    const float* x_scales;
+    uint8_t* rx;
+    uint8_t* rfp8;
+    float* rscales;
+    int32_t* rsrc;
+    int32_t* ridx;
+    float* rw;
+    int64_t cap;
+    uint32_t* err;
+};
+
+// Copy one row of `row_bytes` (multiple of 16) bytes from src to the rows
+// dst + slot_k * row_bytes of every destination lane k in `dest`.
+template <int NV>
+__device__ __forceinline__ void fan_out_row(const uint8_t* src, int64_t row_bytes, uint8_t* dst,
+                                            uint64_t dest, int slot) {
+    const int lane = lane_id();
+    const int nvec = (int)(row_bytes / 16);
+    for (int base = 0; base < nvec; base += kWave * NV) {
+        u32x4 v[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int i = base + j * kWave + lane;
+            if (i < nvec) v[j] = ld16(src + (int64_t)i * 16);
+        }
+        for (uint64_t m = dest; m; m &= m - 1) {
+            const int k = __ffsll((unsigned long long)m) - 1;
+            uint8_t* row = dst + (int64_t)readlane(slot, k) * row_bytes;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int i = base + j * kWave + lane;
+                if (i < nvec) st16_stream(row + (int64_t)i * 16, v[j]);
+            }
+        }
+    }
+}
+
+template <int NV>
+__global__ __launch_bounds__(kBlockThreads) void dispatch_kernel(DispatchArgs a) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+    if (t >= a.T) return;
+
+    // Lanes 0..K-1 hold this token's slots; a lane is a destination if its
+    // slot is valid and no lower lane has the same slot (same rank).
+    int s = -1;
+    int64_t e = -1;
+    float wk = 0.f;
+    if (lane < a.K) {
+        s = a.slot[(int64_t)t * a.K + lane];
+        e = a.topk[(int64_t)t * a.K + lane];
+        if (a.topk_w) wk = a.topk_w[(int64_t)t * a.K + lane];
+    }
+    bool first = s >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int sj = readlane(s, j);
+        if (j < lane && sj == s) first = false;
+    }
+    const bool over = first && s >= a.cap;
+    if (over) report(a.err, EP_DEVERR_CAPACITY);
+    const uint64_t dest = __ballot(first && !over);
+    if (!dest) return;
+
+    if (a.x && a.rx)
+        fan_out_row<NV>(a.x + (int64_t)t * a.H * 2, (int64_t)a.H * 2, a.rx, dest, s);
+    if (a.x_fp8 && a.rfp8)
+        fan_out_row<NV>(a.x_fp8 + (int64_t)t * a.H, a.H, a.rfp8, dest, s);
+    if (a.x_scales && a.rscales) {
+        const int ns = a.H / 128;
+        for (int base = 0; base < ns; base += kWave) {
+            const int i = base + lane;
+            const float v = i < ns ? a.x_scales[(int64_t)t * ns + i] : 0.f;
+            for (uint64_t m = dest; m; m &= m - 1) {
+                const int k = __ffsll((unsigned long long)m) - 1;
+                if (i < ns) a.rscales[(int64_t)readlane(s, k) * ns + i] = v;
+            }
+        }
+    }
+    // Metadata: source token, the token's expert ids (invalid -> -1) and weights.
+    const int32_t id = expert_ok(e, a.E) ? (int32_t)e : -1;
+    for (uint64_t m = dest; m; m &= m - 1) {
+        const int k = __ffsll((unsigned long long)m) - 1;
+        const int64_t row = readlane(s, k);
+        if (a.rsrc && lane == 0) a.rsrc[row] = t;
+        if (lane < a.K) {
+            if (a.ridx) a.ridx[row * a.K + lane] = id;
+            if (a.rw && a.topk_w) a.rw[row * a.K + lane] = wk;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
+                           const ep_recv& rv, char* ws, hipStream_t st) {
+    if (s.T == 0) return hipSuccess;
+    const WsLayout W = ws_layout(s);
+    DispatchArgs a;
+    a.T = s.T; a.H = s.H; a.K = s.K; a.E = s.E;
+    a.slot = L.slot;
+    a.topk = tk.topk_idx;
+    a.topk_w = tk.topk_weights;
+    a.x = reinterpret_cast<const uint8_t*>(tk.x);
+    a.x_fp8 = tk.x_fp8;
+    a.x_scales = tk.x_scales;
+    a.rx = reinterpret_cast<uint8_t*>(rv.x);
+    a.rfp8 = rv.x_fp8;
+    a.rscales = rv.x_scales;
+    a.rsrc = rv.src_idx;
+    a.ridx = rv.topk_idx;
+    a.rw = rv.topk_weights;
+    a.cap = rv.capacity;
+    a.err = reinterpret_cast<uint32_t*>(ws + W.err);
+    const dim3 grid((s.T + kWavesPerBlock - 1) / kWavesPerBlock), block(kBlockThreads);
+    // Vectors per lane held in registers: enough for the widest present row.
+    const int64_t widest = tk.x ? 2 * (int64_t)s.H : (int64_t)s.H;
+    const int64_t per_lane = (widest / 16 + kWave - 1) / kWave;
+    if (per_lane <= 1)
+        hipLaunchKernelGGL(dispatch_kernel<1>, grid, block, 0, st, a);
+    else if (per_lane <= 2)
+        hipLaunchKernelGGL(dispatch_kernel<2>, grid, block, 0, st, a);
+    else if (per_lane <= 4)
+        hipLaunchKernelGGL(dispatch_kernel<4>, grid, block, 0, st, a);
+    else if (per_lane <= 8)
+        hipLaunchKernelGGL(dispatch_kernel<8>, grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL(dispatch_kernel<16>, grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace ep

@@ -1,0 +1,66 @@
+// ep_device.h -- device-side helpers shared by the gfx950 kernels of libep.
+//
+// Wave64 throughout: one wavefront = 64 lanes; a 16-byte vector per lane makes
+// one wave-wide load or store move 1 KiB of contiguous memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep.h"
+
+namespace ep {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;             // 4 waves per workgroup
+constexpr int kWavesPerBlock = kBlockThreads / kWave;
+
+// 512 B data-as-flag blocks: 480 B payload (30 vectors) + 32 B flag (2 vectors).
+constexpr int kChunkBytes = 512;
+constexpr int kChunkPayload = 480;
+constexpr int kChunkPayloadVecs = 30;
+constexpr int kChunkVecs = 32;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_in_block() { return threadIdx.x / kWave; }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+// Streaming store: receive rows and outputs are written once and not re-read
+// by this kernel, so keep them from displacing reusable lines in L2/MALL.
+__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ int readlane(int v, int lane) {
+    return __builtin_amdgcn_readlane(v, lane);
+}
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ void report(uint32_t* err, uint32_t bits) {
+    atomicOr(reinterpret_cast<unsigned int*>(err), bits);
+}
+
+// bf16 bit pattern -> float (bf16 is the upper half of a binary32).
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+}
+
+// Expert id check shared by the kernels: -1 = no expert, anything else outside
+// [0, E) is an error and behaves as -1.
+__device__ __forceinline__ bool expert_ok(int64_t e, int E) { return e >= 0 && e < E; }
+__device__ __forceinline__ bool expert_bad(int64_t e, int E) { return e < -1 || e >= E; }
+
+}  // namespace ep

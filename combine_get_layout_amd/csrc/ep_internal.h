@@ -1,0 +1,53 @@
+// ep_internal.h -- launch entry points of the kernels behind the C ABI.
+// Host-side argument checks live in api.hip; these functions assume a shape and
+// pointers that passed them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ep.h"
+
+namespace ep {
+
+constexpr int kLayoutTokens = 256;  // tokens per layout workgroup (one per thread)
+
+// Workspace carve-up (byte offsets from the workspace base).
+struct WsLayout {
+    int nb;                 // layout workgroups = max(1, ceil(T / kLayoutTokens))
+    size_t err;             // uint32 error word
+    size_t part_rank;       // int32 [nb][R]  per-block counts -> block-exclusive prefix
+    size_t part_group;      // int32 [nb][G]
+    size_t part_expert;     // int32 [nb][E]
+    size_t tot_rank;        // int32 [R]
+    size_t tot_group;       // int32 [G]
+    size_t tot_expert;      // int32 [E]
+    size_t total;
+};
+WsLayout ws_layout(const ep_shape& s);
+
+// Record geometry of a packed token record (vectors are 16 B).
+struct RecordGeom {
+    int nv_x, nv_fp8, nv_scales, nv_idx, nv_w;  // vectors per piece (0 if absent)
+    int q_fp8, q_scales, q_idx, q_w, q_src;     // first vector of each piece
+    int nv;                                     // total vectors = P / 16
+    int64_t bytes;                              // P
+    int nchunks;                                // ceil(P / 480)
+    int64_t stride;                             // 512 * nchunks
+};
+RecordGeom record_geom(const ep_shape& s, int seg_flags);
+
+hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout& L, char* ws,
+                         hipStream_t st);
+hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
+                           const ep_recv& rv, char* ws, hipStream_t st);
+hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
+                       uint32_t epoch, int steps, void* group_buf, int64_t group_cap,
+                       void* peer_buf, int64_t peer_cap, char* ws, hipStream_t st);
+hipError_t launch_combine(const ep_shape& s, const ep_layout& L, const void* y, int64_t y_rows,
+                          int64_t y_stride, int fmt, uint32_t epoch, const float* w,
+                          uint16_t* out, char* ws, hipStream_t st);
+hipError_t launch_clear_errors(char* ws, hipStream_t st);
+
+}  // namespace ep

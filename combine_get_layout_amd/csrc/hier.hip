@@ -1,0 +1,254 @@
+// hier.hip -- ep_hierarchical_dispatch on gfx950: two-level dispatch with
+// 512-byte data-as-flag chunked records.
+//
+// What is computed follows "DeepEP V2 深度深潜：统一接口、SM 估算本质与 TopK
+// 复制机制" §3.6 (scale-out warps write each token to the destination group's
+// receive buffer, forward warps store it from there to the scale-up peer) and
+// "07: DeepEP Intra/Inter-node 协调 — NVLink Scale-up + RDMA Scale-out 三阶段流水
+// 线的代码实证" (hybrid scale-out stage: one store per destination group; forward
+// warps: scale-up rank = expert / experts_per_rank). The record is the
+// TokenLayout of the V2 page, §3.4 (hidden | scales | metadata, 16 B pieces),
+// cut into the blocks of "Ascend Send Ordering", 导言: 512 B = 480 B payload +
+// 32 B flag.
+//
+// CDNA4 mapping: a 512 B block is 32 16-byte vectors, so one wave64 store of a
+// 16-byte vector per lane covers exactly two blocks: lanes 0-29 carry payload
+// vectors of block 2i, lanes 30-31 its flag, lanes 32-61 and 62-63 the same
+// for block 2i+1. Record vector q sits in block q / 30, vector q % 30.
+//   step 1: one wave per token assembles its chunked record in VGPRs (pieces
+//           of 16 wave-iterations = 32 blocks = 16 KiB) and streams it once to
+//           each destination group's row.
+//   step 2: one wave per group-region row (grid-stride; the row count is read
+//           on the device): check every block's flag, read src and top-k ids
+//           from the record, then stream the row to each scale-up peer's row.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+constexpr int kPieceIters = 16;  // wave iterations (2 blocks each) held in VGPRs
+
+struct HierArgs {
+    int T, H, K, E, R, G, epr, P;
+    RecordGeom geom;
+    const int32_t* slot;
+    const int32_t* group_slot;
+    const int32_t* group_offsets;
+    const int64_t* topk;
+    const float* topk_w;
+    const uint8_t* x;
+    const uint8_t* x_fp8;
+    const float* x_scales;
+    uint8_t* group_buf;
+    int64_t group_cap;
+    uint8_t* peer_buf;
+    int64_t peer_cap;
+    uint32_t epoch;
+    uint32_t* err;
+};
+
+// Record vector q of token t (16 bytes), zero past the end of the record.
+__device__ __forceinline__ u32x4 record_vector(const HierArgs& a, int t, int q) {
+    const RecordGeom& g = a.geom;
+    if (q < g.q_fp8) return ld16(a.x + (int64_t)t * a.H * 2 + (int64_t)q * 16);
+    if (q < g.q_scales) return ld16(a.x_fp8 + (int64_t)t * a.H + (int64_t)(q - g.q_fp8) * 16);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (q < g.q_idx) {
+        const int ns = a.H / 128;
+        const int i0 = (q - g.q_scales) * 4;
+        const float* sc = a.x_scales + (int64_t)t * ns;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i0 + j < ns) v[j] = __float_as_uint(sc[i0 + j]);
+        return v;
+    }
+    if (q < g.q_w) {
+        const int k0 = (q - g.q_idx) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (k0 + j < a.K) {
+                const int64_t e = a.topk[(int64_t)t * a.K + k0 + j];
+                v[j] = (uint32_t)(expert_ok(e, a.E) ? (int32_t)e : -1);
+            }
+        return v;
+    }
+    if (q < g.q_src) {
+        const int k0 = (q - g.q_w) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (k0 + j < a.K) v[j] = __float_as_uint(a.topk_w[(int64_t)t * a.K + k0 + j]);
+        return v;
+    }
+    if (q == g.q_src) v[0] = (uint32_t)t;
+    return v;
+}
+
+// Byte offset inside a chunked row of wave-iteration `it`, for this lane.
+__device__ __forceinline__ int64_t chunk_lane_offset(int it, int lane) {
+    const int c = 2 * it + (lane >> 5);
+    return (int64_t)c * kChunkBytes + (int64_t)(lane & 31) * 16;
+}
+
+__global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+    if (t >= a.T) return;
+    int gs = -1;
+    if (lane < a.K) gs = a.group_slot[(int64_t)t * a.K + lane];
+    bool first = gs >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int sj = readlane(gs, j);
+        if (j < lane && sj == gs) first = false;
+    }
+    const bool over = first && gs >= a.group_cap;
+    if (over) report(a.err, EP_DEVERR_CAPACITY);
+    const uint64_t dest = __ballot(first && !over);
+    if (!dest) return;
+
+    const int nchunks = a.geom.nchunks;
+    const int iters = (nchunks + 1) / 2;
+    const int64_t stride = a.geom.stride;
+    const u32x4 flag = {a.epoch, a.epoch, a.epoch, a.epoch};
+    const int c_half = lane >> 5, w = lane & 31;
+    for (int it0 = 0; it0 < iters; it0 += kPieceIters) {
+        u32x4 v[kPieceIters];
+#pragma unroll
+        for (int j = 0; j < kPieceIters; ++j) {
+            const int c = 2 * (it0 + j) + c_half;
+            if (it0 + j < iters && c < nchunks)
+                v[j] = w < kChunkPayloadVecs ? record_vector(a, t, c * kChunkPayloadVecs + w) : flag;
+        }
+        for (uint64_t m = dest; m; m &= m - 1) {
+            const int k = __ffsll((unsigned long long)m) - 1;
+            uint8_t* row = a.group_buf + (int64_t)readlane(gs, k) * stride;
+#pragma unroll
+            for (int j = 0; j < kPieceIters; ++j) {
+                const int c = 2 * (it0 + j) + c_half;
+                if (it0 + j < iters && c < nchunks)
+                    st16_stream(row + chunk_lane_offset(it0 + j, lane), v[j]);
+            }
+        }
+    }
+}
+
+// Address of record byte b (4-byte aligned, never straddling a block) in a
+// chunked row.
+__device__ __forceinline__ const uint8_t* record_byte(const uint8_t* row, int64_t b) {
+    return row + (b / kChunkPayload) * kChunkBytes + b % kChunkPayload;
+}
+
+__global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
+    __shared__ int32_t goff[EP_MAX_GROUPS + 1];
+    for (int i = threadIdx.x; i <= a.G; i += kBlockThreads) goff[i] = a.group_offsets[i];
+    __syncthreads();
+    const int lane = lane_id();
+    const int64_t n_rows = min((int64_t)goff[a.G], a.group_cap);
+    const int nchunks = a.geom.nchunks;
+    const int iters = (nchunks + 1) / 2;
+    const int64_t stride = a.geom.stride;
+    const int64_t off_idx = (int64_t)a.geom.q_idx * 16;
+    const int64_t off_src = (int64_t)a.geom.q_src * 16;
+    const int c_half = lane >> 5, w = lane & 31;
+    const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerBlock;
+
+    for (int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); n < n_rows;
+         n += wave_stride) {
+        const uint8_t* src_row = a.group_buf + n * stride;
+        // The row's group: the number of groups g >= 1 whose region starts at
+        // or before n (empty groups have equal starts).
+        int g = 0;
+        for (int base = 1; base <= a.G; base += kWave) {
+            const int j = base + lane;
+            g += __popcll(__ballot(j <= a.G && goff[j] <= n));
+        }
+        // Every block's flag must equal epoch.
+        bool ok = true;
+        for (int i = lane; i < 2 * nchunks; i += kWave) {
+            const u32x4 f = ld16(src_row + (int64_t)(i >> 1) * kChunkBytes + kChunkPayload + (i & 1) * 16);
+            ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
+        }
+        int32_t src = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_src));
+        if (__ballot(!ok) || src < 0 || src >= a.T) {
+            if (lane == 0) report(a.err, EP_DEVERR_FLAG);
+            continue;
+        }
+        // Destination peers: first lane of each distinct rank inside group g.
+        int32_t r = -1, d = -1;
+        if (lane < a.K) {
+            const int32_t id = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_idx + 4 * lane));
+            if (id >= 0 && id < a.E && (id / a.epr) / a.P == g) {
+                r = id / a.epr;
+                d = a.slot[(int64_t)src * a.K + lane];
+            }
+        }
+        bool first = r >= 0 && d >= 0;
+        for (int j = 0; j < a.K; ++j) {
+            const int rj = readlane(r, j);
+            if (j < lane && rj == r) first = false;
+        }
+        const bool over = first && d >= a.peer_cap;
+        if (over) report(a.err, EP_DEVERR_CAPACITY);
+        const uint64_t dest = __ballot(first && !over);
+        if (!dest) continue;
+
+        for (int it0 = 0; it0 < iters; it0 += kPieceIters) {
+            u32x4 v[kPieceIters];
+#pragma unroll
+            for (int j = 0; j < kPieceIters; ++j) {
+                const int c = 2 * (it0 + j) + c_half;
+                if (it0 + j < iters && c < nchunks) v[j] = ld16(src_row + chunk_lane_offset(it0 + j, lane));
+            }
+            for (uint64_t m = dest; m; m &= m - 1) {
+                const int k = __ffsll((unsigned long long)m) - 1;
+                uint8_t* row = a.peer_buf + (int64_t)readlane(d, k) * stride;
+#pragma unroll
+                for (int j = 0; j < kPieceIters; ++j) {
+                    const int c = 2 * (it0 + j) + c_half;
+                    if (it0 + j < iters && c < nchunks)
+                        st16_stream(row + chunk_lane_offset(it0 + j, lane), v[j]);
+                }
+            }
+        }
+        (void)w;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
+                       uint32_t epoch, int steps, void* group_buf, int64_t group_cap,
+                       void* peer_buf, int64_t peer_cap, char* ws, hipStream_t st) {
+    const WsLayout W = ws_layout(s);
+    int seg = EP_SEG_BF16 | (tk.x_fp8 ? EP_SEG_FP8 : 0) | (tk.x_scales ? EP_SEG_SCALES : 0);
+    HierArgs a;
+    a.T = s.T; a.H = s.H; a.K = s.K; a.E = s.E; a.R = s.R; a.G = s.G;
+    a.epr = s.E / s.R; a.P = s.R / s.G;
+    a.geom = record_geom(s, seg);
+    a.slot = L.slot;
+    a.group_slot = L.group_slot;
+    a.group_offsets = L.group_offsets;
+    a.topk = tk.topk_idx;
+    a.topk_w = tk.topk_weights;
+    a.x = reinterpret_cast<const uint8_t*>(tk.x);
+    a.x_fp8 = tk.x_fp8;
+    a.x_scales = tk.x_scales;
+    a.group_buf = reinterpret_cast<uint8_t*>(group_buf);
+    a.group_cap = group_cap;
+    a.peer_buf = reinterpret_cast<uint8_t*>(peer_buf);
+    a.peer_cap = peer_cap;
+    a.epoch = epoch;
+    a.err = reinterpret_cast<uint32_t*>(ws + W.err);
+    const dim3 block(kBlockThreads);
+    if ((steps & EP_HIER_SCALEOUT) && s.T > 0)
+        hipLaunchKernelGGL(scaleout_kernel, dim3((s.T + kWavesPerBlock - 1) / kWavesPerBlock), block, 0,
+                           st, a);
+    if ((steps & EP_HIER_FORWARD) && group_cap > 0) {
+        const int64_t want = (group_cap + kWavesPerBlock - 1) / kWavesPerBlock;
+        const int blocks = (int)(want < 8192 ? want : 8192);
+        hipLaunchKernelGGL(forward_kernel, dim3(blocks), block, 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ep

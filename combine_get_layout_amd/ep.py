@@ -1,0 +1,234 @@
+"""Thin Python binding of libep.so (include/ep.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls and takes torch
+tensors that already live on the GPU; it passes their data pointers, the shape
+and the current HIP stream through ctypes and turns a negative status into a
+RuntimeError. No step of the computation happens here. The allocation helpers
+at the bottom only create empty tensors of the sizes the C ABI documents.
+
+If libep.so has not been built the first call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libep.so")
+
+EP_OK, EP_ERR_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, -1, -2, -3
+EP_DEVERR_EXPERT_ID, EP_DEVERR_CAPACITY, EP_DEVERR_FLAG = 1, 2, 4
+EP_SEG_BF16, EP_SEG_FP8, EP_SEG_SCALES = 1, 2, 4
+EP_FMT_PLAIN, EP_FMT_CHUNKED = 0, 1
+EP_HIER_SCALEOUT, EP_HIER_FORWARD = 1, 2
+
+_P = ctypes.c_void_p
+
+
+class ep_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "K", "E", "R", "G")]
+
+
+LAYOUT_FIELDS = ("tokens_per_expert", "tokens_per_rank", "tokens_per_group", "expert_offsets",
+                 "rank_offsets", "group_offsets", "is_token_in_rank", "is_token_in_group",
+                 "slot", "group_slot")
+
+
+class ep_layout(ctypes.Structure):
+    _fields_ = [(n, _P) for n in LAYOUT_FIELDS]
+
+
+class ep_tokens(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("x", "x_fp8", "x_scales", "topk_idx", "topk_weights")]
+
+
+class ep_recv(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("x", "x_fp8", "x_scales", "src_idx", "topk_idx",
+                                  "topk_weights")] + [("capacity", ctypes.c_int64)]
+
+
+EXPORTS = ("ep_workspace_bytes", "ep_record_bytes", "ep_chunked_record_bytes", "ep_get_layout",
+           "ep_dispatch", "ep_hierarchical_dispatch", "ep_combine", "ep_clear_errors",
+           "ep_check_errors", "ep_status_string")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libep.so (raises if it is missing: build it first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m combine_get_layout_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    sp = ctypes.POINTER(ep_shape)
+    lp = ctypes.POINTER(ep_layout)
+    i64, u32, sz = ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    L.ep_workspace_bytes.argtypes = [sp]
+    L.ep_workspace_bytes.restype = sz
+    L.ep_record_bytes.argtypes = [sp, ctypes.c_int]
+    L.ep_record_bytes.restype = i64
+    L.ep_chunked_record_bytes.argtypes = [sp, ctypes.c_int]
+    L.ep_chunked_record_bytes.restype = i64
+    L.ep_get_layout.argtypes = [sp, _P, lp, _P, sz, _P]
+    L.ep_dispatch.argtypes = [sp, lp, ctypes.POINTER(ep_tokens), ctypes.POINTER(ep_recv), _P, sz, _P]
+    L.ep_hierarchical_dispatch.argtypes = [sp, lp, ctypes.POINTER(ep_tokens), u32, ctypes.c_int,
+                                           _P, i64, _P, i64, _P, sz, _P]
+    L.ep_combine.argtypes = [sp, lp, _P, i64, i64, ctypes.c_int, u32, _P, _P, _P, sz, _P]
+    L.ep_clear_errors.argtypes = [_P, _P]
+    L.ep_check_errors.argtypes = [_P, _P, ctypes.POINTER(u32)]
+    L.ep_status_string.argtypes = [ctypes.c_int]
+    L.ep_status_string.restype = ctypes.c_char_p
+    for f in ("ep_get_layout", "ep_dispatch", "ep_hierarchical_dispatch", "ep_combine",
+              "ep_clear_errors", "ep_check_errors"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, what: str):
+    if rc != EP_OK:
+        raise RuntimeError(f"{what}: {lib().ep_status_string(rc).decode()} (status {rc})")
+
+
+def make_shape(T, H, K, E, R, G=1) -> ep_shape:
+    return ep_shape(int(T), int(H), int(K), int(E), int(R), int(G))
+
+
+def _layout_struct(layout: dict) -> ep_layout:
+    return ep_layout(*[_ptr(layout.get(n)) for n in LAYOUT_FIELDS])
+
+
+def _tokens_struct(tokens: dict) -> ep_tokens:
+    return ep_tokens(*[_ptr(tokens.get(n)) for n in ("x", "x_fp8", "x_scales", "topk_idx",
+                                                      "topk_weights")])
+
+
+def ep_workspace_bytes(shape: ep_shape) -> int:
+    return int(lib().ep_workspace_bytes(ctypes.byref(shape)))
+
+
+def ep_record_bytes(shape: ep_shape, seg_flags: int) -> int:
+    return int(lib().ep_record_bytes(ctypes.byref(shape), int(seg_flags)))
+
+
+def ep_chunked_record_bytes(shape: ep_shape, seg_flags: int) -> int:
+    return int(lib().ep_chunked_record_bytes(ctypes.byref(shape), int(seg_flags)))
+
+
+def ep_get_layout(shape, topk_idx, layout: dict, ws, stream=None):
+    L = _layout_struct(layout)
+    _check(lib().ep_get_layout(ctypes.byref(shape), _ptr(topk_idx), ctypes.byref(L), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)), "ep_get_layout")
+
+
+def ep_dispatch(shape, layout: dict, tokens: dict, recv: dict, capacity: int, ws, stream=None):
+    L = _layout_struct(layout)
+    tk = _tokens_struct(tokens)
+    rv = ep_recv(*[_ptr(recv.get(n)) for n in ("x", "x_fp8", "x_scales", "src_idx", "topk_idx",
+                                                "topk_weights")], int(capacity))
+    _check(lib().ep_dispatch(ctypes.byref(shape), ctypes.byref(L), ctypes.byref(tk),
+                             ctypes.byref(rv), _ptr(ws), ws.numel() * ws.element_size(),
+                             _stream(stream)), "ep_dispatch")
+
+
+def ep_hierarchical_dispatch(shape, layout: dict, tokens: dict, epoch: int, steps: int, group_buf,
+                             group_cap: int, peer_buf, peer_cap: int, ws, stream=None):
+    L = _layout_struct(layout)
+    tk = _tokens_struct(tokens)
+    _check(lib().ep_hierarchical_dispatch(ctypes.byref(shape), ctypes.byref(L), ctypes.byref(tk),
+                                          int(epoch), int(steps), _ptr(group_buf), int(group_cap),
+                                          _ptr(peer_buf), int(peer_cap), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+           "ep_hierarchical_dispatch")
+
+
+def ep_combine(shape, layout: dict, y, y_rows: int, y_row_stride: int, y_format: int, epoch: int,
+               topk_weights, out, ws, stream=None):
+    L = _layout_struct(layout)
+    _check(lib().ep_combine(ctypes.byref(shape), ctypes.byref(L), _ptr(y), int(y_rows),
+                            int(y_row_stride), int(y_format), int(epoch), _ptr(topk_weights),
+                            _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "ep_combine")
+
+
+def ep_clear_errors(ws, stream=None):
+    _check(lib().ep_clear_errors(_ptr(ws), _stream(stream)), "ep_clear_errors")
+
+
+def ep_check_errors(ws, stream=None) -> int:
+    bits = ctypes.c_uint32(0)
+    _check(lib().ep_check_errors(_ptr(ws), _stream(stream), ctypes.byref(bits)), "ep_check_errors")
+    return int(bits.value)
+
+
+def ep_status_string(status: int) -> str:
+    return lib().ep_status_string(int(status)).decode()
+
+
+# --------------------------------------------------------------------------
+# Allocation helpers (empty tensors of the documented sizes; no compute)
+# --------------------------------------------------------------------------
+
+def alloc_workspace(shape: ep_shape, device="cuda") -> torch.Tensor:
+    n = ep_workspace_bytes(shape)
+    if n == 0:
+        raise RuntimeError("ep_workspace_bytes: unsupported shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def alloc_layout(shape: ep_shape, device="cuda", masks=True, groups=True) -> dict:
+    i32 = dict(dtype=torch.int32, device=device)
+    T, K, E, R, G = shape.T, shape.K, shape.E, shape.R, shape.G
+    out = dict(
+        tokens_per_expert=torch.empty(E, **i32),
+        tokens_per_rank=torch.empty(R, **i32),
+        expert_offsets=torch.empty(E + 1, **i32),
+        rank_offsets=torch.empty(R + 1, **i32),
+        slot=torch.empty((T, K), **i32),
+    )
+    if masks:
+        out["is_token_in_rank"] = torch.empty((T, R), dtype=torch.uint8, device=device)
+    if groups:
+        out["tokens_per_group"] = torch.empty(G, **i32)
+        out["group_offsets"] = torch.empty(G + 1, **i32)
+        out["group_slot"] = torch.empty((T, K), **i32)
+        if masks:
+            out["is_token_in_group"] = torch.empty((T, G), dtype=torch.uint8, device=device)
+    return out
+
+
+def alloc_recv(shape: ep_shape, capacity: int, device="cuda", x=True, fp8=False, scales=False,
+               meta=True) -> dict:
+    H, K = shape.H, shape.K
+    out = {}
+    if x:
+        out["x"] = torch.empty((capacity, H), dtype=torch.uint16, device=device)
+    if fp8:
+        out["x_fp8"] = torch.empty((capacity, H), dtype=torch.uint8, device=device)
+    if scales:
+        out["x_scales"] = torch.empty((capacity, H // 128), dtype=torch.float32, device=device)
+    if meta:
+        out["src_idx"] = torch.empty(capacity, dtype=torch.int32, device=device)
+        out["topk_idx"] = torch.empty((capacity, K), dtype=torch.int32, device=device)
+        out["topk_weights"] = torch.empty((capacity, K), dtype=torch.float32, device=device)
+    return out

@@ -1,0 +1,212 @@
+/*
+ * ep.h -- C ABI of libep.so: the single-GPU data-parallel core of
+ * expert-parallel MoE dispatch and combine on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [V2]   "DeepEP V2 深度深潜：统一接口、SM 估算本质与 TopK 复制机制"
+ *   [PIPE] "07: DeepEP Intra/Inter-node 协调 — NVLink Scale-up + RDMA
+ *          Scale-out 三阶段流水线的代码实证"
+ *   [MEGA] "06_06: NVLink Scale-up + RDMA Scale-out — DeepEP 三阶段流水线 vs
+ *          DeepGEMM 对称内存"
+ *   [ASC]  "Ascend Send Ordering"
+ *
+ * Model. One GPU holds T tokens of one source rank. R logical destination
+ * ranks (E / R experts each, rank of expert e = e / (E / R)) are partitions of
+ * this GPU's HBM; for the two-level path the R ranks form G scale-out groups
+ * of P = R / G scale-up peers, rank r = g * P + peer ([PIPE]
+ * is_nvlink_accessible). Each destination rank owns a compact region of
+ * receive rows; regions are laid end to end in rank order (rank_offsets), and
+ * inside a region rows follow ascending source token.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a DEVICE pointer unless stated, allocated and owned by
+ *     the caller. The library allocates and frees no device memory and keeps
+ *     no global state; calls on distinct workspaces are independent.
+ *   - Work is enqueued asynchronously on `stream` (NULL = default stream).
+ *     Inputs must stay valid until the work completes.
+ *   - Arrays are row-major and densely packed. bf16 values are passed as their
+ *     16-bit patterns (uint16_t), FP8 values as e4m3 bytes.
+ *   - Alignment: hidden rows (bf16, FP8), receive rows and chunk buffers need
+ *     16 B aligned base pointers; other arrays their element alignment.
+ *   - Return value: EP_OK, or a negative EP_ERR_* status. Nothing is enqueued
+ *     when a host-side check fails. Problems only visible on the device set
+ *     bits in the workspace's error word (read with ep_check_errors).
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define EP_OK 0
+#define EP_ERR_ARG (-1)         /* null / misaligned pointer, bad shape, bad size */
+#define EP_ERR_UNSUPPORTED (-2) /* shape outside the supported limits below */
+#define EP_ERR_HIP (-3)         /* a HIP runtime call or launch failed */
+
+/* Device error bits (workspace error word). */
+#define EP_DEVERR_EXPERT_ID 1u  /* an expert id < -1 or >= E (treated as -1) */
+#define EP_DEVERR_CAPACITY 2u   /* a row index >= the given buffer capacity (not written / not read) */
+#define EP_DEVERR_FLAG 4u       /* a 512 B chunk flag != epoch (row dropped / skipped) */
+
+/* Payload pieces present in a token record (ep_record_bytes). */
+#define EP_SEG_BF16 1
+#define EP_SEG_FP8 2
+#define EP_SEG_SCALES 4
+
+/* Row formats accepted by ep_combine. */
+#define EP_FMT_PLAIN 0    /* rows of H bf16 values at a fixed byte stride */
+#define EP_FMT_CHUNKED 1  /* chunked token records (see ep_hierarchical_dispatch) */
+
+/* Two-level dispatch steps. */
+#define EP_HIER_SCALEOUT 1 /* step 1: one write per (token, destination group) */
+#define EP_HIER_FORWARD 2  /* step 2: forward group rows to scale-up peers */
+
+/* Supported limits (EP_ERR_UNSUPPORTED beyond them). */
+#define EP_MAX_TOPK 64
+#define EP_MAX_RANKS 1024
+#define EP_MAX_GROUPS 256
+#define EP_MAX_EXPERTS 4096
+
+/* Problem shape. T >= 0 tokens; H hidden size (H % 8 == 0; H % 128 == 0 when
+ * FP8 scales are used); K in [1, 64] experts per token; E experts; R ranks
+ * with E % R == 0; G groups with R % G == 0 (G = 1 for the flat path). */
+typedef struct ep_shape {
+    int32_t T, H, K, E, R, G;
+} ep_shape;
+
+/* Layout arrays written by ep_get_layout and read by the other calls
+ * ([V2] §3.3 阶段1: per-expert counts, per-rank counts after rank
+ * deduplication, prefix sums; [V2] §3.3 阶段2: one slot per token and
+ * destination; the is-token-in-rank mask of [PIPE]'s RDMA sender). */
+typedef struct ep_layout {
+    int32_t *tokens_per_expert;  /* [E]   valid lanes per expert (not deduplicated) */
+    int32_t *tokens_per_rank;    /* [R]   tokens per rank, each token counted once */
+    int32_t *tokens_per_group;   /* [G]   tokens per group, each token counted once */
+    int32_t *expert_offsets;     /* [E+1] exclusive prefix sum of tokens_per_expert */
+    int32_t *rank_offsets;       /* [R+1] exclusive prefix sum; rank_offsets[R] = N rows */
+    int32_t *group_offsets;      /* [G+1] exclusive prefix sum of tokens_per_group */
+    uint8_t *is_token_in_rank;   /* [T*R] 1 if token t sends to rank r, else 0 */
+    uint8_t *is_token_in_group;  /* [T*G] 1 if token t sends to group g, else 0 */
+    int32_t *slot;               /* [T*K] receive row of (t, rank of lane k); -1 if lane skipped */
+    int32_t *group_slot;         /* [T*K] group-region row of (t, group of lane k); -1 if skipped */
+} ep_layout;
+
+/* Send side: per-token payload and routing of the T local tokens ([V2] §3.5). */
+typedef struct ep_tokens {
+    const uint16_t *x;            /* [T*H] bf16 hidden rows, or NULL */
+    const uint8_t *x_fp8;         /* [T*H] e4m3 hidden rows, or NULL */
+    const float *x_scales;        /* [T*H/128] one fp32 scale per 128 channels, or NULL */
+    const int64_t *topk_idx;      /* [T*K] expert ids, -1 = no expert (required) */
+    const float *topk_weights;    /* [T*K] routing weights, or NULL */
+} ep_tokens;
+
+/* Receive side of the direct dispatch: `capacity` rows each ([V2] §3.5
+ * outputs recv_x / recv_topk_idx / recv_topk_weights; [PIPE] NVL receivers
+ * write recv_x[row] and recv_x_scales[row * H/128]). */
+typedef struct ep_recv {
+    uint16_t *x;               /* [cap*H] or NULL (needs ep_tokens.x) */
+    uint8_t *x_fp8;            /* [cap*H] or NULL (needs ep_tokens.x_fp8) */
+    float *x_scales;           /* [cap*H/128] or NULL (needs ep_tokens.x_scales) */
+    int32_t *src_idx;          /* [cap] source token of each row, or NULL */
+    int32_t *topk_idx;         /* [cap*K] the token's expert ids as int32 (invalid -> -1), or NULL */
+    float *topk_weights;       /* [cap*K] the token's weights, bit for bit, or NULL */
+    int64_t capacity;          /* rows available; rows >= capacity are not written */
+} ep_recv;
+
+/* Bytes of workspace the calls need for `shape` (host only, no GPU work).
+ * Layout: a 4-byte error word at offset 0, then per-block partial counts.
+ * The workspace may be reused by successive calls on one stream. */
+size_t ep_workspace_bytes(const ep_shape *shape);
+
+/* Byte length P of a packed token record with pieces `seg_flags`
+ * (EP_SEG_*): [bf16 H*2][fp8 H][scales (H/128)*4][topk_idx K*4][topk_w K*4]
+ * [src 4], each present piece padded to 16 B ([V2] §3.4 TokenLayout; the
+ * metadata pieces are always present). Host only. Returns -1 on bad args. */
+int64_t ep_record_bytes(const ep_shape *shape, int seg_flags);
+
+/* Row stride of a chunked record: 512 * ceil(P / 480) bytes ([ASC] 导言 and
+ * 能省多少: 512 B blocks of 480 B payload + 32 B flag). Host only. */
+int64_t ep_chunked_record_bytes(const ep_shape *shape, int seg_flags);
+
+/* Layout ([V2] §3.3 阶段1 notify warps and the slot rule of 阶段2).
+ * For each token t and lane k with a valid expert e = topk_idx[t*K+k]:
+ * rank r = e / (E/R), group g = r / (R/G). Counts: tokens_per_expert per lane;
+ * tokens_per_rank / tokens_per_group once per token. Offsets: exclusive
+ * prefix sums. Slot: slot[t*K+k] = rank_offsets[r] + #{t' < t : token t'
+ * sends to r} (repeated ranks in a token share the row); group_slot likewise
+ * with groups. Every output pointer except the workspace may be NULL to skip
+ * that output. Also clears the workspace error word first, so a pass of
+ * calls starts with a clean word. Ids < -1 or >= E set EP_DEVERR_EXPERT_ID
+ * and count as -1. ws: at least ep_workspace_bytes(shape) bytes, 256 B
+ * aligned. */
+int ep_get_layout(const ep_shape *shape, const int64_t *topk_idx, const ep_layout *layout,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* Direct dispatch ([V2] §3.3 阶段2 and §3.5; [PIPE] RDMA sender / NVL
+ * sender record fields). Each token is read once and its record (present
+ * pieces of ep_tokens plus src index, topk ids and weights) is written to
+ * every receive row it owns: recv row layout->slot[t*K+k] for the first lane
+ * k of each distinct rank. Needs layout->slot from ep_get_layout with the
+ * same topk_idx. Receive pointers may be NULL to skip that piece. Rows >=
+ * recv->capacity are not written and set EP_DEVERR_CAPACITY. */
+int ep_dispatch(const ep_shape *shape, const ep_layout *layout, const ep_tokens *tokens,
+                const ep_recv *recv, void *ws, size_t ws_bytes, void *stream);
+
+/* Two-level dispatch ([V2] §3.6; [PIPE] hybrid scale-out stage and forward
+ * warps) with chunked records ([ASC] data-as-flag 512 B blocks).
+ * A record (ep_record_bytes, pieces = the non-NULL ones among x, x_fp8,
+ * x_scales; x is required, topk_weights required) is cut into 512 B blocks:
+ * block c holds record bytes [480c, 480c+480) (zero past the end) and then
+ * eight u32 flag words equal to `epoch`. Row stride = ep_chunked_record_bytes.
+ *  step EP_HIER_SCALEOUT: each token writes its chunked record once per
+ *    destination group g, at row layout->group_slot of group_buf.
+ *  step EP_HIER_FORWARD: each row n < min(group_offsets[G], group_cap) of
+ *    group_buf is read once; if any block flag != epoch the row is dropped
+ *    (EP_DEVERR_FLAG); else its record is written, flags = epoch, to
+ *    peer_buf row layout->slot[src*K+k] for the first lane k of each distinct
+ *    rank of the row's group.
+ * `steps` is EP_HIER_SCALEOUT, EP_HIER_FORWARD or both (two launches, stream
+ * ordered). epoch >= 1 (zeroed memory never passes the flag check). Needs
+ * layout->slot, group_slot and group_offsets. Rows >= a buffer's capacity are
+ * not written (EP_DEVERR_CAPACITY). After both steps the unpacked peer rows
+ * equal what ep_dispatch writes for the same pieces. */
+int ep_hierarchical_dispatch(const ep_shape *shape, const ep_layout *layout,
+                             const ep_tokens *tokens, uint32_t epoch, int steps,
+                             void *group_buf, int64_t group_cap, void *peer_buf,
+                             int64_t peer_cap, void *ws, size_t ws_bytes, void *stream);
+
+/* Combine ([MEGA] combine write of BF16 expert outputs per (token, top-k);
+ * [ASC] BF16 hidden with FP32 top-k weights): the inverse gather plus a
+ * weighted reduction back to token order:
+ *   out[t][h] = bf16_rne(acc), acc = +0.0f, then for k = 0..K-1 with
+ *   s = layout->slot[t*K+k] >= 0:  acc = fmaf(topk_weights[t*K+k], y[s][h], acc)
+ * (fp32, one rounding per step, ascending k; a row shared by two lanes is read
+ * once and used twice). y: `y_rows` rows at `y_row_stride` bytes; format
+ * EP_FMT_PLAIN (H bf16 at the start of each row; stride % 16 == 0) or
+ * EP_FMT_CHUNKED (chunked records whose first piece is the bf16 hidden;
+ * stride % 512 == 0; a row whose hidden-carrying blocks do not all have
+ * flag == epoch is skipped with EP_DEVERR_FLAG). s >= y_rows is skipped with
+ * EP_DEVERR_CAPACITY. A token with no usable lane gets zeros. */
+int ep_combine(const ep_shape *shape, const ep_layout *layout, const void *y, int64_t y_rows,
+               int64_t y_row_stride, int y_format, uint32_t epoch, const float *topk_weights,
+               uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Clear the workspace error word (a stream-ordered kernel, no memset node). */
+int ep_clear_errors(void *ws, void *stream);
+
+/* Synchronise `stream`, then copy the error word to *bits (host pointer). */
+int ep_check_errors(void *ws, void *stream, uint32_t *bits);
+
+/* Static description of a status code. */
+const char *ep_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

@@ -1,0 +1,88 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+that include/ep.h declares, and its host-only logic (sizes, argument checks)
+behaves as documented. No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_get_layout_amd import ep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(ep_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ep.LIB_PATH):
+        from combine_get_layout_amd import build
+        build.build()
+    return ep.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(ep.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_sizes_match_oracle(lib, oracle_lib):
+    for (T, H, K, E, R, G) in [(128, 256, 2, 16, 4, 1), (4096, 7168, 8, 256, 32, 1),
+                               (16384, 7168, 8, 256, 64, 8), (5, 384, 3, 12, 6, 3)]:
+        s = ep.make_shape(T, H, K, E, R, G)
+        for seg, fl in [(1, (1, 0, 0)), (3, (1, 1, 0)), (7, (1, 1, 1))]:
+            P = oracle_lib.record_bytes(H, K, *fl)
+            assert ep.ep_record_bytes(s, seg) == P
+            assert ep.ep_chunked_record_bytes(s, seg) == oracle_lib.chunked_bytes(P)
+        assert ep.ep_workspace_bytes(s) >= 256
+
+
+def test_bad_shapes_rejected(lib):
+    bad = [(-1, 256, 2, 16, 4, 1), (8, 250, 2, 16, 4, 1), (8, 256, 0, 16, 4, 1),
+           (8, 256, 2, 15, 4, 1), (8, 256, 2, 16, 4, 3)]
+    for b in bad:
+        assert ep.ep_workspace_bytes(ep.make_shape(*b)) == 0
+    unsupported = [(8, 256, 65, 16, 4, 1), (8, 256, 2, 8192, 8, 1), (8, 256, 2, 2048, 2048, 1)]
+    for u in unsupported:
+        s = ep.make_shape(*u)
+        assert ep.ep_workspace_bytes(s) == 0
+        rc = lib.ep_get_layout(ctypes.byref(s), None, None, None, 0, None)
+        assert rc == ep.EP_ERR_UNSUPPORTED
+    s = ep.make_shape(8, 264, 2, 16, 4, 1)
+    assert ep.ep_record_bytes(s, ep.EP_SEG_SCALES) == -1  # scales need H % 128 == 0
+
+
+def test_null_and_misaligned_arguments_rejected_before_launch(lib):
+    s = ep.make_shape(128, 256, 2, 16, 4, 1)
+    L = ep.ep_layout()
+    # no workspace
+    assert lib.ep_get_layout(ctypes.byref(s), 0x1000, ctypes.byref(L), None, 1 << 20, None) == ep.EP_ERR_ARG
+    # misaligned workspace
+    assert lib.ep_get_layout(ctypes.byref(s), 0x1000, ctypes.byref(L), 0x1010, 1 << 20, None) == ep.EP_ERR_ARG
+    # undersized workspace
+    assert lib.ep_get_layout(ctypes.byref(s), 0x1000, ctypes.byref(L), 0x1000, 16, None) == ep.EP_ERR_ARG
+    tk = ep.ep_tokens()
+    rv = ep.ep_recv()
+    ws = 0x100000
+    n = ep.ep_workspace_bytes(s)
+    assert lib.ep_dispatch(ctypes.byref(s), ctypes.byref(L), ctypes.byref(tk), ctypes.byref(rv),
+                           ws, n, None) == ep.EP_ERR_ARG  # no slot / topk
+    # epoch 0 is refused by the two-level path and by chunked combine
+    assert lib.ep_hierarchical_dispatch(ctypes.byref(s), ctypes.byref(L), ctypes.byref(tk), 0, 3,
+                                        None, 0, None, 0, ws, n, None) == ep.EP_ERR_ARG
+    assert lib.ep_combine(ctypes.byref(s), ctypes.byref(L), 0x2000, 4, 1024, ep.EP_FMT_CHUNKED, 0,
+                          0x3000, 0x4000, ws, n, None) == ep.EP_ERR_ARG
+    # plain stride smaller than a row
+    assert lib.ep_combine(ctypes.byref(s), ctypes.byref(L), 0x2000, 4, 256, ep.EP_FMT_PLAIN, 0,
+                          0x3000, 0x4000, ws, n, None) == ep.EP_ERR_ARG
+    assert lib.ep_clear_errors(None, None) == ep.EP_ERR_ARG
+    assert lib.ep_check_errors(None, None, None) == ep.EP_ERR_ARG
+    assert ep.ep_status_string(0) == "ok"

@@ -1,0 +1,394 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: layout, masks, offsets, slots and every permuted / chunked byte are
+bit-exact; combine outputs are within max |diff| <= 1e-2 and relative L2
+<= 4e-3 of the oracle (and, because both sides use one fp32 fused
+multiply-add per top-k lane in ascending order, are checked bit-exact too).
+All five workloads run at full size; the edge cases cover empty and ragged
+inputs, invalid ids, duplicates, capacity overflow, stale and corrupted flags.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from combine_get_layout_amd import ep
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL_L2 = 1e-2, 4e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ep.lib()
+    oracle.build(force=False)
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:  # move 16-bit patterns as int16, keep the uint16 view
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.uint16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t):
+    if t.dtype == torch.uint16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def poison(t, byte=0xAB):
+    t.view(torch.uint8).fill_(byte)
+    return t
+
+
+def run_layout(w, topk, masks=True, groups=True):
+    shape = ep.make_shape(topk.shape[0], w.H, topk.shape[1], w.E, w.R, w.G)
+    L = ep.alloc_layout(shape, masks=masks, groups=groups)
+    for t in L.values():
+        poison(t)
+    ws = ep.alloc_workspace(shape)
+    tk = dev(topk)
+    ep.ep_get_layout(shape, tk, L, ws)
+    torch.cuda.synchronize()
+    return shape, L, ws, tk
+
+
+def check_layout(L, O, T):
+    for k in ("tokens_per_expert", "tokens_per_rank", "tokens_per_group", "expert_offsets",
+              "rank_offsets", "group_offsets", "is_token_in_rank", "is_token_in_group",
+              "slot", "group_slot"):
+        if k in L:
+            np.testing.assert_array_equal(host(L[k]).reshape(O[k].shape), O[k], err_msg=k)
+
+
+def combine_close(out_bits, ref_bits):
+    o = synth.bf16_to_float(out_bits).astype(np.float64)
+    r = synth.bf16_to_float(ref_bits).astype(np.float64)
+    d = np.abs(o - r)
+    assert d.max(initial=0.0) <= ATOL
+    nr = np.linalg.norm(r)
+    assert np.linalg.norm(o - r) <= RTOL_L2 * max(nr, 1e-30)
+
+
+WORKLOADS = ["tiny", "ep32", "ep256", "zipf", "hier8x8"]
+
+
+# --------------------------------------------------------------------------
+# Layout
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_layout_full_size(name):
+    w = synth.workload(name)
+    inp = synth.make_inputs(w, with_x=False)
+    shape, L, ws, _ = run_layout(w, inp["topk_idx"])
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    check_layout(L, O, w.T)
+    assert ep.ep_check_errors(ws) == 0
+
+
+LAYOUT_EDGES = [
+    # (T, K, E, R, G, kind)
+    (0, 8, 256, 32, 4, "uniform"),
+    (1, 8, 256, 32, 4, "uniform"),
+    (257, 3, 12, 6, 3, "random"),      # ragged block, K not a power of two
+    (1001, 20, 64, 16, 4, "random"),   # K above 16, duplicates and -1
+    (300, 1, 16, 16, 1, "random"),     # top-1
+    (513, 4, 16, 1, 1, "random"),      # one rank
+    (640, 8, 4096, 1024, 256, "uniform"),  # largest supported R, G, E
+    (200, 4, 16, 4, 2, "one_rank"),    # all tokens to one rank, empty ranks
+]
+
+
+def _edge_topk(T, K, E, R, kind, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "uniform":
+        return synth.topk_uniform(rng, T, E, K)
+    if kind == "one_rank":
+        epr = E // R
+        return rng.integers(epr, 2 * epr, size=(T, K)).astype(np.int64)
+    return rng.integers(-1, E, size=(T, K)).astype(np.int64)
+
+
+@pytest.mark.parametrize("case", LAYOUT_EDGES, ids=[f"T{c[0]}K{c[1]}E{c[2]}R{c[3]}G{c[4]}{c[5]}"
+                                                    for c in LAYOUT_EDGES])
+def test_layout_edges(case):
+    T, K, E, R, G, kind = case
+    w = synth.Workload("edge", T, 128, E, R, G, K, "uniform")
+    topk = _edge_topk(T, K, E, R, kind, seed=T + K)
+    shape, L, ws, _ = run_layout(w, topk)
+    O = oracle.layout(topk, E, R, G)
+    check_layout(L, O, T)
+    assert ep.ep_check_errors(ws) == 0
+
+
+def test_layout_invalid_ids_flagged():
+    w = synth.Workload("bad", 300, 128, 32, 8, 2, 4, "uniform")
+    rng = np.random.default_rng(5)
+    topk = rng.integers(-1, 32, size=(300, 4)).astype(np.int64)
+    topk[3, 1], topk[70, 0], topk[299, 3] = 32, -2, 1 << 40
+    shape, L, ws, _ = run_layout(w, topk)
+    O = oracle.layout(topk, w.E, w.R, w.G)
+    assert O["err"] == oracle.ERR_EXPERT
+    check_layout(L, O, w.T)
+    assert ep.ep_check_errors(ws) == ep.EP_DEVERR_EXPERT_ID
+    # the next pass starts with a clean error word
+    ep.ep_get_layout(shape, dev(np.maximum(topk % 32, 0)), L, ws)
+    assert ep.ep_check_errors(ws) == 0
+
+
+# --------------------------------------------------------------------------
+# Dispatch
+# --------------------------------------------------------------------------
+
+def run_dispatch(w, inp, shape, L, ws, tk, capacity=None, fp8=False, meta=True):
+    N = int(host(L["rank_offsets"])[-1])
+    cap = N if capacity is None else capacity
+    tokens = dict(x=dev(inp["x"]), topk_idx=tk, topk_weights=dev(inp["topk_w"]))
+    if fp8:
+        tokens["x_fp8"] = dev(inp["x_fp8"])
+        tokens["x_scales"] = dev(inp["x_scales"])
+    recv = ep.alloc_recv(shape, max(cap, 1), fp8=fp8, scales=fp8, meta=meta)
+    for t in recv.values():
+        poison(t)
+    ep.ep_dispatch(shape, L, tokens, recv, cap, ws)
+    torch.cuda.synchronize()
+    return recv, N, cap
+
+
+def check_dispatch(recv, D, rows):
+    pairs = [("x", "recv_x"), ("x_fp8", "recv_fp8"), ("x_scales", "recv_scales"),
+             ("src_idx", "recv_src"), ("topk_idx", "recv_topk_idx"),
+             ("topk_weights", "recv_topk_w")]
+    for g, o in pairs:
+        if g in recv and D.get(o) is not None:
+            a = host(recv[g])[:rows]
+            b = D[o][:rows]
+            np.testing.assert_array_equal(a.view(np.uint8), b.view(np.uint8), err_msg=g)
+
+
+@pytest.mark.parametrize("name,fp8", [("tiny", False), ("ep32", False), ("ep32", True),
+                                      ("ep256", False), ("zipf", False), ("hier8x8", False)])
+def test_dispatch_full_size(name, fp8):
+    w = synth.workload(name)
+    inp = synth.make_inputs(w, with_fp8=fp8)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    recv, N, _ = run_dispatch(w, inp, shape, L, ws, tk, fp8=fp8)
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    D = oracle.dispatch(inp["topk_idx"], w.E, w.R, O["rank_offsets"], x=inp["x"],
+                        x_fp8=inp.get("x_fp8"), x_scales=inp.get("x_scales"),
+                        topk_w=inp["topk_w"])
+    assert D["recv_x"].shape[0] == N
+    check_dispatch(recv, D, N)
+    assert ep.ep_check_errors(ws) == 0
+
+
+@pytest.mark.parametrize("T,H,K,E,R", [(1, 8, 1, 4, 2), (3, 1032, 3, 12, 6), (1001, 4096, 20, 64, 16),
+                                       (257, 16, 8, 64, 64), (500, 384, 4, 16, 1)])
+def test_dispatch_edges(T, H, K, E, R):
+    w = synth.Workload("edge", T, H, E, R, 1, K, "uniform")
+    rng = np.random.default_rng(T * 7 + H)
+    inp = dict(x=rng.integers(0, 65536, size=(T, H)).astype(np.uint16),
+               topk_idx=rng.integers(-1, E, size=(T, K)).astype(np.int64),
+               topk_w=rng.standard_normal((T, K)).astype(np.float32))
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    recv, N, _ = run_dispatch(w, inp, shape, L, ws, tk)
+    O = oracle.layout(inp["topk_idx"], E, R, 1)
+    D = oracle.dispatch(inp["topk_idx"], E, R, O["rank_offsets"], x=inp["x"], topk_w=inp["topk_w"])
+    check_dispatch(recv, D, N)
+
+
+def test_dispatch_capacity_overflow():
+    w = synth.workload("tiny")
+    inp = synth.make_inputs(w)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    N = int(host(L["rank_offsets"])[-1])
+    recv, _, cap = run_dispatch(w, inp, shape, L, ws, tk, capacity=N - 17)
+    O = oracle.layout(inp["topk_idx"], w.E, w.R)
+    D = oracle.dispatch(inp["topk_idx"], w.E, w.R, O["rank_offsets"], x=inp["x"],
+                        topk_w=inp["topk_w"], capacity=N - 17)
+    assert D["err"] == oracle.ERR_CAPACITY
+    check_dispatch(recv, D, cap)
+    assert ep.ep_check_errors(ws) == ep.EP_DEVERR_CAPACITY
+
+
+def test_dispatch_zero_tokens():
+    w = synth.Workload("empty", 0, 256, 16, 4, 1, 2, "uniform")
+    topk = np.zeros((0, 2), np.int64)
+    shape, L, ws, tk = run_layout(w, topk)
+    assert (host(L["rank_offsets"]) == 0).all()
+    recv = ep.alloc_recv(shape, 1)
+    ep.ep_dispatch(shape, L, dict(x=torch.empty((0, 256), dtype=torch.uint16, device="cuda"),
+                                  topk_idx=tk), recv, 0, ws)
+    out = torch.empty((0, 256), dtype=torch.uint16, device="cuda")
+    ep.ep_combine(shape, L, recv["x"], 0, 512, ep.EP_FMT_PLAIN, 0,
+                  torch.empty((0, 2), device="cuda"), out, ws)
+    assert ep.ep_check_errors(ws) == 0
+
+
+# --------------------------------------------------------------------------
+# Combine
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "ep32", "ep256", "zipf"])
+def test_combine_full_size(name):
+    """Combine of stand-in expert outputs (random bf16 rows) and, for the
+    identity expert, of the dispatched rows (round trip back to x)."""
+    w = synth.workload(name)
+    inp = synth.make_inputs(w)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    N = int(host(L["rank_offsets"])[-1])
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    y = synth.random_bf16_rows(N, w.H, seed=99)
+    yd = dev(y)
+    wd = dev(inp["topk_w"])
+    out = poison(torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda"))
+    ep.ep_combine(shape, L, yd, N, 2 * w.H, ep.EP_FMT_PLAIN, 0, wd, out, ws)
+    C = oracle.combine(O["slot"], inp["topk_w"], y, w.H)
+    got = host(out)
+    combine_close(got, C["out"])
+    np.testing.assert_array_equal(got, C["out"])
+    assert ep.ep_check_errors(ws) == 0
+    # round trip: dispatch -> identity expert -> combine reproduces x
+    recv, _, _ = run_dispatch(w, inp, shape, L, ws, tk, meta=False)
+    ep.ep_combine(shape, L, recv["x"], N, 2 * w.H, ep.EP_FMT_PLAIN, 0, wd, out, ws)
+    combine_close(host(out), inp["x"])
+
+
+@pytest.mark.parametrize("T,H,K", [(1, 8, 1), (77, 1032, 3), (300, 264, 2), (129, 512, 5),
+                                   (64, 2048, 16), (33, 128, 24)])
+def test_combine_edges(T, H, K):
+    rng = np.random.default_rng(T + H + K)
+    rows = 3 * T + 1
+    slot = rng.integers(-1, rows, size=(T, K)).astype(np.int32)
+    if K > 1:
+        slot[::3, 1] = slot[::3, 0]          # repeated rows
+    slot[0] = -1                              # no usable lane -> zeros
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    y = synth.random_bf16_rows(rows, H, seed=T)
+    shape = ep.make_shape(T, H, K, 4, 2, 1)
+    ws = ep.alloc_workspace(shape)
+    L = dict(slot=dev(slot))
+    out = poison(torch.empty((T, H), dtype=torch.uint16, device="cuda"))
+    ep.ep_clear_errors(ws)
+    ep.ep_combine(shape, L, dev(y), rows, 2 * H, ep.EP_FMT_PLAIN, 0, dev(w), out, ws)
+    C = oracle.combine(slot, w, y, H)
+    np.testing.assert_array_equal(host(out), C["out"])
+    assert ep.ep_check_errors(ws) == 0
+
+
+def test_combine_rows_out_of_range():
+    T, H, K, rows = 50, 256, 4, 40
+    rng = np.random.default_rng(8)
+    slot = rng.integers(-1, 60, size=(T, K)).astype(np.int32)
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    y = synth.random_bf16_rows(64, H, seed=3)
+    shape = ep.make_shape(T, H, K, 4, 2, 1)
+    ws = ep.alloc_workspace(shape)
+    out = torch.empty((T, H), dtype=torch.uint16, device="cuda")
+    ep.ep_clear_errors(ws)
+    ep.ep_combine(shape, dict(slot=dev(slot)), dev(y), rows, 2 * H, ep.EP_FMT_PLAIN, 0, dev(w), out, ws)
+    C = oracle.combine(slot, w, y[:rows], H)
+    assert C["err"] == oracle.ERR_CAPACITY
+    np.testing.assert_array_equal(host(out), C["out"])
+    assert ep.ep_check_errors(ws) == ep.EP_DEVERR_CAPACITY
+
+
+# --------------------------------------------------------------------------
+# Two-level dispatch with 512 B data-as-flag chunks
+# --------------------------------------------------------------------------
+
+def run_hier(w, inp, shape, L, ws, tk, epoch, steps=3, group_buf=None, peer_buf=None, fp8=False):
+    seg = ep.EP_SEG_BF16 | ((ep.EP_SEG_FP8 | ep.EP_SEG_SCALES) if fp8 else 0)
+    stride = ep.ep_chunked_record_bytes(shape, seg)
+    G_rows = int(host(L["group_offsets"])[-1])
+    N = int(host(L["rank_offsets"])[-1])
+    if group_buf is None:
+        group_buf = torch.zeros((max(G_rows, 1), stride), dtype=torch.uint8, device="cuda")
+    if peer_buf is None:
+        peer_buf = torch.zeros((max(N, 1), stride), dtype=torch.uint8, device="cuda")
+    tokens = dict(x=dev(inp["x"]), topk_idx=tk, topk_weights=dev(inp["topk_w"]))
+    if fp8:
+        tokens["x_fp8"] = dev(inp["x_fp8"])
+        tokens["x_scales"] = dev(inp["x_scales"])
+    ep.ep_hierarchical_dispatch(shape, L, tokens, epoch, steps, group_buf, G_rows, peer_buf, N, ws)
+    torch.cuda.synchronize()
+    return group_buf, peer_buf, G_rows, N, stride
+
+
+@pytest.mark.parametrize("name,fp8", [("hier8x8", False), ("small", True), ("small", False)])
+def test_hierarchical_full(name, fp8):
+    w = synth.workload(name) if name != "small" else synth.Workload("small", 1500, 1024, 64, 16, 4, 6, "uniform")
+    inp = synth.make_inputs(w, with_fp8=fp8)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    epoch = 5
+    gb, pb, G_rows, N, stride = run_hier(w, inp, shape, L, ws, tk, epoch, fp8=fp8)
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    Hd = oracle.hier_dispatch(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_offsets"], epoch,
+                              x=inp["x"], x_fp8=inp.get("x_fp8"), x_scales=inp.get("x_scales"),
+                              topk_w=inp["topk_w"])
+    assert Hd["stride"] == stride and Hd["err"] == 0
+    np.testing.assert_array_equal(host(gb)[:G_rows], Hd["group_buf"])
+    np.testing.assert_array_equal(host(pb)[:N], Hd["peer_buf"])
+    assert ep.ep_check_errors(ws) == 0
+    # combine straight from the chunked scale-up rows
+    out = poison(torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda"))
+    ep.ep_combine(shape, L, pb, N, stride, ep.EP_FMT_CHUNKED, epoch, dev(inp["topk_w"]), out, ws)
+    C = oracle.combine(O["slot"], inp["topk_w"], Hd["peer_buf"], w.H, chunked=True, epoch=epoch)
+    assert C["err"] == 0
+    got = host(out)
+    np.testing.assert_array_equal(got, C["out"])
+    combine_close(got, inp["x"])
+    assert ep.ep_check_errors(ws) == 0
+
+
+def test_hierarchical_corrupted_flag_and_stale_epoch():
+    w = synth.Workload("small", 400, 512, 32, 8, 4, 4, "uniform")
+    inp = synth.make_inputs(w, seed=31)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    epoch = 11
+    gb, pb, G_rows, N, stride = run_hier(w, inp, shape, L, ws, tk, epoch, steps=ep.EP_HIER_SCALEOUT)
+    row, byte = 37, 2 * 512 + 480 + 9
+    gb[row, byte] ^= 0x10
+    run_hier(w, inp, shape, L, ws, tk, epoch, steps=ep.EP_HIER_FORWARD, group_buf=gb, peer_buf=pb)
+    assert ep.ep_check_errors(ws) == ep.EP_DEVERR_FLAG
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    kw = dict(x=inp["x"], topk_w=inp["topk_w"])
+    s1 = oracle.hier_dispatch(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_offsets"], epoch,
+                              steps=1, **kw)
+    g = s1["group_buf"].copy()
+    g[row, byte] ^= 0x10
+    s2 = oracle.hier_dispatch(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_offsets"], epoch,
+                              steps=2, group_buf=g, **kw)
+    assert s2["err"] == oracle.ERR_FLAG
+    np.testing.assert_array_equal(host(pb)[:N], s2["peer_buf"])
+    # combine with a stale epoch: every row rejected, zeros out
+    ep.ep_clear_errors(ws)
+    out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
+    ep.ep_combine(shape, L, pb, N, stride, ep.EP_FMT_CHUNKED, epoch + 1, dev(inp["topk_w"]), out, ws)
+    assert ep.ep_check_errors(ws) == ep.EP_DEVERR_FLAG
+    assert (host(out) == 0).all()
+    # combine with the right epoch: the holes left by the dropped row are skipped
+    ep.ep_clear_errors(ws)
+    ep.ep_combine(shape, L, pb, N, stride, ep.EP_FMT_CHUNKED, epoch, dev(inp["topk_w"]), out, ws)
+    C = oracle.combine(O["slot"], inp["topk_w"], s2["peer_buf"], w.H, chunked=True, epoch=epoch)
+    assert C["err"] == oracle.ERR_FLAG
+    np.testing.assert_array_equal(host(out), C["out"])
+    assert ep.ep_check_errors(ws) == ep.EP_DEVERR_FLAG
+
+
+def test_repeat_calls_identical():
+    """Same inputs, two dispatch passes into fresh buffers: identical bytes (a
+    race or ordering bug would show as a difference)."""
+    w = synth.workload("ep32").scaled(2048)
+    inp = synth.make_inputs(w)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    r1, N, _ = run_dispatch(w, inp, shape, L, ws, tk)
+    r2, _, _ = run_dispatch(w, inp, shape, L, ws, tk)
+    for k in r1:
+        assert torch.equal(r1[k][:N].view(torch.uint8), r2[k][:N].view(torch.uint8)), k
