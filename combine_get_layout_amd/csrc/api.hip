@@ -127,8 +127,9 @@ int ep_dispatch(const ep_shape* shape, const ep_layout* layout, const ep_tokens*
     if ((rc = check_ws(shape, ws, ws_bytes)) != EP_OK) return rc;
     if (!layout || !tokens || !recv || recv->capacity < 0) return EP_ERR_ARG;
     if (shape->T > 0 && (!layout->slot || !tokens->topk_idx)) return EP_ERR_ARG;
-    if ((recv->x && !tokens->x) || (recv->x_fp8 && !tokens->x_fp8) ||
-        (recv->x_scales && !tokens->x_scales) || (recv->topk_weights && !tokens->topk_weights))
+    if (shape->T > 0 &&
+        ((recv->x && !tokens->x) || (recv->x_fp8 && !tokens->x_fp8) ||
+         (recv->x_scales && !tokens->x_scales) || (recv->topk_weights && !tokens->topk_weights)))
         return EP_ERR_ARG;
     if ((tokens->x_fp8 || recv->x_fp8) && shape->H % 16 != 0) return EP_ERR_ARG;
     if ((tokens->x_scales || recv->x_scales) && shape->H % 128 != 0) return EP_ERR_ARG;

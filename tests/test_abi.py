@@ -86,3 +86,18 @@ def test_null_and_misaligned_arguments_rejected_before_launch(lib):
     assert lib.ep_clear_errors(None, None) == ep.EP_ERR_ARG
     assert lib.ep_check_errors(None, None, None) == ep.EP_ERR_ARG
     assert ep.ep_status_string(0) == "ok"
+
+
+def test_zero_tokens_dispatch_and_combine_enqueue_nothing(lib):
+    """With T = 0 there is nothing to read or write: both calls succeed
+    without touching the device (so this runs without a GPU)."""
+    s = ep.make_shape(0, 256, 2, 16, 4, 1)
+    n = ep.ep_workspace_bytes(s)
+    L = ep.ep_layout()
+    tk = ep.ep_tokens()
+    rv = ep.ep_recv(0x2000, None, None, 0x3000, None, None, 0)
+    ws = 0x100000
+    assert lib.ep_dispatch(ctypes.byref(s), ctypes.byref(L), ctypes.byref(tk), ctypes.byref(rv),
+                           ws, n, None) == ep.EP_OK
+    assert lib.ep_combine(ctypes.byref(s), ctypes.byref(L), None, 0, 512, ep.EP_FMT_PLAIN, 0,
+                          None, None, ws, n, None) == ep.EP_OK

@@ -222,7 +222,7 @@ def test_dispatch_zero_tokens():
     topk = np.zeros((0, 2), np.int64)
     shape, L, ws, tk = run_layout(w, topk)
     assert (host(L["rank_offsets"]) == 0).all()
-    recv = ep.alloc_recv(shape, 1)
+    recv = ep.alloc_recv(shape, 1, meta=False)
     ep.ep_dispatch(shape, L, dict(x=torch.empty((0, 256), dtype=torch.uint16, device="cuda"),
                                   topk_idx=tk), recv, 0, ws)
     out = torch.empty((0, 256), dtype=torch.uint16, device="cuda")
