@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MALL_EVICT_BYTES = 320 << 20  # more than the 256 MB MALL
 METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
 
 
@@ -92,7 +93,14 @@ def main():
     w = synth.workload(args.workload)
     hier = w.G > 1
     fp8 = bool(args.fp8)
-    inp = synth.make_inputs(w, with_fp8=fp8)
+    # Independent input batches, rotated step by step, so that the x rows a
+    # step reads were not left in the 256 MB MALL by an earlier step: the
+    # other batches' x alone exceed it.
+    x_bytes = w.T * w.H * 2
+    n_batches = max(2, 1 + -(-MALL_EVICT_BYTES // x_bytes))
+    seeds = [synth.seed_of(w) + 1000 * i for i in range(n_batches)]
+    inputs = [synth.make_inputs(w, seed=sd, with_fp8=fp8) for sd in seeds]
+    inp = inputs[0]
 
     def dev(a):
         a = np.ascontiguousarray(a)
@@ -101,29 +109,36 @@ def main():
         return torch.from_numpy(a).cuda()
 
     shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, w.G)
-    tokens = dict(x=dev(inp["x"]), topk_idx=dev(inp["topk_idx"]), topk_weights=dev(inp["topk_w"]))
-    if fp8:
-        tokens["x_fp8"] = dev(inp["x_fp8"])
-        tokens["x_scales"] = dev(inp["x_scales"])
+    batches = []
+    for b_in in inputs:
+        tk = dict(x=dev(b_in["x"]), topk_idx=dev(b_in["topk_idx"]), topk_weights=dev(b_in["topk_w"]))
+        if fp8:
+            tk["x_fp8"] = dev(b_in["x_fp8"])
+            tk["x_scales"] = dev(b_in["x_scales"])
+        batches.append(tk)
     L = ep.alloc_layout(shape, masks=True, groups=hier)
     ws = ep.alloc_workspace(shape)
-    ep.ep_get_layout(shape, tokens["topk_idx"], L, ws)
-    torch.cuda.synchronize()
-    N = int(L["rank_offsets"][-1].item())
-    G_rows = int(L["group_offsets"][-1].item()) if hier else 0
+    Ns, Gs = [], []
+    for tk in batches:
+        ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+        torch.cuda.synchronize()
+        Ns.append(int(L["rank_offsets"][-1].item()))
+        Gs.append(int(L["group_offsets"][-1].item()) if hier else 0)
+    N_cap, G_cap = max(Ns), max(Gs)
     out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
     seg = ep.EP_SEG_BF16 | ((ep.EP_SEG_FP8 | ep.EP_SEG_SCALES) if fp8 else 0)
     if hier:
         stride = ep.ep_chunked_record_bytes(shape, seg)
-        group_buf = torch.empty((G_rows, stride), dtype=torch.uint8, device="cuda")
-        peer_buf = torch.empty((N, stride), dtype=torch.uint8, device="cuda")
+        group_buf = torch.empty((G_cap, stride), dtype=torch.uint8, device="cuda")
+        peer_buf = torch.empty((N_cap, stride), dtype=torch.uint8, device="cuda")
     else:
-        recv = ep.alloc_recv(shape, N, fp8=fp8, scales=fp8, meta=True)
+        recv = ep.alloc_recv(shape, N_cap, fp8=fp8, scales=fp8, meta=True)
 
     epoch = [0]
     stream = torch.cuda.current_stream()
     names = ["layout", "hier" if hier else "dispatch", "combine"]
     ev = {n: [] for n in names}
+    used = []
 
     def timed(name, fn, record):
         if record:
@@ -136,7 +151,11 @@ def main():
             fn()
 
     def step(record):
+        i = epoch[0] % n_batches
         epoch[0] += 1
+        tokens, N, G_rows = batches[i], Ns[i], Gs[i]
+        if record:
+            used.append(i)
         timed("layout", lambda: ep.ep_get_layout(shape, tokens["topk_idx"], L, ws), record)
         if hier:
             timed("hier", lambda: ep.ep_hierarchical_dispatch(
@@ -171,12 +190,15 @@ def main():
     if ep.ep_check_errors(ws) != 0:
         raise RuntimeError("device error bits set during the timed steps")
 
-    # Algorithmic bytes per launch (what the method must move).
+    # Algorithmic bytes per launch (what the method must move),
+    # averaged over the batches the timed steps used.
     T, H, K, R = w.T, w.H, w.K, w.R
     row = 2 * H + ((H + 4 * (H // 128)) if fp8 else 0)
     meta = 4 + 8 * K
     route = T * K * (8 + 4 + 4)  # topk_idx read, weights read, slots read
     bytes_layout = T * K * 8 + T * K * 4 + T * R + (T * K * 4 + T * w.G if hier else 0)
+    N = sum(Ns[i] for i in used) / len(used)
+    G_rows = sum(Gs[i] for i in used) / len(used)
     if hier:
         rec = ep.ep_chunked_record_bytes(shape, seg)
         hid = 512 * ((2 * H + 479) // 480)
@@ -220,7 +242,8 @@ def main():
         "data": "synthetic (seeded; see synth/__init__.py)",
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": w.E,
                    "ranks": R, "groups": w.G, "topk": K, "routing": w.routing,
-                   "receive_rows": N, "fp8_payload": fp8, "parallelism": "single GPU"},
+                   "receive_rows": N, "fp8_payload": fp8, "input_batches": n_batches,
+                   "parallelism": "single GPU"},
         "hbm_gbs_step": step_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernel_ms": avg_ms,

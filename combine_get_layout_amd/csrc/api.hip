@@ -22,12 +22,8 @@ WsLayout ws_layout(const ep_shape& s) {
     off += align256(sizeof(int32_t) * (size_t)w.nb * s.G);
     w.part_expert = off;
     off += align256(sizeof(int32_t) * (size_t)w.nb * s.E);
-    w.tot_rank = off;
-    off += align256(sizeof(int32_t) * (size_t)s.R);
-    w.tot_group = off;
-    off += align256(sizeof(int32_t) * (size_t)s.G);
-    w.tot_expert = off;
-    off += align256(sizeof(int32_t) * (size_t)s.E);
+    w.part_lanes = off;
+    off += align256(sizeof(int32_t) * (size_t)w.nb * s.R);
     w.total = off;
     return w;
 }

@@ -21,8 +21,33 @@
 #include "ep_device.h"
 #include "ep_internal.h"
 
+// Compile-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef EP_CMB_NB8
+#define EP_CMB_NB8 2        // 16-byte vectors per lane per batch when K <= 8
+#endif
+#ifndef EP_CMB_NTLOAD
+#define EP_CMB_NTLOAD 1     // non-temporal loads of the gathered rows
+#endif
+#ifndef EP_CMB_MINB
+#define EP_CMB_MINB 1       // minimum resident workgroups per CU (launch bound)
+#endif
+#ifndef EP_CMB_WPB
+#define EP_CMB_WPB 4        // waves (tokens) per workgroup
+#endif
+
 namespace ep {
 namespace {
+
+constexpr int kCmbWaves = EP_CMB_WPB;
+constexpr int kCmbThreads = kCmbWaves * kWave;
+
+__device__ __forceinline__ u32x4 ld_row(const void* p) {
+#if EP_CMB_NTLOAD
+    return ld16_stream(p);
+#else
+    return ld16(p);
+#endif
+}
 
 struct CombineArgs {
     int T, H, K;
@@ -68,9 +93,9 @@ __device__ __forceinline__ u32x4 pack8(const float (&acc)[8]) {
 // KMAX > 0: up to KMAX lanes unrolled with per-lane registers; KMAX == 0:
 // any K, one lane at a time (repeated rows are simply re-read).
 template <int KMAX, int NB, bool CHUNKED>
-__global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_kernel(CombineArgs a) {
     const int lane = lane_id();
-    const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int t = blockIdx.x * kCmbWaves + wave_in_block();
     if (t >= a.T) return;
     int s = -1;
     float wt = 0.f;
@@ -122,7 +147,7 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a) {
                 if (!((um >> k) & 1)) continue;
                 const int sk = readlane(s, k);
                 const float wk = readlane_f(wt, k);
-                if (valid) fma8(acc, wk, ld16(a.y + (int64_t)sk * a.stride + off));
+                if (valid) fma8(acc, wk, ld_row(a.y + (int64_t)sk * a.stride + off));
             }
             if (valid) st16_stream(out_row + (int64_t)p * 16, pack8(acc));
         }
@@ -153,7 +178,7 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a) {
                 const uint8_t* row = a.y + (int64_t)sk[k] * a.stride;
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
-                    if (valid[j]) v[k][j] = ld16(row + off[j]);
+                    if (valid[j]) v[k][j] = ld_row(row + off[j]);
             }
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
@@ -179,13 +204,13 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a) {
 
 template <bool CHUNKED>
 hipError_t launch_k(const CombineArgs& a, hipStream_t st) {
-    const dim3 grid((a.T + kWavesPerBlock - 1) / kWavesPerBlock), block(kBlockThreads);
+    const dim3 grid((a.T + kCmbWaves - 1) / kCmbWaves), block(kCmbThreads);
     if (a.K <= 2)
         hipLaunchKernelGGL((combine_kernel<2, 8, CHUNKED>), grid, block, 0, st, a);
     else if (a.K <= 4)
         hipLaunchKernelGGL((combine_kernel<4, 4, CHUNKED>), grid, block, 0, st, a);
     else if (a.K <= 8)
-        hipLaunchKernelGGL((combine_kernel<8, 2, CHUNKED>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((combine_kernel<8, EP_CMB_NB8, CHUNKED>), grid, block, 0, st, a);
     else if (a.K <= 16)
         hipLaunchKernelGGL((combine_kernel<16, 1, CHUNKED>), grid, block, 0, st, a);
     else

@@ -18,8 +18,43 @@
 #include "ep_device.h"
 #include "ep_internal.h"
 
+// Compile-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef EP_DSP_NVMAX
+#define EP_DSP_NVMAX 16     // most 16-byte vectors per lane held per pass
+#endif
+#ifndef EP_DSP_NTSTORE
+#define EP_DSP_NTSTORE 1    // non-temporal stores of receive rows
+#endif
+#ifndef EP_DSP_NTLOAD
+#define EP_DSP_NTLOAD 0     // non-temporal loads of the source rows
+#endif
+#ifndef EP_DSP_WPB
+#define EP_DSP_WPB 4        // waves (tokens) per workgroup
+#endif
+#ifndef EP_DSP_MINB
+#define EP_DSP_MINB 1       // minimum resident workgroups per CU (launch bound)
+#endif
+
 namespace ep {
 namespace {
+
+constexpr int kDspWaves = EP_DSP_WPB;
+constexpr int kDspThreads = kDspWaves * kWave;
+
+__device__ __forceinline__ u32x4 ld_src(const void* p) {
+#if EP_DSP_NTLOAD
+    return ld16_stream(p);
+#else
+    return ld16(p);
+#endif
+}
+__device__ __forceinline__ void st_dst(void* p, u32x4 v) {
+#if EP_DSP_NTSTORE
+    st16_stream(p, v);
+#else
+    st16(p, v);
+#endif
+}
 
 struct DispatchArgs {
     int T, H, K, E;
@@ -51,7 +86,7 @@ __device__ __forceinline__ void fan_out_row(const uint8_t* src, int64_t row_byte
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int i = base + j * kWave + lane;
-            if (i < nvec) v[j] = ld16(src + (int64_t)i * 16);
+            if (i < nvec) v[j] = ld_src(src + (int64_t)i * 16);
         }
         for (uint64_t m = dest; m; m &= m - 1) {
             const int k = __ffsll((unsigned long long)m) - 1;
@@ -59,16 +94,16 @@ __device__ __forceinline__ void fan_out_row(const uint8_t* src, int64_t row_byte
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const int i = base + j * kWave + lane;
-                if (i < nvec) st16_stream(row + (int64_t)i * 16, v[j]);
+                if (i < nvec) st_dst(row + (int64_t)i * 16, v[j]);
             }
         }
     }
 }
 
 template <int NV>
-__global__ __launch_bounds__(kBlockThreads) void dispatch_kernel(DispatchArgs a) {
+__global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(DispatchArgs a) {
     const int lane = lane_id();
-    const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int t = blockIdx.x * kDspWaves + wave_in_block();
     if (t >= a.T) return;
 
     // Lanes 0..K-1 hold this token's slots; a lane is a destination if its
@@ -141,7 +176,7 @@ hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_token
     a.rw = rv.topk_weights;
     a.cap = rv.capacity;
     a.err = reinterpret_cast<uint32_t*>(ws + W.err);
-    const dim3 grid((s.T + kWavesPerBlock - 1) / kWavesPerBlock), block(kBlockThreads);
+    const dim3 grid((s.T + kDspWaves - 1) / kDspWaves), block(kDspThreads);
     // Vectors per lane held in registers: enough for the widest present row.
     const int64_t widest = tk.x ? 2 * (int64_t)s.H : (int64_t)s.H;
     const int64_t per_lane = (widest / 16 + kWave - 1) / kWave;
@@ -149,9 +184,9 @@ hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_token
         hipLaunchKernelGGL(dispatch_kernel<1>, grid, block, 0, st, a);
     else if (per_lane <= 2)
         hipLaunchKernelGGL(dispatch_kernel<2>, grid, block, 0, st, a);
-    else if (per_lane <= 4)
+    else if (per_lane <= 4 || EP_DSP_NVMAX <= 4)
         hipLaunchKernelGGL(dispatch_kernel<4>, grid, block, 0, st, a);
-    else if (per_lane <= 8)
+    else if (per_lane <= 8 || EP_DSP_NVMAX <= 8)
         hipLaunchKernelGGL(dispatch_kernel<8>, grid, block, 0, st, a);
     else
         hipLaunchKernelGGL(dispatch_kernel<16>, grid, block, 0, st, a);

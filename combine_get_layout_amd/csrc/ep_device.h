@@ -35,6 +35,10 @@ __device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Streaming load: rows read exactly once by the kernel.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 __device__ __forceinline__ int readlane(int v, int lane) {
     return __builtin_amdgcn_readlane(v, lane);

@@ -20,9 +20,7 @@ struct WsLayout {
     size_t part_rank;       // int32 [nb][R]  per-block counts -> block-exclusive prefix
     size_t part_group;      // int32 [nb][G]
     size_t part_expert;     // int32 [nb][E]
-    size_t tot_rank;        // int32 [R]
-    size_t tot_group;       // int32 [G]
-    size_t tot_expert;      // int32 [E]
+    size_t part_lanes;      // int32 [nb][R]  valid lanes per rank
     size_t total;
 };
 WsLayout ws_layout(const ep_shape& s);
