@@ -11,9 +11,9 @@
 // combine_token_buffer[topk slot][token]).
 //
 // CDNA4 mapping: one wave64 per output token. A lane owns 16-byte vectors (8
-// bf16) of the hidden row. All distinct source rows of a group of NB vectors
-// are loaded before any arithmetic (K x NB loads in flight per lane), a row
-// shared by two lanes k is loaded once, and the fp32 accumulation runs in
+// bf16) of the hidden row. For a group of NB vectors the K source rows are all
+// requested before any arithmetic (K x NB loads in flight per lane, issued
+// without branches or waits in between), and the fp32 accumulation runs in
 // ascending k with v_fma_f32. Chunked rows (512 B blocks, 480 B payload) are
 // read in place: wave iteration i covers blocks 2i and 2i+1, lane L holds
 // payload vector 30 * (2i + L/32) + L%32 when L%32 < 30; every block that
@@ -90,8 +90,28 @@ __device__ __forceinline__ u32x4 pack8(const float (&acc)[8]) {
     return o;
 }
 
+// Flag check of every distinct usable row over its hidden-carrying blocks, as
+// a pass of its own (used by the any-K path). Returns the usable lanes left.
+__device__ uint64_t check_flags_prepass(const CombineArgs& a, int s, uint64_t um) {
+    const int lane = lane_id();
+    const int nch = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
+    uint64_t keep = um;
+    for (uint64_t m = um; m; m &= m - 1) {
+        const int k = __ffsll((unsigned long long)m) - 1;
+        const int sk = readlane(s, k);
+        const uint8_t* row = a.y + (int64_t)sk * a.stride;
+        bool ok = true;
+        for (int i = lane; i < 2 * nch; i += kWave) {
+            const u32x4 f = ld16(row + (int64_t)(i >> 1) * kChunkBytes + kChunkPayload + (i & 1) * 16);
+            ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
+        }
+        if (__ballot(!ok)) keep &= ~(1ull << k);
+    }
+    return keep;
+}
+
 // KMAX > 0: up to KMAX lanes unrolled with per-lane registers; KMAX == 0:
-// any K, one lane at a time (repeated rows are simply re-read).
+// any K, one lane at a time.
 template <int KMAX, int NB, bool CHUNKED>
 __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_kernel(CombineArgs a) {
     const int lane = lane_id();
@@ -108,36 +128,18 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_kernel(Combi
         report(a.err, EP_DEVERR_CAPACITY);
         use = false;
     }
+    uint64_t um = __ballot(use);
     const int nvh = a.H / 8;
-    if (CHUNKED) {
-        // Flag check of every distinct usable row over its hidden-carrying blocks.
-        const int nch = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
-        const uint64_t um = __ballot(use);
-        for (uint64_t m = um; m; m &= m - 1) {
-            const int k = __ffsll((unsigned long long)m) - 1;
-            const int sk = readlane(s, k);
-            bool dup = false;
-            for (uint64_t q = um & ((1ull << k) - 1); q; q &= q - 1)
-                dup |= readlane(s, __ffsll((unsigned long long)q) - 1) == sk;
-            if (dup) continue;
-            const uint8_t* row = a.y + (int64_t)sk * a.stride;
-            bool ok = true;
-            for (int i = lane; i < 2 * nch; i += kWave) {
-                const u32x4 f = ld16(row + (int64_t)(i >> 1) * kChunkBytes + kChunkPayload + (i & 1) * 16);
-                ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
-            }
-            if (__ballot(!ok)) {
-                if (lane == 0) report(a.err, EP_DEVERR_FLAG);
-                if (s == sk) use = false;
-            }
-        }
-    }
-    const uint64_t um = __ballot(use);
-    const int iters = CHUNKED ? ((2 * a.H + kChunkPayload - 1) / kChunkPayload + 1) / 2
-                              : (nvh + kWave - 1) / kWave;
+    const int nch = (2 * a.H + kChunkPayload - 1) / kChunkPayload;  // hidden-carrying blocks
+    const int iters = CHUNKED ? (nch + 1) / 2 : (nvh + kWave - 1) / kWave;
     uint8_t* out_row = reinterpret_cast<uint8_t*>(a.out) + (int64_t)t * a.H * 2;
 
     if constexpr (KMAX == 0) {
+        if (CHUNKED) {
+            const uint64_t keep = check_flags_prepass(a, s, um);
+            if (keep != um && lane == 0) report(a.err, EP_DEVERR_FLAG);
+            um = keep;
+        }
         for (int it = 0; it < iters; ++it) {
             int p;
             int64_t off;
@@ -152,52 +154,83 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_kernel(Combi
             if (valid) st16_stream(out_row + (int64_t)p * 16, pack8(acc));
         }
     } else {
-        int sk[KMAX], src[KMAX];
+        // One uniform row pointer per lane k. Lanes that do not contribute
+        // point at a usable row (so every load is in bounds and can be issued
+        // unconditionally) and are masked out of the sum; a row shared by two
+        // lanes is simply requested twice (the second request is served by
+        // the cache), which keeps the load phase free of branches.
+        // Chunked rows: the lanes that sit on a block's 32-byte flag (L % 32
+        // >= 30) load that flag with the same instruction and check it. A row
+        // with a bad flag is found only after its values were used, so the
+        // token is then computed again without it (an error path only).
         float wk[KMAX];
-        bool uk[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            uk[k] = k < a.K && ((um >> k) & 1);
-            sk[k] = k < a.K ? readlane(s, k) : -1;
-            wk[k] = k < a.K ? readlane_f(wt, k) : 0.f;
-            src[k] = k;
-#pragma unroll
-            for (int j = KMAX - 1; j >= 0; --j)
-                if (j < k && uk[j] && uk[k] && sk[j] == sk[k]) src[k] = j;
-        }
-        for (int it0 = 0; it0 < iters; it0 += NB) {
-            u32x4 v[KMAX][NB];
-            int p[NB];
-            int64_t off[NB];
-            bool valid[NB];
-#pragma unroll
-            for (int j = 0; j < NB; ++j) valid[j] = it0 + j < iters && lane_vector<CHUNKED>(it0 + j, lane, nvh, p[j], off[j]);
+        const uint8_t* rowp[KMAX];
+        for (int pass = 0; pass < 2; ++pass) {
+            if (!um) {
+                for (int it = 0; it < iters; ++it) {
+                    int p;
+                    int64_t off;
+                    if (lane_vector<CHUNKED>(it, lane, nvh, p, off))
+                        st16_stream(out_row + (int64_t)p * 16, u32x4{0u, 0u, 0u, 0u});
+                }
+                return;
+            }
+            const int s_any = readlane(s, __ffsll((unsigned long long)um) - 1);
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
-                if (!uk[k] || src[k] != k) continue;
-                const uint8_t* row = a.y + (int64_t)sk[k] * a.stride;
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    if (valid[j]) v[k][j] = ld_row(row + off[j]);
+                const int kk = min(k, a.K - 1);
+                const int sk = readlane(s, kk);
+                rowp[k] = a.y + (int64_t)(((um >> k) & 1) ? sk : s_any) * a.stride;
+                wk[k] = readlane_f(wt, kk);
             }
+            uint32_t bad = 0;  // per lane: bit k = a flag of row k checked by this lane is wrong
+            for (int it0 = 0; it0 < iters; it0 += NB) {
+                int p[NB];
+                int64_t off[NB];
+                bool valid[NB], flag[NB];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int k = 0; k < KMAX; ++k) {
-                    if (!uk[k]) continue;
-                    u32x4 val;
-                    if (src[k] == k) {
-                        val = v[k][j];
-                    } else {
-#pragma unroll
-                        for (int m = 0; m < KMAX; ++m)
-                            if (m < k && src[k] == m) val = v[m][j];
-                    }
-                    fma8(acc, wk[k], val);
+                for (int j = 0; j < NB; ++j) {
+                    const bool in = it0 + j < iters;
+                    valid[j] = in && lane_vector<CHUNKED>(it0 + j, lane, nvh, p[j], off[j]);
+                    flag[j] = CHUNKED && in && (lane & 31) >= kChunkPayloadVecs &&
+                              2 * (it0 + j) + (lane >> 5) < nch;
+                    if (!valid[j] && !flag[j]) off[j] = 0;
                 }
-                if (valid[j]) st16_stream(out_row + (int64_t)p[j] * 16, pack8(acc));
+                u32x4 v[KMAX][NB];
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) v[k][j] = ld_row(rowp[k] + off[j]);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    if (CHUNKED) {
+#pragma unroll
+                        for (int k = 0; k < KMAX; ++k) {
+                            const u32x4 f = v[k][j];
+                            const bool ok = f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch &&
+                                            f[3] == a.epoch;
+                            bad |= (flag[j] && !ok) ? (1u << k) : 0u;
+                        }
+                    }
+                    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k = 0; k < KMAX; ++k)
+                        if ((um >> k) & 1) fma8(acc, wk[k], v[k][j]);
+                    if (valid[j]) st16_stream(out_row + (int64_t)p[j] * 16, pack8(acc));
+                }
             }
+            if (!CHUNKED) return;
+            uint64_t drop = 0;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (((um >> k) & 1) && __ballot((bad >> k) & 1)) drop |= 1ull << k;
+            if (!drop) return;
+            if (lane == 0) report(a.err, EP_DEVERR_FLAG);
+            // Every lane reading a dropped row drops with it.
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if ((drop >> k) & 1) drop |= __ballot(use && s == readlane(s, min(k, a.K - 1)));
+            um &= ~drop;
         }
     }
 }

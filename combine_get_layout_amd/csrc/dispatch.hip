@@ -34,6 +34,9 @@
 #ifndef EP_DSP_MINB
 #define EP_DSP_MINB 1       // minimum resident workgroups per CU (launch bound)
 #endif
+#ifndef EP_DSP_SPLIT
+#define EP_DSP_SPLIT 4      // waves per token: the row is cut into this many column slices
+#endif
 
 namespace ep {
 namespace {
@@ -78,10 +81,13 @@ struct DispatchArgs {
 // dst + slot_k * row_bytes of every destination lane k in `dest`.
 template <int NV>
 __device__ __forceinline__ void fan_out_row(const uint8_t* src, int64_t row_bytes, uint8_t* dst,
-                                            uint64_t dest, int slot) {
+                                            uint64_t dest, int slot, int part) {
     const int lane = lane_id();
-    const int nvec = (int)(row_bytes / 16);
-    for (int base = 0; base < nvec; base += kWave * NV) {
+    const int nvec_all = (int)(row_bytes / 16);
+    const int per = (nvec_all + EP_DSP_SPLIT - 1) / EP_DSP_SPLIT;
+    const int v0 = min(nvec_all, part * per);
+    const int nvec = min(nvec_all, v0 + per);
+    for (int base = v0; base < nvec; base += kWave * NV) {
         u32x4 v[NV];
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
@@ -103,7 +109,8 @@ __device__ __forceinline__ void fan_out_row(const uint8_t* src, int64_t row_byte
 template <int NV>
 __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(DispatchArgs a) {
     const int lane = lane_id();
-    const int t = blockIdx.x * kDspWaves + wave_in_block();
+    const int gw = blockIdx.x * kDspWaves + wave_in_block();
+    const int t = gw / EP_DSP_SPLIT, part = gw % EP_DSP_SPLIT;
     if (t >= a.T) return;
 
     // Lanes 0..K-1 hold this token's slots; a lane is a destination if its
@@ -122,14 +129,15 @@ __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(Disp
         if (j < lane && sj == s) first = false;
     }
     const bool over = first && s >= a.cap;
-    if (over) report(a.err, EP_DEVERR_CAPACITY);
+    if (over && part == 0) report(a.err, EP_DEVERR_CAPACITY);
     const uint64_t dest = __ballot(first && !over);
     if (!dest) return;
 
     if (a.x && a.rx)
-        fan_out_row<NV>(a.x + (int64_t)t * a.H * 2, (int64_t)a.H * 2, a.rx, dest, s);
+        fan_out_row<NV>(a.x + (int64_t)t * a.H * 2, (int64_t)a.H * 2, a.rx, dest, s, part);
     if (a.x_fp8 && a.rfp8)
-        fan_out_row<NV>(a.x_fp8 + (int64_t)t * a.H, a.H, a.rfp8, dest, s);
+        fan_out_row<NV>(a.x_fp8 + (int64_t)t * a.H, a.H, a.rfp8, dest, s, part);
+    if (part != 0) return;  // scales and metadata: written once per row
     if (a.x_scales && a.rscales) {
         const int ns = a.H / 128;
         for (int base = 0; base < ns; base += kWave) {
@@ -176,10 +184,12 @@ hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_token
     a.rw = rv.topk_weights;
     a.cap = rv.capacity;
     a.err = reinterpret_cast<uint32_t*>(ws + W.err);
-    const dim3 grid((s.T + kDspWaves - 1) / kDspWaves), block(kDspThreads);
-    // Vectors per lane held in registers: enough for the widest present row.
+    const int64_t waves = (int64_t)s.T * EP_DSP_SPLIT;
+    const dim3 grid((unsigned)((waves + kDspWaves - 1) / kDspWaves)), block(kDspThreads);
+    // Vectors per lane held in registers: enough for the widest present slice.
     const int64_t widest = tk.x ? 2 * (int64_t)s.H : (int64_t)s.H;
-    const int64_t per_lane = (widest / 16 + kWave - 1) / kWave;
+    const int64_t slice = (widest / 16 + EP_DSP_SPLIT - 1) / EP_DSP_SPLIT;
+    const int64_t per_lane = (slice + kWave - 1) / kWave;
     if (per_lane <= 1)
         hipLaunchKernelGGL(dispatch_kernel<1>, grid, block, 0, st, a);
     else if (per_lane <= 2)

@@ -48,11 +48,10 @@ struct HierArgs {
     uint32_t* err;
 };
 
-// Record vector q of token t (16 bytes), zero past the end of the record.
-__device__ __forceinline__ u32x4 record_vector(const HierArgs& a, int t, int q) {
+// Record vector q >= q_scales of token t (16 bytes): scales, expert ids,
+// weights, source index, or zero past the end of the record.
+__device__ __forceinline__ u32x4 meta_vector(const HierArgs& a, int t, int q) {
     const RecordGeom& g = a.geom;
-    if (q < g.q_fp8) return ld16(a.x + (int64_t)t * a.H * 2 + (int64_t)q * 16);
-    if (q < g.q_scales) return ld16(a.x_fp8 + (int64_t)t * a.H + (int64_t)(q - g.q_fp8) * 16);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (q < g.q_idx) {
         const int ns = a.H / 128;
@@ -111,14 +110,32 @@ __global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
     const int64_t stride = a.geom.stride;
     const u32x4 flag = {a.epoch, a.epoch, a.epoch, a.epoch};
     const int c_half = lane >> 5, w = lane & 31;
+    const int q_fp8 = a.geom.q_fp8, q_meta = a.geom.q_scales;
+    const uint8_t* x_row = a.x + (int64_t)t * a.H * 2;
+    const uint8_t* f_row = a.x_fp8 ? a.x_fp8 + (int64_t)t * a.H : x_row;
     for (int it0 = 0; it0 < iters; it0 += kPieceIters) {
         u32x4 v[kPieceIters];
+        // 1. Hidden vectors (bf16, then fp8): one unconditional load per
+        //    iteration; lanes holding anything else load the row's first
+        //    vector (in bounds, cached) and are overwritten below.
 #pragma unroll
         for (int j = 0; j < kPieceIters; ++j) {
-            const int c = 2 * (it0 + j) + c_half;
-            if (it0 + j < iters && c < nchunks)
-                v[j] = w < kChunkPayloadVecs ? record_vector(a, t, c * kChunkPayloadVecs + w) : flag;
+            const int q = (2 * (it0 + j) + c_half) * kChunkPayloadVecs + w;
+            const uint8_t* src = q < q_fp8 ? x_row + (int64_t)q * 16
+                                 : (q < q_meta ? f_row + (int64_t)(q - q_fp8) * 16 : x_row);
+            v[j] = ld16(src);
         }
+        // 2. Metadata and padding: only in the iterations that reach them.
+#pragma unroll
+        for (int j = 0; j < kPieceIters; ++j) {
+            const int q = (2 * (it0 + j) + c_half) * kChunkPayloadVecs + w;
+            const int q_last = (2 * (it0 + j) + 2) * kChunkPayloadVecs - 1;  // wave-uniform
+            if (q_last >= q_meta && w < kChunkPayloadVecs && q >= q_meta) v[j] = meta_vector(a, t, q);
+        }
+        // 3. Flags.
+#pragma unroll
+        for (int j = 0; j < kPieceIters; ++j)
+            if (w >= kChunkPayloadVecs) v[j] = flag;
         for (uint64_t m = dest; m; m &= m - 1) {
             const int k = __ffsll((unsigned long long)m) - 1;
             uint8_t* row = a.group_buf + (int64_t)readlane(gs, k) * stride;
@@ -149,12 +166,26 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
     const int64_t stride = a.geom.stride;
     const int64_t off_idx = (int64_t)a.geom.q_idx * 16;
     const int64_t off_src = (int64_t)a.geom.q_src * 16;
-    const int c_half = lane >> 5, w = lane & 31;
+    const int c_half = lane >> 5, wv = lane & 31;
     const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerBlock;
+    const bool one_piece = iters <= kPieceIters;
 
     for (int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); n < n_rows;
          n += wave_stride) {
         const uint8_t* src_row = a.group_buf + n * stride;
+        // Issued together: the whole record (its flag lanes load the flags),
+        // the source index and this lane's expert id.
+        u32x4 v[kPieceIters];
+        if (one_piece) {
+#pragma unroll
+            for (int j = 0; j < kPieceIters; ++j) {
+                const int c = min(2 * j + c_half, nchunks - 1);
+                v[j] = ld16(src_row + (int64_t)c * kChunkBytes + (int64_t)wv * 16);
+            }
+        }
+        const int32_t src = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_src));
+        const int32_t id = *reinterpret_cast<const int32_t*>(
+            record_byte(src_row, off_idx + 4 * min(lane, a.K - 1)));
         // The row's group: the number of groups g >= 1 whose region starts at
         // or before n (empty groups have equal starts).
         int g = 0;
@@ -164,23 +195,28 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
         }
         // Every block's flag must equal epoch.
         bool ok = true;
-        for (int i = lane; i < 2 * nchunks; i += kWave) {
-            const u32x4 f = ld16(src_row + (int64_t)(i >> 1) * kChunkBytes + kChunkPayload + (i & 1) * 16);
-            ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
+        if (one_piece) {
+#pragma unroll
+            for (int j = 0; j < kPieceIters; ++j) {
+                const bool is_flag = wv >= kChunkPayloadVecs && j < iters && 2 * j + c_half < nchunks;
+                const u32x4 f = v[j];
+                ok &= !is_flag || (f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch);
+            }
+        } else {
+            for (int i = lane; i < 2 * nchunks; i += kWave) {
+                const u32x4 f = ld16(src_row + (int64_t)(i >> 1) * kChunkBytes + kChunkPayload + (i & 1) * 16);
+                ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
+            }
         }
-        int32_t src = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_src));
         if (__ballot(!ok) || src < 0 || src >= a.T) {
             if (lane == 0) report(a.err, EP_DEVERR_FLAG);
             continue;
         }
         // Destination peers: first lane of each distinct rank inside group g.
         int32_t r = -1, d = -1;
-        if (lane < a.K) {
-            const int32_t id = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_idx + 4 * lane));
-            if (id >= 0 && id < a.E && (id / a.epr) / a.P == g) {
-                r = id / a.epr;
-                d = a.slot[(int64_t)src * a.K + lane];
-            }
+        if (lane < a.K && id >= 0 && id < a.E && (id / a.epr) / a.P == g) {
+            r = id / a.epr;
+            d = a.slot[(int64_t)src * a.K + lane];
         }
         bool first = r >= 0 && d >= 0;
         for (int j = 0; j < a.K; ++j) {
@@ -193,11 +229,12 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
         if (!dest) continue;
 
         for (int it0 = 0; it0 < iters; it0 += kPieceIters) {
-            u32x4 v[kPieceIters];
+            if (!one_piece) {
 #pragma unroll
-            for (int j = 0; j < kPieceIters; ++j) {
-                const int c = 2 * (it0 + j) + c_half;
-                if (it0 + j < iters && c < nchunks) v[j] = ld16(src_row + chunk_lane_offset(it0 + j, lane));
+                for (int j = 0; j < kPieceIters; ++j) {
+                    const int c = 2 * (it0 + j) + c_half;
+                    if (it0 + j < iters && c < nchunks) v[j] = ld16(src_row + chunk_lane_offset(it0 + j, lane));
+                }
             }
             for (uint64_t m = dest; m; m &= m - 1) {
                 const int k = __ffsll((unsigned long long)m) - 1;
@@ -210,7 +247,6 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
                 }
             }
         }
-        (void)w;
     }
 }
 
