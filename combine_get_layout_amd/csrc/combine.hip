@@ -32,7 +32,10 @@
 #define EP_CMB_MINB 1       // minimum resident workgroups per CU (launch bound)
 #endif
 #ifndef EP_CMB_WPB
-#define EP_CMB_WPB 4        // waves (tokens) per workgroup
+#define EP_CMB_WPB 4        // waves per workgroup
+#endif
+#ifndef EP_CMB_ROWS
+#define EP_CMB_ROWS 1       // row-streaming kernel: 1 = plain rows, 2 = plain and chunked rows
 #endif
 
 namespace ep {
@@ -235,9 +238,138 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_kernel(Combi
     }
 }
 
+// Row-streaming variant: a token is cut into slices of VPW wave-iterations,
+// one wave per slice. For each lane k in ascending order the wave reads its
+// slice of row k as one burst of VPW 16-byte vectors per lane (the next row's
+// burst is requested before the current one is used) and accumulates it into
+// VPW x 8 fp32 registers. Same sums in the same order as combine_kernel.
+template <int KMAX, int VPW, bool CHUNKED>
+__global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(CombineArgs a, int slices) {
+    const int lane = lane_id();
+    const int gw = blockIdx.x * kCmbWaves + wave_in_block();
+    const int t = gw / slices, part = gw % slices;
+    if (t >= a.T) return;
+    int s = -1;
+    float wt = 0.f;
+    if (lane < a.K) {
+        s = a.slot[(int64_t)t * a.K + lane];
+        wt = a.w[(int64_t)t * a.K + lane];
+    }
+    bool use = s >= 0;
+    if (use && s >= a.y_rows) {
+        if (part == 0) report(a.err, EP_DEVERR_CAPACITY);
+        use = false;
+    }
+    uint64_t um = __ballot(use);
+    const int nvh = a.H / 8;
+    const int nch = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
+    const int iters = CHUNKED ? (nch + 1) / 2 : (nvh + kWave - 1) / kWave;
+    const int it0 = part * VPW;
+    uint8_t* out_row = reinterpret_cast<uint8_t*>(a.out) + (int64_t)t * a.H * 2;
+    int p[VPW];
+    int64_t off[VPW];
+    bool valid[VPW], flag[VPW];
+#pragma unroll
+    for (int j = 0; j < VPW; ++j) {
+        const bool in = it0 + j < iters;
+        valid[j] = in && lane_vector<CHUNKED>(it0 + j, lane, nvh, p[j], off[j]);
+        flag[j] = CHUNKED && in && (lane & 31) >= kChunkPayloadVecs && 2 * (it0 + j) + (lane >> 5) < nch;
+        if (!valid[j] && !flag[j]) off[j] = 0;
+    }
+    for (int pass = 0; pass < 2; ++pass) {
+        if (!um) {
+#pragma unroll
+            for (int j = 0; j < VPW; ++j)
+                if (valid[j]) st16_stream(out_row + (int64_t)p[j] * 16, u32x4{0u, 0u, 0u, 0u});
+            return;
+        }
+        const int s_any = readlane(s, __ffsll((unsigned long long)um) - 1);
+        float acc[VPW][8];
+#pragma unroll
+        for (int j = 0; j < VPW; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+        uint32_t bad = 0;
+        u32x4 buf[2][VPW];
+        auto row_of = [&](int k) {
+            const int kk = min(k, a.K - 1);
+            return a.y + (int64_t)(((um >> k) & 1) ? readlane(s, kk) : s_any) * a.stride;
+        };
+        {
+            const uint8_t* r0 = row_of(0);
+#pragma unroll
+            for (int j = 0; j < VPW; ++j) buf[0][j] = ld_row(r0 + off[j]);
+        }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k + 1 < KMAX) {
+                const uint8_t* rn = row_of(k + 1);
+#pragma unroll
+                for (int j = 0; j < VPW; ++j) buf[(k + 1) & 1][j] = ld_row(rn + off[j]);
+            }
+            const float wk = readlane_f(wt, min(k, a.K - 1));
+            const bool uk = (um >> k) & 1;
+#pragma unroll
+            for (int j = 0; j < VPW; ++j) {
+                const u32x4 v = buf[k & 1][j];
+                if (CHUNKED) {
+                    const bool ok = v[0] == a.epoch && v[1] == a.epoch && v[2] == a.epoch && v[3] == a.epoch;
+                    bad |= (flag[j] && !ok) ? (1u << k) : 0u;
+                }
+                if (uk) fma8(acc[j], wk, v);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VPW; ++j)
+            if (valid[j]) st16_stream(out_row + (int64_t)p[j] * 16, pack8(acc[j]));
+        if (!CHUNKED) return;
+        // A bad flag anywhere in a row drops the row for the whole token: the
+        // slices compare notes through the shared row flags, so every slice
+        // checks all flags of the rows it uses (see below) before finishing.
+        uint64_t drop = 0;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (((um >> k) & 1) && __ballot((bad >> k) & 1)) drop |= 1ull << k;
+        // Flags outside this slice: checked here so that all slices agree.
+        for (uint64_t m = um & ~drop; m; m &= m - 1) {
+            const int k = __ffsll((unsigned long long)m) - 1;
+            const uint8_t* row = a.y + (int64_t)readlane(s, k) * a.stride;
+            bool ok = true;
+            for (int i = lane; i < 2 * nch; i += kWave) {
+                const int c = i >> 1;
+                if (c >= 2 * it0 && c < 2 * (it0 + VPW)) continue;  // already checked in-slice
+                const u32x4 f = ld16(row + (int64_t)c * kChunkBytes + kChunkPayload + (i & 1) * 16);
+                ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
+            }
+            if (__ballot(!ok)) drop |= 1ull << k;
+        }
+        if (!drop) return;
+        if (lane == 0 && part == 0) report(a.err, EP_DEVERR_FLAG);
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if ((drop >> k) & 1) drop |= __ballot(use && s == readlane(s, min(k, a.K - 1)));
+        um &= ~drop;
+    }
+}
+
 template <bool CHUNKED>
 hipError_t launch_k(const CombineArgs& a, hipStream_t st) {
-    const dim3 grid((a.T + kCmbWaves - 1) / kCmbWaves), block(kCmbThreads);
+    const dim3 block(kCmbThreads);
+#if EP_CMB_ROWS
+    if (a.K <= 8 && (!CHUNKED || EP_CMB_ROWS >= 2)) {
+        const int nch = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
+        const int iters = CHUNKED ? (nch + 1) / 2 : (a.H / 8 + kWave - 1) / kWave;
+        const int vpw = iters > 8 ? 8 : 4;
+        const int slices = (iters + vpw - 1) / vpw;
+        const dim3 grid((unsigned)(((int64_t)a.T * slices + kCmbWaves - 1) / kCmbWaves));
+        if (vpw == 8)
+            hipLaunchKernelGGL((combine_rows_kernel<8, 8, CHUNKED>), grid, block, 0, st, a, slices);
+        else
+            hipLaunchKernelGGL((combine_rows_kernel<8, 4, CHUNKED>), grid, block, 0, st, a, slices);
+        return hipGetLastError();
+    }
+#endif
+    const dim3 grid((a.T + kCmbWaves - 1) / kCmbWaves);
     if (a.K <= 2)
         hipLaunchKernelGGL((combine_kernel<2, 8, CHUNKED>), grid, block, 0, st, a);
     else if (a.K <= 4)
