@@ -71,6 +71,8 @@ def _load():
         lib.oracle_unpack_rows.restype = i64
         lib.oracle_combine.argtypes = [i32, i32, i32, P, P, P, i64, i64, i32, u32, P, P]
         lib.oracle_combine.restype = None
+        lib.oracle_expert_slots.argtypes = [i32, i32, i32, P, P, P]
+        lib.oracle_expert_slots.restype = i32
         lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
         lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
@@ -121,6 +123,48 @@ def layout(topk_idx: np.ndarray, E: int, R: int, G: int = 1) -> dict:
     if rc != 0:
         raise ValueError("oracle_layout: bad shape")
     out["err"] = int(err[0])
+    return out
+
+
+def expert_slots(topk_idx, E, expert_offsets) -> np.ndarray:
+    """Expand-mode row of every (token, lane): [T, K] int32, -1 if skipped."""
+    topk_idx = _c(topk_idx, np.int64)
+    T, K = topk_idx.shape
+    expert_offsets = _c(expert_offsets, np.int32)
+    out = np.zeros((T, K), np.int32)
+    if _load().oracle_expert_slots(T, K, E, _p(topk_idx), _p(expert_offsets), _p(out)) != 0:
+        raise MemoryError("oracle_expert_slots")
+    return out
+
+
+def dispatch_rows(topk_idx, E, rows, n_rows, x=None, x_fp8=None, x_scales=None, topk_w=None):
+    """Receive buffers when the token of each (t, k) with rows[t, k] >= 0 is
+    written to row rows[t, k] (expand mode: one row per lane). Written from
+    the definition with numpy indexing, as the record is the same as in
+    direct dispatch."""
+    topk_idx = _c(topk_idx, np.int64)
+    T, K = topk_idx.shape
+    rows = np.asarray(rows)
+    tt, kk = np.nonzero(rows >= 0)
+    dst = rows[tt, kk]
+    clean = np.where((topk_idx >= 0) & (topk_idx < E), topk_idx, -1).astype(np.int32)
+    out = {}
+    if x is not None:
+        out["recv_x"] = np.zeros((n_rows, x.shape[1]), np.uint16)
+        out["recv_x"][dst] = x[tt]
+    if x_fp8 is not None:
+        out["recv_fp8"] = np.zeros((n_rows, x_fp8.shape[1]), np.uint8)
+        out["recv_fp8"][dst] = x_fp8[tt]
+    if x_scales is not None:
+        out["recv_scales"] = np.zeros((n_rows, x_scales.shape[1]), np.float32)
+        out["recv_scales"][dst] = x_scales[tt]
+    out["recv_src"] = np.full(n_rows, -7, np.int32)
+    out["recv_src"][dst] = tt
+    out["recv_topk_idx"] = np.full((n_rows, K), -7, np.int32)
+    out["recv_topk_idx"][dst] = clean[tt]
+    if topk_w is not None:
+        out["recv_topk_w"] = np.zeros((n_rows, K), np.float32)
+        out["recv_topk_w"][dst] = topk_w[tt]
     return out
 
 

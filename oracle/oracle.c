@@ -211,6 +211,32 @@ int oracle_layout(int T, int K, int E, int R, int G, const int64_t *topk_idx,
 }
 
 /* ----------------------------------------------------------------------- */
+/* Expand-mode rows ([V2] §3.3 阶段3, copy epilogue with expand: one row    */
+/* per (token, lane), grouped by expert).                                  */
+/* ----------------------------------------------------------------------- */
+
+/* expert_slot[t][k] = row of lane k of token t in the expert-major receive
+ * buffer: expert e's rows start at expert_offsets[e] and follow the lanes
+ * (t, k) that chose e in ascending t, then ascending k (the order one copy
+ * warp walking the received tokens and lanes in order would hand out with
+ * its per-expert atomic counter). -1 for lanes without a valid expert. */
+int oracle_expert_slots(int T, int K, int E, const int64_t *topk_idx,
+                        const int32_t *expert_offsets, int32_t *expert_slot) {
+    int32_t *next = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    if (!next) return -1;
+    for (int e = 0; e < E; e++) next[e] = expert_offsets[e];
+    for (int t = 0; t < T; t++) {
+        for (int k = 0; k < K; k++) {
+            uint32_t dummy = 0;
+            int64_t e = checked_expert(topk_idx[(size_t)t * K + k], E, &dummy);
+            expert_slot[(size_t)t * K + k] = e < 0 ? -1 : next[e]++;
+        }
+    }
+    free(next);
+    return 0;
+}
+
+/* ----------------------------------------------------------------------- */
 /* Direct dispatch ([V2] §3.3 阶段2, §3.5; [PIPE] NVL receivers).          */
 /* ----------------------------------------------------------------------- */
 

@@ -555,3 +555,71 @@ def test_stale_epoch_rejected_by_combine(oracle_lib):
                                   L["group_offsets"], 5, x=inp["x"], topk_w=inp["topk_w"])
     C = oracle_lib.combine(L["slot"], inp["topk_w"], Hd["peer_buf"], w.H, chunked=True, epoch=6)
     assert C["err"] == oracle_lib.ERR_FLAG and (C["out"] == 0).all()
+
+
+# --------------------------------------------------------------------------
+# Expand mode: one row per (token, lane), grouped by expert
+# --------------------------------------------------------------------------
+
+def brute_expert_slots(topk, E):
+    """Rows are the positions of the sorted valid (expert, token, lane) triples."""
+    T, K = topk.shape
+    trip = sorted((int(topk[t, k]), t, k) for t in range(T) for k in range(K) if 0 <= topk[t, k] < E)
+    out = np.full((T, K), -1, np.int64)
+    for i, (_, t, k) in enumerate(trip):
+        out[t, k] = i
+    return out
+
+
+def test_expert_slots_brute_force(oracle_lib):
+    for topk, E, R, G in _tiny_cases():
+        L = oracle_lib.layout(topk, E, R, G)
+        es = oracle_lib.expert_slots(topk, E, L["expert_offsets"])
+        np.testing.assert_array_equal(es, brute_expert_slots(topk, E))
+
+
+@pytest.mark.parametrize("name", ["ep32", "zipf"])
+def test_expert_slots_regions(oracle_lib, name):
+    w = synth.workload(name)
+    inp = synth.make_inputs(w, with_x=False)
+    topk = inp["topk_idx"]
+    L = oracle_lib.layout(topk, w.E, w.R, w.G)
+    es = oracle_lib.expert_slots(topk, w.E, L["expert_offsets"])
+    assert (es >= 0).all() and len(np.unique(es)) == w.T * w.K
+    order = np.argsort(es.ravel())
+    # rows are expert-major, then token, then lane
+    e_sorted = topk.ravel()[order]
+    assert (np.diff(e_sorted) >= 0).all()
+    np.testing.assert_array_equal(np.bincount(e_sorted, minlength=w.E), L["tokens_per_expert"])
+    tk = np.arange(w.T * w.K)[order]
+    same = np.diff(e_sorted) == 0
+    assert (np.diff(tk)[same] > 0).all()
+
+
+def test_expert_slots_equal_rank_slots_with_one_expert_per_rank(oracle_lib):
+    """With one expert per rank and distinct experts per token, a lane's rank
+    row and its expert row coincide."""
+    w = synth.Workload("e_eq_r", 500, 128, 64, 64, 1, 4, "uniform")
+    inp = synth.make_inputs(w, with_x=False)
+    L = oracle_lib.layout(inp["topk_idx"], w.E, w.R)
+    es = oracle_lib.expert_slots(inp["topk_idx"], w.E, L["expert_offsets"])
+    np.testing.assert_array_equal(es, L["slot"])
+
+
+def test_expand_round_trip_equals_rank_combine(oracle_lib):
+    """Identity expert: combining the per-lane rows gives bit for bit what
+    combining the deduplicated per-rank rows gives (same values, same order)."""
+    w = synth.workload("ep32").scaled(300)
+    inp = synth.make_inputs(w)
+    topk = inp["topk_idx"].copy()
+    topk[3, 5] = topk[3, 1]   # repeated expert
+    topk[7, 2] = -1
+    L = oracle_lib.layout(topk, w.E, w.R)
+    es = oracle_lib.expert_slots(topk, w.E, L["expert_offsets"])
+    n_rows = int(L["expert_offsets"][-1])
+    Dx = oracle_lib.dispatch_rows(topk, w.E, es, n_rows, x=inp["x"], topk_w=inp["topk_w"])
+    assert (Dx["recv_src"] >= 0).all()
+    D = oracle_lib.dispatch(topk, w.E, w.R, L["rank_offsets"], x=inp["x"])
+    C1 = oracle_lib.combine(es, inp["topk_w"], Dx["recv_x"], w.H)
+    C2 = oracle_lib.combine(L["slot"], inp["topk_w"], D["recv_x"], w.H)
+    np.testing.assert_array_equal(C1["out"], C2["out"])
