@@ -107,9 +107,10 @@ int ep_get_layout(const ep_shape* shape, const int64_t* topk_idx, const ep_layou
     if (!layout || (shape->T > 0 && !topk_idx) || !aligned(topk_idx, 8)) return EP_ERR_ARG;
     const ep_layout& L = *layout;
     if (!aligned(L.is_token_in_rank, 16) || !aligned(L.is_token_in_group, 16)) return EP_ERR_ARG;
+    if (L.expert_slot && (!L.expert_offsets || shape->K > 16)) return L.expert_offsets ? EP_ERR_UNSUPPORTED : EP_ERR_ARG;
     const void* i32s[] = {L.tokens_per_expert, L.tokens_per_rank, L.tokens_per_group,
                           L.expert_offsets, L.rank_offsets, L.group_offsets, L.slot,
-                          L.group_slot};
+                          L.group_slot, L.expert_slot};
     for (const void* p : i32s)
         if (!aligned(p, 4)) return EP_ERR_ARG;
     return hip_status(launch_layout(*shape, topk_idx, L, static_cast<char*>(ws),
@@ -137,6 +138,14 @@ int ep_dispatch(const ep_shape* shape, const ep_layout* layout, const ep_tokens*
         return EP_ERR_ARG;
     return hip_status(launch_dispatch(*shape, *layout, *tokens, *recv, static_cast<char*>(ws),
                                       static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch_expand(const ep_shape* shape, const ep_layout* layout, const ep_tokens* tokens,
+                       const ep_recv* recv, void* ws, size_t ws_bytes, void* stream) {
+    if (!layout) return EP_ERR_ARG;
+    ep_layout rows = *layout;
+    rows.slot = layout->expert_slot;
+    return ep_dispatch(shape, &rows, tokens, recv, ws, ws_bytes, stream);
 }
 
 int ep_hierarchical_dispatch(const ep_shape* shape, const ep_layout* layout,
@@ -189,6 +198,17 @@ int ep_combine(const ep_shape* shape, const ep_layout* layout, const void* y, in
     return hip_status(launch_combine(*shape, *layout, y, y_rows, y_row_stride, y_format, epoch,
                                      topk_weights, out, static_cast<char*>(ws),
                                      static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine_expand(const ep_shape* shape, const ep_layout* layout, const void* y,
+                      int64_t y_rows, int64_t y_row_stride, int y_format, uint32_t epoch,
+                      const float* topk_weights, uint16_t* out, void* ws, size_t ws_bytes,
+                      void* stream) {
+    if (!layout) return EP_ERR_ARG;
+    ep_layout rows = *layout;
+    rows.slot = layout->expert_slot;
+    return ep_combine(shape, &rows, y, y_rows, y_row_stride, y_format, epoch, topk_weights, out, ws,
+                      ws_bytes, stream);
 }
 
 int ep_clear_errors(void* ws, void* stream) {

@@ -25,6 +25,8 @@
 //               every workgroup already sums. Workgroups never wait for each
 //               other and no grid-wide fence is needed (the launch boundary
 //               orders the two kernels).
+#include <rocprim/block/block_radix_sort.hpp>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -232,6 +234,7 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
         const int cr = min(c, a.R - 1), cg = min(c, a.G - 1);
         const int ce = min(e0 + c, a.E - 1);
         constexpr int kBatch = 16;
+        const bool own_e = c < ne && a.out.expert_slot != nullptr;
         int rb = 0, ra = 0, la = 0, gb = 0, ga = 0, ea = 0;
         for (int b0 = 0; b0 < a.nb; b0 += kBatch) {
             int32_t vr[kBatch], vl[kBatch], vg[kBatch], ve[kBatch];
@@ -251,6 +254,9 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
                 la += in ? vl[j] : 0;
                 gb += early ? vg[j] : 0;
                 ga += in ? vg[j] : 0;
+                // Expand mode: this column becomes the exclusive prefix over
+                // workgroups (each expert column is owned by one workgroup).
+                if (own_e && in) a.part_expert[(int64_t)(b0 + j) * a.E + ce] = ea;
                 ea += in ? ve[j] : 0;
             }
         }
@@ -358,6 +364,57 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
     }
 }
 
+// Expand-mode rows: the (token, lane) entries of a 256-token workgroup are
+// sorted by expert, stably (entries keep token-then-lane order inside an
+// expert), with a block radix sort in LDS. The row of an entry is
+//   expert_offsets[e] + (lanes of e in earlier workgroups) + (position of the
+//   entry among the workgroup's entries of e).
+// The middle term is the count table turned into per-workgroup prefixes by
+// the assign launch.
+template <int ITEMS>
+__global__ __launch_bounds__(kBlockThreads) void layout_expand_kernel(LayoutArgs a, int key_bits) {
+    using sort_t = rocprim::block_radix_sort<int, kBlockThreads, ITEMS, int>;
+    __shared__ union {
+        typename sort_t::storage_type sort;
+        int keys[kBlockThreads * ITEMS];
+    } sh;
+    const int b = blockIdx.x;
+    const int t0 = b * kLayoutTokens;
+    const int t = t0 + threadIdx.x;
+    int keys[ITEMS], vals[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+        int64_t e = -1;
+        if (t < a.T && k < a.K) e = a.topk[(int64_t)t * a.K + k];
+        keys[k] = expert_ok(e, a.E) ? (int)e : a.E;  // no expert: sorted last
+        vals[k] = threadIdx.x * ITEMS + k;
+    }
+    sort_t().sort(keys, vals, sh.sort, 0, key_bits);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) sh.keys[threadIdx.x * ITEMS + j] = keys[j];
+    __syncthreads();
+    const int n = kBlockThreads * ITEMS;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int pos = threadIdx.x * ITEMS + j;
+        const int key = keys[j];
+        const int lt = vals[j] / ITEMS, k = vals[j] % ITEMS;
+        if (k >= a.K || t0 + lt >= a.T) continue;  // padding entry
+        int32_t row = -1;
+        if (key < a.E) {
+            int lo = 0, hi = pos;  // first position holding `key`
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (sh.keys[mid] < key) lo = mid + 1; else hi = mid;
+            }
+            row = a.out.expert_offsets[key] + a.part_expert[(int64_t)b * a.E + key] + (pos - lo);
+        }
+        a.out.expert_slot[(int64_t)(t0 + lt) * a.K + k] = row;
+        (void)n;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout& L, char* ws,
@@ -392,6 +449,14 @@ hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout
     else
         EP_LAYOUT_LAUNCH(0);
 #undef EP_LAYOUT_LAUNCH
+    if (L.expert_slot) {
+        int bits = 1;
+        while ((1 << bits) <= s.E) ++bits;  // keys 0..E
+        if (s.K <= 8)
+            hipLaunchKernelGGL(layout_expand_kernel<8>, grid, block, 0, st, a, bits);
+        else
+            hipLaunchKernelGGL(layout_expand_kernel<16>, grid, block, 0, st, a, bits);
+    }
     return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ class ep_shape(ctypes.Structure):
 
 LAYOUT_FIELDS = ("tokens_per_expert", "tokens_per_rank", "tokens_per_group", "expert_offsets",
                  "rank_offsets", "group_offsets", "is_token_in_rank", "is_token_in_group",
-                 "slot", "group_slot")
+                 "slot", "group_slot", "expert_slot")
 
 
 class ep_layout(ctypes.Structure):
@@ -50,8 +50,8 @@ class ep_recv(ctypes.Structure):
 
 
 EXPORTS = ("ep_workspace_bytes", "ep_record_bytes", "ep_chunked_record_bytes", "ep_get_layout",
-           "ep_dispatch", "ep_hierarchical_dispatch", "ep_combine", "ep_clear_errors",
-           "ep_check_errors", "ep_status_string")
+           "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch", "ep_combine",
+           "ep_combine_expand", "ep_clear_errors", "ep_check_errors", "ep_status_string")
 
 _lib = None
 
@@ -75,15 +75,17 @@ def lib() -> ctypes.CDLL:
     L.ep_chunked_record_bytes.restype = i64
     L.ep_get_layout.argtypes = [sp, _P, lp, _P, sz, _P]
     L.ep_dispatch.argtypes = [sp, lp, ctypes.POINTER(ep_tokens), ctypes.POINTER(ep_recv), _P, sz, _P]
+    L.ep_dispatch_expand.argtypes = L.ep_dispatch.argtypes
     L.ep_hierarchical_dispatch.argtypes = [sp, lp, ctypes.POINTER(ep_tokens), u32, ctypes.c_int,
                                            _P, i64, _P, i64, _P, sz, _P]
     L.ep_combine.argtypes = [sp, lp, _P, i64, i64, ctypes.c_int, u32, _P, _P, _P, sz, _P]
+    L.ep_combine_expand.argtypes = L.ep_combine.argtypes
     L.ep_clear_errors.argtypes = [_P, _P]
     L.ep_check_errors.argtypes = [_P, _P, ctypes.POINTER(u32)]
     L.ep_status_string.argtypes = [ctypes.c_int]
     L.ep_status_string.restype = ctypes.c_char_p
-    for f in ("ep_get_layout", "ep_dispatch", "ep_hierarchical_dispatch", "ep_combine",
-              "ep_clear_errors", "ep_check_errors"):
+    for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch",
+              "ep_combine", "ep_combine_expand", "ep_clear_errors", "ep_check_errors"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -151,6 +153,16 @@ def ep_dispatch(shape, layout: dict, tokens: dict, recv: dict, capacity: int, ws
                              _stream(stream)), "ep_dispatch")
 
 
+def ep_dispatch_expand(shape, layout: dict, tokens: dict, recv: dict, capacity: int, ws, stream=None):
+    L = _layout_struct(layout)
+    tk = _tokens_struct(tokens)
+    rv = ep_recv(*[_ptr(recv.get(n)) for n in ("x", "x_fp8", "x_scales", "src_idx", "topk_idx",
+                                                "topk_weights")], int(capacity))
+    _check(lib().ep_dispatch_expand(ctypes.byref(shape), ctypes.byref(L), ctypes.byref(tk),
+                                    ctypes.byref(rv), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)), "ep_dispatch_expand")
+
+
 def ep_hierarchical_dispatch(shape, layout: dict, tokens: dict, epoch: int, steps: int, group_buf,
                              group_cap: int, peer_buf, peer_cap: int, ws, stream=None):
     L = _layout_struct(layout)
@@ -169,6 +181,16 @@ def ep_combine(shape, layout: dict, y, y_rows: int, y_row_stride: int, y_format:
                             int(y_row_stride), int(y_format), int(epoch), _ptr(topk_weights),
                             _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "ep_combine")
+
+
+def ep_combine_expand(shape, layout: dict, y, y_rows: int, y_row_stride: int, y_format: int,
+                      epoch: int, topk_weights, out, ws, stream=None):
+    L = _layout_struct(layout)
+    _check(lib().ep_combine_expand(ctypes.byref(shape), ctypes.byref(L), _ptr(y), int(y_rows),
+                                   int(y_row_stride), int(y_format), int(epoch),
+                                   _ptr(topk_weights), _ptr(out), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)),
+           "ep_combine_expand")
 
 
 def ep_clear_errors(ws, stream=None):
@@ -196,7 +218,7 @@ def alloc_workspace(shape: ep_shape, device="cuda") -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def alloc_layout(shape: ep_shape, device="cuda", masks=True, groups=True) -> dict:
+def alloc_layout(shape: ep_shape, device="cuda", masks=True, groups=True, expand=False) -> dict:
     i32 = dict(dtype=torch.int32, device=device)
     T, K, E, R, G = shape.T, shape.K, shape.E, shape.R, shape.G
     out = dict(
@@ -214,6 +236,8 @@ def alloc_layout(shape: ep_shape, device="cuda", masks=True, groups=True) -> dic
         out["group_slot"] = torch.empty((T, K), **i32)
         if masks:
             out["is_token_in_group"] = torch.empty((T, G), dtype=torch.uint8, device=device)
+    if expand:
+        out["expert_slot"] = torch.empty((T, K), **i32)
     return out
 
 

@@ -94,6 +94,8 @@ typedef struct ep_layout {
     uint8_t *is_token_in_group;  /* [T*G] 1 if token t sends to group g, else 0 */
     int32_t *slot;               /* [T*K] receive row of (t, rank of lane k); -1 if lane skipped */
     int32_t *group_slot;         /* [T*K] group-region row of (t, group of lane k); -1 if skipped */
+    int32_t *expert_slot;        /* [T*K] expand-mode row of (t, k); -1 if skipped (K <= 16;
+                                    needs expert_offsets) */
 } ep_layout;
 
 /* Send side: per-token payload and routing of the T local tokens ([V2] §3.5). */
@@ -147,6 +149,15 @@ int64_t ep_chunked_record_bytes(const ep_shape *shape, int seg_flags);
 int ep_get_layout(const ep_shape *shape, const int64_t *topk_idx, const ep_layout *layout,
                   void *ws, size_t ws_bytes, void *stream);
 
+/* Expand-mode rows ([V2] §3.3 阶段3: the copy epilogue with expand, where a
+ * received token gets one row per chosen expert, grouped by expert for the
+ * expert GEMMs). When layout->expert_slot is non-NULL, ep_get_layout also
+ * writes expert_slot[t*K+k] = expert_offsets[e] + #{lanes (t', k') before
+ * (t, k) in token-then-lane order with the same expert e}, -1 for skipped
+ * lanes; the rows of expert e are [expert_offsets[e], expert_offsets[e+1]),
+ * expert_offsets[E] rows in all. Requires K <= 16 (EP_ERR_UNSUPPORTED) and
+ * layout->expert_offsets. */
+
 /* Direct dispatch ([V2] §3.3 阶段2 and §3.5; [PIPE] RDMA sender / NVL
  * sender record fields). Each token is read once and its record (present
  * pieces of ep_tokens plus src index, topk ids and weights) is written to
@@ -156,6 +167,12 @@ int ep_get_layout(const ep_shape *shape, const int64_t *topk_idx, const ep_layou
  * recv->capacity are not written and set EP_DEVERR_CAPACITY. */
 int ep_dispatch(const ep_shape *shape, const ep_layout *layout, const ep_tokens *tokens,
                 const ep_recv *recv, void *ws, size_t ws_bytes, void *stream);
+
+/* Expand-mode dispatch: like ep_dispatch, but the token's record goes to the
+ * row layout->expert_slot[t*K+k] of every valid lane k (one row per lane, no
+ * rank deduplication). recv->capacity counts expand rows. */
+int ep_dispatch_expand(const ep_shape *shape, const ep_layout *layout, const ep_tokens *tokens,
+                       const ep_recv *recv, void *ws, size_t ws_bytes, void *stream);
 
 /* Two-level dispatch ([V2] §3.6; [PIPE] hybrid scale-out stage and forward
  * warps) with chunked records ([ASC] data-as-flag 512 B blocks).
@@ -195,6 +212,13 @@ int ep_hierarchical_dispatch(const ep_shape *shape, const ep_layout *layout,
 int ep_combine(const ep_shape *shape, const ep_layout *layout, const void *y, int64_t y_rows,
                int64_t y_row_stride, int y_format, uint32_t epoch, const float *topk_weights,
                uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Expand-mode combine: ep_combine over expand rows, s = layout->expert_slot
+ * instead of layout->slot (each lane has its own row). */
+int ep_combine_expand(const ep_shape *shape, const ep_layout *layout, const void *y,
+                      int64_t y_rows, int64_t y_row_stride, int y_format, uint32_t epoch,
+                      const float *topk_weights, uint16_t *out, void *ws, size_t ws_bytes,
+                      void *stream);
 
 /* Clear the workspace error word (a stream-ordered kernel, no memset node). */
 int ep_clear_errors(void *ws, void *stream);

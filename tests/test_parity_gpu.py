@@ -392,3 +392,95 @@ def test_repeat_calls_identical():
     r2, _, _ = run_dispatch(w, inp, shape, L, ws, tk)
     for k in r1:
         assert torch.equal(r1[k][:N].view(torch.uint8), r2[k][:N].view(torch.uint8)), k
+
+
+# --------------------------------------------------------------------------
+# Expand mode (one row per token and lane, grouped by expert)
+# --------------------------------------------------------------------------
+
+def run_expand(w, inp, fp8=False):
+    topk = inp["topk_idx"]
+    shape = ep.make_shape(topk.shape[0], w.H, topk.shape[1], w.E, w.R, w.G)
+    L = ep.alloc_layout(shape, groups=w.G > 1, expand=True)
+    for t in L.values():
+        poison(t)
+    ws = ep.alloc_workspace(shape)
+    tk = dev(topk)
+    ep.ep_get_layout(shape, tk, L, ws)
+    torch.cuda.synchronize()
+    return shape, L, ws, tk
+
+
+@pytest.mark.parametrize("name", ["tiny", "ep32", "ep256", "zipf", "hier8x8"])
+def test_expand_layout_full_size(name):
+    w = synth.workload(name)
+    inp = synth.make_inputs(w, with_x=False)
+    shape, L, ws, _ = run_expand(w, inp)
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    check_layout(L, O, w.T)
+    es = oracle.expert_slots(inp["topk_idx"], w.E, O["expert_offsets"])
+    np.testing.assert_array_equal(host(L["expert_slot"]), es)
+    assert ep.ep_check_errors(ws) == 0
+
+
+@pytest.mark.parametrize("T,K,E,R", [(0, 8, 64, 8), (1, 1, 4, 2), (300, 3, 12, 6), (777, 16, 64, 16),
+                                     (513, 8, 4096, 1024), (1000, 6, 16, 1)])
+def test_expand_layout_edges(T, K, E, R):
+    w = synth.Workload("edge", T, 128, E, R, 1, K, "uniform")
+    rng = np.random.default_rng(T + K + E)
+    topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
+    if T > 5:
+        topk[5, :] = topk[5, 0]        # the same expert on every lane
+        topk[2, 0] = E + 3             # invalid id
+    shape, L, ws, _ = run_expand(w, dict(topk_idx=topk))
+    O = oracle.layout(topk, E, R, 1)
+    np.testing.assert_array_equal(host(L["expert_slot"]).reshape(T, K),
+                                  oracle.expert_slots(topk, E, O["expert_offsets"]))
+    np.testing.assert_array_equal(host(L["expert_offsets"]), O["expert_offsets"])
+    assert ep.ep_check_errors(ws) == (ep.EP_DEVERR_EXPERT_ID if T > 5 else 0)
+
+
+def test_expand_topk_above_16_rejected():
+    w = synth.Workload("edge", 64, 128, 64, 8, 1, 20, "uniform")
+    topk = np.zeros((64, 20), np.int64)
+    shape = ep.make_shape(64, 128, 20, 64, 8, 1)
+    L = ep.alloc_layout(shape, expand=True)
+    ws = ep.alloc_workspace(shape)
+    with pytest.raises(RuntimeError):
+        ep.ep_get_layout(shape, dev(topk), L, ws)
+
+
+@pytest.mark.parametrize("name,fp8", [("ep32", False), ("ep32", True), ("zipf", False)])
+def test_expand_dispatch_and_combine(name, fp8):
+    w = synth.workload(name)
+    inp = synth.make_inputs(w, with_fp8=fp8)
+    shape, L, ws, tk = run_expand(w, inp)
+    n_rows = int(host(L["expert_offsets"])[-1])
+    assert n_rows == w.T * w.K
+    tokens = dict(x=dev(inp["x"]), topk_idx=tk, topk_weights=dev(inp["topk_w"]))
+    if fp8:
+        tokens["x_fp8"] = dev(inp["x_fp8"])
+        tokens["x_scales"] = dev(inp["x_scales"])
+    recv = ep.alloc_recv(shape, n_rows, fp8=fp8, scales=fp8)
+    for t in recv.values():
+        poison(t)
+    ep.ep_dispatch_expand(shape, L, tokens, recv, n_rows, ws)
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    es = oracle.expert_slots(inp["topk_idx"], w.E, O["expert_offsets"])
+    D = oracle.dispatch_rows(inp["topk_idx"], w.E, es, n_rows, x=inp["x"], x_fp8=inp.get("x_fp8"),
+                             x_scales=inp.get("x_scales"), topk_w=inp["topk_w"])
+    check_dispatch(recv, D, n_rows)
+    # combine of stand-in expert outputs over the expand rows
+    y = synth.random_bf16_rows(n_rows, w.H, seed=77)
+    out = poison(torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda"))
+    ep.ep_combine_expand(shape, L, dev(y), n_rows, 2 * w.H, ep.EP_FMT_PLAIN, 0,
+                         tokens["topk_weights"], out, ws)
+    C = oracle.combine(es, inp["topk_w"], y, w.H)
+    got = host(out)
+    combine_close(got, C["out"])
+    np.testing.assert_array_equal(got, C["out"])
+    # identity expert: round trip back to x
+    ep.ep_combine_expand(shape, L, recv["x"], n_rows, 2 * w.H, ep.EP_FMT_PLAIN, 0,
+                         tokens["topk_weights"], out, ws)
+    combine_close(host(out), inp["x"])
+    assert ep.ep_check_errors(ws) == 0
