@@ -71,6 +71,11 @@ def _load():
         lib.oracle_unpack_rows.restype = i64
         lib.oracle_combine.argtypes = [i32, i32, i32, P, P, P, i64, i64, i32, u32, P, P]
         lib.oracle_combine.restype = None
+        lib.oracle_partial_row_bytes.argtypes = [i32]
+        lib.oracle_partial_row_bytes.restype = i64
+        lib.oracle_combine_two_level.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, i64, i64,
+                                                 i32, u32, P, i64, i32, P, P]
+        lib.oracle_combine_two_level.restype = None
         lib.oracle_expert_slots.argtypes = [i32, i32, i32, P, P, P]
         lib.oracle_expert_slots.restype = i32
         lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -325,6 +330,34 @@ def combine(slot, topk_w, y, H, chunked=False, epoch=0, row_stride=None) -> dict
     _load().oracle_combine(T, H, K, _p(slot), _p(topk_w), _p(y), rows, stride, int(bool(chunked)),
                            int(epoch), _p(out), _p(err))
     return dict(out=out, err=int(err[0]))
+
+
+def partial_row_bytes(H: int) -> int:
+    return int(_load().oracle_partial_row_bytes(int(H)))
+
+
+def combine_two_level(topk_idx, E, R, G, slot, group_slot, topk_w, y, H, group_cap, epoch,
+                      chunked=False, row_stride=None, steps=3, group_buf=None) -> dict:
+    """Two-level combine: partial rows per (token, group) in group_buf (uint8
+    [group_cap, partial stride]) and the final out [T, H] bf16 bits."""
+    topk_idx = _c(topk_idx, np.int64)
+    slot = _c(slot, np.int32)
+    group_slot = _c(group_slot, np.int32)
+    topk_w = _c(topk_w, np.float32)
+    T, K = slot.shape
+    y = np.ascontiguousarray(y)
+    rows = y.shape[0]
+    stride = int(row_stride) if row_stride is not None else (y.nbytes // rows if rows else 2 * H)
+    pstride = partial_row_bytes(H)
+    if group_buf is None:
+        group_buf = np.zeros((int(group_cap), pstride), np.uint8)
+    assert group_buf.shape == (int(group_cap), pstride) and group_buf.flags["C_CONTIGUOUS"]
+    out = np.zeros((T, H), np.uint16)
+    err = np.zeros(1, np.uint32)
+    _load().oracle_combine_two_level(T, H, K, E, R, G, _p(topk_idx), _p(slot), _p(group_slot),
+                                     _p(topk_w), _p(y), rows, stride, int(bool(chunked)), int(epoch),
+                                     _p(group_buf), int(group_cap), int(steps), _p(out), _p(err))
+    return dict(out=out, group_buf=group_buf, err=int(err[0]))
 
 
 def f32_to_bf16(f: float) -> int:

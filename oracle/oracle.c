@@ -565,6 +565,109 @@ void oracle_combine(int T, int H, int K, const int32_t *slot, const float *topk_
     free(use);
 }
 
+/* ----------------------------------------------------------------------- */
+/* Two-level combine: the two-level dispatch run backwards ([PIPE] combine  */
+/* roles kNVLSender -> kNVLAndRDMAForwarder -> kRDMAReceiver on the legacy  */
+/* internode page; [V2] §3.6 hybrid path).                                 */
+/* ----------------------------------------------------------------------- */
+
+/* Byte stride of a partial row: the bf16 hidden row alone, cut into 512 B
+ * blocks of 480 B payload + 32 B flag. */
+int64_t oracle_partial_row_bytes(int H) { return oracle_chunked_bytes(2 * (int64_t)H); }
+
+/* Is lane k of a token usable for combine (valid slot, in range, flags)? */
+static int combine_lane_ok(int32_t s, const uint8_t *y, int64_t y_rows, int64_t row_stride,
+                           int chunked, int64_t hidden_blocks, uint32_t epoch, uint32_t *err) {
+    if (s < 0) return 0;
+    if (s >= y_rows) { *err |= ORC_ERR_CAPACITY; return 0; }
+    if (chunked) {
+        for (int64_t c = 0; c < hidden_blocks; c++)
+            if (!block_flag_ok(y + (int64_t)s * row_stride, c, epoch)) { *err |= ORC_ERR_FLAG; return 0; }
+    }
+    return 1;
+}
+
+/* steps & 1 (intra-group reduce): for every token t and every group g it
+ * sends to, partial[t, g][h] = bf16_rne(acc), acc = +0.0f, then for the
+ * usable lanes k of t whose rank lies in g, in ascending k:
+ * acc = fmaf(w[t][k], y[slot[t][k]][h], acc). The partial is written, as a
+ * chunked row with flags = epoch, to row group_slot[t][k0] of group_buf (k0 =
+ * the first lane of g); rows >= group_cap are not written (error bit 1).
+ * steps & 2 (cross-group reduce): out[t][h] = bf16_rne(acc), acc = +0.0f,
+ * then for the groups g of t in ascending g whose partial row has all flags
+ * == epoch (else error bit 2, skipped): acc = acc + partial[t, g][h].
+ * Lanes of y are usable as in oracle_combine. */
+void oracle_combine_two_level(int T, int H, int K, int E, int R, int G, const int64_t *topk_idx,
+                              const int32_t *slot, const int32_t *group_slot, const float *topk_w,
+                              const uint8_t *y, int64_t y_rows, int64_t row_stride, int chunked,
+                              uint32_t epoch, uint8_t *group_buf, int64_t group_cap, int steps,
+                              uint16_t *out, uint32_t *err) {
+    const int epr = E / R, P = R / G;
+    const int64_t hidden_blocks = (2 * (int64_t)H + ORC_CHUNK_PAYLOAD - 1) / ORC_CHUNK_PAYLOAD;
+    const int64_t pstride = oracle_partial_row_bytes(H);
+    int *use = (int *)malloc(sizeof(int) * (size_t)K);
+    int *grp = (int *)malloc(sizeof(int) * (size_t)K);
+    uint16_t *prow = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H);
+    if (!use || !grp || !prow) { free(use); free(grp); free(prow); return; }
+    for (int t = 0; t < T; t++) {
+        for (int k = 0; k < K; k++) {
+            uint32_t dummy = 0;
+            int64_t e = checked_expert(topk_idx[(size_t)t * K + k], E, &dummy);
+            grp[k] = e < 0 ? -1 : (int)((e / epr) / P);
+        }
+        if (steps & 1) {
+            for (int k = 0; k < K; k++)
+                use[k] = combine_lane_ok(slot[(size_t)t * K + k], y, y_rows, row_stride, chunked,
+                                         hidden_blocks, epoch, err);
+            for (int k0 = 0; k0 < K; k0++) {
+                int g = grp[k0];
+                if (g < 0) continue;
+                int first = 1;
+                for (int j = 0; j < k0; j++)
+                    if (grp[j] == g) first = 0;
+                if (!first) continue;
+                int64_t dst = group_slot[(size_t)t * K + k0];
+                if (dst >= group_cap) { *err |= ORC_ERR_CAPACITY; continue; }
+                for (int h = 0; h < H; h++) {
+                    float acc = 0.0f;
+                    for (int k = 0; k < K; k++) {
+                        if (!use[k] || grp[k] != g) continue;
+                        int32_t s = slot[(size_t)t * K + k];
+                        acc = fmaf(topk_w[(size_t)t * K + k],
+                                   bf16_bits_to_float(y_elem(y, row_stride, chunked, s, h)), acc);
+                    }
+                    prow[h] = float_to_bf16_bits(acc);
+                }
+                oracle_chunk((const uint8_t *)prow, 2 * (int64_t)H, epoch, group_buf + dst * pstride);
+            }
+        }
+        if (steps & 2) {
+            float *acc = (float *)calloc((size_t)H, sizeof(float));
+            if (!acc) break;
+            for (int g = 0; g < G; g++) {
+                int k0 = -1;
+                for (int k = 0; k < K; k++)
+                    if (grp[k] == g) { k0 = k; break; }
+                if (k0 < 0) continue;
+                int64_t row = group_slot[(size_t)t * K + k0];
+                if (row >= group_cap) { *err |= ORC_ERR_CAPACITY; continue; }
+                const uint8_t *pr = group_buf + row * pstride;
+                int ok = 1;
+                for (int64_t c = 0; c < hidden_blocks; c++)
+                    if (!block_flag_ok(pr, c, epoch)) ok = 0;
+                if (!ok) { *err |= ORC_ERR_FLAG; continue; }
+                for (int h = 0; h < H; h++)
+                    acc[h] = acc[h] + bf16_bits_to_float(y_elem(pr, 0, 1, 0, h));
+            }
+            for (int h = 0; h < H; h++) out[(size_t)t * H + h] = float_to_bf16_bits(acc[h]);
+            free(acc);
+        }
+    }
+    free(use);
+    free(grp);
+    free(prow);
+}
+
 /* Exposed for the pin tests of the number helpers. */
 uint16_t oracle_f32_to_bf16(float f) { return float_to_bf16_bits(f); }
 float oracle_bf16_to_f32(uint16_t h) { return bf16_bits_to_float(h); }

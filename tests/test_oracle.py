@@ -623,3 +623,84 @@ def test_expand_round_trip_equals_rank_combine(oracle_lib):
     C1 = oracle_lib.combine(es, inp["topk_w"], Dx["recv_x"], w.H)
     C2 = oracle_lib.combine(L["slot"], inp["topk_w"], D["recv_x"], w.H)
     np.testing.assert_array_equal(C1["out"], C2["out"])
+
+
+# --------------------------------------------------------------------------
+# Two-level combine (intra-group partials, then the cross-group sum)
+# --------------------------------------------------------------------------
+
+def test_two_level_combine_one_group_is_flat_combine(oracle_lib):
+    w = synth.Workload("g1", 200, 256, 32, 8, 1, 4, "uniform")
+    inp = synth.make_inputs(w, seed=21)
+    L = oracle_lib.layout(inp["topk_idx"], w.E, w.R, w.G)
+    N = int(L["rank_offsets"][-1])
+    y = synth.random_bf16_rows(N, w.H, seed=5)
+    C2 = oracle_lib.combine_two_level(inp["topk_idx"], w.E, w.R, w.G, L["slot"], L["group_slot"],
+                                      inp["topk_w"], y, w.H, int(L["group_offsets"][-1]), 3)
+    C1 = oracle_lib.combine(L["slot"], inp["topk_w"], y, w.H)
+    assert C2["err"] == 0
+    np.testing.assert_array_equal(C2["out"], C1["out"])
+
+
+def test_two_level_combine_exact_rational(oracle_lib):
+    """partial[t,g] = bf16(sequential fmas of the group's lanes), out =
+    bf16(sum of the partials in ascending group, fp32 adds), recomputed with
+    exact rationals and torch's bf16 cast."""
+    w = synth.Workload("g4", 12, 40, 16, 8, 4, 5, "uniform")
+    rng = np.random.default_rng(8)
+    topk = rng.integers(-1, w.E, size=(w.T, w.K)).astype(np.int64)
+    topk[0] = -1
+    wts = rng.standard_normal((w.T, w.K)).astype(np.float32)
+    L = oracle_lib.layout(topk, w.E, w.R, w.G)
+    N = int(L["rank_offsets"][-1])
+    y = synth.bf16_bits(rng.standard_normal((max(N, 1), w.H)).astype(np.float32) * 2)
+    C = oracle_lib.combine_two_level(topk, w.E, w.R, w.G, L["slot"], L["group_slot"], wts, y, w.H,
+                                     int(L["group_offsets"][-1]), 7)
+    yf = synth.bf16_to_float(y)
+    epr, P = w.E // w.R, w.R // w.G
+    exp = np.zeros((w.T, w.H), np.float32)
+    for t in range(w.T):
+        groups = sorted({(int(e) // epr) // P for e in topk[t] if e >= 0})
+        for h in range(w.H):
+            total = 0.0
+            for g in groups:
+                acc = 0.0
+                for k in range(w.K):
+                    e = int(topk[t, k])
+                    if e < 0 or (e // epr) // P != g:
+                        continue
+                    acc = round_to_f32(Fraction(float(wts[t, k])) * Fraction(float(yf[L["slot"][t, k], h]))
+                                       + Fraction(acc))
+                part = synth.bf16_to_float(torch_bf16_bits([acc]))[0]
+                total = round_to_f32(Fraction(total) + Fraction(float(part)))
+            exp[t, h] = total
+    np.testing.assert_array_equal(C["out"], torch_bf16_bits(exp))
+    assert (C["out"][0] == 0).all()
+
+
+def test_two_level_combine_round_trip_and_corruption(oracle_lib):
+    w = synth.Workload("hier_small", 400, 512, 64, 16, 4, 6, "uniform")
+    inp = synth.make_inputs(w, seed=22)
+    L = oracle_lib.layout(inp["topk_idx"], w.E, w.R, w.G)
+    Hd = oracle_lib.hier_dispatch(inp["topk_idx"], w.E, w.R, w.G, L["slot"], L["group_offsets"], 4,
+                                  x=inp["x"], topk_w=inp["topk_w"])
+    gcap = int(L["group_offsets"][-1])
+    C = oracle_lib.combine_two_level(inp["topk_idx"], w.E, w.R, w.G, L["slot"], L["group_slot"],
+                                     inp["topk_w"], Hd["peer_buf"], w.H, gcap, 4, chunked=True)
+    assert C["err"] == 0
+    x = synth.bf16_to_float(inp["x"]).astype(np.float64)
+    o = synth.bf16_to_float(C["out"]).astype(np.float64)
+    assert np.abs(o - x).max() <= 2e-2 and np.linalg.norm(o - x) / np.linalg.norm(x) <= 4e-3
+    flat = oracle_lib.combine(L["slot"], inp["topk_w"], Hd["peer_buf"], w.H, chunked=True, epoch=4)
+    f = synth.bf16_to_float(flat["out"]).astype(np.float64)
+    assert np.linalg.norm(o - f) / np.linalg.norm(f) <= 4e-3
+    # a corrupted partial flag drops that (token, group) from the sum
+    gb = C["group_buf"].copy()
+    gb[11, 480 + 3] ^= 1
+    C2 = oracle_lib.combine_two_level(inp["topk_idx"], w.E, w.R, w.G, L["slot"], L["group_slot"],
+                                      inp["topk_w"], Hd["peer_buf"], w.H, gcap, 4, chunked=True,
+                                      steps=2, group_buf=gb)
+    assert C2["err"] == oracle_lib.ERR_FLAG
+    t_bad = int(np.nonzero((L["group_slot"] == 11).any(axis=1))[0][0])
+    diff = np.nonzero((C2["out"] != C["out"]).any(axis=1))[0]
+    assert set(diff.tolist()) <= {t_bad}
