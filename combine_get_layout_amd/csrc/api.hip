@@ -211,6 +211,42 @@ int ep_combine_expand(const ep_shape* shape, const ep_layout* layout, const void
                       ws_bytes, stream);
 }
 
+int64_t ep_partial_row_bytes(const ep_shape* shape) {
+    if (check_shape(shape) != EP_OK) return -1;
+    return (int64_t)kChunkBytes * ((2 * (int64_t)shape->H + kChunkPayload - 1) / kChunkPayload);
+}
+
+int ep_combine_two_level(const ep_shape* shape, const ep_layout* layout, const int64_t* topk_idx,
+                         const void* y, int64_t y_rows, int64_t y_row_stride, int y_format,
+                         uint32_t epoch, const float* topk_weights, void* group_buf,
+                         int64_t group_cap, int steps, uint16_t* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+    int rc = check_shape(shape);
+    if (rc != EP_OK) return rc;
+    if (shape->K > 16) return EP_ERR_UNSUPPORTED;
+    if ((rc = check_ws(shape, ws, ws_bytes)) != EP_OK) return rc;
+    if (!layout || y_rows < 0 || group_cap < 0 || epoch == 0 || steps < 1 || steps > 3) return EP_ERR_ARG;
+    if (y_format != EP_FMT_PLAIN && y_format != EP_FMT_CHUNKED) return EP_ERR_ARG;
+    if (shape->T > 0) {
+        if (!topk_idx || !layout->group_slot || (group_cap > 0 && !group_buf)) return EP_ERR_ARG;
+        if ((steps & 1) && (!layout->slot || !topk_weights || (y_rows > 0 && !y))) return EP_ERR_ARG;
+        if ((steps & 2) && !out) return EP_ERR_ARG;
+    }
+    const int64_t hidden_blocks = (2 * (int64_t)shape->H + kChunkPayload - 1) / kChunkPayload;
+    if ((steps & 1) && y_format == EP_FMT_PLAIN && (y_row_stride % 16 != 0 || y_row_stride < 2 * (int64_t)shape->H))
+        return EP_ERR_ARG;
+    if ((steps & 1) && y_format == EP_FMT_CHUNKED &&
+        (y_row_stride % kChunkBytes != 0 || y_row_stride < hidden_blocks * kChunkBytes))
+        return EP_ERR_ARG;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(group_buf, 16) || !aligned(topk_weights, 4) ||
+        !aligned(topk_idx, 8) || !aligned(layout->slot, 4) || !aligned(layout->group_slot, 4))
+        return EP_ERR_ARG;
+    return hip_status(launch_combine_two_level(*shape, *layout, topk_idx, y, y_rows, y_row_stride,
+                                               y_format, epoch, topk_weights, group_buf, group_cap,
+                                               steps, out, static_cast<char*>(ws),
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int ep_clear_errors(void* ws, void* stream) {
     if (!ws || !aligned(ws, 256)) return EP_ERR_ARG;
     hipLaunchKernelGGL(clear_error_kernel, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream),

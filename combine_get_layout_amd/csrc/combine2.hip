@@ -1,0 +1,286 @@
+// combine2.hip -- ep_combine_two_level on gfx950: the two-level dispatch run
+// backwards.
+//
+// What is computed follows the combine roles of "06_06: NVLink Scale-up +
+// RDMA Scale-out — DeepEP 三阶段流水线 vs DeepGEMM 对称内存" (combine warps
+// kNVLSender -> kNVLAndRDMAForwarder -> kRDMAReceiver: reduce inside the
+// scale-up domain first, then across scale-out groups) on the rows of the
+// hybrid path of "DeepEP V2 深度深潜：统一接口、SM 估算本质与 TopK 复制机制"
+// §3.6:
+//   step 1 (group reduce): for every token t and group g it sends to,
+//     partial[t, g] = bf16_rne(fp32 fused multiply-adds of the lanes of t whose
+//     rank is in g, ascending k, from +0), written as a chunked row (512 B
+//     blocks of 480 B payload + 32 B flag = epoch, "Ascend Send Ordering",
+//     导言) at the token's group-region row;
+//   step 2 (cross-group reduce): out[t] = bf16_rne(fp32 sum of the token's
+//     partial rows in ascending g, from +0); a partial row whose flags are not
+//     all epoch is skipped.
+//
+// CDNA4 mapping: one wave64 per token for both steps. Both use the chunked
+// lane mapping (wave iteration i covers blocks 2i and 2i+1; lane L holds
+// hidden vector 30 * (2i + L/32) + L%32 when L%32 < 30, else a flag vector),
+// so a partial row is produced and consumed with whole-wave 1 KiB stores and
+// loads. Flags of all rows a token reads are checked in one batched pass
+// before the sums.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+struct Combine2Args {
+    int T, H, K, E, R, G, epr, P;
+    const int64_t* topk;
+    const int32_t* slot;
+    const int32_t* group_slot;
+    const float* w;
+    const uint8_t* y;
+    int64_t y_rows, y_stride;
+    int y_chunked;
+    uint32_t epoch;
+    uint8_t* group_buf;
+    int64_t group_cap, pstride;
+    uint16_t* out;
+    uint32_t* err;
+};
+
+// This lane's vector of wave iteration `it` in the chunked mapping: block c,
+// slot wv; p = hidden vector index. Returns whether it is a hidden vector.
+__device__ __forceinline__ bool chunk_vec(int it, int lane, int nvh, int& c, int& wv, int& p) {
+    c = 2 * it + (lane >> 5);
+    wv = lane & 31;
+    p = c * kChunkPayloadVecs + wv;
+    return wv < kChunkPayloadVecs && p < nvh;
+}
+
+__device__ __forceinline__ bool flag_ok(u32x4 f, uint32_t epoch) {
+    return f[0] == epoch && f[1] == epoch && f[2] == epoch && f[3] == epoch;
+}
+
+// Lanes k (bit k) among `cand` whose row (row_of(k)) has a wrong flag in one
+// of its first nblk blocks. All flag loads of all rows are issued together:
+// pair i = (lane k = i / (2 nblk), flag vector i % (2 nblk)).
+template <typename RowOf>
+__device__ uint64_t bad_rows(uint64_t cand, int nblk, uint32_t epoch, RowOf row_of) {
+    const int lane = lane_id();
+    const int per = 2 * nblk;
+    uint64_t bad = 0;
+    const int n = 64 * per;  // every lane index 0..63 (only candidates matter)
+    for (int i0 = 0; i0 < n; i0 += kWave) {
+        const int i = i0 + lane;
+        const int k = i / per, f = i % per;
+        const bool mine = ((cand >> k) & 1) != 0;
+        const uint8_t* row = row_of(k);
+        if (mine) {
+            const u32x4 v = ld16(row + (int64_t)(f >> 1) * kChunkBytes + kChunkPayload + (f & 1) * 16);
+            if (!flag_ok(v, epoch)) bad |= 1ull << k;
+        }
+        // waves whose remaining pairs are past every candidate lane stop early
+        if (!(cand >> min(63, (i0 + kWave) / per))) break;
+    }
+    // combine the per-lane bits
+    uint64_t all = 0;
+    for (uint64_t m = cand; m; m &= m - 1) {
+        const int k = __ffsll((unsigned long long)m) - 1;
+        if (__ballot((bad >> k) & 1)) all |= 1ull << k;
+    }
+    return all;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kBlockThreads) void combine_group_kernel(Combine2Args a) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+    if (t >= a.T) return;
+    int s = -1, g = -1, gs = -1;
+    float wt = 0.f;
+    if (lane < a.K) {
+        const int64_t e = a.topk[(int64_t)t * a.K + lane];
+        s = a.slot[(int64_t)t * a.K + lane];
+        gs = a.group_slot[(int64_t)t * a.K + lane];
+        wt = a.w[(int64_t)t * a.K + lane];
+        if (expert_ok(e, a.E)) g = ((int)e / a.epr) / a.P;
+    }
+    bool use = s >= 0 && g >= 0;
+    if (use && s >= a.y_rows) {
+        report(a.err, EP_DEVERR_CAPACITY);
+        use = false;
+    }
+    uint64_t um = __ballot(use);
+    const int nvh = a.H / 8;
+    const int nblk = (2 * a.H + kChunkPayload - 1) / kChunkPayload;  // blocks of a hidden row
+    const int iters = (nblk + 1) / 2;
+    if (a.y_chunked && um) {
+        const uint64_t bad = bad_rows(um, nblk, a.epoch, [&](int k) {
+            return a.y + (int64_t)__shfl(s, k) * a.y_stride;
+        });
+        if (bad) {
+            if (lane == 0) report(a.err, EP_DEVERR_FLAG);
+            um &= ~bad;
+        }
+    }
+    // Groups of this token: the first lane of each.
+    bool first = g >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int gj = readlane(g, j);
+        if (j < lane && gj == g) first = false;
+    }
+    const u32x4 flagv = {a.epoch, a.epoch, a.epoch, a.epoch};
+    for (uint64_t fm = __ballot(first); fm; fm &= fm - 1) {
+        const int k0 = __ffsll((unsigned long long)fm) - 1;
+        const int g0 = readlane(g, k0);
+        const int64_t dst = readlane(gs, k0);
+        if (dst < 0) continue;
+        if (dst >= a.group_cap) {
+            if (lane == 0) report(a.err, EP_DEVERR_CAPACITY);
+            continue;
+        }
+        const uint64_t gm = um & __ballot(g == g0);
+        uint8_t* prow = a.group_buf + dst * a.pstride;
+        const int s_any = gm ? readlane(s, __ffsll((unsigned long long)gm) - 1) : 0;
+        const uint8_t* rowp[KMAX];
+        float wk[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int kk = min(k, a.K - 1);
+            rowp[k] = a.y + (int64_t)(((gm >> k) & 1) ? readlane(s, kk) : s_any) * a.y_stride;
+            wk[k] = readlane_f(wt, kk);
+        }
+        for (int it = 0; it < iters; ++it) {
+            int c, wv, p;
+            const bool hv = chunk_vec(it, lane, nvh, c, wv, p);
+            const int64_t off = hv ? (a.y_chunked ? (int64_t)c * kChunkBytes + (int64_t)wv * 16 : (int64_t)p * 16) : 0;
+            u32x4 v[KMAX];
+            if (gm) {
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k) v[k] = ld16(rowp[k] + off);
+            }
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (!((gm >> k) & 1)) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = __builtin_fmaf(wk[k], bf16_lo(v[k][q]), acc[2 * q]);
+                    acc[2 * q + 1] = __builtin_fmaf(wk[k], bf16_hi(v[k][q]), acc[2 * q + 1]);
+                }
+            }
+            u32x4 o = {0u, 0u, 0u, 0u};
+            if (hv) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    o[q] = f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16);
+            }
+            if (wv >= kChunkPayloadVecs) o = flagv;
+            if (c < nblk) st16_stream(prow + (int64_t)c * kChunkBytes + (int64_t)wv * 16, o);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void combine_cross_kernel(Combine2Args a) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+    if (t >= a.T) return;
+    int g = -1, gs = -1;
+    if (lane < a.K) {
+        const int64_t e = a.topk[(int64_t)t * a.K + lane];
+        gs = a.group_slot[(int64_t)t * a.K + lane];
+        if (expert_ok(e, a.E)) g = ((int)e / a.epr) / a.P;
+    }
+    bool first = g >= 0 && gs >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int gj = readlane(g, j);
+        if (j < lane && gj == g) first = false;
+    }
+    if (first && gs >= a.group_cap) {
+        report(a.err, EP_DEVERR_CAPACITY);
+        first = false;
+    }
+    uint64_t fm = __ballot(first);
+    const int nvh = a.H / 8;
+    const int nblk = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
+    const int iters = (nblk + 1) / 2;
+    if (fm) {
+        const uint64_t bad = bad_rows(fm, nblk, a.epoch, [&](int k) {
+            return a.group_buf + (int64_t)__shfl(gs, k) * a.pstride;
+        });
+        if (bad) {
+            if (lane == 0) report(a.err, EP_DEVERR_FLAG);
+            fm &= ~bad;
+        }
+    }
+    // Order of the partials: ascending group. rank of a first lane = number
+    // of first lanes with a smaller group.
+    int rank = 0;
+    for (uint64_t m = fm; m; m &= m - 1) {
+        const int j = __ffsll((unsigned long long)m) - 1;
+        rank += readlane(g, j) < g ? 1 : 0;
+    }
+    const int ng = __popcll(fm);
+    uint8_t* out_row = reinterpret_cast<uint8_t*>(a.out) + (int64_t)t * a.H * 2;
+    for (int it = 0; it < iters; ++it) {
+        int c, wv, p;
+        const bool hv = chunk_vec(it, lane, nvh, c, wv, p);
+        const int64_t off = hv ? (int64_t)c * kChunkBytes + (int64_t)wv * 16 : 0;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int pos = 0; pos < ng; ++pos) {
+            const uint64_t who = __ballot(((fm >> lane) & 1) && rank == pos);
+            const int k = __ffsll((unsigned long long)who) - 1;
+            const u32x4 v = ld16(a.group_buf + (int64_t)readlane(gs, k) * a.pstride + off);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = acc[2 * q] + bf16_lo(v[q]);
+                acc[2 * q + 1] = acc[2 * q + 1] + bf16_hi(v[q]);
+            }
+        }
+        if (hv) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16);
+            st16_stream(out_row + (int64_t)p * 16, o);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const int64_t* topk,
+                                    const void* y, int64_t y_rows, int64_t y_stride, int fmt,
+                                    uint32_t epoch, const float* w, void* group_buf,
+                                    int64_t group_cap, int steps, uint16_t* out, char* ws,
+                                    hipStream_t st) {
+    if (s.T == 0) return hipSuccess;
+    const WsLayout W = ws_layout(s);
+    Combine2Args a;
+    a.T = s.T; a.H = s.H; a.K = s.K; a.E = s.E; a.R = s.R; a.G = s.G;
+    a.epr = s.E / s.R; a.P = s.R / s.G;
+    a.topk = topk;
+    a.slot = L.slot;
+    a.group_slot = L.group_slot;
+    a.w = w;
+    a.y = reinterpret_cast<const uint8_t*>(y);
+    a.y_rows = y_rows;
+    a.y_stride = y_stride;
+    a.y_chunked = fmt == EP_FMT_CHUNKED;
+    a.epoch = epoch;
+    a.group_buf = reinterpret_cast<uint8_t*>(group_buf);
+    a.group_cap = group_cap;
+    a.pstride = (int64_t)kChunkBytes * ((2 * (int64_t)s.H + kChunkPayload - 1) / kChunkPayload);
+    a.out = out;
+    a.err = reinterpret_cast<uint32_t*>(ws + W.err);
+    const dim3 grid((s.T + kWavesPerBlock - 1) / kWavesPerBlock), block(kBlockThreads);
+    if (steps & 1) {
+        if (s.K <= 2)
+            hipLaunchKernelGGL(combine_group_kernel<2>, grid, block, 0, st, a);
+        else if (s.K <= 4)
+            hipLaunchKernelGGL(combine_group_kernel<4>, grid, block, 0, st, a);
+        else if (s.K <= 8)
+            hipLaunchKernelGGL(combine_group_kernel<8>, grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL(combine_group_kernel<16>, grid, block, 0, st, a);
+    }
+    if (steps & 2) hipLaunchKernelGGL(combine_cross_kernel, grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace ep

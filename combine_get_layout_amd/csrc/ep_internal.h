@@ -46,6 +46,10 @@ hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& t
 hipError_t launch_combine(const ep_shape& s, const ep_layout& L, const void* y, int64_t y_rows,
                           int64_t y_stride, int fmt, uint32_t epoch, const float* w,
                           uint16_t* out, char* ws, hipStream_t st);
-hipError_t launch_clear_errors(char* ws, hipStream_t st);
+hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const int64_t* topk,
+                                    const void* y, int64_t y_rows, int64_t y_stride, int fmt,
+                                    uint32_t epoch, const float* w, void* group_buf,
+                                    int64_t group_cap, int steps, uint16_t* out, char* ws,
+                                    hipStream_t st);
 
 }  // namespace ep

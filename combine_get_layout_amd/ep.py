@@ -51,7 +51,8 @@ class ep_recv(ctypes.Structure):
 
 EXPORTS = ("ep_workspace_bytes", "ep_record_bytes", "ep_chunked_record_bytes", "ep_get_layout",
            "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch", "ep_combine",
-           "ep_combine_expand", "ep_clear_errors", "ep_check_errors", "ep_status_string")
+           "ep_combine_expand", "ep_partial_row_bytes", "ep_combine_two_level", "ep_clear_errors",
+           "ep_check_errors", "ep_status_string")
 
 _lib = None
 
@@ -80,12 +81,17 @@ def lib() -> ctypes.CDLL:
                                            _P, i64, _P, i64, _P, sz, _P]
     L.ep_combine.argtypes = [sp, lp, _P, i64, i64, ctypes.c_int, u32, _P, _P, _P, sz, _P]
     L.ep_combine_expand.argtypes = L.ep_combine.argtypes
+    L.ep_partial_row_bytes.argtypes = [sp]
+    L.ep_partial_row_bytes.restype = i64
+    L.ep_combine_two_level.argtypes = [sp, lp, _P, _P, i64, i64, ctypes.c_int, u32, _P, _P, i64,
+                                       ctypes.c_int, _P, _P, sz, _P]
     L.ep_clear_errors.argtypes = [_P, _P]
     L.ep_check_errors.argtypes = [_P, _P, ctypes.POINTER(u32)]
     L.ep_status_string.argtypes = [ctypes.c_int]
     L.ep_status_string.restype = ctypes.c_char_p
     for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch",
-              "ep_combine", "ep_combine_expand", "ep_clear_errors", "ep_check_errors"):
+              "ep_combine", "ep_combine_expand", "ep_combine_two_level", "ep_clear_errors",
+              "ep_check_errors"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -191,6 +197,21 @@ def ep_combine_expand(shape, layout: dict, y, y_rows: int, y_row_stride: int, y_
                                    _ptr(topk_weights), _ptr(out), _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(stream)),
            "ep_combine_expand")
+
+
+def ep_partial_row_bytes(shape: ep_shape) -> int:
+    return int(lib().ep_partial_row_bytes(ctypes.byref(shape)))
+
+
+def ep_combine_two_level(shape, layout: dict, topk_idx, y, y_rows: int, y_row_stride: int,
+                         y_format: int, epoch: int, topk_weights, group_buf, group_cap: int,
+                         steps: int, out, ws, stream=None):
+    L = _layout_struct(layout)
+    _check(lib().ep_combine_two_level(ctypes.byref(shape), ctypes.byref(L), _ptr(topk_idx), _ptr(y),
+                                      int(y_rows), int(y_row_stride), int(y_format), int(epoch),
+                                      _ptr(topk_weights), _ptr(group_buf), int(group_cap), int(steps),
+                                      _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream)), "ep_combine_two_level")
 
 
 def ep_clear_errors(ws, stream=None):

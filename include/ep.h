@@ -220,6 +220,33 @@ int ep_combine_expand(const ep_shape *shape, const ep_layout *layout, const void
                       const float *topk_weights, uint16_t *out, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* Byte stride of a partial row of the two-level combine: the bf16 hidden row
+ * alone in 512 B data-as-flag blocks, 512 * ceil(2H / 480). Host only. */
+int64_t ep_partial_row_bytes(const ep_shape *shape);
+
+/* Two-level combine: the two-level dispatch run backwards (the combine roles
+ * of [MEGA]'s legacy internode walk-through: scale-up reduce, then
+ * scale-out; [V2] §3.6 groups). y holds the per-(token, rank) expert outputs
+ * at layout->slot rows (EP_FMT_PLAIN or EP_FMT_CHUNKED as for ep_combine).
+ *  step 1 (steps & 1): for each token t and group g it sends to, partial =
+ *    bf16_rne(acc), acc = +0.0f, then for the usable lanes k of t whose rank
+ *    lies in g, ascending k: acc = fmaf(topk_weights[t*K+k], y[slot][h], acc);
+ *    written with flags = epoch as a chunked row (stride
+ *    ep_partial_row_bytes) at row layout->group_slot[t*K+k0] of group_buf (k0
+ *    = first lane of g). Rows >= group_cap are not written
+ *    (EP_DEVERR_CAPACITY).
+ *  step 2 (steps & 2): out[t][h] = bf16_rne(acc), acc = +0.0f, then for the
+ *    groups of t in ascending g: acc = acc + partial[t, g][h] (fp32 add); a
+ *    partial row with a flag != epoch is skipped (EP_DEVERR_FLAG).
+ * Needs layout->slot, layout->group_slot, tokens' topk_idx; K <= 16; epoch
+ * >= 1. Usable lanes are as in ep_combine. With G = 1 the result equals
+ * ep_combine bit for bit. */
+int ep_combine_two_level(const ep_shape *shape, const ep_layout *layout, const int64_t *topk_idx,
+                         const void *y, int64_t y_rows, int64_t y_row_stride, int y_format,
+                         uint32_t epoch, const float *topk_weights, void *group_buf,
+                         int64_t group_cap, int steps, uint16_t *out, void *ws, size_t ws_bytes,
+                         void *stream);
+
 /* Clear the workspace error word (a stream-ordered kernel, no memset node). */
 int ep_clear_errors(void *ws, void *stream);
 

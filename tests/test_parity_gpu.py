@@ -484,3 +484,93 @@ def test_expand_dispatch_and_combine(name, fp8):
                          tokens["topk_weights"], out, ws)
     combine_close(host(out), inp["x"])
     assert ep.ep_check_errors(ws) == 0
+
+
+# --------------------------------------------------------------------------
+# Two-level combine (partials per token and group, then the cross-group sum)
+# --------------------------------------------------------------------------
+
+def run_two_level(shape, L, tk, y, y_rows, y_stride, fmt, epoch, w_dev, steps=3, group_buf=None):
+    gcap = int(host(L["group_offsets"])[-1])
+    pstride = ep.ep_partial_row_bytes(shape)
+    if group_buf is None:
+        group_buf = torch.zeros((max(gcap, 1), pstride), dtype=torch.uint8, device="cuda")
+    out = poison(torch.empty((shape.T, shape.H), dtype=torch.uint16, device="cuda"))
+    ep.ep_combine_two_level(shape, L, tk, y, y_rows, y_stride, fmt, epoch, w_dev, group_buf, gcap,
+                            steps, out, ws=L["_ws"])
+    torch.cuda.synchronize()
+    return group_buf, out, gcap
+
+
+@pytest.mark.parametrize("name", ["hier8x8", "small"])
+def test_two_level_combine_chunked(name):
+    w = synth.workload(name) if name != "small" else synth.Workload("small", 900, 1024, 64, 16, 4, 6, "uniform")
+    inp = synth.make_inputs(w)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    L["_ws"] = ws
+    epoch = 6
+    gb, pb, G_rows, N, stride = run_hier(w, inp, shape, L, ws, tk, epoch)
+    wd = dev(inp["topk_w"])
+    gbuf, out, gcap = run_two_level(shape, L, tk, pb, N, stride, ep.EP_FMT_CHUNKED, epoch, wd)
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    Hd = oracle.hier_dispatch(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_offsets"], epoch,
+                              x=inp["x"], topk_w=inp["topk_w"])
+    C = oracle.combine_two_level(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_slot"],
+                                 inp["topk_w"], Hd["peer_buf"], w.H, gcap, epoch, chunked=True)
+    assert C["err"] == 0
+    np.testing.assert_array_equal(host(gbuf)[:gcap], C["group_buf"])
+    got = host(out)
+    np.testing.assert_array_equal(got, C["out"])
+    # round trip to x: the bf16 partials add one more rounding, so the max
+    # error bound is one bf16 half-ulp looser than the flat combine's
+    o = synth.bf16_to_float(got).astype(np.float64)
+    x = synth.bf16_to_float(inp["x"]).astype(np.float64)
+    assert np.abs(o - x).max() <= 2e-2 and np.linalg.norm(o - x) <= RTOL_L2 * np.linalg.norm(x)
+    assert ep.ep_check_errors(ws) == 0
+
+
+@pytest.mark.parametrize("T,H,K,E,R,G", [(300, 512, 3, 24, 8, 4), (257, 264, 12, 64, 16, 2),
+                                         (64, 7168, 8, 256, 64, 8), (128, 256, 2, 16, 4, 1)])
+def test_two_level_combine_plain(T, H, K, E, R, G):
+    w = synth.Workload("edge", T, H, E, R, G, K, "uniform")
+    rng = np.random.default_rng(T + H + K)
+    topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
+    wts = rng.standard_normal((T, K)).astype(np.float32)
+    shape, L, ws, tk = run_layout(w, topk)
+    L["_ws"] = ws
+    N = int(host(L["rank_offsets"])[-1])
+    y = synth.random_bf16_rows(max(N, 1), H, seed=T)
+    gbuf, out, gcap = run_two_level(shape, L, tk, dev(y), N, 2 * H, ep.EP_FMT_PLAIN, 9, dev(wts))
+    O = oracle.layout(topk, E, R, G)
+    C = oracle.combine_two_level(topk, E, R, G, O["slot"], O["group_slot"], wts, y[:N], H, gcap, 9)
+    np.testing.assert_array_equal(host(gbuf)[:gcap], C["group_buf"])
+    np.testing.assert_array_equal(host(out), C["out"])
+    if G == 1:  # one group: identical to the flat combine
+        flat = poison(torch.empty((T, H), dtype=torch.uint16, device="cuda"))
+        ep.ep_combine(shape, L, dev(y), N, 2 * H, ep.EP_FMT_PLAIN, 0, dev(wts), flat, ws)
+        np.testing.assert_array_equal(host(flat), host(out))
+    assert ep.ep_check_errors(ws) == 0
+
+
+def test_two_level_combine_corrupted_partial():
+    w = synth.Workload("small", 300, 512, 32, 8, 4, 4, "uniform")
+    inp = synth.make_inputs(w, seed=41)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    L["_ws"] = ws
+    N = int(host(L["rank_offsets"])[-1])
+    y = synth.random_bf16_rows(N, w.H, seed=2)
+    wd = dev(inp["topk_w"])
+    gbuf, out, gcap = run_two_level(shape, L, tk, dev(y), N, 2 * w.H, ep.EP_FMT_PLAIN, 3, wd, steps=1)
+    gbuf[7, 512 + 480 + 1] ^= 0x20
+    _, out2, _ = run_two_level(shape, L, tk, dev(y), N, 2 * w.H, ep.EP_FMT_PLAIN, 3, wd, steps=2,
+                               group_buf=gbuf)
+    assert ep.ep_check_errors(ws) == ep.EP_DEVERR_FLAG
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    C1 = oracle.combine_two_level(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_slot"],
+                                  inp["topk_w"], y, w.H, gcap, 3, steps=1)
+    g = C1["group_buf"].copy()
+    g[7, 512 + 480 + 1] ^= 0x20
+    C2 = oracle.combine_two_level(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_slot"],
+                                  inp["topk_w"], y, w.H, gcap, 3, steps=2, group_buf=g)
+    assert C2["err"] == oracle.ERR_FLAG
+    np.testing.assert_array_equal(host(out2), C2["out"])
