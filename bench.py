@@ -41,6 +41,10 @@ def parse():
     p.add_argument("--workload", default="ep32",
                    choices=["tiny", "ep32", "ep256", "zipf", "hier8x8"])
     p.add_argument("--fp8", action="store_true", help="also move the FP8 payload + scales")
+    p.add_argument("--two-level-combine", action="store_true",
+                   help="two-level workloads: combine through per-group partial rows")
+    p.add_argument("--expand", action="store_true",
+                   help="expand mode: one receive row per (token, lane), grouped by expert")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU-oracle baseline (0 = skip)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -93,6 +97,14 @@ def main():
     w = synth.workload(args.workload)
     hier = w.G > 1
     fp8 = bool(args.fp8)
+    expand = bool(args.expand)
+    two_level = bool(args.two_level_combine)
+    if two_level and not hier:
+        print("--two-level-combine applies to the two-level workloads", file=sys.stderr)
+        sys.exit(2)
+    if expand and hier:
+        print("--expand applies to the flat workloads", file=sys.stderr)
+        sys.exit(2)
     # Independent input batches, rotated step by step, so that the x rows a
     # step reads were not left in the 256 MB MALL by an earlier step: the
     # other batches' x alone exceed it.
@@ -116,13 +128,13 @@ def main():
             tk["x_fp8"] = dev(b_in["x_fp8"])
             tk["x_scales"] = dev(b_in["x_scales"])
         batches.append(tk)
-    L = ep.alloc_layout(shape, masks=True, groups=hier)
+    L = ep.alloc_layout(shape, masks=True, groups=hier, expand=expand)
     ws = ep.alloc_workspace(shape)
     Ns, Gs = [], []
     for tk in batches:
         ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
         torch.cuda.synchronize()
-        Ns.append(int(L["rank_offsets"][-1].item()))
+        Ns.append(int((L["expert_offsets"] if expand else L["rank_offsets"])[-1].item()))
         Gs.append(int(L["group_offsets"][-1].item()) if hier else 0)
     N_cap, G_cap = max(Ns), max(Gs)
     out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
@@ -131,6 +143,9 @@ def main():
         stride = ep.ep_chunked_record_bytes(shape, seg)
         group_buf = torch.empty((G_cap, stride), dtype=torch.uint8, device="cuda")
         peer_buf = torch.empty((N_cap, stride), dtype=torch.uint8, device="cuda")
+        if two_level:
+            pstride = ep.ep_partial_row_bytes(shape)
+            part_buf = torch.empty((G_cap, pstride), dtype=torch.uint8, device="cuda")
     else:
         recv = ep.alloc_recv(shape, N_cap, fp8=fp8, scales=fp8, meta=True)
 
@@ -161,8 +176,18 @@ def main():
             timed("hier", lambda: ep.ep_hierarchical_dispatch(
                 shape, L, tokens, epoch[0], ep.EP_HIER_SCALEOUT | ep.EP_HIER_FORWARD,
                 group_buf, G_rows, peer_buf, N, ws), record)
-            timed("combine", lambda: ep.ep_combine(shape, L, peer_buf, N, stride, ep.EP_FMT_CHUNKED,
-                                                   epoch[0], tokens["topk_weights"], out, ws), record)
+            if two_level:
+                timed("combine", lambda: ep.ep_combine_two_level(
+                    shape, L, tokens["topk_idx"], peer_buf, N, stride, ep.EP_FMT_CHUNKED, epoch[0],
+                    tokens["topk_weights"], part_buf, G_rows, 3, out, ws), record)
+            else:
+                timed("combine", lambda: ep.ep_combine(shape, L, peer_buf, N, stride, ep.EP_FMT_CHUNKED,
+                                                       epoch[0], tokens["topk_weights"], out, ws), record)
+        elif expand:
+            timed("dispatch", lambda: ep.ep_dispatch_expand(shape, L, tokens, recv, N, ws), record)
+            timed("combine", lambda: ep.ep_combine_expand(shape, L, recv["x"], N, 2 * w.H,
+                                                          ep.EP_FMT_PLAIN, 0, tokens["topk_weights"],
+                                                          out, ws), record)
         else:
             timed("dispatch", lambda: ep.ep_dispatch(shape, L, tokens, recv, N, ws), record)
             timed("combine", lambda: ep.ep_combine(shape, L, recv["x"], N, 2 * w.H, ep.EP_FMT_PLAIN,
@@ -196,7 +221,8 @@ def main():
     row = 2 * H + ((H + 4 * (H // 128)) if fp8 else 0)
     meta = 4 + 8 * K
     route = T * K * (8 + 4 + 4)  # topk_idx read, weights read, slots read
-    bytes_layout = T * K * 8 + T * K * 4 + T * R + (T * K * 4 + T * w.G if hier else 0)
+    bytes_layout = T * K * 8 + T * K * 4 + T * R + (T * K * 4 + T * w.G if hier else 0) + \
+        (T * K * 8 + T * K * 4 if expand else 0)
     N = sum(Ns[i] for i in used) / len(used)
     G_rows = sum(Gs[i] for i in used) / len(used)
     if hier:
@@ -204,16 +230,21 @@ def main():
         hid = 512 * ((2 * H + 479) // 480)
         bytes_main = T * row + route + T * K * 4 + 2 * G_rows * rec + N * rec
         bytes_combine = N * hid + T * 2 * H + T * K * 8
+        if two_level:  # partial rows written, then read back
+            bytes_combine += 2 * G_rows * hid + T * K * 8
     else:
         bytes_main = T * row + route + N * (row + meta)
         bytes_combine = N * 2 * H + T * 2 * H + T * K * 8
     by = {"layout": bytes_layout, names[1]: bytes_main, "combine": bytes_combine}
     step_bytes = sum(by.values())
     kernel_of = {"layout": "layout_*", "dispatch": "dispatch_kernel",
-                 "hier": "scaleout_kernel+forward_kernel", "combine": "combine_kernel"}
+                 "hier": "scaleout_kernel+forward_kernel",
+                 "combine": "combine_group_kernel+combine_cross_kernel" if two_level else "combine_kernel"}
     dom = max(names[1:], key=lambda n: avg_ms[n])
     achieved = by[dom] / (avg_ms[dom] * 1e-3) / 1e9
-    traffic = committed_traffic(w.name + ("_fp8" if fp8 else ""), kernel_of[dom])
+    traffic = committed_traffic(w.name + ("_fp8" if fp8 else "") + ("_expand" if expand else "") +
+                                ("_2lc" if two_level else ""),
+                                kernel_of[dom])
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -223,7 +254,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, inp, fp8, hier, args.cpu_seconds)
+        cpu = cpu_baseline(w, inp, fp8, hier, args.cpu_seconds, expand)
 
     rec = {
         "metric": METRIC,
@@ -242,7 +273,9 @@ def main():
         "data": "synthetic (seeded; see synth/__init__.py)",
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": w.E,
                    "ranks": R, "groups": w.G, "topk": K, "routing": w.routing,
-                   "receive_rows": N, "fp8_payload": fp8, "input_batches": n_batches,
+                   "receive_rows": N, "fp8_payload": fp8, "expand_rows": expand,
+                   "two_level_combine": two_level,
+                   "input_batches": n_batches,
                    "parallelism": "single GPU"},
         "hbm_gbs_step": step_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -256,7 +289,7 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(w, inp, fp8, hier, budget_s):
+def cpu_baseline(w, inp, fp8, hier, budget_s, expand=False):
     """The oracle as it stands, single-threaded, on repeated full passes of the
     same batch until the time budget is spent (at least one pass)."""
     import oracle
@@ -270,6 +303,13 @@ def cpu_baseline(w, inp, fp8, hier, budget_s):
                                       1, x=inp["x"], x_fp8=inp.get("x_fp8"),
                                       x_scales=inp.get("x_scales"), topk_w=inp["topk_w"])
             oracle.combine(L["slot"], inp["topk_w"], Hd["peer_buf"], w.H, chunked=True, epoch=1)
+        elif expand:
+            es = oracle.expert_slots(inp["topk_idx"], w.E, L["expert_offsets"])
+            n_rows = int(L["expert_offsets"][-1])
+            D = oracle.dispatch_rows(inp["topk_idx"], w.E, es, n_rows, x=inp["x"],
+                                     x_fp8=inp.get("x_fp8"), x_scales=inp.get("x_scales"),
+                                     topk_w=inp["topk_w"])
+            oracle.combine(es, inp["topk_w"], D["recv_x"], w.H)
         else:
             D = oracle.dispatch(inp["topk_idx"], w.E, w.R, L["rank_offsets"], x=inp["x"],
                                 x_fp8=inp.get("x_fp8"), x_scales=inp.get("x_scales"),

@@ -119,64 +119,99 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_kernel(Combine2Ar
             um &= ~bad;
         }
     }
-    // Groups of this token: the first lane of each.
+    // Groups of this token: the first lane of each, numbered in lane order.
     bool first = g >= 0;
     for (int j = 0; j < a.K; ++j) {
         const int gj = readlane(g, j);
         if (j < lane && gj == g) first = false;
     }
-    const u32x4 flagv = {a.epoch, a.epoch, a.epoch, a.epoch};
-    for (uint64_t fm = __ballot(first); fm; fm &= fm - 1) {
-        const int k0 = __ffsll((unsigned long long)fm) - 1;
-        const int g0 = readlane(g, k0);
+    const uint64_t fm = __ballot(first);
+    // gpos: position of this lane's group among the token's groups.
+    int gpos = -1;
+    for (uint64_t m = fm; m; m &= m - 1) {
+        const int k0 = __ffsll((unsigned long long)m) - 1;
+        if (readlane(g, k0) == g) gpos = __popcll(fm & ((1ull << k0) - 1));
+    }
+    const int ng = __popcll(fm);
+    // Partial row of each group (its first lane's group slot); rows past the
+    // capacity are not written.
+    uint8_t* prow[KMAX];
+    uint32_t wmask = 0;  // groups whose partial row is written
+#pragma unroll
+    for (int gi = 0; gi < KMAX; ++gi) {
+        prow[gi] = a.group_buf;
+        if (gi >= ng) continue;
+        int k0 = -1, cnt = 0;
+        for (uint64_t m = fm; m; m &= m - 1, ++cnt)
+            if (cnt == gi) { k0 = __ffsll((unsigned long long)m) - 1; break; }
         const int64_t dst = readlane(gs, k0);
-        if (dst < 0) continue;
         if (dst >= a.group_cap) {
             if (lane == 0) report(a.err, EP_DEVERR_CAPACITY);
             continue;
         }
-        const uint64_t gm = um & __ballot(g == g0);
-        uint8_t* prow = a.group_buf + dst * a.pstride;
-        const int s_any = gm ? readlane(s, __ffsll((unsigned long long)gm) - 1) : 0;
-        const uint8_t* rowp[KMAX];
-        float wk[KMAX];
+        prow[gi] = a.group_buf + dst * a.pstride;
+        wmask |= 1u << gi;
+    }
+    if (!wmask) return;
+    // One pass over the hidden row: every lane's row is read once and feeds
+    // its group's accumulator (ascending k inside each group).
+    const int s_any = um ? readlane(s, __ffsll((unsigned long long)um) - 1) : 0;
+    const uint8_t* rowp[KMAX];
+    float wk[KMAX];
+    int gk[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int kk = min(k, a.K - 1);
+        rowp[k] = a.y + (int64_t)(((um >> k) & 1) ? readlane(s, kk) : s_any) * a.y_stride;
+        wk[k] = readlane_f(wt, kk);
+        gk[k] = readlane(gpos, kk);
+    }
+    const u32x4 flagv = {a.epoch, a.epoch, a.epoch, a.epoch};
+    for (int it = 0; it < iters; ++it) {
+        int c, wv, p;
+        const bool hv = chunk_vec(it, lane, nvh, c, wv, p);
+        const int64_t off = hv ? (a.y_chunked ? (int64_t)c * kChunkBytes + (int64_t)wv * 16 : (int64_t)p * 16) : 0;
+        u32x4 v[KMAX];
+        if (um) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) v[k] = ld16(rowp[k] + off);
+        }
+        float acc[KMAX][8];
+#pragma unroll
+        for (int gi = 0; gi < KMAX; ++gi)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[gi][q] = 0.f;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            const int kk = min(k, a.K - 1);
-            rowp[k] = a.y + (int64_t)(((gm >> k) & 1) ? readlane(s, kk) : s_any) * a.y_stride;
-            wk[k] = readlane_f(wt, kk);
-        }
-        for (int it = 0; it < iters; ++it) {
-            int c, wv, p;
-            const bool hv = chunk_vec(it, lane, nvh, c, wv, p);
-            const int64_t off = hv ? (a.y_chunked ? (int64_t)c * kChunkBytes + (int64_t)wv * 16 : (int64_t)p * 16) : 0;
-            u32x4 v[KMAX];
-            if (gm) {
+            if (!((um >> k) & 1)) continue;
 #pragma unroll
-                for (int k = 0; k < KMAX; ++k) v[k] = ld16(rowp[k] + off);
-            }
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (!((gm >> k) & 1)) continue;
+            for (int gi = 0; gi < KMAX; ++gi) {
+                if (gk[k] != gi) continue;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] = __builtin_fmaf(wk[k], bf16_lo(v[k][q]), acc[2 * q]);
-                    acc[2 * q + 1] = __builtin_fmaf(wk[k], bf16_hi(v[k][q]), acc[2 * q + 1]);
+                    acc[gi][2 * q] = __builtin_fmaf(wk[k], bf16_lo(v[k][q]), acc[gi][2 * q]);
+                    acc[gi][2 * q + 1] = __builtin_fmaf(wk[k], bf16_hi(v[k][q]), acc[gi][2 * q + 1]);
                 }
             }
+        }
+        if (c >= nblk) continue;
+        const int64_t o_off = (int64_t)c * kChunkBytes + (int64_t)wv * 16;
+#pragma unroll
+        for (int gi = 0; gi < KMAX; ++gi) {
+            if (!((wmask >> gi) & 1)) continue;
             u32x4 o = {0u, 0u, 0u, 0u};
             if (hv) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    o[q] = f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16);
+                    o[q] = f32_to_bf16(acc[gi][2 * q]) | (f32_to_bf16(acc[gi][2 * q + 1]) << 16);
             }
             if (wv >= kChunkPayloadVecs) o = flagv;
-            if (c < nblk) st16_stream(prow + (int64_t)c * kChunkBytes + (int64_t)wv * 16, o);
+            st16_stream(prow[gi] + o_off, o);
         }
     }
 }
 
+template <int GMAX>
 __global__ __launch_bounds__(kBlockThreads) void combine_cross_kernel(Combine2Args a) {
     const int lane = lane_id();
     const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
@@ -209,35 +244,58 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_kernel(Combine2Ar
             fm &= ~bad;
         }
     }
-    // Order of the partials: ascending group. rank of a first lane = number
-    // of first lanes with a smaller group.
+    uint8_t* out_row = reinterpret_cast<uint8_t*>(a.out) + (int64_t)t * a.H * 2;
+    // The token's partial rows in ascending group: position = number of
+    // partials with a smaller group; unused positions point at a used row.
     int rank = 0;
     for (uint64_t m = fm; m; m &= m - 1) {
         const int j = __ffsll((unsigned long long)m) - 1;
         rank += readlane(g, j) < g ? 1 : 0;
     }
     const int ng = __popcll(fm);
-    uint8_t* out_row = reinterpret_cast<uint8_t*>(a.out) + (int64_t)t * a.H * 2;
-    for (int it = 0; it < iters; ++it) {
-        int c, wv, p;
-        const bool hv = chunk_vec(it, lane, nvh, c, wv, p);
-        const int64_t off = hv ? (int64_t)c * kChunkBytes + (int64_t)wv * 16 : 0;
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int pos = 0; pos < ng; ++pos) {
-            const uint64_t who = __ballot(((fm >> lane) & 1) && rank == pos);
-            const int k = __ffsll((unsigned long long)who) - 1;
-            const u32x4 v = ld16(a.group_buf + (int64_t)readlane(gs, k) * a.pstride + off);
+    const int row_any = fm ? readlane(gs, __ffsll((unsigned long long)fm) - 1) : 0;
+    const uint8_t* rowp[GMAX];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = acc[2 * q] + bf16_lo(v[q]);
-                acc[2 * q + 1] = acc[2 * q + 1] + bf16_hi(v[q]);
-            }
+    for (int pos = 0; pos < GMAX; ++pos) {
+        const uint64_t who = __ballot(((fm >> lane) & 1) && rank == pos);
+        const int row = who ? readlane(gs, __ffsll((unsigned long long)who) - 1) : row_any;
+        rowp[pos] = a.group_buf + (int64_t)row * a.pstride;
+    }
+    constexpr int NB = 2;
+    for (int it0 = 0; it0 < iters; it0 += NB) {
+        int c[NB], wv[NB], p[NB];
+        bool hv[NB];
+        int64_t off[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            hv[j] = it0 + j < iters && chunk_vec(it0 + j, lane, nvh, c[j], wv[j], p[j]);
+            off[j] = hv[j] ? (int64_t)c[j] * kChunkBytes + (int64_t)wv[j] * 16 : 0;
         }
-        if (hv) {
-            u32x4 o;
+        u32x4 v[GMAX][NB];
+        if (fm) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16);
-            st16_stream(out_row + (int64_t)p * 16, o);
+            for (int pos = 0; pos < GMAX; ++pos)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) v[pos][j] = ld16(rowp[pos] + off[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int pos = 0; pos < GMAX; ++pos) {
+                if (pos >= ng) break;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = acc[2 * q] + bf16_lo(v[pos][j][q]);
+                    acc[2 * q + 1] = acc[2 * q + 1] + bf16_hi(v[pos][j][q]);
+                }
+            }
+            if (hv[j]) {
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16);
+                st16_stream(out_row + (int64_t)p[j] * 16, o);
+            }
         }
     }
 }
@@ -279,7 +337,12 @@ hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const
         else
             hipLaunchKernelGGL(combine_group_kernel<16>, grid, block, 0, st, a);
     }
-    if (steps & 2) hipLaunchKernelGGL(combine_cross_kernel, grid, block, 0, st, a);
+    if (steps & 2) {
+        if (s.K <= 8)
+            hipLaunchKernelGGL(combine_cross_kernel<8>, grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL(combine_cross_kernel<16>, grid, block, 0, st, a);
+    }
     return hipGetLastError();
 }
 
