@@ -76,6 +76,8 @@ def _load():
         lib.oracle_combine_two_level.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, i64, i64,
                                                  i32, u32, P, i64, i32, P, P]
         lib.oracle_combine_two_level.restype = None
+        lib.oracle_source_counts.argtypes = [i32, i32, i32, i32, i32, P, P, P]
+        lib.oracle_source_counts.restype = i32
         lib.oracle_expert_slots.argtypes = [i32, i32, i32, P, P, P]
         lib.oracle_expert_slots.restype = i32
         lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -129,6 +131,18 @@ def layout(topk_idx: np.ndarray, E: int, R: int, G: int = 1) -> dict:
         raise ValueError("oracle_layout: bad shape")
     out["err"] = int(err[0])
     return out
+
+
+def source_counts(topk_idx, E, R, S) -> dict:
+    """Counts exchange of S source ranks: counts [S, R] and the rank-major
+    receive offsets [R * S + 1]."""
+    topk_idx = _c(topk_idx, np.int64)
+    T, K = topk_idx.shape
+    counts = np.zeros((S, R), np.int32)
+    offs = np.zeros(R * S + 1, np.int32)
+    if _load().oracle_source_counts(T, K, E, R, S, _p(topk_idx), _p(counts), _p(offs)) != 0:
+        raise ValueError("oracle_source_counts: bad arguments")
+    return dict(counts=counts, recv_offsets=offs)
 
 
 def expert_slots(topk_idx, E, expert_offsets) -> np.ndarray:

@@ -237,6 +237,47 @@ int oracle_expert_slots(int T, int K, int E, const int64_t *topk_idx,
 }
 
 /* ----------------------------------------------------------------------- */
+/* Several source ranks on one GPU: the counts exchange ([V2] §3.3 阶段3,   */
+/* psum_num_recv_tokens_per_scaleup_rank; §3.5 handle).                    */
+/* ----------------------------------------------------------------------- */
+
+/* S source ranks own consecutive token ranges of Ts = ceil(T / S) tokens
+ * (the last may be shorter). Each source counts its tokens per destination
+ * rank: counts[s][r] = #{t of source s : t sends to r}. The exchange hands
+ * destination r the column counts[.][r]; recv_offsets[r][s] = rank_offsets[r]
+ * + sum_{s' < s} counts[s'][r] is where source s's tokens start in r's
+ * region (rank-major, recv_offsets[R * S] = N). Returns -1 on bad args. */
+int oracle_source_counts(int T, int K, int E, int R, int S, const int64_t *topk_idx,
+                         int32_t *counts, int32_t *recv_offsets) {
+    if (S < 1 || R < 1 || E % R != 0) return -1;
+    const int epr = E / R;
+    const int Ts = (T + S - 1) / S;
+    uint8_t *seen = (uint8_t *)calloc((size_t)R, 1);
+    if (!seen) return -1;
+    memset(counts, 0, sizeof(int32_t) * (size_t)S * (size_t)R);
+    for (int t = 0; t < T; t++) {
+        const int src = Ts ? t / Ts : 0;
+        memset(seen, 0, (size_t)R);
+        for (int k = 0; k < K; k++) {
+            uint32_t dummy = 0;
+            int64_t e = checked_expert(topk_idx[(size_t)t * K + k], E, &dummy);
+            if (e < 0) continue;
+            int64_t r = e / epr;
+            if (!seen[r]) { seen[r] = 1; counts[(size_t)src * R + r] += 1; }
+        }
+    }
+    int32_t run = 0;
+    for (int r = 0; r < R; r++)
+        for (int src = 0; src < S; src++) {
+            recv_offsets[(size_t)r * S + src] = run;
+            run += counts[(size_t)src * R + r];
+        }
+    recv_offsets[(size_t)R * S] = run;
+    free(seen);
+    return 0;
+}
+
+/* ----------------------------------------------------------------------- */
 /* Direct dispatch ([V2] §3.3 阶段2, §3.5; [PIPE] NVL receivers).          */
 /* ----------------------------------------------------------------------- */
 

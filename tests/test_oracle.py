@@ -704,3 +704,31 @@ def test_two_level_combine_round_trip_and_corruption(oracle_lib):
     t_bad = int(np.nonzero((L["group_slot"] == 11).any(axis=1))[0][0])
     diff = np.nonzero((C2["out"] != C["out"]).any(axis=1))[0]
     assert set(diff.tolist()) <= {t_bad}
+
+
+# --------------------------------------------------------------------------
+# Several source ranks: the counts exchange
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S", [1, 2, 7, 32])
+def test_source_counts_invariants(oracle_lib, S):
+    w = synth.workload("ep32").scaled(1000)
+    inp = synth.make_inputs(w, with_x=False)
+    topk = inp["topk_idx"]
+    L = oracle_lib.layout(topk, w.E, w.R)
+    X = oracle_lib.source_counts(topk, w.E, w.R, S)
+    c, off = X["counts"], X["recv_offsets"]
+    np.testing.assert_array_equal(c.sum(axis=0), L["tokens_per_rank"])
+    np.testing.assert_array_equal(off.reshape(-1)[:-1].reshape(w.R, S)[:, 0], L["rank_offsets"][:-1])
+    assert off[-1] == L["rank_offsets"][-1]
+    np.testing.assert_array_equal(np.diff(off), c.T.reshape(-1))
+    # brute force: source s's rows in rank r are exactly its tokens, in order
+    Ts = -(-w.T // S)
+    epr = w.E // w.R
+    for r in (0, 5, w.R - 1):
+        toks = [t for t in range(w.T) if any(0 <= e < w.E and e // epr == r for e in topk[t])]
+        for s in range(S):
+            mine = [t for t in toks if t // Ts == s]
+            assert c[s, r] == len(mine)
+            rows = [L["slot"][t][[k for k in range(w.K) if topk[t, k] // epr == r][0]] for t in mine]
+            np.testing.assert_array_equal(rows, off[r * S + s] + np.arange(len(mine)))
