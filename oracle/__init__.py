@@ -78,6 +78,12 @@ def _load():
         lib.oracle_combine_two_level.restype = None
         lib.oracle_source_counts.argtypes = [i32, i32, i32, i32, i32, P, P, P]
         lib.oracle_source_counts.restype = i32
+        lib.oracle_source_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P,
+                                               u32, P, i64, P]
+        lib.oracle_source_dispatch.restype = i32
+        lib.oracle_copy_epilogue.argtypes = [i32, i32, i32, i32, P, P, i64, i32, i32, i32, u32,
+                                             i64, P, P, P, P, P, P, P]
+        lib.oracle_copy_epilogue.restype = i32
         lib.oracle_expert_slots.argtypes = [i32, i32, i32, P, P, P]
         lib.oracle_expert_slots.restype = i32
         lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -322,6 +328,61 @@ def unpack_rows(buf, H, K, epoch, with_bf16=True, with_fp8=False, with_scales=Fa
                                      _p(out["recv_src"]), _p(out["recv_topk_idx"]),
                                      _p(out["recv_topk_w"]))
     out["bad_rows"] = int(bad)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Several source ranks: send into per-source regions, copy epilogue
+# --------------------------------------------------------------------------
+
+def source_dispatch(topk_idx, E, R, S, cap, epoch, x=None, x_fp8=None, x_scales=None,
+                    topk_w=None) -> dict:
+    """Staging buffer [R * S * cap, stride] (uint8, zero where not written)
+    after every source rank sent its tokens into its regions."""
+    topk_idx = _c(topk_idx, np.int64)
+    T, K = topk_idx.shape
+    x = _c(x, np.uint16)
+    x_fp8 = _c(x_fp8, np.uint8)
+    x_scales = _c(x_scales, np.float32)
+    topk_w = _c(topk_w, np.float32)
+    H = x.shape[1] if x is not None else x_fp8.shape[1]
+    P = record_bytes(H, K, x is not None, x_fp8 is not None, x_scales is not None)
+    stride = chunked_bytes(P)
+    staging = np.zeros((R * S * cap, stride), np.uint8)
+    err = np.zeros(1, np.uint32)
+    rc = _load().oracle_source_dispatch(T, H, K, E, R, S, _p(topk_idx), _p(topk_w), _p(x),
+                                        _p(x_fp8), _p(x_scales), int(epoch), _p(staging),
+                                        int(cap), _p(err))
+    if rc != 0:
+        raise ValueError("oracle_source_dispatch: bad arguments")
+    return dict(staging=staging, stride=stride, err=int(err[0]))
+
+
+def copy_epilogue(recv_offsets, staging, H, K, R, S, cap, epoch, with_bf16=True,
+                  with_fp8=False, with_scales=False, recv_cap=None) -> dict:
+    """Dense receive arrays (rows = recv_cap, default N) filled from the
+    staging regions; rows not written keep -7 (ids, src) or 0."""
+    recv_offsets = _c(recv_offsets, np.int32)
+    staging = _c(staging, np.uint8)
+    N = int(recv_offsets[R * S])
+    rows = N if recv_cap is None else int(recv_cap)
+    out = dict(
+        recv_x=np.zeros((rows, H), np.uint16) if with_bf16 else None,
+        recv_fp8=np.zeros((rows, H), np.uint8) if with_fp8 else None,
+        recv_scales=np.zeros((rows, H // 128), np.float32) if with_scales else None,
+        recv_src=np.full(rows, -7, np.int32),
+        recv_topk_idx=np.full((rows, K), -7, np.int32),
+        recv_topk_w=np.zeros((rows, K), np.float32),
+    )
+    err = np.zeros(1, np.uint32)
+    rc = _load().oracle_copy_epilogue(H, K, R, S, _p(recv_offsets), _p(staging), int(cap),
+                                      int(with_bf16), int(with_fp8), int(with_scales), int(epoch),
+                                      rows, _p(out["recv_x"]), _p(out["recv_fp8"]),
+                                      _p(out["recv_scales"]), _p(out["recv_src"]),
+                                      _p(out["recv_topk_idx"]), _p(out["recv_topk_w"]), _p(err))
+    if rc != 0:
+        raise ValueError("oracle_copy_epilogue: bad arguments")
+    out["err"] = int(err[0])
     return out
 
 

@@ -554,6 +554,106 @@ int64_t oracle_unpack_rows(const uint8_t *buf, int64_t rows, int H, int K, int w
 }
 
 /* ----------------------------------------------------------------------- */
+/* Several source ranks: send into per-source regions, then the copy       */
+/* epilogue ([V2] §3.3 阶段2 slot per destination rank, 阶段3 copy         */
+/* epilogue walking psum_num_recv_tokens_per_scaleup_rank).                */
+/* ----------------------------------------------------------------------- */
+
+/* Send step. Source s (tokens [s*Ts, min((s+1)*Ts, T)), Ts = ceil(T / S))
+ * sends each token once per distinct destination rank r, in token order, to
+ * the next row of the region (r, s) of `staging`: row (r*S + s)*cap + j with
+ * j = #{earlier tokens of s that send to r}. Rows are chunked records (row
+ * stride oracle_chunked_bytes(P)) carrying `epoch`. j >= cap sets error bit 1
+ * and the row is not written. Returns -1 on bad args. */
+int oracle_source_dispatch(int T, int H, int K, int E, int R, int S, const int64_t *topk_idx,
+                           const float *topk_w, const uint16_t *x, const uint8_t *x_fp8,
+                           const float *x_scales, uint32_t epoch, uint8_t *staging, int64_t cap,
+                           uint32_t *err) {
+    if (S < 1 || R < 1 || E % R != 0 || cap < 0) return -1;
+    const int epr = E / R;
+    const int Ts = (T + S - 1) / S;
+    const int64_t Prec = oracle_record_bytes(H, K, x != NULL, x_fp8 != NULL, x_scales != NULL);
+    const int64_t stride = oracle_chunked_bytes(Prec);
+    uint8_t *rec = (uint8_t *)malloc((size_t)Prec);
+    int64_t *next = (int64_t *)malloc(sizeof(int64_t) * (size_t)R);
+    if (!rec || !next) { free(rec); free(next); return -1; }
+    for (int src = 0; src < S; src++) {
+        for (int r = 0; r < R; r++) next[r] = 0;
+        const int t_end = (src + 1) * Ts < T ? (src + 1) * Ts : T;
+        for (int t = src * Ts; t < t_end; t++) {
+            const int64_t *row = topk_idx + (size_t)t * K;
+            oracle_pack_record(t, H, K, E, topk_idx, topk_w, x, x_fp8, x_scales, rec);
+            for (int k = 0; k < K; k++) {
+                int64_t e = checked_expert(row[k], E, err);
+                if (e < 0) continue;
+                int64_t r = e / epr;
+                int seen = 0;
+                for (int j = 0; j < k; j++)
+                    if (row[j] >= 0 && row[j] < E && row[j] / epr == r) seen = 1;
+                if (seen) continue;
+                int64_t j = next[r]++;
+                if (j >= cap) { *err |= ORC_ERR_CAPACITY; continue; }
+                oracle_chunk(rec, Prec, epoch, staging + (((int64_t)r * S + src) * cap + j) * stride);
+            }
+        }
+    }
+    free(rec);
+    free(next);
+    return 0;
+}
+
+/* Copy epilogue. Dense receive row i in [0, N), N = recv_offsets[R*S],
+ * comes from the region (r, s) found by walking recv_offsets (rank-major)
+ * until recv_offsets[r*S + s] <= i < recv_offsets[r*S + s + 1]; its staging
+ * row is (r*S + s)*cap + (i - recv_offsets[r*S + s]). The record's fields
+ * go to row i of the receive arrays (any may be NULL). Rows left unwritten:
+ * i >= recv_cap or a region row beyond cap (error bit 1), a staging row
+ * whose flags are not all `epoch` (error bit 2). Returns -1 on bad args. */
+int oracle_copy_epilogue(int H, int K, int R, int S, const int32_t *recv_offsets,
+                         const uint8_t *staging, int64_t cap, int with_bf16, int with_fp8,
+                         int with_scales, uint32_t epoch, int64_t recv_cap, uint16_t *recv_x,
+                         uint8_t *recv_fp8, float *recv_scales, int32_t *recv_src,
+                         int32_t *recv_topk_idx, float *recv_topk_w, uint32_t *err) {
+    if (S < 1 || R < 1 || cap < 0 || recv_cap < 0) return -1;
+    const int S8 = H / 128;
+    const int64_t Prec = oracle_record_bytes(H, K, with_bf16, with_fp8, with_scales);
+    const int64_t stride = oracle_chunked_bytes(Prec);
+    uint8_t *rec = (uint8_t *)malloc((size_t)Prec);
+    if (!rec) return -1;
+    const int64_t n_rows = recv_offsets[(size_t)R * S];
+    int64_t region = 0;  /* r*S + s of the current region */
+    for (int64_t i = 0; i < n_rows; i++) {
+        while (i >= recv_offsets[region + 1]) region++;
+        const int64_t j = i - recv_offsets[region];
+        if (j >= cap || i >= recv_cap) { *err |= ORC_ERR_CAPACITY; continue; }
+        if (oracle_unchunk(staging + (region * cap + j) * stride, Prec, epoch, rec)) {
+            *err |= ORC_ERR_FLAG;
+            continue;
+        }
+        int64_t off = 0;
+        if (with_bf16) {
+            if (recv_x) memcpy(recv_x + i * H, rec + off, 2 * (size_t)H);
+            off += round_up16(2 * (int64_t)H);
+        }
+        if (with_fp8) {
+            if (recv_fp8) memcpy(recv_fp8 + i * H, rec + off, (size_t)H);
+            off += round_up16((int64_t)H);
+        }
+        if (with_scales) {
+            if (recv_scales) memcpy(recv_scales + i * S8, rec + off, 4 * (size_t)S8);
+            off += round_up16(4 * (int64_t)S8);
+        }
+        if (recv_topk_idx) memcpy(recv_topk_idx + i * K, rec + off, 4 * (size_t)K);
+        off += round_up16(4 * (int64_t)K);
+        if (recv_topk_w) memcpy(recv_topk_w + i * K, rec + off, 4 * (size_t)K);
+        off += round_up16(4 * (int64_t)K);
+        if (recv_src) memcpy(recv_src + i, rec + off, 4);
+    }
+    free(rec);
+    return 0;
+}
+
+/* ----------------------------------------------------------------------- */
 /* Combine ([MEGA] combine write; [ASC] BF16 hidden + FP32 weights).       */
 /* ----------------------------------------------------------------------- */
 

@@ -732,3 +732,84 @@ def test_source_counts_invariants(oracle_lib, S):
             assert c[s, r] == len(mine)
             rows = [L["slot"][t][[k for k in range(w.K) if topk[t, k] // epr == r][0]] for t in mine]
             np.testing.assert_array_equal(rows, off[r * S + s] + np.arange(len(mine)))
+
+
+def _multi_source(oracle_lib, w, S, cap=None, fp8=False, corrupt=None):
+    inp = synth.make_inputs(w, with_fp8=fp8)
+    topk = inp["topk_idx"]
+    X = oracle_lib.source_counts(topk, w.E, w.R, S)
+    cap = int(X["counts"].max()) if cap is None else cap
+    extra = dict(x_fp8=inp["x_fp8"], x_scales=inp["x_scales"]) if fp8 else {}
+    sd = oracle_lib.source_dispatch(topk, w.E, w.R, S, cap, 5, x=inp["x"], topk_w=inp["topk_w"], **extra)
+    if corrupt is not None:
+        corrupt(sd["staging"])
+    ce = oracle_lib.copy_epilogue(X["recv_offsets"], sd["staging"], w.H, w.K, w.R, S, cap, 5,
+                                  with_fp8=fp8, with_scales=fp8)
+    return inp, X, sd, ce
+
+
+@pytest.mark.parametrize("S", [1, 3, 4, 32])
+def test_multi_source_equals_direct(oracle_lib, S):
+    """Per-source regions then the copy epilogue give exactly the direct
+    dispatch's receive rows: the sources are ascending token ranges, so the
+    concatenation of their regions in each rank is ascending token order."""
+    w = synth.workload("tiny")
+    inp, X, sd, ce = _multi_source(oracle_lib, w, S, fp8=True)
+    L = oracle_lib.layout(inp["topk_idx"], w.E, w.R)
+    D = oracle_lib.dispatch(inp["topk_idx"], w.E, w.R, L["rank_offsets"], x=inp["x"],
+                            x_fp8=inp["x_fp8"], x_scales=inp["x_scales"], topk_w=inp["topk_w"])
+    assert sd["err"] == 0 and ce["err"] == 0
+    for f in ("recv_x", "recv_fp8", "recv_scales", "recv_src", "recv_topk_idx", "recv_topk_w"):
+        np.testing.assert_array_equal(ce[f], D[f], err_msg=f)
+
+
+def test_multi_source_staging_brute_force(oracle_lib):
+    """Row j of region (r, s) holds the j-th token of source s that sends to r."""
+    w = synth.workload("tiny")
+    S = 3
+    inp, X, sd, _ = _multi_source(oracle_lib, w, S)
+    topk = inp["topk_idx"]
+    Ts = -(-w.T // S)
+    epr = w.E // w.R
+    cap = int(X["counts"].max())
+    rows = oracle_lib.unpack_rows(sd["staging"], w.H, w.K, 5)
+    for s in range(S):
+        for r in range(w.R):
+            toks = [t for t in range(s * Ts, min((s + 1) * Ts, w.T))
+                    if any(0 <= e < w.E and e // epr == r for e in topk[t])]
+            base = (r * S + s) * cap
+            np.testing.assert_array_equal(rows["recv_src"][base:base + len(toks)], toks)
+            np.testing.assert_array_equal(rows["recv_x"][base:base + len(toks)], inp["x"][toks])
+            assert not sd["staging"][base + len(toks):base + cap].any()
+
+
+def test_multi_source_capacity_and_flags(oracle_lib):
+    w = synth.workload("tiny")
+    S = 2
+    inp, X, sd, ce = _multi_source(oracle_lib, w, S)
+    full_cap = int(X["counts"].max())
+    # A smaller region capacity: rows j >= cap are neither sent nor copied.
+    cap = full_cap - 3
+    _, _, sd2, ce2 = _multi_source(oracle_lib, w, S, cap=cap)
+    assert sd2["err"] == 2 and ce2["err"] == 2  # capacity
+    off = X["recv_offsets"]
+    for reg in range(w.R * S):
+        for i in range(off[reg], off[reg + 1]):
+            if i - off[reg] < cap:
+                assert ce2["recv_src"][i] == ce["recv_src"][i]
+            else:
+                assert ce2["recv_src"][i] == -7
+    # A staging row with one stale flag word is dropped and reported.
+    stride = sd["stride"]
+    reg = 1 * S + 1  # rank 1, source 1
+    victim = reg * full_cap + 2
+
+    def corrupt(st):
+        st[victim, 512 + 480 + 4] ^= 1  # second block's flag
+
+    _, _, _, ce3 = _multi_source(oracle_lib, w, S, corrupt=corrupt)
+    i = off[reg] + 2
+    assert ce3["err"] == 4 and ce3["recv_src"][i] == -7  # stale flag
+    keep = np.arange(len(ce["recv_src"])) != i
+    np.testing.assert_array_equal(ce3["recv_src"][keep], ce["recv_src"][keep])
+    assert stride >= 1024
