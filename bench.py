@@ -6,6 +6,10 @@ A step is one pass of the whole path over one batch of synthetic tokens:
                      the combine gathers the dispatched rows back)
   two-level (hier) : ep_get_layout -> ep_hierarchical_dispatch (both steps) ->
                      ep_combine on the chunked scale-up rows
+  --sources S      : S source ranks (default R) on the flat workloads:
+                     ep_source_layout -> ep_source_dispatch into per-(rank,
+                     source) staging regions -> ep_copy_epilogue into dense
+                     receive rows -> ep_combine over the staging rows
 Inputs are seeded and already resident in HBM when the timed region starts.
 W untimed warm-up steps, then exactly K timed steps between two device
 synchronisations. Prints one JSON line.
@@ -45,6 +49,8 @@ def parse():
                    help="two-level workloads: combine through per-group partial rows")
     p.add_argument("--expand", action="store_true",
                    help="expand mode: one receive row per (token, lane), grouped by expert")
+    p.add_argument("--sources", type=int, default=None, const=0, nargs="?",
+                   help="several source ranks on one GPU (S; bare flag = one per rank)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU-oracle baseline (0 = skip)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -105,6 +111,11 @@ def main():
     if expand and hier:
         print("--expand applies to the flat workloads", file=sys.stderr)
         sys.exit(2)
+    multi = args.sources is not None
+    S = (args.sources or w.R) if multi else 1
+    if multi and (hier or expand or two_level):
+        print("--sources applies to the flat workloads without --expand", file=sys.stderr)
+        sys.exit(2)
     # Independent input batches, rotated step by step, so that the x rows a
     # step reads were not left in the 256 MB MALL by an earlier step: the
     # other batches' x alone exceed it.
@@ -131,11 +142,27 @@ def main():
     L = ep.alloc_layout(shape, masks=True, groups=hier, expand=expand)
     ws = ep.alloc_workspace(shape)
     Ns, Gs = [], []
-    for tk in batches:
-        ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
-        torch.cuda.synchronize()
-        Ns.append(int((L["expert_offsets"] if expand else L["rank_offsets"])[-1].item()))
-        Gs.append(int(L["group_offsets"][-1].item()) if hier else 0)
+    if multi:
+        # Region capacity: the largest per-(source, rank) count over the
+        # batches (a first pass with capacity = tokens per source cannot
+        # overflow).
+        ws = ep.alloc_source_workspace(shape, S)
+        Ts = -(-w.T // S)
+        src = ep.alloc_sources(shape, S, Ts)
+        cap = 1
+        for tk in batches:
+            ep.ep_source_layout(shape, tk["topk_idx"], src, ws)
+            torch.cuda.synchronize()
+            cap = max(cap, int(src["counts"].max().item()))
+            Ns.append(int(src["recv_offsets"][-1].item()))
+            Gs.append(0)
+        src["capacity"] = cap
+    else:
+        for tk in batches:
+            ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+            torch.cuda.synchronize()
+            Ns.append(int((L["expert_offsets"] if expand else L["rank_offsets"])[-1].item()))
+            Gs.append(int(L["group_offsets"][-1].item()) if hier else 0)
     N_cap, G_cap = max(Ns), max(Gs)
     out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
     seg = ep.EP_SEG_BF16 | ((ep.EP_SEG_FP8 | ep.EP_SEG_SCALES) if fp8 else 0)
@@ -148,10 +175,15 @@ def main():
             part_buf = torch.empty((G_cap, pstride), dtype=torch.uint8, device="cuda")
     else:
         recv = ep.alloc_recv(shape, N_cap, fp8=fp8, scales=fp8, meta=True)
+    if multi:
+        stride = ep.ep_chunked_record_bytes(shape, seg)
+        staging = torch.empty((w.R * S * cap, stride), dtype=torch.uint8, device="cuda")
+        y_src = dict(slot=src["src_slot"])
 
     epoch = [0]
     stream = torch.cuda.current_stream()
-    names = ["layout", "hier" if hier else "dispatch", "combine"]
+    names = (["layout", "send", "epilogue", "combine"] if multi else
+             ["layout", "hier" if hier else "dispatch", "combine"])
     ev = {n: [] for n in names}
     used = []
 
@@ -171,6 +203,16 @@ def main():
         tokens, N, G_rows = batches[i], Ns[i], Gs[i]
         if record:
             used.append(i)
+        if multi:
+            e = epoch[0]
+            timed("layout", lambda: ep.ep_source_layout(shape, tokens["topk_idx"], src, ws), record)
+            timed("send", lambda: ep.ep_source_dispatch(shape, src, tokens, e, staging, ws), record)
+            timed("epilogue", lambda: ep.ep_copy_epilogue(shape, src, staging, e, seg, recv, N, ws),
+                  record)
+            timed("combine", lambda: ep.ep_combine(shape, y_src, staging, staging.shape[0], stride,
+                                                   ep.EP_FMT_CHUNKED, e, tokens["topk_weights"],
+                                                   out, ws), record)
+            return
         timed("layout", lambda: ep.ep_get_layout(shape, tokens["topk_idx"], L, ws), record)
         if hier:
             timed("hier", lambda: ep.ep_hierarchical_dispatch(
@@ -225,7 +267,15 @@ def main():
         (T * K * 8 + T * K * 4 if expand else 0)
     N = sum(Ns[i] for i in used) / len(used)
     G_rows = sum(Gs[i] for i in used) / len(used)
-    if hier:
+    if multi:
+        rec = ep.ep_chunked_record_bytes(shape, seg)
+        hid = 512 * ((2 * H + 479) // 480)
+        bytes_layout = T * K * 8 + T * K * 4
+        by = {"layout": bytes_layout,
+              "send": T * row + route + N * rec,
+              "epilogue": N * rec + N * (row + meta),
+              "combine": N * hid + T * 2 * H + T * K * 8}
+    elif hier:
         rec = ep.ep_chunked_record_bytes(shape, seg)
         hid = 512 * ((2 * H + 479) // 480)
         bytes_main = T * row + route + T * K * 4 + 2 * G_rows * rec + N * rec
@@ -235,15 +285,17 @@ def main():
     else:
         bytes_main = T * row + route + N * (row + meta)
         bytes_combine = N * 2 * H + T * 2 * H + T * K * 8
-    by = {"layout": bytes_layout, names[1]: bytes_main, "combine": bytes_combine}
+    if not multi:
+        by = {"layout": bytes_layout, names[1]: bytes_main, "combine": bytes_combine}
     step_bytes = sum(by.values())
-    kernel_of = {"layout": "layout_*", "dispatch": "dispatch_kernel",
+    kernel_of = {"layout": "layout_*", "dispatch": "dispatch_kernel", "send": "scaleout_kernel",
+                 "epilogue": "copy_epilogue_kernel",
                  "hier": "scaleout_kernel+forward_kernel",
                  "combine": "combine_group_kernel+combine_cross_kernel" if two_level else "combine_kernel"}
     dom = max(names[1:], key=lambda n: avg_ms[n])
     achieved = by[dom] / (avg_ms[dom] * 1e-3) / 1e9
     traffic = committed_traffic(w.name + ("_fp8" if fp8 else "") + ("_expand" if expand else "") +
-                                ("_2lc" if two_level else ""),
+                                ("_2lc" if two_level else "") + (f"_s{S}" if multi else ""),
                                 kernel_of[dom])
 
     if args.copy_calibration:
@@ -254,7 +306,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, inp, fp8, hier, args.cpu_seconds, expand)
+        cpu = cpu_baseline(w, inp, fp8, hier, args.cpu_seconds, expand, S if multi else 0)
 
     rec = {
         "metric": METRIC,
@@ -275,6 +327,8 @@ def main():
                    "ranks": R, "groups": w.G, "topk": K, "routing": w.routing,
                    "receive_rows": N, "fp8_payload": fp8, "expand_rows": expand,
                    "two_level_combine": two_level,
+                   "sources": S if multi else None,
+                   "region_capacity": cap if multi else None,
                    "input_batches": n_batches,
                    "parallelism": "single GPU"},
         "hbm_gbs_step": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -289,7 +343,7 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(w, inp, fp8, hier, budget_s, expand=False):
+def cpu_baseline(w, inp, fp8, hier, budget_s, expand=False, sources=0):
     """The oracle as it stands, single-threaded, on repeated full passes of the
     same batch until the time budget is spent (at least one pass)."""
     import oracle
@@ -297,6 +351,21 @@ def cpu_baseline(w, inp, fp8, hier, budget_s, expand=False):
     oracle.build(force=False)
     passes, t0 = 0, time.perf_counter()
     while True:
+        if sources:
+            X = oracle.source_counts(inp["topk_idx"], w.E, w.R, sources)
+            cap = int(X["counts"].max())
+            Sd = oracle.source_dispatch(inp["topk_idx"], w.E, w.R, sources, cap, 1, x=inp["x"],
+                                        x_fp8=inp.get("x_fp8"), x_scales=inp.get("x_scales"),
+                                        topk_w=inp["topk_w"])
+            oracle.copy_epilogue(X["recv_offsets"], Sd["staging"], w.H, w.K, w.R, sources, cap, 1,
+                                 with_fp8=fp8, with_scales=fp8)
+            slot = oracle.source_slots(inp["topk_idx"], w.E, w.R, sources, cap)["src_slot"]
+            oracle.combine(slot, inp["topk_w"], Sd["staging"], w.H, chunked=True, epoch=1)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+            continue
         L = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
         if hier:
             Hd = oracle.hier_dispatch(inp["topk_idx"], w.E, w.R, w.G, L["slot"], L["group_offsets"],
@@ -328,8 +397,10 @@ def cpu_baseline(w, inp, fp8, hier, budget_s, expand=False):
     except OSError:
         pass
     return {"value": w.T * passes / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} full pass(es) of layout+{'two-level dispatch' if hier else 'dispatch'}"
-                      f"+combine over the same {w.T}-token batch, {el:.1f} s, single thread",
+            "sample": (f"{passes} full pass(es) of source counts+send+copy epilogue "
+                       f"+combine ({sources} sources)" if sources else
+                       f"{passes} full pass(es) of layout+{'two-level dispatch' if hier else 'dispatch'}"
+                       "+combine") + f" over the same {w.T}-token batch, {el:.1f} s, single thread",
             "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
 
 

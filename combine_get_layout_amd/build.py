@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libep.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "hier.hip", "combine.hip", "combine2.hip"]
+SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "hier.hip", "combine.hip", "combine2.hip",
+           "source.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -247,6 +247,73 @@ int ep_combine_two_level(const ep_shape* shape, const ep_layout* layout, const i
                                                static_cast<hipStream_t>(stream)));
 }
 
+size_t ep_source_workspace_bytes(const ep_shape* shape, int32_t S) {
+    if (check_shape(shape) != EP_OK || S < 1 || S > EP_MAX_RANKS) return 0;
+    return ws_source(*shape, S).total;
+}
+
+static int check_sources(const ep_shape* shape, const ep_sources* src, void* ws, size_t ws_bytes) {
+    int rc = check_shape(shape);
+    if (rc != EP_OK) return rc;
+    if (!src || src->S < 1 || src->capacity < 0) return EP_ERR_ARG;
+    if (src->S > EP_MAX_RANKS) return EP_ERR_UNSUPPORTED;
+    if ((int64_t)shape->R * src->S * src->capacity > INT32_MAX) return EP_ERR_UNSUPPORTED;
+    if (!ws || !aligned(ws, 256) || ws_bytes < ws_source(*shape, src->S).total) return EP_ERR_ARG;
+    return EP_OK;
+}
+
+int ep_source_layout(const ep_shape* shape, const int64_t* topk_idx, const ep_sources* sources,
+                     void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sources(shape, sources, ws, ws_bytes);
+    if (rc != EP_OK) return rc;
+    const ep_sources& X = *sources;
+    if (!X.counts || !X.recv_offsets || (shape->T > 0 && (!topk_idx || !X.src_slot))) return EP_ERR_ARG;
+    if (!aligned(topk_idx, 8) || !aligned(X.counts, 4) || !aligned(X.recv_offsets, 4) ||
+        !aligned(X.src_slot, 4))
+        return EP_ERR_ARG;
+    return hip_status(launch_source_layout(*shape, topk_idx, X, static_cast<char*>(ws),
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int ep_source_dispatch(const ep_shape* shape, const ep_sources* sources, const ep_tokens* tokens,
+                       uint32_t epoch, void* staging, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sources(shape, sources, ws, ws_bytes);
+    if (rc != EP_OK) return rc;
+    if (!tokens || epoch == 0) return EP_ERR_ARG;
+    const int64_t rows = (int64_t)shape->R * sources->S * sources->capacity;
+    if (shape->T > 0 && (!tokens->x || !tokens->topk_idx || !tokens->topk_weights ||
+                         !sources->src_slot || (rows > 0 && !staging)))
+        return EP_ERR_ARG;
+    if (tokens->x_fp8 && shape->H % 16 != 0) return EP_ERR_ARG;
+    if (tokens->x_scales && shape->H % 128 != 0) return EP_ERR_ARG;
+    if (!aligned(tokens->x, 16) || !aligned(tokens->x_fp8, 16) || !aligned(tokens->x_scales, 4) ||
+        !aligned(tokens->topk_idx, 8) || !aligned(tokens->topk_weights, 4) ||
+        !aligned(staging, 16) || !aligned(sources->src_slot, 4))
+        return EP_ERR_ARG;
+    return hip_status(launch_send_rows(*shape, *tokens, sources->src_slot, rows, epoch, staging,
+                                       static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+int ep_copy_epilogue(const ep_shape* shape, const ep_sources* sources, const void* staging,
+                     uint32_t epoch, int seg_flags, const ep_recv* recv, void* ws,
+                     size_t ws_bytes, void* stream) {
+    int rc = check_sources(shape, sources, ws, ws_bytes);
+    if (rc != EP_OK) return rc;
+    if (!recv || recv->capacity < 0 || epoch == 0 || !sources->recv_offsets) return EP_ERR_ARG;
+    if (!(seg_flags & EP_SEG_BF16) || (seg_flags & ~7)) return EP_ERR_ARG;
+    if ((seg_flags & EP_SEG_FP8) && shape->H % 16 != 0) return EP_ERR_ARG;
+    if ((seg_flags & EP_SEG_SCALES) && shape->H % 128 != 0) return EP_ERR_ARG;
+    if ((recv->x_fp8 && !(seg_flags & EP_SEG_FP8)) || (recv->x_scales && !(seg_flags & EP_SEG_SCALES)))
+        return EP_ERR_ARG;
+    if (sources->capacity > 0 && !staging) return EP_ERR_ARG;
+    if (!aligned(staging, 16) || !aligned(recv->x, 16) || !aligned(recv->x_fp8, 16) ||
+        !aligned(recv->x_scales, 4) || !aligned(recv->src_idx, 4) || !aligned(recv->topk_idx, 4) ||
+        !aligned(recv->topk_weights, 4) || !aligned(sources->recv_offsets, 4))
+        return EP_ERR_ARG;
+    return hip_status(launch_copy_epilogue(*shape, *sources, staging, epoch, seg_flags, *recv,
+                                           static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+}
+
 int ep_clear_errors(void* ws, void* stream) {
     if (!ws || !aligned(ws, 256)) return EP_ERR_ARG;
     hipLaunchKernelGGL(clear_error_kernel, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream),

@@ -23,6 +23,14 @@ constexpr int kChunkPayload = 480;
 constexpr int kChunkPayloadVecs = 30;
 constexpr int kChunkVecs = 32;
 
+// A chunked row is moved one wave-iteration (two 512 B blocks, 1 KiB) at a
+// time: lanes 0-31 cover block 2*it, lanes 32-63 block 2*it + 1. Byte offset
+// of this lane's 16-byte vector of iteration `it`.
+__device__ __forceinline__ int64_t chunk_lane_offset(int it, int lane) {
+    const int c = 2 * it + (lane >> 5);
+    return (int64_t)c * kChunkBytes + (int64_t)(lane & 31) * 16;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_in_block() { return threadIdx.x / kWave; }
 

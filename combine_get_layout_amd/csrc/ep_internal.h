@@ -25,6 +25,16 @@ struct WsLayout {
 };
 WsLayout ws_layout(const ep_shape& s);
 
+// Workspace of the several-source calls: the layout workspace, then per-tile
+// counts [S][nbs][R] (nbs = tiles of 256 tokens per source).
+struct WsSource {
+    int Ts;       // tokens per source, ceil(T / S)
+    int nbs;      // tiles per source, max(1, ceil(Ts / 256))
+    size_t part;  // int32 [S][nbs][R]
+    size_t total;
+};
+WsSource ws_source(const ep_shape& s, int S);
+
 // Record geometry of a packed token record (vectors are 16 B).
 struct RecordGeom {
     int nv_x, nv_fp8, nv_scales, nv_idx, nv_w;  // vectors per piece (0 if absent)
@@ -51,5 +61,12 @@ hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const
                                     uint32_t epoch, const float* w, void* group_buf,
                                     int64_t group_cap, int steps, uint16_t* out, char* ws,
                                     hipStream_t st);
+hipError_t launch_send_rows(const ep_shape& s, const ep_tokens& tk, const int32_t* rows,
+                            int64_t n_rows, uint32_t epoch, void* buf, char* ws, hipStream_t st);
+hipError_t launch_source_layout(const ep_shape& s, const int64_t* topk, const ep_sources& src,
+                                char* ws, hipStream_t st);
+hipError_t launch_copy_epilogue(const ep_shape& s, const ep_sources& src, const void* staging,
+                                uint32_t epoch, int seg, const ep_recv& rv, char* ws,
+                                hipStream_t st);
 
 }  // namespace ep

@@ -21,6 +21,8 @@
 //   step 2: one wave per group-region row (grid-stride; the row count is read
 //           on the device): check every block's flag, read src and top-k ids
 //           from the record, then stream the row to each scale-up peer's row.
+// Step 1 also serves several source ranks on one GPU: given one staging row
+// per (token, destination rank) instead of per group, it is their send.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -81,12 +83,6 @@ __device__ __forceinline__ u32x4 meta_vector(const HierArgs& a, int t, int q) {
     }
     if (q == g.q_src) v[0] = (uint32_t)t;
     return v;
-}
-
-// Byte offset inside a chunked row of wave-iteration `it`, for this lane.
-__device__ __forceinline__ int64_t chunk_lane_offset(int it, int lane) {
-    const int c = 2 * it + (lane >> 5);
-    return (int64_t)c * kChunkBytes + (int64_t)(lane & 31) * 16;
 }
 
 __global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
@@ -250,31 +246,36 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
     }
 }
 
-}  // namespace
-
-hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
-                       uint32_t epoch, int steps, void* group_buf, int64_t group_cap,
-                       void* peer_buf, int64_t peer_cap, char* ws, hipStream_t st) {
+HierArgs hier_args(const ep_shape& s, const ep_tokens& tk, uint32_t epoch, char* ws) {
     const WsLayout W = ws_layout(s);
     int seg = EP_SEG_BF16 | (tk.x_fp8 ? EP_SEG_FP8 : 0) | (tk.x_scales ? EP_SEG_SCALES : 0);
-    HierArgs a;
+    HierArgs a = {};
     a.T = s.T; a.H = s.H; a.K = s.K; a.E = s.E; a.R = s.R; a.G = s.G;
     a.epr = s.E / s.R; a.P = s.R / s.G;
     a.geom = record_geom(s, seg);
-    a.slot = L.slot;
-    a.group_slot = L.group_slot;
-    a.group_offsets = L.group_offsets;
     a.topk = tk.topk_idx;
     a.topk_w = tk.topk_weights;
     a.x = reinterpret_cast<const uint8_t*>(tk.x);
     a.x_fp8 = tk.x_fp8;
     a.x_scales = tk.x_scales;
+    a.epoch = epoch;
+    a.err = reinterpret_cast<uint32_t*>(ws + W.err);
+    return a;
+}
+
+}  // namespace
+
+hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
+                       uint32_t epoch, int steps, void* group_buf, int64_t group_cap,
+                       void* peer_buf, int64_t peer_cap, char* ws, hipStream_t st) {
+    HierArgs a = hier_args(s, tk, epoch, ws);
+    a.slot = L.slot;
+    a.group_slot = L.group_slot;
+    a.group_offsets = L.group_offsets;
     a.group_buf = reinterpret_cast<uint8_t*>(group_buf);
     a.group_cap = group_cap;
     a.peer_buf = reinterpret_cast<uint8_t*>(peer_buf);
     a.peer_cap = peer_cap;
-    a.epoch = epoch;
-    a.err = reinterpret_cast<uint32_t*>(ws + W.err);
     const dim3 block(kBlockThreads);
     if ((steps & EP_HIER_SCALEOUT) && s.T > 0)
         hipLaunchKernelGGL(scaleout_kernel, dim3((s.T + kWavesPerBlock - 1) / kWavesPerBlock), block, 0,
@@ -284,6 +285,18 @@ hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& t
         const int blocks = (int)(want < 8192 ? want : 8192);
         hipLaunchKernelGGL(forward_kernel, dim3(blocks), block, 0, st, a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_send_rows(const ep_shape& s, const ep_tokens& tk, const int32_t* rows,
+                            int64_t n_rows, uint32_t epoch, void* buf, char* ws, hipStream_t st) {
+    if (s.T == 0) return hipSuccess;
+    HierArgs a = hier_args(s, tk, epoch, ws);
+    a.group_slot = rows;
+    a.group_buf = reinterpret_cast<uint8_t*>(buf);
+    a.group_cap = n_rows;
+    hipLaunchKernelGGL(scaleout_kernel, dim3((s.T + kWavesPerBlock - 1) / kWavesPerBlock),
+                       dim3(kBlockThreads), 0, st, a);
     return hipGetLastError();
 }
 

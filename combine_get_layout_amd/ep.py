@@ -49,10 +49,16 @@ class ep_recv(ctypes.Structure):
                                   "topk_weights")] + [("capacity", ctypes.c_int64)]
 
 
+class ep_sources(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int32), ("capacity", ctypes.c_int64), ("counts", _P),
+                ("recv_offsets", _P), ("src_slot", _P)]
+
+
 EXPORTS = ("ep_workspace_bytes", "ep_record_bytes", "ep_chunked_record_bytes", "ep_get_layout",
            "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch", "ep_combine",
-           "ep_combine_expand", "ep_partial_row_bytes", "ep_combine_two_level", "ep_clear_errors",
-           "ep_check_errors", "ep_status_string")
+           "ep_combine_expand", "ep_partial_row_bytes", "ep_combine_two_level",
+           "ep_source_workspace_bytes", "ep_source_layout", "ep_source_dispatch",
+           "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors", "ep_status_string")
 
 _lib = None
 
@@ -85,13 +91,20 @@ def lib() -> ctypes.CDLL:
     L.ep_partial_row_bytes.restype = i64
     L.ep_combine_two_level.argtypes = [sp, lp, _P, _P, i64, i64, ctypes.c_int, u32, _P, _P, i64,
                                        ctypes.c_int, _P, _P, sz, _P]
+    xp = ctypes.POINTER(ep_sources)
+    L.ep_source_workspace_bytes.argtypes = [sp, ctypes.c_int32]
+    L.ep_source_workspace_bytes.restype = sz
+    L.ep_source_layout.argtypes = [sp, _P, xp, _P, sz, _P]
+    L.ep_source_dispatch.argtypes = [sp, xp, ctypes.POINTER(ep_tokens), u32, _P, _P, sz, _P]
+    L.ep_copy_epilogue.argtypes = [sp, xp, _P, u32, ctypes.c_int, ctypes.POINTER(ep_recv), _P, sz,
+                                   _P]
     L.ep_clear_errors.argtypes = [_P, _P]
     L.ep_check_errors.argtypes = [_P, _P, ctypes.POINTER(u32)]
     L.ep_status_string.argtypes = [ctypes.c_int]
     L.ep_status_string.restype = ctypes.c_char_p
     for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch",
-              "ep_combine", "ep_combine_expand", "ep_combine_two_level", "ep_clear_errors",
-              "ep_check_errors"):
+              "ep_combine", "ep_combine_expand", "ep_combine_two_level", "ep_source_layout",
+              "ep_source_dispatch", "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -214,6 +227,46 @@ def ep_combine_two_level(shape, layout: dict, topk_idx, y, y_rows: int, y_row_st
                                       _stream(stream)), "ep_combine_two_level")
 
 
+def _sources_struct(sources: dict) -> ep_sources:
+    return ep_sources(int(sources["S"]), int(sources["capacity"]), _ptr(sources.get("counts")),
+                      _ptr(sources.get("recv_offsets")), _ptr(sources.get("src_slot")))
+
+
+def _recv_struct(recv: dict, capacity: int) -> ep_recv:
+    return ep_recv(*[_ptr(recv.get(n)) for n in ("x", "x_fp8", "x_scales", "src_idx", "topk_idx",
+                                                  "topk_weights")], int(capacity))
+
+
+def ep_source_workspace_bytes(shape: ep_shape, S: int) -> int:
+    return int(lib().ep_source_workspace_bytes(ctypes.byref(shape), int(S)))
+
+
+def ep_source_layout(shape, topk_idx, sources: dict, ws, stream=None):
+    X = _sources_struct(sources)
+    _check(lib().ep_source_layout(ctypes.byref(shape), _ptr(topk_idx), ctypes.byref(X), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)),
+           "ep_source_layout")
+
+
+def ep_source_dispatch(shape, sources: dict, tokens: dict, epoch: int, staging, ws, stream=None):
+    X = _sources_struct(sources)
+    tk = _tokens_struct(tokens)
+    _check(lib().ep_source_dispatch(ctypes.byref(shape), ctypes.byref(X), ctypes.byref(tk),
+                                    int(epoch), _ptr(staging), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)),
+           "ep_source_dispatch")
+
+
+def ep_copy_epilogue(shape, sources: dict, staging, epoch: int, seg_flags: int, recv: dict,
+                     capacity: int, ws, stream=None):
+    X = _sources_struct(sources)
+    rv = _recv_struct(recv, capacity)
+    _check(lib().ep_copy_epilogue(ctypes.byref(shape), ctypes.byref(X), _ptr(staging), int(epoch),
+                                  int(seg_flags), ctypes.byref(rv), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)),
+           "ep_copy_epilogue")
+
+
 def ep_clear_errors(ws, stream=None):
     _check(lib().ep_clear_errors(_ptr(ws), _stream(stream)), "ep_clear_errors")
 
@@ -237,6 +290,21 @@ def alloc_workspace(shape: ep_shape, device="cuda") -> torch.Tensor:
     if n == 0:
         raise RuntimeError("ep_workspace_bytes: unsupported shape")
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def alloc_source_workspace(shape: ep_shape, S: int, device="cuda") -> torch.Tensor:
+    n = ep_source_workspace_bytes(shape, S)
+    if n == 0:
+        raise RuntimeError("ep_source_workspace_bytes: unsupported shape or source count")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def alloc_sources(shape: ep_shape, S: int, capacity: int, device="cuda") -> dict:
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(S=int(S), capacity=int(capacity),
+                counts=torch.empty((S, shape.R), **i32),
+                recv_offsets=torch.empty(shape.R * S + 1, **i32),
+                src_slot=torch.empty((shape.T, shape.K), **i32))
 
 
 def alloc_layout(shape: ep_shape, device="cuda", masks=True, groups=True, expand=False) -> dict:

@@ -247,6 +247,59 @@ int ep_combine_two_level(const ep_shape *shape, const ep_layout *layout, const i
                          int64_t group_cap, int steps, uint16_t *out, void *ws, size_t ws_bytes,
                          void *stream);
 
+/* Several source ranks on one GPU ([V2] §3.3 阶段2: each source hands out,
+ * per destination rank, the next slot of its own region there, addressed as
+ * rank * capacity + slot; 阶段3: the copy epilogue finds each received row's
+ * source from the prefix sum of tokens received per source rank
+ * (psum_num_recv_tokens_per_scaleup_rank) and copies the row out of that
+ * source's region). Source s owns tokens [s*Ts, min((s+1)*Ts, T)), Ts =
+ * ceil(T / S). The staging buffer holds one region of `capacity` chunked
+ * rows per (destination rank r, source s), region index r*S + s. */
+typedef struct ep_sources {
+    int32_t S;               /* source ranks, 1 <= S <= EP_MAX_RANKS */
+    int64_t capacity;        /* rows per (rank, source) region; R*S*capacity <= INT32_MAX */
+    int32_t *counts;         /* [S*R] tokens source s sends to rank r, each token once */
+    int32_t *recv_offsets;   /* [R*S+1] rank-major exclusive prefix of counts: the dense rows
+                                of region (r, s) start at recv_offsets[r*S+s]; [R*S] = N */
+    int32_t *src_slot;       /* [T*K] staging row (r*S+s)*capacity + j of (t, rank r of lane
+                                k), j = #{earlier tokens of s sending to r}; -1 if skipped */
+} ep_sources;
+
+/* Workspace bytes of the several-source calls (>= ep_workspace_bytes; the
+ * error word is at the same place). Host only; 0 on bad args. */
+size_t ep_source_workspace_bytes(const ep_shape *shape, int32_t S);
+
+/* Per-source counts, the counts exchange (recv_offsets, what every
+ * destination learns from an all-to-all of counts) and src_slot. Clears the
+ * workspace error word first. j >= capacity sets EP_DEVERR_CAPACITY and the
+ * lane gets -1; invalid ids set EP_DEVERR_EXPERT_ID. Deterministic: with
+ * contiguous sources, region (r, s) of the dense rows is exactly the part of
+ * rank r's region (ep_get_layout) that holds source s's tokens, so dense row
+ * recv_offsets[r*S+s] + j == layout slot of the same (t, r). */
+int ep_source_layout(const ep_shape *shape, const int64_t *topk_idx, const ep_sources *sources,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Send step: each token's chunked record (pieces as for
+ * ep_hierarchical_dispatch; x and topk_weights required) goes once to each
+ * distinct staging row src_slot[t*K+k] >= 0, flags = epoch (>= 1). staging:
+ * R*S*capacity rows of ep_chunked_record_bytes. */
+int ep_source_dispatch(const ep_shape *shape, const ep_sources *sources, const ep_tokens *tokens,
+                       uint32_t epoch, void *staging, void *ws, size_t ws_bytes, void *stream);
+
+/* Copy epilogue: dense row i < N = recv_offsets[R*S] of region (r, s)
+ * (recv_offsets[r*S+s] <= i < recv_offsets[r*S+s+1]) is staging row
+ * (r*S+s)*capacity + (i - recv_offsets[r*S+s]); its record (pieces
+ * `seg_flags`, as written by ep_source_dispatch) is unpacked into row i of
+ * the receive arrays (NULL ones skipped; a piece must be in the record to be
+ * asked for). A row whose flags are not all epoch is skipped
+ * (EP_DEVERR_FLAG); rows >= recv->capacity and region rows >= capacity are
+ * skipped (EP_DEVERR_CAPACITY). The result equals ep_dispatch's receive
+ * rows. The combine of this layout is ep_combine with layout->slot =
+ * src_slot over y rows indexed like the staging buffer. */
+int ep_copy_epilogue(const ep_shape *shape, const ep_sources *sources, const void *staging,
+                     uint32_t epoch, int seg_flags, const ep_recv *recv, void *ws,
+                     size_t ws_bytes, void *stream);
+
 /* Clear the workspace error word (a stream-ordered kernel, no memset node). */
 int ep_clear_errors(void *ws, void *stream);
 

@@ -78,6 +78,8 @@ def _load():
         lib.oracle_combine_two_level.restype = None
         lib.oracle_source_counts.argtypes = [i32, i32, i32, i32, i32, P, P, P]
         lib.oracle_source_counts.restype = i32
+        lib.oracle_source_slots.argtypes = [i32, i32, i32, i32, i32, P, i64, P, P]
+        lib.oracle_source_slots.restype = i32
         lib.oracle_source_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P,
                                                u32, P, i64, P]
         lib.oracle_source_dispatch.restype = i32
@@ -334,6 +336,17 @@ def unpack_rows(buf, H, K, epoch, with_bf16=True, with_fp8=False, with_scales=Fa
 # --------------------------------------------------------------------------
 # Several source ranks: send into per-source regions, copy epilogue
 # --------------------------------------------------------------------------
+
+def source_slots(topk_idx, E, R, S, cap) -> dict:
+    """Staging row [T, K] of every lane (-1 if skipped) and the error bits."""
+    topk_idx = _c(topk_idx, np.int64)
+    T, K = topk_idx.shape
+    out = np.zeros((T, K), np.int32)
+    err = np.zeros(1, np.uint32)
+    if _load().oracle_source_slots(T, K, E, R, S, _p(topk_idx), int(cap), _p(out), _p(err)) != 0:
+        raise ValueError("oracle_source_slots: bad arguments")
+    return dict(src_slot=out, err=int(err[0]))
+
 
 def source_dispatch(topk_idx, E, R, S, cap, epoch, x=None, x_fp8=None, x_scales=None,
                     topk_w=None) -> dict:

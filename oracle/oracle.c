@@ -277,6 +277,42 @@ int oracle_source_counts(int T, int K, int E, int R, int S, const int64_t *topk_
     return 0;
 }
 
+/* Staging row of every lane: src_slot[t*K+k] = (r*S + s)*cap + j for a
+ * valid lane of rank r, j = #{earlier tokens of source s that send to r}
+ * (lanes of one rank share the row); -1 for an invalid lane, and -1 with
+ * error bit 1 when j >= cap. Returns -1 on bad args. */
+int oracle_source_slots(int T, int K, int E, int R, int S, const int64_t *topk_idx, int64_t cap,
+                        int32_t *src_slot, uint32_t *err) {
+    if (S < 1 || R < 1 || E % R != 0 || cap < 0) return -1;
+    const int epr = E / R;
+    const int Ts = (T + S - 1) / S;
+    int64_t *next = (int64_t *)malloc(sizeof(int64_t) * (size_t)R);
+    if (!next) return -1;
+    for (int t = 0; t < T; t++) {
+        const int src = t / Ts;
+        if (t == src * Ts)
+            for (int r = 0; r < R; r++) next[r] = 0;
+        const int64_t *row = topk_idx + (size_t)t * K;
+        for (int k = 0; k < K; k++) {
+            int64_t e = checked_expert(row[k], E, err);
+            int32_t v = -1;
+            if (e >= 0) {
+                int64_t r = e / epr;
+                int64_t j = next[r];
+                for (int q = 0; q < k; q++)
+                    if (row[q] >= 0 && row[q] < E && row[q] / epr == r) j = next[r] - 1;
+                int first = (j == next[r]);
+                if (first) next[r]++;
+                if (j < cap) v = (int32_t)((r * S + src) * cap + j);
+                else if (first) *err |= ORC_ERR_CAPACITY;
+            }
+            src_slot[(size_t)t * K + k] = v;
+        }
+    }
+    free(next);
+    return 0;
+}
+
 /* ----------------------------------------------------------------------- */
 /* Direct dispatch ([V2] §3.3 阶段2, §3.5; [PIPE] NVL receivers).          */
 /* ----------------------------------------------------------------------- */

@@ -101,3 +101,40 @@ def test_zero_tokens_dispatch_and_combine_enqueue_nothing(lib):
                            ws, n, None) == ep.EP_OK
     assert lib.ep_combine(ctypes.byref(s), ctypes.byref(L), None, 0, 512, ep.EP_FMT_PLAIN, 0,
                           None, None, ws, n, None) == ep.EP_OK
+
+
+def test_source_calls_checked_before_launch(lib):
+    s = ep.make_shape(4096, 7168, 8, 256, 32, 1)
+    base = ep.ep_workspace_bytes(s)
+    n = ep.ep_source_workspace_bytes(s, 32)
+    assert n > base and n % 256 == 0
+    # one tile of 128 tokens per source: [S][1][R] int32 counts after the layout workspace
+    assert n - base == 32 * 1 * 32 * 4
+    assert ep.ep_source_workspace_bytes(s, 0) == 0
+    assert ep.ep_source_workspace_bytes(s, 2048) == 0
+    ws = 0x100000
+
+    def src(S=32, cap=128):
+        return ep.ep_sources(S, cap, 0x2000, 0x3000, 0x4000)
+
+    X = src()
+    assert lib.ep_source_layout(ctypes.byref(s), 0x1000, ctypes.byref(X), ws, base, None) == ep.EP_ERR_ARG
+    X = src(S=0)
+    assert lib.ep_source_layout(ctypes.byref(s), 0x1000, ctypes.byref(X), ws, n, None) == ep.EP_ERR_ARG
+    X = src(cap=-1)
+    assert lib.ep_source_layout(ctypes.byref(s), 0x1000, ctypes.byref(X), ws, n, None) == ep.EP_ERR_ARG
+    X = src(cap=1 << 22)  # R * S * capacity beyond int32 rows
+    assert lib.ep_source_layout(ctypes.byref(s), 0x1000, ctypes.byref(X), ws, n, None) == ep.EP_ERR_UNSUPPORTED
+    X = src()
+    tk = ep.ep_tokens()
+    assert lib.ep_source_dispatch(ctypes.byref(s), ctypes.byref(X), ctypes.byref(tk), 1, 0x5000,
+                                  ws, n, None) == ep.EP_ERR_ARG  # no x / topk / weights
+    tk = ep.ep_tokens(0x10000, None, None, 0x20000, 0x30000)
+    assert lib.ep_source_dispatch(ctypes.byref(s), ctypes.byref(X), ctypes.byref(tk), 0, 0x5000,
+                                  ws, n, None) == ep.EP_ERR_ARG  # epoch 0
+    rv = ep.ep_recv(0x10000, 0x20000, None, None, None, None, 100)
+    # fp8 receive rows asked for but not in the record
+    assert lib.ep_copy_epilogue(ctypes.byref(s), ctypes.byref(X), 0x5000, 1, ep.EP_SEG_BF16,
+                                ctypes.byref(rv), ws, n, None) == ep.EP_ERR_ARG
+    assert lib.ep_copy_epilogue(ctypes.byref(s), ctypes.byref(X), 0x5000, 1, ep.EP_SEG_FP8,
+                                ctypes.byref(rv), ws, n, None) == ep.EP_ERR_ARG  # no bf16 piece

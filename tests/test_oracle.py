@@ -813,3 +813,41 @@ def test_multi_source_capacity_and_flags(oracle_lib):
     keep = np.arange(len(ce["recv_src"])) != i
     np.testing.assert_array_equal(ce3["recv_src"][keep], ce["recv_src"][keep])
     assert stride >= 1024
+
+
+@pytest.mark.parametrize("S", [1, 3, 32])
+def test_source_slots_against_layout_and_staging(oracle_lib, S):
+    """src_slot is pinned two ways: its in-region index j equals the layout
+    slot minus the region's dense start (both count earlier tokens of the same
+    rank, the sources being ascending token ranges), and the staging row it
+    names holds that token's record."""
+    w = synth.workload("tiny")
+    inp = synth.make_inputs(w)
+    topk = inp["topk_idx"].copy()
+    topk[5, 1] = topk[5, 0]          # a repeated expert
+    topk[9, 0] = -1                  # an empty lane
+    L = oracle_lib.layout(topk, w.E, w.R)
+    X = oracle_lib.source_counts(topk, w.E, w.R, S)
+    cap = int(X["counts"].max())
+    ss = oracle_lib.source_slots(topk, w.E, w.R, S, cap)
+    assert ss["err"] == 0
+    Ts = -(-w.T // S)
+    epr = w.E // w.R
+    for t in range(w.T):
+        for k in range(w.K):
+            e = topk[t, k]
+            if not 0 <= e < w.E:
+                assert ss["src_slot"][t, k] == -1
+                continue
+            reg = (e // epr) * S + t // Ts
+            assert ss["src_slot"][t, k] == reg * cap + L["slot"][t, k] - X["recv_offsets"][reg]
+    sd = oracle_lib.source_dispatch(topk, w.E, w.R, S, cap, 3, x=inp["x"], topk_w=inp["topk_w"])
+    rows = oracle_lib.unpack_rows(sd["staging"], w.H, w.K, 3)
+    valid = ss["src_slot"] >= 0
+    tt = np.nonzero(valid)[0]
+    np.testing.assert_array_equal(rows["recv_src"][ss["src_slot"][valid]], tt)
+    # capacity: lanes beyond it get -1 and the error bit
+    small = oracle_lib.source_slots(topk, w.E, w.R, S, cap - 1)
+    assert small["err"] == 2
+    assert ((small["src_slot"] == -1) | (small["src_slot"] % (cap - 1) < cap - 1)).all()
+    assert (small["src_slot"] == -1).sum() > (~valid).sum()

@@ -574,3 +574,189 @@ def test_two_level_combine_corrupted_partial():
                                   inp["topk_w"], y, w.H, gcap, 3, steps=2, group_buf=g)
     assert C2["err"] == oracle.ERR_FLAG
     np.testing.assert_array_equal(host(out2), C2["out"])
+
+
+# --------------------------------------------------------------------------
+# Several source ranks: per-source regions, counts exchange, copy epilogue
+# --------------------------------------------------------------------------
+
+def expected_src_slot(topk, E, R, S, cap):
+    return oracle.source_slots(topk, E, R, S, cap)["src_slot"]
+
+
+def run_sources(w, inp, S, cap=None, fp8=False, epoch=9, steps=("layout", "send", "epilogue")):
+    topk = inp["topk_idx"]
+    T = topk.shape[0]
+    shape = ep.make_shape(T, w.H, topk.shape[1], w.E, w.R, 1)
+    X = oracle.source_counts(topk, w.E, w.R, S)
+    cap = max(int(X["counts"].max(initial=0)), 1) if cap is None else cap
+    src = ep.alloc_sources(shape, S, cap)
+    for k in ("counts", "recv_offsets", "src_slot"):
+        poison(src[k])
+    ws = ep.alloc_source_workspace(shape, S)
+    tk = dev(topk)
+    ep.ep_source_layout(shape, tk, src, ws)
+    seg = ep.EP_SEG_BF16 | ((ep.EP_SEG_FP8 | ep.EP_SEG_SCALES) if fp8 else 0)
+    stride = ep.ep_chunked_record_bytes(shape, seg)
+    staging = torch.zeros((max(w.R * S * cap, 1), stride), dtype=torch.uint8, device="cuda")
+    tokens = dict(x=dev(inp["x"]), topk_idx=tk, topk_weights=dev(inp["topk_w"]))
+    if fp8:
+        tokens["x_fp8"] = dev(inp["x_fp8"])
+        tokens["x_scales"] = dev(inp["x_scales"])
+    if "send" in steps:
+        ep.ep_source_dispatch(shape, src, tokens, epoch, staging, ws)
+    torch.cuda.synchronize()
+    return dict(shape=shape, src=src, ws=ws, staging=staging, stride=stride, seg=seg, cap=cap,
+                X=X, epoch=epoch, tokens=tokens)
+
+
+def run_epilogue(ctx, fp8=False, capacity=None):
+    N = int(host(ctx["src"]["recv_offsets"])[-1])
+    rows = N if capacity is None else capacity
+    recv = ep.alloc_recv(ctx["shape"], max(rows, 1), fp8=fp8, scales=fp8)
+    for t in recv.values():
+        poison(t)
+    ep.ep_copy_epilogue(ctx["shape"], ctx["src"], ctx["staging"], ctx["epoch"], ctx["seg"], recv,
+                        rows, ctx["ws"])
+    torch.cuda.synchronize()
+    return recv, N
+
+
+def check_sources_layout(ctx, topk, w, S):
+    X = ctx["X"]
+    O = oracle.layout(topk, w.E, w.R, 1)
+    np.testing.assert_array_equal(host(ctx["src"]["counts"]), X["counts"])
+    np.testing.assert_array_equal(host(ctx["src"]["recv_offsets"]), X["recv_offsets"])
+    np.testing.assert_array_equal(host(ctx["src"]["src_slot"]).reshape(topk.shape),
+                                  expected_src_slot(topk, w.E, w.R, S, ctx["cap"]))
+    return O
+
+
+@pytest.mark.parametrize("name,S", [("tiny", 1), ("tiny", 3), ("tiny", 4), ("ep32", 32),
+                                    ("ep256", 256), ("zipf", 256), ("hier8x8", 64)])
+def test_source_layout_full_size(name, S):
+    w = synth.workload(name)
+    inp = synth.make_inputs(w, with_x=False)
+    inp["x"] = np.zeros((w.T, w.H), np.uint16)
+    ctx = run_sources(w, inp, S, steps=("layout",))
+    check_sources_layout(ctx, inp["topk_idx"], w, S)
+    assert ep.ep_check_errors(ctx["ws"]) == 0
+
+
+@pytest.mark.parametrize("name,S,fp8", [("tiny", 1, False), ("tiny", 3, True), ("ep32", 32, False),
+                                        ("small", 5, True)])
+def test_source_dispatch_and_epilogue(name, S, fp8):
+    """Staging buffer byte for byte against the oracle's send step, dense
+    rows against the oracle's copy epilogue and its direct dispatch, and the
+    combine over the staging rows against the oracle's combine."""
+    w = synth.workload(name) if name != "small" else synth.Workload("small", 1500, 1024, 64, 16, 1, 6, "uniform")
+    inp = synth.make_inputs(w, with_fp8=fp8)
+    topk = inp["topk_idx"]
+    ctx = run_sources(w, inp, S, fp8=fp8)
+    O = check_sources_layout(ctx, topk, w, S)
+    extra = dict(x_fp8=inp["x_fp8"], x_scales=inp["x_scales"]) if fp8 else {}
+    Sd = oracle.source_dispatch(topk, w.E, w.R, S, ctx["cap"], ctx["epoch"], x=inp["x"],
+                                topk_w=inp["topk_w"], **extra)
+    assert Sd["err"] == 0 and Sd["stride"] == ctx["stride"]
+    np.testing.assert_array_equal(host(ctx["staging"]), Sd["staging"])
+    recv, N = run_epilogue(ctx, fp8=fp8)
+    Ce = oracle.copy_epilogue(ctx["X"]["recv_offsets"], Sd["staging"], w.H, w.K, w.R, S, ctx["cap"],
+                              ctx["epoch"], with_fp8=fp8, with_scales=fp8)
+    assert Ce["err"] == 0
+    check_dispatch(recv, Ce, N)
+    D = oracle.dispatch(topk, w.E, w.R, O["rank_offsets"], x=inp["x"], topk_w=inp["topk_w"], **extra)
+    check_dispatch(recv, D, N)
+    assert ep.ep_check_errors(ctx["ws"]) == 0
+    # combine over the staging rows, addressed by src_slot
+    out = poison(torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda"))
+    L = dict(slot=ctx["src"]["src_slot"])
+    ep.ep_combine(ctx["shape"], L, ctx["staging"], ctx["staging"].shape[0], ctx["stride"],
+                  ep.EP_FMT_CHUNKED, ctx["epoch"], ctx["tokens"]["topk_weights"], out, ctx["ws"])
+    slot = expected_src_slot(topk, w.E, w.R, S, ctx["cap"])
+    C = oracle.combine(slot, inp["topk_w"], Sd["staging"], w.H, chunked=True, epoch=ctx["epoch"])
+    assert C["err"] == 0
+    np.testing.assert_array_equal(host(out), C["out"])
+    assert ep.ep_check_errors(ctx["ws"]) == 0
+
+
+@pytest.mark.parametrize("name,S", [("ep256", 256), ("zipf", 16), ("hier8x8", 64)])
+def test_source_epilogue_full_size(name, S):
+    """Full-size workloads whose staging buffers are too large for the oracle's
+    send step: the dense rows are compared with the oracle's direct dispatch
+    (equal to its copy epilogue, a pinned identity), and sampled staging rows
+    with the oracle's chunked record of their token."""
+    w = synth.workload(name)
+    inp = synth.make_inputs(w)
+    topk = inp["topk_idx"]
+    ctx = run_sources(w, inp, S)
+    O = check_sources_layout(ctx, topk, w, S)
+    recv, N = run_epilogue(ctx)
+    D = oracle.dispatch(topk, w.E, w.R, O["rank_offsets"], x=inp["x"], topk_w=inp["topk_w"])
+    check_dispatch(recv, D, N)
+    assert ep.ep_check_errors(ctx["ws"]) == 0
+    slot = expected_src_slot(topk, w.E, w.R, S, ctx["cap"])
+    rng = np.random.default_rng(5)
+    for t in rng.choice(w.T, size=24, replace=False):
+        k = int(np.argmax(slot[t] >= 0))
+        if slot[t, k] < 0:
+            continue
+        rec = oracle.pack_record(int(t), topk, w.E, x=inp["x"], topk_w=inp["topk_w"])
+        want = oracle.chunk(rec, ctx["epoch"])
+        np.testing.assert_array_equal(host(ctx["staging"][int(slot[t, k])]), want)
+
+
+@pytest.mark.parametrize("T,K,E,R,S", [(0, 8, 64, 8, 4), (5, 2, 16, 4, 8), (300, 3, 12, 6, 7),
+                                       (1001, 20, 64, 16, 3), (513, 4, 16, 1, 2)])
+def test_source_edges(T, K, E, R, S):
+    """Empty input, more sources than tokens (empty sources), ragged sources,
+    K above 16 with duplicates and -1, one rank."""
+    w = synth.Workload("edge", T, 264, E, R, 1, K, "uniform")
+    rng = np.random.default_rng(T + 13 * S)
+    inp = dict(x=rng.integers(0, 65536, size=(T, 264)).astype(np.uint16),
+               topk_idx=rng.integers(-1, E, size=(T, K)).astype(np.int64),
+               topk_w=rng.standard_normal((T, K)).astype(np.float32))
+    ctx = run_sources(w, inp, S)
+    O = check_sources_layout(ctx, inp["topk_idx"], w, S)
+    recv, N = run_epilogue(ctx)
+    Sd = oracle.source_dispatch(inp["topk_idx"], E, R, S, ctx["cap"], ctx["epoch"], x=inp["x"],
+                                topk_w=inp["topk_w"])
+    if T:
+        np.testing.assert_array_equal(host(ctx["staging"]), Sd["staging"])
+    D = oracle.dispatch(inp["topk_idx"], E, R, O["rank_offsets"], x=inp["x"], topk_w=inp["topk_w"])
+    check_dispatch(recv, D, N)
+    assert ep.ep_check_errors(ctx["ws"]) == 0
+
+
+def test_source_capacity_and_corrupted_flag():
+    w = synth.workload("tiny")
+    inp = synth.make_inputs(w, seed=77)
+    topk = inp["topk_idx"]
+    S = 2
+    X = oracle.source_counts(topk, w.E, w.R, S)
+    cap = int(X["counts"].max()) - 3
+    ctx = run_sources(w, inp, S, cap=cap)
+    check_sources_layout(ctx, topk, w, S)
+    assert ep.ep_check_errors(ctx["ws"]) == ep.EP_DEVERR_CAPACITY
+    Sd = oracle.source_dispatch(topk, w.E, w.R, S, cap, ctx["epoch"], x=inp["x"], topk_w=inp["topk_w"])
+    assert Sd["err"] == oracle.ERR_CAPACITY
+    np.testing.assert_array_equal(host(ctx["staging"]), Sd["staging"])
+    # one stale flag word in a region row; a receive capacity below N
+    victim = (1 * S + 1) * cap + 2
+    ctx["staging"][victim, 512 + 480 + 4] ^= 1
+    st = Sd["staging"].copy()
+    st[victim, 512 + 480 + 4] ^= 1
+    N = int(X["recv_offsets"][-1])
+    ep.ep_clear_errors(ctx["ws"])
+    recv, _ = run_epilogue(ctx, capacity=N - 5)
+    Ce = oracle.copy_epilogue(X["recv_offsets"], st, w.H, w.K, w.R, S, cap, ctx["epoch"],
+                              recv_cap=N - 5)
+    assert Ce["err"] == oracle.ERR_CAPACITY | oracle.ERR_FLAG
+    assert ep.ep_check_errors(ctx["ws"]) == ep.EP_DEVERR_CAPACITY | ep.EP_DEVERR_FLAG
+    written = Ce["recv_src"] != -7
+    assert written.sum() < N - 5
+    # rows the epilogue skipped keep their poison
+    assert (host(recv["src_idx"])[~written].view(np.uint32) == 0xABABABAB).all()
+    for g, o in [("x", "recv_x"), ("src_idx", "recv_src"), ("topk_idx", "recv_topk_idx"),
+                 ("topk_weights", "recv_topk_w")]:
+        np.testing.assert_array_equal(host(recv[g])[written].view(np.uint8),
+                                      Ce[o][written].view(np.uint8), err_msg=g)
