@@ -58,17 +58,35 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash() -> str:
+# Source files behind each kernel whose traffic bench.py reports. A counter
+# summary stays valid while these files (and the shared headers and launch
+# code) are unchanged.
+KERNEL_FILES = {
+    "layout_*": ["layout.hip"],
+    "dispatch_kernel": ["dispatch.hip"],
+    "combine_kernel": ["combine.hip"],
+    "scaleout_kernel+forward_kernel": ["hier.hip"],
+    "scaleout_kernel": ["hier.hip"],
+    "copy_epilogue_kernel": ["source.hip"],
+    "combine_group_kernel+combine_cross_kernel": ["combine2.hip"],
+}
+COMMON_FILES = ["ep_device.h", "ep_internal.h", "api.hip"]
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """sha256 prefix of the sources `kernel` is built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_get_layout_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in COMMON_FILES + KERNEL_FILES[kernel]:
+        h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "ep.h"), "rb").read())
     return h.hexdigest()[:16]
 
 
 def committed_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None if there is none or it was taken from other kernel sources."""
+    None if there is none or it was taken from other sources of that kernel."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -76,10 +94,10 @@ def committed_traffic(workload: str, kernel: str):
         d = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if d.get("kernel_source_sha") != kernel_source_hash():
-        return None
     k = d.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    if k is None or k.get("source_sha") != kernel_source_hash(kernel):
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
 def main():
