@@ -11,8 +11,11 @@ A step is one pass of the whole path over one batch of synthetic tokens:
                      source) staging regions -> ep_copy_epilogue into dense
                      receive rows -> ep_combine over the staging rows
 Inputs are seeded and already resident in HBM when the timed region starts.
-W untimed warm-up steps, then exactly K timed steps between two device
-synchronisations. Prints one JSON line.
+W untimed warm-up steps; then K eager steps with every launch bracketed by
+events (the per-kernel durations); then, unless --eager, one HIP graph per
+input batch is captured and exactly K graph replays are timed between two
+device synchronisations: that is `value` and `ms_per_step`. Prints one JSON
+line.
 
 Also reported: per-kernel average durations from HIP events recorded on the
 stream the kernels run on, the roofline of the dominant kernel (algorithmic
@@ -51,6 +54,8 @@ def parse():
                    help="expand mode: one receive row per (token, lane), grouped by expert")
     p.add_argument("--sources", type=int, default=None, const=0, nargs="?",
                    help="several source ranks on one GPU (S; bare flag = one per rank)")
+    p.add_argument("--eager", action="store_true",
+                   help="time eager launches only (default: replay one HIP graph per step)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU-oracle baseline (0 = skip)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -215,14 +220,10 @@ def main():
         else:
             fn()
 
-    def step(record):
-        i = epoch[0] % n_batches
-        epoch[0] += 1
+    def run_step(i, e, record):
+        """One pass of the path over batch i with flag epoch e."""
         tokens, N, G_rows = batches[i], Ns[i], Gs[i]
-        if record:
-            used.append(i)
         if multi:
-            e = epoch[0]
             timed("layout", lambda: ep.ep_source_layout(shape, tokens["topk_idx"], src, ws), record)
             timed("send", lambda: ep.ep_source_dispatch(shape, src, tokens, e, staging, ws), record)
             timed("epilogue", lambda: ep.ep_copy_epilogue(shape, src, staging, e, seg, recv, N, ws),
@@ -234,15 +235,15 @@ def main():
         timed("layout", lambda: ep.ep_get_layout(shape, tokens["topk_idx"], L, ws), record)
         if hier:
             timed("hier", lambda: ep.ep_hierarchical_dispatch(
-                shape, L, tokens, epoch[0], ep.EP_HIER_SCALEOUT | ep.EP_HIER_FORWARD,
+                shape, L, tokens, e, ep.EP_HIER_SCALEOUT | ep.EP_HIER_FORWARD,
                 group_buf, G_rows, peer_buf, N, ws), record)
             if two_level:
                 timed("combine", lambda: ep.ep_combine_two_level(
-                    shape, L, tokens["topk_idx"], peer_buf, N, stride, ep.EP_FMT_CHUNKED, epoch[0],
+                    shape, L, tokens["topk_idx"], peer_buf, N, stride, ep.EP_FMT_CHUNKED, e,
                     tokens["topk_weights"], part_buf, G_rows, 3, out, ws), record)
             else:
                 timed("combine", lambda: ep.ep_combine(shape, L, peer_buf, N, stride, ep.EP_FMT_CHUNKED,
-                                                       epoch[0], tokens["topk_weights"], out, ws), record)
+                                                       e, tokens["topk_weights"], out, ws), record)
         elif expand:
             timed("dispatch", lambda: ep.ep_dispatch_expand(shape, L, tokens, recv, N, ws), record)
             timed("combine", lambda: ep.ep_combine_expand(shape, L, recv["x"], N, 2 * w.H,
@@ -253,27 +254,63 @@ def main():
             timed("combine", lambda: ep.ep_combine(shape, L, recv["x"], N, 2 * w.H, ep.EP_FMT_PLAIN,
                                                    0, tokens["topk_weights"], out, ws), record)
 
+    def step(record):
+        i = epoch[0] % n_batches
+        epoch[0] += 1
+        if record:
+            used.append(i)
+        run_step(i, epoch[0], record)
+
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
     if ep.ep_check_errors(ws) != 0:
         raise RuntimeError("device error bits set during warm-up")
 
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step(True)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
+    def timed_region(body):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        a.record(stream)
+        for k in range(args.steps):
+            body(k)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b), time.perf_counter() - w0
+
+    # Eager pass: every launch bracketed by events on the launch stream, for
+    # the per-kernel durations.
+    ms_eager, wall_eager = timed_region(lambda k: step(True))
     avg_ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
     if ep.ep_check_errors(ws) != 0:
         raise RuntimeError("device error bits set during the timed steps")
+
+    ms_total, wall = ms_eager, wall_eager
+    graph_used = not args.eager
+    if graph_used:
+        # One HIP graph per batch holding the whole step (its launches only:
+        # no memset or host work). Batch i's graph writes flag epoch 1000 + i,
+        # so consecutive replays (different batches) never share an epoch.
+        graphs = []
+        for i in range(n_batches):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(i, 1000 + i, False)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        used.clear()
+
+        def replay(k):
+            i = k % n_batches
+            used.append(i)
+            graphs[i].replay()
+
+        ms_total, wall = timed_region(replay)
+        if ep.ep_check_errors(ws) != 0:
+            raise RuntimeError("device error bits set during the graph replays")
+    ms_step = ms_total / args.steps
 
     # Algorithmic bytes per launch (what the method must move),
     # averaged over the batches the timed steps used.
@@ -334,6 +371,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_eager": ms_eager / args.steps,
+        "launch": "hip graph per step" if graph_used else "eager",
         "wall_s": wall,
         "higher_is_better": True,
         "scaling": "weak",

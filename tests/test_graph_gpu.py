@@ -1,0 +1,133 @@
+"""The path captured into a HIP graph (torch.cuda.CUDAGraph over the C ABI
+calls) and replayed several times, with eager work and synchronisations
+between the replays: every replay must equal the eager result bit for bit.
+The graph holds kernel launches only (the error word is cleared by the layout
+kernel, not by a memset)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from combine_get_layout_amd import ep
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ep.lib()
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.uint16)
+    return torch.from_numpy(a).cuda()
+
+
+def replay_and_compare(run, outputs, replays=3):
+    """run() enqueues the path; outputs are the tensors it writes."""
+    run()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for r in range(replays):
+        for o in outputs:  # eager work between replays: clobber every output
+            o.view(torch.uint8).fill_(0x5A + r)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, w) in enumerate(zip(outputs, want)):
+            assert torch.equal(o.view(torch.uint8), w.view(torch.uint8)), (r, i)
+
+
+def test_graph_flat_step():
+    w = synth.workload("ep32").scaled(1024)
+    inp = synth.make_inputs(w)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, 1)
+    L = ep.alloc_layout(shape, masks=True, groups=False, expand=True)
+    ws = ep.alloc_workspace(shape)
+    tk = dict(x=dev(inp["x"]), topk_idx=dev(inp["topk_idx"]), topk_weights=dev(inp["topk_w"]))
+    ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+    torch.cuda.synchronize()
+    N = int(L["rank_offsets"][-1].item())
+    NE = int(L["expert_offsets"][-1].item())
+    recv = ep.alloc_recv(shape, N)
+    recv_e = ep.alloc_recv(shape, NE)
+    out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
+    out_e = torch.empty_like(out)
+
+    def run():
+        ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+        ep.ep_dispatch(shape, L, tk, recv, N, ws)
+        ep.ep_combine(shape, L, recv["x"], N, 2 * w.H, ep.EP_FMT_PLAIN, 0, tk["topk_weights"], out, ws)
+        ep.ep_dispatch_expand(shape, L, tk, recv_e, NE, ws)
+        ep.ep_combine_expand(shape, L, recv_e["x"], NE, 2 * w.H, ep.EP_FMT_PLAIN, 0,
+                             tk["topk_weights"], out_e, ws)
+
+    outputs = [L["slot"], L["rank_offsets"], L["is_token_in_rank"], L["expert_slot"], out, out_e] + \
+        [recv[k][:N] for k in recv] + [recv_e[k][:NE] for k in recv_e]
+    replay_and_compare(run, outputs)
+    assert ep.ep_check_errors(ws) == 0
+
+
+def test_graph_two_level_step():
+    w = synth.workload("hier8x8").scaled(2048)
+    inp = synth.make_inputs(w)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, w.G)
+    L = ep.alloc_layout(shape, masks=False, groups=True)
+    ws = ep.alloc_workspace(shape)
+    tk = dict(x=dev(inp["x"]), topk_idx=dev(inp["topk_idx"]), topk_weights=dev(inp["topk_w"]))
+    ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+    torch.cuda.synchronize()
+    N = int(L["rank_offsets"][-1].item())
+    GR = int(L["group_offsets"][-1].item())
+    stride = ep.ep_chunked_record_bytes(shape, ep.EP_SEG_BF16)
+    gbuf = torch.zeros((GR, stride), dtype=torch.uint8, device="cuda")
+    pbuf = torch.zeros((N, stride), dtype=torch.uint8, device="cuda")
+    part = torch.zeros((GR, ep.ep_partial_row_bytes(shape)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
+    out2 = torch.empty_like(out)
+
+    def run():
+        ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+        ep.ep_hierarchical_dispatch(shape, L, tk, 7, 3, gbuf, GR, pbuf, N, ws)
+        ep.ep_combine(shape, L, pbuf, N, stride, ep.EP_FMT_CHUNKED, 7, tk["topk_weights"], out, ws)
+        ep.ep_combine_two_level(shape, L, tk["topk_idx"], pbuf, N, stride, ep.EP_FMT_CHUNKED, 7,
+                                tk["topk_weights"], part, GR, 3, out2, ws)
+
+    replay_and_compare(run, [L["slot"], L["group_slot"], gbuf, pbuf, part, out, out2])
+    assert ep.ep_check_errors(ws) == 0
+
+
+def test_graph_sources_step():
+    w = synth.workload("ep32").scaled(1024)
+    inp = synth.make_inputs(w)
+    S = 8
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, 1)
+    ws = ep.alloc_source_workspace(shape, S)
+    tk = dict(x=dev(inp["x"]), topk_idx=dev(inp["topk_idx"]), topk_weights=dev(inp["topk_w"]))
+    src = ep.alloc_sources(shape, S, -(-w.T // S))
+    stride = ep.ep_chunked_record_bytes(shape, ep.EP_SEG_BF16)
+    staging = torch.zeros((w.R * S * src["capacity"], stride), dtype=torch.uint8, device="cuda")
+    ep.ep_source_layout(shape, tk["topk_idx"], src, ws)
+    torch.cuda.synchronize()
+    N = int(src["recv_offsets"][-1].item())
+    recv = ep.alloc_recv(shape, N)
+    out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
+
+    def run():
+        ep.ep_source_layout(shape, tk["topk_idx"], src, ws)
+        ep.ep_source_dispatch(shape, src, tk, 3, staging, ws)
+        ep.ep_copy_epilogue(shape, src, staging, 3, ep.EP_SEG_BF16, recv, N, ws)
+        ep.ep_combine(shape, dict(slot=src["src_slot"]), staging, staging.shape[0], stride,
+                      ep.EP_FMT_CHUNKED, 3, tk["topk_weights"], out, ws)
+
+    outputs = [src["counts"], src["recv_offsets"], src["src_slot"], out] + [recv[k][:N] for k in recv]
+    replay_and_compare(run, outputs)
+    assert ep.ep_check_errors(ws) == 0
