@@ -37,6 +37,12 @@
 #ifndef EP_CMB_ROWS
 #define EP_CMB_ROWS 1       // row-streaming kernel: 1 = plain rows, 2 = plain and chunked rows
 #endif
+#ifndef EP_CMB_VPWMAX
+#define EP_CMB_VPWMAX 8     // row-streaming kernel: most wave-iterations per slice (4 or 8)
+#endif
+#ifndef EP_CMB_DUP
+#define EP_CMB_DUP 1        // row-streaming kernel: keep one repeated row in VGPRs instead of re-reading it
+#endif
 
 namespace ep {
 namespace {
@@ -284,6 +290,29 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(
             return;
         }
         const int s_any = readlane(s, __ffsll((unsigned long long)um) - 1);
+        // A rank reached by two lanes of the token shares one row. The first
+        // such row (lowest lane k1) is kept in VGPRs after its use, and the
+        // later lanes with the same row take it from there instead of
+        // loading it again (kept: lanes that read the kept copy).
+        uint64_t kept = 0;
+        int k1 = KMAX;
+#if EP_CMB_DUP
+        {
+            bool d = false;
+            for (int j = 0; j < a.K; ++j) {
+                const int sj = readlane(s, j);
+                if (j < lane && ((um >> j) & 1) && sj == s) d = true;
+            }
+            const uint64_t dupm = __ballot(use && d);
+            if (dupm) {
+                const int kd = __ffsll((unsigned long long)dupm) - 1;  // first repeating lane
+                const int sd = readlane(s, kd);
+                const uint64_t same = __ballot(use && s == sd);
+                k1 = __ffsll((unsigned long long)same) - 1;
+                kept = same & ~(1ull << k1);
+            }
+        }
+#endif
         float acc[VPW][8];
 #pragma unroll
         for (int j = 0; j < VPW; ++j)
@@ -291,6 +320,7 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(
             for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
         uint32_t bad = 0;
         u32x4 buf[2][VPW];
+        u32x4 keep[EP_CMB_DUP ? VPW : 1];
         auto row_of = [&](int k) {
             const int kk = min(k, a.K - 1);
             return a.y + (int64_t)(((um >> k) & 1) ? readlane(s, kk) : s_any) * a.stride;
@@ -302,16 +332,27 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(
         }
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (k + 1 < KMAX) {
+            if (k + 1 < KMAX && !((kept >> (k + 1)) & 1)) {
                 const uint8_t* rn = row_of(k + 1);
 #pragma unroll
                 for (int j = 0; j < VPW; ++j) buf[(k + 1) & 1][j] = ld_row(rn + off[j]);
             }
             const float wk = readlane_f(wt, min(k, a.K - 1));
             const bool uk = (um >> k) & 1;
+#if EP_CMB_DUP
+            const bool from_keep = (kept >> k) & 1;
+            if (k == k1) {
+#pragma unroll
+                for (int j = 0; j < VPW; ++j) keep[j] = buf[k & 1][j];
+            }
+#endif
 #pragma unroll
             for (int j = 0; j < VPW; ++j) {
+#if EP_CMB_DUP
+                const u32x4 v = from_keep ? keep[j] : buf[k & 1][j];
+#else
                 const u32x4 v = buf[k & 1][j];
+#endif
                 if (CHUNKED) {
                     const bool ok = v[0] == a.epoch && v[1] == a.epoch && v[2] == a.epoch && v[3] == a.epoch;
                     bad |= (flag[j] && !ok) ? (1u << k) : 0u;
@@ -359,7 +400,7 @@ hipError_t launch_k(const CombineArgs& a, hipStream_t st) {
     if (a.K <= 8 && (!CHUNKED || EP_CMB_ROWS >= 2)) {
         const int nch = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
         const int iters = CHUNKED ? (nch + 1) / 2 : (a.H / 8 + kWave - 1) / kWave;
-        const int vpw = iters > 8 ? 8 : 4;
+        const int vpw = iters > 8 && EP_CMB_VPWMAX >= 8 ? 8 : 4;
         const int slices = (iters + vpw - 1) / vpw;
         const dim3 grid((unsigned)(((int64_t)a.T * slices + kCmbWaves - 1) / kCmbWaves));
         if (vpw == 8)
