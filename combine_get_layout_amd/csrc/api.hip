@@ -13,17 +13,16 @@ static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 WsLayout ws_layout(const ep_shape& s) {
     WsLayout w;
     w.nb = s.T > 0 ? (s.T + kLayoutTokens - 1) / kLayoutTokens : 1;
+    w.rp = (s.R + 3) / 4 * 4;
+    w.gp = (s.G + 3) / 4 * 4;
+    w.wrow = 2 * w.rp + w.gp;
     size_t off = 0;
     w.err = off;
     off += 256;
-    w.part_rank = off;
-    off += align256(sizeof(int32_t) * (size_t)w.nb * s.R);
-    w.part_group = off;
-    off += align256(sizeof(int32_t) * (size_t)w.nb * s.G);
+    w.part_rlg = off;
+    off += align256(sizeof(int32_t) * (size_t)w.nb * w.wrow);
     w.part_expert = off;
     off += align256(sizeof(int32_t) * (size_t)w.nb * s.E);
-    w.part_lanes = off;
-    off += align256(sizeof(int32_t) * (size_t)w.nb * s.R);
     w.total = off;
     return w;
 }

@@ -16,11 +16,14 @@ constexpr int kLayoutTokens = 256;  // tokens per layout workgroup (one per thre
 // Workspace carve-up (byte offsets from the workspace base).
 struct WsLayout {
     int nb;                 // layout workgroups = max(1, ceil(T / kLayoutTokens))
+    int rp, gp;             // R and G rounded up to multiples of 4
+    int wrow;               // ints per row of the rank/lane/group table: 2 * rp + gp
     size_t err;             // uint32 error word
-    size_t part_rank;       // int32 [nb][R]  per-block counts -> block-exclusive prefix
-    size_t part_group;      // int32 [nb][G]
-    size_t part_expert;     // int32 [nb][E]
-    size_t part_lanes;      // int32 [nb][R]  valid lanes per rank
+    // Per-workgroup count tables, one row per layout workgroup (row-major):
+    size_t part_rlg;        // int32 [nb][wrow]: deduplicated tokens per rank (columns
+                            // [0, R)), valid lanes per rank ([rp, rp + R)) and
+                            // deduplicated tokens per group ([2 rp, 2 rp + G))
+    size_t part_expert;     // int32 [nb][E] lanes per expert
     size_t total;
 };
 WsLayout ws_layout(const ep_shape& s);

@@ -26,6 +26,7 @@
 //               other and no grid-wide fence is needed (the launch boundary
 //               orders the two kernels).
 #include <rocprim/block/block_radix_sort.hpp>
+#include <rocprim/warp/warp_scan.hpp>
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -37,12 +38,12 @@ constexpr int kWords = kLayoutTokens / 32;  // bit-matrix words per rank per wor
 
 struct LayoutArgs {
     int T, K, E, R, G, epr, P, nb;
+    int rp, wrow;            // rank/lane/group table: lanes start at column rp, groups at 2 rp
     const int64_t* topk;
     uint32_t* err;
-    int32_t* part_rank;      // [nb][R] per-workgroup counts
-    int32_t* part_group;     // [nb][G]
-    int32_t* part_expert;    // [nb][E]
-    int32_t* part_lanes;     // [nb][R] valid lanes per rank (not deduplicated)
+    // Per-workgroup count tables, one row per workgroup:
+    int32_t* part_rlg;       // [nb][wrow] ranks | lanes per rank | groups
+    int32_t* part_expert;    // [nb][E] lanes per expert
     ep_layout out;
 };
 
@@ -63,8 +64,14 @@ struct TokenIds {
     }
 };
 
-// Set this token's bit for every rank (and group) its valid lanes reach and
-// count its experts. Returns whether any lane held an invalid id.
+// Set this token's bit for every rank its valid lanes reach (LDS atomics: a
+// repeated rank sets the same bit) and, with cnt_e, count its experts. The
+// group bits: with one group, bit (0, t) is "the token has a valid lane",
+// written by the wave from one ballot (lane 0 holds the word of lanes 0-31,
+// lane 32 that of lanes 32-63; tokens past T form a suffix of inactive
+// lanes, so both writers are active whenever their half has a token); with
+// several groups, LDS atomics as for ranks. Returns whether any lane held an
+// invalid id.
 template <int KMAX>
 __device__ __forceinline__ bool mark_token(const LayoutArgs& a, const TokenIds<KMAX>& ids,
                                            const int64_t* row, uint32_t* bits_r, uint32_t* bits_g,
@@ -72,17 +79,24 @@ __device__ __forceinline__ bool mark_token(const LayoutArgs& a, const TokenIds<K
     const int w = threadIdx.x / 32;
     const uint32_t bit = 1u << (threadIdx.x & 31);
     const int kn = KMAX > 0 ? KMAX : a.K;
-    bool bad = false;
+    const bool group_atomics = bits_g && a.G > 1;
+    bool bad = false, any = false;
 #pragma unroll
     for (int k = 0; k < kn; ++k) {
         if (KMAX > 0 && k >= a.K) break;
         const int64_t e = ids.get(row, k);
         bad |= expert_bad(e, a.E);
         if (!expert_ok(e, a.E)) continue;
+        any = true;
         const int r = (int)e / a.epr;
         atomicOr(&bits_r[r * kWords + w], bit);
-        if (bits_g) atomicOr(&bits_g[(r / a.P) * kWords + w], bit);
+        if (group_atomics) atomicOr(&bits_g[(r / a.P) * kWords + w], bit);
         if (cnt_e) atomicAdd(&cnt_e[(int)e], 1);
+    }
+    if (bits_g && a.G == 1) {
+        const uint64_t m = __ballot(any);
+        const int lane = lane_id();
+        if (lane == 0 || lane == 32) bits_g[w] = (uint32_t)(m >> lane);
     }
     return bad;
 }
@@ -136,231 +150,383 @@ __global__ __launch_bounds__(kBlockThreads) void layout_count_kernel(LayoutArgs 
     if (t < a.T) mark_token<KMAX>(a, ids, row, bits_r, bits_g, cnt_e);
     __syncthreads();
 
-    for (int c = threadIdx.x; c < a.R; c += kBlockThreads)
-        a.part_rank[(int64_t)b * a.R + c] = popc_row(bits_r, c);
-    for (int c = threadIdx.x; c < a.G; c += kBlockThreads)
-        a.part_group[(int64_t)b * a.G + c] = popc_row(bits_g, c);
-    for (int c = threadIdx.x; c < a.E; c += kBlockThreads)
-        a.part_expert[(int64_t)b * a.E + c] = cnt_e[c];
+    int32_t* rlg = a.part_rlg + (int64_t)b * a.wrow;
     for (int c = threadIdx.x; c < a.R; c += kBlockThreads) {
+        rlg[c] = popc_row(bits_r, c);
         int lanes = 0;
         for (int e = c * a.epr; e < (c + 1) * a.epr; ++e) lanes += cnt_e[e];
-        a.part_lanes[(int64_t)b * a.R + c] = lanes;
+        rlg[a.rp + c] = lanes;
     }
+    for (int c = threadIdx.x; c < a.G; c += kBlockThreads) rlg[2 * a.rp + c] = popc_row(bits_g, c);
+    for (int c = threadIdx.x; c < a.E; c += kBlockThreads)
+        a.part_expert[(int64_t)b * a.E + c] = cnt_e[c];
 
     const int nt = min(kLayoutTokens, a.T - t0);
     if (nt > 0 && a.out.is_token_in_rank) write_mask(bits_r, a.R, t0, nt, a.out.is_token_in_rank);
     if (nt > 0 && a.out.is_token_in_group) write_mask(bits_g, a.G, t0, nt, a.out.is_token_in_group);
 }
 
-// Inclusive scan of one int across the 64 lanes of a wave.
+// Inclusive scan of one int across the 64 lanes of a wave (rocPRIM's
+// cross-lane scan: DPP row shifts and row broadcasts, no LDS round trips).
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    return x;
+    using scan_t = rocprim::warp_scan<int, kWave>;
+    static_assert(sizeof(scan_t::storage_type) <= 1, "cross-lane scan: no shared storage");
+    scan_t::storage_type none;
+    int y;
+    scan_t().inclusive_scan(x, y, none, rocprim::plus<int>());
+    return y;
 }
 
-// Workgroup-wide exclusive scan where thread i owns the contiguous elements
-// [i*per, min(n, (i+1)*per)) through get(i) / put(i, prefix). Returns the
-// total. scratch: kWavesPerBlock ints of LDS. Contains two barriers.
-template <typename Get, typename Put>
-__device__ int block_scan(int n, Get get, Put put, int* scratch) {
-    const int tid = threadIdx.x;
-    const int per = (n + kBlockThreads - 1) / kBlockThreads;
-    const int lo = min(n, tid * per), hi = min(n, lo + per);
-    int s = 0;
-    for (int i = lo; i < hi; ++i) s += get(i);
-    const int inc = wave_inclusive_scan(s);
-    if (lane_id() == kWave - 1) scratch[wave_in_block()] = inc;
-    __syncthreads();
-    int before = 0, total = 0;
+// The assign kernel's ownership of table columns:
+//   * vector v = q*256 + thread (round q) of a rank/lane/group row: columns
+//     4v .. 4v+3, all in one section since rp and gp are multiples of 4;
+//   * column q*256 + thread of this workgroup's slice of experts.
+constexpr int kVecRounds = (2 * EP_MAX_RANKS + EP_MAX_GROUPS + 4 * kBlockThreads - 1) / (4 * kBlockThreads);
+constexpr int kSliceRounds = EP_MAX_EXPERTS / kBlockThreads;
+constexpr int kRowBatch = 8;  // table rows (workgroups) loaded per batch (measured best of 8, 16, 32)
+// Scan slots of the LDS scratch, one int per wave each.
+constexpr int kScRank = 0;                          // rank totals, per vector round
+constexpr int kScLane = kScRank + kVecRounds;       // lane totals, per vector round
+constexpr int kScGroup = kScLane + kVecRounds;      // group totals, per vector round
+constexpr int kScSlice = kScGroup + kVecRounds;     // expert slice totals, per slice round
+constexpr int kScLaneStart = kScSlice + kSliceRounds;  // lanes of the ranks before the slice
+constexpr int kScSlots = kScLaneStart + 1;
+
+// Workgroup-wide exclusive prefix of the value x that this thread holds in
+// round q, from its wave-inclusive scan `inc` and the per-wave totals of
+// every round in sc[round * waves + wave]. Also returns the grand total.
+template <int NR>
+__device__ __forceinline__ int round_prefix(const int32_t* sc, int nr, int q, int inc, int x,
+                                            int& total) {
+    int before = 0;
+    total = 0;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-        const int v = scratch[w];
-        before += w < wave_in_block() ? v : 0;
-        total += v;
+    for (int j = 0; j < NR; ++j) {
+        if (j >= nr) break;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+            const int y = sc[j * kWavesPerBlock + w];
+            total += y;
+            before += (j < q || (j == q && w < wave_in_block())) ? y : 0;
+        }
     }
-    int run = before + inc - s;
-    for (int i = lo; i < hi; ++i) {
-        const int v = get(i);
-        put(i, run);
-        run += v;
-    }
-    __syncthreads();
-    return total;
+    return before + inc - x;
 }
 
-constexpr int kMaxSliceRounds = EP_MAX_EXPERTS / kBlockThreads;
+// Running sums over the rows of a batch: rows < b (earlier workgroups) and
+// rows < nb (all); clamped repeats past the last row are masked.
+__device__ __forceinline__ void add_rows(const u32x4* x, int b0, int b, int nb, int (&bef)[4],
+                                         int (&all)[4]) {
+#pragma unroll
+    for (int j = 0; j < kRowBatch; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bef[i] += b0 + j < b ? (int)x[j][i] : 0;
+            all[i] += b0 + j < nb ? (int)x[j][i] : 0;
+        }
+    }
+}
 
 template <int KMAX>
 __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs a) {
     extern __shared__ uint32_t lds[];
-    uint32_t* bits_r = lds;
-    uint32_t* bits_g = bits_r + a.R * kWords;
+    uint32_t* bits_r = lds;                                                // [R][kWords]
+    uint32_t* bits_g = bits_r + a.R * kWords;                              // [G][kWords]
     int32_t* base_r = reinterpret_cast<int32_t*>(bits_g + a.G * kWords);  // [R]
-    int32_t* tot_r = base_r + a.R;                                        // [R]
-    int32_t* lane_base = tot_r + a.R;                                     // [R]
-    int32_t* base_g = lane_base + a.R;                                    // [G]
-    int32_t* tot_g = base_g + a.G;                                        // [G]
-    int32_t* scratch = tot_g + a.G;                                       // [waves + 1]
+    int32_t* base_g = base_r + a.R;                                        // [G]
+    int32_t* scratch = base_g + a.G;                                       // [kScSlots][waves]
+    uint8_t* pre_r = reinterpret_cast<uint8_t*>(scratch + kScSlots * kWavesPerBlock);  // [R][kWords]
+    uint8_t* pre_g = pre_r + a.R * kWords;                                 // [G][kWords]
     const int b = blockIdx.x;
+    const int tid = threadIdx.x;
     const bool groups = a.out.group_slot != nullptr;
     const int t0 = b * kLayoutTokens;
-    const int t = t0 + threadIdx.x;
+    const int t = t0 + tid;
     const int64_t* row = a.topk + (int64_t)t * a.K;
 
-    // Every global read this workgroup needs is issued first and together: the
-    // token's ids, and for column c of each count table (ranks, lanes, groups,
-    // this workgroup's slice of experts) the sums over the earlier workgroups
-    // and over all of them. Column and row indices are clamped so that every
-    // load is unconditional; out-of-range terms are masked from the sums.
+    // The token's ids first; the bit matrices are cleared while they are in
+    // flight.
     TokenIds<KMAX> ids;
     if (t < a.T) ids.load(row, a.K);
+    for (int i = tid; i < (a.R + a.G) * kWords; i += kBlockThreads) lds[i] = 0u;
+    for (int i = tid; i < kScSlots * kWavesPerBlock; i += kBlockThreads) scratch[i] = 0;
+
+    // Count tables. The rank/lane/group rows are read as 16-byte vectors,
+    // thread v taking vector v of every row, so a wave's load is 1 KiB of one
+    // row. The slice of experts this workgroup owns (the experts of ranks
+    // [r0, r1)) is read one column per thread. Round 0 of both is loaded in
+    // the same batches; every load of a batch is unconditional (rows clamped,
+    // repeats masked). For each column the sums over the earlier workgroups
+    // (bef) and over all of them (all, etot) are kept.
     int32_t* te = a.out.tokens_per_expert;
     int32_t* eo = a.out.expert_offsets;
     const bool experts = te || eo;
     const int rpb = (a.R + a.nb - 1) / a.nb;
     const int r0 = min(a.R, b * rpb), r1 = min(a.R, r0 + rpb);
     const int e0 = r0 * a.epr, ne = experts ? (r1 - r0) * a.epr : 0;
-    const int ncols = max(max(a.R, a.G), ne);
-    int etot[kMaxSliceRounds];
+    const int nvec = a.wrow / 4;
+    const int vec_rounds = (nvec + kBlockThreads - 1) / kBlockThreads;
+    const int slice_rounds = (ne + kBlockThreads - 1) / kBlockThreads;
+    const bool expand = a.out.expert_slot != nullptr;
+    int bef[kVecRounds][4], all[kVecRounds][4], etot[kSliceRounds];
 #pragma unroll
-    for (int j = 0; j < kMaxSliceRounds; ++j) etot[j] = 0;
-    for (int c = threadIdx.x, round = 0; c < ncols; c += kBlockThreads, ++round) {
-        const int cr = min(c, a.R - 1), cg = min(c, a.G - 1);
-        const int ce = min(e0 + c, a.E - 1);
-        constexpr int kBatch = 16;
-        const bool own_e = c < ne && a.out.expert_slot != nullptr;
-        int rb = 0, ra = 0, la = 0, gb = 0, ga = 0, ea = 0;
-        for (int b0 = 0; b0 < a.nb; b0 += kBatch) {
-            int32_t vr[kBatch], vl[kBatch], vg[kBatch], ve[kBatch];
+    for (int q = 0; q < kVecRounds; ++q)
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int64_t rowj = min(b0 + j, a.nb - 1);
-                vr[j] = a.part_rank[rowj * a.R + cr];
-                vl[j] = a.part_lanes[rowj * a.R + cr];
-                vg[j] = a.part_group[rowj * a.G + cg];
-                ve[j] = a.part_expert[rowj * a.E + ce];
+        for (int i = 0; i < 4; ++i) bef[q][i] = all[q][i] = 0;
+#pragma unroll
+    for (int q = 0; q < kSliceRounds; ++q) etot[q] = 0;
+    // Expert column c of the slice: its total; in expand mode the column is
+    // rewritten in place as the exclusive prefix over workgroups (each expert
+    // column is owned by one workgroup).
+    auto expert_rows = [&](const int32_t* x, int32_t* pe, int b0, bool own, int& ea) {
+#pragma unroll
+        for (int j = 0; j < kRowBatch; ++j) {
+            if (own && b0 + j < a.nb) pe[(int64_t)(b0 + j) * a.E] = ea;
+            ea += b0 + j < a.nb ? x[j] : 0;
+        }
+    };
+    {
+        const int v = min(tid, nvec - 1);
+        const int32_t* pv = a.part_rlg + 4 * v;
+        const bool own = tid < ne && expand;
+        int32_t* pe = a.part_expert + min(e0 + tid, a.E - 1);
+        int ea = 0;
+        for (int b0 = 0; b0 < a.nb; b0 += kRowBatch) {
+            u32x4 x[kRowBatch];
+            int32_t xe[kRowBatch];
+#pragma unroll
+            for (int j = 0; j < kRowBatch; ++j) {
+                const int64_t rj = min(b0 + j, a.nb - 1);
+                x[j] = ld16(pv + rj * a.wrow);
+                xe[j] = pe[rj * a.E];
             }
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const bool in = b0 + j < a.nb, early = b0 + j < b;
-                rb += early ? vr[j] : 0;
-                ra += in ? vr[j] : 0;
-                la += in ? vl[j] : 0;
-                gb += early ? vg[j] : 0;
-                ga += in ? vg[j] : 0;
-                // Expand mode: this column becomes the exclusive prefix over
-                // workgroups (each expert column is owned by one workgroup).
-                if (own_e && in) a.part_expert[(int64_t)(b0 + j) * a.E + ce] = ea;
-                ea += in ? ve[j] : 0;
-            }
+            add_rows(x, b0, b, a.nb, bef[0], all[0]);
+            expert_rows(xe, pe, b0, own, ea);
         }
-        if (c < a.R) {
-            base_r[c] = rb;
-            tot_r[c] = ra;
-            lane_base[c] = la;
-        }
-        if (c < a.G) {
-            base_g[c] = gb;
-            tot_g[c] = ga;
-        }
-        if (c < ne) {
-#pragma unroll
-            for (int j = 0; j < kMaxSliceRounds; ++j)
-                if (j == round) etot[j] = ea;
-            if (te) te[e0 + c] = ea;
+        if (tid < ne) {
+            etot[0] = ea;
+            if (te) te[e0 + tid] = ea;
         }
     }
-
-    for (int i = threadIdx.x; i < (a.R + a.G) * kWords; i += kBlockThreads) lds[i] = 0u;
+    // Further rounds: only for tables wider than 1,024 columns or slices
+    // wider than 256 experts.
+#pragma unroll
+    for (int q = 1; q < kVecRounds; ++q) {
+        if (q < vec_rounds) {
+            const int32_t* pv = a.part_rlg + 4 * min(q * kBlockThreads + tid, nvec - 1);
+            for (int b0 = 0; b0 < a.nb; b0 += kRowBatch) {
+                u32x4 x[kRowBatch];
+#pragma unroll
+                for (int j = 0; j < kRowBatch; ++j) x[j] = ld16(pv + (int64_t)min(b0 + j, a.nb - 1) * a.wrow);
+                add_rows(x, b0, b, a.nb, bef[q], all[q]);
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 1; q < kSliceRounds; ++q) {
+        if (q < slice_rounds) {
+            const int c = q * kBlockThreads + tid;
+            const bool own = c < ne && expand;
+            int32_t* pe = a.part_expert + min(e0 + c, a.E - 1);
+            int ea = 0;
+            for (int b0 = 0; b0 < a.nb; b0 += kRowBatch) {
+                int32_t xe[kRowBatch];
+#pragma unroll
+                for (int j = 0; j < kRowBatch; ++j) xe[j] = pe[(int64_t)min(b0 + j, a.nb - 1) * a.E];
+                expert_rows(xe, pe, b0, own, ea);
+            }
+            if (c < ne) {
+                etot[q] = ea;
+                if (te) te[e0 + c] = ea;
+            }
+        }
+    }
     __syncthreads();
+
     bool bad = false;
     if (t < a.T) bad = mark_token<KMAX>(a, ids, row, bits_r, groups ? bits_g : nullptr, nullptr);
 
-    // Region starts = exclusive scan of the totals; workgroup 0 publishes the
-    // counts and offsets.
+    // The section of this thread's vector in round q (0 ranks, 1 lanes,
+    // 2 groups, -1 none), its first column inside the section, and whether
+    // column i of the vector is a real column (padding columns are masked).
+    auto section = [&](int q, int& col0) {
+        const int v = q * kBlockThreads + tid;
+        const int c4 = 4 * v;
+        if (v >= nvec) { col0 = 0; return -1; }
+        if (c4 < a.rp) { col0 = c4; return 0; }
+        if (c4 < 2 * a.rp) { col0 = c4 - a.rp; return 1; }
+        col0 = c4 - 2 * a.rp;
+        return 2;
+    };
+    auto col_ok = [&](int sec, int col) { return sec >= 0 && col < (sec == 2 ? a.G : a.R); };
+
+    // Wave scans of the section totals and of the expert slice; the wave
+    // totals go to the scratch slots. The lanes of the ranks before this
+    // workgroup's slice (r < r0) are one more workgroup-wide sum.
+    int inc[kVecRounds], tot[kVecRounds], inc_e[kSliceRounds];
+    int before_slice = 0;
+    const bool last_lane = lane_id() == kWave - 1;
+    const int wv = wave_in_block();
+#pragma unroll
+    for (int q = 0; q < kVecRounds; ++q) {
+        inc[q] = tot[q] = 0;
+        if (q >= vec_rounds) continue;
+        int col0;
+        const int sec = section(q, col0);
+        int x = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int v = col_ok(sec, col0 + i) ? all[q][i] : 0;
+            x += v;
+            before_slice += sec == 1 && col0 + i < r0 ? v : 0;
+        }
+        tot[q] = x;
+        const int xr = wave_inclusive_scan(sec == 0 ? x : 0);
+        const int xl = wave_inclusive_scan(sec == 1 ? x : 0);
+        const int xg = wave_inclusive_scan(sec == 2 ? x : 0);
+        inc[q] = sec == 0 ? xr : (sec == 1 ? xl : xg);
+        if (last_lane) {
+            scratch[(kScRank + q) * kWavesPerBlock + wv] = xr;
+            scratch[(kScLane + q) * kWavesPerBlock + wv] = xl;
+            scratch[(kScGroup + q) * kWavesPerBlock + wv] = xg;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kSliceRounds; ++q) {
+        inc_e[q] = 0;
+        if (q >= slice_rounds) continue;
+        inc_e[q] = wave_inclusive_scan(etot[q]);
+        if (last_lane) scratch[(kScSlice + q) * kWavesPerBlock + wv] = inc_e[q];
+    }
+    before_slice = wave_inclusive_scan(before_slice);
+    if (last_lane) scratch[kScLaneStart * kWavesPerBlock + wv] = before_slice;
+    __syncthreads();
+
+    // Region starts. Each owned rank (group) column gets its first row for
+    // this workgroup, base = region start + earlier workgroups, and the u8
+    // count of this workgroup's tokens to it before each 32-token word.
+    // Workgroup 0 publishes the counts and offsets.
     const bool pub = b == 0;
     int32_t* ro = a.out.rank_offsets;
     int32_t* go = a.out.group_offsets;
-    const int n_rows = block_scan(
-        a.R, [&](int i) { return tot_r[i]; },
-        [&](int i, int p) {
-            base_r[i] += p;
-            if (pub && ro) ro[i] = p;
-            if (pub && a.out.tokens_per_rank) a.out.tokens_per_rank[i] = tot_r[i];
-        },
-        scratch);
-    const int n_grows = block_scan(
-        a.G, [&](int i) { return tot_g[i]; },
-        [&](int i, int p) {
-            base_g[i] += p;
-            if (pub && go) go[i] = p;
-            if (pub && a.out.tokens_per_group) a.out.tokens_per_group[i] = tot_g[i];
-        },
-        scratch);
-    // lane_base: lane totals -> exclusive prefix (in place; each thread owns its chunk)
-    const int n_lanes = block_scan(
-        a.R, [&](int i) { return lane_base[i]; }, [&](int i, int p) { lane_base[i] = p; }, scratch);
-    if (pub && threadIdx.x == 0) {
-        if (ro) ro[a.R] = n_rows;
-        if (go) go[a.G] = n_grows;
-        if (eo) eo[a.E] = n_lanes;
-    }
-
-    if (bad) report(a.err, EP_DEVERR_EXPERT_ID);
-    if (t < a.T) {
-        const int w = threadIdx.x / 32;
-        const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
-        const int kn = KMAX > 0 ? KMAX : a.K;
 #pragma unroll
-        for (int k = 0; k < kn; ++k) {
-            if (KMAX > 0 && k >= a.K) break;
-            const int64_t e = ids.get(row, k);
-            int32_t s = -1, gs = -1;
-            if (expert_ok(e, a.E)) {
-                const int r = (int)e / a.epr;
-                int pre = __popc(bits_r[r * kWords + w] & below);
-                for (int j = 0; j < w; ++j) pre += __popc(bits_r[r * kWords + j]);
-                s = base_r[r] + pre;
-                if (groups) {
-                    const int g = r / a.P;
-                    int gpre = __popc(bits_g[g * kWords + w] & below);
-                    for (int j = 0; j < w; ++j) gpre += __popc(bits_g[g * kWords + j]);
-                    gs = base_g[g] + gpre;
+    for (int q = 0; q < kVecRounds; ++q) {
+        if (q >= vec_rounds) break;
+        int col0;
+        const int sec = section(q, col0);
+        if (sec < 0) continue;
+        const int sc = sec == 0 ? kScRank : (sec == 1 ? kScLane : kScGroup);
+        // Exclusive prefix of this thread's vector within its section, over
+        // the rounds and waves before it, and the section total.
+        int run = 0, total = 0;
+        for (int j = 0; j < vec_rounds; ++j) {
+#pragma unroll
+            for (int w = 0; w < kWavesPerBlock; ++w) {
+                const int y = scratch[(sc + j) * kWavesPerBlock + w];
+                total += y;
+                run += (j < q || (j == q && w < wv)) ? y : 0;
+            }
+        }
+        run += inc[q] - tot[q];
+        if (sec == 1) {
+            if (pub && eo && col_ok(sec, col0) && col0 + 4 >= a.R && col0 < a.R) eo[a.E] = total;
+            continue;
+        }
+        uint32_t* bits = sec == 0 ? bits_r : bits_g;
+        int32_t* base = sec == 0 ? base_r : base_g;
+        uint8_t* pre = sec == 0 ? pre_r : pre_g;
+        int32_t* off = sec == 0 ? ro : go;
+        int32_t* cnt = sec == 0 ? a.out.tokens_per_rank : a.out.tokens_per_group;
+        const int n = sec == 0 ? a.R : a.G;
+        const bool want_pre = sec == 0 || groups;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = col0 + i;
+            if (c >= n) break;
+            base[c] = run + bef[q][i];
+            if (want_pre) {
+                int p = 0;
+#pragma unroll
+                for (int w = 0; w < kWords; ++w) {
+                    pre[c * kWords + w] = (uint8_t)p;
+                    p += __popc(bits[c * kWords + w]);
                 }
             }
-            if (a.out.slot) a.out.slot[(int64_t)t * a.K + k] = s;
-            if (groups) a.out.group_slot[(int64_t)t * a.K + k] = gs;
+            if (pub) {
+                if (off) off[c] = run;
+                if (cnt) cnt[c] = all[q][i];
+                if (off && c == n - 1) off[n] = total;
+            }
+            run += all[q][i];
         }
     }
-
-    // Expert offsets of this workgroup's slice of ranks: lanes of the earlier
-    // ranks + prefix inside the slice (column c of the slice sits in round
-    // c / 256 of thread c % 256).
-    if (!eo || ne == 0) return;
-    int carry = lane_base[r0];
+    // Expert offsets of this workgroup's slice: lanes of the ranks before the
+    // slice + prefix inside the slice.
+    if (eo && ne > 0) {
+        int lane_start = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxSliceRounds; ++j) {
-        if (j * kBlockThreads >= ne) break;
-        const int v = etot[j];
-        const int inc = wave_inclusive_scan(v);
-        if (lane_id() == kWave - 1) scratch[wave_in_block()] = inc;
-        __syncthreads();
-        int before = 0, total = 0;
+        for (int w = 0; w < kWavesPerBlock; ++w) lane_start += scratch[kScLaneStart * kWavesPerBlock + w];
 #pragma unroll
-        for (int w = 0; w < kWavesPerBlock; ++w) {
-            before += w < wave_in_block() ? scratch[w] : 0;
-            total += scratch[w];
+        for (int q = 0; q < kSliceRounds; ++q) {
+            const int c = q * kBlockThreads + tid;
+            if (q >= slice_rounds) break;
+            int unused;
+            const int p = round_prefix<kSliceRounds>(scratch + kScSlice * kWavesPerBlock, slice_rounds, q,
+                                                      inc_e[q], etot[q], unused);
+            if (c < ne) eo[e0 + c] = lane_start + p;
         }
-        const int c = j * kBlockThreads + threadIdx.x;
-        if (c < ne) eo[e0 + c] = carry + before + inc - v;
-        carry += total;
-        __syncthreads();
+    }
+    __syncthreads();
+
+    if (bad) report(a.err, EP_DEVERR_EXPERT_ID);
+    if (t >= a.T) return;
+    // Slot of lane k = base of its rank + tokens of this workgroup to that
+    // rank in earlier words + earlier tokens of its own word.
+    const int w = tid / 32;
+    const uint32_t below = (1u << (tid & 31)) - 1u;
+    auto slot_of = [&](int64_t e, int32_t& s, int32_t& gs) {
+        s = gs = -1;
+        if (!expert_ok(e, a.E)) return;
+        const int r = (int)e / a.epr;
+        s = base_r[r] + pre_r[r * kWords + w] + __popc(bits_r[r * kWords + w] & below);
+        if (groups) {
+            const int g = r / a.P;
+            gs = base_g[g] + pre_g[g * kWords + w] + __popc(bits_g[g * kWords + w] & below);
+        }
+    };
+    if constexpr (KMAX == 4 || KMAX == 8) {
+        // Whole rows of 16-byte vectors when they are aligned (t*K*4 bytes is
+        // a multiple of 16 for K = 4 and 8).
+        const bool vec = a.K == KMAX && (reinterpret_cast<uintptr_t>(a.out.slot) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(a.out.group_slot) & 15) == 0;
+        if (vec) {
+            int32_t s[KMAX], gs[KMAX];
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) slot_of(ids.get(row, k), s[k], gs[k]);
+#pragma unroll
+            for (int v = 0; v < KMAX / 4; ++v) {
+                if (a.out.slot) {
+                    u32x4 o = {(uint32_t)s[4 * v], (uint32_t)s[4 * v + 1], (uint32_t)s[4 * v + 2],
+                               (uint32_t)s[4 * v + 3]};
+                    st16(a.out.slot + (int64_t)t * a.K + 4 * v, o);
+                }
+                if (groups) {
+                    u32x4 o = {(uint32_t)gs[4 * v], (uint32_t)gs[4 * v + 1],
+                               (uint32_t)gs[4 * v + 2], (uint32_t)gs[4 * v + 3]};
+                    st16(a.out.group_slot + (int64_t)t * a.K + 4 * v, o);
+                }
+            }
+            return;
+        }
+    }
+    const int kn = KMAX > 0 ? KMAX : a.K;
+#pragma unroll
+    for (int k = 0; k < kn; ++k) {
+        if (KMAX > 0 && k >= a.K) break;
+        int32_t s, gs;
+        slot_of(ids.get(row, k), s, gs);
+        if (a.out.slot) a.out.slot[(int64_t)t * a.K + k] = s;
+        if (groups) a.out.group_slot[(int64_t)t * a.K + k] = gs;
     }
 }
 
@@ -423,17 +589,17 @@ hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout
     LayoutArgs a;
     a.T = s.T; a.K = s.K; a.E = s.E; a.R = s.R; a.G = s.G;
     a.epr = s.E / s.R; a.P = s.R / s.G; a.nb = W.nb;
+    a.rp = W.rp; a.wrow = W.wrow;
     a.topk = topk;
     a.err = reinterpret_cast<uint32_t*>(ws + W.err);
-    a.part_rank = reinterpret_cast<int32_t*>(ws + W.part_rank);
-    a.part_group = reinterpret_cast<int32_t*>(ws + W.part_group);
+    a.part_rlg = reinterpret_cast<int32_t*>(ws + W.part_rlg);
     a.part_expert = reinterpret_cast<int32_t*>(ws + W.part_expert);
-    a.part_lanes = reinterpret_cast<int32_t*>(ws + W.part_lanes);
     a.out = L;
 
     const size_t lds_count = sizeof(uint32_t) * ((size_t)(s.R + s.G) * kWords + s.E);
-    const size_t lds_assign = sizeof(uint32_t) * ((size_t)(s.R + s.G) * kWords + 3 * (size_t)s.R +
-                                                  2 * (size_t)s.G + kWavesPerBlock + 1);
+    const size_t lds_assign = sizeof(uint32_t) * ((size_t)(s.R + s.G) * kWords + s.R + s.G +
+                                                  (size_t)kScSlots * kWavesPerBlock) +
+                              (size_t)(s.R + s.G) * kWords;
     const dim3 grid(W.nb), block(kBlockThreads);
 #define EP_LAYOUT_LAUNCH(KM)                                                          \
     do {                                                                              \
