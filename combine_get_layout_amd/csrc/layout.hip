@@ -25,6 +25,8 @@
 //               every workgroup already sums. Workgroups never wait for each
 //               other and no grid-wide fence is needed (the launch boundary
 //               orders the two kernels).
+#include <algorithm>
+
 #include <rocprim/block/block_radix_sort.hpp>
 #include <rocprim/warp/warp_scan.hpp>
 
@@ -530,40 +532,89 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
     }
 }
 
-// Expand-mode rows: the (token, lane) entries of a 256-token workgroup are
-// sorted by expert, stably (entries keep token-then-lane order inside an
-// expert), with a block radix sort in LDS. The row of an entry is
-//   expert_offsets[e] + (lanes of e in earlier workgroups) + (position of the
-//   entry among the workgroup's entries of e).
+// Expand-mode rows. The row of entry (t, k) with expert e is
+//   expert_offsets[e] + (lanes of e in earlier workgroups)
+//                     + (entries of e before (t, k) in this workgroup, in
+//                        token-then-lane order).
 // The middle term is the count table turned into per-workgroup prefixes by
-// the assign launch.
+// the assign launch. The last term has two ways:
+//   * bit matrix (E <= 2048 and no token of the workgroup names an expert on
+//     two lanes): each entry ORs its token's bit into bits[e][t/32] in LDS;
+//     the term is the popcount of the bits of earlier tokens;
+//   * otherwise the entries are sorted by expert, stably, with a block radix
+//     sort in LDS, and the term is the entry's distance from the first
+//     position holding e.
+constexpr int kExpandBitsMaxE = 2048;  // E * kWords words of LDS = 64 KiB
+
 template <int ITEMS>
-__global__ __launch_bounds__(kBlockThreads) void layout_expand_kernel(LayoutArgs a, int key_bits) {
-    using sort_t = rocprim::block_radix_sort<int, kBlockThreads, ITEMS, int>;
-    __shared__ union {
-        typename sort_t::storage_type sort;
-        int keys[kBlockThreads * ITEMS];
-    } sh;
+using ExpandSort = rocprim::block_radix_sort<int, kBlockThreads, ITEMS, int>;
+
+template <int ITEMS>
+__global__ __launch_bounds__(kBlockThreads) void layout_expand_kernel(LayoutArgs a, int key_bits,
+                                                                      int use_bits) {
+    using sort_t = ExpandSort<ITEMS>;
+    extern __shared__ __align__(16) uint32_t lds_x[];
     const int b = blockIdx.x;
+    const int tid = threadIdx.x;
     const int t0 = b * kLayoutTokens;
-    const int t = t0 + threadIdx.x;
-    int keys[ITEMS], vals[ITEMS];
+    const int t = t0 + tid;
+    int keys[ITEMS];
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
         int64_t e = -1;
         if (t < a.T && k < a.K) e = a.topk[(int64_t)t * a.K + k];
-        keys[k] = expert_ok(e, a.E) ? (int)e : a.E;  // no expert: sorted last
-        vals[k] = threadIdx.x * ITEMS + k;
+        keys[k] = expert_ok(e, a.E) ? (int)e : a.E;  // no expert: key E
     }
-    sort_t().sort(keys, vals, sh.sort, 0, key_bits);
+    bool dup = false;
+#pragma unroll
+    for (int k = 1; k < ITEMS; ++k)
+#pragma unroll
+        for (int j = 0; j < k; ++j) dup |= keys[k] < a.E && keys[k] == keys[j];
+
+    if (use_bits && !__syncthreads_or(dup)) {
+        uint32_t* bits = lds_x;  // [E][kWords]
+        for (int i = tid; i < a.E * kWords; i += kBlockThreads) bits[i] = 0u;
+        __syncthreads();
+        const int w = tid / 32;
+        const uint32_t bit = 1u << (tid & 31);
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k)
+            if (keys[k] < a.E) atomicOr(&bits[keys[k] * kWords + w], bit);
+        __syncthreads();
+        if (t >= a.T) return;
+        // Both global terms of every lane are loaded together (clamped ids).
+        int base[ITEMS];
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k) {
+            const int e = min(keys[k], a.E - 1);
+            base[k] = a.out.expert_offsets[e] + a.part_expert[(int64_t)b * a.E + e];
+        }
+        const uint32_t below = bit - 1u;
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k) {
+            if (k >= a.K) break;
+            const int e = min(keys[k], a.E - 1);
+            int rank = __popc(bits[e * kWords + w] & below);
+#pragma unroll
+            for (int j = 0; j < kWords; ++j) rank += j < w ? __popc(bits[e * kWords + j]) : 0;
+            a.out.expert_slot[(int64_t)t * a.K + k] = keys[k] < a.E ? base[k] + rank : -1;
+        }
+        return;
+    }
+
+    typename sort_t::storage_type& sort_st = *reinterpret_cast<typename sort_t::storage_type*>(lds_x);
+    int* sorted = reinterpret_cast<int*>(lds_x);  // [kBlockThreads * ITEMS], after the sort
+    int vals[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) vals[k] = tid * ITEMS + k;
+    sort_t().sort(keys, vals, sort_st, 0, key_bits);
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) sh.keys[threadIdx.x * ITEMS + j] = keys[j];
+    for (int j = 0; j < ITEMS; ++j) sorted[tid * ITEMS + j] = keys[j];
     __syncthreads();
-    const int n = kBlockThreads * ITEMS;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-        const int pos = threadIdx.x * ITEMS + j;
+        const int pos = tid * ITEMS + j;
         const int key = keys[j];
         const int lt = vals[j] / ITEMS, k = vals[j] % ITEMS;
         if (k >= a.K || t0 + lt >= a.T) continue;  // padding entry
@@ -572,12 +623,11 @@ __global__ __launch_bounds__(kBlockThreads) void layout_expand_kernel(LayoutArgs
             int lo = 0, hi = pos;  // first position holding `key`
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
-                if (sh.keys[mid] < key) lo = mid + 1; else hi = mid;
+                if (sorted[mid] < key) lo = mid + 1; else hi = mid;
             }
             row = a.out.expert_offsets[key] + a.part_expert[(int64_t)b * a.E + key] + (pos - lo);
         }
         a.out.expert_slot[(int64_t)(t0 + lt) * a.K + k] = row;
-        (void)n;
     }
 }
 
@@ -618,10 +668,17 @@ hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout
     if (L.expert_slot) {
         int bits = 1;
         while ((1 << bits) <= s.E) ++bits;  // keys 0..E
-        if (s.K <= 8)
-            hipLaunchKernelGGL(layout_expand_kernel<8>, grid, block, 0, st, a, bits);
-        else
-            hipLaunchKernelGGL(layout_expand_kernel<16>, grid, block, 0, st, a, bits);
+        const int use_bits = s.E <= kExpandBitsMaxE;
+        const size_t bit_lds = use_bits ? sizeof(uint32_t) * (size_t)s.E * kWords : 0;
+        if (s.K <= 8) {
+            const size_t lds = std::max({sizeof(typename ExpandSort<8>::storage_type),
+                                         sizeof(int) * kBlockThreads * 8, bit_lds});
+            hipLaunchKernelGGL(layout_expand_kernel<8>, grid, block, lds, st, a, bits, use_bits);
+        } else {
+            const size_t lds = std::max({sizeof(typename ExpandSort<16>::storage_type),
+                                         sizeof(int) * kBlockThreads * 16, bit_lds});
+            hipLaunchKernelGGL(layout_expand_kernel<16>, grid, block, lds, st, a, bits, use_bits);
+        }
     }
     return hipGetLastError();
 }

@@ -440,6 +440,23 @@ def test_expand_layout_edges(T, K, E, R):
     assert ep.ep_check_errors(ws) == (ep.EP_DEVERR_EXPERT_ID if T > 5 else 0)
 
 
+@pytest.mark.parametrize("T,K,E,R", [(1100, 8, 256, 32), (700, 4, 2048, 256), (600, 8, 4096, 512)])
+def test_expand_layout_mixed_paths(T, K, E, R):
+    """Workgroups of distinct top-k (the LDS bit-matrix rows) next to one whose
+    token repeats an expert (the sorted rows), plus skipped lanes."""
+    w = synth.Workload("edge", T, 128, E, R, 1, K, "uniform")
+    topk = synth.topk_uniform(np.random.default_rng(T + E), T, E, K)
+    topk[300, K - 1] = topk[300, 0]   # workgroup 1: a repeated expert
+    topk[520, 1] = -1                 # workgroup 2: a skipped lane
+    topk[T - 3, :] = -1               # a token with no expert
+    shape, L, ws, _ = run_expand(w, dict(topk_idx=topk))
+    O = oracle.layout(topk, E, R, 1)
+    np.testing.assert_array_equal(host(L["expert_offsets"]), O["expert_offsets"])
+    np.testing.assert_array_equal(host(L["expert_slot"]).reshape(T, K),
+                                  oracle.expert_slots(topk, E, O["expert_offsets"]))
+    assert ep.ep_check_errors(ws) == 0
+
+
 def test_expand_topk_above_16_rejected():
     w = synth.Workload("edge", 64, 128, 64, 8, 1, 20, "uniform")
     topk = np.zeros((64, 20), np.int64)
