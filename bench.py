@@ -60,7 +60,41 @@ def parse():
                    help="time budget of the CPU-oracle baseline (0 = skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
+    p.add_argument("--ceilings", action="store_true",
+                   help="measure the chip's practical HBM rates with library kernels "
+                        "(read, constant write, copy over 1 GiB buffers), print one JSON line and exit")
     return p.parse_args()
+
+
+def ceilings(reps: int = 20) -> dict:
+    """Practical HBM rates of library kernels on 1 GiB buffers (GB/s): a
+    reduction (read only), a constant fill (write only) and a device copy
+    (read + write). Context for the roofline fractions, not a target."""
+    import torch
+
+    n = 1 << 30
+    a = torch.randn(n // 4, device="cuda")  # fp32, 1 GiB
+    b = torch.empty_like(a)
+    out = torch.empty((), device="cuda")
+    ops = {
+        "read (torch.sum, fp32)": (lambda: torch.sum(a, dim=(0,), out=out), n),
+        "write (fill_, constant)": (lambda: b.fill_(1.5), n),
+        "copy (copy_, device to device)": (lambda: b.copy_(a), 2 * n),
+    }
+    res = {}
+    for name, (fn, nbytes) in ops.items():
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"GB/s": nbytes / (ms * 1e-3) / 1e9, "us": ms * 1e3, "bytes": nbytes}
+    return res
 
 
 # Source files behind each kernel whose traffic bench.py reports. A counter
@@ -121,6 +155,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.ceilings:
+        torch.cuda.set_device(0)
+        print(json.dumps({"ceilings": ceilings(), "peak_GB/s": HBM_PEAK_GBS,
+                          "device": torch.cuda.get_device_name(0)}), flush=True)
+        return
     ep.lib()
     torch.cuda.set_device(0)
     w = synth.workload(args.workload)
