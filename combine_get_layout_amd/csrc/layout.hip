@@ -6,25 +6,32 @@
 // made deterministic: the row of (token t, rank r) is
 //     rank_offsets[r] + #{t' < t : token t' sends to r}.
 //
-// Two stream-ordered launches, all integer work, no waiting between
-// workgroups:
+// Two stream-ordered launches (three with expand rows), all integer work, no
+// waiting between workgroups:
 //   1. count  : one thread per token, 256 tokens per workgroup. Each token ORs
 //               its bit into an LDS bit matrix bits[r][t/32] (a repeated rank
 //               sets the same bit: that is the deduplication) and bumps an
-//               LDS expert histogram. Per-workgroup counts are popcounts of
-//               the bit rows; the is-token-in-rank mask is expanded from the
-//               same bits with 16-byte stores.
-//   2. assign : every workgroup rebuilds its bit matrix, sums the count table
-//               of the earlier workgroups (and of all of them) for each rank
-//               and group, scans the totals in LDS (wave shuffles), and gives
-//               every lane its slot = region start + earlier workgroups +
-//               popcount of the bits of earlier tokens in its own workgroup.
-//               Expert totals and offsets are split by rank: workgroup b owns
-//               the experts of a slice of ranks, and the offset of a slice's
-//               first expert is the prefix of the per-rank lane counts, which
-//               every workgroup already sums. Workgroups never wait for each
-//               other and no grid-wide fence is needed (the launch boundary
-//               orders the two kernels).
+//               LDS expert histogram; with one group, the group bits are one
+//               wave ballot. Per-workgroup counts are popcounts of the bit
+//               rows, written as one row per workgroup of two tables
+//               ([ranks | lanes per rank | groups] and [experts]); the
+//               is-token-in-rank mask is expanded from the same bits with
+//               16-byte stores.
+//   2. assign : every workgroup rebuilds its bit matrix and reads every row of
+//               the rank/lane/group table as 16-byte vectors, keeping for each
+//               column the sum over the earlier workgroups and over all of
+//               them. The section totals go through DPP wave scans and one
+//               barrier; each lane's slot = region start + earlier
+//               workgroups + this workgroup's tokens to the rank in earlier
+//               32-token words (a u8 table) + popcount of the earlier bits of
+//               its own word. Expert totals and offsets are split by rank:
+//               workgroup b owns the experts of a slice of ranks, and the
+//               offset of a slice's first expert is the prefix of the
+//               per-rank lane counts, which every workgroup already sums.
+//   3. expand : (only when expand rows are asked for) the row of each
+//               (token, lane) inside its expert's region.
+// Workgroups never wait for each other and no grid-wide fence is needed (the
+// launch boundaries order the kernels).
 #include <algorithm>
 
 #include <rocprim/block/block_radix_sort.hpp>
