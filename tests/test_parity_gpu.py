@@ -203,6 +203,38 @@ def test_dispatch_edges(T, H, K, E, R):
     check_dispatch(recv, D, N)
 
 
+@pytest.mark.parametrize("segs", ["fp8+scales", "x", "scales", "meta", "fp8"])
+def test_dispatch_segment_subsets(segs):
+    """Every payload piece is optional on its own; the metadata too."""
+    w = synth.Workload("segs", 700, 1024, 48, 12, 1, 6, "uniform")
+    inp = synth.make_inputs(w, with_fp8=True)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    N = int(host(L["rank_offsets"])[-1])
+    want_x, want_fp8 = segs == "x", "fp8" in segs
+    want_sc, meta = "scales" in segs, segs in ("fp8+scales", "scales", "meta")
+    tokens = dict(topk_idx=tk, topk_weights=dev(inp["topk_w"]))
+    if want_x:
+        tokens["x"] = dev(inp["x"])
+    if want_fp8:
+        tokens["x_fp8"] = dev(inp["x_fp8"])
+    if want_sc:
+        tokens["x_scales"] = dev(inp["x_scales"])
+    recv = ep.alloc_recv(shape, N, x=want_x, fp8=want_fp8, scales=want_sc, meta=meta)
+    for t in recv.values():
+        poison(t)
+    ep.ep_dispatch(shape, L, tokens, recv, N, ws)
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, 1)
+    D = oracle.dispatch(inp["topk_idx"], w.E, w.R, O["rank_offsets"],
+                        x=inp["x"] if want_x else None, x_fp8=inp["x_fp8"] if want_fp8 else None,
+                        x_scales=inp["x_scales"] if want_sc else None, topk_w=inp["topk_w"],
+                        with_meta=meta)
+    assert set(recv) == {k for k, o in [("x", "recv_x"), ("x_fp8", "recv_fp8"), ("x_scales", "recv_scales"),
+                                         ("src_idx", "recv_src"), ("topk_idx", "recv_topk_idx"),
+                                         ("topk_weights", "recv_topk_w")] if D.get(o) is not None}
+    check_dispatch(recv, D, N)
+    assert ep.ep_check_errors(ws) == 0
+
+
 def test_dispatch_capacity_overflow():
     w = synth.workload("tiny")
     inp = synth.make_inputs(w)
@@ -282,6 +314,27 @@ def test_combine_edges(T, H, K):
     assert ep.ep_check_errors(ws) == 0
 
 
+@pytest.mark.parametrize("pad", [8, 64, 1000])
+def test_combine_padded_row_stride(pad):
+    """Expert outputs in rows wider than the hidden size (stride > 2H bytes)."""
+    T, H, K = 333, 2048, 8
+    rng = np.random.default_rng(pad)
+    rows = 2 * T
+    slot = rng.integers(-1, rows, size=(T, K)).astype(np.int32)
+    slot[::5, 3] = slot[::5, 1]
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    y_wide = synth.random_bf16_rows(rows, H + pad, seed=pad)
+    shape = ep.make_shape(T, H, K, 4, 2, 1)
+    ws = ep.alloc_workspace(shape)
+    out = poison(torch.empty((T, H), dtype=torch.uint16, device="cuda"))
+    ep.ep_clear_errors(ws)
+    ep.ep_combine(shape, dict(slot=dev(slot)), dev(y_wide), rows, 2 * (H + pad), ep.EP_FMT_PLAIN, 0,
+                  dev(w), out, ws)
+    C = oracle.combine(slot, w, np.ascontiguousarray(y_wide[:, :H]), H)
+    np.testing.assert_array_equal(host(out), C["out"])
+    assert ep.ep_check_errors(ws) == 0
+
+
 def test_combine_rows_out_of_range():
     T, H, K, rows = 50, 256, 4, 40
     rng = np.random.default_rng(8)
@@ -344,6 +397,34 @@ def test_hierarchical_full(name, fp8):
     got = host(out)
     np.testing.assert_array_equal(got, C["out"])
     combine_close(got, inp["x"])
+    assert ep.ep_check_errors(ws) == 0
+
+
+@pytest.mark.parametrize("T,H,K,E,R,G,ids", [
+    (257, 264, 3, 24, 8, 8, "uniform"),     # one peer per group (G = R)
+    (300, 512, 4, 32, 8, 1, "uniform"),     # one group holding every rank
+    (129, 1032, 12, 48, 16, 4, "uniform"),  # K > 8, hidden row not a whole number of blocks
+    (1, 8, 1, 4, 2, 2, "uniform"),          # one token, one lane
+    (400, 256, 5, 20, 10, 5, "random")])    # skipped lanes and repeated experts
+def test_hierarchical_edges(T, H, K, E, R, G, ids):
+    w = synth.Workload("edge", T, H, E, R, G, K, "uniform")
+    inp = synth.make_inputs(w)
+    if ids == "random":
+        inp["topk_idx"] = np.random.default_rng(T + H).integers(-1, E, size=(T, K)).astype(np.int64)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    epoch = 9
+    gb, pb, G_rows, N, stride = run_hier(w, inp, shape, L, ws, tk, epoch)
+    O = oracle.layout(inp["topk_idx"], E, R, G)
+    np.testing.assert_array_equal(host(L["group_slot"]), O["group_slot"])
+    Hd = oracle.hier_dispatch(inp["topk_idx"], E, R, G, O["slot"], O["group_offsets"], epoch,
+                              x=inp["x"], topk_w=inp["topk_w"])
+    assert Hd["stride"] == stride and Hd["err"] == 0
+    np.testing.assert_array_equal(host(gb)[:G_rows], Hd["group_buf"])
+    np.testing.assert_array_equal(host(pb)[:N], Hd["peer_buf"])
+    out = poison(torch.empty((T, H), dtype=torch.uint16, device="cuda"))
+    ep.ep_combine(shape, L, pb, N, stride, ep.EP_FMT_CHUNKED, epoch, dev(inp["topk_w"]), out, ws)
+    C = oracle.combine(O["slot"], inp["topk_w"], Hd["peer_buf"], H, chunked=True, epoch=epoch)
+    np.testing.assert_array_equal(host(out), C["out"])
     assert ep.ep_check_errors(ws) == 0
 
 
