@@ -142,8 +142,8 @@ def committed_traffic(workload: str, kernel: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
-              "cross-GPU step in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path has no "
+              "cross-GPU step; several GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -351,8 +351,9 @@ def main():
             raise RuntimeError("device error bits set during the graph replays")
     ms_step = ms_total / args.steps
 
-    # Algorithmic bytes per launch (what the method must move),
-    # averaged over the batches the timed steps used.
+    # Algorithmic bytes per launch: what the method must move, from the byte
+    # model per token (read each row once, write each receive row once, plus
+    # the routing metadata), averaged over the batches the timed steps used.
     T, H, K, R = w.T, w.H, w.K, w.R
     row = 2 * H + ((H + 4 * (H // 128)) if fp8 else 0)
     meta = 4 + 8 * K
