@@ -20,8 +20,9 @@
 // lane mapping (wave iteration i covers blocks 2i and 2i+1; lane L holds
 // hidden vector 30 * (2i + L/32) + L%32 when L%32 < 30, else a flag vector),
 // so a partial row is produced and consumed with whole-wave 1 KiB stores and
-// loads. Flags of all rows a token reads are checked in one batched pass
-// before the sums.
+// loads. The flags of every chunked row read are checked by the flag lanes of
+// the same loads that bring in its values; a row with a bad flag makes the
+// token run a second pass without it (error path only).
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -57,36 +58,6 @@ __device__ __forceinline__ bool flag_ok(u32x4 f, uint32_t epoch) {
     return f[0] == epoch && f[1] == epoch && f[2] == epoch && f[3] == epoch;
 }
 
-// Lanes k (bit k) among `cand` whose row (row_of(k)) has a wrong flag in one
-// of its first nblk blocks. All flag loads of all rows are issued together:
-// pair i = (lane k = i / (2 nblk), flag vector i % (2 nblk)).
-template <typename RowOf>
-__device__ uint64_t bad_rows(uint64_t cand, int nblk, uint32_t epoch, RowOf row_of) {
-    const int lane = lane_id();
-    const int per = 2 * nblk;
-    uint64_t bad = 0;
-    const int n = 64 * per;  // every lane index 0..63 (only candidates matter)
-    for (int i0 = 0; i0 < n; i0 += kWave) {
-        const int i = i0 + lane;
-        const int k = i / per, f = i % per;
-        const bool mine = ((cand >> k) & 1) != 0;
-        const uint8_t* row = row_of(k);
-        if (mine) {
-            const u32x4 v = ld16(row + (int64_t)(f >> 1) * kChunkBytes + kChunkPayload + (f & 1) * 16);
-            if (!flag_ok(v, epoch)) bad |= 1ull << k;
-        }
-        // waves whose remaining pairs are past every candidate lane stop early
-        if (!(cand >> min(63, (i0 + kWave) / per))) break;
-    }
-    // combine the per-lane bits
-    uint64_t all = 0;
-    for (uint64_t m = cand; m; m &= m - 1) {
-        const int k = __ffsll((unsigned long long)m) - 1;
-        if (__ballot((bad >> k) & 1)) all |= 1ull << k;
-    }
-    return all;
-}
-
 template <int KMAX>
 __global__ __launch_bounds__(kBlockThreads) void combine_group_kernel(Combine2Args a) {
     const int lane = lane_id();
@@ -110,15 +81,6 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_kernel(Combine2Ar
     const int nvh = a.H / 8;
     const int nblk = (2 * a.H + kChunkPayload - 1) / kChunkPayload;  // blocks of a hidden row
     const int iters = (nblk + 1) / 2;
-    if (a.y_chunked && um) {
-        const uint64_t bad = bad_rows(um, nblk, a.epoch, [&](int k) {
-            return a.y + (int64_t)__shfl(s, k) * a.y_stride;
-        });
-        if (bad) {
-            if (lane == 0) report(a.err, EP_DEVERR_FLAG);
-            um &= ~bad;
-        }
-    }
     // Groups of this token: the first lane of each, numbered in lane order.
     bool first = g >= 0;
     for (int j = 0; j < a.K; ++j) {
@@ -154,60 +116,82 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_kernel(Combine2Ar
     }
     if (!wmask) return;
     // One pass over the hidden row: every lane's row is read once and feeds
-    // its group's accumulator (ascending k inside each group).
-    const int s_any = um ? readlane(s, __ffsll((unsigned long long)um) - 1) : 0;
-    const uint8_t* rowp[KMAX];
-    float wk[KMAX];
-    int gk[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        const int kk = min(k, a.K - 1);
-        rowp[k] = a.y + (int64_t)(((um >> k) & 1) ? readlane(s, kk) : s_any) * a.y_stride;
-        wk[k] = readlane_f(wt, kk);
-        gk[k] = readlane(gpos, kk);
-    }
+    // its group's accumulator (ascending k inside each group). With chunked
+    // rows, the lanes on a block's 32-byte flag load that flag with the same
+    // instruction and check it; a row with a bad flag is found only after
+    // its values were used, so the token is then computed again without it
+    // (an error path only; the second pass rewrites the partial rows).
     const u32x4 flagv = {a.epoch, a.epoch, a.epoch, a.epoch};
-    for (int it = 0; it < iters; ++it) {
-        int c, wv, p;
-        const bool hv = chunk_vec(it, lane, nvh, c, wv, p);
-        const int64_t off = hv ? (a.y_chunked ? (int64_t)c * kChunkBytes + (int64_t)wv * 16 : (int64_t)p * 16) : 0;
-        u32x4 v[KMAX];
-        if (um) {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) v[k] = ld16(rowp[k] + off);
-        }
-        float acc[KMAX][8];
-#pragma unroll
-        for (int gi = 0; gi < KMAX; ++gi)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) acc[gi][q] = 0.f;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int s_any = um ? readlane(s, __ffsll((unsigned long long)um) - 1) : 0;
+        const uint8_t* rowp[KMAX];
+        float wk[KMAX];
+        int gk[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (!((um >> k) & 1)) continue;
+            const int kk = min(k, a.K - 1);
+            rowp[k] = a.y + (int64_t)(((um >> k) & 1) ? readlane(s, kk) : s_any) * a.y_stride;
+            wk[k] = readlane_f(wt, kk);
+            gk[k] = readlane(gpos, kk);
+        }
+        uint32_t bad = 0;  // per lane: bit k = a flag of row k checked by this lane is wrong
+        for (int it = 0; it < iters; ++it) {
+            int c, wv, p;
+            const bool hv = chunk_vec(it, lane, nvh, c, wv, p);
+            const bool fl = a.y_chunked && wv >= kChunkPayloadVecs && c < nblk;
+            const int64_t blk = (int64_t)c * kChunkBytes + (int64_t)wv * 16;
+            const int64_t off = hv ? (a.y_chunked ? blk : (int64_t)p * 16) : (fl ? blk : 0);
+            u32x4 v[KMAX];
+            if (um) {
 #pragma unroll
-            for (int gi = 0; gi < KMAX; ++gi) {
-                if (gk[k] != gi) continue;
+                for (int k = 0; k < KMAX; ++k) v[k] = ld16(rowp[k] + off);
+            }
+            if (fl) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[gi][2 * q] = __builtin_fmaf(wk[k], bf16_lo(v[k][q]), acc[gi][2 * q]);
-                    acc[gi][2 * q + 1] = __builtin_fmaf(wk[k], bf16_hi(v[k][q]), acc[gi][2 * q + 1]);
+                for (int k = 0; k < KMAX; ++k)
+                    if (((um >> k) & 1) && !flag_ok(v[k], a.epoch)) bad |= 1u << k;
+            }
+            float acc[KMAX][8];
+#pragma unroll
+            for (int gi = 0; gi < KMAX; ++gi)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[gi][q] = 0.f;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (!((um >> k) & 1)) continue;
+#pragma unroll
+                for (int gi = 0; gi < KMAX; ++gi) {
+                    if (gk[k] != gi) continue;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[gi][2 * q] = __builtin_fmaf(wk[k], bf16_lo(v[k][q]), acc[gi][2 * q]);
+                        acc[gi][2 * q + 1] = __builtin_fmaf(wk[k], bf16_hi(v[k][q]), acc[gi][2 * q + 1]);
+                    }
                 }
             }
-        }
-        if (c >= nblk) continue;
-        const int64_t o_off = (int64_t)c * kChunkBytes + (int64_t)wv * 16;
+            if (c >= nblk) continue;
+            const int64_t o_off = (int64_t)c * kChunkBytes + (int64_t)wv * 16;
 #pragma unroll
-        for (int gi = 0; gi < KMAX; ++gi) {
-            if (!((wmask >> gi) & 1)) continue;
-            u32x4 o = {0u, 0u, 0u, 0u};
-            if (hv) {
+            for (int gi = 0; gi < KMAX; ++gi) {
+                if (!((wmask >> gi) & 1)) continue;
+                u32x4 o = {0u, 0u, 0u, 0u};
+                if (hv) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    o[q] = f32_to_bf16(acc[gi][2 * q]) | (f32_to_bf16(acc[gi][2 * q + 1]) << 16);
+                    for (int q = 0; q < 4; ++q)
+                        o[q] = f32_to_bf16(acc[gi][2 * q]) | (f32_to_bf16(acc[gi][2 * q + 1]) << 16);
+                }
+                if (wv >= kChunkPayloadVecs) o = flagv;
+                st16_stream(prow[gi] + o_off, o);
             }
-            if (wv >= kChunkPayloadVecs) o = flagv;
-            st16_stream(prow[gi] + o_off, o);
         }
+        if (!a.y_chunked) return;
+        uint64_t drop = 0;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (((um >> k) & 1) && __ballot((bad >> k) & 1)) drop |= 1ull << k;
+        if (!drop) return;
+        if (lane == 0) report(a.err, EP_DEVERR_FLAG);
+        um &= ~drop;
     }
 }
 
@@ -235,68 +219,80 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_kernel(Combine2Ar
     const int nvh = a.H / 8;
     const int nblk = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
     const int iters = (nblk + 1) / 2;
-    if (fm) {
-        const uint64_t bad = bad_rows(fm, nblk, a.epoch, [&](int k) {
-            return a.group_buf + (int64_t)__shfl(gs, k) * a.pstride;
-        });
-        if (bad) {
-            if (lane == 0) report(a.err, EP_DEVERR_FLAG);
-            fm &= ~bad;
-        }
-    }
     uint8_t* out_row = reinterpret_cast<uint8_t*>(a.out) + (int64_t)t * a.H * 2;
-    // The token's partial rows in ascending group: position = number of
-    // partials with a smaller group; unused positions point at a used row.
-    int rank = 0;
-    for (uint64_t m = fm; m; m &= m - 1) {
-        const int j = __ffsll((unsigned long long)m) - 1;
-        rank += readlane(g, j) < g ? 1 : 0;
-    }
-    const int ng = __popcll(fm);
-    const int row_any = fm ? readlane(gs, __ffsll((unsigned long long)fm) - 1) : 0;
-    const uint8_t* rowp[GMAX];
-#pragma unroll
-    for (int pos = 0; pos < GMAX; ++pos) {
-        const uint64_t who = __ballot(((fm >> lane) & 1) && rank == pos);
-        const int row = who ? readlane(gs, __ffsll((unsigned long long)who) - 1) : row_any;
-        rowp[pos] = a.group_buf + (int64_t)row * a.pstride;
-    }
-    constexpr int NB = 2;
-    for (int it0 = 0; it0 < iters; it0 += NB) {
-        int c[NB], wv[NB], p[NB];
-        bool hv[NB];
-        int64_t off[NB];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            hv[j] = it0 + j < iters && chunk_vec(it0 + j, lane, nvh, c[j], wv[j], p[j]);
-            off[j] = hv[j] ? (int64_t)c[j] * kChunkBytes + (int64_t)wv[j] * 16 : 0;
+    // Partial rows whose flags are checked with the same loads as their
+    // values (the lanes on a block's 32-byte flag load the flag); a bad flag
+    // drops the row and the token is summed again without it (error path
+    // only; the second pass rewrites the output row).
+    for (int pass = 0; pass < 2; ++pass) {
+        // The token's partial rows in ascending group: position = number of
+        // partials with a smaller group; unused positions point at a used row.
+        int rank = 0;
+        for (uint64_t m = fm; m; m &= m - 1) {
+            const int j = __ffsll((unsigned long long)m) - 1;
+            rank += readlane(g, j) < g ? 1 : 0;
         }
-        u32x4 v[GMAX][NB];
-        if (fm) {
+        const int ng = __popcll(fm);
+        const int row_any = fm ? readlane(gs, __ffsll((unsigned long long)fm) - 1) : 0;
+        const uint8_t* rowp[GMAX];
 #pragma unroll
-            for (int pos = 0; pos < GMAX; ++pos)
-#pragma unroll
-                for (int j = 0; j < NB; ++j) v[pos][j] = ld16(rowp[pos] + off[j]);
+        for (int pos = 0; pos < GMAX; ++pos) {
+            const uint64_t who = __ballot(((fm >> lane) & 1) && rank == pos);
+            const int row = who ? readlane(gs, __ffsll((unsigned long long)who) - 1) : row_any;
+            rowp[pos] = a.group_buf + (int64_t)row * a.pstride;
         }
+        uint32_t bad = 0;  // per lane: bit pos = a flag of partial `pos` checked by this lane is wrong
+        constexpr int NB = 2;
+        for (int it0 = 0; it0 < iters; it0 += NB) {
+            int c[NB], wv[NB], p[NB];
+            bool hv[NB], fl[NB];
+            int64_t off[NB];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NB; ++j) {
+                const bool in = it0 + j < iters;
+                hv[j] = in && chunk_vec(it0 + j, lane, nvh, c[j], wv[j], p[j]);
+                fl[j] = in && wv[j] >= kChunkPayloadVecs && c[j] < nblk;
+                off[j] = (hv[j] || fl[j]) ? (int64_t)c[j] * kChunkBytes + (int64_t)wv[j] * 16 : 0;
+            }
+            u32x4 v[GMAX][NB];
+            if (fm) {
 #pragma unroll
-            for (int pos = 0; pos < GMAX; ++pos) {
-                if (pos >= ng) break;
+                for (int pos = 0; pos < GMAX; ++pos)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] = acc[2 * q] + bf16_lo(v[pos][j][q]);
-                    acc[2 * q + 1] = acc[2 * q + 1] + bf16_hi(v[pos][j][q]);
+                    for (int j = 0; j < NB; ++j) v[pos][j] = ld16(rowp[pos] + off[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (fl[j]) {
+#pragma unroll
+                    for (int pos = 0; pos < GMAX; ++pos)
+                        if (pos < ng && !flag_ok(v[pos][j], a.epoch)) bad |= 1u << pos;
+                }
+                float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int pos = 0; pos < GMAX; ++pos) {
+                    if (pos >= ng) break;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[2 * q] = acc[2 * q] + bf16_lo(v[pos][j][q]);
+                        acc[2 * q + 1] = acc[2 * q + 1] + bf16_hi(v[pos][j][q]);
+                    }
+                }
+                if (hv[j]) {
+                    u32x4 o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) o[q] = f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16);
+                    st16_stream(out_row + (int64_t)p[j] * 16, o);
                 }
             }
-            if (hv[j]) {
-                u32x4 o;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) o[q] = f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16);
-                st16_stream(out_row + (int64_t)p[j] * 16, o);
-            }
         }
+        uint32_t badpos = 0;
+#pragma unroll
+        for (int pos = 0; pos < GMAX; ++pos)
+            if (pos < ng && __ballot((bad >> pos) & 1)) badpos |= 1u << pos;
+        if (!badpos) return;
+        if (lane == 0) report(a.err, EP_DEVERR_FLAG);
+        fm &= ~__ballot(((fm >> lane) & 1) && ((badpos >> rank) & 1));
     }
 }
 

@@ -650,6 +650,35 @@ def test_two_level_combine_plain(T, H, K, E, R, G):
     assert ep.ep_check_errors(ws) == 0
 
 
+def test_two_level_combine_corrupted_input_rows():
+    """A chunked expert-output row with a bad flag in its first or last hidden
+    block is dropped by the group step, for every lane that reads it."""
+    w = synth.Workload("small", 700, 1024, 64, 16, 4, 6, "uniform")
+    inp = synth.make_inputs(w, seed=43)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    L["_ws"] = ws
+    epoch = 11
+    gb, pb, G_rows, N, stride = run_hier(w, inp, shape, L, ws, tk, epoch)
+    nblk = (2 * w.H + 479) // 480
+    bad = {5: 0, 211: nblk - 1, 1000: 2}  # row -> block whose flag is hit
+    for row, blk in bad.items():
+        pb[row, blk * 512 + 480 + 5] ^= 0x40
+    wd = dev(inp["topk_w"])
+    gbuf, out, gcap = run_two_level(shape, L, tk, pb, N, stride, ep.EP_FMT_CHUNKED, epoch, wd)
+    assert ep.ep_check_errors(ws) == ep.EP_DEVERR_FLAG
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    Hd = oracle.hier_dispatch(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_offsets"], epoch,
+                              x=inp["x"], topk_w=inp["topk_w"])
+    y = Hd["peer_buf"].copy()
+    for row, blk in bad.items():
+        y[row, blk * 512 + 480 + 5] ^= 0x40
+    C = oracle.combine_two_level(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_slot"],
+                                 inp["topk_w"], y, w.H, gcap, epoch, chunked=True)
+    assert C["err"] == oracle.ERR_FLAG
+    np.testing.assert_array_equal(host(gbuf)[:gcap], C["group_buf"])
+    np.testing.assert_array_equal(host(out), C["out"])
+
+
 def test_two_level_combine_corrupted_partial():
     w = synth.Workload("small", 300, 512, 32, 8, 4, 4, "uniform")
     inp = synth.make_inputs(w, seed=41)
