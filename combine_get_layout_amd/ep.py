@@ -110,11 +110,24 @@ def lib() -> ctypes.CDLL:
     return L
 
 
-def _ptr(t):
+def _ptr(t, name="tensor", nbytes=0):
+    """Device address of a tensor argument (None passes through as NULL).
+
+    A tensor must live on the GPU, be contiguous and hold at least `nbytes`
+    bytes (the size the C ABI reads or writes for the given shape); anything
+    else raises before a kernel can touch memory it does not own. A plain int
+    is taken as a device address the caller vouches for."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: {have} bytes, the call needs {nbytes}")
     return t.data_ptr()
 
 
@@ -135,13 +148,41 @@ def make_shape(T, H, K, E, R, G=1) -> ep_shape:
     return ep_shape(int(T), int(H), int(K), int(E), int(R), int(G))
 
 
-def _layout_struct(layout: dict) -> ep_layout:
-    return ep_layout(*[_ptr(layout.get(n)) for n in LAYOUT_FIELDS])
+def _ws(ws):
+    return _ptr(ws, "workspace"), ws.numel() * ws.element_size()
 
 
-def _tokens_struct(tokens: dict) -> ep_tokens:
-    return ep_tokens(*[_ptr(tokens.get(n)) for n in ("x", "x_fp8", "x_scales", "topk_idx",
-                                                      "topk_weights")])
+def _layout_struct(shape: ep_shape, layout: dict) -> ep_layout:
+    T, K, E, R, G = shape.T, shape.K, shape.E, shape.R, shape.G
+    need = dict(tokens_per_expert=4 * E, tokens_per_rank=4 * R, tokens_per_group=4 * G,
+                expert_offsets=4 * (E + 1), rank_offsets=4 * (R + 1), group_offsets=4 * (G + 1),
+                is_token_in_rank=T * R, is_token_in_group=T * G, slot=4 * T * K,
+                group_slot=4 * T * K, expert_slot=4 * T * K)
+    return ep_layout(*[_ptr(layout.get(n), n, need[n]) for n in LAYOUT_FIELDS])
+
+
+def _seg_of(tokens: dict) -> int:
+    return ((EP_SEG_BF16 if tokens.get("x") is not None else 0) |
+            (EP_SEG_FP8 if tokens.get("x_fp8") is not None else 0) |
+            (EP_SEG_SCALES if tokens.get("x_scales") is not None else 0))
+
+
+def _tokens_struct(shape: ep_shape, tokens: dict) -> ep_tokens:
+    T, H, K = shape.T, shape.H, shape.K
+    need = dict(x=2 * T * H, x_fp8=T * H, x_scales=4 * T * (H // 128), topk_idx=8 * T * K,
+                topk_weights=4 * T * K)
+    return ep_tokens(*[_ptr(tokens.get(n), n, need[n]) for n in ("x", "x_fp8", "x_scales",
+                                                                  "topk_idx", "topk_weights")])
+
+
+def _recv_struct(shape: ep_shape, recv: dict, capacity: int) -> ep_recv:
+    H, K, cap = shape.H, shape.K, max(int(capacity), 0)
+    need = dict(x=2 * cap * H, x_fp8=cap * H, x_scales=4 * cap * (H // 128), src_idx=4 * cap,
+                topk_idx=4 * cap * K, topk_weights=4 * cap * K)
+    return ep_recv(*[_ptr(recv.get(n), "recv " + n, need[n]) for n in ("x", "x_fp8", "x_scales",
+                                                                        "src_idx", "topk_idx",
+                                                                        "topk_weights")],
+                   int(capacity))
 
 
 def ep_workspace_bytes(shape: ep_shape) -> int:
@@ -157,59 +198,62 @@ def ep_chunked_record_bytes(shape: ep_shape, seg_flags: int) -> int:
 
 
 def ep_get_layout(shape, topk_idx, layout: dict, ws, stream=None):
-    L = _layout_struct(layout)
-    _check(lib().ep_get_layout(ctypes.byref(shape), _ptr(topk_idx), ctypes.byref(L), _ptr(ws),
-                               ws.numel() * ws.element_size(), _stream(stream)), "ep_get_layout")
+    L = _layout_struct(shape, layout)
+    _check(lib().ep_get_layout(ctypes.byref(shape), _ptr(topk_idx, "topk_idx", 8 * shape.T * shape.K),
+                               ctypes.byref(L), *_ws(ws), _stream(stream)), "ep_get_layout")
 
 
 def ep_dispatch(shape, layout: dict, tokens: dict, recv: dict, capacity: int, ws, stream=None):
-    L = _layout_struct(layout)
-    tk = _tokens_struct(tokens)
-    rv = ep_recv(*[_ptr(recv.get(n)) for n in ("x", "x_fp8", "x_scales", "src_idx", "topk_idx",
-                                                "topk_weights")], int(capacity))
+    L = _layout_struct(shape, layout)
+    tk = _tokens_struct(shape, tokens)
+    rv = _recv_struct(shape, recv, capacity)
     _check(lib().ep_dispatch(ctypes.byref(shape), ctypes.byref(L), ctypes.byref(tk),
-                             ctypes.byref(rv), _ptr(ws), ws.numel() * ws.element_size(),
-                             _stream(stream)), "ep_dispatch")
+                             ctypes.byref(rv), *_ws(ws), _stream(stream)), "ep_dispatch")
 
 
 def ep_dispatch_expand(shape, layout: dict, tokens: dict, recv: dict, capacity: int, ws, stream=None):
-    L = _layout_struct(layout)
-    tk = _tokens_struct(tokens)
-    rv = ep_recv(*[_ptr(recv.get(n)) for n in ("x", "x_fp8", "x_scales", "src_idx", "topk_idx",
-                                                "topk_weights")], int(capacity))
+    L = _layout_struct(shape, layout)
+    tk = _tokens_struct(shape, tokens)
+    rv = _recv_struct(shape, recv, capacity)
     _check(lib().ep_dispatch_expand(ctypes.byref(shape), ctypes.byref(L), ctypes.byref(tk),
-                                    ctypes.byref(rv), _ptr(ws), ws.numel() * ws.element_size(),
-                                    _stream(stream)), "ep_dispatch_expand")
+                                    ctypes.byref(rv), *_ws(ws), _stream(stream)), "ep_dispatch_expand")
 
 
 def ep_hierarchical_dispatch(shape, layout: dict, tokens: dict, epoch: int, steps: int, group_buf,
                              group_cap: int, peer_buf, peer_cap: int, ws, stream=None):
-    L = _layout_struct(layout)
-    tk = _tokens_struct(tokens)
+    L = _layout_struct(shape, layout)
+    tk = _tokens_struct(shape, tokens)
+    stride = max(ep_chunked_record_bytes(shape, _seg_of(tokens) or EP_SEG_BF16), 0)
     _check(lib().ep_hierarchical_dispatch(ctypes.byref(shape), ctypes.byref(L), ctypes.byref(tk),
-                                          int(epoch), int(steps), _ptr(group_buf), int(group_cap),
-                                          _ptr(peer_buf), int(peer_cap), _ptr(ws),
-                                          ws.numel() * ws.element_size(), _stream(stream)),
+                                          int(epoch), int(steps),
+                                          _ptr(group_buf, "group_buf", max(int(group_cap), 0) * stride),
+                                          int(group_cap),
+                                          _ptr(peer_buf, "peer_buf", max(int(peer_cap), 0) * stride),
+                                          int(peer_cap), *_ws(ws), _stream(stream)),
            "ep_hierarchical_dispatch")
+
+
+def _combine_args(shape, y, y_rows, y_row_stride, topk_weights, out):
+    T, H, K = shape.T, shape.H, shape.K
+    return (_ptr(y, "y", max(int(y_rows), 0) * max(int(y_row_stride), 0)), int(y_rows),
+            int(y_row_stride), _ptr(topk_weights, "topk_weights", 4 * T * K),
+            _ptr(out, "out", 2 * T * H))
 
 
 def ep_combine(shape, layout: dict, y, y_rows: int, y_row_stride: int, y_format: int, epoch: int,
                topk_weights, out, ws, stream=None):
-    L = _layout_struct(layout)
-    _check(lib().ep_combine(ctypes.byref(shape), ctypes.byref(L), _ptr(y), int(y_rows),
-                            int(y_row_stride), int(y_format), int(epoch), _ptr(topk_weights),
-                            _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "ep_combine")
+    L = _layout_struct(shape, layout)
+    yp, yr, ys, wp, op = _combine_args(shape, y, y_rows, y_row_stride, topk_weights, out)
+    _check(lib().ep_combine(ctypes.byref(shape), ctypes.byref(L), yp, yr, ys, int(y_format),
+                            int(epoch), wp, op, *_ws(ws), _stream(stream)), "ep_combine")
 
 
 def ep_combine_expand(shape, layout: dict, y, y_rows: int, y_row_stride: int, y_format: int,
                       epoch: int, topk_weights, out, ws, stream=None):
-    L = _layout_struct(layout)
-    _check(lib().ep_combine_expand(ctypes.byref(shape), ctypes.byref(L), _ptr(y), int(y_rows),
-                                   int(y_row_stride), int(y_format), int(epoch),
-                                   _ptr(topk_weights), _ptr(out), _ptr(ws),
-                                   ws.numel() * ws.element_size(), _stream(stream)),
-           "ep_combine_expand")
+    L = _layout_struct(shape, layout)
+    yp, yr, ys, wp, op = _combine_args(shape, y, y_rows, y_row_stride, topk_weights, out)
+    _check(lib().ep_combine_expand(ctypes.byref(shape), ctypes.byref(L), yp, yr, ys, int(y_format),
+                                   int(epoch), wp, op, *_ws(ws), _stream(stream)), "ep_combine_expand")
 
 
 def ep_partial_row_bytes(shape: ep_shape) -> int:
@@ -219,61 +263,67 @@ def ep_partial_row_bytes(shape: ep_shape) -> int:
 def ep_combine_two_level(shape, layout: dict, topk_idx, y, y_rows: int, y_row_stride: int,
                          y_format: int, epoch: int, topk_weights, group_buf, group_cap: int,
                          steps: int, out, ws, stream=None):
-    L = _layout_struct(layout)
-    _check(lib().ep_combine_two_level(ctypes.byref(shape), ctypes.byref(L), _ptr(topk_idx), _ptr(y),
-                                      int(y_rows), int(y_row_stride), int(y_format), int(epoch),
-                                      _ptr(topk_weights), _ptr(group_buf), int(group_cap), int(steps),
-                                      _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                                      _stream(stream)), "ep_combine_two_level")
+    L = _layout_struct(shape, layout)
+    yp, yr, ys, wp, op = _combine_args(shape, y, y_rows, y_row_stride, topk_weights, out)
+    pstride = max(ep_partial_row_bytes(shape), 0)
+    _check(lib().ep_combine_two_level(ctypes.byref(shape), ctypes.byref(L),
+                                      _ptr(topk_idx, "topk_idx", 8 * shape.T * shape.K), yp, yr, ys,
+                                      int(y_format), int(epoch), wp,
+                                      _ptr(group_buf, "group_buf", max(int(group_cap), 0) * pstride),
+                                      int(group_cap), int(steps), op, *_ws(ws), _stream(stream)),
+           "ep_combine_two_level")
 
 
-def _sources_struct(sources: dict) -> ep_sources:
-    return ep_sources(int(sources["S"]), int(sources["capacity"]), _ptr(sources.get("counts")),
-                      _ptr(sources.get("recv_offsets")), _ptr(sources.get("src_slot")))
-
-
-def _recv_struct(recv: dict, capacity: int) -> ep_recv:
-    return ep_recv(*[_ptr(recv.get(n)) for n in ("x", "x_fp8", "x_scales", "src_idx", "topk_idx",
-                                                  "topk_weights")], int(capacity))
+def _sources_struct(shape: ep_shape, sources: dict) -> ep_sources:
+    S, R = int(sources["S"]), shape.R
+    return ep_sources(S, int(sources["capacity"]),
+                      _ptr(sources.get("counts"), "counts", 4 * S * R),
+                      _ptr(sources.get("recv_offsets"), "recv_offsets", 4 * (R * S + 1)),
+                      _ptr(sources.get("src_slot"), "src_slot", 4 * shape.T * shape.K))
 
 
 def ep_source_workspace_bytes(shape: ep_shape, S: int) -> int:
     return int(lib().ep_source_workspace_bytes(ctypes.byref(shape), int(S)))
 
 
+def _staging_bytes(shape: ep_shape, sources: dict, seg: int) -> int:
+    rows = shape.R * int(sources["S"]) * max(int(sources["capacity"]), 0)
+    return rows * max(ep_chunked_record_bytes(shape, seg or EP_SEG_BF16), 0)
+
+
 def ep_source_layout(shape, topk_idx, sources: dict, ws, stream=None):
-    X = _sources_struct(sources)
-    _check(lib().ep_source_layout(ctypes.byref(shape), _ptr(topk_idx), ctypes.byref(X), _ptr(ws),
-                                  ws.numel() * ws.element_size(), _stream(stream)),
-           "ep_source_layout")
+    X = _sources_struct(shape, sources)
+    _check(lib().ep_source_layout(ctypes.byref(shape), _ptr(topk_idx, "topk_idx", 8 * shape.T * shape.K),
+                                  ctypes.byref(X), *_ws(ws), _stream(stream)), "ep_source_layout")
 
 
 def ep_source_dispatch(shape, sources: dict, tokens: dict, epoch: int, staging, ws, stream=None):
-    X = _sources_struct(sources)
-    tk = _tokens_struct(tokens)
+    X = _sources_struct(shape, sources)
+    tk = _tokens_struct(shape, tokens)
     _check(lib().ep_source_dispatch(ctypes.byref(shape), ctypes.byref(X), ctypes.byref(tk),
-                                    int(epoch), _ptr(staging), _ptr(ws),
-                                    ws.numel() * ws.element_size(), _stream(stream)),
-           "ep_source_dispatch")
+                                    int(epoch),
+                                    _ptr(staging, "staging", _staging_bytes(shape, sources, _seg_of(tokens))),
+                                    *_ws(ws), _stream(stream)), "ep_source_dispatch")
 
 
 def ep_copy_epilogue(shape, sources: dict, staging, epoch: int, seg_flags: int, recv: dict,
                      capacity: int, ws, stream=None):
-    X = _sources_struct(sources)
-    rv = _recv_struct(recv, capacity)
-    _check(lib().ep_copy_epilogue(ctypes.byref(shape), ctypes.byref(X), _ptr(staging), int(epoch),
-                                  int(seg_flags), ctypes.byref(rv), _ptr(ws),
-                                  ws.numel() * ws.element_size(), _stream(stream)),
-           "ep_copy_epilogue")
+    X = _sources_struct(shape, sources)
+    rv = _recv_struct(shape, recv, capacity)
+    _check(lib().ep_copy_epilogue(ctypes.byref(shape), ctypes.byref(X),
+                                  _ptr(staging, "staging", _staging_bytes(shape, sources, int(seg_flags))),
+                                  int(epoch), int(seg_flags), ctypes.byref(rv), *_ws(ws),
+                                  _stream(stream)), "ep_copy_epilogue")
 
 
 def ep_clear_errors(ws, stream=None):
-    _check(lib().ep_clear_errors(_ptr(ws), _stream(stream)), "ep_clear_errors")
+    _check(lib().ep_clear_errors(_ptr(ws, "workspace"), _stream(stream)), "ep_clear_errors")
 
 
 def ep_check_errors(ws, stream=None) -> int:
     bits = ctypes.c_uint32(0)
-    _check(lib().ep_check_errors(_ptr(ws), _stream(stream), ctypes.byref(bits)), "ep_check_errors")
+    _check(lib().ep_check_errors(_ptr(ws, "workspace"), _stream(stream), ctypes.byref(bits)),
+           "ep_check_errors")
     return int(bits.value)
 
 

@@ -138,3 +138,59 @@ def test_source_calls_checked_before_launch(lib):
                                 ctypes.byref(rv), ws, n, None) == ep.EP_ERR_ARG
     assert lib.ep_copy_epilogue(ctypes.byref(s), ctypes.byref(X), 0x5000, 1, ep.EP_SEG_FP8,
                                 ctypes.byref(rv), ws, n, None) == ep.EP_ERR_ARG  # no bf16 piece
+
+
+def test_binding_rejects_host_small_and_strided_tensors():
+    """The binding checks every tensor argument before the C call: on the GPU,
+    contiguous and at least as long as the shape needs (no GPU required: the
+    checks fire before any kernel could run)."""
+    import pytest
+    import torch
+
+    from combine_get_layout_amd import ep
+
+    shape = ep.make_shape(4, 16, 2, 8, 4, 1)
+    cpu = torch.zeros(4 * 2, dtype=torch.int64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ep._ptr(cpu, "topk_idx", 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ep._layout_struct(shape, dict(slot=torch.zeros((4, 2), dtype=torch.int32)))
+    assert ep._ptr(None, "x", 100) is None
+    assert ep._ptr(12345, "x", 100) == 12345  # a raw device address passes through
+
+
+class _FakeCuda:
+    """Minimal stand-in for a GPU tensor's metadata (no device needed)."""
+    def __init__(self, nbytes, contiguous=True):
+        self.is_cuda = True
+        self._n = nbytes
+        self._c = contiguous
+
+    def is_contiguous(self):
+        return self._c
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
+
+    def data_ptr(self):
+        return 4096
+
+
+def test_binding_size_and_stride_checks():
+    import pytest
+
+    from combine_get_layout_amd import ep
+
+    assert ep._ptr(_FakeCuda(64), "topk_idx", 64) == 4096
+    with pytest.raises(ValueError, match="needs 65"):
+        ep._ptr(_FakeCuda(64), "topk_idx", 65)
+    with pytest.raises(ValueError, match="contiguous"):
+        ep._ptr(_FakeCuda(64, contiguous=False), "x", 8)
+    shape = ep.make_shape(5, 256, 3, 12, 4, 2)
+    # recv rows: capacity * H * 2 bytes of bf16
+    with pytest.raises(ValueError, match="recv x"):
+        ep._recv_struct(shape, dict(x=_FakeCuda(10 * 256 * 2 - 2)), 10)
+    ep._recv_struct(shape, dict(x=_FakeCuda(10 * 256 * 2)), 10)
