@@ -31,6 +31,12 @@ namespace {
 
 constexpr int kPieceIters = 16;  // wave iterations (2 blocks each) held in VGPRs
 
+#ifndef EP_SO_SPLIT
+#define EP_SO_SPLIT 4  // scale-out: waves per token, each writing a run of the record's blocks (measured best of 1, 2, 4)
+#endif
+constexpr int kSoSplit = EP_SO_SPLIT;
+constexpr int kSoPiece = kPieceIters / kSoSplit;  // wave iterations a scale-out wave holds
+
 struct HierArgs {
     int T, H, K, E, R, G, epr, P;
     RecordGeom geom;
@@ -87,7 +93,8 @@ __device__ __forceinline__ u32x4 meta_vector(const HierArgs& a, int t, int q) {
 
 __global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
     const int lane = lane_id();
-    const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int gw = blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int t = gw / kSoSplit, part = gw % kSoSplit;
     if (t >= a.T) return;
     int gs = -1;
     if (lane < a.K) gs = a.group_slot[(int64_t)t * a.K + lane];
@@ -109,13 +116,16 @@ __global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
     const int q_fp8 = a.geom.q_fp8, q_meta = a.geom.q_scales;
     const uint8_t* x_row = a.x + (int64_t)t * a.H * 2;
     const uint8_t* f_row = a.x_fp8 ? a.x_fp8 + (int64_t)t * a.H : x_row;
-    for (int it0 = 0; it0 < iters; it0 += kPieceIters) {
-        u32x4 v[kPieceIters];
+    // This wave's run of wave-iterations of the record.
+    const int per = (iters + kSoSplit - 1) / kSoSplit;
+    const int it_lo = min(iters, part * per), it_hi = min(iters, it_lo + per);
+    for (int it0 = it_lo; it0 < it_hi; it0 += kSoPiece) {
+        u32x4 v[kSoPiece];
         // 1. Hidden vectors (bf16, then fp8): one unconditional load per
         //    iteration; lanes holding anything else load the row's first
         //    vector (in bounds, cached) and are overwritten below.
 #pragma unroll
-        for (int j = 0; j < kPieceIters; ++j) {
+        for (int j = 0; j < kSoPiece; ++j) {
             const int q = (2 * (it0 + j) + c_half) * kChunkPayloadVecs + w;
             const uint8_t* src = q < q_fp8 ? x_row + (int64_t)q * 16
                                  : (q < q_meta ? f_row + (int64_t)(q - q_fp8) * 16 : x_row);
@@ -123,22 +133,22 @@ __global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
         }
         // 2. Metadata and padding: only in the iterations that reach them.
 #pragma unroll
-        for (int j = 0; j < kPieceIters; ++j) {
+        for (int j = 0; j < kSoPiece; ++j) {
             const int q = (2 * (it0 + j) + c_half) * kChunkPayloadVecs + w;
             const int q_last = (2 * (it0 + j) + 2) * kChunkPayloadVecs - 1;  // wave-uniform
             if (q_last >= q_meta && w < kChunkPayloadVecs && q >= q_meta) v[j] = meta_vector(a, t, q);
         }
         // 3. Flags.
 #pragma unroll
-        for (int j = 0; j < kPieceIters; ++j)
+        for (int j = 0; j < kSoPiece; ++j)
             if (w >= kChunkPayloadVecs) v[j] = flag;
         for (uint64_t m = dest; m; m &= m - 1) {
             const int k = __ffsll((unsigned long long)m) - 1;
             uint8_t* row = a.group_buf + (int64_t)readlane(gs, k) * stride;
 #pragma unroll
-            for (int j = 0; j < kPieceIters; ++j) {
+            for (int j = 0; j < kSoPiece; ++j) {
                 const int c = 2 * (it0 + j) + c_half;
-                if (it0 + j < iters && c < nchunks)
+                if (it0 + j < it_hi && c < nchunks)
                     st16_stream(row + chunk_lane_offset(it0 + j, lane), v[j]);
             }
         }
@@ -278,7 +288,8 @@ hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& t
     a.peer_cap = peer_cap;
     const dim3 block(kBlockThreads);
     if ((steps & EP_HIER_SCALEOUT) && s.T > 0)
-        hipLaunchKernelGGL(scaleout_kernel, dim3((s.T + kWavesPerBlock - 1) / kWavesPerBlock), block, 0,
+        hipLaunchKernelGGL(scaleout_kernel,
+                           dim3((unsigned)(((int64_t)s.T * kSoSplit + kWavesPerBlock - 1) / kWavesPerBlock)), block, 0,
                            st, a);
     if ((steps & EP_HIER_FORWARD) && group_cap > 0) {
         const int64_t want = (group_cap + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -295,7 +306,8 @@ hipError_t launch_send_rows(const ep_shape& s, const ep_tokens& tk, const int32_
     a.group_slot = rows;
     a.group_buf = reinterpret_cast<uint8_t*>(buf);
     a.group_cap = n_rows;
-    hipLaunchKernelGGL(scaleout_kernel, dim3((s.T + kWavesPerBlock - 1) / kWavesPerBlock),
+    hipLaunchKernelGGL(scaleout_kernel,
+                       dim3((unsigned)(((int64_t)s.T * kSoSplit + kWavesPerBlock - 1) / kWavesPerBlock)),
                        dim3(kBlockThreads), 0, st, a);
     return hipGetLastError();
 }
