@@ -374,9 +374,17 @@ def run_hier(w, inp, shape, L, ws, tk, epoch, steps=3, group_buf=None, peer_buf=
     return group_buf, peer_buf, G_rows, N, stride
 
 
-@pytest.mark.parametrize("name,fp8", [("hier8x8", False), ("small", True), ("small", False)])
+@pytest.mark.parametrize("name,fp8", [("hier8x8", False), ("small", True), ("small", False),
+                                      ("big", True)])
 def test_hierarchical_full(name, fp8):
-    w = synth.workload(name) if name != "small" else synth.Workload("small", 1500, 1024, 64, 16, 4, 6, "uniform")
+    """("big", True): a 21.8 KB record of 46 blocks, more than one piece of
+    wave-iterations in both steps."""
+    if name == "small":
+        w = synth.Workload("small", 1500, 1024, 64, 16, 4, 6, "uniform")
+    elif name == "big":
+        w = synth.Workload("big", 300, 7168, 64, 16, 4, 8, "uniform")
+    else:
+        w = synth.workload(name)
     inp = synth.make_inputs(w, with_fp8=fp8)
     shape, L, ws, tk = run_layout(w, inp["topk_idx"])
     epoch = 5
