@@ -35,10 +35,13 @@
 #define EP_CMB_WPB 4        // waves per workgroup
 #endif
 #ifndef EP_CMB_ROWS
-#define EP_CMB_ROWS 1       // row-streaming kernel: 1 = plain rows, 2 = plain and chunked rows
+#define EP_CMB_ROWS 2       // row-streaming kernel: 1 = plain rows, 2 = plain and chunked rows
 #endif
 #ifndef EP_CMB_VPWMAX
 #define EP_CMB_VPWMAX 8     // row-streaming kernel: most wave-iterations per slice (4 or 8)
+#endif
+#ifndef EP_CMB_VPWMAX_CH
+#define EP_CMB_VPWMAX_CH 4  // row-streaming kernel on chunked rows: most wave-iterations per slice
 #endif
 #ifndef EP_CMB_DUP
 #define EP_CMB_DUP 1        // row-streaming kernel: keep one repeated row in VGPRs instead of re-reading it
@@ -249,15 +252,25 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_kernel(Combi
 // slice of row k as one burst of VPW 16-byte vectors per lane (the next row's
 // burst is requested before the current one is used) and accumulates it into
 // VPW x 8 fp32 registers. Same sums in the same order as combine_kernel.
+// Chunked rows: each slice checks the flags of its own blocks with the loads
+// that bring in the values. The slices of a token are waves of one workgroup
+// (the launch keeps `slices` a divisor of the waves per workgroup); they post
+// the rows whose flags failed to LDS and read each other's after one barrier,
+// which every wave of the workgroup reaches exactly once, so a bad row is
+// dropped for the whole token and the token is summed again without it (an
+// error path only; the second pass rewrites the output).
 template <int KMAX, int VPW, bool CHUNKED>
 __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(CombineArgs a, int slices) {
+    __shared__ uint32_t drop_lds[CHUNKED ? 2 * kCmbWaves : 1];
     const int lane = lane_id();
-    const int gw = blockIdx.x * kCmbWaves + wave_in_block();
+    const int wave = wave_in_block();
+    const int gw = blockIdx.x * kCmbWaves + wave;
     const int t = gw / slices, part = gw % slices;
-    if (t >= a.T) return;
+    const bool live = t < a.T;
+    if (!CHUNKED && !live) return;
     int s = -1;
     float wt = 0.f;
-    if (lane < a.K) {
+    if (live && lane < a.K) {
         s = a.slot[(int64_t)t * a.K + lane];
         wt = a.w[(int64_t)t * a.K + lane];
     }
@@ -271,121 +284,116 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(
     const int nch = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
     const int iters = CHUNKED ? (nch + 1) / 2 : (nvh + kWave - 1) / kWave;
     const int it0 = part * VPW;
-    uint8_t* out_row = reinterpret_cast<uint8_t*>(a.out) + (int64_t)t * a.H * 2;
+    uint8_t* out_row = reinterpret_cast<uint8_t*>(a.out) + (int64_t)(live ? t : 0) * a.H * 2;
     int p[VPW];
     int64_t off[VPW];
     bool valid[VPW], flag[VPW];
 #pragma unroll
     for (int j = 0; j < VPW; ++j) {
-        const bool in = it0 + j < iters;
+        const bool in = live && it0 + j < iters;
         valid[j] = in && lane_vector<CHUNKED>(it0 + j, lane, nvh, p[j], off[j]);
         flag[j] = CHUNKED && in && (lane & 31) >= kChunkPayloadVecs && 2 * (it0 + j) + (lane >> 5) < nch;
         if (!valid[j] && !flag[j]) off[j] = 0;
     }
     for (int pass = 0; pass < 2; ++pass) {
+        uint32_t bad = 0;  // per lane: bit k = a flag of row k checked by this lane is wrong
         if (!um) {
 #pragma unroll
             for (int j = 0; j < VPW; ++j)
                 if (valid[j]) st16_stream(out_row + (int64_t)p[j] * 16, u32x4{0u, 0u, 0u, 0u});
-            return;
-        }
-        const int s_any = readlane(s, __ffsll((unsigned long long)um) - 1);
-        // A rank reached by two lanes of the token shares one row. The first
-        // such row (lowest lane k1) is kept in VGPRs after its use, and the
-        // later lanes with the same row take it from there instead of
-        // loading it again (kept: lanes that read the kept copy).
-        uint64_t kept = 0;
-        int k1 = KMAX;
+        } else {
+            const int s_any = readlane(s, __ffsll((unsigned long long)um) - 1);
+            // A rank reached by two lanes of the token shares one row. The
+            // first such row (lowest lane k1) is kept in VGPRs after its use,
+            // and the later lanes with the same row take it from there instead
+            // of loading it again (kept: lanes that read the kept copy).
+            uint64_t kept = 0;
+            int k1 = KMAX;
 #if EP_CMB_DUP
-        {
-            bool d = false;
-            for (int j = 0; j < a.K; ++j) {
-                const int sj = readlane(s, j);
-                if (j < lane && ((um >> j) & 1) && sj == s) d = true;
-            }
-            const uint64_t dupm = __ballot(use && d);
-            if (dupm) {
-                const int kd = __ffsll((unsigned long long)dupm) - 1;  // first repeating lane
-                const int sd = readlane(s, kd);
-                const uint64_t same = __ballot(use && s == sd);
-                k1 = __ffsll((unsigned long long)same) - 1;
-                kept = same & ~(1ull << k1);
-            }
-        }
-#endif
-        float acc[VPW][8];
-#pragma unroll
-        for (int j = 0; j < VPW; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
-        uint32_t bad = 0;
-        u32x4 buf[2][VPW];
-        u32x4 keep[EP_CMB_DUP ? VPW : 1];
-        auto row_of = [&](int k) {
-            const int kk = min(k, a.K - 1);
-            return a.y + (int64_t)(((um >> k) & 1) ? readlane(s, kk) : s_any) * a.stride;
-        };
-        {
-            const uint8_t* r0 = row_of(0);
-#pragma unroll
-            for (int j = 0; j < VPW; ++j) buf[0][j] = ld_row(r0 + off[j]);
-        }
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            if (k + 1 < KMAX && !((kept >> (k + 1)) & 1)) {
-                const uint8_t* rn = row_of(k + 1);
-#pragma unroll
-                for (int j = 0; j < VPW; ++j) buf[(k + 1) & 1][j] = ld_row(rn + off[j]);
-            }
-            const float wk = readlane_f(wt, min(k, a.K - 1));
-            const bool uk = (um >> k) & 1;
-#if EP_CMB_DUP
-            const bool from_keep = (kept >> k) & 1;
-            if (k == k1) {
-#pragma unroll
-                for (int j = 0; j < VPW; ++j) keep[j] = buf[k & 1][j];
-            }
-#endif
-#pragma unroll
-            for (int j = 0; j < VPW; ++j) {
-#if EP_CMB_DUP
-                const u32x4 v = from_keep ? keep[j] : buf[k & 1][j];
-#else
-                const u32x4 v = buf[k & 1][j];
-#endif
-                if (CHUNKED) {
-                    const bool ok = v[0] == a.epoch && v[1] == a.epoch && v[2] == a.epoch && v[3] == a.epoch;
-                    bad |= (flag[j] && !ok) ? (1u << k) : 0u;
+            {
+                bool d = false;
+                for (int j = 0; j < a.K; ++j) {
+                    const int sj = readlane(s, j);
+                    if (j < lane && ((um >> j) & 1) && sj == s) d = true;
                 }
-                if (uk) fma8(acc[j], wk, v);
+                const uint64_t dupm = __ballot(use && d);
+                if (dupm) {
+                    const int kd = __ffsll((unsigned long long)dupm) - 1;  // first repeating lane
+                    const int sd = readlane(s, kd);
+                    const uint64_t same = __ballot(use && s == sd);
+                    k1 = __ffsll((unsigned long long)same) - 1;
+                    kept = same & ~(1ull << k1);
+                }
             }
-        }
+#endif
+            float acc[VPW][8];
 #pragma unroll
-        for (int j = 0; j < VPW; ++j)
-            if (valid[j]) st16_stream(out_row + (int64_t)p[j] * 16, pack8(acc[j]));
-        if (!CHUNKED) return;
-        // A bad flag anywhere in a row drops the row for the whole token: the
-        // slices compare notes through the shared row flags, so every slice
-        // checks all flags of the rows it uses (see below) before finishing.
+            for (int j = 0; j < VPW; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+            u32x4 buf[2][VPW];
+            u32x4 keep[EP_CMB_DUP ? VPW : 1];
+            auto row_of = [&](int k) {
+                const int kk = min(k, a.K - 1);
+                return a.y + (int64_t)(((um >> k) & 1) ? readlane(s, kk) : s_any) * a.stride;
+            };
+            {
+                const uint8_t* r0 = row_of(0);
+#pragma unroll
+                for (int j = 0; j < VPW; ++j) buf[0][j] = ld_row(r0 + off[j]);
+            }
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (k + 1 < KMAX && !((kept >> (k + 1)) & 1)) {
+                    const uint8_t* rn = row_of(k + 1);
+#pragma unroll
+                    for (int j = 0; j < VPW; ++j) buf[(k + 1) & 1][j] = ld_row(rn + off[j]);
+                }
+                const float wk = readlane_f(wt, min(k, a.K - 1));
+                const bool uk = (um >> k) & 1;
+#if EP_CMB_DUP
+                const bool from_keep = (kept >> k) & 1;
+                if (k == k1) {
+#pragma unroll
+                    for (int j = 0; j < VPW; ++j) keep[j] = buf[k & 1][j];
+                }
+#endif
+#pragma unroll
+                for (int j = 0; j < VPW; ++j) {
+#if EP_CMB_DUP
+                    const u32x4 v = from_keep ? keep[j] : buf[k & 1][j];
+#else
+                    const u32x4 v = buf[k & 1][j];
+#endif
+                    if (CHUNKED) {
+                        const bool ok = v[0] == a.epoch && v[1] == a.epoch && v[2] == a.epoch && v[3] == a.epoch;
+                        bad |= (flag[j] && uk && !ok) ? (1u << k) : 0u;
+                    }
+                    if (uk) fma8(acc[j], wk, v);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < VPW; ++j)
+                if (valid[j]) st16_stream(out_row + (int64_t)p[j] * 16, pack8(acc[j]));
+        }
+        if (!CHUNKED || pass == 1) return;
+        // The rows whose flags failed in this slice's blocks, then in any
+        // slice of the token.
         uint64_t drop = 0;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
             if (((um >> k) & 1) && __ballot((bad >> k) & 1)) drop |= 1ull << k;
-        // Flags outside this slice: checked here so that all slices agree.
-        for (uint64_t m = um & ~drop; m; m &= m - 1) {
-            const int k = __ffsll((unsigned long long)m) - 1;
-            const uint8_t* row = a.y + (int64_t)readlane(s, k) * a.stride;
-            bool ok = true;
-            for (int i = lane; i < 2 * nch; i += kWave) {
-                const int c = i >> 1;
-                if (c >= 2 * it0 && c < 2 * (it0 + VPW)) continue;  // already checked in-slice
-                const u32x4 f = ld16(row + (int64_t)c * kChunkBytes + kChunkPayload + (i & 1) * 16);
-                ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
-            }
-            if (__ballot(!ok)) drop |= 1ull << k;
+        if (lane == 0) {
+            drop_lds[2 * wave] = (uint32_t)drop;
+            drop_lds[2 * wave + 1] = (uint32_t)(drop >> 32);
         }
-        if (!drop) return;
+        __syncthreads();
+        const int w0 = wave - part;  // first wave of this token in the workgroup
+        for (int q = 0; q < slices; ++q)
+            drop |= ((uint64_t)drop_lds[2 * (w0 + q) + 1] << 32) | drop_lds[2 * (w0 + q)];
+        if (!drop || !live) return;
         if (lane == 0 && part == 0) report(a.err, EP_DEVERR_FLAG);
+        // Every lane reading a dropped row drops with it.
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
             if ((drop >> k) & 1) drop |= __ballot(use && s == readlane(s, min(k, a.K - 1)));
@@ -397,17 +405,20 @@ template <bool CHUNKED>
 hipError_t launch_k(const CombineArgs& a, hipStream_t st) {
     const dim3 block(kCmbThreads);
 #if EP_CMB_ROWS
-    if (a.K <= 8 && (!CHUNKED || EP_CMB_ROWS >= 2)) {
+    if (a.K <= 8) {
         const int nch = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
         const int iters = CHUNKED ? (nch + 1) / 2 : (a.H / 8 + kWave - 1) / kWave;
-        const int vpw = iters > 8 && EP_CMB_VPWMAX >= 8 ? 8 : 4;
+        const int vpw = iters > 8 && (CHUNKED ? EP_CMB_VPWMAX_CH : EP_CMB_VPWMAX) >= 8 ? 8 : 4;
         const int slices = (iters + vpw - 1) / vpw;
-        const dim3 grid((unsigned)(((int64_t)a.T * slices + kCmbWaves - 1) / kCmbWaves));
-        if (vpw == 8)
-            hipLaunchKernelGGL((combine_rows_kernel<8, 8, CHUNKED>), grid, block, 0, st, a, slices);
-        else
-            hipLaunchKernelGGL((combine_rows_kernel<8, 4, CHUNKED>), grid, block, 0, st, a, slices);
-        return hipGetLastError();
+        // Chunked rows need the slices of a token inside one workgroup.
+        if (!CHUNKED || (EP_CMB_ROWS >= 2 && kCmbWaves % slices == 0)) {
+            const dim3 grid((unsigned)(((int64_t)a.T * slices + kCmbWaves - 1) / kCmbWaves));
+            if (vpw == 8)
+                hipLaunchKernelGGL((combine_rows_kernel<8, 8, CHUNKED>), grid, block, 0, st, a, slices);
+            else
+                hipLaunchKernelGGL((combine_rows_kernel<8, 4, CHUNKED>), grid, block, 0, st, a, slices);
+            return hipGetLastError();
+        }
     }
 #endif
     const dim3 grid((a.T + kCmbWaves - 1) / kCmbWaves);
