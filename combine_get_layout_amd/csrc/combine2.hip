@@ -26,6 +26,10 @@
 #include "ep_device.h"
 #include "ep_internal.h"
 
+#ifndef EP_C2_ROWS
+#define EP_C2_ROWS 1  // group step: row-streaming kernel when K <= 8 (0 = one wave per token)
+#endif
+
 namespace ep {
 namespace {
 
@@ -52,6 +56,13 @@ __device__ __forceinline__ bool chunk_vec(int it, int lane, int nvh, int& c, int
     wv = lane & 31;
     p = c * kChunkPayloadVecs + wv;
     return wv < kChunkPayloadVecs && p < nvh;
+}
+
+__device__ __forceinline__ u32x4 pack8(const float (&acc)[8]) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16);
+    return o;
 }
 
 __device__ __forceinline__ bool flag_ok(u32x4 f, uint32_t epoch) {
@@ -195,6 +206,187 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_kernel(Combine2Ar
     }
 }
 
+// Row-streaming group step (K <= 8): a token is cut into slices of VPW
+// wave-iterations, one wave per slice, the slices of a token in one
+// workgroup. The token's used lanes are walked in (group, lane) order, the
+// order of the set bits of seq = sum over groups gi of (lanes of gi) << 8 gi.
+// Each lane's slice of its row is read once as one burst, the next lane's
+// burst requested before the current one is used, and accumulated into one
+// VPW x 8 fp32 set; when the next lane belongs to another group (or none is
+// left) the set is rounded and stored as the group's partial slice. Groups
+// with no usable lane get a zero partial. Chunked rows: each slice checks the
+// flags of its own blocks with the same loads; the slices post the rows whose
+// flags failed to LDS and meet at one barrier (reached once by every wave of
+// the workgroup), and a token with a dropped row is computed again without
+// it (error path only; the second pass rewrites the partial slices).
+template <int VPW>
+__global__ __launch_bounds__(kBlockThreads) void combine_group_rows_kernel(Combine2Args a, int slices) {
+    constexpr int KMAX = 8;
+    __shared__ uint32_t drop_lds[kWavesPerBlock];
+    const int lane = lane_id(), wave = wave_in_block();
+    const int gw = blockIdx.x * kWavesPerBlock + wave;
+    const int t = gw / slices, part = gw % slices;
+    const bool live = t < a.T;
+    int s = -1, g = -1, gs = -1;
+    float wt = 0.f;
+    if (live && lane < a.K) {
+        const int64_t e = a.topk[(int64_t)t * a.K + lane];
+        s = a.slot[(int64_t)t * a.K + lane];
+        gs = a.group_slot[(int64_t)t * a.K + lane];
+        wt = a.w[(int64_t)t * a.K + lane];
+        if (expert_ok(e, a.E)) g = ((int)e / a.epr) / a.P;
+    }
+    bool use = s >= 0 && g >= 0;
+    if (use && s >= a.y_rows) {
+        if (part == 0) report(a.err, EP_DEVERR_CAPACITY);
+        use = false;
+    }
+    uint64_t um = __ballot(use);
+    const int nvh = a.H / 8;
+    const int nblk = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
+    const int iters = (nblk + 1) / 2;
+    const int it0 = part * VPW;
+    // Groups of this token (first lane of each, in lane order) and the
+    // position of each lane's group.
+    bool first = g >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int gj = readlane(g, j);
+        if (j < lane && gj == g) first = false;
+    }
+    const uint64_t fm = __ballot(first);
+    int gpos = -1;
+    for (uint64_t m = fm; m; m &= m - 1) {
+        const int k0 = __ffsll((unsigned long long)m) - 1;
+        if (readlane(g, k0) == g) gpos = __popcll(fm & ((1ull << k0) - 1));
+    }
+    // Partial row of each group position; rows past the capacity are not written.
+    int64_t pdst[KMAX];
+    uint32_t wmask = 0;
+#pragma unroll
+    for (int gi = 0; gi < KMAX; ++gi) {
+        pdst[gi] = 0;
+        const uint64_t who = __ballot(((fm >> lane) & 1) && gpos == gi);
+        if (!who) continue;
+        const int64_t dst = readlane(gs, __ffsll((unsigned long long)who) - 1);
+        if (dst >= a.group_cap) {
+            if (lane == 0 && part == 0) report(a.err, EP_DEVERR_CAPACITY);
+            continue;
+        }
+        pdst[gi] = dst;
+        wmask |= 1u << gi;
+    }
+    // This lane's vectors of the slice: read offset in a row, whether it is a
+    // hidden vector or a flag vector of a hidden block, and whether the
+    // partial row has a vector there.
+    int p[VPW];
+    int64_t off[VPW], o_off[VPW];
+    bool hv[VPW], fl[VPW], st[VPW], fw[VPW];
+#pragma unroll
+    for (int j = 0; j < VPW; ++j) {
+        int c, wv;
+        const bool in = live && it0 + j < iters;
+        const bool hvec = chunk_vec(it0 + j, lane, nvh, c, wv, p[j]);
+        hv[j] = in && hvec;
+        fl[j] = in && a.y_chunked && wv >= kChunkPayloadVecs && c < nblk;
+        const int64_t blk = (int64_t)c * kChunkBytes + (int64_t)wv * 16;
+        off[j] = hv[j] ? (a.y_chunked ? blk : (int64_t)p[j] * 16) : (fl[j] ? blk : 0);
+        st[j] = in && c < nblk;
+        fw[j] = wv >= kChunkPayloadVecs;
+        o_off[j] = blk;
+    }
+    const u32x4 flagv = {a.epoch, a.epoch, a.epoch, a.epoch};
+    auto store_partial = [&](int gi, const float (&acc)[VPW][8], bool zero) {
+        if (!((wmask >> gi) & 1)) return;
+        int64_t dst = 0;
+#pragma unroll
+        for (int q = 0; q < KMAX; ++q) dst = q == gi ? pdst[q] : dst;
+        uint8_t* prow = a.group_buf + dst * a.pstride;
+#pragma unroll
+        for (int j = 0; j < VPW; ++j) {
+            if (!st[j]) continue;
+            u32x4 o = {0u, 0u, 0u, 0u};
+            if (hv[j] && !zero) o = pack8(acc[j]);
+            if (fw[j]) o = flagv;
+            st16_stream(prow + o_off[j], o);
+        }
+    };
+    for (int pass = 0; pass < 2; ++pass) {
+        uint32_t bad = 0;  // per lane: bit k = a flag of row k checked by this lane is wrong
+        // Lanes in (group, lane) order.
+        uint64_t seq = 0;
+#pragma unroll
+        for (int gi = 0; gi < KMAX; ++gi)
+            seq |= (uint64_t)(__ballot(((um >> lane) & 1) && gpos == gi) & 0xFFu) << (8 * gi);
+        uint32_t stored = 0;
+        if (seq && live) {
+            float acc[VPW][8];
+#pragma unroll
+            for (int j = 0; j < VPW; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+            int cur = __ffsll((unsigned long long)seq) - 1;
+            uint64_t rest = seq & (seq - 1);
+            u32x4 vc[VPW], vn[VPW];
+            {
+                const uint8_t* r0 = a.y + (int64_t)readlane(s, cur & 7) * a.y_stride;
+#pragma unroll
+                for (int j = 0; j < VPW; ++j) vc[j] = ld16(r0 + off[j]);
+            }
+            while (true) {
+                const int nxt = rest ? __ffsll((unsigned long long)rest) - 1 : -1;
+                if (nxt >= 0) {
+                    const uint8_t* rn = a.y + (int64_t)readlane(s, nxt & 7) * a.y_stride;
+#pragma unroll
+                    for (int j = 0; j < VPW; ++j) vn[j] = ld16(rn + off[j]);
+                }
+                const int k = cur & 7, gi = cur >> 3;
+                const float wk = readlane_f(wt, k);
+#pragma unroll
+                for (int j = 0; j < VPW; ++j) {
+                    if (fl[j] && !flag_ok(vc[j], a.epoch)) bad |= 1u << k;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[j][2 * q] = __builtin_fmaf(wk, bf16_lo(vc[j][q]), acc[j][2 * q]);
+                        acc[j][2 * q + 1] = __builtin_fmaf(wk, bf16_hi(vc[j][q]), acc[j][2 * q + 1]);
+                    }
+                }
+                if (nxt < 0 || (nxt >> 3) != gi) {
+                    store_partial(gi, acc, false);
+                    stored |= 1u << gi;
+#pragma unroll
+                    for (int j = 0; j < VPW; ++j)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+                }
+                if (nxt < 0) break;
+#pragma unroll
+                for (int j = 0; j < VPW; ++j) vc[j] = vn[j];
+                cur = nxt;
+                rest &= rest - 1;
+            }
+        }
+        if (live) {
+            float none[VPW][8];
+            for (uint32_t z = wmask & ~stored; z; z &= z - 1) store_partial(__ffs(z) - 1, none, true);
+        }
+        if (!a.y_chunked || pass == 1) return;
+        uint32_t drop = 0;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (((um >> k) & 1) && __ballot((bad >> k) & 1)) drop |= 1u << k;
+        if (lane == 0) drop_lds[wave] = drop;
+        __syncthreads();
+        const int w0 = wave - part;
+        for (int q = 0; q < slices; ++q) drop |= drop_lds[w0 + q];
+        if (!drop || !live) return;
+        if (lane == 0 && part == 0) report(a.err, EP_DEVERR_FLAG);
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if ((drop >> k) & 1) drop |= (uint32_t)__ballot(use && s == readlane(s, min(k, a.K - 1)));
+        um &= ~(uint64_t)drop;
+    }
+}
+
 template <int GMAX>
 __global__ __launch_bounds__(kBlockThreads) void combine_cross_kernel(Combine2Args a) {
     const int lane = lane_id();
@@ -323,7 +515,14 @@ hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const
     a.out = out;
     a.err = reinterpret_cast<uint32_t*>(ws + W.err);
     const dim3 grid((s.T + kWavesPerBlock - 1) / kWavesPerBlock), block(kBlockThreads);
-    if (steps & 1) {
+    const int nblk = (2 * s.H + kChunkPayload - 1) / kChunkPayload;
+    const int iters = (nblk + 1) / 2;
+    constexpr int kGroupVpw = 4;
+    const int slices = (iters + kGroupVpw - 1) / kGroupVpw;
+    if ((steps & 1) && s.K <= 8 && EP_C2_ROWS && (!a.y_chunked || kWavesPerBlock % slices == 0)) {
+        const dim3 g2((unsigned)(((int64_t)s.T * slices + kWavesPerBlock - 1) / kWavesPerBlock));
+        hipLaunchKernelGGL(combine_group_rows_kernel<kGroupVpw>, g2, block, 0, st, a, slices);
+    } else if (steps & 1) {
         if (s.K <= 2)
             hipLaunchKernelGGL(combine_group_kernel<2>, grid, block, 0, st, a);
         else if (s.K <= 4)
