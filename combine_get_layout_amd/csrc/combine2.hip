@@ -27,7 +27,7 @@
 #include "ep_internal.h"
 
 #ifndef EP_C2_ROWS
-#define EP_C2_ROWS 1  // group step: row-streaming kernel when K <= 8 (0 = one wave per token)
+#define EP_C2_ROWS 1  // both steps: row-streaming kernels when K <= 8 (0 = one wave per token)
 #endif
 
 namespace ep {
@@ -488,6 +488,133 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_kernel(Combine2Ar
     }
 }
 
+// Row-streaming cross-group step: slices of VPW wave-iterations, one wave per
+// slice, the slices of a token in one workgroup. The token's partial rows are
+// read in ascending group, one burst per row with the next row's burst
+// requested first, and summed in fp32; flags are checked by the flag lanes of
+// the same loads and exchanged between the slices through LDS at one barrier,
+// as in the group step.
+template <int VPW>
+__global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combine2Args a, int slices) {
+    constexpr int GMAX = 8;
+    __shared__ uint32_t drop_lds[kWavesPerBlock];
+    const int lane = lane_id(), wave = wave_in_block();
+    const int gw = blockIdx.x * kWavesPerBlock + wave;
+    const int t = gw / slices, part = gw % slices;
+    const bool live = t < a.T;
+    int g = -1, gs = -1;
+    if (live && lane < a.K) {
+        const int64_t e = a.topk[(int64_t)t * a.K + lane];
+        gs = a.group_slot[(int64_t)t * a.K + lane];
+        if (expert_ok(e, a.E)) g = ((int)e / a.epr) / a.P;
+    }
+    bool first = g >= 0 && gs >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int gj = readlane(g, j);
+        if (j < lane && gj == g) first = false;
+    }
+    if (first && gs >= a.group_cap) {
+        if (part == 0) report(a.err, EP_DEVERR_CAPACITY);
+        first = false;
+    }
+    uint64_t fm = __ballot(first);
+    const int nvh = a.H / 8;
+    const int nblk = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
+    const int iters = (nblk + 1) / 2;
+    const int it0 = part * VPW;
+    uint8_t* out_row = reinterpret_cast<uint8_t*>(a.out) + (int64_t)(live ? t : 0) * a.H * 2;
+    int p[VPW];
+    int64_t off[VPW];
+    bool hv[VPW], fl[VPW];
+#pragma unroll
+    for (int j = 0; j < VPW; ++j) {
+        int c, wv;
+        const bool in = live && it0 + j < iters;
+        const bool hvec = chunk_vec(it0 + j, lane, nvh, c, wv, p[j]);
+        hv[j] = in && hvec;
+        fl[j] = in && wv >= kChunkPayloadVecs && c < nblk;
+        off[j] = (hv[j] || fl[j]) ? (int64_t)c * kChunkBytes + (int64_t)wv * 16 : 0;
+    }
+    for (int pass = 0; pass < 2; ++pass) {
+        // Partial rows in ascending group: position = number of the token's
+        // partials with a smaller group.
+        int rank = 0;
+        for (uint64_t m = fm; m; m &= m - 1) {
+            const int j = __ffsll((unsigned long long)m) - 1;
+            rank += readlane(g, j) < g ? 1 : 0;
+        }
+        uint32_t posmask = 0;  // bit pos: a partial at position pos exists
+        int prow_lane[GMAX];   // lane holding the partial of each position
+#pragma unroll
+        for (int pos = 0; pos < GMAX; ++pos) {
+            const uint64_t who = __ballot(((fm >> lane) & 1) && rank == pos);
+            prow_lane[pos] = who ? __ffsll((unsigned long long)who) - 1 : 0;
+            posmask |= who ? (1u << pos) : 0u;
+        }
+        uint32_t bad = 0;  // per lane: bit pos = a flag of partial `pos` checked by this lane is wrong
+        float acc[VPW][8];
+#pragma unroll
+        for (int j = 0; j < VPW; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+        if (posmask && live) {
+            u32x4 vc[VPW], vn[VPW];
+            auto row_at = [&](int pos) {
+                int ln = 0;
+#pragma unroll
+                for (int q = 0; q < GMAX; ++q) ln = q == pos ? prow_lane[q] : ln;
+                return a.group_buf + (int64_t)readlane(gs, ln) * a.pstride;
+            };
+            int cur = __ffs(posmask) - 1;
+            uint32_t rest = posmask & (posmask - 1);
+            {
+                const uint8_t* r0 = row_at(cur);
+#pragma unroll
+                for (int j = 0; j < VPW; ++j) vc[j] = ld16(r0 + off[j]);
+            }
+            while (true) {
+                const int nxt = rest ? __ffs(rest) - 1 : -1;
+                if (nxt >= 0) {
+                    const uint8_t* rn = row_at(nxt);
+#pragma unroll
+                    for (int j = 0; j < VPW; ++j) vn[j] = ld16(rn + off[j]);
+                }
+#pragma unroll
+                for (int j = 0; j < VPW; ++j) {
+                    if (fl[j] && !flag_ok(vc[j], a.epoch)) bad |= 1u << cur;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[j][2 * q] = acc[j][2 * q] + bf16_lo(vc[j][q]);
+                        acc[j][2 * q + 1] = acc[j][2 * q + 1] + bf16_hi(vc[j][q]);
+                    }
+                }
+                if (nxt < 0) break;
+#pragma unroll
+                for (int j = 0; j < VPW; ++j) vc[j] = vn[j];
+                cur = nxt;
+                rest &= rest - 1;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VPW; ++j)
+            if (hv[j]) st16_stream(out_row + (int64_t)p[j] * 16, pack8(acc[j]));
+        if (pass == 1) return;
+        uint32_t badpos = 0;
+#pragma unroll
+        for (int pos = 0; pos < GMAX; ++pos)
+            if (((posmask >> pos) & 1) && __ballot((bad >> pos) & 1)) badpos |= 1u << pos;
+        // Exchange as lane masks (positions depend on which rows survive).
+        uint32_t drop = (uint32_t)__ballot(((fm >> lane) & 1) && ((badpos >> rank) & 1));
+        if (lane == 0) drop_lds[wave] = drop;
+        __syncthreads();
+        const int w0 = wave - part;
+        for (int q = 0; q < slices; ++q) drop |= drop_lds[w0 + q];
+        if (!drop || !live) return;
+        if (lane == 0 && part == 0) report(a.err, EP_DEVERR_FLAG);
+        fm &= ~(uint64_t)drop;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const int64_t* topk,
@@ -532,7 +659,10 @@ hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const
         else
             hipLaunchKernelGGL(combine_group_kernel<16>, grid, block, 0, st, a);
     }
-    if (steps & 2) {
+    if ((steps & 2) && s.K <= 8 && EP_C2_ROWS && kWavesPerBlock % slices == 0) {
+        const dim3 g2((unsigned)(((int64_t)s.T * slices + kWavesPerBlock - 1) / kWavesPerBlock));
+        hipLaunchKernelGGL(combine_cross_rows_kernel<kGroupVpw>, g2, block, 0, st, a, slices);
+    } else if (steps & 2) {
         if (s.K <= 8)
             hipLaunchKernelGGL(combine_cross_kernel<8>, grid, block, 0, st, a);
         else
