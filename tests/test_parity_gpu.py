@@ -413,7 +413,8 @@ def test_hierarchical_full(name, fp8):
     (300, 512, 4, 32, 8, 1, "uniform"),     # one group holding every rank
     (129, 1032, 12, 48, 16, 4, "uniform"),  # K > 8, hidden row not a whole number of blocks
     (1, 8, 1, 4, 2, 2, "uniform"),          # one token, one lane
-    (400, 256, 5, 20, 10, 5, "random")])    # skipped lanes and repeated experts
+    (400, 256, 5, 20, 10, 5, "random"),     # skipped lanes and repeated experts
+    (300, 4608, 6, 24, 8, 4, "uniform")])   # 20 hidden blocks: slices that do not fill a workgroup
 def test_hierarchical_edges(T, H, K, E, R, G, ids):
     w = synth.Workload("edge", T, H, E, R, G, K, "uniform")
     inp = synth.make_inputs(w)
@@ -608,9 +609,16 @@ def run_two_level(shape, L, tk, y, y_rows, y_stride, fmt, epoch, w_dev, steps=3,
     return group_buf, out, gcap
 
 
-@pytest.mark.parametrize("name", ["hier8x8", "small"])
+@pytest.mark.parametrize("name", ["hier8x8", "small", "mid"])
 def test_two_level_combine_chunked(name):
-    w = synth.workload(name) if name != "small" else synth.Workload("small", 900, 1024, 64, 16, 4, 6, "uniform")
+    """"mid": 20 hidden blocks per row, whose 3 slices do not fill a
+    workgroup, so both steps take the one-wave-per-token kernels."""
+    if name == "small":
+        w = synth.Workload("small", 900, 1024, 64, 16, 4, 6, "uniform")
+    elif name == "mid":
+        w = synth.Workload("mid", 500, 4608, 64, 16, 4, 8, "uniform")
+    else:
+        w = synth.workload(name)
     inp = synth.make_inputs(w)
     shape, L, ws, tk = run_layout(w, inp["topk_idx"])
     L["_ws"] = ws
