@@ -102,6 +102,8 @@ LAYOUT_EDGES = [
     (513, 4, 16, 1, 1, "random"),      # one rank
     (640, 8, 4096, 1024, 256, "uniform"),  # largest supported R, G, E
     (200, 4, 16, 4, 2, "one_rank"),    # all tokens to one rank, empty ranks
+    (700, 64, 128, 16, 4, "random"),   # largest supported K
+    (70000, 2, 64, 8, 2, "uniform"),   # 274 layout workgroups (many row batches)
 ]
 
 
@@ -189,7 +191,8 @@ def test_dispatch_full_size(name, fp8):
 
 
 @pytest.mark.parametrize("T,H,K,E,R", [(1, 8, 1, 4, 2), (3, 1032, 3, 12, 6), (1001, 4096, 20, 64, 16),
-                                       (257, 16, 8, 64, 64), (500, 384, 4, 16, 1)])
+                                       (257, 16, 8, 64, 64), (500, 384, 4, 16, 1),
+                                       (300, 256, 64, 256, 64)])
 def test_dispatch_edges(T, H, K, E, R):
     w = synth.Workload("edge", T, H, E, R, 1, K, "uniform")
     rng = np.random.default_rng(T * 7 + H)
@@ -293,7 +296,7 @@ def test_combine_full_size(name):
 
 
 @pytest.mark.parametrize("T,H,K", [(1, 8, 1), (77, 1032, 3), (300, 264, 2), (129, 512, 5),
-                                   (64, 2048, 16), (33, 128, 24)])
+                                   (64, 2048, 16), (33, 128, 24), (40, 512, 64)])
 def test_combine_edges(T, H, K):
     rng = np.random.default_rng(T + H + K)
     rows = 3 * T + 1
