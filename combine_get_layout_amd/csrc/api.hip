@@ -106,7 +106,7 @@ int ep_get_layout(const ep_shape* shape, const int64_t* topk_idx, const ep_layou
     if (!layout || (shape->T > 0 && !topk_idx) || !aligned(topk_idx, 8)) return EP_ERR_ARG;
     const ep_layout& L = *layout;
     if (!aligned(L.is_token_in_rank, 16) || !aligned(L.is_token_in_group, 16)) return EP_ERR_ARG;
-    if (L.expert_slot && (!L.expert_offsets || shape->K > 16)) return L.expert_offsets ? EP_ERR_UNSUPPORTED : EP_ERR_ARG;
+    if (L.expert_slot && !L.expert_offsets) return EP_ERR_ARG;
     const void* i32s[] = {L.tokens_per_expert, L.tokens_per_rank, L.tokens_per_group,
                           L.expert_offsets, L.rank_offsets, L.group_offsets, L.slot,
                           L.group_slot, L.expert_slot};
@@ -222,7 +222,6 @@ int ep_combine_two_level(const ep_shape* shape, const ep_layout* layout, const i
                          void* stream) {
     int rc = check_shape(shape);
     if (rc != EP_OK) return rc;
-    if (shape->K > 16) return EP_ERR_UNSUPPORTED;
     if ((rc = check_ws(shape, ws, ws_bytes)) != EP_OK) return rc;
     if (!layout || y_rows < 0 || group_cap < 0 || epoch == 0 || steps < 1 || steps > 3) return EP_ERR_ARG;
     if (y_format != EP_FMT_PLAIN && y_format != EP_FMT_CHUNKED) return EP_ERR_ARG;

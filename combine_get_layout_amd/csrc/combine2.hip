@@ -615,6 +615,182 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combi
     }
 }
 
+// Whether every flag vector of the first `nblk` blocks of chunked row `row`
+// equals epoch; the wave's lanes take the 2 * nblk flag vectors between them.
+__device__ __forceinline__ bool row_flags_ok(const uint8_t* row, int nblk, uint32_t epoch, int lane) {
+    bool bad = false;
+    for (int j = lane; j < 2 * nblk; j += kWave)
+        bad |= !flag_ok(ld16(row + (int64_t)(j >> 1) * kChunkBytes + kChunkPayload + (j & 1) * 16), epoch);
+    return __ballot(bad) == 0;
+}
+
+constexpr int kAnyBatch = 4;  // rows per load batch in the any-K kernels
+
+// Group step for any K (used when K > 16): one wave per token. With chunked
+// rows the flags of each usable lane's row are checked first, so a row with
+// a bad flag is left out before any of its values is used. Then the token's
+// groups are taken one at a time: per wave-iteration the group's lanes are
+// read in ascending k, kAnyBatch rows per load batch, accumulated into one
+// fp32 set and stored as the group's partial vectors.
+__global__ __launch_bounds__(kBlockThreads) void combine_group_any_kernel(Combine2Args a) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+    if (t >= a.T) return;
+    int s = -1, g = -1, gs = -1;
+    float wt = 0.f;
+    if (lane < a.K) {
+        const int64_t e = a.topk[(int64_t)t * a.K + lane];
+        s = a.slot[(int64_t)t * a.K + lane];
+        gs = a.group_slot[(int64_t)t * a.K + lane];
+        wt = a.w[(int64_t)t * a.K + lane];
+        if (expert_ok(e, a.E)) g = ((int)e / a.epr) / a.P;
+    }
+    bool use = s >= 0 && g >= 0;
+    if (use && s >= a.y_rows) {
+        report(a.err, EP_DEVERR_CAPACITY);
+        use = false;
+    }
+    uint64_t um = __ballot(use);
+    const int nvh = a.H / 8;
+    const int nblk = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
+    const int iters = (nblk + 1) / 2;
+    if (a.y_chunked) {
+        uint64_t drop = 0;
+        for (uint64_t m = um; m; m &= m - 1) {
+            const int k = __ffsll((unsigned long long)m) - 1;
+            if (!row_flags_ok(a.y + (int64_t)readlane(s, k) * a.y_stride, nblk, a.epoch, lane))
+                drop |= 1ull << k;
+        }
+        if (drop && lane == 0) report(a.err, EP_DEVERR_FLAG);
+        um &= ~drop;
+    }
+    bool first = g >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int gj = readlane(g, j);
+        if (j < lane && gj == g) first = false;
+    }
+    const u32x4 flagv = {a.epoch, a.epoch, a.epoch, a.epoch};
+    for (uint64_t fm = __ballot(first); fm; fm &= fm - 1) {
+        const int k0 = __ffsll((unsigned long long)fm) - 1;
+        const int g0 = readlane(g, k0);
+        const int64_t dst = readlane(gs, k0);
+        if (dst >= a.group_cap) {
+            if (lane == 0) report(a.err, EP_DEVERR_CAPACITY);
+            continue;
+        }
+        uint8_t* prow = a.group_buf + dst * a.pstride;
+        const uint64_t gm = um & __ballot(g == g0);
+        for (int it = 0; it < iters; ++it) {
+            int c, wv, p;
+            const bool hv = chunk_vec(it, lane, nvh, c, wv, p);
+            const int64_t blk = (int64_t)c * kChunkBytes + (int64_t)wv * 16;
+            const int64_t off = a.y_chunked ? blk : (int64_t)p * 16;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (uint64_t m = gm; m;) {
+                int kk[kAnyBatch];
+                int nk = 0;
+                for (; nk < kAnyBatch && m; ++nk, m &= m - 1) kk[nk] = __ffsll((unsigned long long)m) - 1;
+                u32x4 v[kAnyBatch];
+#pragma unroll
+                for (int j = 0; j < kAnyBatch; ++j) {
+                    v[j] = u32x4{0u, 0u, 0u, 0u};
+                    if (j < nk && hv) v[j] = ld16(a.y + (int64_t)readlane(s, kk[j]) * a.y_stride + off);
+                }
+#pragma unroll
+                for (int j = 0; j < kAnyBatch; ++j) {
+                    if (j >= nk) break;
+                    const float wk = readlane_f(wt, kk[j]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[2 * q] = __builtin_fmaf(wk, bf16_lo(v[j][q]), acc[2 * q]);
+                        acc[2 * q + 1] = __builtin_fmaf(wk, bf16_hi(v[j][q]), acc[2 * q + 1]);
+                    }
+                }
+            }
+            if (c >= nblk) continue;
+            u32x4 o = hv ? pack8(acc) : u32x4{0u, 0u, 0u, 0u};
+            if (wv >= kChunkPayloadVecs) o = flagv;
+            st16_stream(prow + blk, o);
+        }
+    }
+}
+
+// Cross-group step for any K (used when K > 16): one wave per token. The
+// flags of each partial row are checked first (a bad row is left out); lane
+// `pos` then holds the row of the token's pos-th partial in ascending group,
+// and per wave-iteration the partials are read kAnyBatch per load batch and
+// summed in that order.
+__global__ __launch_bounds__(kBlockThreads) void combine_cross_any_kernel(Combine2Args a) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+    if (t >= a.T) return;
+    int g = -1, gs = -1;
+    if (lane < a.K) {
+        const int64_t e = a.topk[(int64_t)t * a.K + lane];
+        gs = a.group_slot[(int64_t)t * a.K + lane];
+        if (expert_ok(e, a.E)) g = ((int)e / a.epr) / a.P;
+    }
+    bool first = g >= 0 && gs >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int gj = readlane(g, j);
+        if (j < lane && gj == g) first = false;
+    }
+    if (first && gs >= a.group_cap) {
+        report(a.err, EP_DEVERR_CAPACITY);
+        first = false;
+    }
+    uint64_t fm = __ballot(first);
+    const int nvh = a.H / 8;
+    const int nblk = (2 * a.H + kChunkPayload - 1) / kChunkPayload;
+    const int iters = (nblk + 1) / 2;
+    uint64_t drop = 0;
+    for (uint64_t m = fm; m; m &= m - 1) {
+        const int k = __ffsll((unsigned long long)m) - 1;
+        if (!row_flags_ok(a.group_buf + (int64_t)readlane(gs, k) * a.pstride, nblk, a.epoch, lane))
+            drop |= 1ull << k;
+    }
+    if (drop && lane == 0) report(a.err, EP_DEVERR_FLAG);
+    fm &= ~drop;
+    int rank = 0;  // position of this lane's partial among the token's, by group
+    for (uint64_t m = fm; m; m &= m - 1) {
+        const int j = __ffsll((unsigned long long)m) - 1;
+        rank += readlane(g, j) < g ? 1 : 0;
+    }
+    const int ng = __popcll(fm);
+    int ordrow = 0;  // lane pos: the row of partial pos
+    for (int pos = 0; pos < ng; ++pos) {
+        const uint64_t who = __ballot(((fm >> lane) & 1) && rank == pos);
+        const int row = readlane(gs, __ffsll((unsigned long long)who) - 1);
+        if (lane == pos) ordrow = row;
+    }
+    uint8_t* out_row = reinterpret_cast<uint8_t*>(a.out) + (int64_t)t * a.H * 2;
+    for (int it = 0; it < iters; ++it) {
+        int c, wv, p;
+        const bool hv = chunk_vec(it, lane, nvh, c, wv, p);
+        const int64_t blk = (int64_t)c * kChunkBytes + (int64_t)wv * 16;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int pos0 = 0; pos0 < ng; pos0 += kAnyBatch) {
+            u32x4 v[kAnyBatch];
+#pragma unroll
+            for (int j = 0; j < kAnyBatch; ++j) {
+                v[j] = u32x4{0u, 0u, 0u, 0u};
+                if (pos0 + j < ng && hv)
+                    v[j] = ld16(a.group_buf + (int64_t)readlane(ordrow, pos0 + j) * a.pstride + blk);
+            }
+#pragma unroll
+            for (int j = 0; j < kAnyBatch; ++j) {
+                if (pos0 + j >= ng) break;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = acc[2 * q] + bf16_lo(v[j][q]);
+                    acc[2 * q + 1] = acc[2 * q + 1] + bf16_hi(v[j][q]);
+                }
+            }
+        }
+        if (hv) st16_stream(out_row + (int64_t)p * 16, pack8(acc));
+    }
+}
+
 }  // namespace
 
 hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const int64_t* topk,
@@ -656,8 +832,10 @@ hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const
             hipLaunchKernelGGL(combine_group_kernel<4>, grid, block, 0, st, a);
         else if (s.K <= 8)
             hipLaunchKernelGGL(combine_group_kernel<8>, grid, block, 0, st, a);
-        else
+        else if (s.K <= 16)
             hipLaunchKernelGGL(combine_group_kernel<16>, grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL(combine_group_any_kernel, grid, block, 0, st, a);
     }
     if ((steps & 2) && s.K <= 8 && EP_C2_ROWS && kWavesPerBlock % slices == 0) {
         const dim3 g2((unsigned)(((int64_t)s.T * slices + kWavesPerBlock - 1) / kWavesPerBlock));
@@ -665,8 +843,10 @@ hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const
     } else if (steps & 2) {
         if (s.K <= 8)
             hipLaunchKernelGGL(combine_cross_kernel<8>, grid, block, 0, st, a);
-        else
+        else if (s.K <= 16)
             hipLaunchKernelGGL(combine_cross_kernel<16>, grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL(combine_cross_any_kernel, grid, block, 0, st, a);
     }
     return hipGetLastError();
 }

@@ -638,6 +638,74 @@ __global__ __launch_bounds__(kBlockThreads) void layout_expand_kernel(LayoutArgs
     }
 }
 
+// Expand-mode rows for K > 16: the workgroup's entries, in token-then-lane
+// order (entry i = token i / K, lane i % K), are taken in passes of
+// kBlockThreads * 16; each pass is sorted stably by expert as above and an
+// LDS histogram carries, per expert, the entries of the earlier passes.
+constexpr int kWideItems = 16;
+constexpr int kWidePass = kBlockThreads * kWideItems;
+using WideSort = rocprim::block_radix_sort<int, kBlockThreads, kWideItems, int>;
+
+__global__ __launch_bounds__(kBlockThreads) void layout_expand_wide_kernel(LayoutArgs a, int key_bits) {
+    extern __shared__ __align__(16) uint32_t lds_x[];
+    typename WideSort::storage_type& sort_st = *reinterpret_cast<typename WideSort::storage_type*>(lds_x);
+    int* sorted = reinterpret_cast<int*>(lds_x);  // [kWidePass], after each sort
+    const size_t hist_off = std::max(sizeof(typename WideSort::storage_type), sizeof(int) * kWidePass);
+    int* hist = reinterpret_cast<int*>(reinterpret_cast<char*>(lds_x) + hist_off);  // [E]
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int t0 = b * kLayoutTokens;
+    const int nt = min(kLayoutTokens, a.T - t0);
+    const int n = nt * a.K;  // entries of this workgroup
+    for (int e = tid; e < a.E; e += kBlockThreads) hist[e] = 0;
+    for (int base = 0; base < n; base += kWidePass) {
+        int keys[kWideItems], vals[kWideItems];
+#pragma unroll
+        for (int j = 0; j < kWideItems; ++j) {
+            const int i = base + tid * kWideItems + j;
+            int key = a.E;  // no expert, or past the last entry
+            if (i < n) {
+                const int64_t e = a.topk[(int64_t)t0 * a.K + i];
+                if (expert_ok(e, a.E)) key = (int)e;
+            }
+            keys[j] = key;
+            vals[j] = i;
+        }
+        __syncthreads();  // the previous pass is done with `sorted` and `hist`
+        WideSort().sort(keys, vals, sort_st, 0, key_bits);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kWideItems; ++j) sorted[tid * kWideItems + j] = keys[j];
+        __syncthreads();
+        int run_end[kWideItems];  // entries of the key up to here, at the last of its run
+#pragma unroll
+        for (int j = 0; j < kWideItems; ++j) {
+            const int pos = tid * kWideItems + j;
+            const int key = keys[j];
+            run_end[j] = 0;
+            if (key >= a.E) continue;
+            int lo = 0, hi = pos;  // first position holding `key`
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (sorted[mid] < key) lo = mid + 1; else hi = mid;
+            }
+            const int i = vals[j];
+            a.out.expert_slot[(int64_t)t0 * a.K + i] =
+                a.out.expert_offsets[key] + a.part_expert[(int64_t)b * a.E + key] + hist[key] + (pos - lo);
+            if (pos + 1 == kWidePass || sorted[pos + 1] != key) run_end[j] = pos - lo + 1;
+        }
+        __syncthreads();  // every row of this pass has read hist
+#pragma unroll
+        for (int j = 0; j < kWideItems; ++j)
+            if (run_end[j]) hist[keys[j]] += run_end[j];
+    }
+    // Lanes with no expert.
+    for (int i = tid; i < n; i += kBlockThreads) {
+        const int64_t e = a.topk[(int64_t)t0 * a.K + i];
+        if (!expert_ok(e, a.E)) a.out.expert_slot[(int64_t)t0 * a.K + i] = -1;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout& L, char* ws,
@@ -681,10 +749,14 @@ hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout
             const size_t lds = std::max({sizeof(typename ExpandSort<8>::storage_type),
                                          sizeof(int) * kBlockThreads * 8, bit_lds});
             hipLaunchKernelGGL(layout_expand_kernel<8>, grid, block, lds, st, a, bits, use_bits);
-        } else {
+        } else if (s.K <= 16) {
             const size_t lds = std::max({sizeof(typename ExpandSort<16>::storage_type),
                                          sizeof(int) * kBlockThreads * 16, bit_lds});
             hipLaunchKernelGGL(layout_expand_kernel<16>, grid, block, lds, st, a, bits, use_bits);
+        } else {
+            const size_t lds = std::max(sizeof(typename WideSort::storage_type), sizeof(int) * kWidePass) +
+                               sizeof(int) * (size_t)s.E;
+            hipLaunchKernelGGL(layout_expand_wide_kernel, grid, block, lds, st, a, bits);
         }
     }
     return hipGetLastError();

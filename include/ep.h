@@ -94,8 +94,8 @@ typedef struct ep_layout {
     uint8_t *is_token_in_group;  /* [T*G] 1 if token t sends to group g, else 0 */
     int32_t *slot;               /* [T*K] receive row of (t, rank of lane k); -1 if lane skipped */
     int32_t *group_slot;         /* [T*K] group-region row of (t, group of lane k); -1 if skipped */
-    int32_t *expert_slot;        /* [T*K] expand-mode row of (t, k); -1 if skipped (K <= 16;
-                                    needs expert_offsets) */
+    int32_t *expert_slot;        /* [T*K] expand-mode row of (t, k); -1 if skipped (needs
+                                    expert_offsets) */
 } ep_layout;
 
 /* Send side: per-token payload and routing of the T local tokens ([V2] §3.5). */
@@ -155,8 +155,8 @@ int ep_get_layout(const ep_shape *shape, const int64_t *topk_idx, const ep_layou
  * writes expert_slot[t*K+k] = expert_offsets[e] + #{lanes (t', k') before
  * (t, k) in token-then-lane order with the same expert e}, -1 for skipped
  * lanes; the rows of expert e are [expert_offsets[e], expert_offsets[e+1]),
- * expert_offsets[E] rows in all. Requires K <= 16 (EP_ERR_UNSUPPORTED) and
- * layout->expert_offsets. */
+ * expert_offsets[E] rows in all. Requires layout->expert_offsets
+ * (EP_ERR_ARG without it). */
 
 /* Direct dispatch ([V2] §3.3 阶段2 and §3.5; [PIPE] RDMA sender / NVL
  * sender record fields). Each token is read once and its record (present
@@ -238,8 +238,8 @@ int64_t ep_partial_row_bytes(const ep_shape *shape);
  *  step 2 (steps & 2): out[t][h] = bf16_rne(acc), acc = +0.0f, then for the
  *    groups of t in ascending g: acc = acc + partial[t, g][h] (fp32 add); a
  *    partial row with a flag != epoch is skipped (EP_DEVERR_FLAG).
- * Needs layout->slot, layout->group_slot, tokens' topk_idx; K <= 16; epoch
- * >= 1. Usable lanes are as in ep_combine. With G = 1 the result equals
+ * Needs layout->slot, layout->group_slot, tokens' topk_idx; epoch >= 1.
+ * Usable lanes are as in ep_combine. With G = 1 the result equals
  * ep_combine bit for bit. */
 int ep_combine_two_level(const ep_shape *shape, const ep_layout *layout, const int64_t *topk_idx,
                          const void *y, int64_t y_rows, int64_t y_row_stride, int y_format,

@@ -54,7 +54,13 @@ def draw_case(seed):
     G = int(rng.choice([g for g in range(1, R + 1) if R % g == 0]))
     epr = int(rng.choice([1, 2, 3, 4, 8]))
     E = R * epr
-    K = int(rng.integers(1, min(16, E + 1) + 1)) if rng.random() < 0.3 else int(rng.integers(1, min(8, E) + 1))
+    r = rng.random()
+    if r < 0.15:
+        K = int(rng.integers(17, 65))
+    elif r < 0.4:
+        K = int(rng.integers(1, min(16, E + 1) + 1))
+    else:
+        K = int(rng.integers(1, min(8, E) + 1))
     T = int(rng.integers(1, 900))
     fp8 = bool(rng.random() < 0.5)
     H = int(rng.choice([128, 256, 384, 1024, 1536])) if fp8 else int(8 * rng.integers(1, 200))

@@ -517,7 +517,10 @@ def test_expand_layout_full_size(name):
 
 
 @pytest.mark.parametrize("T,K,E,R", [(0, 8, 64, 8), (1, 1, 4, 2), (300, 3, 12, 6), (777, 16, 64, 16),
-                                     (513, 8, 4096, 1024), (1000, 6, 16, 1)])
+                                     (513, 8, 4096, 1024), (1000, 6, 16, 1),
+                                     # K > 16: sorted passes of 4096 entries per workgroup
+                                     (1100, 17, 64, 16), (600, 64, 128, 16), (300, 40, 4096, 512),
+                                     (513, 64, 2048, 256), (70, 24, 24, 8)])
 def test_expand_layout_edges(T, K, E, R):
     w = synth.Workload("edge", T, 128, E, R, 1, K, "uniform")
     rng = np.random.default_rng(T + K + E)
@@ -550,19 +553,10 @@ def test_expand_layout_mixed_paths(T, K, E, R):
     assert ep.ep_check_errors(ws) == 0
 
 
-def test_expand_topk_above_16_rejected():
-    w = synth.Workload("edge", 64, 128, 64, 8, 1, 20, "uniform")
-    topk = np.zeros((64, 20), np.int64)
-    shape = ep.make_shape(64, 128, 20, 64, 8, 1)
-    L = ep.alloc_layout(shape, expand=True)
-    ws = ep.alloc_workspace(shape)
-    with pytest.raises(RuntimeError):
-        ep.ep_get_layout(shape, dev(topk), L, ws)
-
-
-@pytest.mark.parametrize("name,fp8", [("ep32", False), ("ep32", True), ("zipf", False)])
+@pytest.mark.parametrize("name,fp8", [("ep32", False), ("ep32", True), ("zipf", False), ("wide", False)])
 def test_expand_dispatch_and_combine(name, fp8):
-    w = synth.workload(name)
+    """"wide": top-32 of 256 experts, so expand rows take the sorted passes."""
+    w = synth.Workload("wide", 1000, 2048, 256, 32, 1, 32, "uniform") if name == "wide" else synth.workload(name)
     inp = synth.make_inputs(w, with_fp8=fp8)
     shape, L, ws, tk = run_expand(w, inp)
     n_rows = int(host(L["expert_offsets"])[-1])
@@ -612,11 +606,14 @@ def run_two_level(shape, L, tk, y, y_rows, y_stride, fmt, epoch, w_dev, steps=3,
     return group_buf, out, gcap
 
 
-@pytest.mark.parametrize("name", ["hier8x8", "small", "mid"])
+@pytest.mark.parametrize("name", ["hier8x8", "small", "mid", "wide"])
 def test_two_level_combine_chunked(name):
     """"mid": 20 hidden blocks per row, whose 3 slices do not fill a
-    workgroup, so both steps take the one-wave-per-token kernels."""
-    if name == "small":
+    workgroup, so both steps take the one-wave-per-token kernels. "wide":
+    top-24 over 16 groups, so both steps take the any-K kernels."""
+    if name == "wide":
+        w = synth.Workload("wide", 600, 2048, 256, 64, 16, 24, "uniform")
+    elif name == "small":
         w = synth.Workload("small", 900, 1024, 64, 16, 4, 6, "uniform")
     elif name == "mid":
         w = synth.Workload("mid", 500, 4608, 64, 16, 4, 8, "uniform")
@@ -647,7 +644,9 @@ def test_two_level_combine_chunked(name):
 
 
 @pytest.mark.parametrize("T,H,K,E,R,G", [(300, 512, 3, 24, 8, 4), (257, 264, 12, 64, 16, 2),
-                                         (64, 7168, 8, 256, 64, 8), (128, 256, 2, 16, 4, 1)])
+                                         (64, 7168, 8, 256, 64, 8), (128, 256, 2, 16, 4, 1),
+                                         (300, 1032, 24, 64, 16, 4), (150, 264, 40, 128, 64, 64),
+                                         (77, 4608, 64, 128, 32, 8), (50, 520, 17, 34, 17, 1)])
 def test_two_level_combine_plain(T, H, K, E, R, G):
     w = synth.Workload("edge", T, H, E, R, G, K, "uniform")
     rng = np.random.default_rng(T + H + K)
@@ -669,10 +668,12 @@ def test_two_level_combine_plain(T, H, K, E, R, G):
     assert ep.ep_check_errors(ws) == 0
 
 
-def test_two_level_combine_corrupted_input_rows():
+@pytest.mark.parametrize("K", [6, 24])
+def test_two_level_combine_corrupted_input_rows(K):
     """A chunked expert-output row with a bad flag in its first or last hidden
-    block is dropped by the group step, for every lane that reads it."""
-    w = synth.Workload("small", 700, 1024, 64, 16, 4, 6, "uniform")
+    block is dropped by the group step, for every lane that reads it (K = 24:
+    the any-K kernels, which check the flags before the sums)."""
+    w = synth.Workload("small", 700, 1024, 64, 16, 4, K, "uniform")
     inp = synth.make_inputs(w, seed=43)
     shape, L, ws, tk = run_layout(w, inp["topk_idx"])
     L["_ws"] = ws
@@ -698,8 +699,9 @@ def test_two_level_combine_corrupted_input_rows():
     np.testing.assert_array_equal(host(out), C["out"])
 
 
-def test_two_level_combine_corrupted_partial():
-    w = synth.Workload("small", 300, 512, 32, 8, 4, 4, "uniform")
+@pytest.mark.parametrize("K", [4, 20])
+def test_two_level_combine_corrupted_partial(K):
+    w = synth.Workload("small", 300, 512, 32, 8, 4, K, "uniform")
     inp = synth.make_inputs(w, seed=41)
     shape, L, ws, tk = run_layout(w, inp["topk_idx"])
     L["_ws"] = ws
