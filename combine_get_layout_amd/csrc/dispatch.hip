@@ -77,6 +77,15 @@ struct DispatchArgs {
     uint32_t* err;
 };
 
+// Vectors of one wave's column slice of a row of `nvec` vectors: a multiple of
+// 8 (128 bytes), so that no two waves write parts of one cache line of a
+// receive row whose bytes are a multiple of 128 (the last slice is shorter).
+// Slices that split lines cost 16-22% (H = 7232: 115.7 vs 100.1 us; H =
+// 4160 at 16,384 tokens: 288.9 vs 236.6 us).
+__host__ __device__ __forceinline__ int slice_vecs(int64_t nvec) {
+    return (int)((((nvec + EP_DSP_SPLIT - 1) / EP_DSP_SPLIT) + 7) & ~(int64_t)7);
+}
+
 // Copy one row of `row_bytes` (multiple of 16) bytes from src to the rows
 // dst + slot_k * row_bytes of every destination lane k in `dest`.
 template <int NV>
@@ -84,7 +93,7 @@ __device__ __forceinline__ void fan_out_row(const uint8_t* src, int64_t row_byte
                                             uint64_t dest, int slot, int part) {
     const int lane = lane_id();
     const int nvec_all = (int)(row_bytes / 16);
-    const int per = (nvec_all + EP_DSP_SPLIT - 1) / EP_DSP_SPLIT;
+    const int per = slice_vecs(nvec_all);
     const int v0 = min(nvec_all, part * per);
     const int nvec = min(nvec_all, v0 + per);
     for (int base = v0; base < nvec; base += kWave * NV) {
@@ -188,7 +197,7 @@ hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_token
     const dim3 grid((unsigned)((waves + kDspWaves - 1) / kDspWaves)), block(kDspThreads);
     // Vectors per lane held in registers: enough for the widest present slice.
     const int64_t widest = tk.x ? 2 * (int64_t)s.H : (int64_t)s.H;
-    const int64_t slice = (widest / 16 + EP_DSP_SPLIT - 1) / EP_DSP_SPLIT;
+    const int64_t slice = slice_vecs(widest / 16);
     const int64_t per_lane = (slice + kWave - 1) / kWave;
     if (per_lane <= 1)
         hipLaunchKernelGGL(dispatch_kernel<1>, grid, block, 0, st, a);

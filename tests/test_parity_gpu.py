@@ -192,7 +192,9 @@ def test_dispatch_full_size(name, fp8):
 
 @pytest.mark.parametrize("T,H,K,E,R", [(1, 8, 1, 4, 2), (3, 1032, 3, 12, 6), (1001, 4096, 20, 64, 16),
                                        (257, 16, 8, 64, 64), (500, 384, 4, 16, 1),
-                                       (300, 256, 64, 256, 64)])
+                                       (300, 256, 64, 256, 64),
+                                       # column slices rounded to 128 B: the last one is shorter
+                                       (200, 7232, 8, 64, 16), (130, 4104, 5, 40, 8)])
 def test_dispatch_edges(T, H, K, E, R):
     w = synth.Workload("edge", T, H, E, R, 1, K, "uniform")
     rng = np.random.default_rng(T * 7 + H)
