@@ -194,7 +194,9 @@ def test_dispatch_full_size(name, fp8):
                                        (257, 16, 8, 64, 64), (500, 384, 4, 16, 1),
                                        (300, 256, 64, 256, 64),
                                        # column slices rounded to 128 B: the last one is shorter
-                                       (200, 7232, 8, 64, 16), (130, 4104, 5, 40, 8)])
+                                       (200, 7232, 8, 64, 16), (130, 4104, 5, 40, 8),
+                                       # long rows: 8 and 16 vectors per lane, two passes per slice
+                                       (40, 16384, 8, 64, 16), (12, 65536, 4, 32, 8)])
 def test_dispatch_edges(T, H, K, E, R):
     w = synth.Workload("edge", T, H, E, R, 1, K, "uniform")
     rng = np.random.default_rng(T * 7 + H)
@@ -298,7 +300,8 @@ def test_combine_full_size(name):
 
 
 @pytest.mark.parametrize("T,H,K", [(1, 8, 1), (77, 1032, 3), (300, 264, 2), (129, 512, 5),
-                                   (64, 2048, 16), (33, 128, 24), (40, 512, 64)])
+                                   (64, 2048, 16), (33, 128, 24), (40, 512, 64),
+                                   (40, 16384, 8), (12, 65536, 4)])
 def test_combine_edges(T, H, K):
     rng = np.random.default_rng(T + H + K)
     rows = 3 * T + 1
@@ -419,7 +422,10 @@ def test_hierarchical_full(name, fp8):
     (129, 1032, 12, 48, 16, 4, "uniform"),  # K > 8, hidden row not a whole number of blocks
     (1, 8, 1, 4, 2, 2, "uniform"),          # one token, one lane
     (400, 256, 5, 20, 10, 5, "random"),     # skipped lanes and repeated experts
-    (300, 4608, 6, 24, 8, 4, "uniform")])   # 20 hidden blocks: slices that do not fill a workgroup
+    (300, 4608, 6, 24, 8, 4, "uniform"),    # 20 hidden blocks: slices that do not fill a workgroup
+    (40, 16384, 8, 64, 16, 4, "uniform"),   # records of several 32-block pieces
+    (12, 65536, 4, 32, 8, 2, "random"),     # 275-block records
+    (150, 1024, 64, 1024, 512, 256, "random")])  # largest K and G
 def test_hierarchical_edges(T, H, K, E, R, G, ids):
     w = synth.Workload("edge", T, H, E, R, G, K, "uniform")
     inp = synth.make_inputs(w)
@@ -648,7 +654,9 @@ def test_two_level_combine_chunked(name):
 @pytest.mark.parametrize("T,H,K,E,R,G", [(300, 512, 3, 24, 8, 4), (257, 264, 12, 64, 16, 2),
                                          (64, 7168, 8, 256, 64, 8), (128, 256, 2, 16, 4, 1),
                                          (300, 1032, 24, 64, 16, 4), (150, 264, 40, 128, 64, 64),
-                                         (77, 4608, 64, 128, 32, 8), (50, 520, 17, 34, 17, 1)])
+                                         (77, 4608, 64, 128, 32, 8), (50, 520, 17, 34, 17, 1),
+                                         (40, 16384, 8, 64, 16, 4), (30, 16384, 24, 64, 16, 4),
+                                         (100, 1024, 64, 1024, 512, 256)])
 def test_two_level_combine_plain(T, H, K, E, R, G):
     w = synth.Workload("edge", T, H, E, R, G, K, "uniform")
     rng = np.random.default_rng(T + H + K)
@@ -872,6 +880,22 @@ def test_source_edges(T, K, E, R, S):
                                 topk_w=inp["topk_w"])
     if T:
         np.testing.assert_array_equal(host(ctx["staging"]), Sd["staging"])
+    D = oracle.dispatch(inp["topk_idx"], E, R, O["rank_offsets"], x=inp["x"], topk_w=inp["topk_w"])
+    check_dispatch(recv, D, N)
+    assert ep.ep_check_errors(ctx["ws"]) == 0
+
+
+@pytest.mark.parametrize("T,H,K,E,R,S", [(64, 16384, 8, 64, 16, 4), (20, 65536, 4, 32, 8, 2)])
+def test_source_long_records(T, H, K, E, R, S):
+    """Records longer than the 32 blocks the copy epilogue holds at once."""
+    w = synth.Workload("edge", T, H, E, R, 1, K, "uniform")
+    inp = synth.make_inputs(w, seed=T + S)
+    ctx = run_sources(w, inp, S)
+    O = check_sources_layout(ctx, inp["topk_idx"], w, S)
+    recv, N = run_epilogue(ctx)
+    Sd = oracle.source_dispatch(inp["topk_idx"], E, R, S, ctx["cap"], ctx["epoch"], x=inp["x"],
+                                topk_w=inp["topk_w"])
+    np.testing.assert_array_equal(host(ctx["staging"]), Sd["staging"])
     D = oracle.dispatch(inp["topk_idx"], E, R, O["rank_offsets"], x=inp["x"], topk_w=inp["topk_w"])
     check_dispatch(recv, D, N)
     assert ep.ep_check_errors(ctx["ws"]) == 0
