@@ -68,17 +68,25 @@ def parse():
 
 def ceilings(reps: int = 20) -> dict:
     """Practical HBM rates of library kernels on 1 GiB buffers (GB/s): a
-    reduction (read only), a constant fill (write only) and a device copy
-    (read + write). Context for the roofline fractions, not a target."""
+    reduction (read only), a constant fill (write only), two ways of writing
+    an 8 MiB random tile 128 times (a broadcast copy and a concatenation: the
+    source stays cached, so HBM sees writes of varying data, the shape of a
+    read-once, write-many fan-out) and a device copy (read + write). Context
+    for the roofline fractions, not a target."""
     import torch
 
     n = 1 << 30
     a = torch.randn(n // 4, device="cuda")  # fp32, 1 GiB
     b = torch.empty_like(a)
+    bi = torch.empty(n // 4, dtype=torch.int32, device="cuda")
+    tile = torch.randn(1, n // 4 // 128, device="cuda")  # 8 MiB of random values
     out = torch.empty((), device="cuda")
     ops = {
         "read (torch.sum, fp32)": (lambda: torch.sum(a, dim=(0,), out=out), n),
         "write (fill_, constant)": (lambda: b.fill_(1.5), n),
+        "write (fill_, int32 constant)": (lambda: bi.fill_(7), n),
+        "broadcast copy (8 MiB random tile x 128)": (lambda: b.view(128, -1).copy_(tile), n),
+        "cat (8 MiB random tile x 128)": (lambda: torch.cat([tile.view(-1)] * 128, out=b), n),
         "copy (copy_, device to device)": (lambda: b.copy_(a), 2 * n),
     }
     res = {}
