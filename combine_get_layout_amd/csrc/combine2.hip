@@ -22,7 +22,9 @@
 // so a partial row is produced and consumed with whole-wave 1 KiB stores and
 // loads. The flags of every chunked row read are checked by the flag lanes of
 // the same loads that bring in its values; a row with a bad flag makes the
-// token run a second pass without it (error path only).
+// token run a second pass without it (error path only). Past 16 top-k lanes,
+// any-K kernels check each row's flags in a short pass before its values are
+// used and take the token's groups one at a time.
 #include "ep_device.h"
 #include "ep_internal.h"
 
