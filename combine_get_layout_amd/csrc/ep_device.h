@@ -70,6 +70,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
 }
 
+// Division by a divisor that is fixed for a launch, as one multiply-high
+// instead of the ~40-instruction integer division sequence. With m =
+// ceil(2^32 / d) = (2^32 + eps) / d, 0 <= eps < d, n * m / 2^32 = n / d +
+// n * eps / (d * 2^32), so floor(n * m / 2^32) = floor(n / d) whenever
+// n * eps < 2^32: for every n < 2^20 and d <= 4096 (ids, ranks and groups stay
+// below 4096 here). d = 1 (m would be 2^32) passes n through.
+struct FastDiv {
+    uint32_t m;  // ceil(2^32 / d), or 0 for d == 1
+    static FastDiv make(uint32_t d) {
+        FastDiv f;
+        f.m = d == 1 ? 0u : (uint32_t)(((1ull << 32) + d - 1) / d);
+        return f;
+    }
+    __device__ __forceinline__ int operator()(int n) const {
+        return m ? (int)__umulhi((uint32_t)n, m) : n;
+    }
+};
+
 // Expert id check shared by the kernels: -1 = no expert, anything else outside
 // [0, E) is an error and behaves as -1.
 __device__ __forceinline__ bool expert_ok(int64_t e, int E) { return e >= 0 && e < E; }

@@ -47,6 +47,7 @@ constexpr int kWords = kLayoutTokens / 32;  // bit-matrix words per rank per wor
 
 struct LayoutArgs {
     int T, K, E, R, G, epr, P, nb;
+    FastDiv div_epr, div_P;  // e / epr (rank of an expert), r / P (group of a rank)
     int rp, wrow;            // rank/lane/group table: lanes start at column rp, groups at 2 rp
     const int64_t* topk;
     uint32_t* err;
@@ -97,9 +98,9 @@ __device__ __forceinline__ bool mark_token(const LayoutArgs& a, const TokenIds<K
         bad |= expert_bad(e, a.E);
         if (!expert_ok(e, a.E)) continue;
         any = true;
-        const int r = (int)e / a.epr;
+        const int r = a.div_epr((int)e);
         atomicOr(&bits_r[r * kWords + w], bit);
-        if (group_atomics) atomicOr(&bits_g[(r / a.P) * kWords + w], bit);
+        if (group_atomics) atomicOr(&bits_g[a.div_P(r) * kWords + w], bit);
         if (cnt_e) atomicAdd(&cnt_e[(int)e], 1);
     }
     if (bits_g && a.G == 1) {
@@ -238,7 +239,7 @@ __device__ __forceinline__ void add_rows(const u32x4* x, int b0, int b, int nb, 
 
 template <int KMAX>
 __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs a) {
-    extern __shared__ uint32_t lds[];
+    extern __shared__ __align__(16) uint32_t lds[];
     uint32_t* bits_r = lds;                                                // [R][kWords]
     uint32_t* bits_g = bits_r + a.R * kWords;                              // [G][kWords]
     int32_t* base_r = reinterpret_cast<int32_t*>(bits_g + a.G * kWords);  // [R]
@@ -454,12 +455,18 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
             if (c >= n) break;
             base[c] = run + bef[q][i];
             if (want_pre) {
-                int p = 0;
-#pragma unroll
-                for (int w = 0; w < kWords; ++w) {
-                    pre[c * kWords + w] = (uint8_t)p;
-                    p += __popc(bits[c * kWords + w]);
-                }
+                // The column's 8 words in two 16-byte LDS reads (rows of the
+                // bit matrix are 32-byte aligned), then its 8 u8 prefixes in
+                // two 4-byte writes: no read waits behind a write.
+                static_assert(kWords == 8, "pre table packing assumes 8 words per column");
+                const u32x4 w0 = *reinterpret_cast<const u32x4*>(bits + c * kWords);
+                const u32x4 w1 = *reinterpret_cast<const u32x4*>(bits + c * kWords + 4);
+                const uint32_t n0 = __popc(w0[0]), n1 = n0 + __popc(w0[1]), n2 = n1 + __popc(w0[2]),
+                               n3 = n2 + __popc(w0[3]), n4 = n3 + __popc(w1[0]), n5 = n4 + __popc(w1[1]),
+                               n6 = n5 + __popc(w1[2]);
+                uint32_t* pw = reinterpret_cast<uint32_t*>(pre + c * kWords);
+                pw[0] = (n0 << 8) | (n1 << 16) | (n2 << 24);
+                pw[1] = n3 | (n4 << 8) | (n5 << 16) | (n6 << 24);
             }
             if (pub) {
                 if (off) off[c] = run;
@@ -496,10 +503,10 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
     auto slot_of = [&](int64_t e, int32_t& s, int32_t& gs) {
         s = gs = -1;
         if (!expert_ok(e, a.E)) return;
-        const int r = (int)e / a.epr;
+        const int r = a.div_epr((int)e);
         s = base_r[r] + pre_r[r * kWords + w] + __popc(bits_r[r * kWords + w] & below);
         if (groups) {
-            const int g = r / a.P;
+            const int g = a.div_P(r);
             gs = base_g[g] + pre_g[g * kWords + w] + __popc(bits_g[g * kWords + w] & below);
         }
     };
@@ -714,6 +721,8 @@ hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout
     LayoutArgs a;
     a.T = s.T; a.K = s.K; a.E = s.E; a.R = s.R; a.G = s.G;
     a.epr = s.E / s.R; a.P = s.R / s.G; a.nb = W.nb;
+    a.div_epr = FastDiv::make(a.epr);
+    a.div_P = FastDiv::make(a.P);
     a.rp = W.rp; a.wrow = W.wrow;
     a.topk = topk;
     a.err = reinterpret_cast<uint32_t*>(ws + W.err);

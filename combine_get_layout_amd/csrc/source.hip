@@ -39,6 +39,7 @@ constexpr int kEpiloguePieceIters = 16;  // wave iterations (2 blocks each) held
 
 struct SourceArgs {
     int T, K, E, R, S, Ts, nbs, epr;
+    FastDiv div_epr;  // e / epr: rank of an expert
     int64_t cap;
     const int64_t* topk;
     int32_t* part;      // [S][nbs][R] per-tile counts -> per-source exclusive prefix
@@ -70,7 +71,7 @@ __device__ bool tile_bits(const SourceArgs& a, int t0, int nt, uint32_t* bits) {
         for (int k = 0; k < a.K; ++k) {
             const int64_t e = row[k];
             bad |= expert_bad(e, a.E);
-            if (expert_ok(e, a.E)) atomicOr(&bits[((int)e / a.epr) * kTileWords + (i >> 5)], bit);
+            if (expert_ok(e, a.E)) atomicOr(&bits[a.div_epr((int)e) * kTileWords + (i >> 5)], bit);
         }
     }
     __syncthreads();
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kBlockThreads) void source_assign_kernel(SourceArgs
         const int64_t e = a.topk[t * a.K + k];
         int32_t v = -1;
         if (expert_ok(e, a.E)) {
-            const int r = (int)e / a.epr;
+            const int r = a.div_epr((int)e);
             int64_t j = base[r] + __popc(bits[r * kTileWords + w] & below);
             for (int q = 0; q < w; ++q) j += __popc(bits[r * kTileWords + q]);
             if (j < a.cap) v = (int32_t)(((int64_t)r * a.S + s) * a.cap + j);
@@ -301,6 +302,7 @@ hipError_t launch_source_layout(const ep_shape& s, const int64_t* topk, const ep
     SourceArgs a;
     a.T = s.T; a.K = s.K; a.E = s.E; a.R = s.R; a.S = src.S;
     a.Ts = W.Ts; a.nbs = W.nbs; a.epr = s.E / s.R;
+    a.div_epr = FastDiv::make(a.epr);
     a.cap = src.capacity;
     a.topk = topk;
     a.part = reinterpret_cast<int32_t*>(ws + W.part);
