@@ -602,6 +602,53 @@ def test_expand_dispatch_and_combine(name, fp8):
 # Two-level combine (partials per token and group, then the cross-group sum)
 # --------------------------------------------------------------------------
 
+# Shapes beyond the five workloads, at full size: an expert count that is not
+# a power of two (384 over 48 ranks), a 4096-wide hidden row, a hidden size
+# that is not a multiple of 128 (2880: bf16 only; its 90 hidden vectors are
+# not a multiple of the 64 lanes of a wave) and six experts per token over 160
+# experts in 4 groups.
+OTHER_SHAPES = [
+    ("E384", synth.Workload("E384", 4096, 7168, 384, 48, 1, 8, "uniform"), True),
+    ("H4096", synth.Workload("H4096", 4096, 4096, 128, 16, 1, 8, "uniform"), True),
+    ("H2880", synth.Workload("H2880", 3000, 2880, 128, 32, 4, 4, "uniform"), False),
+    ("E160", synth.Workload("E160", 2048, 5120, 160, 20, 4, 6, "uniform"), True),
+]
+
+
+@pytest.mark.parametrize("name,w,fp8", OTHER_SHAPES, ids=[o[0] for o in OTHER_SHAPES])
+def test_other_shapes_end_to_end(name, w, fp8):
+    inp = synth.make_inputs(w, with_fp8=fp8)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    L["_ws"] = ws
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    check_layout(L, O, w.T)
+    recv, N, _ = run_dispatch(w, inp, shape, L, ws, tk, fp8=fp8)
+    D = oracle.dispatch(inp["topk_idx"], w.E, w.R, O["rank_offsets"], x=inp["x"],
+                        x_fp8=inp.get("x_fp8"), x_scales=inp.get("x_scales"), topk_w=inp["topk_w"])
+    check_dispatch(recv, D, N)
+    wd = dev(inp["topk_w"])
+    out = poison(torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda"))
+    ep.ep_combine(shape, L, recv["x"], N, 2 * w.H, ep.EP_FMT_PLAIN, 0, wd, out, ws)
+    combine_close(host(out), inp["x"])  # identity expert: back to x
+    y = synth.random_bf16_rows(N, w.H, seed=5)
+    ep.ep_combine(shape, L, dev(y), N, 2 * w.H, ep.EP_FMT_PLAIN, 0, wd, out, ws)
+    np.testing.assert_array_equal(host(out), oracle.combine(O["slot"], inp["topk_w"], y, w.H)["out"])
+    if w.G > 1:
+        epoch = 21
+        gb, pb, G_rows, _, stride = run_hier(w, inp, shape, L, ws, tk, epoch, fp8=fp8)
+        Hd = oracle.hier_dispatch(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_offsets"], epoch,
+                                  x=inp["x"], x_fp8=inp.get("x_fp8"), x_scales=inp.get("x_scales"),
+                                  topk_w=inp["topk_w"])
+        np.testing.assert_array_equal(host(gb)[:G_rows], Hd["group_buf"])
+        np.testing.assert_array_equal(host(pb)[:N], Hd["peer_buf"])
+        gbuf, out2, gcap = run_two_level(shape, L, tk, pb, N, stride, ep.EP_FMT_CHUNKED, epoch, wd)
+        C2 = oracle.combine_two_level(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_slot"],
+                                      inp["topk_w"], Hd["peer_buf"], w.H, gcap, epoch, chunked=True)
+        np.testing.assert_array_equal(host(gbuf)[:gcap], C2["group_buf"])
+        np.testing.assert_array_equal(host(out2), C2["out"])
+    assert ep.ep_check_errors(ws) == 0
+
+
 def run_two_level(shape, L, tk, y, y_rows, y_stride, fmt, epoch, w_dev, steps=3, group_buf=None):
     gcap = int(host(L["group_offsets"])[-1])
     pstride = ep.ep_partial_row_bytes(shape)
