@@ -604,7 +604,7 @@ def test_expand_dispatch_and_combine(name, fp8):
 
 # Shapes beyond the five workloads, at full size: an expert count that is not
 # a power of two (384 over 48 ranks), a 4096-wide hidden row, a hidden size
-# that is not a multiple of 128 (2880: bf16 only; its 90 hidden vectors are
+# that is not a multiple of 128 (2880: bf16 only; its 360 16-byte vectors are
 # not a multiple of the 64 lanes of a wave) and six experts per token over 160
 # experts in 4 groups.
 OTHER_SHAPES = [
