@@ -10,14 +10,20 @@
 // DeepEP 三阶段流水线 vs DeepGEMM 对称内存" (combine write into
 // combine_token_buffer[topk slot][token]).
 //
-// CDNA4 mapping: one wave64 per output token. A lane owns 16-byte vectors (8
-// bf16) of the hidden row. For a group of NB vectors the K source rows are all
-// requested before any arithmetic (K x NB loads in flight per lane, issued
-// without branches or waits in between), and the fp32 accumulation runs in
-// ascending k with v_fma_f32. Chunked rows (512 B blocks, 480 B payload) are
-// read in place: wave iteration i covers blocks 2i and 2i+1, lane L holds
-// payload vector 30 * (2i + L/32) + L%32 when L%32 < 30; every block that
-// carries hidden bytes must have its 32-byte flag equal to epoch.
+// CDNA4 mapping. A lane owns 16-byte vectors (8 bf16) of the hidden row and
+// the fp32 accumulation runs in ascending k with v_fma_f32. Two kernels:
+//   * row-streaming (K <= 8, the common case): a token is cut into slices of
+//     4 or 8 wave-iterations, one wave per slice; the wave reads its slice of
+//     one row at a time as a burst, the next row's burst requested before the
+//     current one is summed;
+//   * one wave per token (K > 8, or chunked rows whose slices would not fill
+//     a workgroup): for a group of NB vectors all K source rows are requested
+//     before any arithmetic (K x NB loads in flight per lane, issued without
+//     branches or waits in between).
+// Chunked rows (512 B blocks, 480 B payload) are read in place: wave
+// iteration i covers blocks 2i and 2i+1, lane L holds payload vector
+// 30 * (2i + L/32) + L%32 when L%32 < 30; every block that carries hidden
+// bytes must have its 32-byte flag equal to epoch.
 #include "ep_device.h"
 #include "ep_internal.h"
 

@@ -9,12 +9,14 @@
 // (hidden, scales, source index, top-k ids and weights; NVL receivers write
 // recv_x[row] and recv_x_scales[row * H/128]).
 //
-// Mapping on CDNA4: one wave64 per source token, four tokens per workgroup.
-// The wave loads up to 16 16-byte vectors per lane of the row (16 KiB in
-// flight per wave) into VGPRs, then streams them to each destination row with
-// non-temporal 16-byte stores: one HBM read, D writes, no LDS round trip.
-// Destinations are the lanes k whose slot differs from every earlier lane's
-// (the rank deduplication), found with one ballot.
+// Mapping on CDNA4: each source token's row is cut into EP_DSP_SPLIT column
+// slices of whole 128-byte lines, one wave64 per slice, four waves per
+// workgroup. A wave loads its slice into VGPRs (up to 16 16-byte vectors per
+// lane per pass), then streams it to each destination row with non-temporal
+// 16-byte stores: one HBM read, D writes, no LDS round trip. Destinations
+// are the lanes k whose slot differs from every earlier lane's (the rank
+// deduplication), found with one ballot. The first slice's wave also writes
+// the scales and the metadata.
 #include "ep_device.h"
 #include "ep_internal.h"
 
