@@ -3,11 +3,14 @@ oracle: layout (all outputs, groups and expand rows), dispatch with a random
 subset of payload pieces, combine, the two-level chunked dispatch with the
 flat and the two-level combine, and expand-mode dispatch and combine.
 
-The shapes are drawn from a fixed seed list, so a failure names a case that
+The shapes are drawn from a fixed seed list (200 seeds; EP_FUZZ_SEEDS sets
+another count), so a failure names a case that
 reproduces exactly. Sizes stay small (the oracle runs each in milliseconds)
 but ragged: T, H, K, E, R and G take values that are not powers of two, and
 the routing mixes distinct top-k with skipped lanes and repeated experts.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,7 +21,7 @@ from combine_get_layout_amd import ep
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = list(range(1, 201))
+SEEDS = list(range(1, 1 + int(os.environ.get("EP_FUZZ_SEEDS", "200"))))
 
 
 @pytest.fixture(scope="module", autouse=True)
