@@ -194,3 +194,24 @@ def test_binding_size_and_stride_checks():
     with pytest.raises(ValueError, match="recv x"):
         ep._recv_struct(shape, dict(x=_FakeCuda(10 * 256 * 2 - 2)), 10)
     ep._recv_struct(shape, dict(x=_FakeCuda(10 * 256 * 2)), 10)
+
+
+def test_plain_c_caller(lib, tmp_path):
+    """include/ep.h is a C header: a C99 program built with gcc links libep.so
+    and its host-only calls behave as documented (tests/c/abi_from_c.c)."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    libdir = os.path.dirname(ep.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    src = os.path.join(ROOT, "tests", "c", "abi_from_c.c")
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", f"-I{os.path.join(ROOT, 'include')}",
+                        src, f"-L{libdir}", "-l:libep.so", f"-Wl,-rpath,{libdir}", "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 failure(s)" in r.stdout
