@@ -1,9 +1,12 @@
-/* The whole flat path driven from plain C99 through libep.so, with device
- * buffers from the HIP runtime's C API and one caller-created stream:
- * ep_get_layout -> ep_dispatch -> ep_combine (identity expert: the combine
- * reads the dispatched rows back). The results are compared bit for bit with
- * the CPU oracle (liboracle.so, test infrastructure), called from the same
- * program. Inputs come from a fixed xorshift generator: ids in [-1, E) with
+/* The path driven from plain C99 through libep.so, with device buffers from
+ * the HIP runtime's C API and one caller-created stream:
+ *   flat: ep_get_layout -> ep_dispatch -> ep_combine (identity expert: the
+ *         combine reads the dispatched rows back);
+ *   two-level (2 groups of 4 ranks): ep_get_layout with groups ->
+ *         ep_hierarchical_dispatch (both steps) -> ep_combine on the chunked
+ *         rows and ep_combine_two_level.
+ * The results are compared bit for bit with the CPU oracle (liboracle.so,
+ * test infrastructure), called from the same program. Inputs come from a fixed xorshift generator: ids in [-1, E) with
  * repeats, bf16 rows in [-2, 2), weights in [0, 1).
  * Prints one line per step and exits non-zero on the first mismatch. */
 #include <hip/hip_runtime_api.h>
@@ -27,12 +30,24 @@ void oracle_dispatch(int T, int H, int K, int E, int R, const int64_t *topk_idx,
 void oracle_combine(int T, int H, int K, const int32_t *slot, const float *topk_w, const uint8_t *y,
                     int64_t y_rows, int64_t row_stride, int chunked, uint32_t epoch, uint16_t *out,
                     uint32_t *err);
+int oracle_hier_dispatch(int T, int H, int K, int E, int R, int G, const int64_t *topk_idx,
+                         const float *topk_w, const uint16_t *x, const uint8_t *x_fp8,
+                         const float *x_scales, const int32_t *slot, const int32_t *group_offsets,
+                         uint32_t epoch, uint8_t *group_buf, int64_t group_cap, uint8_t *peer_buf,
+                         int64_t peer_cap, int steps, uint32_t *err);
+void oracle_combine_two_level(int T, int H, int K, int E, int R, int G, const int64_t *topk_idx,
+                              const int32_t *slot, const int32_t *group_slot, const float *topk_w,
+                              const uint8_t *y, int64_t y_rows, int64_t row_stride, int chunked,
+                              uint32_t epoch, uint8_t *group_buf, int64_t group_cap, int steps,
+                              uint16_t *out, uint32_t *err);
 
 #define T 1000
 #define H 512
 #define K 4
 #define E 32
 #define R 8
+#define G2 2
+#define EPOCH 7u
 
 static uint64_t rng_state = 0x9E3779B97F4A7C15ull;
 static uint32_t next_u32(void) {
@@ -194,6 +209,90 @@ int main(void) {
         printf("FAIL error bits %u != %u\n", bits, want_bits);
         ok = 0;
     }
+    /* two-level path on the same tokens, R ranks in G2 groups */
+    {
+        static int32_t p_tpe[E], p_tpr[R], p_tpg[G2], p_eo[E + 1], p_ro[R + 1], p_go[G2 + 1], p_slot[T * K],
+            p_gslot[T * K];
+        static uint8_t p_in_rank[T * R], p_in_group[T * G2];
+        uint32_t p_err = 0;
+        if (oracle_layout(T, K, E, R, G2, ids, p_tpe, p_tpr, p_tpg, p_eo, p_ro, p_go, p_in_rank, p_in_group,
+                          p_slot, p_gslot, &p_err) != 0) {
+            printf("FAIL oracle_layout with groups\n");
+            return 1;
+        }
+        ep_shape s2 = {T, H, K, E, R, G2};
+        const int64_t stride = ep_chunked_record_bytes(&s2, EP_SEG_BF16);
+        const int64_t pstride = ep_partial_row_bytes(&s2);
+        const int GR = p_go[G2], N2 = p_ro[R];
+        uint8_t *o_gbuf = calloc((size_t)GR, (size_t)stride), *o_pbuf = calloc((size_t)N2, (size_t)stride);
+        uint8_t *o_part = calloc((size_t)GR, (size_t)pstride);
+        static uint16_t o_out2[T * H], o_out3[T * H], g_out2[T * H], g_out3[T * H];
+        oracle_hier_dispatch(T, H, K, E, R, G2, ids, w, x, NULL, NULL, p_slot, p_go, EPOCH, o_gbuf, GR, o_pbuf,
+                             N2, 3, &p_err);
+        oracle_combine(T, H, K, p_slot, w, o_pbuf, N2, stride, 1, EPOCH, o_out2, &p_err);
+        oracle_combine_two_level(T, H, K, E, R, G2, ids, p_slot, p_gslot, w, o_pbuf, N2, stride, 1, EPOCH,
+                                 o_part, GR, 3, o_out3, &p_err);
+        printf("oracle two-level done: %d group rows, %d peer rows\n", GR, N2);
+
+        size_t ws2_bytes = ep_workspace_bytes(&s2);
+        void *ws2;
+        int32_t *d2_tpg, *d2_go, *d2_slot, *d2_gslot, *d2_ro;
+        uint8_t *d2_gbuf, *d2_pbuf, *d2_part;
+        uint16_t *d2_out;
+        HIP_OK(hipMalloc(&ws2, ws2_bytes));
+        HIP_OK(hipMalloc((void **)&d2_tpg, sizeof p_tpg));
+        HIP_OK(hipMalloc((void **)&d2_go, sizeof p_go));
+        HIP_OK(hipMalloc((void **)&d2_ro, sizeof p_ro));
+        HIP_OK(hipMalloc((void **)&d2_slot, sizeof p_slot));
+        HIP_OK(hipMalloc((void **)&d2_gslot, sizeof p_gslot));
+        HIP_OK(hipMalloc((void **)&d2_gbuf, (size_t)GR * stride));
+        HIP_OK(hipMalloc((void **)&d2_pbuf, (size_t)N2 * stride));
+        HIP_OK(hipMalloc((void **)&d2_part, (size_t)GR * pstride));
+        HIP_OK(hipMalloc((void **)&d2_out, sizeof g_out2));
+        HIP_OK(hipMemset(d2_gbuf, 0, (size_t)GR * stride));
+        HIP_OK(hipMemset(d2_pbuf, 0, (size_t)N2 * stride));
+        HIP_OK(hipMemset(d2_part, 0, (size_t)GR * pstride));
+        ep_layout L2;
+        memset(&L2, 0, sizeof L2);
+        L2.tokens_per_group = d2_tpg;
+        L2.group_offsets = d2_go;
+        L2.rank_offsets = d2_ro;
+        L2.slot = d2_slot;
+        L2.group_slot = d2_gslot;
+        EP_OK_(ep_get_layout(&s2, d_ids, &L2, ws2, ws2_bytes, st));
+        EP_OK_(ep_hierarchical_dispatch(&s2, &L2, &tk, EPOCH, EP_HIER_SCALEOUT | EP_HIER_FORWARD, d2_gbuf, GR,
+                                        d2_pbuf, N2, ws2, ws2_bytes, st));
+        EP_OK_(ep_combine(&s2, &L2, d2_pbuf, N2, stride, EP_FMT_CHUNKED, EPOCH, d_w, d2_out, ws2, ws2_bytes, st));
+        HIP_OK(hipMemcpyAsync(g_out2, d2_out, sizeof g_out2, hipMemcpyDeviceToHost, st));
+        EP_OK_(ep_combine_two_level(&s2, &L2, d_ids, d2_pbuf, N2, stride, EP_FMT_CHUNKED, EPOCH, d_w, d2_part,
+                                    GR, 3, d2_out, ws2, ws2_bytes, st));
+        HIP_OK(hipMemcpyAsync(g_out3, d2_out, sizeof g_out3, hipMemcpyDeviceToHost, st));
+        uint32_t bits2 = 0;
+        EP_OK_(ep_check_errors(ws2, st, &bits2));
+        printf("two-level path done: device error bits %u\n", bits2);
+        static int32_t g2_tpg[G2], g2_go[G2 + 1], g2_gslot[T * K];
+        uint8_t *g_gbuf = malloc((size_t)GR * stride), *g_pbuf = malloc((size_t)N2 * stride);
+        uint8_t *g_part = malloc((size_t)GR * pstride);
+        HIP_OK(hipMemcpy(g2_tpg, d2_tpg, sizeof g2_tpg, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g2_go, d2_go, sizeof g2_go, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g2_gslot, d2_gslot, sizeof g2_gslot, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_gbuf, d2_gbuf, (size_t)GR * stride, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_pbuf, d2_pbuf, (size_t)N2 * stride, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_part, d2_part, (size_t)GR * pstride, hipMemcpyDeviceToHost));
+        ok &= same("tokens_per_group", g2_tpg, p_tpg, sizeof p_tpg);
+        ok &= same("group_offsets", g2_go, p_go, sizeof p_go);
+        ok &= same("group_slot", g2_gslot, p_gslot, sizeof p_gslot);
+        ok &= same("group rows (scale-out step)", g_gbuf, o_gbuf, (size_t)GR * stride);
+        ok &= same("peer rows (forward step)", g_pbuf, o_pbuf, (size_t)N2 * stride);
+        ok &= same("combine out, chunked rows", g_out2, o_out2, sizeof o_out2);
+        ok &= same("two-level partial rows", g_part, o_part, (size_t)GR * pstride);
+        ok &= same("two-level combine out", g_out3, o_out3, sizeof o_out3);
+        if (bits2 != p_err) {
+            printf("FAIL two-level error bits %u != %u\n", bits2, p_err);
+            ok = 0;
+        }
+    }
+
     HIP_OK(hipStreamDestroy(st));
     printf("%s\n", ok ? "path ok" : "path FAILED");
     return ok ? 0 : 1;

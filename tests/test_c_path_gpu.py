@@ -1,7 +1,9 @@
-"""The flat path driven from a plain C99 program (tests/c/path_from_c.c):
-device buffers from the HIP runtime's C API, one caller-created stream,
-ep_get_layout -> ep_dispatch -> ep_combine through libep.so, every output
-compared bit for bit with the CPU oracle inside the same program."""
+"""The path driven from a plain C99 program (tests/c/path_from_c.c): device
+buffers from the HIP runtime's C API, one caller-created stream; the flat path
+(ep_get_layout -> ep_dispatch -> ep_combine) and the two-level one
+(ep_hierarchical_dispatch -> ep_combine on chunked rows, ep_combine_two_level)
+through libep.so, every output compared bit for bit with the CPU oracle inside
+the same program."""
 import os
 import shutil
 import subprocess
