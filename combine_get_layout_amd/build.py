@@ -28,7 +28,10 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}",
+    # -Wno-pass-failed: a `#pragma unroll` over top-k lanes cannot be honoured
+    # in the instantiation whose lane count is only known at run time; the
+    # remark is about that instantiation and changes nothing in the code.
+    "-Wall", "-Wno-unused-result", "-Wno-pass-failed", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
 
