@@ -33,6 +33,7 @@
 // Workgroups never wait for each other and no grid-wide fence is needed (the
 // launch boundaries order the kernels).
 #include <algorithm>
+#include <type_traits>
 
 #include <rocprim/block/block_radix_sort.hpp>
 #include <rocprim/warp/warp_scan.hpp>
@@ -193,7 +194,8 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 //   * column q*256 + thread of this workgroup's slice of experts.
 constexpr int kVecRounds = (2 * EP_MAX_RANKS + EP_MAX_GROUPS + 4 * kBlockThreads - 1) / (4 * kBlockThreads);
 constexpr int kSliceRounds = EP_MAX_EXPERTS / kBlockThreads;
-constexpr int kRowBatch = 8;  // table rows (workgroups) loaded per batch (measured best of 8, 16, 32)
+constexpr int kRowBatch = 8;
+constexpr int kSpreadStride = 17;  // ints per (thread group, column) partial: 2 x (4 + 4) + 1  // table rows (workgroups) loaded per batch (measured best of 8, 16, 32)
 // Scan slots of the LDS scratch, one int per wave each.
 constexpr int kScRank = 0;                          // rank totals, per vector round
 constexpr int kScLane = kScRank + kVecRounds;       // lane totals, per vector round
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
     int32_t* scratch = base_g + a.G;                                       // [kScSlots][waves]
     uint8_t* pre_r = reinterpret_cast<uint8_t*>(scratch + kScSlots * kWavesPerBlock);  // [R][kWords]
     uint8_t* pre_g = pre_r + a.R * kWords;                                 // [G][kWords]
-    int32_t* red = reinterpret_cast<int32_t*>(pre_g + a.G * kWords);       // [kBlockThreads][9]
+    int32_t* red = reinterpret_cast<int32_t*>(pre_g + a.G * kWords);       // [kBlockThreads][kSpreadStride]
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const bool groups = a.out.group_slot != nullptr;
@@ -296,52 +298,68 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
             ea += b0 + j < a.nb ? x[j] : 0;
         }
     };
-    // Many rows of a narrow table, no expand rows: the threads form J groups
-    // of `cols` threads, group j reading rows j, j + J, j + 2J, ..., so each
-    // thread follows about nb / J rows instead of nb. The groups' partial
-    // sums (4 columns before b, 4 columns over all rows, one expert column)
-    // meet in LDS at the barrier after the loads. Measured: 22.2 -> 18.9 us
-    // per layout call at 64 workgroups and 136 table columns; with 2 batches
-    // of rows or fewer the extra LDS pass costs more than it saves.
-    const int cols = max(max(nvec, ne), 1);
+    // Many rows of a table of at most 256 vectors, no expand rows: a thread
+    // takes vpt (1 or 2) neighbouring vectors and one expert column, and the
+    // threads form J = 256 / cols groups, group j reading rows j, j + J,
+    // j + 2J, ..., so each thread follows about nb / J rows instead of nb.
+    // The groups' partial sums (per vector: 4 columns before b and 4 over all
+    // rows; the expert column's total) meet in LDS at the barrier after the
+    // loads. Measured: 22.2 -> 18.8 us per layout call at 64 workgroups and
+    // 34 vectors per row; with 2 batches of rows or fewer the extra LDS pass
+    // costs more than it saves.
+    const int vpt = nvec > 128 ? 2 : 1;
+    const int cols = max(max((nvec + vpt - 1) / vpt, ne), 1);
     const int J = kBlockThreads / cols;
     const bool spread = !expand && vec_rounds == 1 && slice_rounds <= 1 && J >= 2 &&
                         a.nb > 2 * kRowBatch;
-    if (spread) {
+    auto spread_loads = [&](auto vpt_c) {
+        constexpr int VPT = decltype(vpt_c)::value;
         const int c = tid % cols, j = tid / cols;
-        if (j < J) {
-            const int32_t* pv = a.part_rlg + 4 * min(c, nvec - 1);
-            const int32_t* pcol = a.part_expert + min(e0 + c, a.E - 1);
-            int pb[4] = {0, 0, 0, 0}, pa[4] = {0, 0, 0, 0}, pe_sum = 0;
-            for (int rb = j; rb < a.nb; rb += J * kRowBatch) {
-                u32x4 x[kRowBatch];
-                int32_t xe[kRowBatch];
+        if (j >= J) return;
+        const int32_t* pv[VPT];
 #pragma unroll
-                for (int i = 0; i < kRowBatch; ++i) {
-                    const int64_t rr = min(rb + i * J, a.nb - 1);
-                    x[i] = ld16(pv + rr * a.wrow);
-                    xe[i] = pcol[rr * a.E];
-                }
+        for (int u = 0; u < VPT; ++u) pv[u] = a.part_rlg + 4 * min(c * VPT + u, nvec - 1);
+        const int32_t* pcol = a.part_expert + min(e0 + c, a.E - 1);
+        int pb[VPT][4] = {}, pa[VPT][4] = {}, pe_sum = 0;
+        for (int rb = j; rb < a.nb; rb += J * kRowBatch) {
+            u32x4 x[VPT][kRowBatch];
+            int32_t xe[kRowBatch];
 #pragma unroll
-                for (int i = 0; i < kRowBatch; ++i) {
-                    const int rr = rb + i * J;
-                    const bool in = rr < a.nb, before = rr < b;
+            for (int i = 0; i < kRowBatch; ++i) {
+                const int64_t rr = min(rb + i * J, a.nb - 1);
+#pragma unroll
+                for (int u = 0; u < VPT; ++u) x[u][i] = ld16(pv[u] + rr * a.wrow);
+                xe[i] = pcol[rr * a.E];
+            }
+#pragma unroll
+            for (int i = 0; i < kRowBatch; ++i) {
+                const int rr = rb + i * J;
+                const bool in = rr < a.nb, before = rr < b;
+#pragma unroll
+                for (int u = 0; u < VPT; ++u)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        pa[q] += in ? (int)x[i][q] : 0;
-                        pb[q] += before ? (int)x[i][q] : 0;
+                        pa[u][q] += in ? (int)x[u][i][q] : 0;
+                        pb[u][q] += before ? (int)x[u][i][q] : 0;
                     }
-                    pe_sum += in ? xe[i] : 0;
-                }
+                pe_sum += in ? xe[i] : 0;
             }
-            int32_t* o = red + (j * cols + c) * 9;
+        }
+        int32_t* o = red + (j * cols + c) * kSpreadStride;
+#pragma unroll
+        for (int u = 0; u < VPT; ++u)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                o[q] = pb[q];
-                o[4 + q] = pa[q];
+                o[8 * u + q] = pb[u][q];
+                o[8 * u + 4 + q] = pa[u][q];
             }
-            o[8] = pe_sum;
-        }
+        o[16] = pe_sum;
+    };
+    if (spread) {
+        if (vpt == 2)
+            spread_loads(std::integral_constant<int, 2>{});
+        else
+            spread_loads(std::integral_constant<int, 1>{});
     } else {
         const int v = min(tid, nvec - 1);
         const int32_t* pv = a.part_rlg + 4 * v;
@@ -399,18 +417,18 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
         }
     }
     __syncthreads();
-    if (spread && tid < cols) {
-        int sb[4] = {0, 0, 0, 0}, sa[4] = {0, 0, 0, 0}, se = 0;
-        for (int j = 0; j < J; ++j) {
-            const int32_t* o = red + (j * cols + tid) * 9;
+    if (spread) {
+        if (tid < nvec) {  // vector tid = neighbour tid % vpt of column tid / vpt
+            const int c = tid / vpt, u = tid % vpt;
+            int sb[4] = {0, 0, 0, 0}, sa[4] = {0, 0, 0, 0};
+            for (int j = 0; j < J; ++j) {
+                const int32_t* o = red + (j * cols + c) * kSpreadStride + 8 * u;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sb[q] += o[q];
-                sa[q] += o[4 + q];
+                for (int q = 0; q < 4; ++q) {
+                    sb[q] += o[q];
+                    sa[q] += o[4 + q];
+                }
             }
-            se += o[8];
-        }
-        if (tid < nvec) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 bef[0][q] = sb[q];
@@ -418,6 +436,8 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
             }
         }
         if (tid < ne) {
+            int se = 0;
+            for (int j = 0; j < J; ++j) se += red[(j * cols + tid) * kSpreadStride + 16];
             etot[0] = se;
             if (te) te[e0 + tid] = se;
         }
@@ -805,7 +825,7 @@ hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout
                                                   (size_t)kScSlots * kWavesPerBlock) +
                               (size_t)(s.R + s.G) * kWords +
                               // partial sums of the spread table loads (only used with many rows)
-                              ((W.nb > 2 * kRowBatch && !L.expert_slot) ? sizeof(int32_t) * kBlockThreads * 9 : 0);
+                              ((W.nb > 2 * kRowBatch && !L.expert_slot) ? sizeof(int32_t) * kBlockThreads * kSpreadStride : 0);
     const dim3 grid(W.nb), block(kBlockThreads);
 #define EP_LAYOUT_LAUNCH(KM)                                                          \
     do {                                                                              \
