@@ -239,7 +239,10 @@ __device__ __forceinline__ void add_rows(const u32x4* x, int b0, int b, int nb, 
     }
 }
 
-template <int KMAX>
+// SPREAD: the launch has more than 2 batches of table rows and no expand
+// rows, so the spread loads below may apply (a separate instantiation keeps
+// the code of the other launches as it is).
+template <int KMAX, bool SPREAD>
 __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs a) {
     extern __shared__ __align__(16) uint32_t lds[];
     uint32_t* bits_r = lds;                                                // [R][kWords]
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
     const int vpt = nvec > 128 ? 2 : 1;
     const int cols = max(max((nvec + vpt - 1) / vpt, ne), 1);
     const int J = kBlockThreads / cols;
-    const bool spread = !expand && vec_rounds == 1 && slice_rounds <= 1 && J >= 2 &&
+    const bool spread = SPREAD && !expand && vec_rounds == 1 && slice_rounds <= 1 && J >= 2 &&
                         a.nb > 2 * kRowBatch;
     auto spread_loads = [&](auto vpt_c) {
         constexpr int VPT = decltype(vpt_c)::value;
@@ -821,16 +824,20 @@ hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout
     a.out = L;
 
     const size_t lds_count = sizeof(uint32_t) * ((size_t)(s.R + s.G) * kWords + s.E);
+    const bool spread_launch = W.nb > 2 * kRowBatch && !L.expert_slot;
     const size_t lds_assign = sizeof(uint32_t) * ((size_t)(s.R + s.G) * kWords + s.R + s.G +
                                                   (size_t)kScSlots * kWavesPerBlock) +
                               (size_t)(s.R + s.G) * kWords +
                               // partial sums of the spread table loads (only used with many rows)
-                              ((W.nb > 2 * kRowBatch && !L.expert_slot) ? sizeof(int32_t) * kBlockThreads * kSpreadStride : 0);
+                              (spread_launch ? sizeof(int32_t) * kBlockThreads * kSpreadStride : 0);
     const dim3 grid(W.nb), block(kBlockThreads);
-#define EP_LAYOUT_LAUNCH(KM)                                                          \
-    do {                                                                              \
-        hipLaunchKernelGGL(layout_count_kernel<KM>, grid, block, lds_count, st, a);   \
-        hipLaunchKernelGGL(layout_assign_kernel<KM>, grid, block, lds_assign, st, a); \
+#define EP_LAYOUT_LAUNCH(KM)                                                                  \
+    do {                                                                                      \
+        hipLaunchKernelGGL(layout_count_kernel<KM>, grid, block, lds_count, st, a);           \
+        if (spread_launch)                                                                    \
+            hipLaunchKernelGGL((layout_assign_kernel<KM, true>), grid, block, lds_assign, st, a); \
+        else                                                                                  \
+            hipLaunchKernelGGL((layout_assign_kernel<KM, false>), grid, block, lds_assign, st, a); \
     } while (0)
     if (s.K <= 2)
         EP_LAYOUT_LAUNCH(2);
