@@ -66,6 +66,9 @@ def parse():
     return p.parse_args()
 
 
+EVENT_STEPS = 20  # eager steps whose launches are bracketed by timing events
+
+
 def ceilings(reps: int = 20) -> dict:
     """Practical HBM rates of library kernels on 1 GiB buffers (GB/s): a
     reduction (read only), a constant fill (write only), two ways of writing
@@ -301,12 +304,14 @@ def main():
             timed("combine", lambda: ep.ep_combine(shape, L, recv["x"], N, 2 * w.H, ep.EP_FMT_PLAIN,
                                                    0, tokens["topk_weights"], out, ws), record)
 
-    def step(record):
+    def step(record, events=None):
+        """One step; `record` counts it as timed, `events` (default: record)
+        brackets its launches with events."""
         i = epoch[0] % n_batches
         epoch[0] += 1
         if record:
             used.append(i)
-        run_step(i, epoch[0], record)
+        run_step(i, epoch[0], record if events is None else events)
 
     for _ in range(args.warmup):
         step(False)
@@ -327,7 +332,10 @@ def main():
 
     # Eager pass: every launch bracketed by events on the launch stream, for
     # the per-kernel durations.
-    ms_eager, wall_eager = timed_region(lambda k: step(True))
+    # Events only on the first EVENT_STEPS steps: every timing event holds a
+    # runtime signal until it is read, and with hundreds of them outstanding
+    # the runtime stalls between launches, which the events would then time.
+    ms_eager, wall_eager = timed_region(lambda k: step(True, k < EVENT_STEPS))
     avg_ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
     if ep.ep_check_errors(ws) != 0:
         raise RuntimeError("device error bits set during the timed steps")
@@ -344,15 +352,28 @@ def main():
             with torch.cuda.graph(g):
                 run_step(i, 1000 + i, False)
             graphs.append(g)
+        # One more graph holding a whole cycle: the steps of every batch in
+        # order, so that one graph launch serves n_batches steps. The timed
+        # steps replay it K // n_batches times, then the single-step graphs of
+        # the first K % n_batches batches.
+        cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cycle):
+            for i in range(n_batches):
+                run_step(i, 1000 + i, False)
         for g in graphs:
             g.replay()
+        cycle.replay()
         torch.cuda.synchronize()
         used.clear()
+        full_until = (args.steps // n_batches) * n_batches
 
         def replay(k):
             i = k % n_batches
             used.append(i)
-            graphs[i].replay()
+            if k >= full_until:
+                graphs[i].replay()
+            elif i == 0:
+                cycle.replay()
 
         ms_total, wall = timed_region(replay)
         if ep.ep_check_errors(ws) != 0:
@@ -420,7 +441,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "ms_per_step_eager": ms_eager / args.steps,
-        "launch": "hip graph per step" if graph_used else "eager",
+        "launch": "hip graphs: one per cycle of the input batches (one step per batch), single-step graphs for the remainder" if graph_used else "eager",
         "wall_s": wall,
         "higher_is_better": True,
         "scaling": "weak",

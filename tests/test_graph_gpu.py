@@ -131,3 +131,33 @@ def test_graph_sources_step():
     outputs = [src["counts"], src["recv_offsets"], src["src_slot"], out] + [recv[k][:N] for k in recv]
     replay_and_compare(run, outputs)
     assert ep.ep_check_errors(ws) == 0
+
+
+def test_graph_cycle_of_steps():
+    """Several steps, one per input batch, captured in one graph (how the
+    benchmark amortises graph launches): the steps share the workspace and the
+    receive buffer, and each step's combine output must equal its eager run."""
+    w = synth.workload("ep32").scaled(1024)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, 1)
+    ws = ep.alloc_workspace(shape)
+    batches = []
+    for i in range(3):
+        inp = synth.make_inputs(w, seed=100 + i)
+        batches.append(dict(x=dev(inp["x"]), topk_idx=dev(inp["topk_idx"]), topk_weights=dev(inp["topk_w"])))
+    Ls = [ep.alloc_layout(shape, masks=True, groups=False) for _ in batches]
+    cap = w.T * min(w.K, w.R)
+    recv = ep.alloc_recv(shape, cap)
+    outs = [torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda") for _ in batches]
+
+    def step(i):
+        tk, L = batches[i], Ls[i]
+        ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+        ep.ep_dispatch(shape, L, tk, recv, cap, ws)
+        ep.ep_combine(shape, L, recv["x"], cap, 2 * w.H, ep.EP_FMT_PLAIN, 0, tk["topk_weights"], outs[i], ws)
+
+    def run():
+        for i in range(len(batches)):
+            step(i)
+
+    replay_and_compare(run, outs + [L["slot"] for L in Ls])
+    assert ep.ep_check_errors(ws) == 0
