@@ -598,6 +598,24 @@ def test_expand_dispatch_and_combine(name, fp8):
     assert ep.ep_check_errors(ws) == 0
 
 
+def test_many_tokens_end_to_end():
+    """262,144 tokens: 1,024 layout workgroups, so every assign workgroup
+    sums 1,024 rows of the count tables (spread over 15 thread groups); then
+    dispatch and combine over about 1.9 M receive rows of a 256-wide hidden."""
+    w = synth.Workload("many", 262144, 256, 256, 32, 1, 8, "uniform")
+    inp = synth.make_inputs(w, seed=5)
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    check_layout(L, O, w.T)
+    recv, N, _ = run_dispatch(w, inp, shape, L, ws, tk)
+    D = oracle.dispatch(inp["topk_idx"], w.E, w.R, O["rank_offsets"], x=inp["x"], topk_w=inp["topk_w"])
+    check_dispatch(recv, D, N)
+    out = poison(torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda"))
+    ep.ep_combine(shape, L, recv["x"], N, 2 * w.H, ep.EP_FMT_PLAIN, 0, dev(inp["topk_w"]), out, ws)
+    np.testing.assert_array_equal(host(out), oracle.combine(O["slot"], inp["topk_w"], D["recv_x"], w.H)["out"])
+    assert ep.ep_check_errors(ws) == 0
+
+
 # --------------------------------------------------------------------------
 # Two-level combine (partials per token and group, then the cross-group sum)
 # --------------------------------------------------------------------------
