@@ -322,6 +322,39 @@ def test_combine_edges(T, H, K):
     assert ep.ep_check_errors(ws) == 0
 
 
+def test_combine_special_values():
+    """bf16 rows and fp32 weights holding +-0, +-Inf, NaN with several
+    payloads, subnormals, the largest finite values and products that
+    overflow: the GPU's fused multiply-adds (subnormals kept, no flush to
+    zero) and its bf16 rounding (NaN -> 0x7FC0) match the oracle bit for bit."""
+    rng = np.random.default_rng(8)
+    T, H, K, rows = 96, 264, 6, 200
+    specials16 = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81, 0x0001, 0x8001,
+                           0x007F, 0x0080, 0x7F7F, 0xFF7F, 0x3F80, 0xBF80], np.uint16)
+    y = synth.random_bf16_rows(rows, H, seed=9)
+    pick = rng.random((rows, H)) < 0.05
+    y[pick] = rng.choice(specials16, size=int(pick.sum()))
+    # rows 0-49: bf16 subnormals only (sums of them stay subnormal or become
+    # the smallest normals)
+    y[:50] = rng.integers(1, 0x80, size=(50, H)).astype(np.uint16) | \
+        (rng.integers(0, 2, size=(50, H)).astype(np.uint16) << 15)
+    specials32 = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e-45, -1e-45, 1e-40, 3.0e38, -3.0e38,
+                           1.0, 0.5], np.float32)
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    pickw = rng.random((T, K)) < 0.1
+    w[pickw] = rng.choice(specials32, size=int(pickw.sum()))
+    slot = rng.integers(-1, rows, size=(T, K)).astype(np.int32)
+    slot[: T // 2] = rng.integers(0, 50, size=(T // 2, K))  # half the tokens read only subnormal rows
+    shape = ep.make_shape(T, H, K, 4, 2, 1)
+    ws = ep.alloc_workspace(shape)
+    out = poison(torch.empty((T, H), dtype=torch.uint16, device="cuda"))
+    ep.ep_clear_errors(ws)
+    ep.ep_combine(shape, dict(slot=dev(slot)), dev(y), rows, 2 * H, ep.EP_FMT_PLAIN, 0, dev(w), out, ws)
+    C = oracle.combine(slot, w, y, H)
+    np.testing.assert_array_equal(host(out), C["out"])
+    assert ep.ep_check_errors(ws) == 0
+
+
 @pytest.mark.parametrize("pad", [8, 64, 1000])
 def test_combine_padded_row_stride(pad):
     """Expert outputs in rows wider than the hidden size (stride > 2H bytes)."""
