@@ -776,6 +776,35 @@ def test_two_level_combine_plain(T, H, K, E, R, G):
     assert ep.ep_check_errors(ws) == 0
 
 
+def test_two_level_combine_special_values():
+    """The two-level combine on rows and weights holding signed zeros,
+    infinities, NaN, subnormals and overflowing products: the bf16 partials
+    and the fp32 cross-group sums match the oracle bit for bit."""
+    T, H, K, E, R, G = 200, 264, 6, 48, 12, 4
+    w = synth.Workload("edge", T, H, E, R, G, K, "uniform")
+    rng = np.random.default_rng(12)
+    topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
+    shape, L, ws, tk = run_layout(w, topk)
+    L["_ws"] = ws
+    N = int(host(L["rank_offsets"])[-1])
+    specials16 = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0x0001, 0x8001, 0x007F, 0x7F7F,
+                           0xFF7F], np.uint16)
+    y = synth.random_bf16_rows(N, H, seed=13)
+    pick = rng.random((N, H)) < 0.05
+    y[pick] = rng.choice(specials16, size=int(pick.sum()))
+    y[: N // 3] = rng.integers(1, 0x80, size=(N // 3, H)).astype(np.uint16)  # subnormal rows
+    wts = rng.standard_normal((T, K)).astype(np.float32)
+    pickw = rng.random((T, K)) < 0.1
+    wts[pickw] = rng.choice(np.array([0.0, -0.0, np.inf, np.nan, 1e-40, 3.0e38], np.float32),
+                            size=int(pickw.sum()))
+    gbuf, out, gcap = run_two_level(shape, L, tk, dev(y), N, 2 * H, ep.EP_FMT_PLAIN, 5, dev(wts))
+    O = oracle.layout(topk, E, R, G)
+    C = oracle.combine_two_level(topk, E, R, G, O["slot"], O["group_slot"], wts, y, H, gcap, 5)
+    np.testing.assert_array_equal(host(gbuf)[:gcap], C["group_buf"])
+    np.testing.assert_array_equal(host(out), C["out"])
+    assert ep.ep_check_errors(ws) == 0
+
+
 @pytest.mark.parametrize("K", [6, 24])
 def test_two_level_combine_corrupted_input_rows(K):
     """A chunked expert-output row with a bad flag in its first or last hidden
