@@ -161,3 +161,55 @@ def test_graph_cycle_of_steps():
 
     replay_and_compare(run, outs + [L["slot"] for L in Ls])
     assert ep.ep_check_errors(ws) == 0
+
+
+@pytest.mark.parametrize("name", ["ep32", "zipf"])
+def test_graph_cycle_full_size_against_oracle(name):
+    """The full-size workload in the launch configuration the benchmark times:
+    the steps of two input batches captured in one graph (shared workspace
+    and receive buffer, per-batch layouts), replayed, and every output of the
+    last replay compared with the CPU oracle."""
+    import oracle
+
+    oracle.build(force=False)
+    w = synth.workload(name)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, 1)
+    ws = ep.alloc_workspace(shape)
+    inps = [synth.make_inputs(w, seed=synth.seed_of(w) + 1000 * i) for i in range(2)]
+    batches = [dict(x=dev(b["x"]), topk_idx=dev(b["topk_idx"]), topk_weights=dev(b["topk_w"])) for b in inps]
+    Ls = [ep.alloc_layout(shape, masks=True, groups=False) for _ in batches]
+    cap = w.T * min(w.K, w.R)
+    recv = ep.alloc_recv(shape, cap)
+    outs = [torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda") for _ in batches]
+
+    def run():
+        for i, tk in enumerate(batches):
+            ep.ep_get_layout(shape, tk["topk_idx"], Ls[i], ws)
+            ep.ep_dispatch(shape, Ls[i], tk, recv, cap, ws)
+            ep.ep_combine(shape, Ls[i], recv["x"], cap, 2 * w.H, ep.EP_FMT_PLAIN, 0, tk["topk_weights"],
+                          outs[i], ws)
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for o in outs:
+        o.view(torch.uint8).fill_(0xA5)
+    recv["x"].view(torch.uint8).fill_(0xA5)
+    torch.cuda.synchronize()
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    assert ep.ep_check_errors(ws) == 0
+    for i, b in enumerate(inps):
+        O = oracle.layout(b["topk_idx"], w.E, w.R, 1)
+        np.testing.assert_array_equal(Ls[i]["slot"].cpu().numpy().reshape(w.T, w.K), O["slot"])
+        D = oracle.dispatch(b["topk_idx"], w.E, w.R, O["rank_offsets"], x=b["x"], topk_w=b["topk_w"])
+        C = oracle.combine(O["slot"], b["topk_w"], D["recv_x"], w.H)
+        got = outs[i].view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, C["out"], err_msg=f"batch {i}")
+        if i == len(inps) - 1:  # the receive rows hold the last batch's dispatch
+            N = int(O["rank_offsets"][-1])
+            rx = recv["x"].view(torch.int16).cpu().numpy().view(np.uint16)[:N]
+            np.testing.assert_array_equal(rx, D["recv_x"])
