@@ -606,6 +606,85 @@ def test_expert_slots_equal_rank_slots_with_one_expert_per_rank(oracle_lib):
     np.testing.assert_array_equal(es, L["slot"])
 
 
+def brute_expand_receive(topk, E, x, fp8, sc, w):
+    """Receive arrays of expand mode built by enumeration: the i-th valid
+    (expert, token, lane) triple in sorted order is row i, and it holds its
+    token's record: hidden, FP8, scales and weights copied from token t, the
+    source index t, and the token's ids with every id outside [0, E) shown
+    as -1."""
+    T, K = topk.shape
+    trip = sorted((int(topk[t, k]), t, k) for t in range(T) for k in range(K) if 0 <= topk[t, k] < E)
+    n = len(trip)
+    out = dict(recv_x=np.zeros((n, x.shape[1]), np.uint16), recv_fp8=np.zeros((n, fp8.shape[1]), np.uint8),
+               recv_scales=np.zeros((n, sc.shape[1]), np.float32), recv_src=np.zeros(n, np.int32),
+               recv_topk_idx=np.zeros((n, K), np.int32), recv_topk_w=np.zeros((n, K), np.float32))
+    for i, (_, t, _) in enumerate(trip):
+        out["recv_x"][i] = x[t]
+        out["recv_fp8"][i] = fp8[t]
+        out["recv_scales"][i] = sc[t]
+        out["recv_src"][i] = t
+        for k in range(K):
+            e = int(topk[t, k])
+            out["recv_topk_idx"][i, k] = e if 0 <= e < E else -1
+        out["recv_topk_w"][i] = w[t]
+    return out
+
+
+def _assert_receive_equal(got, want, fields):
+    for f in fields:
+        a, b = np.asarray(got[f]), np.asarray(want[f])
+        assert a.shape == b.shape, f
+        if a.dtype == np.float32:
+            a, b = a.view(np.uint32), b.view(np.uint32)
+        np.testing.assert_array_equal(a, b, err_msg=f)
+
+
+EXPAND_FIELDS = ("recv_x", "recv_fp8", "recv_scales", "recv_src", "recv_topk_idx", "recv_topk_w")
+
+
+def test_expand_receive_arrays_brute_force(oracle_lib):
+    """Every field of the expand-mode receive rows (DeepEP V2 page, 3.3 阶段3:
+    the copy epilogue's per-expert rows) against the sorted-triple
+    enumeration, on the tiny cases plus ids below -1 and at or above E (they
+    are skipped and show as -1 in the copied ids)."""
+    rng = np.random.default_rng(29)
+    cases = list(_tiny_cases())
+    for i in range(30):  # invalid ids other than -1
+        E = int(rng.choice([4, 6, 8]))
+        T, K = int(rng.integers(1, 6)), int(rng.integers(1, 5))
+        topk = rng.integers(-3, E + 3, size=(T, K)).astype(np.int64)
+        cases.append((topk, E, 1, 1))
+    for topk, E, R, G in cases:
+        T, K = topk.shape
+        H = 256
+        x = rng.integers(0, 65536, size=(T, H)).astype(np.uint16)
+        fp8 = rng.integers(0, 256, size=(T, H)).astype(np.uint8)
+        sc = rng.standard_normal((T, H // 128)).astype(np.float32)
+        w = rng.standard_normal((T, K)).astype(np.float32)
+        L = oracle_lib.layout(topk, E, R, G)
+        es = oracle_lib.expert_slots(topk, E, L["expert_offsets"])
+        n_rows = int(L["expert_offsets"][-1])
+        D = oracle_lib.dispatch_rows(topk, E, es, n_rows, x=x, x_fp8=fp8, x_scales=sc, topk_w=w)
+        _assert_receive_equal(D, brute_expand_receive(topk, E, x, fp8, sc, w), EXPAND_FIELDS)
+
+
+def test_expand_receive_equals_direct_with_one_expert_per_rank(oracle_lib):
+    """With one expert per rank (E = R) and distinct experts per token, each
+    lane's expert row is its rank row, so the expand-mode receive arrays are
+    the direct dispatch's, byte for byte, in every field."""
+    w = synth.Workload("e_eq_r", 700, 256, 64, 64, 1, 6, "uniform")
+    inp = synth.make_inputs(w, seed=31, with_fp8=True)
+    topk = inp["topk_idx"]
+    L = oracle_lib.layout(topk, w.E, w.R)
+    es = oracle_lib.expert_slots(topk, w.E, L["expert_offsets"])
+    n_rows = int(L["expert_offsets"][-1])
+    assert n_rows == int(L["rank_offsets"][-1]) == w.T * w.K
+    kw = dict(x=inp["x"], x_fp8=inp["x_fp8"], x_scales=inp["x_scales"], topk_w=inp["topk_w"])
+    Dx = oracle_lib.dispatch_rows(topk, w.E, es, n_rows, **kw)
+    D = oracle_lib.dispatch(topk, w.E, w.R, L["rank_offsets"], **kw)
+    _assert_receive_equal(Dx, D, EXPAND_FIELDS)
+
+
 def test_expand_round_trip_equals_rank_combine(oracle_lib):
     """Identity expert: combining the per-lane rows gives bit for bit what
     combining the deduplicated per-rank rows gives (same values, same order)."""
