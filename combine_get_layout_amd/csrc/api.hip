@@ -50,7 +50,10 @@ RecordGeom record_geom(const ep_shape& s, int seg) {
 
 namespace {
 
-__global__ void clear_error_kernel(uint32_t* err) { *err = 0u; }
+__global__ void clear_error_kernel(uint32_t* err) {
+    err[0] = 0u;  // current pass
+    err[1] = 0u;  // since the last clear
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -319,14 +322,23 @@ int ep_clear_errors(void* ws, void* stream) {
     return hip_status(hipGetLastError());
 }
 
-int ep_check_errors(void* ws, void* stream, uint32_t* bits) {
+// Reads error word `which` (0: current pass, 1: since the last clear).
+static int read_error_word(void* ws, void* stream, uint32_t* bits, int which) {
     if (!ws || !bits || !aligned(ws, 256)) return EP_ERR_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    uint32_t v = 0;
-    if (hipMemcpyAsync(&v, ws, sizeof v, hipMemcpyDeviceToHost, st) != hipSuccess) return EP_ERR_HIP;
+    uint32_t v[2] = {0u, 0u};
+    if (hipMemcpyAsync(v, ws, sizeof v, hipMemcpyDeviceToHost, st) != hipSuccess) return EP_ERR_HIP;
     if (hipStreamSynchronize(st) != hipSuccess) return EP_ERR_HIP;
-    *bits = v;
-    return EP_OK;
+    *bits = v[which];
+    return v[which] ? EP_ERR_DEVICE : EP_OK;
+}
+
+int ep_check_errors(void* ws, void* stream, uint32_t* bits) {
+    return read_error_word(ws, stream, bits, 0);
+}
+
+int ep_check_sticky_errors(void* ws, void* stream, uint32_t* bits) {
+    return read_error_word(ws, stream, bits, 1);
 }
 
 const char* ep_status_string(int status) {
@@ -335,6 +347,9 @@ const char* ep_status_string(int status) {
         case EP_ERR_ARG: return "invalid argument (null or misaligned pointer, bad shape or size)";
         case EP_ERR_UNSUPPORTED: return "shape outside the supported limits";
         case EP_ERR_HIP: return "HIP runtime or launch error";
+        case EP_ERR_DEVICE:
+            return "device-detected error: bad expert id, capacity exceeded or flag/epoch mismatch "
+                   "(the bits are in the workspace error word)";
         default: return "unknown status";
     }
 }

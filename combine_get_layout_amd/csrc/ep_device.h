@@ -55,8 +55,12 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// The workspace holds two error words: err[0] covers the current pass of
+// calls (the layout calls clear it), err[1] every call since the last
+// ep_clear_errors (nothing else clears it). A report sets the bits in both.
 __device__ __forceinline__ void report(uint32_t* err, uint32_t bits) {
     atomicOr(reinterpret_cast<unsigned int*>(err), bits);
+    atomicOr(reinterpret_cast<unsigned int*>(err) + 1, bits);
 }
 
 // bf16 bit pattern -> float (bf16 is the upper half of a binary32).

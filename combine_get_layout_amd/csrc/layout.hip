@@ -808,8 +808,11 @@ __global__ __launch_bounds__(kBlockThreads) void layout_expand_wide_kernel(Layou
 
 }  // namespace
 
-hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout& L, char* ws,
-                         hipStream_t st) {
+// The count tables of the launches below sit at the offsets ws_layout gives,
+// from `tables` (a workspace, or the scratch array of the allocation-free
+// entry point); the error words are at `err`.
+static hipError_t launch_layout_tables(const ep_shape& s, const int64_t* topk, const ep_layout& L,
+                                       uint32_t* err, char* tables, hipStream_t st) {
     const WsLayout W = ws_layout(s);
     LayoutArgs a;
     a.T = s.T; a.K = s.K; a.E = s.E; a.R = s.R; a.G = s.G;
@@ -818,9 +821,9 @@ hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout
     a.div_P = FastDiv::make(a.P);
     a.rp = W.rp; a.wrow = W.wrow;
     a.topk = topk;
-    a.err = reinterpret_cast<uint32_t*>(ws + W.err);
-    a.part_rlg = reinterpret_cast<int32_t*>(ws + W.part_rlg);
-    a.part_expert = reinterpret_cast<int32_t*>(ws + W.part_expert);
+    a.err = err;
+    a.part_rlg = reinterpret_cast<int32_t*>(tables + W.part_rlg);
+    a.part_expert = reinterpret_cast<int32_t*>(tables + W.part_expert);
     a.out = L;
 
     const size_t lds_count = sizeof(uint32_t) * ((size_t)(s.R + s.G) * kWords + s.E);
@@ -868,6 +871,11 @@ hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout
         }
     }
     return hipGetLastError();
+}
+
+hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout& L, char* ws,
+                         hipStream_t st) {
+    return launch_layout_tables(s, topk, L, reinterpret_cast<uint32_t*>(ws + ws_layout(s).err), ws, st);
 }
 
 }  // namespace ep

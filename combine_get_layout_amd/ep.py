@@ -18,7 +18,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libep.so")
 
-EP_OK, EP_ERR_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, -1, -2, -3
+EP_OK, EP_ERR_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP, EP_ERR_DEVICE = 0, -1, -2, -3, -4
 EP_DEVERR_EXPERT_ID, EP_DEVERR_CAPACITY, EP_DEVERR_FLAG = 1, 2, 4
 EP_SEG_BF16, EP_SEG_FP8, EP_SEG_SCALES = 1, 2, 4
 EP_FMT_PLAIN, EP_FMT_CHUNKED = 0, 1
@@ -58,7 +58,8 @@ EXPORTS = ("ep_workspace_bytes", "ep_record_bytes", "ep_chunked_record_bytes", "
            "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch", "ep_combine",
            "ep_combine_expand", "ep_partial_row_bytes", "ep_combine_two_level",
            "ep_source_workspace_bytes", "ep_source_layout", "ep_source_dispatch",
-           "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors", "ep_status_string")
+           "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors", "ep_check_sticky_errors",
+           "ep_status_string")
 
 _lib = None
 
@@ -100,11 +101,14 @@ def lib() -> ctypes.CDLL:
                                    _P]
     L.ep_clear_errors.argtypes = [_P, _P]
     L.ep_check_errors.argtypes = [_P, _P, ctypes.POINTER(u32)]
+    L.ep_check_sticky_errors.argtypes = [_P, _P, ctypes.POINTER(u32)]
     L.ep_status_string.argtypes = [ctypes.c_int]
     L.ep_status_string.restype = ctypes.c_char_p
-    for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch",
+    for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_expand",
+              "ep_hierarchical_dispatch",
               "ep_combine", "ep_combine_expand", "ep_combine_two_level", "ep_source_layout",
-              "ep_source_dispatch", "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors"):
+              "ep_source_dispatch", "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors",
+              "ep_check_sticky_errors"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -320,11 +324,23 @@ def ep_clear_errors(ws, stream=None):
     _check(lib().ep_clear_errors(_ptr(ws, "workspace"), _stream(stream)), "ep_clear_errors")
 
 
-def ep_check_errors(ws, stream=None) -> int:
+def _error_bits(fn, name, ws, stream) -> int:
     bits = ctypes.c_uint32(0)
-    _check(lib().ep_check_errors(_ptr(ws, "workspace"), _stream(stream), ctypes.byref(bits)),
-           "ep_check_errors")
+    rc = fn(_ptr(ws, "workspace"), _stream(stream), ctypes.byref(bits))
+    if rc != EP_ERR_DEVICE:  # EP_ERR_DEVICE: bits are set, and returned
+        _check(rc, name)
     return int(bits.value)
+
+
+def ep_check_errors(ws, stream=None) -> int:
+    """Error bits of the current pass (0 when none; EP_ERR_DEVICE is not
+    raised: the bits are the answer)."""
+    return _error_bits(lib().ep_check_errors, "ep_check_errors", ws, stream)
+
+
+def ep_check_sticky_errors(ws, stream=None) -> int:
+    """Error bits of every call since the last ep_clear_errors."""
+    return _error_bits(lib().ep_check_sticky_errors, "ep_check_sticky_errors", ws, stream)
 
 
 def ep_status_string(status: int) -> str:
@@ -336,17 +352,19 @@ def ep_status_string(status: int) -> str:
 # --------------------------------------------------------------------------
 
 def alloc_workspace(shape: ep_shape, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (both error words start clear)."""
     n = ep_workspace_bytes(shape)
     if n == 0:
         raise RuntimeError("ep_workspace_bytes: unsupported shape")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def alloc_source_workspace(shape: ep_shape, S: int, device="cuda") -> torch.Tensor:
+    """A zero-filled several-source workspace."""
     n = ep_source_workspace_bytes(shape, S)
     if n == 0:
         raise RuntimeError("ep_source_workspace_bytes: unsupported shape or source count")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def alloc_sources(shape: ep_shape, S: int, capacity: int, device="cuda") -> dict:

@@ -30,7 +30,8 @@
  *     16 B aligned base pointers; other arrays their element alignment.
  *   - Return value: EP_OK, or a negative EP_ERR_* status. Nothing is enqueued
  *     when a host-side check fails. Problems only visible on the device set
- *     bits in the workspace's error word (read with ep_check_errors).
+ *     bits in the workspace's error words (read with ep_check_errors and
+ *     ep_check_sticky_errors, which return EP_ERR_DEVICE when a bit is set).
  */
 #ifndef EP_H
 #define EP_H
@@ -47,8 +48,11 @@ extern "C" {
 #define EP_ERR_ARG (-1)         /* null / misaligned pointer, bad shape, bad size */
 #define EP_ERR_UNSUPPORTED (-2) /* shape outside the supported limits below */
 #define EP_ERR_HIP (-3)         /* a HIP runtime call or launch failed */
+#define EP_ERR_DEVICE (-4)      /* the device reported an error: ep_check_errors /
+                                   ep_check_sticky_errors return it when error bits are
+                                   set and write the bits (EP_DEVERR_*) to *bits */
 
-/* Device error bits (workspace error word). */
+/* Device error bits (workspace error words). */
 #define EP_DEVERR_EXPERT_ID 1u  /* an expert id < -1 or >= E (treated as -1) */
 #define EP_DEVERR_CAPACITY 2u   /* a row index >= the given buffer capacity (not written / not read) */
 #define EP_DEVERR_FLAG 4u       /* a 512 B chunk flag != epoch (row dropped / skipped) */
@@ -121,8 +125,11 @@ typedef struct ep_recv {
 } ep_recv;
 
 /* Bytes of workspace the calls need for `shape` (host only, no GPU work).
- * Layout: a 4-byte error word at offset 0, then per-block partial counts.
- * The workspace may be reused by successive calls on one stream. */
+ * Layout: two u32 error words at offset 0 (word 0: errors of the current
+ * pass of calls, cleared by the layout calls; word 1: errors since the last
+ * ep_clear_errors, cleared by nothing else; undefined in a new workspace
+ * until its first ep_clear_errors), then per-block partial counts. The
+ * workspace may be reused by successive calls on one stream. */
 size_t ep_workspace_bytes(const ep_shape *shape);
 
 /* Byte length P of a packed token record with pieces `seg_flags`
@@ -142,7 +149,7 @@ int64_t ep_chunked_record_bytes(const ep_shape *shape, int seg_flags);
  * prefix sums. Slot: slot[t*K+k] = rank_offsets[r] + #{t' < t : token t'
  * sends to r} (repeated ranks in a token share the row); group_slot likewise
  * with groups. Every output pointer except the workspace may be NULL to skip
- * that output. Also clears the workspace error word first, so a pass of
+ * that output. Also clears workspace error word 0 first, so a pass of
  * calls starts with a clean word. Ids < -1 or >= E set EP_DEVERR_EXPERT_ID
  * and count as -1. ws: at least ep_workspace_bytes(shape) bytes, 256 B
  * aligned. */
@@ -271,7 +278,7 @@ size_t ep_source_workspace_bytes(const ep_shape *shape, int32_t S);
 
 /* Per-source counts, the counts exchange (recv_offsets, what every
  * destination learns from an all-to-all of counts) and src_slot. Clears the
- * workspace error word first. j >= capacity sets EP_DEVERR_CAPACITY and the
+ * workspace error word 0 first. j >= capacity sets EP_DEVERR_CAPACITY and the
  * lane gets -1; invalid ids set EP_DEVERR_EXPERT_ID. Deterministic: with
  * contiguous sources, region (r, s) of the dense rows is exactly the part of
  * rank r's region (ep_get_layout) that holds source s's tokens, so dense row
@@ -300,11 +307,22 @@ int ep_copy_epilogue(const ep_shape *shape, const ep_sources *sources, const voi
                      uint32_t epoch, int seg_flags, const ep_recv *recv, void *ws,
                      size_t ws_bytes, void *stream);
 
-/* Clear the workspace error word (a stream-ordered kernel, no memset node). */
+/* Clear both workspace error words (a stream-ordered kernel, no memset
+ * node). */
 int ep_clear_errors(void *ws, void *stream);
 
-/* Synchronise `stream`, then copy the error word to *bits (host pointer). */
+/* Synchronise `stream`, then copy error word 0 (the errors since the last
+ * ep_get_layout / ep_source_layout call on this workspace) to *bits (host
+ * pointer). Returns EP_OK when no bit is set, EP_ERR_DEVICE when one is
+ * ([V2] §3.5: the caller learns of a failed pass from the call, not only
+ * from the data), EP_ERR_ARG / EP_ERR_HIP when the word could not be read
+ * (*bits is then left unchanged). */
 int ep_check_errors(void *ws, void *stream, uint32_t *bits);
+
+/* As ep_check_errors, for error word 1: every error any call on this
+ * workspace reported since the last ep_clear_errors, across passes (a pass
+ * that follows a failed one does not hide it). */
+int ep_check_sticky_errors(void *ws, void *stream, uint32_t *bits);
 
 /* Static description of a status code. */
 const char *ep_status_string(int status);

@@ -49,6 +49,9 @@ int main(void) {
     check(ep_clear_errors(NULL, NULL) == EP_ERR_ARG, "clear_errors without workspace");
     uint32_t bits = 7;
     check(ep_check_errors(NULL, NULL, &bits) == EP_ERR_ARG, "check_errors without workspace");
+    check(ep_check_sticky_errors(NULL, NULL, &bits) == EP_ERR_ARG, "check_sticky_errors without workspace");
+    check(bits == 7, "bits left unchanged when the word cannot be read");
+    check(strstr(ep_status_string(EP_ERR_DEVICE), "device") != NULL, "status string of EP_ERR_DEVICE");
 
     check(strcmp(ep_status_string(EP_OK), "ok") == 0, "status string of EP_OK");
     check(strlen(ep_status_string(EP_ERR_HIP)) > 0, "status string of EP_ERR_HIP");

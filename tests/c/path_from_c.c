@@ -209,6 +209,32 @@ int main(void) {
         printf("FAIL error bits %u != %u\n", bits, want_bits);
         ok = 0;
     }
+    /* error reporting: an invalid id makes ep_check_errors return
+     * EP_ERR_DEVICE with the id bit; a clean pass after it clears word 0,
+     * while word 1 keeps the bit until ep_clear_errors. */
+    {
+        const int64_t bad_id = E + 3, good_id = ids[5];
+        uint32_t b0 = 99, b1 = 99;
+        EP_OK_(ep_clear_errors(ws, st));
+        HIP_OK(hipMemcpy(d_ids + 5, &bad_id, sizeof bad_id, hipMemcpyHostToDevice));
+        EP_OK_(ep_get_layout(&s, d_ids, &L, ws, ws_bytes, st));
+        int rc = ep_check_errors(ws, st, &b0);
+        ok &= rc == EP_ERR_DEVICE && b0 == EP_DEVERR_EXPERT_ID;
+        printf("%s invalid id: status %d, bits %u\n", rc == EP_ERR_DEVICE && b0 == EP_DEVERR_EXPERT_ID ? "ok" : "FAIL",
+               rc, b0);
+        HIP_OK(hipMemcpy(d_ids + 5, &good_id, sizeof good_id, hipMemcpyHostToDevice));
+        EP_OK_(ep_get_layout(&s, d_ids, &L, ws, ws_bytes, st));
+        rc = ep_check_errors(ws, st, &b0);
+        const int rc1 = ep_check_sticky_errors(ws, st, &b1);
+        const int pass_ok = rc == EP_OK && b0 == 0 && rc1 == EP_ERR_DEVICE && b1 == EP_DEVERR_EXPERT_ID;
+        ok &= pass_ok;
+        printf("%s clean pass after it: status %d bits %u, since clear: status %d bits %u\n",
+               pass_ok ? "ok" : "FAIL", rc, b0, rc1, b1);
+        EP_OK_(ep_clear_errors(ws, st));
+        rc = ep_check_sticky_errors(ws, st, &b1);
+        ok &= rc == EP_OK && b1 == 0;
+        printf("%s cleared: status %d bits %u\n", rc == EP_OK && b1 == 0 ? "ok" : "FAIL", rc, b1);
+    }
     /* two-level path on the same tokens, R ranks in G2 groups */
     {
         static int32_t p_tpe[E], p_tpr[R], p_tpg[G2], p_eo[E + 1], p_ro[R + 1], p_go[G2 + 1], p_slot[T * K],

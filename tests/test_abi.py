@@ -85,6 +85,8 @@ def test_null_and_misaligned_arguments_rejected_before_launch(lib):
                           0x3000, 0x4000, ws, n, None) == ep.EP_ERR_ARG
     assert lib.ep_clear_errors(None, None) == ep.EP_ERR_ARG
     assert lib.ep_check_errors(None, None, None) == ep.EP_ERR_ARG
+    assert lib.ep_check_sticky_errors(None, None, None) == ep.EP_ERR_ARG
+    assert ep.EP_ERR_DEVICE == -4 and "device" in ep.ep_status_string(ep.EP_ERR_DEVICE)
     assert ep.ep_status_string(0) == "ok"
 
 

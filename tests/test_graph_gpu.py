@@ -1,8 +1,8 @@
 """The path captured into a HIP graph (torch.cuda.CUDAGraph over the C ABI
 calls) and replayed several times, with eager work and synchronisations
 between the replays: every replay must equal the eager result bit for bit.
-The graph holds kernel launches only (the error word is cleared by the layout
-kernel, not by a memset)."""
+The graph holds kernel launches only (the per-pass error word is cleared by
+the layout kernel, not by a memset)."""
 import numpy as np
 import pytest
 import torch
@@ -161,6 +161,49 @@ def test_graph_cycle_of_steps():
 
     replay_and_compare(run, outs + [L["slot"] for L in Ls])
     assert ep.ep_check_errors(ws) == 0
+    assert ep.ep_check_sticky_errors(ws) == 0
+
+
+def test_graph_cycle_error_in_an_earlier_step_is_kept():
+    """An invalid expert id in the first batch of a two-step cycle graph:
+    the second step's layout clears the per-pass error word, so only the
+    word kept since ep_clear_errors still shows the error after the replay."""
+    w = synth.workload("ep32").scaled(1024)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, 1)
+    ws = ep.alloc_workspace(shape)
+    batches = []
+    for i in range(2):
+        inp = synth.make_inputs(w, seed=200 + i)
+        ids = inp["topk_idx"].copy()
+        if i == 0:
+            ids[17, 3] = w.E + 5
+        batches.append(dict(x=dev(inp["x"]), topk_idx=dev(ids), topk_weights=dev(inp["topk_w"])))
+    Ls = [ep.alloc_layout(shape, masks=False, groups=False) for _ in batches]
+    cap = w.T * min(w.K, w.R)
+    recv = ep.alloc_recv(shape, cap)
+    out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
+
+    def run():
+        for tk, L in zip(batches, Ls):
+            ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+            ep.ep_dispatch(shape, L, tk, recv, cap, ws)
+            ep.ep_combine(shape, L, recv["x"], cap, 2 * w.H, ep.EP_FMT_PLAIN, 0, tk["topk_weights"], out, ws)
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    ep.ep_clear_errors(ws)
+    assert ep.ep_check_sticky_errors(ws) == 0
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    assert ep.ep_check_errors(ws) == 0  # the last step's pass is clean
+    assert ep.ep_check_sticky_errors(ws) == ep.EP_DEVERR_EXPERT_ID
+    ep.ep_clear_errors(ws)
+    assert ep.ep_check_sticky_errors(ws) == 0
 
 
 @pytest.mark.parametrize("name", ["ep32", "zipf"])
@@ -202,6 +245,7 @@ def test_graph_cycle_full_size_against_oracle(name):
     g.replay()
     torch.cuda.synchronize()
     assert ep.ep_check_errors(ws) == 0
+    assert ep.ep_check_sticky_errors(ws) == 0
     for i, b in enumerate(inps):
         O = oracle.layout(b["topk_idx"], w.E, w.R, 1)
         np.testing.assert_array_equal(Ls[i]["slot"].cpu().numpy().reshape(w.T, w.K), O["slot"])
