@@ -10,18 +10,25 @@ A step is one pass of the whole path over one batch of synthetic tokens:
                      ep_source_layout -> ep_source_dispatch into per-(rank,
                      source) staging regions -> ep_copy_epilogue into dense
                      receive rows -> ep_combine over the staging rows
-Inputs are seeded and already resident in HBM when the timed region starts.
-W untimed warm-up steps; then K eager steps with every launch bracketed by
-events (the per-kernel durations); then, unless --eager, one HIP graph per
-input batch is captured and exactly K graph replays are timed between two
-device synchronisations: that is `value` and `ms_per_step`. Prints one JSON
-line.
+With no --workload the run times every target configuration in turn (ep32,
+ep32 with the FP8 + scales payload, ep256, zipf, hier8x8); the headline
+fields are ep32's and `per_config` holds one entry per configuration. With
+--workload only that one is timed.
 
-Also reported: per-kernel average durations from HIP events recorded on the
-stream the kernels run on, the roofline of the dominant kernel (algorithmic
-bytes per launch / average duration, against 8 TB/s HBM), HBM traffic from the
-committed rocprofv3 counter summary when it matches the current kernel
-sources, and the CPU oracle timed on the host cores on a bounded sample.
+Inputs are seeded and already resident in HBM when the timed region starts.
+Per configuration: W untimed warm-up steps; then K eager steps whose launches
+(the first 20) are bracketed by events on the launch stream (the per-kernel
+durations); then, unless --eager, the K steps are captured into one HIP graph
+(for K <= 512; above that one graph per cycle of input batches, replayed,
+plus single-step graphs for the remainder) and replayed between two device
+synchronisations: that is `value` and `ms_per_step`. Prints one JSON line.
+
+Also reported per configuration: per-kernel average durations from HIP events
+recorded on the stream the kernels run on, the roofline of the dominant kernel
+(algorithmic bytes per launch / average duration, against 8 TB/s HBM), HBM
+traffic from the committed rocprofv3 counter summary when it matches the
+current kernel sources, and the CPU oracle timed on the host cores on a
+bounded sample.
 """
 from __future__ import annotations
 
@@ -45,9 +52,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="ep32",
-                   choices=["tiny", "ep32", "ep256", "zipf", "hier8x8"])
+    p.add_argument("--workload", default=None,
+                   choices=["tiny", "ep32", "ep256", "zipf", "hier8x8"],
+                   help="time only this workload (default: every target configuration, ep32 first)")
     p.add_argument("--fp8", action="store_true", help="also move the FP8 payload + scales")
+    p.add_argument("--fused", action="store_true",
+                   help="two-level workloads: both dispatch steps in one persistent launch with "
+                        "per-batch flags (ep_hierarchical_dispatch_fused)")
+    p.add_argument("--fused-tile", type=int, default=0, help="tokens per batch of --fused (0: default)")
     p.add_argument("--two-level-combine", action="store_true",
                    help="two-level workloads: combine through per-group partial rows")
     p.add_argument("--expand", action="store_true",
@@ -55,9 +67,10 @@ def parse():
     p.add_argument("--sources", type=int, default=None, const=0, nargs="?",
                    help="several source ranks on one GPU (S; bare flag = one per rank)")
     p.add_argument("--eager", action="store_true",
-                   help="time eager launches only (default: replay one HIP graph per step)")
+                   help="time eager launches only (default: replay a HIP graph of the timed steps)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="time budget of the CPU-oracle baseline (0 = skip)")
+                   help="time budget of the CPU-oracle baseline of the headline configuration "
+                        f"(the others get at most {CPU_SECONDS_OTHER} s and at least one pass; 0 = skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     p.add_argument("--ceilings", action="store_true",
@@ -116,6 +129,7 @@ KERNEL_FILES = {
     "dispatch_kernel": ["dispatch.hip"],
     "combine_kernel": ["combine.hip"],
     "scaleout_kernel+forward_kernel": ["hier.hip"],
+    "fused_hier_kernel": ["hier.hip"],
     "scaleout_kernel": ["hier.hip"],
     "copy_epilogue_kernel": ["source.hip"],
     "combine_group_kernel+combine_cross_kernel": ["combine2.hip"],
@@ -150,6 +164,18 @@ def committed_traffic(workload: str, kernel: str):
     return k.get("hbm_bytes_per_launch")
 
 
+# The configurations the default run times: the headline first.
+TARGET_CONFIGS = [
+    ("ep32", dict(fp8=False)),
+    ("ep32_fp8", dict(fp8=True)),
+    ("ep256", dict(fp8=False)),
+    ("zipf", dict(fp8=False)),
+    ("hier8x8", dict(fp8=False)),
+]
+GRAPH_MAX_STEPS = 512  # up to this many timed steps go into one graph
+CPU_SECONDS_OTHER = 3.0  # CPU-oracle budget of the non-headline configurations
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -157,10 +183,8 @@ def main():
               "cross-GPU step; several GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    import synth
     from combine_get_layout_amd import ep
 
     if not torch.cuda.is_available():
@@ -173,11 +197,51 @@ def main():
         return
     ep.lib()
     torch.cuda.set_device(0)
-    w = synth.workload(args.workload)
+    variants = args.fp8 or args.expand or args.two_level_combine or args.fused or args.sources is not None
+    if args.workload is None and not variants:
+        runs = [(label, "ep32" if label.startswith("ep32") else label, kw) for label, kw in TARGET_CONFIGS]
+    else:
+        w = args.workload or "ep32"
+        runs = [(w, w, dict(fp8=bool(args.fp8)))]
+    per = {}
+    for n, (label, wname, kw) in enumerate(runs):
+        print(f"[bench] {label}: {args.warmup} warm-up + {args.steps} timed steps", file=sys.stderr,
+              flush=True)
+        cpu_s = args.cpu_seconds if n == 0 else min(args.cpu_seconds, CPU_SECONDS_OTHER)
+        per[label] = run_config(args, wname, kw["fp8"], cpu_s)
+        print(f"[bench] {label}: {per[label]['ms_per_step'] * 1e3:.1f} us per step, "
+              f"{100 * per[label]['hbm_frac_step']:.1f}% of HBM peak", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+
+    head = per[runs[0][0]]
+    rec = {"metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup}
+    rec.update({k: v for k, v in head.items() if k not in ("value",)})
+    if len(per) > 1:
+        rec["per_config"] = {label: {k: r[k] for k in PER_CONFIG_KEYS} for label, r in per.items()}
+    print(json.dumps(rec), flush=True)
+
+
+PER_CONFIG_KEYS = ("value", "unit", "ms_per_step", "hbm_gbs_step", "hbm_frac_step", "launch", "config",
+                   "kernel_ms", "roofline", "cpu_baseline")
+
+
+def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
+    """Time one configuration; returns its record (without the run-wide fields)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from combine_get_layout_amd import ep
+
+    w = synth.workload(wname)
     hier = w.G > 1
-    fp8 = bool(args.fp8)
     expand = bool(args.expand)
     two_level = bool(args.two_level_combine)
+    fused = bool(args.fused)
+    if fused and not hier:
+        print("--fused applies to the two-level workloads", file=sys.stderr)
+        sys.exit(2)
     if two_level and not hier:
         print("--two-level-combine applies to the two-level workloads", file=sys.stderr)
         sys.exit(2)
@@ -212,6 +276,8 @@ def main():
             tk["x_fp8"] = dev(b_in["x_fp8"])
             tk["x_scales"] = dev(b_in["x_scales"])
         batches.append(tk)
+    if n_batches > 64:  # (tiny) keep the host copies of only the batch the CPU leg uses
+        inputs = [inp]
     L = ep.alloc_layout(shape, masks=True, groups=hier, expand=expand)
     ws = ep.alloc_workspace(shape)
     Ns, Gs = [], []
@@ -283,10 +349,14 @@ def main():
                                                    out, ws), record)
             return
         timed("layout", lambda: ep.ep_get_layout(shape, tokens["topk_idx"], L, ws), record)
-        if hier:
+        if hier and fused:
+            timed("hier", lambda: ep.ep_hierarchical_dispatch_fused(
+                shape, L, tokens, e, group_buf, G_rows, peer_buf, N, ws, tile=args.fused_tile), record)
+        if hier and not fused:
             timed("hier", lambda: ep.ep_hierarchical_dispatch(
                 shape, L, tokens, e, ep.EP_HIER_SCALEOUT | ep.EP_HIER_FORWARD,
                 group_buf, G_rows, peer_buf, N, ws), record)
+        if hier:
             if two_level:
                 timed("combine", lambda: ep.ep_combine_two_level(
                     shape, L, tokens["topk_idx"], peer_buf, N, stride, ep.EP_FMT_CHUNKED, e,
@@ -313,11 +383,18 @@ def main():
             used.append(i)
         run_step(i, epoch[0], record if events is None else events)
 
+    def check_errors(when):
+        # the word kept since the last clear: an error in any step counts, not
+        # only in the last step's pass
+        bits = ep.ep_check_sticky_errors(ws)
+        if bits != 0:
+            raise RuntimeError(f"device error bits {bits} set during {when}")
+
+    ep.ep_clear_errors(ws)
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    if ep.ep_check_errors(ws) != 0:
-        raise RuntimeError("device error bits set during warm-up")
+    check_errors("warm-up")
 
     def timed_region(body):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -337,26 +414,38 @@ def main():
     # the runtime stalls between launches, which the events would then time.
     ms_eager, wall_eager = timed_region(lambda k: step(True, k < EVENT_STEPS))
     avg_ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
-    if ep.ep_check_errors(ws) != 0:
-        raise RuntimeError("device error bits set during the timed steps")
+    check_errors("the eager steps")
 
     ms_total, wall = ms_eager, wall_eager
     graph_used = not args.eager
-    if graph_used:
-        # One HIP graph per batch holding the whole step (its launches only:
-        # no memset or host work). Batch i's graph writes flag epoch 1000 + i,
-        # so consecutive replays (different batches) never share an epoch.
+    launch = "eager"
+    if graph_used and args.steps <= GRAPH_MAX_STEPS:
+        # One graph holding exactly the K timed steps (their launches only:
+        # no memset or host work), batches in rotation; step k writes flag
+        # epoch 1000 + k, so consecutive steps never share an epoch.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(args.steps):
+                run_step(k % n_batches, 1000 + k, False)
+        g.replay()  # untimed: first replay
+        torch.cuda.synchronize()
+        used.clear()
+        used.extend(k % n_batches for k in range(args.steps))
+        ms_total, wall = timed_region(lambda k: g.replay() if k == 0 else None)
+        launch = f"one hip graph holding the {args.steps} timed steps"
+        check_errors("the graph replay")
+    elif graph_used:
+        # One graph per batch holding its whole step, and one holding a whole
+        # cycle (the step of every batch in order), so that one graph launch
+        # serves n_batches steps. The timed steps replay the cycle K //
+        # n_batches times, then the single-step graphs of the first K %
+        # n_batches batches. Batch i's graphs write flag epoch 1000 + i.
         graphs = []
         for i in range(n_batches):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 run_step(i, 1000 + i, False)
             graphs.append(g)
-        # One more graph holding a whole cycle: the steps of every batch in
-        # order, so that one graph launch serves n_batches steps. The timed
-        # steps replay it K // n_batches times, then the single-step graphs of
-        # the first K % n_batches batches. Only for short cycles (the tiny
-        # workload rotates thousands of batches to keep x out of the MALL).
         use_cycle = n_batches <= 64 and args.steps >= n_batches
         if use_cycle:
             cycle = torch.cuda.CUDAGraph()
@@ -380,8 +469,9 @@ def main():
                 cycle.replay()
 
         ms_total, wall = timed_region(replay)
-        if ep.ep_check_errors(ws) != 0:
-            raise RuntimeError("device error bits set during the graph replays")
+        launch = ("hip graphs: one per cycle of the input batches (one step per batch), single-step "
+                  "graphs for the remainder" if use_cycle else "hip graph per step")
+        check_errors("the graph replays")
     ms_step = ms_total / args.steps
 
     # Algorithmic bytes per launch: what the method must move, from the byte
@@ -396,17 +486,17 @@ def main():
     N = sum(Ns[i] for i in used) / len(used)
     G_rows = sum(Gs[i] for i in used) / len(used)
     if multi:
-        rec = ep.ep_chunked_record_bytes(shape, seg)
+        rec_b = ep.ep_chunked_record_bytes(shape, seg)
         hid = 512 * ((2 * H + 479) // 480)
         bytes_layout = T * K * 8 + T * K * 4
         by = {"layout": bytes_layout,
-              "send": T * row + route + N * rec,
-              "epilogue": N * rec + N * (row + meta),
+              "send": T * row + route + N * rec_b,
+              "epilogue": N * rec_b + N * (row + meta),
               "combine": N * hid + T * 2 * H + T * K * 8}
     elif hier:
-        rec = ep.ep_chunked_record_bytes(shape, seg)
+        rec_b = ep.ep_chunked_record_bytes(shape, seg)
         hid = 512 * ((2 * H + 479) // 480)
-        bytes_main = T * row + route + T * K * 4 + 2 * G_rows * rec + N * rec
+        bytes_main = T * row + route + T * K * 4 + 2 * G_rows * rec_b + N * rec_b
         bytes_combine = N * hid + T * 2 * H + T * K * 8
         if two_level:  # partial rows written, then read back
             bytes_combine += 2 * G_rows * hid + T * K * 8
@@ -418,36 +508,31 @@ def main():
     step_bytes = sum(by.values())
     kernel_of = {"layout": "layout_*", "dispatch": "dispatch_kernel", "send": "scaleout_kernel",
                  "epilogue": "copy_epilogue_kernel",
-                 "hier": "scaleout_kernel+forward_kernel",
+                 "hier": "fused_hier_kernel" if fused else "scaleout_kernel+forward_kernel",
                  "combine": "combine_group_kernel+combine_cross_kernel" if two_level else "combine_kernel"}
     dom = max(names[1:], key=lambda n: avg_ms[n])
     achieved = by[dom] / (avg_ms[dom] * 1e-3) / 1e9
-    traffic = committed_traffic(w.name + ("_fp8" if fp8 else "") + ("_expand" if expand else "") +
-                                ("_2lc" if two_level else "") + (f"_s{S}" if multi else ""),
-                                kernel_of[dom])
+    label = w.name + ("_fp8" if fp8 else "") + ("_expand" if expand else "") + \
+        ("_fused" if fused else "") + ("_2lc" if two_level else "") + (f"_s{S}" if multi else "")
+    traffic = committed_traffic(label, kernel_of[dom])
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
     cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, inp, fp8, hier, args.cpu_seconds, expand, S if multi else 0)
+    if cpu_seconds > 0:
+        cpu = cpu_baseline(w, inp, fp8, hier, cpu_seconds, expand, S if multi else 0)
 
-    rec = {
-        "metric": METRIC,
+    return {
         "value": T * args.steps / (ms_total * 1e-3),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_step,
         "ms_per_step_eager": ms_eager / args.steps,
-        "launch": ("hip graphs: one per cycle of the input batches (one step per batch), single-step "
-                   "graphs for the remainder" if graph_used and use_cycle else
-                   "hip graph per step" if graph_used else "eager"),
+        "launch": launch,
         "wall_s": wall,
         "higher_is_better": True,
         "scaling": "weak",
@@ -455,10 +540,10 @@ def main():
         "dtype": "f32",
         "payload_dtype": "bf16" + ("+fp8e4m3" if fp8 else ""),
         "data": "synthetic (seeded; see synth/__init__.py)",
-        "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": w.E,
+        "config": {"workload": label, "tokens": T, "hidden": H, "experts": w.E,
                    "ranks": R, "groups": w.G, "topk": K, "routing": w.routing,
                    "receive_rows": N, "fp8_payload": fp8, "expand_rows": expand,
-                   "two_level_combine": two_level,
+                   "two_level_combine": two_level, "fused_two_level_dispatch": fused,
                    "sources": S if multi else None,
                    "region_capacity": cap if multi else None,
                    "input_batches": n_batches,
@@ -472,7 +557,6 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec), flush=True)
 
 
 def cpu_baseline(w, inp, fp8, hier, budget_s, expand=False, sources=0):

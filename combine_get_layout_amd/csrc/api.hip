@@ -23,6 +23,8 @@ WsLayout ws_layout(const ep_shape& s) {
     off += align256(sizeof(int32_t) * (size_t)w.nb * w.wrow);
     w.part_expert = off;
     off += align256(sizeof(int32_t) * (size_t)w.nb * s.E);
+    w.fused = off;
+    off += align256(sizeof(uint32_t) * (kFusedCounters + (size_t)(s.T + kFusedMinTile - 1) / kFusedMinTile));
     w.total = off;
     return w;
 }
@@ -176,6 +178,36 @@ int ep_hierarchical_dispatch(const ep_shape* shape, const ep_layout* layout,
     return hip_status(launch_hier(*shape, *layout, *tokens, epoch, steps, group_buf, group_cap,
                                   peer_buf, peer_cap, static_cast<char*>(ws),
                                   static_cast<hipStream_t>(stream)));
+}
+
+int ep_hierarchical_dispatch_fused(const ep_shape* shape, const ep_layout* layout,
+                                   const ep_tokens* tokens, uint32_t epoch, void* group_buf,
+                                   int64_t group_cap, void* peer_buf, int64_t peer_cap,
+                                   const ep_fused_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(shape);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_ws(shape, ws, ws_bytes)) != EP_OK) return rc;
+    if (!layout || !tokens || epoch == 0 || group_cap < 0 || peer_cap < 0) return EP_ERR_ARG;
+    if (shape->T > 0 &&
+        (!tokens->x || !tokens->topk_idx || !tokens->topk_weights || !layout->group_slot ||
+         !layout->slot || (group_cap > 0 && !group_buf) || (peer_cap > 0 && !peer_buf)))
+        return EP_ERR_ARG;
+    if (tokens->x_fp8 && shape->H % 16 != 0) return EP_ERR_ARG;
+    if (tokens->x_scales && shape->H % 128 != 0) return EP_ERR_ARG;
+    if (!aligned(tokens->x, 16) || !aligned(tokens->x_fp8, 16) || !aligned(tokens->x_scales, 4) ||
+        !aligned(tokens->topk_idx, 8) || !aligned(tokens->topk_weights, 4) ||
+        !aligned(group_buf, 16) || !aligned(peer_buf, 16) || !aligned(layout->slot, 4) ||
+        !aligned(layout->group_slot, 4))
+        return EP_ERR_ARG;
+    ep_fused_opts o = {0, 0, 0, 0};
+    if (opts) o = *opts;
+    const int tile = o.tile_tokens ? o.tile_tokens : 64;
+    if (tile < kFusedMinTile || tile > 4096 || (o.test_flags & ~EP_FUSED_WITHHOLD)) return EP_ERR_ARG;
+    const uint32_t timeout = o.timeout_us ? o.timeout_us : 100000u;
+    const int withhold = (o.test_flags & EP_FUSED_WITHHOLD) ? o.withhold_batch : -1;
+    return hip_status(launch_hier_fused(*shape, *layout, *tokens, epoch, group_buf, group_cap, peer_buf,
+                                        peer_cap, tile, timeout, withhold, static_cast<char*>(ws),
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int ep_combine(const ep_shape* shape, const ep_layout* layout, const void* y, int64_t y_rows,

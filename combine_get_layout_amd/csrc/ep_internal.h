@@ -12,6 +12,8 @@
 namespace ep {
 
 constexpr int kLayoutTokens = 256;  // tokens per layout workgroup (one per thread)
+constexpr int kFusedMinTile = 16;   // smallest batch of the fused two-level dispatch
+constexpr int kFusedCounters = 64;  // u32 words before the batch flags (two used)
 
 // Workspace carve-up (byte offsets from the workspace base).
 struct WsLayout {
@@ -24,6 +26,8 @@ struct WsLayout {
                             // [0, R)), valid lanes per rank ([rp, rp + R)) and
                             // deduplicated tokens per group ([2 rp, 2 rp + G))
     size_t part_expert;     // int32 [nb][E] lanes per expert
+    size_t fused;           // fused two-level dispatch: u32 [kFusedCounters] work counters,
+                            // then u32 [ceil(T / kFusedMinTile)] batch flags
     size_t total;
 };
 WsLayout ws_layout(const ep_shape& s);
@@ -56,6 +60,10 @@ hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_token
 hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
                        uint32_t epoch, int steps, void* group_buf, int64_t group_cap,
                        void* peer_buf, int64_t peer_cap, char* ws, hipStream_t st);
+hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
+                             uint32_t epoch, void* group_buf, int64_t group_cap, void* peer_buf,
+                             int64_t peer_cap, int tile, uint32_t timeout_us, int withhold, char* ws,
+                             hipStream_t st);
 hipError_t launch_combine(const ep_shape& s, const ep_layout& L, const void* y, int64_t y_rows,
                           int64_t y_stride, int fmt, uint32_t epoch, const float* w,
                           uint16_t* out, char* ws, hipStream_t st);

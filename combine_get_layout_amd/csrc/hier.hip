@@ -23,6 +23,9 @@
 //           from the record, then stream the row to each scale-up peer's row.
 // Step 1 also serves several source ranks on one GPU: given one staging row
 // per (token, destination rank) instead of per group, it is their send.
+#include <algorithm>
+#include <mutex>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -91,11 +94,10 @@ __device__ __forceinline__ u32x4 meta_vector(const HierArgs& a, int t, int q) {
     return v;
 }
 
-__global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
+// Scale-out write of wave-slice `part` (of kSoSplit) of token t's chunked
+// record to each destination group's row.
+__device__ __forceinline__ void scaleout_token(const HierArgs& a, int t, int part) {
     const int lane = lane_id();
-    const int gw = blockIdx.x * kWavesPerBlock + wave_in_block();
-    const int t = gw / kSoSplit, part = gw % kSoSplit;
-    if (t >= a.T) return;
     int gs = -1;
     if (lane < a.K) gs = a.group_slot[(int64_t)t * a.K + lane];
     bool first = gs >= 0;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
         if (j < lane && sj == gs) first = false;
     }
     const bool over = first && gs >= a.group_cap;
-    if (over) report(a.err, EP_DEVERR_CAPACITY);
+    if (over && part == 0) report(a.err, EP_DEVERR_CAPACITY);
     const uint64_t dest = __ballot(first && !over);
     if (!dest) return;
 
@@ -155,102 +157,258 @@ __global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
     }
 }
 
+__global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
+    const int gw = blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int t = gw / kSoSplit, part = gw % kSoSplit;
+    if (t >= a.T) return;
+    scaleout_token(a, t, part);
+}
+
 // Address of record byte b (4-byte aligned, never straddling a block) in a
 // chunked row.
 __device__ __forceinline__ const uint8_t* record_byte(const uint8_t* row, int64_t b) {
     return row + (b / kChunkPayload) * kChunkBytes + b % kChunkPayload;
 }
 
-__global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
-    __shared__ int32_t goff[EP_MAX_GROUPS + 1];
-    for (int i = threadIdx.x; i <= a.G; i += kBlockThreads) goff[i] = a.group_offsets[i];
-    __syncthreads();
+// Forward of group row n (of group g) to each of its scale-up peers: the
+// whole record is loaded together with src and this lane's expert id (its
+// flag lanes load the flags); every block's flag must equal epoch, else the
+// row is dropped with EP_DEVERR_FLAG. Destinations: the first lane of each
+// distinct rank of group g among the record's ids, at the layout's slot of
+// (src, lane).
+__device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g) {
     const int lane = lane_id();
-    const int64_t n_rows = min((int64_t)goff[a.G], a.group_cap);
     const int nchunks = a.geom.nchunks;
     const int iters = (nchunks + 1) / 2;
     const int64_t stride = a.geom.stride;
     const int64_t off_idx = (int64_t)a.geom.q_idx * 16;
     const int64_t off_src = (int64_t)a.geom.q_src * 16;
     const int c_half = lane >> 5, wv = lane & 31;
-    const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerBlock;
     const bool one_piece = iters <= kPieceIters;
+    const uint8_t* src_row = a.group_buf + n * stride;
+    u32x4 v[kPieceIters];
+    if (one_piece) {
+#pragma unroll
+        for (int j = 0; j < kPieceIters; ++j) {
+            const int c = min(2 * j + c_half, nchunks - 1);
+            v[j] = ld16(src_row + (int64_t)c * kChunkBytes + (int64_t)wv * 16);
+        }
+    }
+    const int32_t src = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_src));
+    const int32_t id = *reinterpret_cast<const int32_t*>(
+        record_byte(src_row, off_idx + 4 * min(lane, a.K - 1)));
+    bool ok = true;
+    if (one_piece) {
+#pragma unroll
+        for (int j = 0; j < kPieceIters; ++j) {
+            const bool is_flag = wv >= kChunkPayloadVecs && j < iters && 2 * j + c_half < nchunks;
+            const u32x4 f = v[j];
+            ok &= !is_flag || (f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch);
+        }
+    } else {
+        for (int i = lane; i < 2 * nchunks; i += kWave) {
+            const u32x4 f = ld16(src_row + (int64_t)(i >> 1) * kChunkBytes + kChunkPayload + (i & 1) * 16);
+            ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
+        }
+    }
+    if (__ballot(!ok) || src < 0 || src >= a.T) {
+        if (lane == 0) report(a.err, EP_DEVERR_FLAG);
+        return;
+    }
+    int32_t r = -1, d = -1;
+    if (lane < a.K && id >= 0 && id < a.E && (id / a.epr) / a.P == g) {
+        r = id / a.epr;
+        d = a.slot[(int64_t)src * a.K + lane];
+    }
+    bool first = r >= 0 && d >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int rj = readlane(r, j);
+        if (j < lane && rj == r) first = false;
+    }
+    const bool over = first && d >= a.peer_cap;
+    if (over) report(a.err, EP_DEVERR_CAPACITY);
+    const uint64_t dest = __ballot(first && !over);
+    if (!dest) return;
 
-    for (int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); n < n_rows;
-         n += wave_stride) {
-        const uint8_t* src_row = a.group_buf + n * stride;
-        // Issued together: the whole record (its flag lanes load the flags),
-        // the source index and this lane's expert id.
-        u32x4 v[kPieceIters];
-        if (one_piece) {
+    for (int it0 = 0; it0 < iters; it0 += kPieceIters) {
+        if (!one_piece) {
 #pragma unroll
             for (int j = 0; j < kPieceIters; ++j) {
-                const int c = min(2 * j + c_half, nchunks - 1);
-                v[j] = ld16(src_row + (int64_t)c * kChunkBytes + (int64_t)wv * 16);
+                const int c = 2 * (it0 + j) + c_half;
+                if (it0 + j < iters && c < nchunks) v[j] = ld16(src_row + chunk_lane_offset(it0 + j, lane));
             }
         }
-        const int32_t src = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_src));
-        const int32_t id = *reinterpret_cast<const int32_t*>(
-            record_byte(src_row, off_idx + 4 * min(lane, a.K - 1)));
-        // The row's group: the number of groups g >= 1 whose region starts at
-        // or before n (empty groups have equal starts).
+        for (uint64_t m = dest; m; m &= m - 1) {
+            const int k = __ffsll((unsigned long long)m) - 1;
+            uint8_t* row = a.peer_buf + (int64_t)readlane(d, k) * stride;
+#pragma unroll
+            for (int j = 0; j < kPieceIters; ++j) {
+                const int c = 2 * (it0 + j) + c_half;
+                if (it0 + j < iters && c < nchunks)
+                    st16_stream(row + chunk_lane_offset(it0 + j, lane), v[j]);
+            }
+        }
+    }
+}
+
+// One wave per group-region row, grid-stride; the row count is read on the
+// device. The row's group is the number of groups g >= 1 whose region starts
+// at or before n (empty groups have equal starts).
+__global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
+    __shared__ int32_t goff[EP_MAX_GROUPS + 1];
+    for (int i = threadIdx.x; i <= a.G; i += kBlockThreads) goff[i] = a.group_offsets[i];
+    __syncthreads();
+    const int lane = lane_id();
+    const int64_t n_rows = min((int64_t)goff[a.G], a.group_cap);
+    const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); n < n_rows;
+         n += wave_stride) {
         int g = 0;
         for (int base = 1; base <= a.G; base += kWave) {
             const int j = base + lane;
             g += __popcll(__ballot(j <= a.G && goff[j] <= n));
         }
-        // Every block's flag must equal epoch.
-        bool ok = true;
-        if (one_piece) {
-#pragma unroll
-            for (int j = 0; j < kPieceIters; ++j) {
-                const bool is_flag = wv >= kChunkPayloadVecs && j < iters && 2 * j + c_half < nchunks;
-                const u32x4 f = v[j];
-                ok &= !is_flag || (f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch);
+        forward_row(a, n, g);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Both steps in one persistent launch, with one flag per batch of tokens
+// ("Ascend Send Ordering", 方案一: the payload of a batch is written without
+// ordering, then one ordered flag publishes the whole batch; Stage1 of the
+// hierarchical path the same; "07: DeepEP Intra/Inter-node 协调": forward
+// warps take records from the scale-out buffer as they arrive, waiting with
+// a time limit). Batch b = tokens [b*tile, (b+1)*tile).
+//   * Production: a workgroup takes the next batch from a counter, writes the
+//     scale-out records of its tokens (plain stores), then every wave makes
+//     them visible device-wide (release fence: L2 write-back, wait for the
+//     stores), and after a barrier one thread stores the batch's flag = epoch.
+//   * Forwarding: a workgroup takes the next batch to forward from a second
+//     counter, in batch order. While batches remain to be produced it takes
+//     one only if its flag is already published; once production is all
+//     handed out it takes the next one and waits for its flag (one thread
+//     polls; bounded by `timeout` clock ticks, after which the batch is
+//     skipped with EP_DEVERR_TIMEOUT). After the flag, every wave makes
+//     later loads see memory (acquire fence: L2 invalidate), and the group
+//     rows of the batch's tokens are forwarded as in step 2 (block flags
+//     checked, record's src and ids, the layout's slots).
+// A workgroup waits only for batches whose production another running
+// workgroup has already taken on, and production never waits, so every wait
+// ends even if the grid is not co-resident; the time limit covers the rest.
+// Counters and flags live in the workspace and are zeroed by a one-workgroup
+// kernel launched just before (stream ordered, no memset node).
+// ---------------------------------------------------------------------------
+struct FusedArgs {
+    HierArgs h;
+    int tile;               // tokens per batch
+    int nbatch;             // ceil(T / tile)
+    int withhold;           // batch whose flag is never published (-1: none)
+    uint64_t timeout;       // wall-clock ticks a batch wait may last
+    uint32_t* ctr;          // [0] next batch to produce, [1] next batch to forward
+    uint32_t* flags;        // [nbatch] epoch once batch b is written
+};
+
+__global__ void fused_reset_kernel(uint32_t* ctr, uint32_t* flags, int nbatch) {
+    if (threadIdx.x < 2) ctr[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < nbatch; i += blockDim.x) flags[i] = 0u;
+}
+
+__device__ __forceinline__ uint32_t flag_load(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) {
+    const HierArgs& a = f.h;
+    __shared__ int sh_job, sh_kind;  // kind: 0 produce, 1 forward (flag seen), 2 forward (wait), 3 done
+    __shared__ int sh_ok;
+    const int wave = wave_in_block();
+    const int lane = lane_id();
+    for (;;) {
+        if (threadIdx.x == 0) {
+            int kind = 3, job = 0;
+            // A published batch first, if one is waiting to be forwarded.
+            const uint32_t fb = flag_load(&f.ctr[1]);
+            if ((int)fb < f.nbatch && flag_load(&f.flags[fb]) == a.epoch) {
+                uint32_t want = fb;
+                if (__hip_atomic_compare_exchange_strong(&f.ctr[1], &want, fb + 1, __ATOMIC_RELAXED,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                    kind = 1;
+                    job = (int)fb;
+                }
             }
-        } else {
-            for (int i = lane; i < 2 * nchunks; i += kWave) {
-                const u32x4 f = ld16(src_row + (int64_t)(i >> 1) * kChunkBytes + kChunkPayload + (i & 1) * 16);
-                ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
+            if (kind == 3 && flag_load(&f.ctr[0]) < (uint32_t)f.nbatch) {
+                const uint32_t b = atomicAdd(&f.ctr[0], 1u);
+                if ((int)b < f.nbatch) {
+                    kind = 0;
+                    job = (int)b;
+                }
             }
+            if (kind == 3 && flag_load(&f.ctr[0]) >= (uint32_t)f.nbatch) {
+                const uint32_t b = atomicAdd(&f.ctr[1], 1u);
+                if ((int)b < f.nbatch) {
+                    kind = 2;
+                    job = (int)b;
+                }
+            }
+            sh_kind = kind;
+            sh_job = job;
         }
-        if (__ballot(!ok) || src < 0 || src >= a.T) {
-            if (lane == 0) report(a.err, EP_DEVERR_FLAG);
+        __syncthreads();
+        const int kind = sh_kind, job = sh_job;
+        __syncthreads();
+        if (kind == 3) return;
+        const int t0 = job * f.tile, t1 = min(a.T, t0 + f.tile);
+        if (kind == 0) {
+            // Wave w writes part w % kSoSplit of every kWavesPerBlock / kSoSplit-th token.
+            constexpr int kTokPerPass = kWavesPerBlock / kSoSplit;
+            for (int t = t0 + wave / kSoSplit; t < t1; t += kTokPerPass) scaleout_token(a, t, wave % kSoSplit);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __syncthreads();
+            if (threadIdx.x == 0 && job != f.withhold)
+                __hip_atomic_store(&f.flags[job], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             continue;
         }
-        // Destination peers: first lane of each distinct rank inside group g.
-        int32_t r = -1, d = -1;
-        if (lane < a.K && id >= 0 && id < a.E && (id / a.epr) / a.P == g) {
-            r = id / a.epr;
-            d = a.slot[(int64_t)src * a.K + lane];
-        }
-        bool first = r >= 0 && d >= 0;
-        for (int j = 0; j < a.K; ++j) {
-            const int rj = readlane(r, j);
-            if (j < lane && rj == r) first = false;
-        }
-        const bool over = first && d >= a.peer_cap;
-        if (over) report(a.err, EP_DEVERR_CAPACITY);
-        const uint64_t dest = __ballot(first && !over);
-        if (!dest) continue;
-
-        for (int it0 = 0; it0 < iters; it0 += kPieceIters) {
-            if (!one_piece) {
-#pragma unroll
-                for (int j = 0; j < kPieceIters; ++j) {
-                    const int c = 2 * (it0 + j) + c_half;
-                    if (it0 + j < iters && c < nchunks) v[j] = ld16(src_row + chunk_lane_offset(it0 + j, lane));
+        if (kind == 2) {
+            if (threadIdx.x == 0) {
+                const uint64_t start = (uint64_t)wall_clock64();
+                int ok = 0;
+                for (;;) {
+                    if (flag_load(&f.flags[job]) == a.epoch) {
+                        ok = 1;
+                        break;
+                    }
+                    if ((uint64_t)wall_clock64() - start > f.timeout) break;
+                    __builtin_amdgcn_s_sleep(8);
                 }
+                sh_ok = ok;
             }
-            for (uint64_t m = dest; m; m &= m - 1) {
+            __syncthreads();
+            const int ok = sh_ok;
+            __syncthreads();
+            if (!ok) {
+                if (threadIdx.x == 0) report(a.err, EP_DEVERR_TIMEOUT);
+                continue;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // Forward the group rows of the batch's tokens: wave w takes tokens
+        // t0 + w, t0 + w + kWavesPerBlock, ..., and each of its groups in
+        // ascending lane order (first lane of each group).
+        for (int t = t0 + wave; t < t1; t += kWavesPerBlock) {
+            int gs = -1, g = -1;
+            if (lane < a.K) {
+                gs = a.group_slot[(int64_t)t * a.K + lane];
+                const int64_t e = a.topk[(int64_t)t * a.K + lane];
+                if (gs >= 0 && expert_ok(e, a.E)) g = ((int)e / a.epr) / a.P;
+            }
+            bool first = gs >= 0 && g >= 0;
+            for (int j = 0; j < a.K; ++j) {
+                const int sj = readlane(gs, j);
+                if (j < lane && sj == gs) first = false;
+            }
+            for (uint64_t m = __ballot(first && gs < a.group_cap); m; m &= m - 1) {
                 const int k = __ffsll((unsigned long long)m) - 1;
-                uint8_t* row = a.peer_buf + (int64_t)readlane(d, k) * stride;
-#pragma unroll
-                for (int j = 0; j < kPieceIters; ++j) {
-                    const int c = 2 * (it0 + j) + c_half;
-                    if (it0 + j < iters && c < nchunks)
-                        st16_stream(row + chunk_lane_offset(it0 + j, lane), v[j]);
-                }
+                forward_row(a, readlane(gs, k), readlane(g, k));
             }
         }
     }
@@ -296,6 +454,71 @@ hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& t
         const int blocks = (int)(want < 8192 ? want : 8192);
         hipLaunchKernelGGL(forward_kernel, dim3(blocks), block, 0, st, a);
     }
+    return hipGetLastError();
+}
+
+// Per-device launch facts of the fused kernel (wall-clock rate in kHz, CUs,
+// resident workgroups per CU), queried on the first call on each device and
+// kept, so that later calls (also under stream capture) make no queries.
+struct FusedDeviceInfo {
+    int rate_khz, cus, per_cu;
+};
+
+static hipError_t fused_device_info(hipStream_t st, FusedDeviceInfo* out) {
+    constexpr int kMaxDev = 64;
+    static FusedDeviceInfo info[kMaxDev];
+    static bool known[kMaxDev];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!known[dev]) {
+        FusedDeviceInfo d = {0, 0, 0};
+        if ((e = hipDeviceGetAttribute(&d.rate_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
+            return e;
+        if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+            return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu, fused_hier_kernel, kBlockThreads, 0)) !=
+            hipSuccess)
+            return e;
+        info[dev] = d;
+        known[dev] = true;
+    }
+    *out = info[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
+                             uint32_t epoch, void* group_buf, int64_t group_cap, void* peer_buf,
+                             int64_t peer_cap, int tile, uint32_t timeout_us, int withhold, char* ws,
+                             hipStream_t st) {
+    if (s.T == 0) return hipSuccess;
+    const WsLayout W = ws_layout(s);
+    FusedArgs f;
+    f.h = hier_args(s, tk, epoch, ws);
+    f.h.slot = L.slot;
+    f.h.group_slot = L.group_slot;
+    f.h.group_offsets = L.group_offsets;
+    f.h.group_buf = reinterpret_cast<uint8_t*>(group_buf);
+    f.h.group_cap = group_cap;
+    f.h.peer_buf = reinterpret_cast<uint8_t*>(peer_buf);
+    f.h.peer_cap = peer_cap;
+    f.tile = tile;
+    f.nbatch = (s.T + tile - 1) / tile;
+    f.withhold = withhold;
+    f.ctr = reinterpret_cast<uint32_t*>(ws + W.fused);
+    f.flags = f.ctr + kFusedCounters;
+    FusedDeviceInfo d;
+    const hipError_t e = fused_device_info(st, &d);
+    if (e != hipSuccess) return e;
+    f.timeout = (uint64_t)timeout_us * (uint64_t)(d.rate_khz > 0 ? d.rate_khz : 100000) / 1000u;
+    // No more workgroups than are resident at once (more would find no work).
+    const int resident = std::max(1, d.cus * std::max(1, d.per_cu));
+    const int blocks = std::min(resident, std::max(1, 2 * f.nbatch));
+    hipLaunchKernelGGL(fused_reset_kernel, dim3(1), dim3(kBlockThreads), 0, st, f.ctr, f.flags, f.nbatch);
+    hipLaunchKernelGGL(fused_hier_kernel, dim3(blocks), dim3(kBlockThreads), 0, st, f);
     return hipGetLastError();
 }
 

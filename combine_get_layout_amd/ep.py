@@ -19,7 +19,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libep.so")
 
 EP_OK, EP_ERR_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP, EP_ERR_DEVICE = 0, -1, -2, -3, -4
-EP_DEVERR_EXPERT_ID, EP_DEVERR_CAPACITY, EP_DEVERR_FLAG = 1, 2, 4
+EP_DEVERR_EXPERT_ID, EP_DEVERR_CAPACITY, EP_DEVERR_FLAG, EP_DEVERR_TIMEOUT = 1, 2, 4, 8
+EP_FUSED_WITHHOLD = 1
 EP_SEG_BF16, EP_SEG_FP8, EP_SEG_SCALES = 1, 2, 4
 EP_FMT_PLAIN, EP_FMT_CHUNKED = 0, 1
 EP_HIER_SCALEOUT, EP_HIER_FORWARD = 1, 2
@@ -49,13 +50,19 @@ class ep_recv(ctypes.Structure):
                                   "topk_weights")] + [("capacity", ctypes.c_int64)]
 
 
+class ep_fused_opts(ctypes.Structure):
+    _fields_ = [("tile_tokens", ctypes.c_int32), ("timeout_us", ctypes.c_uint32),
+                ("test_flags", ctypes.c_uint32), ("withhold_batch", ctypes.c_int32)]
+
+
 class ep_sources(ctypes.Structure):
     _fields_ = [("S", ctypes.c_int32), ("capacity", ctypes.c_int64), ("counts", _P),
                 ("recv_offsets", _P), ("src_slot", _P)]
 
 
 EXPORTS = ("ep_workspace_bytes", "ep_record_bytes", "ep_chunked_record_bytes", "ep_get_layout",
-           "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch", "ep_combine",
+           "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch",
+           "ep_hierarchical_dispatch_fused", "ep_combine",
            "ep_combine_expand", "ep_partial_row_bytes", "ep_combine_two_level",
            "ep_source_workspace_bytes", "ep_source_layout", "ep_source_dispatch",
            "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors", "ep_check_sticky_errors",
@@ -86,6 +93,8 @@ def lib() -> ctypes.CDLL:
     L.ep_dispatch_expand.argtypes = L.ep_dispatch.argtypes
     L.ep_hierarchical_dispatch.argtypes = [sp, lp, ctypes.POINTER(ep_tokens), u32, ctypes.c_int,
                                            _P, i64, _P, i64, _P, sz, _P]
+    L.ep_hierarchical_dispatch_fused.argtypes = [sp, lp, ctypes.POINTER(ep_tokens), u32, _P, i64, _P,
+                                                 i64, ctypes.POINTER(ep_fused_opts), _P, sz, _P]
     L.ep_combine.argtypes = [sp, lp, _P, i64, i64, ctypes.c_int, u32, _P, _P, _P, sz, _P]
     L.ep_combine_expand.argtypes = L.ep_combine.argtypes
     L.ep_partial_row_bytes.argtypes = [sp]
@@ -105,7 +114,7 @@ def lib() -> ctypes.CDLL:
     L.ep_status_string.argtypes = [ctypes.c_int]
     L.ep_status_string.restype = ctypes.c_char_p
     for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_expand",
-              "ep_hierarchical_dispatch",
+              "ep_hierarchical_dispatch", "ep_hierarchical_dispatch_fused",
               "ep_combine", "ep_combine_expand", "ep_combine_two_level", "ep_source_layout",
               "ep_source_dispatch", "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors",
               "ep_check_sticky_errors"):
@@ -235,6 +244,21 @@ def ep_hierarchical_dispatch(shape, layout: dict, tokens: dict, epoch: int, step
                                           _ptr(peer_buf, "peer_buf", max(int(peer_cap), 0) * stride),
                                           int(peer_cap), *_ws(ws), _stream(stream)),
            "ep_hierarchical_dispatch")
+
+
+def ep_hierarchical_dispatch_fused(shape, layout: dict, tokens: dict, epoch: int, group_buf,
+                                   group_cap: int, peer_buf, peer_cap: int, ws, tile: int = 0,
+                                   timeout_us: int = 0, withhold: int | None = None, stream=None):
+    L = _layout_struct(shape, layout)
+    tk = _tokens_struct(shape, tokens)
+    stride = max(ep_chunked_record_bytes(shape, _seg_of(tokens) or EP_SEG_BF16), 0)
+    opts = ep_fused_opts(int(tile), int(timeout_us), EP_FUSED_WITHHOLD if withhold is not None else 0,
+                         int(withhold) if withhold is not None else 0)
+    _check(lib().ep_hierarchical_dispatch_fused(
+        ctypes.byref(shape), ctypes.byref(L), ctypes.byref(tk), int(epoch),
+        _ptr(group_buf, "group_buf", max(int(group_cap), 0) * stride), int(group_cap),
+        _ptr(peer_buf, "peer_buf", max(int(peer_cap), 0) * stride), int(peer_cap),
+        ctypes.byref(opts), *_ws(ws), _stream(stream)), "ep_hierarchical_dispatch_fused")
 
 
 def _combine_args(shape, y, y_rows, y_row_stride, topk_weights, out):

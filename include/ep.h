@@ -56,6 +56,7 @@ extern "C" {
 #define EP_DEVERR_EXPERT_ID 1u  /* an expert id < -1 or >= E (treated as -1) */
 #define EP_DEVERR_CAPACITY 2u   /* a row index >= the given buffer capacity (not written / not read) */
 #define EP_DEVERR_FLAG 4u       /* a 512 B chunk flag != epoch (row dropped / skipped) */
+#define EP_DEVERR_TIMEOUT 8u    /* a bounded wait for a batch flag gave up (batch not forwarded) */
 
 /* Payload pieces present in a token record (ep_record_bytes). */
 #define EP_SEG_BF16 1
@@ -203,6 +204,40 @@ int ep_hierarchical_dispatch(const ep_shape *shape, const ep_layout *layout,
                              const ep_tokens *tokens, uint32_t epoch, int steps,
                              void *group_buf, int64_t group_cap, void *peer_buf,
                              int64_t peer_cap, void *ws, size_t ws_bytes, void *stream);
+
+/* Both two-level steps in one persistent launch, forwarders consuming each
+ * batch of records as soon as its flag is published ([ASC] 方案一 and the
+ * hierarchical Stage1: the batch's payload written without ordering, then
+ * one ordered flag per batch; [PIPE] forward warps: records taken from the
+ * scale-out buffer as they arrive, each wait bounded by a time limit).
+ * Batch b = tokens [b * tile, (b+1) * tile). A workgroup writing batch b's
+ * group rows (as step EP_HIER_SCALEOUT) makes them visible device-wide (a
+ * release fence per wave), then stores flag b = epoch; a workgroup
+ * forwarding batch b waits for that flag (at most timeout_us; then the
+ * batch's rows are not forwarded and EP_DEVERR_TIMEOUT is set), acquires,
+ * and forwards the group rows of the batch's tokens (as step
+ * EP_HIER_FORWARD, block flags checked). Batches are forwarded in order,
+ * each as soon as it is published while production is still running. The
+ * results are those of ep_hierarchical_dispatch with both steps, byte for
+ * byte. Same arguments and requirements as ep_hierarchical_dispatch with
+ * steps = 3; the workspace (ep_workspace_bytes) also holds the batch flags
+ * and work counters, which the call zeroes first with a small kernel (no
+ * memset), so calls on one workspace must not overlap. opts may be NULL
+ * (defaults); all-zero fields mean the defaults. */
+typedef struct ep_fused_opts {
+    int32_t tile_tokens;    /* tokens per batch, 16..4096 (0: 64) */
+    uint32_t timeout_us;    /* longest wait for one batch flag (0: 100000 us) */
+    uint32_t test_flags;    /* EP_FUSED_WITHHOLD: batch `withhold_batch`'s flag is never
+                               published, to test the bounded wait (its group rows are
+                               still written; it is not forwarded; EP_DEVERR_TIMEOUT) */
+    int32_t withhold_batch;
+} ep_fused_opts;
+#define EP_FUSED_WITHHOLD 1u
+int ep_hierarchical_dispatch_fused(const ep_shape *shape, const ep_layout *layout,
+                                   const ep_tokens *tokens, uint32_t epoch, void *group_buf,
+                                   int64_t group_cap, void *peer_buf, int64_t peer_cap,
+                                   const ep_fused_opts *opts, void *ws, size_t ws_bytes,
+                                   void *stream);
 
 /* Combine ([MEGA] combine write of BF16 expert outputs per (token, top-k);
  * [ASC] BF16 hidden with FP32 top-k weights): the inverse gather plus a
