@@ -121,6 +121,25 @@ int ep_get_layout(const ep_shape* shape, const int64_t* topk_idx, const ep_layou
                                     static_cast<hipStream_t>(stream)));
 }
 
+int ep_get_layout_noalloc(const ep_shape* shape, const int64_t* topk_idx, const ep_layout* layout,
+                          uint32_t* errors, void* stream) {
+    int rc = check_shape(shape);
+    if (rc != EP_OK) return rc;
+    if (ws_layout(*shape).total > (size_t)EP_LAYOUT_SCRATCH_BYTES) return EP_ERR_SCRATCH;
+    if (!layout || !errors || !aligned(errors, 4) || (shape->T > 0 && !topk_idx) || !aligned(topk_idx, 8))
+        return EP_ERR_ARG;
+    const ep_layout& L = *layout;
+    if (!aligned(L.is_token_in_rank, 16) || !aligned(L.is_token_in_group, 16)) return EP_ERR_ARG;
+    if (L.expert_slot && !L.expert_offsets) return EP_ERR_ARG;
+    const void* i32s[] = {L.tokens_per_expert, L.tokens_per_rank, L.tokens_per_group,
+                          L.expert_offsets, L.rank_offsets, L.group_offsets, L.slot,
+                          L.group_slot, L.expert_slot};
+    for (const void* p : i32s)
+        if (!aligned(p, 4)) return EP_ERR_ARG;
+    return hip_status(launch_layout_noalloc(*shape, topk_idx, L, errors,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int ep_dispatch(const ep_shape* shape, const ep_layout* layout, const ep_tokens* tokens,
                 const ep_recv* recv, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_shape(shape);
@@ -379,6 +398,9 @@ const char* ep_status_string(int status) {
         case EP_ERR_ARG: return "invalid argument (null or misaligned pointer, bad shape or size)";
         case EP_ERR_UNSUPPORTED: return "shape outside the supported limits";
         case EP_ERR_HIP: return "HIP runtime or launch error";
+        case EP_ERR_SCRATCH:
+            return "shape too large for the allocation-free call's static scratch "
+                   "(ep_workspace_bytes(shape) > EP_LAYOUT_SCRATCH_BYTES); use ep_get_layout";
         case EP_ERR_DEVICE:
             return "device-detected error: bad expert id, capacity exceeded or flag/epoch mismatch "
                    "(the bits are in the workspace error word)";

@@ -55,6 +55,11 @@ RecordGeom record_geom(const ep_shape& s, int seg_flags);
 
 hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout& L, char* ws,
                          hipStream_t st);
+// The allocation-free variant: count tables in the library's per-device
+// scratch array (needs ws_layout(s).total <= EP_LAYOUT_SCRATCH_BYTES), error
+// words at `err`.
+hipError_t launch_layout_noalloc(const ep_shape& s, const int64_t* topk, const ep_layout& L,
+                                 uint32_t* err, hipStream_t st);
 hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
                            const ep_recv& rv, char* ws, hipStream_t st);
 hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,

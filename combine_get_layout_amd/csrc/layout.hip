@@ -33,6 +33,7 @@
 // Workgroups never wait for each other and no grid-wide fence is needed (the
 // launch boundaries order the kernels).
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include <rocprim/block/block_radix_sort.hpp>
@@ -876,6 +877,56 @@ static hipError_t launch_layout_tables(const ep_shape& s, const int64_t* topk, c
 hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout& L, char* ws,
                          hipStream_t st) {
     return launch_layout_tables(s, topk, L, reinterpret_cast<uint32_t*>(ws + ws_layout(s).err), ws, st);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free layout: the count tables in a file-scope device array
+// instead of the caller's workspace. Each GPU the library runs on holds its
+// own copy of the array until the process ends; every call on that GPU uses
+// it, so calls that overlap on one GPU race. In host code `scratch` names a
+// host-side stand-in, not a device address: the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current
+// and kept in scratch_addr[]. Only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[EP_LAYOUT_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+char* scratch_addr[kMaxDevices];
+std::mutex scratch_mutex;
+
+// Device address of `scratch` on device `dev`, looked up on first use.
+hipError_t scratch_on(int dev, char** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_addr[dev]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_addr[dev] = static_cast<char*>(p);
+    }
+    *out = scratch_addr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_layout_noalloc(const ep_shape& s, const int64_t* topk, const ep_layout& L,
+                                 uint32_t* err, hipStream_t st) {
+    int dev = -1;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    char* tables = nullptr;
+    if ((e = scratch_on(dev, &tables)) != hipSuccess) return e;
+    return launch_layout_tables(s, topk, L, err, tables, st);
 }
 
 }  // namespace ep

@@ -18,7 +18,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libep.so")
 
-EP_OK, EP_ERR_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP, EP_ERR_DEVICE = 0, -1, -2, -3, -4
+EP_OK, EP_ERR_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP, EP_ERR_DEVICE, EP_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+EP_LAYOUT_SCRATCH_BYTES = 4 << 20
 EP_DEVERR_EXPERT_ID, EP_DEVERR_CAPACITY, EP_DEVERR_FLAG, EP_DEVERR_TIMEOUT = 1, 2, 4, 8
 EP_FUSED_WITHHOLD = 1
 EP_SEG_BF16, EP_SEG_FP8, EP_SEG_SCALES = 1, 2, 4
@@ -61,6 +62,7 @@ class ep_sources(ctypes.Structure):
 
 
 EXPORTS = ("ep_workspace_bytes", "ep_record_bytes", "ep_chunked_record_bytes", "ep_get_layout",
+           "ep_get_layout_noalloc",
            "ep_dispatch", "ep_dispatch_expand", "ep_hierarchical_dispatch",
            "ep_hierarchical_dispatch_fused", "ep_combine",
            "ep_combine_expand", "ep_partial_row_bytes", "ep_combine_two_level",
@@ -89,6 +91,7 @@ def lib() -> ctypes.CDLL:
     L.ep_chunked_record_bytes.argtypes = [sp, ctypes.c_int]
     L.ep_chunked_record_bytes.restype = i64
     L.ep_get_layout.argtypes = [sp, _P, lp, _P, sz, _P]
+    L.ep_get_layout_noalloc.argtypes = [sp, _P, lp, _P, _P]
     L.ep_dispatch.argtypes = [sp, lp, ctypes.POINTER(ep_tokens), ctypes.POINTER(ep_recv), _P, sz, _P]
     L.ep_dispatch_expand.argtypes = L.ep_dispatch.argtypes
     L.ep_hierarchical_dispatch.argtypes = [sp, lp, ctypes.POINTER(ep_tokens), u32, ctypes.c_int,
@@ -113,7 +116,7 @@ def lib() -> ctypes.CDLL:
     L.ep_check_sticky_errors.argtypes = [_P, _P, ctypes.POINTER(u32)]
     L.ep_status_string.argtypes = [ctypes.c_int]
     L.ep_status_string.restype = ctypes.c_char_p
-    for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_expand",
+    for f in ("ep_get_layout", "ep_get_layout_noalloc", "ep_dispatch", "ep_dispatch_expand",
               "ep_hierarchical_dispatch", "ep_hierarchical_dispatch_fused",
               "ep_combine", "ep_combine_expand", "ep_combine_two_level", "ep_source_layout",
               "ep_source_dispatch", "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors",
@@ -214,6 +217,16 @@ def ep_get_layout(shape, topk_idx, layout: dict, ws, stream=None):
     L = _layout_struct(shape, layout)
     _check(lib().ep_get_layout(ctypes.byref(shape), _ptr(topk_idx, "topk_idx", 8 * shape.T * shape.K),
                                ctypes.byref(L), *_ws(ws), _stream(stream)), "ep_get_layout")
+
+
+def ep_get_layout_noalloc(shape, topk_idx, layout: dict, errors, stream=None):
+    """errors: a GPU tensor of at least 8 bytes (two u32 error words), e.g. a
+    workspace."""
+    L = _layout_struct(shape, layout)
+    _check(lib().ep_get_layout_noalloc(ctypes.byref(shape),
+                                       _ptr(topk_idx, "topk_idx", 8 * shape.T * shape.K),
+                                       ctypes.byref(L), _ptr(errors, "errors", 8), _stream(stream)),
+           "ep_get_layout_noalloc")
 
 
 def ep_dispatch(shape, layout: dict, tokens: dict, recv: dict, capacity: int, ws, stream=None):

@@ -51,6 +51,8 @@ extern "C" {
 #define EP_ERR_DEVICE (-4)      /* the device reported an error: ep_check_errors /
                                    ep_check_sticky_errors return it when error bits are
                                    set and write the bits (EP_DEVERR_*) to *bits */
+#define EP_ERR_SCRATCH (-5)     /* ep_get_layout_noalloc: the shape's count tables do not
+                                   fit the static scratch (EP_LAYOUT_SCRATCH_BYTES) */
 
 /* Device error bits (workspace error words). */
 #define EP_DEVERR_EXPERT_ID 1u  /* an expert id < -1 or >= E (treated as -1) */
@@ -156,6 +158,26 @@ int64_t ep_chunked_record_bytes(const ep_shape *shape, int seg_flags);
  * aligned. */
 int ep_get_layout(const ep_shape *shape, const int64_t *topk_idx, const ep_layout *layout,
                   void *ws, size_t ws_bytes, void *stream);
+
+/* Allocation-free layout, for callers that cannot allocate device memory at
+ * call time (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): ep_get_layout with the same outputs, bit for bit,
+ * but its per-workgroup count tables live in a static device array of
+ * EP_LAYOUT_SCRATCH_BYTES inside the library instead of a workspace. Each GPU
+ * the library runs on holds one such array until the process ends (its
+ * address is looked up on the first call on that GPU); every call on a GPU
+ * shares it, so calls that overlap on one GPU (several streams, several host
+ * threads) race and must be serialised by the caller. The call allocates and
+ * frees nothing. Limit: ep_workspace_bytes(shape) <= EP_LAYOUT_SCRATCH_BYTES
+ * (4 MiB: e.g. 262,144 tokens with E = 256 and R = 64, or 16,384 tokens with
+ * E = 2048 and R = 256), else EP_ERR_SCRATCH and nothing is enqueued.
+ * errors: device pointer to two u32 error words with the meaning of the
+ * workspace's (word 0 cleared by this call, then EP_DEVERR_EXPERT_ID set for
+ * invalid ids in both); passing a workspace's base makes ep_check_errors on
+ * that workspace read them. Other arguments and checks as ep_get_layout. */
+#define EP_LAYOUT_SCRATCH_BYTES (4u << 20)
+int ep_get_layout_noalloc(const ep_shape *shape, const int64_t *topk_idx, const ep_layout *layout,
+                          uint32_t *errors, void *stream);
 
 /* Expand-mode rows ([V2] §3.3 阶段3: the copy epilogue with expand, where a
  * received token gets one row per chosen expert, grouped by expert for the

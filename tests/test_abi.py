@@ -86,6 +86,12 @@ def test_null_and_misaligned_arguments_rejected_before_launch(lib):
     assert lib.ep_clear_errors(None, None) == ep.EP_ERR_ARG
     assert lib.ep_check_errors(None, None, None) == ep.EP_ERR_ARG
     assert lib.ep_check_sticky_errors(None, None, None) == ep.EP_ERR_ARG
+    # the allocation-free layout refuses, before any launch, a shape whose
+    # count tables exceed its static scratch array
+    big = ep.make_shape(1 << 20, 7168, 8, 256, 64, 1)
+    assert ep.ep_workspace_bytes(big) > ep.EP_LAYOUT_SCRATCH_BYTES
+    assert lib.ep_get_layout_noalloc(ctypes.byref(big), 0x1000, ctypes.byref(L), 0x2000, None) == ep.EP_ERR_SCRATCH
+    assert lib.ep_get_layout_noalloc(ctypes.byref(s), 0x1000, ctypes.byref(L), None, None) == ep.EP_ERR_ARG
     assert ep.EP_ERR_DEVICE == -4 and "device" in ep.ep_status_string(ep.EP_ERR_DEVICE)
     assert ep.ep_status_string(0) == "ok"
 
