@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=None,
-                   choices=["tiny", "ep32", "ep256", "zipf", "hier8x8"],
+                   choices=["tiny", "ep32", "ep256", "zipf", "hier8x8", "many"],
                    help="time only this workload (default: every target configuration, ep32 first)")
     p.add_argument("--fp8", action="store_true", help="also move the FP8 payload + scales")
     p.add_argument("--fused", action="store_true",

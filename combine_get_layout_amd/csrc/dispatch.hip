@@ -17,6 +17,8 @@
 // are the lanes k whose slot differs from every earlier lane's (the rank
 // deduplication), found with one ballot. The first slice's wave also writes
 // the scales and the metadata.
+#include <algorithm>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -38,6 +40,12 @@
 #endif
 #ifndef EP_DSP_SPLIT
 #define EP_DSP_SPLIT 4      // waves per token: the row is cut into this many column slices
+#endif
+#ifndef EP_DSP_PERSIST
+#define EP_DSP_PERSIST 0    // persistent, software-pipelined kernel (experiment)
+#endif
+#ifndef EP_DSP_PERSIST_BPC
+#define EP_DSP_PERSIST_BPC 64  // most workgroups per CU of the persistent grid
 #endif
 
 namespace ep {
@@ -173,6 +181,150 @@ __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(Disp
     }
 }
 
+// Persistent form: a grid of at most the resident waves; wave w takes the
+// items (token, slice) w, w + W, w + 2W, ... (W = waves in the grid) and
+// issues the next item's slot and row-slice loads before the current item's
+// stores, so that a wave's loads are in flight while its stores drain.
+// Needs the widest slice to fit in one pass (NV vectors per lane).
+struct Item {
+    int t, part;
+    int s;        // slot of lane k < K
+    int64_t e;    // expert id of lane k
+    float wk;     // weight of lane k
+};
+
+template <int NV>
+__device__ __forceinline__ void load_item(const DispatchArgs& a, int item, Item& it, u32x4 (&v)[NV],
+                                          u32x4 (&f)[NV]) {
+    const int lane = lane_id();
+    it.t = item / EP_DSP_SPLIT;
+    it.part = item % EP_DSP_SPLIT;
+    it.s = -1;
+    it.e = -1;
+    it.wk = 0.f;
+    if (lane < a.K) {
+        it.s = a.slot[(int64_t)it.t * a.K + lane];
+        it.e = a.topk[(int64_t)it.t * a.K + lane];
+        if (a.topk_w) it.wk = a.topk_w[(int64_t)it.t * a.K + lane];
+    }
+    if (a.x && a.rx) {
+        const int64_t row_bytes = (int64_t)a.H * 2;
+        const int nvec_all = (int)(row_bytes / 16);
+        const int per = slice_vecs(nvec_all);
+        const int v0 = min(nvec_all, it.part * per), v1 = min(nvec_all, v0 + per);
+        const uint8_t* src = a.x + (int64_t)it.t * row_bytes;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int i = v0 + j * kWave + lane;
+            v[j] = ld_src(src + (int64_t)min(i, max(v1 - 1, 0)) * 16);
+        }
+    }
+    if (a.x_fp8 && a.rfp8) {
+        const int64_t row_bytes = a.H;
+        const int nvec_all = (int)(row_bytes / 16);
+        const int per = slice_vecs(nvec_all);
+        const int v0 = min(nvec_all, it.part * per), v1 = min(nvec_all, v0 + per);
+        const uint8_t* src = a.x_fp8 + (int64_t)it.t * row_bytes;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int i = v0 + j * kWave + lane;
+            f[j] = ld_src(src + (int64_t)min(i, max(v1 - 1, 0)) * 16);
+        }
+    }
+}
+
+template <int NV>
+__device__ __forceinline__ void store_slice(const u32x4 (&v)[NV], int64_t row_bytes, uint8_t* dst,
+                                            uint64_t dest, int slot, int part) {
+    const int lane = lane_id();
+    const int nvec_all = (int)(row_bytes / 16);
+    const int per = slice_vecs(nvec_all);
+    const int v0 = min(nvec_all, part * per), v1 = min(nvec_all, v0 + per);
+    for (uint64_t m = dest; m; m &= m - 1) {
+        const int k = __ffsll((unsigned long long)m) - 1;
+        uint8_t* row = dst + (int64_t)readlane(slot, k) * row_bytes;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int i = v0 + j * kWave + lane;
+            if (i < v1) st_dst(row + (int64_t)i * 16, v[j]);
+        }
+    }
+}
+
+template <int NV>
+__device__ __forceinline__ void store_item(const DispatchArgs& a, const Item& it, const u32x4 (&v)[NV],
+                                           const u32x4 (&f)[NV]) {
+    const int lane = lane_id();
+    bool first = it.s >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int sj = readlane(it.s, j);
+        if (j < lane && sj == it.s) first = false;
+    }
+    const bool over = first && it.s >= a.cap;
+    if (over && it.part == 0) report(a.err, EP_DEVERR_CAPACITY);
+    const uint64_t dest = __ballot(first && !over);
+    if (!dest) return;
+    if (a.x && a.rx) store_slice<NV>(v, (int64_t)a.H * 2, a.rx, dest, it.s, it.part);
+    if (a.x_fp8 && a.rfp8) store_slice<NV>(f, a.H, a.rfp8, dest, it.s, it.part);
+    if (it.part != 0) return;
+    if (a.x_scales && a.rscales) {
+        const int ns = a.H / 128;
+        for (int base = 0; base < ns; base += kWave) {
+            const int i = base + lane;
+            const float sv = i < ns ? a.x_scales[(int64_t)it.t * ns + i] : 0.f;
+            for (uint64_t m = dest; m; m &= m - 1) {
+                const int k = __ffsll((unsigned long long)m) - 1;
+                if (i < ns) a.rscales[(int64_t)readlane(it.s, k) * ns + i] = sv;
+            }
+        }
+    }
+    const int32_t id = expert_ok(it.e, a.E) ? (int32_t)it.e : -1;
+    for (uint64_t m = dest; m; m &= m - 1) {
+        const int k = __ffsll((unsigned long long)m) - 1;
+        const int64_t row = readlane(it.s, k);
+        if (a.rsrc && lane == 0) a.rsrc[row] = it.t;
+        if (lane < a.K) {
+            if (a.ridx) a.ridx[row * a.K + lane] = id;
+            if (a.rw && a.topk_w) a.rw[row * a.K + lane] = it.wk;
+        }
+    }
+}
+
+template <int NV>
+__global__ __launch_bounds__(kDspThreads) void dispatch_persistent_kernel(DispatchArgs a, int nitems) {
+    const int gw = blockIdx.x * kDspWaves + wave_in_block();
+    const int nw = gridDim.x * kDspWaves;
+    int item = gw;
+    if (item >= nitems) return;
+    Item cur;
+    u32x4 v[NV], f[NV];
+    load_item<NV>(a, item, cur, v, f);
+    for (;;) {
+        const int next = item + nw;
+        Item nx;
+        u32x4 vn[NV], fn[NV];
+        const bool more = next < nitems;
+#if EP_DSP_PERSIST == 2
+        // The current item's stores first, then the next item's loads: the
+        // wave then waits once for both, the loads in flight while the
+        // stores drain.
+        store_item<NV>(a, cur, v, f);
+        if (more) load_item<NV>(a, next, nx, vn, fn);
+#else
+        if (more) load_item<NV>(a, next, nx, vn, fn);
+        store_item<NV>(a, cur, v, f);
+#endif
+        if (!more) break;
+        cur = nx;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            v[j] = vn[j];
+            f[j] = fn[j];
+        }
+        item = next;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
@@ -201,6 +353,21 @@ hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_token
     const int64_t widest = tk.x ? 2 * (int64_t)s.H : (int64_t)s.H;
     const int64_t slice = slice_vecs(widest / 16);
     const int64_t per_lane = (slice + kWave - 1) / kWave;
+#if EP_DSP_PERSIST
+    if (per_lane <= 4 && waves <= INT32_MAX) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dispatch_persistent_kernel<4>,
+                                                              kDspThreads, 0)) != hipSuccess)
+            return e;
+        const int64_t resident = (int64_t)cus * std::max(1, std::min(per_cu, EP_DSP_PERSIST_BPC));
+        const int64_t blocks = std::min<int64_t>(resident, (waves + kDspWaves - 1) / kDspWaves);
+        hipLaunchKernelGGL(dispatch_persistent_kernel<4>, dim3((unsigned)blocks), block, 0, st, a, (int)waves);
+        return hipGetLastError();
+    }
+#endif
     if (per_lane <= 1)
         hipLaunchKernelGGL(dispatch_kernel<1>, grid, block, 0, st, a);
     else if (per_lane <= 2)

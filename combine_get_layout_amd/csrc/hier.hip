@@ -38,6 +38,33 @@ constexpr int kPieceIters = 16;  // wave iterations (2 blocks each) held in VGPR
 #define EP_SO_SPLIT 4  // scale-out: waves per token, each writing a run of the record's blocks (measured best of 1, 2, 4)
 #endif
 constexpr int kSoSplit = EP_SO_SPLIT;
+#ifndef EP_FUSED_COHERENT
+#define EP_FUSED_COHERENT 1  // fused kernel: device-scope stores and loads of group rows (else fences)
+#endif
+
+// How a scale-out wave stores its record: non-temporal, plain, or with
+// device scope (written through the XCD's L2, so that once the wave's stores
+// are acknowledged every CU of the device reads them).
+constexpr int kStoreStream = 0, kStorePlain = 1, kStoreDevice = 2;
+
+// Device-scope 16-byte store / load at byte `off` of a row of `bytes` bytes
+// (a buffer resource over the row: an access past its end is dropped by the
+// hardware). Cache-policy 16 is the device-scope bit (sc1).
+constexpr int kDeviceScope = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void st16_device(void* row, int64_t bytes, int64_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, row_rsrc(row, bytes), (int)off, 0, kDeviceScope);
+}
+__device__ __forceinline__ u32x4 ld16_device(const void* row, int64_t bytes, int64_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(row, bytes), (int)off, 0, kDeviceScope);
+}
+__device__ __forceinline__ uint32_t ld4_device(const void* row, int64_t bytes, int64_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(row, bytes), (int)off, 0, kDeviceScope);
+}
+// Wait until every vector memory access of this wave has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 constexpr int kSoPiece = kPieceIters / kSoSplit;  // wave iterations a scale-out wave holds
 
 struct HierArgs {
@@ -94,8 +121,67 @@ __device__ __forceinline__ u32x4 meta_vector(const HierArgs& a, int t, int q) {
     return v;
 }
 
-// Scale-out write of wave-slice `part` (of kSoSplit) of token t's chunked
-// record to each destination group's row.
+// Scale-out write of wave-slice `part` (of SPLIT) of token t's chunked record
+// to each destination group's row, PIECE wave-iterations held at a time.
+// Wave-slice `part` (of SPLIT) of token t's chunked record, PIECE
+// wave-iterations held at a time, stored to group row gs (lane k's value)
+// for every lane k in dest.
+template <int SPLIT, int PIECE, int STORE>
+__device__ __forceinline__ void write_record(const HierArgs& a, int t, int part, uint64_t dest, int gs) {
+    const int lane = lane_id();
+    const int nchunks = a.geom.nchunks;
+    const int iters = (nchunks + 1) / 2;
+    const int64_t stride = a.geom.stride;
+    const u32x4 flag = {a.epoch, a.epoch, a.epoch, a.epoch};
+    const int c_half = lane >> 5, w = lane & 31;
+    const int q_fp8 = a.geom.q_fp8, q_meta = a.geom.q_scales;
+    const uint8_t* x_row = a.x + (int64_t)t * a.H * 2;
+    const uint8_t* f_row = a.x_fp8 ? a.x_fp8 + (int64_t)t * a.H : x_row;
+    // This wave's run of wave-iterations of the record.
+    const int per = (iters + SPLIT - 1) / SPLIT;
+    const int it_lo = min(iters, part * per), it_hi = min(iters, it_lo + per);
+    for (int it0 = it_lo; it0 < it_hi; it0 += PIECE) {
+        u32x4 v[PIECE];
+        // 1. Hidden vectors (bf16, then fp8): one unconditional load per
+        //    iteration; lanes holding anything else load the row's first
+        //    vector (in bounds, cached) and are overwritten below.
+#pragma unroll
+        for (int j = 0; j < PIECE; ++j) {
+            const int q = (2 * (it0 + j) + c_half) * kChunkPayloadVecs + w;
+            const uint8_t* src = q < q_fp8 ? x_row + (int64_t)q * 16
+                                 : (q < q_meta ? f_row + (int64_t)(q - q_fp8) * 16 : x_row);
+            v[j] = ld16(src);
+        }
+        // 2. Metadata and padding: only in the iterations that reach them.
+#pragma unroll
+        for (int j = 0; j < PIECE; ++j) {
+            const int q = (2 * (it0 + j) + c_half) * kChunkPayloadVecs + w;
+            const int q_last = (2 * (it0 + j) + 2) * kChunkPayloadVecs - 1;  // wave-uniform
+            if (q_last >= q_meta && w < kChunkPayloadVecs && q >= q_meta) v[j] = meta_vector(a, t, q);
+        }
+        // 3. Flags.
+#pragma unroll
+        for (int j = 0; j < PIECE; ++j)
+            if (w >= kChunkPayloadVecs) v[j] = flag;
+        for (uint64_t m = dest; m; m &= m - 1) {
+            const int k = __ffsll((unsigned long long)m) - 1;
+            uint8_t* row = a.group_buf + (int64_t)readlane(gs, k) * stride;
+#pragma unroll
+            for (int j = 0; j < PIECE; ++j) {
+                const int c = 2 * (it0 + j) + c_half;
+                if (it0 + j < it_hi && c < nchunks) {
+                    if constexpr (STORE == kStoreStream) st16_stream(row + chunk_lane_offset(it0 + j, lane), v[j]);
+                    else if constexpr (STORE == kStorePlain) st16(row + chunk_lane_offset(it0 + j, lane), v[j]);
+                    else st16_device(row, stride, chunk_lane_offset(it0 + j, lane), v[j]);
+                }
+            }
+        }
+    }
+}
+
+// Scale-out write of wave-slice `part` of token t's record to each
+// destination group's row (the first lane of each group).
+template <int SPLIT, int PIECE, int STORE = kStoreStream>
 __device__ __forceinline__ void scaleout_token(const HierArgs& a, int t, int part) {
     const int lane = lane_id();
     int gs = -1;
@@ -109,59 +195,14 @@ __device__ __forceinline__ void scaleout_token(const HierArgs& a, int t, int par
     if (over && part == 0) report(a.err, EP_DEVERR_CAPACITY);
     const uint64_t dest = __ballot(first && !over);
     if (!dest) return;
-
-    const int nchunks = a.geom.nchunks;
-    const int iters = (nchunks + 1) / 2;
-    const int64_t stride = a.geom.stride;
-    const u32x4 flag = {a.epoch, a.epoch, a.epoch, a.epoch};
-    const int c_half = lane >> 5, w = lane & 31;
-    const int q_fp8 = a.geom.q_fp8, q_meta = a.geom.q_scales;
-    const uint8_t* x_row = a.x + (int64_t)t * a.H * 2;
-    const uint8_t* f_row = a.x_fp8 ? a.x_fp8 + (int64_t)t * a.H : x_row;
-    // This wave's run of wave-iterations of the record.
-    const int per = (iters + kSoSplit - 1) / kSoSplit;
-    const int it_lo = min(iters, part * per), it_hi = min(iters, it_lo + per);
-    for (int it0 = it_lo; it0 < it_hi; it0 += kSoPiece) {
-        u32x4 v[kSoPiece];
-        // 1. Hidden vectors (bf16, then fp8): one unconditional load per
-        //    iteration; lanes holding anything else load the row's first
-        //    vector (in bounds, cached) and are overwritten below.
-#pragma unroll
-        for (int j = 0; j < kSoPiece; ++j) {
-            const int q = (2 * (it0 + j) + c_half) * kChunkPayloadVecs + w;
-            const uint8_t* src = q < q_fp8 ? x_row + (int64_t)q * 16
-                                 : (q < q_meta ? f_row + (int64_t)(q - q_fp8) * 16 : x_row);
-            v[j] = ld16(src);
-        }
-        // 2. Metadata and padding: only in the iterations that reach them.
-#pragma unroll
-        for (int j = 0; j < kSoPiece; ++j) {
-            const int q = (2 * (it0 + j) + c_half) * kChunkPayloadVecs + w;
-            const int q_last = (2 * (it0 + j) + 2) * kChunkPayloadVecs - 1;  // wave-uniform
-            if (q_last >= q_meta && w < kChunkPayloadVecs && q >= q_meta) v[j] = meta_vector(a, t, q);
-        }
-        // 3. Flags.
-#pragma unroll
-        for (int j = 0; j < kSoPiece; ++j)
-            if (w >= kChunkPayloadVecs) v[j] = flag;
-        for (uint64_t m = dest; m; m &= m - 1) {
-            const int k = __ffsll((unsigned long long)m) - 1;
-            uint8_t* row = a.group_buf + (int64_t)readlane(gs, k) * stride;
-#pragma unroll
-            for (int j = 0; j < kSoPiece; ++j) {
-                const int c = 2 * (it0 + j) + c_half;
-                if (it0 + j < it_hi && c < nchunks)
-                    st16_stream(row + chunk_lane_offset(it0 + j, lane), v[j]);
-            }
-        }
-    }
+    write_record<SPLIT, PIECE, STORE>(a, t, part, dest, gs);
 }
 
 __global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
     const int gw = blockIdx.x * kWavesPerBlock + wave_in_block();
     const int t = gw / kSoSplit, part = gw % kSoSplit;
     if (t >= a.T) return;
-    scaleout_token(a, t, part);
+    scaleout_token<kSoSplit, kSoPiece>(a, t, part);
 }
 
 // Address of record byte b (4-byte aligned, never straddling a block) in a
@@ -176,7 +217,10 @@ __device__ __forceinline__ const uint8_t* record_byte(const uint8_t* row, int64_
 // row is dropped with EP_DEVERR_FLAG. Destinations: the first lane of each
 // distinct rank of group g among the record's ids, at the layout's slot of
 // (src, lane).
-__device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g) {
+// t_known >= 0: the caller knows the row's token, so the slots are loaded
+// together with the record and the record's src must equal it.
+template <bool DEVICE_LOADS = false>
+__device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g, int t_known = -1) {
     const int lane = lane_id();
     const int nchunks = a.geom.nchunks;
     const int iters = (nchunks + 1) / 2;
@@ -191,12 +235,20 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g)
 #pragma unroll
         for (int j = 0; j < kPieceIters; ++j) {
             const int c = min(2 * j + c_half, nchunks - 1);
-            v[j] = ld16(src_row + (int64_t)c * kChunkBytes + (int64_t)wv * 16);
+            const int64_t off = (int64_t)c * kChunkBytes + (int64_t)wv * 16;
+            if constexpr (DEVICE_LOADS) v[j] = ld16_device(src_row, stride, off);
+            else v[j] = ld16(src_row + off);
         }
     }
-    const int32_t src = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_src));
-    const int32_t id = *reinterpret_cast<const int32_t*>(
-        record_byte(src_row, off_idx + 4 * min(lane, a.K - 1)));
+    int32_t src, id, d_early = -1;
+    if (t_known >= 0 && lane < a.K) d_early = a.slot[(int64_t)t_known * a.K + lane];
+    if constexpr (DEVICE_LOADS) {
+        src = (int32_t)ld4_device(src_row, stride, record_byte(src_row, off_src) - src_row);
+        id = (int32_t)ld4_device(src_row, stride, record_byte(src_row, off_idx + 4 * min(lane, a.K - 1)) - src_row);
+    } else {
+        src = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_src));
+        id = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_idx + 4 * min(lane, a.K - 1)));
+    }
     bool ok = true;
     if (one_piece) {
 #pragma unroll
@@ -207,18 +259,19 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g)
         }
     } else {
         for (int i = lane; i < 2 * nchunks; i += kWave) {
-            const u32x4 f = ld16(src_row + (int64_t)(i >> 1) * kChunkBytes + kChunkPayload + (i & 1) * 16);
+            const int64_t off = (int64_t)(i >> 1) * kChunkBytes + kChunkPayload + (i & 1) * 16;
+            const u32x4 f = DEVICE_LOADS ? ld16_device(src_row, stride, off) : ld16(src_row + off);
             ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
         }
     }
-    if (__ballot(!ok) || src < 0 || src >= a.T) {
+    if (__ballot(!ok) || src < 0 || src >= a.T || (t_known >= 0 && src != t_known)) {
         if (lane == 0) report(a.err, EP_DEVERR_FLAG);
         return;
     }
     int32_t r = -1, d = -1;
     if (lane < a.K && id >= 0 && id < a.E && (id / a.epr) / a.P == g) {
         r = id / a.epr;
-        d = a.slot[(int64_t)src * a.K + lane];
+        d = t_known >= 0 ? d_early : a.slot[(int64_t)src * a.K + lane];
     }
     bool first = r >= 0 && d >= 0;
     for (int j = 0; j < a.K; ++j) {
@@ -235,7 +288,9 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g)
 #pragma unroll
             for (int j = 0; j < kPieceIters; ++j) {
                 const int c = 2 * (it0 + j) + c_half;
-                if (it0 + j < iters && c < nchunks) v[j] = ld16(src_row + chunk_lane_offset(it0 + j, lane));
+                if (it0 + j < iters && c < nchunks)
+                    v[j] = DEVICE_LOADS ? ld16_device(src_row, stride, chunk_lane_offset(it0 + j, lane))
+                                        : ld16(src_row + chunk_lane_offset(it0 + j, lane));
             }
         }
         for (uint64_t m = dest; m; m &= m - 1) {
@@ -359,19 +414,38 @@ __global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) 
         if (kind == 3) return;
         const int t0 = job * f.tile, t1 = min(a.T, t0 + f.tile);
         if (kind == 0) {
-            // Wave w writes part w % kSoSplit of every kWavesPerBlock / kSoSplit-th token.
-            constexpr int kTokPerPass = kWavesPerBlock / kSoSplit;
-            for (int t = t0 + wave / kSoSplit; t < t1; t += kTokPerPass) scaleout_token(a, t, wave % kSoSplit);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            // Wave w writes whole records of tokens t0 + w, t0 + w + 4, ...
+            // (the kernel's register budget is set by the forward part, so a
+            // wave holds a 32-block piece of the record at once).
+            for (int t = t0 + wave; t < t1; t += kWavesPerBlock)
+                scaleout_token<1, kPieceIters, EP_FUSED_COHERENT ? kStoreDevice : kStorePlain>(a, t, 0);
+#if EP_FUSED_COHERENT
+            // Publish: the rows were stored with device scope; each wave waits
+            // until its stores are acknowledged, and after the barrier thread
+            // 0 stores the flag (device scope). No L2 write-back is needed.
+            wait_vmem();
             __syncthreads();
             if (threadIdx.x == 0 && job != f.withhold)
                 __hip_atomic_store(&f.flags[job], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+            // Release: the barrier orders every wave's stores before thread
+            // 0's flag store, whose agent-scope release makes them visible
+            // device-wide (an L2 write-back, then the store).
+            __syncthreads();
+            if (threadIdx.x == 0 && job != f.withhold)
+                __hip_atomic_store(&f.flags[job], a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+#endif
             continue;
         }
-        if (kind == 2) {
-            if (threadIdx.x == 0) {
+        // Acquire: thread 0 sees the flag (kind 1: seen while claiming; kind
+        // 2: waited for, with a time limit); after the barrier every wave
+        // reads the batch's rows (with device-scope loads, or after an
+        // agent-scope acquire fence).
+        if (threadIdx.x == 0) {
+            int ok = 1;
+            if (kind == 2) {
                 const uint64_t start = (uint64_t)wall_clock64();
-                int ok = 0;
+                ok = 0;
                 for (;;) {
                     if (flag_load(&f.flags[job]) == a.epoch) {
                         ok = 1;
@@ -380,20 +454,20 @@ __global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) 
                     if ((uint64_t)wall_clock64() - start > f.timeout) break;
                     __builtin_amdgcn_s_sleep(8);
                 }
-                sh_ok = ok;
+                if (!ok) report(a.err, EP_DEVERR_TIMEOUT);
             }
-            __syncthreads();
-            const int ok = sh_ok;
-            __syncthreads();
-            if (!ok) {
-                if (threadIdx.x == 0) report(a.err, EP_DEVERR_TIMEOUT);
-                continue;
-            }
+#if !EP_FUSED_COHERENT
+            if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#endif
+            sh_ok = ok;
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __syncthreads();
+        const int ok = sh_ok;
+        __syncthreads();
+        if (!ok) continue;
         // Forward the group rows of the batch's tokens: wave w takes tokens
-        // t0 + w, t0 + w + kWavesPerBlock, ..., and each of its groups in
-        // ascending lane order (first lane of each group).
+        // t0 + w, t0 + w + 4, ..., and each of its groups in ascending lane
+        // order (the first lane of each group).
         for (int t = t0 + wave; t < t1; t += kWavesPerBlock) {
             int gs = -1, g = -1;
             if (lane < a.K) {
@@ -408,7 +482,7 @@ __global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) 
             }
             for (uint64_t m = __ballot(first && gs < a.group_cap); m; m &= m - 1) {
                 const int k = __ffsll((unsigned long long)m) - 1;
-                forward_row(a, readlane(gs, k), readlane(g, k));
+                forward_row<EP_FUSED_COHERENT != 0>(a, readlane(gs, k), readlane(g, k), t);
             }
         }
     }

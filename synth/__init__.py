@@ -16,6 +16,8 @@ ep32       4096   7168  256   32   1    8  uniform distinct (+ FP8 option)
 ep256      8192   7168  256   256  1    8  uniform distinct
 zipf       16384  4096  2048  256  1    8  Zipf(1.2) without replacement
 hier8x8    16384  7168  256   64   8    8  uniform distinct, two-level
+many       262144 256   256   32   1    8  uniform distinct (1,024 layout
+                                            workgroups; not a target config)
 =========  =====  ====  ====  ===  ===  =  =============================
 
 Recipe (numpy PCG64, seed = 20261200 + workload index unless given):
@@ -65,6 +67,9 @@ WORKLOADS = [
     Workload("ep256", 8192, 7168, 256, 256, 1, 8, "uniform"),
     Workload("zipf", 16384, 4096, 2048, 256, 1, 8, "zipf"),
     Workload("hier8x8", 16384, 7168, 256, 64, 8, 8, "uniform"),
+    # Beyond the five configurations: many layout workgroups (1,024 of 256
+    # tokens) over a narrow hidden row, so the layout's share of a step is large.
+    Workload("many", 262144, 256, 256, 32, 1, 8, "uniform"),
 ]
 
 

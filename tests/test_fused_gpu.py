@@ -85,11 +85,13 @@ def test_fused_small_first():
 
 @pytest.mark.parametrize("T,H,K,E,R,G,tile,fp8", [
     (1000, 512, 6, 64, 16, 4, 64, False),     # ragged last batch
-    (1000, 512, 6, 64, 16, 4, 4096, False),   # one batch holds every token
+    (1000, 512, 6, 64, 16, 4, 4, False),      # smallest batches
+    (50, 512, 6, 64, 16, 4, 64, False),       # one batch holds every token
     (777, 1024, 8, 128, 32, 8, 16, True),     # FP8 + scales, many small batches
     (300, 512, 4, 32, 8, 1, 32, False),       # one group holding every rank
     (257, 264, 3, 24, 8, 8, 16, False),       # one peer per group
     (129, 1032, 12, 48, 16, 4, 64, False),    # K > 8, row not a whole number of blocks
+    (200, 256, 64, 1024, 256, 256, 64, False),  # K = 64, 256 groups of one rank
     (40, 16384, 8, 64, 16, 4, 16, False),     # records of several 32-block pieces
     (1, 8, 1, 4, 2, 2, 16, False),            # one token, one lane
 ])
