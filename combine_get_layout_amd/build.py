@@ -6,6 +6,11 @@ Every HIP source is compiled with hipcc for gfx950 only. Packed fp32 vector
 instructions are switched off (-packed-fp32-ops); fp32 denormals are kept
 (hipcc's default); floating-point contraction is off so the only fused
 multiply-adds are the explicit ones.
+
+EP_HIPCC_DEFINES (environment, optional) adds preprocessor definitions, e.g.
+EP_HIPCC_DEFINES="-DEP_DSP_PERSIST=2", to build one of the measured kernel
+alternatives that the sources keep behind compile-time switches (the
+default build uses none).
 """
 from __future__ import annotations
 
@@ -36,9 +41,17 @@ FLAGS = [
 ]
 
 
+def _defines() -> list:
+    extra = os.environ.get("EP_HIPCC_DEFINES", "").split()
+    bad = [d for d in extra if not d.startswith("-D")]
+    if bad:
+        raise ValueError(f"EP_HIPCC_DEFINES takes -DNAME[=VALUE] items only: {bad}")
+    return extra
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *_defines(), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -23,6 +23,7 @@ WsLayout ws_layout(const ep_shape& s) {
     off += align256(sizeof(int32_t) * (size_t)w.nb * w.wrow);
     w.part_expert = off;
     off += align256(sizeof(int32_t) * (size_t)w.nb * s.E);
+    w.tables_end = off;
     w.fused = off;
     off += align256(sizeof(uint32_t) * (kFusedCounters + (size_t)(s.T + kFusedMinTile - 1) / kFusedMinTile));
     w.total = off;
@@ -125,7 +126,7 @@ int ep_get_layout_noalloc(const ep_shape* shape, const int64_t* topk_idx, const 
                           uint32_t* errors, void* stream) {
     int rc = check_shape(shape);
     if (rc != EP_OK) return rc;
-    if (ws_layout(*shape).total > (size_t)EP_LAYOUT_SCRATCH_BYTES) return EP_ERR_SCRATCH;
+    if (ws_layout(*shape).tables_end > (size_t)EP_LAYOUT_SCRATCH_BYTES) return EP_ERR_SCRATCH;
     if (!layout || !errors || !aligned(errors, 4) || (shape->T > 0 && !topk_idx) || !aligned(topk_idx, 8))
         return EP_ERR_ARG;
     const ep_layout& L = *layout;

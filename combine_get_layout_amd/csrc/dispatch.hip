@@ -181,11 +181,14 @@ __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(Disp
     }
 }
 
-// Persistent form: a grid of at most the resident waves; wave w takes the
-// items (token, slice) w, w + W, w + 2W, ... (W = waves in the grid) and
-// issues the next item's slot and row-slice loads before the current item's
-// stores, so that a wave's loads are in flight while its stores drain.
-// Needs the widest slice to fit in one pass (NV vectors per lane).
+// Persistent form (EP_DSP_PERSIST, off by default: measured slower than the
+// one-shot kernel on every workload). A grid of at most the resident waves;
+// wave w takes the items (token, slice) w, w + W, w + 2W, ... (W = waves in
+// the grid) with two register sets. EP_DSP_PERSIST=1 issues the next item's
+// loads before the current item's stores; =2 after them (loads and stores
+// share one in-order counter, so with 1 the wave waits for the next loads
+// before its first store, and with 2 it waits once for both). Needs the
+// widest slice to fit in one pass (NV vectors per lane).
 struct Item {
     int t, part;
     int s;        // slot of lane k < K

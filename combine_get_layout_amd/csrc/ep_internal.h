@@ -27,6 +27,7 @@ struct WsLayout {
                             // [0, R)), valid lanes per rank ([rp, rp + R)) and
                             // deduplicated tokens per group ([2 rp, 2 rp + G))
     size_t part_expert;     // int32 [nb][E] lanes per expert
+    size_t tables_end;      // end of the count tables (all the layout kernels use)
     size_t fused;           // fused two-level dispatch: u32 [kFusedCounters] work counters,
                             // then u32 [ceil(T / kFusedMinTile)] batch flags
     size_t total;
