@@ -105,6 +105,34 @@ def test_graph_two_level_step():
     assert ep.ep_check_errors(ws) == 0
 
 
+def test_graph_fused_two_level_step():
+    """The fused two-level dispatch in a graph: its flag-and-counter reset is a
+    kernel node, so every replay (same epoch) starts from zeroed flags."""
+    w = synth.workload("hier8x8").scaled(2048)
+    inp = synth.make_inputs(w, seed=3)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, w.G)
+    L = ep.alloc_layout(shape, masks=False, groups=True)
+    ws = ep.alloc_workspace(shape)
+    tk = dict(x=dev(inp["x"]), topk_idx=dev(inp["topk_idx"]), topk_weights=dev(inp["topk_w"]))
+    ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+    torch.cuda.synchronize()
+    N = int(L["rank_offsets"][-1].item())
+    GR = int(L["group_offsets"][-1].item())
+    stride = ep.ep_chunked_record_bytes(shape, ep.EP_SEG_BF16)
+    gbuf = torch.zeros((GR, stride), dtype=torch.uint8, device="cuda")
+    pbuf = torch.zeros((N, stride), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
+
+    def run():
+        ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+        ep.ep_hierarchical_dispatch_fused(shape, L, tk, 9, gbuf, GR, pbuf, N, ws, tile=16)
+        ep.ep_combine(shape, L, pbuf, N, stride, ep.EP_FMT_CHUNKED, 9, tk["topk_weights"], out, ws)
+
+    replay_and_compare(run, [L["slot"], L["group_slot"], gbuf, pbuf, out])
+    assert ep.ep_check_errors(ws) == 0
+    assert ep.ep_check_sticky_errors(ws) == 0
+
+
 def test_graph_sources_step():
     w = synth.workload("ep32").scaled(1024)
     inp = synth.make_inputs(w)
