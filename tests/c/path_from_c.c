@@ -4,7 +4,8 @@
  *         combine reads the dispatched rows back);
  *   two-level (2 groups of 4 ranks): ep_get_layout with groups ->
  *         ep_hierarchical_dispatch (both steps) -> ep_combine on the chunked
- *         rows and ep_combine_two_level.
+ *         rows and ep_combine_two_level; the fused one-launch two-level
+ *         dispatch; the allocation-free layout.
  * The results are compared bit for bit with the CPU oracle (liboracle.so,
  * test infrastructure), called from the same program. Inputs come from a fixed xorshift generator: ids in [-1, E) with
  * repeats, bf16 rows in [-2, 2), weights in [0, 1).
@@ -235,6 +236,29 @@ int main(void) {
         ok &= rc == EP_OK && b1 == 0;
         printf("%s cleared: status %d bits %u\n", rc == EP_OK && b1 == 0 ? "ok" : "FAIL", rc, b1);
     }
+    /* the allocation-free layout: same outputs, error words in ws */
+    {
+        static int32_t n_tpr[R], n_ro[R + 1], n_slot[T * K];
+        int32_t *dn_tpr, *dn_ro, *dn_slot;
+        HIP_OK(hipMalloc((void **)&dn_tpr, sizeof n_tpr));
+        HIP_OK(hipMalloc((void **)&dn_ro, sizeof n_ro));
+        HIP_OK(hipMalloc((void **)&dn_slot, sizeof n_slot));
+        ep_layout Ln;
+        memset(&Ln, 0, sizeof Ln);
+        Ln.tokens_per_rank = dn_tpr;
+        Ln.rank_offsets = dn_ro;
+        Ln.slot = dn_slot;
+        EP_OK_(ep_get_layout_noalloc(&s, d_ids, &Ln, (uint32_t *)ws, st));
+        uint32_t bn = 99;
+        EP_OK_(ep_check_errors(ws, st, &bn));
+        HIP_OK(hipMemcpy(n_tpr, dn_tpr, sizeof n_tpr, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(n_ro, dn_ro, sizeof n_ro, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(n_slot, dn_slot, sizeof n_slot, hipMemcpyDeviceToHost));
+        ok &= same("noalloc tokens_per_rank", n_tpr, o_tpr, sizeof o_tpr);
+        ok &= same("noalloc rank_offsets", n_ro, o_ro, sizeof o_ro);
+        ok &= same("noalloc slot", n_slot, o_slot, sizeof o_slot);
+        ok &= bn == 0;
+    }
     /* two-level path on the same tokens, R ranks in G2 groups */
     {
         static int32_t p_tpe[E], p_tpr[R], p_tpg[G2], p_eo[E + 1], p_ro[R + 1], p_go[G2 + 1], p_slot[T * K],
@@ -313,6 +337,27 @@ int main(void) {
         ok &= same("combine out, chunked rows", g_out2, o_out2, sizeof o_out2);
         ok &= same("two-level partial rows", g_part, o_part, (size_t)GR * pstride);
         ok &= same("two-level combine out", g_out3, o_out3, sizeof o_out3);
+        /* the fused one-launch form (16-token batches), fresh buffers, next epoch */
+        {
+            uint8_t *o_gbuf2 = calloc((size_t)GR, (size_t)stride), *o_pbuf2 = calloc((size_t)N2, (size_t)stride);
+            uint32_t f_err = 0;
+            oracle_hier_dispatch(T, H, K, E, R, G2, ids, w, x, NULL, NULL, p_slot, p_go, EPOCH + 1, o_gbuf2, GR,
+                                 o_pbuf2, N2, 3, &f_err);
+            HIP_OK(hipMemset(d2_gbuf, 0, (size_t)GR * stride));
+            HIP_OK(hipMemset(d2_pbuf, 0, (size_t)N2 * stride));
+            ep_fused_opts fo;
+            memset(&fo, 0, sizeof fo);
+            fo.tile_tokens = 16;
+            EP_OK_(ep_hierarchical_dispatch_fused(&s2, &L2, &tk, EPOCH + 1, d2_gbuf, GR, d2_pbuf, N2, &fo, ws2,
+                                                  ws2_bytes, st));
+            uint32_t fb = 99;
+            EP_OK_(ep_check_errors(ws2, st, &fb));
+            HIP_OK(hipMemcpy(g_gbuf, d2_gbuf, (size_t)GR * stride, hipMemcpyDeviceToHost));
+            HIP_OK(hipMemcpy(g_pbuf, d2_pbuf, (size_t)N2 * stride, hipMemcpyDeviceToHost));
+            ok &= same("fused group rows", g_gbuf, o_gbuf2, (size_t)GR * stride);
+            ok &= same("fused peer rows", g_pbuf, o_pbuf2, (size_t)N2 * stride);
+            ok &= fb == 0 && f_err == 0;
+        }
         if (bits2 != p_err) {
             printf("FAIL two-level error bits %u != %u\n", bits2, p_err);
             ok = 0;

@@ -1,7 +1,9 @@
 """Seeded random shapes through every entry point, each compared with the CPU
-oracle: layout (all outputs, groups and expand rows), dispatch with a random
-subset of payload pieces, combine, the two-level chunked dispatch with the
-flat and the two-level combine, and expand-mode dispatch and combine.
+oracle: layout (all outputs, groups and expand rows; also through the
+allocation-free entry point), dispatch with a random subset of payload
+pieces, combine, the two-level chunked dispatch (two launches, and the fused
+one-launch form with a random batch size) with the flat and the two-level
+combine, and expand-mode dispatch and combine.
 
 The shapes are drawn from a fixed seed list (200 seeds; EP_FUZZ_SEEDS sets
 another count), so a failure names a case that
@@ -106,6 +108,14 @@ def test_fuzz_all_entry_points(seed):
     es = oracle.expert_slots(topk, E, O["expert_offsets"])
     np.testing.assert_array_equal(host(L["expert_slot"]).reshape(T, K), es, err_msg="expert_slot")
     assert ep.ep_check_errors(ws) == 0
+    # the allocation-free layout gives the same outputs
+    L2 = ep.alloc_layout(shape, masks=True, groups=True, expand=True)
+    for t in L2.values():
+        poison(t)
+    ep.ep_get_layout_noalloc(shape, tk, L2, ws)
+    for k in L:
+        assert torch.equal(L2[k].view(torch.uint8), L[k].view(torch.uint8)), "noalloc " + k
+    assert ep.ep_check_errors(ws) == 0
     N = int(O["rank_offsets"][R])
     G_rows = int(O["group_offsets"][G])
 
@@ -153,6 +163,15 @@ def test_fuzz_all_entry_points(seed):
     Hd = oracle.hier_dispatch(topk, E, R, G, O["slot"], O["group_offsets"], epoch, x=x, topk_w=w)
     np.testing.assert_array_equal(host(gb)[:G_rows], Hd["group_buf"])
     np.testing.assert_array_equal(host(pb)[:N], Hd["peer_buf"])
+    # the fused one-launch form, a random batch size, a new epoch
+    tile = int(rng.choice([4, 7, 16, 33, 64]))
+    gbf = poison(torch.empty_like(gb))
+    pbf = poison(torch.empty_like(pb))
+    ep.ep_hierarchical_dispatch_fused(shape, L, htok, epoch + 1000, gbf, G_rows, pbf, N, ws, tile=tile)
+    Hf = oracle.hier_dispatch(topk, E, R, G, O["slot"], O["group_offsets"], epoch + 1000, x=x, topk_w=w)
+    np.testing.assert_array_equal(host(gbf)[:G_rows], Hf["group_buf"], err_msg=f"fused tile {tile}")
+    np.testing.assert_array_equal(host(pbf)[:N], Hf["peer_buf"], err_msg=f"fused tile {tile}")
+    assert ep.ep_check_errors(ws) == 0
     ep.ep_combine(shape, L, pb, N, stride, ep.EP_FMT_CHUNKED, epoch, wd, out, ws)
     C = oracle.combine(O["slot"], w, Hd["peer_buf"], H, chunked=True, epoch=epoch)
     np.testing.assert_array_equal(host(out), C["out"])
