@@ -234,8 +234,8 @@ def test_graph_cycle_error_in_an_earlier_step_is_kept():
     assert ep.ep_check_sticky_errors(ws) == 0
 
 
-@pytest.mark.parametrize("name", ["ep32", "zipf"])
-def test_graph_cycle_full_size_against_oracle(name):
+@pytest.mark.parametrize("name,fp8", [("ep32", False), ("ep32", True), ("ep256", False), ("zipf", False)])
+def test_graph_cycle_full_size_against_oracle(name, fp8):
     """The full-size workload in the launch configuration the benchmark times:
     the steps of two input batches captured in one graph (shared workspace
     and receive buffer, per-batch layouts), replayed, and every output of the
@@ -244,13 +244,18 @@ def test_graph_cycle_full_size_against_oracle(name):
 
     oracle.build(force=False)
     w = synth.workload(name)
+    print(f"graph cycle: {name} fp8={fp8}", flush=True)
     shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, 1)
     ws = ep.alloc_workspace(shape)
-    inps = [synth.make_inputs(w, seed=synth.seed_of(w) + 1000 * i) for i in range(2)]
+    inps = [synth.make_inputs(w, seed=synth.seed_of(w) + 1000 * i, with_fp8=fp8) for i in range(2)]
     batches = [dict(x=dev(b["x"]), topk_idx=dev(b["topk_idx"]), topk_weights=dev(b["topk_w"])) for b in inps]
+    if fp8:
+        for tk, b in zip(batches, inps):
+            tk["x_fp8"] = dev(b["x_fp8"])
+            tk["x_scales"] = dev(b["x_scales"])
     Ls = [ep.alloc_layout(shape, masks=True, groups=False) for _ in batches]
     cap = w.T * min(w.K, w.R)
-    recv = ep.alloc_recv(shape, cap)
+    recv = ep.alloc_recv(shape, cap, fp8=fp8, scales=fp8)
     outs = [torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda") for _ in batches]
 
     def run():
@@ -277,7 +282,8 @@ def test_graph_cycle_full_size_against_oracle(name):
     for i, b in enumerate(inps):
         O = oracle.layout(b["topk_idx"], w.E, w.R, 1)
         np.testing.assert_array_equal(Ls[i]["slot"].cpu().numpy().reshape(w.T, w.K), O["slot"])
-        D = oracle.dispatch(b["topk_idx"], w.E, w.R, O["rank_offsets"], x=b["x"], topk_w=b["topk_w"])
+        D = oracle.dispatch(b["topk_idx"], w.E, w.R, O["rank_offsets"], x=b["x"], topk_w=b["topk_w"],
+                            x_fp8=b.get("x_fp8"), x_scales=b.get("x_scales"))
         C = oracle.combine(O["slot"], b["topk_w"], D["recv_x"], w.H)
         got = outs[i].view(torch.int16).cpu().numpy().view(np.uint16)
         np.testing.assert_array_equal(got, C["out"], err_msg=f"batch {i}")
@@ -285,3 +291,70 @@ def test_graph_cycle_full_size_against_oracle(name):
             N = int(O["rank_offsets"][-1])
             rx = recv["x"].view(torch.int16).cpu().numpy().view(np.uint16)[:N]
             np.testing.assert_array_equal(rx, D["recv_x"])
+            np.testing.assert_array_equal(recv["src_idx"].cpu().numpy()[:N], D["recv_src"])
+            np.testing.assert_array_equal(recv["topk_idx"].cpu().numpy()[:N], D["recv_topk_idx"])
+            if fp8:
+                np.testing.assert_array_equal(recv["x_fp8"].cpu().numpy()[:N], D["recv_fp8"])
+                np.testing.assert_array_equal(recv["x_scales"].cpu().numpy()[:N].view(np.uint32),
+                                              D["recv_scales"].view(np.uint32))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_cycle_full_size_hier8x8_against_oracle(fused):
+    """hier8x8 at full size as the benchmark times it: the steps of two input
+    batches (layout, two-level dispatch (two launches, or the fused one),
+    combine on the chunked scale-up rows) in one graph, replayed twice, and
+    the last replay's group rows, scale-up rows and combine outputs compared
+    with the CPU oracle."""
+    import oracle
+
+    oracle.build(force=False)
+    w = synth.workload("hier8x8")
+    print(f"graph cycle: hier8x8 fused={fused}", flush=True)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, w.G)
+    ws = ep.alloc_workspace(shape)
+    inps = [synth.make_inputs(w, seed=synth.seed_of(w) + 1000 * i) for i in range(2)]
+    batches = [dict(x=dev(b["x"]), topk_idx=dev(b["topk_idx"]), topk_weights=dev(b["topk_w"])) for b in inps]
+    Ls = [ep.alloc_layout(shape, masks=False, groups=True) for _ in batches]
+    Os = [oracle.layout(b["topk_idx"], w.E, w.R, w.G) for b in inps]
+    Ns = [int(O["rank_offsets"][-1]) for O in Os]
+    Gs = [int(O["group_offsets"][-1]) for O in Os]
+    stride = ep.ep_chunked_record_bytes(shape, ep.EP_SEG_BF16)
+    gbuf = torch.zeros((max(Gs), stride), dtype=torch.uint8, device="cuda")
+    pbuf = torch.zeros((max(Ns), stride), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda") for _ in batches]
+
+    def run():
+        for i, tk in enumerate(batches):
+            e = 40 + i
+            ep.ep_get_layout(shape, tk["topk_idx"], Ls[i], ws)
+            if fused:
+                ep.ep_hierarchical_dispatch_fused(shape, Ls[i], tk, e, gbuf, Gs[i], pbuf, Ns[i], ws)
+            else:
+                ep.ep_hierarchical_dispatch(shape, Ls[i], tk, e, 3, gbuf, Gs[i], pbuf, Ns[i], ws)
+            ep.ep_combine(shape, Ls[i], pbuf, Ns[i], stride, ep.EP_FMT_CHUNKED, e, tk["topk_weights"], outs[i], ws)
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for o in outs:
+        o.view(torch.uint8).fill_(0xA5)
+    pbuf.fill_(0)
+    torch.cuda.synchronize()
+    ep.ep_clear_errors(ws)
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    assert ep.ep_check_sticky_errors(ws) == 0
+    for i, b in enumerate(inps):
+        O = Os[i]
+        Hd = oracle.hier_dispatch(b["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_offsets"], 40 + i,
+                                  x=b["x"], topk_w=b["topk_w"])
+        C = oracle.combine(O["slot"], b["topk_w"], Hd["peer_buf"], w.H, chunked=True, epoch=40 + i)
+        got = outs[i].view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, C["out"], err_msg=f"batch {i}")
+        if i == len(inps) - 1:  # the buffers hold the last batch's dispatch
+            np.testing.assert_array_equal(gbuf.cpu().numpy()[:Gs[i]], Hd["group_buf"])
+            np.testing.assert_array_equal(pbuf.cpu().numpy()[:Ns[i]], Hd["peer_buf"])
