@@ -20,9 +20,9 @@ WsLayout ws_layout(const ep_shape& s) {
     w.err = off;
     off += 256;
     w.part_rlg = off;
-    off += align256(sizeof(int32_t) * (size_t)w.nb * w.wrow);
+    off += align256(sizeof(int32_t) * (size_t)(w.nb + 1) * w.wrow);
     w.part_expert = off;
-    off += align256(sizeof(int32_t) * (size_t)w.nb * s.E);
+    off += align256(sizeof(int32_t) * (size_t)(w.nb + 1) * s.E);
     w.tables_end = off;
     w.fused = off;
     off += align256(sizeof(uint32_t) * (kFusedCounters + (size_t)(s.T + kFusedMinTile - 1) / kFusedMinTile));

@@ -22,11 +22,12 @@ struct WsLayout {
     int rp, gp;             // R and G rounded up to multiples of 4
     int wrow;               // ints per row of the rank/lane/group table: 2 * rp + gp
     size_t err;             // uint32 error word
-    // Per-workgroup count tables, one row per layout workgroup (row-major):
-    size_t part_rlg;        // int32 [nb][wrow]: deduplicated tokens per rank (columns
+    // Per-workgroup count tables, one row per layout workgroup (row-major),
+    // plus one row for the column totals when many workgroups are scanned:
+    size_t part_rlg;        // int32 [nb + 1][wrow]: deduplicated tokens per rank (columns
                             // [0, R)), valid lanes per rank ([rp, rp + R)) and
                             // deduplicated tokens per group ([2 rp, 2 rp + G))
-    size_t part_expert;     // int32 [nb][E] lanes per expert
+    size_t part_expert;     // int32 [nb + 1][E] lanes per expert
     size_t tables_end;      // end of the count tables (all the layout kernels use)
     size_t fused;           // fused two-level dispatch: u32 [kFusedCounters] work counters,
                             // then u32 [ceil(T / kFusedMinTile)] batch flags

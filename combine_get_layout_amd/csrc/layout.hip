@@ -30,6 +30,12 @@
 //               per-rank lane counts, which every workgroup already sums.
 //   3. expand : (only when expand rows are asked for) the row of each
 //               (token, lane) inside its expert's region.
+// With many workgroups (kScanMinBlocks or more) the assign launch would read
+// nb rows in each of nb workgroups; a scan launch between count and assign
+// then turns every column of both tables into its exclusive prefix over the
+// workgroup rows (in place, totals in an extra row nb), and each assign
+// workgroup reads two rows: O(nb * columns) work in all instead of
+// O(nb^2 * columns).
 // Workgroups never wait for each other and no grid-wide fence is needed (the
 // launch boundaries order the kernels).
 #include <algorithm>
@@ -242,8 +248,10 @@ __device__ __forceinline__ void add_rows(const u32x4* x, int b0, int b, int nb, 
 
 // SPREAD: the launch has more than 2 batches of table rows and no expand
 // rows, so the spread loads below may apply (a separate instantiation keeps
-// the code of the other launches as it is).
-template <int KMAX, bool SPREAD>
+// the code of the other launches as it is). SCANNED: the scan launch has
+// already turned the tables into per-workgroup prefixes with the totals in
+// row nb, so only rows b and nb are read.
+template <int KMAX, bool SPREAD, bool SCANNED>
 __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs a) {
     extern __shared__ __align__(16) uint32_t lds[];
     uint32_t* bits_r = lds;                                                // [R][kWords]
@@ -314,8 +322,8 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
     const int vpt = nvec > 128 ? 2 : 1;
     const int cols = max(max((nvec + vpt - 1) / vpt, ne), 1);
     const int J = kBlockThreads / cols;
-    const bool spread = SPREAD && !expand && vec_rounds == 1 && slice_rounds <= 1 && J >= 2 &&
-                        a.nb > 2 * kRowBatch;
+    const bool spread = SPREAD && !SCANNED && !expand && vec_rounds == 1 && slice_rounds <= 1 &&
+                        J >= 2 && a.nb > 2 * kRowBatch;
     auto spread_loads = [&](auto vpt_c) {
         constexpr int VPT = decltype(vpt_c)::value;
         const int c = tid % cols, j = tid / cols;
@@ -359,7 +367,37 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
             }
         o[16] = pe_sum;
     };
-    if (spread) {
+    if constexpr (SCANNED) {
+        // This workgroup's prefix row and the totals row, every round at once.
+        const int32_t* pb = a.part_rlg + (int64_t)b * a.wrow;
+        const int32_t* pa = a.part_rlg + (int64_t)a.nb * a.wrow;
+        const int32_t* ea = a.part_expert + (int64_t)a.nb * a.E;
+        u32x4 xb[kVecRounds], xa[kVecRounds];
+        int32_t xe[kSliceRounds];
+#pragma unroll
+        for (int q = 0; q < kVecRounds; ++q) {
+            const int v = min(q * kBlockThreads + tid, nvec - 1);
+            xb[q] = ld16(pb + 4 * v);
+            xa[q] = ld16(pa + 4 * v);
+        }
+#pragma unroll
+        for (int q = 0; q < kSliceRounds; ++q) xe[q] = ea[min(e0 + q * kBlockThreads + tid, a.E - 1)];
+#pragma unroll
+        for (int q = 0; q < kVecRounds; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bef[q][i] = q < vec_rounds ? (int)xb[q][i] : 0;
+                all[q][i] = q < vec_rounds ? (int)xa[q][i] : 0;
+            }
+#pragma unroll
+        for (int q = 0; q < kSliceRounds; ++q) {
+            const int c = q * kBlockThreads + tid;
+            if (q < slice_rounds && c < ne) {
+                etot[q] = xe[q];
+                if (te) te[e0 + c] = xe[q];
+            }
+        }
+    } else if (spread) {
         if (vpt == 2)
             spread_loads(std::integral_constant<int, 2>{});
         else
@@ -391,7 +429,7 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
     // wider than 256 experts.
 #pragma unroll
     for (int q = 1; q < kVecRounds; ++q) {
-        if (q < vec_rounds) {
+        if (!SCANNED && q < vec_rounds) {
             const int32_t* pv = a.part_rlg + 4 * min(q * kBlockThreads + tid, nvec - 1);
             for (int b0 = 0; b0 < a.nb; b0 += kRowBatch) {
                 u32x4 x[kRowBatch];
@@ -403,7 +441,7 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
     }
 #pragma unroll
     for (int q = 1; q < kSliceRounds; ++q) {
-        if (q < slice_rounds) {
+        if (!SCANNED && q < slice_rounds) {
             const int c = q * kBlockThreads + tid;
             const bool own = c < ne && expand;
             int32_t* pe = a.part_expert + min(e0 + c, a.E - 1);
@@ -640,6 +678,61 @@ __global__ __launch_bounds__(kBlockThreads) void layout_assign_kernel(LayoutArgs
     }
 }
 
+// Column scan for launches with many workgroups. The columns of both tables
+// ([rank | lane | group] columns, then expert columns) are cut into tiles of
+// 64, one workgroup of 16 waves per tile, one column per lane (a wave's load
+// of a row is 256 contiguous bytes). Wave w sums its segment of rows
+// [w nb / 16, (w + 1) nb / 16); the segment sums meet in LDS; the wave then
+// rewrites its rows as exclusive prefixes and the last wave writes the
+// column total into row nb. Padding columns are scanned like the others and
+// never read as counts.
+#ifndef EP_LAYOUT_SCAN_MIN
+#define EP_LAYOUT_SCAN_MIN 512  // workgroups from which the scan pays for its launch
+#endif
+constexpr int kScanMinBlocks = EP_LAYOUT_SCAN_MIN;
+constexpr int kScanWaves = 16;
+constexpr int kScanRows = 16;        // rows loaded per batch
+
+__global__ __launch_bounds__(kScanWaves * kWave) void layout_scan_kernel(LayoutArgs a) {
+    __shared__ int seg[kScanWaves][kWave];
+    const int lane = lane_id();
+    const int w = threadIdx.x / kWave;
+    const int c = blockIdx.x * kWave + lane;
+    const bool in = c < a.wrow + a.E;
+    const bool rlg = c < a.wrow;
+    int32_t* col = rlg ? a.part_rlg + c : a.part_expert + min(c - a.wrow, a.E - 1);
+    const int64_t stride = rlg ? a.wrow : a.E;
+    const int r0 = (int)((int64_t)a.nb * w / kScanWaves), r1 = (int)((int64_t)a.nb * (w + 1) / kScanWaves);
+    int sum = 0;
+    for (int rb = r0; rb < r1; rb += kScanRows) {
+        int x[kScanRows];
+#pragma unroll
+        for (int j = 0; j < kScanRows; ++j) x[j] = col[(int64_t)min(rb + j, r1 - 1) * stride];
+#pragma unroll
+        for (int j = 0; j < kScanRows; ++j) sum += rb + j < r1 ? x[j] : 0;
+    }
+    seg[w][lane] = sum;
+    __syncthreads();
+    int run = 0, total = 0;
+#pragma unroll
+    for (int j = 0; j < kScanWaves; ++j) {
+        const int y = seg[j][lane];
+        total += y;
+        run += j < w ? y : 0;
+    }
+    for (int rb = r0; rb < r1; rb += kScanRows) {
+        int x[kScanRows];
+#pragma unroll
+        for (int j = 0; j < kScanRows; ++j) x[j] = col[(int64_t)min(rb + j, r1 - 1) * stride];
+#pragma unroll
+        for (int j = 0; j < kScanRows; ++j) {
+            if (in && rb + j < r1) col[(int64_t)(rb + j) * stride] = run;
+            run += rb + j < r1 ? x[j] : 0;
+        }
+    }
+    if (in && w == kScanWaves - 1) col[(int64_t)a.nb * stride] = total;
+}
+
 // Expand-mode rows. The row of entry (t, k) with expert e is
 //   expert_offsets[e] + (lanes of e in earlier workgroups)
 //                     + (entries of e before (t, k) in this workgroup, in
@@ -828,7 +921,8 @@ static hipError_t launch_layout_tables(const ep_shape& s, const int64_t* topk, c
     a.out = L;
 
     const size_t lds_count = sizeof(uint32_t) * ((size_t)(s.R + s.G) * kWords + s.E);
-    const bool spread_launch = W.nb > 2 * kRowBatch && !L.expert_slot;
+    const bool scanned = W.nb >= kScanMinBlocks;
+    const bool spread_launch = !scanned && W.nb > 2 * kRowBatch && !L.expert_slot;
     const size_t lds_assign = sizeof(uint32_t) * ((size_t)(s.R + s.G) * kWords + s.R + s.G +
                                                   (size_t)kScSlots * kWavesPerBlock) +
                               (size_t)(s.R + s.G) * kWords +
@@ -838,10 +932,14 @@ static hipError_t launch_layout_tables(const ep_shape& s, const int64_t* topk, c
 #define EP_LAYOUT_LAUNCH(KM)                                                                  \
     do {                                                                                      \
         hipLaunchKernelGGL(layout_count_kernel<KM>, grid, block, lds_count, st, a);           \
-        if (spread_launch)                                                                    \
-            hipLaunchKernelGGL((layout_assign_kernel<KM, true>), grid, block, lds_assign, st, a); \
+        if (scanned) {                                                                        \
+            hipLaunchKernelGGL(layout_scan_kernel, dim3((unsigned)((W.wrow + s.E + kWave - 1) / kWave)), \
+                               dim3(kScanWaves * kWave), 0, st, a);                           \
+            hipLaunchKernelGGL((layout_assign_kernel<KM, false, true>), grid, block, lds_assign, st, a); \
+        } else if (spread_launch)                                                             \
+            hipLaunchKernelGGL((layout_assign_kernel<KM, true, false>), grid, block, lds_assign, st, a); \
         else                                                                                  \
-            hipLaunchKernelGGL((layout_assign_kernel<KM, false>), grid, block, lds_assign, st, a); \
+            hipLaunchKernelGGL((layout_assign_kernel<KM, false, false>), grid, block, lds_assign, st, a); \
     } while (0)
     if (s.K <= 2)
         EP_LAYOUT_LAUNCH(2);

@@ -168,8 +168,8 @@ int ep_get_layout(const ep_shape *shape, const int64_t *topk_idx, const ep_layou
  * address is looked up on the first call on that GPU); every call on a GPU
  * shares it, so calls that overlap on one GPU (several streams, several host
  * threads) race and must be serialised by the caller. The call allocates and
- * frees nothing. Limit: the count tables, 256 + a(4 * nb * (2 * R4 + G4)) +
- * a(4 * nb * E) bytes (nb = ceil(T / 256), R4 and G4 = R and G rounded up to
+ * frees nothing. Limit: the count tables, 256 + a(4 * (nb + 1) * (2 * R4 + G4))
+ * + a(4 * (nb + 1) * E) bytes (nb = ceil(T / 256), R4 and G4 = R and G rounded up to
  * multiples of 4, a() rounds up to a multiple of 256), must not exceed
  * EP_LAYOUT_SCRATCH_BYTES (4 MiB: e.g. 262,144 tokens with E = 256 and R =
  * 64 need 1.6 MB, 16,384 tokens with E = 2048 and R = 256 need 0.66 MB),

@@ -631,6 +631,35 @@ def test_expand_dispatch_and_combine(name, fp8):
     assert ep.ep_check_errors(ws) == 0
 
 
+@pytest.mark.parametrize("T,H,K,E,R,G,expand", [
+    (140000, 64, 8, 256, 64, 8, True),      # 547 workgroups: the scanned count tables, groups, expand rows
+    (1048576, 8, 4, 64, 16, 4, False),      # 4,096 workgroups
+])
+def test_layout_many_workgroups_scanned(T, H, K, E, R, G, expand):
+    """From 512 layout workgroups up, a scan launch turns the count tables into
+    per-workgroup prefixes and each assign workgroup reads two rows: every
+    layout output must still be the oracle's."""
+    w = synth.Workload("scan", T, H, E, R, G, K, "uniform")
+    print(f"scanned layout: T={T} K={K} E={E} R={R} G={G} expand={expand}", flush=True)
+    topk = np.random.default_rng(T).integers(-1, E, size=(T, K)).astype(np.int64)
+    topk[::97, 0] = E + 3  # some invalid ids
+    shape = ep.make_shape(T, H, K, E, R, G)
+    L = ep.alloc_layout(shape, masks=True, groups=True, expand=expand)
+    for t in L.values():
+        poison(t)
+    ws = ep.alloc_workspace(shape)
+    ep.ep_get_layout(shape, dev(topk), L, ws)
+    torch.cuda.synchronize()
+    O = oracle.layout(topk, E, R, G)
+    for k in ("tokens_per_expert", "tokens_per_rank", "tokens_per_group", "expert_offsets", "rank_offsets",
+              "group_offsets", "is_token_in_rank", "is_token_in_group", "slot", "group_slot"):
+        np.testing.assert_array_equal(host(L[k]).reshape(O[k].shape), O[k], err_msg=k)
+    if expand:
+        es = oracle.expert_slots(topk, E, O["expert_offsets"])
+        np.testing.assert_array_equal(host(L["expert_slot"]).reshape(T, K), es, err_msg="expert_slot")
+    assert ep.ep_check_errors(ws) == ep.EP_DEVERR_EXPERT_ID
+
+
 def test_many_tokens_end_to_end():
     """262,144 tokens: 1,024 layout workgroups, so every assign workgroup
     sums 1,024 rows of the count tables (spread over 15 thread groups); then
