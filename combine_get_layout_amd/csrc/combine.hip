@@ -407,9 +407,78 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(
     }
 }
 
+// Narrow plain rows (at most 32 vectors: H <= 256) with K <= 8: one token
+// per wave would leave most lanes idle, so a wave holds TPW tokens, one per
+// group of G = 64 / TPW lanes (the row's vectors padded to a power of two).
+// Each lane loads its token's K rows' vector (clamped to a usable row,
+// issued together), then sums them in ascending k with fmaf from +0.0f and
+// rounds once to bf16: the same arithmetic as the kernels above.
+template <int TPW>
+__global__ __launch_bounds__(kCmbThreads) void combine_narrow_kernel(CombineArgs a) {
+    constexpr int G = kWave / TPW;
+    const int lane = lane_id();
+    const int gw = blockIdx.x * kCmbWaves + wave_in_block();
+    const int t = gw * TPW + lane / G;
+    const int v = lane % G;
+    if (t >= a.T) return;
+    int s[8];
+    float wk[8];
+    int any = -1;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        s[k] = -1;
+        wk[k] = 0.f;
+        if (k < a.K) {
+            s[k] = a.slot[(int64_t)t * a.K + k];
+            wk[k] = a.w[(int64_t)t * a.K + k];
+        }
+    }
+    bool over = false;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (s[k] >= a.y_rows) {
+            over = true;
+            s[k] = -1;
+        }
+        if (any < 0 && s[k] >= 0) any = s[k];
+    }
+    if (over && v == 0) report(a.err, EP_DEVERR_CAPACITY);
+    const int nvh = a.H / 8;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (any >= 0) {
+        const int64_t off = (int64_t)min(v, nvh - 1) * 16;
+        u32x4 y[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = ld_row(a.y + (int64_t)(s[k] >= 0 ? s[k] : any) * a.stride + off);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (s[k] >= 0) fma8(acc, wk[k], y[k]);
+    }
+    if (v < nvh) st16_stream(reinterpret_cast<uint8_t*>(a.out) + ((int64_t)t * nvh + v) * 16, pack8(acc));
+}
+
 template <bool CHUNKED>
 hipError_t launch_k(const CombineArgs& a, hipStream_t st) {
     const dim3 block(kCmbThreads);
+    const int nvh = a.H / 8;
+    if (!CHUNKED && a.K <= 8 && nvh <= kWave / 2) {
+        int g = 1;
+        while (g < nvh) g *= 2;
+        const int tpw = kWave / g;
+        const int64_t waves = ((int64_t)a.T + tpw - 1) / tpw;
+        const dim3 grid((unsigned)((waves + kCmbWaves - 1) / kCmbWaves));
+        switch (tpw) {
+            case 2: hipLaunchKernelGGL(combine_narrow_kernel<2>, grid, block, 0, st, a); break;
+            case 4: hipLaunchKernelGGL(combine_narrow_kernel<4>, grid, block, 0, st, a); break;
+            case 8: hipLaunchKernelGGL(combine_narrow_kernel<8>, grid, block, 0, st, a); break;
+            case 16: hipLaunchKernelGGL(combine_narrow_kernel<16>, grid, block, 0, st, a); break;
+            case 32: hipLaunchKernelGGL(combine_narrow_kernel<32>, grid, block, 0, st, a); break;
+            default: hipLaunchKernelGGL(combine_narrow_kernel<64>, grid, block, 0, st, a); break;
+        }
+        return hipGetLastError();
+    }
 #if EP_CMB_ROWS
     if (a.K <= 8) {
         const int nch = (2 * a.H + kChunkPayload - 1) / kChunkPayload;

@@ -9,9 +9,10 @@
 // (hidden, scales, source index, top-k ids and weights; NVL receivers write
 // recv_x[row] and recv_x_scales[row * H/128]).
 //
-// Mapping on CDNA4: each source token's row is cut into EP_DSP_SPLIT column
+// Mapping on CDNA4: each source token's row is cut into `split` column
 // slices of whole 128-byte lines, one wave64 per slice, four waves per
-// workgroup. A wave loads its slice into VGPRs (up to 16 16-byte vectors per
+// workgroup (split = EP_DSP_SPLIT, 4, for rows of 2,048 bf16 values and
+// more; fewer for narrower rows, so that a slice fills a wave's 64 lanes). A wave loads its slice into VGPRs (up to 16 16-byte vectors per
 // lane per pass), then streams it to each destination row with non-temporal
 // 16-byte stores: one HBM read, D writes, no LDS round trip. Destinations
 // are the lanes k whose slot differs from every earlier lane's (the rank
@@ -39,7 +40,7 @@
 #define EP_DSP_MINB 1       // minimum resident workgroups per CU (launch bound)
 #endif
 #ifndef EP_DSP_SPLIT
-#define EP_DSP_SPLIT 4      // waves per token: the row is cut into this many column slices
+#define EP_DSP_SPLIT 4      // most waves per token: the row is cut into this many column slices
 #endif
 #ifndef EP_DSP_PERSIST
 #define EP_DSP_PERSIST 0    // persistent, software-pipelined kernel (experiment)
@@ -85,6 +86,7 @@ struct DispatchArgs {
     float* rw;
     int64_t cap;
     uint32_t* err;
+    int split;              // waves (column slices) per token
 };
 
 // Vectors of one wave's column slice of a row of `nvec` vectors: a multiple of
@@ -92,18 +94,18 @@ struct DispatchArgs {
 // receive row whose bytes are a multiple of 128 (the last slice is shorter).
 // Slices that split lines cost 16-22% (H = 7232: 115.7 vs 100.1 us; H =
 // 4160 at 16,384 tokens: 288.9 vs 236.6 us).
-__host__ __device__ __forceinline__ int slice_vecs(int64_t nvec) {
-    return (int)((((nvec + EP_DSP_SPLIT - 1) / EP_DSP_SPLIT) + 7) & ~(int64_t)7);
+__host__ __device__ __forceinline__ int slice_vecs(int64_t nvec, int split) {
+    return (int)((((nvec + split - 1) / split) + 7) & ~(int64_t)7);
 }
 
 // Copy one row of `row_bytes` (multiple of 16) bytes from src to the rows
 // dst + slot_k * row_bytes of every destination lane k in `dest`.
 template <int NV>
 __device__ __forceinline__ void fan_out_row(const uint8_t* src, int64_t row_bytes, uint8_t* dst,
-                                            uint64_t dest, int slot, int part) {
+                                            uint64_t dest, int slot, int part, int split) {
     const int lane = lane_id();
     const int nvec_all = (int)(row_bytes / 16);
-    const int per = slice_vecs(nvec_all);
+    const int per = slice_vecs(nvec_all, split);
     const int v0 = min(nvec_all, part * per);
     const int nvec = min(nvec_all, v0 + per);
     for (int base = v0; base < nvec; base += kWave * NV) {
@@ -129,7 +131,7 @@ template <int NV>
 __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(DispatchArgs a) {
     const int lane = lane_id();
     const int gw = blockIdx.x * kDspWaves + wave_in_block();
-    const int t = gw / EP_DSP_SPLIT, part = gw % EP_DSP_SPLIT;
+    const int t = gw / a.split, part = gw % a.split;
     if (t >= a.T) return;
 
     // Lanes 0..K-1 hold this token's slots; a lane is a destination if its
@@ -153,9 +155,9 @@ __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(Disp
     if (!dest) return;
 
     if (a.x && a.rx)
-        fan_out_row<NV>(a.x + (int64_t)t * a.H * 2, (int64_t)a.H * 2, a.rx, dest, s, part);
+        fan_out_row<NV>(a.x + (int64_t)t * a.H * 2, (int64_t)a.H * 2, a.rx, dest, s, part, a.split);
     if (a.x_fp8 && a.rfp8)
-        fan_out_row<NV>(a.x_fp8 + (int64_t)t * a.H, a.H, a.rfp8, dest, s, part);
+        fan_out_row<NV>(a.x_fp8 + (int64_t)t * a.H, a.H, a.rfp8, dest, s, part, a.split);
     if (part != 0) return;  // scales and metadata: written once per row
     if (a.x_scales && a.rscales) {
         const int ns = a.H / 128;
@@ -200,8 +202,8 @@ template <int NV>
 __device__ __forceinline__ void load_item(const DispatchArgs& a, int item, Item& it, u32x4 (&v)[NV],
                                           u32x4 (&f)[NV]) {
     const int lane = lane_id();
-    it.t = item / EP_DSP_SPLIT;
-    it.part = item % EP_DSP_SPLIT;
+    it.t = item / a.split;
+    it.part = item % a.split;
     it.s = -1;
     it.e = -1;
     it.wk = 0.f;
@@ -213,7 +215,7 @@ __device__ __forceinline__ void load_item(const DispatchArgs& a, int item, Item&
     if (a.x && a.rx) {
         const int64_t row_bytes = (int64_t)a.H * 2;
         const int nvec_all = (int)(row_bytes / 16);
-        const int per = slice_vecs(nvec_all);
+        const int per = slice_vecs(nvec_all, a.split);
         const int v0 = min(nvec_all, it.part * per), v1 = min(nvec_all, v0 + per);
         const uint8_t* src = a.x + (int64_t)it.t * row_bytes;
 #pragma unroll
@@ -225,7 +227,7 @@ __device__ __forceinline__ void load_item(const DispatchArgs& a, int item, Item&
     if (a.x_fp8 && a.rfp8) {
         const int64_t row_bytes = a.H;
         const int nvec_all = (int)(row_bytes / 16);
-        const int per = slice_vecs(nvec_all);
+        const int per = slice_vecs(nvec_all, a.split);
         const int v0 = min(nvec_all, it.part * per), v1 = min(nvec_all, v0 + per);
         const uint8_t* src = a.x_fp8 + (int64_t)it.t * row_bytes;
 #pragma unroll
@@ -238,10 +240,10 @@ __device__ __forceinline__ void load_item(const DispatchArgs& a, int item, Item&
 
 template <int NV>
 __device__ __forceinline__ void store_slice(const u32x4 (&v)[NV], int64_t row_bytes, uint8_t* dst,
-                                            uint64_t dest, int slot, int part) {
+                                            uint64_t dest, int slot, int part, int split) {
     const int lane = lane_id();
     const int nvec_all = (int)(row_bytes / 16);
-    const int per = slice_vecs(nvec_all);
+    const int per = slice_vecs(nvec_all, split);
     const int v0 = min(nvec_all, part * per), v1 = min(nvec_all, v0 + per);
     for (uint64_t m = dest; m; m &= m - 1) {
         const int k = __ffsll((unsigned long long)m) - 1;
@@ -267,8 +269,8 @@ __device__ __forceinline__ void store_item(const DispatchArgs& a, const Item& it
     if (over && it.part == 0) report(a.err, EP_DEVERR_CAPACITY);
     const uint64_t dest = __ballot(first && !over);
     if (!dest) return;
-    if (a.x && a.rx) store_slice<NV>(v, (int64_t)a.H * 2, a.rx, dest, it.s, it.part);
-    if (a.x_fp8 && a.rfp8) store_slice<NV>(f, a.H, a.rfp8, dest, it.s, it.part);
+    if (a.x && a.rx) store_slice<NV>(v, (int64_t)a.H * 2, a.rx, dest, it.s, it.part, a.split);
+    if (a.x_fp8 && a.rfp8) store_slice<NV>(f, a.H, a.rfp8, dest, it.s, it.part, a.split);
     if (it.part != 0) return;
     if (a.x_scales && a.rscales) {
         const int ns = a.H / 128;
@@ -350,11 +352,15 @@ hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_token
     a.rw = rv.topk_weights;
     a.cap = rv.capacity;
     a.err = reinterpret_cast<uint32_t*>(ws + W.err);
-    const int64_t waves = (int64_t)s.T * EP_DSP_SPLIT;
+    // Slices per token: EP_DSP_SPLIT, halved while a slice of the widest
+    // present row would not fill a wave's 64 lanes (narrow rows).
+    const int64_t widest = tk.x ? 2 * (int64_t)s.H : (int64_t)s.H;
+    a.split = EP_DSP_SPLIT;
+    while (a.split > 1 && slice_vecs(widest / 16, a.split) < kWave) a.split = (a.split + 1) / 2;
+    const int64_t waves = (int64_t)s.T * a.split;
     const dim3 grid((unsigned)((waves + kDspWaves - 1) / kDspWaves)), block(kDspThreads);
     // Vectors per lane held in registers: enough for the widest present slice.
-    const int64_t widest = tk.x ? 2 * (int64_t)s.H : (int64_t)s.H;
-    const int64_t slice = slice_vecs(widest / 16);
+    const int64_t slice = slice_vecs(widest / 16, a.split);
     const int64_t per_lane = (slice + kWave - 1) / kWave;
 #if EP_DSP_PERSIST
     if (per_lane <= 4 && waves <= INT32_MAX) {

@@ -301,7 +301,9 @@ def test_combine_full_size(name):
 
 @pytest.mark.parametrize("T,H,K", [(1, 8, 1), (77, 1032, 3), (300, 264, 2), (129, 512, 5),
                                    (64, 2048, 16), (33, 128, 24), (40, 512, 64),
-                                   (40, 16384, 8), (12, 65536, 4)])
+                                   (40, 16384, 8), (12, 65536, 4),
+                                   # narrow rows, several tokens per wave
+                                   (77, 128, 8), (1001, 64, 3), (5, 8, 8), (333, 256, 8), (65, 24, 7)])
 def test_combine_edges(T, H, K):
     rng = np.random.default_rng(T + H + K)
     rows = 3 * T + 1
@@ -322,13 +324,15 @@ def test_combine_edges(T, H, K):
     assert ep.ep_check_errors(ws) == 0
 
 
-def test_combine_special_values():
+@pytest.mark.parametrize("H", [264, 256, 40])
+def test_combine_special_values(H):
     """bf16 rows and fp32 weights holding +-0, +-Inf, NaN with several
     payloads, subnormals, the largest finite values and products that
     overflow: the GPU's fused multiply-adds (subnormals kept, no flush to
-    zero) and its bf16 rounding (NaN -> 0x7FC0) match the oracle bit for bit."""
+    zero) and its bf16 rounding (NaN -> 0x7FC0) match the oracle bit for bit
+    (H = 256 and 40: the narrow-row kernel, several tokens per wave)."""
     rng = np.random.default_rng(8)
-    T, H, K, rows = 96, 264, 6, 200
+    T, K, rows = 96, 6, 200
     specials16 = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81, 0x0001, 0x8001,
                            0x007F, 0x0080, 0x7F7F, 0xFF7F, 0x3F80, 0xBF80], np.uint16)
     y = synth.random_bf16_rows(rows, H, seed=9)
