@@ -221,7 +221,7 @@ int ep_hierarchical_dispatch_fused(const ep_shape* shape, const ep_layout* layou
         return EP_ERR_ARG;
     ep_fused_opts o = {0, 0, 0, 0};
     if (opts) o = *opts;
-    const int tile = o.tile_tokens ? o.tile_tokens : 16;
+    const int tile = o.tile_tokens ? o.tile_tokens : kFusedDefaultTile;
     if (tile < kFusedMinTile || tile > kFusedMaxTile || (o.test_flags & ~EP_FUSED_WITHHOLD)) return EP_ERR_ARG;
     const uint32_t timeout = o.timeout_us ? o.timeout_us : 100000u;
     const int withhold = (o.test_flags & EP_FUSED_WITHHOLD) ? o.withhold_batch : -1;

@@ -38,6 +38,10 @@ constexpr int kPieceIters = 16;  // wave iterations (2 blocks each) held in VGPR
 #define EP_SO_SPLIT 4  // scale-out: waves per token, each writing a run of the record's blocks (measured best of 1, 2, 4)
 #endif
 constexpr int kSoSplit = EP_SO_SPLIT;
+#ifndef EP_FUSED_WAVE
+#define EP_FUSED_WAVE 0  // fused kernel: each wave takes its own batches (else each workgroup;
+                         // measured slower: the counters' atomics serialise at small batches)
+#endif
 #ifndef EP_FUSED_COHERENT
 #define EP_FUSED_COHERENT 1  // fused kernel: device-scope stores and loads of group rows (else fences)
 #endif
@@ -372,6 +376,98 @@ __device__ __forceinline__ uint32_t flag_load(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Take the next job: a published batch to forward if there is one, else a
+// batch to produce, else (production all handed out) the next batch to
+// forward, to be waited for. kind: 0 produce, 1 forward (flag seen), 2
+// forward (wait), 3 done. Called by one thread.
+__device__ __forceinline__ int take_job(const FusedArgs& f, int& job) {
+    const uint32_t fb = flag_load(&f.ctr[1]);
+    if ((int)fb < f.nbatch && flag_load(&f.flags[fb]) == f.h.epoch) {
+        uint32_t want = fb;
+        if (__hip_atomic_compare_exchange_strong(&f.ctr[1], &want, fb + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+            job = (int)fb;
+            return 1;
+        }
+    }
+    if (flag_load(&f.ctr[0]) < (uint32_t)f.nbatch) {
+        const uint32_t b = atomicAdd(&f.ctr[0], 1u);
+        if ((int)b < f.nbatch) {
+            job = (int)b;
+            return 0;
+        }
+    }
+    const uint32_t b = atomicAdd(&f.ctr[1], 1u);
+    if ((int)b < f.nbatch) {
+        job = (int)b;
+        return 2;
+    }
+    return 3;
+}
+
+// Wait (one thread) until batch `job`'s flag is out, at most f.timeout
+// wall-clock ticks; false (and EP_DEVERR_TIMEOUT) if it never comes.
+__device__ __forceinline__ bool wait_batch(const FusedArgs& f, int job) {
+    const uint64_t start = (uint64_t)wall_clock64();
+    for (;;) {
+        if (flag_load(&f.flags[job]) == f.h.epoch) return true;
+        if ((uint64_t)wall_clock64() - start > f.timeout) break;
+        __builtin_amdgcn_s_sleep(8);
+    }
+    report(f.h.err, EP_DEVERR_TIMEOUT);
+    return false;
+}
+
+// The group rows of token t, forwarded in ascending lane order (the first
+// lane of each group).
+template <bool DEVICE_LOADS>
+__device__ __forceinline__ void forward_token(const HierArgs& a, int t) {
+    const int lane = lane_id();
+    int gs = -1, g = -1;
+    if (lane < a.K) {
+        gs = a.group_slot[(int64_t)t * a.K + lane];
+        const int64_t e = a.topk[(int64_t)t * a.K + lane];
+        if (gs >= 0 && expert_ok(e, a.E)) g = ((int)e / a.epr) / a.P;
+    }
+    bool first = gs >= 0 && g >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int sj = readlane(gs, j);
+        if (j < lane && sj == gs) first = false;
+    }
+    for (uint64_t m = __ballot(first && gs < a.group_cap); m; m &= m - 1) {
+        const int k = __ffsll((unsigned long long)m) - 1;
+        forward_row<DEVICE_LOADS>(a, readlane(gs, k), readlane(g, k), t);
+    }
+}
+
+#if EP_FUSED_WAVE
+// Each wave takes its own jobs: no barrier, no LDS; a batch is written (or
+// forwarded) by one wave, and the flag is stored by that wave's lane 0 after
+// the wave's stores are acknowledged.
+__global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) {
+    const HierArgs& a = f.h;
+    const int lane = lane_id();
+    for (;;) {
+        int kind = 3, job = 0;
+        if (lane == 0) kind = take_job(f, job);
+        kind = readlane(kind, 0);
+        job = readlane(job, 0);
+        if (kind == 3) return;
+        const int t0 = job * f.tile, t1 = min(a.T, t0 + f.tile);
+        if (kind == 0) {
+            for (int t = t0; t < t1; ++t) scaleout_token<1, kPieceIters, kStoreDevice>(a, t, 0);
+            wait_vmem();
+            if (lane == 0 && job != f.withhold)
+                __hip_atomic_store(&f.flags[job], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            continue;
+        }
+        int ok = 1;
+        if (kind == 2 && lane == 0) ok = wait_batch(f, job) ? 1 : 0;
+        if (!readlane(ok, 0)) continue;
+        for (int t = t0; t < t1; ++t) forward_token<true>(a, t);
+    }
+}
+#else
 __global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) {
     const HierArgs& a = f.h;
     __shared__ int sh_job, sh_kind;  // kind: 0 produce, 1 forward (flag seen), 2 forward (wait), 3 done
@@ -488,6 +584,8 @@ __global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) 
     }
 }
 
+#endif  // EP_FUSED_WAVE
+
 HierArgs hier_args(const ep_shape& s, const ep_tokens& tk, uint32_t epoch, char* ws) {
     const WsLayout W = ws_layout(s);
     int seg = EP_SEG_BF16 | (tk.x_fp8 ? EP_SEG_FP8 : 0) | (tk.x_scales ? EP_SEG_SCALES : 0);
@@ -590,7 +688,8 @@ hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tok
     f.timeout = (uint64_t)timeout_us * (uint64_t)(d.rate_khz > 0 ? d.rate_khz : 100000) / 1000u;
     // No more workgroups than are resident at once (more would find no work).
     const int resident = std::max(1, d.cus * std::max(1, d.per_cu));
-    const int blocks = std::min(resident, std::max(1, 2 * f.nbatch));
+    const int jobs_per_block = EP_FUSED_WAVE ? kWavesPerBlock : 1;
+    const int blocks = std::min(resident, std::max(1, (2 * f.nbatch + jobs_per_block - 1) / jobs_per_block));
     hipLaunchKernelGGL(fused_reset_kernel, dim3(1), dim3(kBlockThreads), 0, st, f.ctr, f.flags, f.nbatch);
     hipLaunchKernelGGL(fused_hier_kernel, dim3(blocks), dim3(kBlockThreads), 0, st, f);
     return hipGetLastError();

@@ -85,7 +85,8 @@ def test_fused_small_first():
 
 @pytest.mark.parametrize("T,H,K,E,R,G,tile,fp8", [
     (1000, 512, 6, 64, 16, 4, 64, False),     # ragged last batch
-    (1000, 512, 6, 64, 16, 4, 4, False),      # smallest batches
+    (1000, 512, 6, 64, 16, 4, 4, False),      # small batches
+    (300, 256, 4, 32, 8, 4, 1, False),        # one token per batch
     (50, 512, 6, 64, 16, 4, 64, False),       # one batch holds every token
     (777, 1024, 8, 128, 32, 8, 16, True),     # FP8 + scales, many small batches
     (300, 512, 4, 32, 8, 1, 32, False),       # one group holding every rank
