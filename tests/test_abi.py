@@ -96,6 +96,28 @@ def test_null_and_misaligned_arguments_rejected_before_launch(lib):
     assert ep.ep_status_string(0) == "ok"
 
 
+def test_fused_options_checked_before_launch(lib):
+    """The fused two-level dispatch refuses batch sizes outside 1..64, unknown
+    test flags and epoch 0 on the host; with T = 0 it enqueues nothing."""
+    s = ep.make_shape(128, 256, 4, 32, 8, 4)
+    n = ep.ep_workspace_bytes(s)
+    ws = 0x100000
+    L = ep.ep_layout(None, None, None, None, None, 0x3000, None, None, 0x4000, 0x5000, None)
+    tk = ep.ep_tokens(0x6000, None, None, 0x7000, 0x8000)
+
+    def call(opts, epoch=3):
+        return lib.ep_hierarchical_dispatch_fused(ctypes.byref(s), ctypes.byref(L), ctypes.byref(tk), epoch,
+                                                  0x10000, 10, 0x20000, 10, opts, ws, n, None)
+
+    assert call(ctypes.byref(ep.ep_fused_opts(65, 0, 0, 0))) == ep.EP_ERR_ARG
+    assert call(ctypes.byref(ep.ep_fused_opts(-1, 0, 0, 0))) == ep.EP_ERR_ARG
+    assert call(ctypes.byref(ep.ep_fused_opts(16, 0, 2, 0))) == ep.EP_ERR_ARG  # unknown test flag
+    assert call(None, epoch=0) == ep.EP_ERR_ARG
+    z = ep.make_shape(0, 256, 4, 32, 8, 4)
+    assert lib.ep_hierarchical_dispatch_fused(ctypes.byref(z), ctypes.byref(L), ctypes.byref(tk), 3, None, 0,
+                                              None, 0, None, ws, ep.ep_workspace_bytes(z), None) == ep.EP_OK
+
+
 def test_zero_tokens_dispatch_and_combine_enqueue_nothing(lib):
     """With T = 0 there is nothing to read or write: both calls succeed
     without touching the device (so this runs without a GPU)."""
