@@ -98,30 +98,40 @@ __host__ __device__ __forceinline__ int slice_vecs(int64_t nvec, int split) {
     return (int)((((nvec + split - 1) / split) + 7) & ~(int64_t)7);
 }
 
-// Copy one row of `row_bytes` (multiple of 16) bytes from src to the rows
-// dst + slot_k * row_bytes of every destination lane k in `dest`.
+// Vectors [v0, v1) of a row of `nvec` vectors: column slice `part` of `split`.
+__device__ __forceinline__ void slice_range(int nvec, int part, int split, int& v0, int& v1) {
+    const int per = (((nvec + split - 1) / split) + 7) & ~7;  // slice_vecs in 32-bit arithmetic
+    v0 = min(nvec, part * per);
+    v1 = min(nvec, v0 + per);
+}
+
+// One pass of a slice: v[j] = vector base + j * 64 + lane of the row at src.
+// Every load is issued; addresses past the slice are clamped to its last
+// vector (or to vector 0 of an empty slice) and the stores mask them.
+template <int NV>
+__device__ __forceinline__ void load_pass(const uint8_t* src, int base, int v1, u32x4 (&v)[NV]) {
+    const int lane = lane_id();
+    const int last = max(v1 - 1, 0);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = ld_src(src + (int64_t)min(base + j * kWave + lane, last) * 16);
+}
+
+// Copy vectors [v0, v1) of the row at src to the rows dst + slot_k * row_bytes
+// of every destination lane k in `dest`. v holds the first pass (loaded by
+// the caller); later passes of slices wider than 64 NV vectors load here.
 template <int NV>
 __device__ __forceinline__ void fan_out_row(const uint8_t* src, int64_t row_bytes, uint8_t* dst,
-                                            uint64_t dest, int slot, int part, int split) {
+                                            uint64_t dest, int slot, int v0, int v1, u32x4 (&v)[NV]) {
     const int lane = lane_id();
-    const int nvec_all = (int)(row_bytes / 16);
-    const int per = slice_vecs(nvec_all, split);
-    const int v0 = min(nvec_all, part * per);
-    const int nvec = min(nvec_all, v0 + per);
-    for (int base = v0; base < nvec; base += kWave * NV) {
-        u32x4 v[NV];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int i = base + j * kWave + lane;
-            if (i < nvec) v[j] = ld_src(src + (int64_t)i * 16);
-        }
+    for (int base = v0; base < v1; base += kWave * NV) {
+        if (base != v0) load_pass<NV>(src, base, v1, v);
         for (uint64_t m = dest; m; m &= m - 1) {
             const int k = __ffsll((unsigned long long)m) - 1;
             uint8_t* row = dst + (int64_t)readlane(slot, k) * row_bytes;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const int i = base + j * kWave + lane;
-                if (i < nvec) st_dst(row + (int64_t)i * 16, v[j]);
+                if (i < v1) st_dst(row + (int64_t)i * 16, v[j]);
             }
         }
     }
@@ -134,16 +144,29 @@ __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(Disp
     const int t = gw / a.split, part = gw % a.split;
     if (t >= a.T) return;
 
-    // Lanes 0..K-1 hold this token's slots; a lane is a destination if its
-    // slot is valid and no lower lane has the same slot (same rank).
-    int s = -1;
-    int64_t e = -1;
-    float wk = 0.f;
-    if (lane < a.K) {
-        s = a.slot[(int64_t)t * a.K + lane];
-        e = a.topk[(int64_t)t * a.K + lane];
-        if (a.topk_w) wk = a.topk_w[(int64_t)t * a.K + lane];
+    // Lanes 0..K-1 hold this token's slots, ids and weights (the other lanes
+    // load lane 0's and drop them). The first pass of the bf16 slice is
+    // requested together with them, so the wave waits for one round trip,
+    // not two (measured 1-2 us at 4,096 tokens x 7,168).
+    const int kl = lane < a.K ? lane : 0;
+    int s = a.slot[(int64_t)t * a.K + kl];
+    int64_t e = a.topk[(int64_t)t * a.K + kl];
+    float wk = a.topk_w ? a.topk_w[(int64_t)t * a.K + kl] : 0.f;
+    const bool bf16 = a.x && a.rx;
+    const int64_t xrow = (int64_t)a.H * 2;
+    const uint8_t* xsrc = bf16 ? a.x + (int64_t)t * xrow : nullptr;
+    int xv0 = 0, xv1 = 0;
+    slice_range((int)(xrow / 16), part, a.split, xv0, xv1);
+    u32x4 v[NV];
+    if (bf16) load_pass<NV>(xsrc, xv0, xv1, v);
+    if (lane >= a.K) {
+        s = -1;
+        e = -1;
+        wk = 0.f;
     }
+
+    // A lane is a destination if its slot is valid and no lower lane has the
+    // same slot (same rank).
     bool first = s >= 0;
     for (int j = 0; j < a.K; ++j) {
         const int sj = readlane(s, j);
@@ -154,19 +177,23 @@ __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(Disp
     const uint64_t dest = __ballot(first && !over);
     if (!dest) return;
 
-    if (a.x && a.rx)
-        fan_out_row<NV>(a.x + (int64_t)t * a.H * 2, (int64_t)a.H * 2, a.rx, dest, s, part, a.split);
-    if (a.x_fp8 && a.rfp8)
-        fan_out_row<NV>(a.x_fp8 + (int64_t)t * a.H, a.H, a.rfp8, dest, s, part, a.split);
+    if (bf16) fan_out_row<NV>(xsrc, xrow, a.rx, dest, s, xv0, xv1, v);
+    if (a.x_fp8 && a.rfp8) {
+        const uint8_t* fsrc = a.x_fp8 + (int64_t)t * a.H;
+        int fv0 = 0, fv1 = 0;
+        slice_range(a.H / 16, part, a.split, fv0, fv1);
+        load_pass<NV>(fsrc, fv0, fv1, v);
+        fan_out_row<NV>(fsrc, a.H, a.rfp8, dest, s, fv0, fv1, v);
+    }
     if (part != 0) return;  // scales and metadata: written once per row
     if (a.x_scales && a.rscales) {
         const int ns = a.H / 128;
         for (int base = 0; base < ns; base += kWave) {
             const int i = base + lane;
-            const float v = i < ns ? a.x_scales[(int64_t)t * ns + i] : 0.f;
+            const float sv = i < ns ? a.x_scales[(int64_t)t * ns + i] : 0.f;
             for (uint64_t m = dest; m; m &= m - 1) {
                 const int k = __ffsll((unsigned long long)m) - 1;
-                if (i < ns) a.rscales[(int64_t)readlane(s, k) * ns + i] = v;
+                if (i < ns) a.rscales[(int64_t)readlane(s, k) * ns + i] = sv;
             }
         }
     }
