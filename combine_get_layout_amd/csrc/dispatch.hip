@@ -210,6 +210,58 @@ __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(Disp
     }
 }
 
+// Narrow rows (every present payload row at most 32 vectors: H <= 256 for
+// the bf16 row) with K <= 8: one token per wave would leave most lanes idle,
+// so a wave holds TPW tokens, one per group of G = 64 / TPW lanes, and lane
+// v of a group holds vector v of each payload row of its token (G >= K, so
+// lanes v < K also hold the token's id and weight of lane v). Every lane
+// reads its token's K slots (the same addresses within a group) and walks
+// the destinations in ascending k: one store instruction then writes the
+// vector of every group whose token has k as a destination.
+template <int TPW>
+__global__ __launch_bounds__(kDspThreads) void dispatch_narrow_kernel(DispatchArgs a) {
+    constexpr int G = kWave / TPW;
+    const int lane = lane_id();
+    const int v = lane % G;
+    const int t = (blockIdx.x * kDspWaves + wave_in_block()) * TPW + lane / G;
+    if (t >= a.T) return;  // no cross-lane operations below
+    int s[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s[k] = a.slot[(int64_t)t * a.K + min(k, a.K - 1)];
+    const int kv = min(v, a.K - 1);
+    const int64_t e = a.topk[(int64_t)t * a.K + kv];
+    const float wk = a.topk_w ? a.topk_w[(int64_t)t * a.K + kv] : 0.f;
+    const int nvx = a.H / 8, nvf = a.H / 16, ns = a.H / 128;
+    const bool bf16 = a.x && a.rx, fp8 = a.x_fp8 && a.rfp8, scales = a.x_scales && a.rscales && ns > 0;
+    u32x4 vx = {0u, 0u, 0u, 0u}, vf = {0u, 0u, 0u, 0u};
+    float sc = 0.f;
+    if (bf16) vx = ld_src(a.x + (int64_t)t * a.H * 2 + (int64_t)min(v, nvx - 1) * 16);
+    if (fp8) vf = ld_src(a.x_fp8 + (int64_t)t * a.H + (int64_t)min(v, nvf - 1) * 16);
+    if (scales) sc = a.x_scales[(int64_t)t * ns + min(v, ns - 1)];
+    const int32_t id = expert_ok(e, a.E) ? (int32_t)e : -1;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (k >= a.K) break;
+        bool first = s[k] >= 0;  // a rank reached by an earlier lane is written once
+#pragma unroll
+        for (int j = 0; j < k; ++j) first = first && s[j] != s[k];
+        if (!first) continue;
+        if (s[k] >= a.cap) {
+            if (v == 0) report(a.err, EP_DEVERR_CAPACITY);
+            continue;
+        }
+        const int64_t row = s[k];
+        if (bf16 && v < nvx) st_dst(a.rx + row * a.H * 2 + (int64_t)v * 16, vx);
+        if (fp8 && v < nvf) st_dst(a.rfp8 + row * a.H + (int64_t)v * 16, vf);
+        if (scales && v < ns) a.rscales[row * ns + v] = sc;
+        if (a.rsrc && v == 0) a.rsrc[row] = t;
+        if (v < a.K) {
+            if (a.ridx) a.ridx[row * a.K + v] = id;
+            if (a.rw && a.topk_w) a.rw[row * a.K + v] = wk;
+        }
+    }
+}
+
 // Persistent form (EP_DSP_PERSIST, off by default: measured slower than the
 // one-shot kernel on every workload). A grid of at most the resident waves;
 // wave w takes the items (token, slice) w, w + W, w + 2W, ... (W = waves in
@@ -379,8 +431,31 @@ hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_token
     a.rw = rv.topk_weights;
     a.cap = rv.capacity;
     a.err = reinterpret_cast<uint32_t*>(ws + W.err);
+    // Narrow rows: several tokens per wave, one per power-of-two group of
+    // lanes wide enough for the widest present row (in 16-byte vectors) and
+    // for the K lanes of the metadata.
+    {
+        int widest_v = 1;
+        if (tk.x) widest_v = std::max(widest_v, s.H / 8);
+        if (tk.x_fp8) widest_v = std::max(widest_v, s.H / 16);
+        if (tk.x_scales) widest_v = std::max(widest_v, s.H / 128);
+        if (s.K <= 8 && widest_v <= kWave / 2) {
+            const int g = std::max(widest_v, s.K);
+            int G = 8;  // groups of 8, 16 or 32 lanes: 8, 4 or 2 tokens per wave
+            while (G < g) G *= 2;
+            const int tpw = kWave / G;
+            const int64_t nw = ((int64_t)s.T + tpw - 1) / tpw;
+            const dim3 g2((unsigned)((nw + kDspWaves - 1) / kDspWaves)), b2(kDspThreads);
+            switch (tpw) {
+                case 2: hipLaunchKernelGGL(dispatch_narrow_kernel<2>, g2, b2, 0, st, a); break;
+                case 4: hipLaunchKernelGGL(dispatch_narrow_kernel<4>, g2, b2, 0, st, a); break;
+                default: hipLaunchKernelGGL(dispatch_narrow_kernel<8>, g2, b2, 0, st, a); break;
+            }
+            return hipGetLastError();
+        }
+    }
     // Slices per token: EP_DSP_SPLIT, halved while a slice of the widest
-    // present row would not fill a wave's 64 lanes (narrow rows).
+    // present row would not fill a wave's 64 lanes.
     const int64_t widest = tk.x ? 2 * (int64_t)s.H : (int64_t)s.H;
     a.split = EP_DSP_SPLIT;
     while (a.split > 1 && slice_vecs(widest / 16, a.split) < kWave) a.split = (a.split + 1) / 2;

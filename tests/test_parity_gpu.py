@@ -210,6 +210,47 @@ def test_dispatch_edges(T, H, K, E, R):
     check_dispatch(recv, D, N)
 
 
+@pytest.mark.parametrize("T,H,K,E,R,segs", [
+    # rows of at most 32 vectors and K <= 8: 2, 4 or 8 tokens per wave
+    (1000, 128, 8, 64, 16, "x+fp8+scales"), (77, 256, 3, 24, 6, "x+fp8+scales"),
+    (999, 64, 6, 32, 32, "x"), (5, 32, 8, 8, 8, "x"), (130, 8, 1, 4, 4, "x"),
+    (333, 512, 5, 40, 10, "fp8"), (257, 256, 8, 16, 2, "scales")])
+def test_dispatch_narrow_rows(T, H, K, E, R, segs):
+    """The several-tokens-per-wave dispatch: skipped (-1) and repeated lanes,
+    every payload piece on its own, rows compared byte for byte."""
+    w = synth.Workload("narrow", T, H, E, R, 1, K, "uniform")
+    rng = np.random.default_rng(T * 31 + H * 7 + K)
+    x = rng.integers(0, 65536, size=(T, H)).astype(np.uint16)
+    topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
+    topk[::5, -1] = topk[::5, 0]  # repeated experts in some tokens
+    inp = dict(x=x, topk_idx=topk, topk_w=rng.standard_normal((T, K)).astype(np.float32))
+    want_x, want_fp8, want_sc = "x" in segs.split("+"), "fp8" in segs, "scales" in segs
+    if want_fp8 or want_sc:
+        inp["x_fp8"] = rng.integers(0, 256, size=(T, H)).astype(np.uint8)
+        inp["x_scales"] = rng.standard_normal((T, max(H // 128, 1))).astype(np.float32)[:, :H // 128]
+    shape, L, ws, tk = run_layout(w, inp["topk_idx"])
+    N = int(host(L["rank_offsets"])[-1])
+    tokens = dict(topk_idx=tk, topk_weights=dev(inp["topk_w"]))
+    if want_x:
+        tokens["x"] = dev(inp["x"])
+    if want_fp8:
+        tokens["x_fp8"] = dev(inp["x_fp8"])
+    if want_sc:
+        tokens["x_scales"] = dev(np.ascontiguousarray(inp["x_scales"]))
+    recv = ep.alloc_recv(shape, N, x=want_x, fp8=want_fp8, scales=want_sc, meta=True)
+    for t in recv.values():
+        poison(t)
+    ep.ep_dispatch(shape, L, tokens, recv, N, ws)
+    torch.cuda.synchronize()
+    O = oracle.layout(inp["topk_idx"], E, R, 1)
+    D = oracle.dispatch(inp["topk_idx"], E, R, O["rank_offsets"], x=inp["x"] if want_x else None,
+                        x_fp8=inp["x_fp8"] if want_fp8 else None,
+                        x_scales=np.ascontiguousarray(inp["x_scales"]) if want_sc else None,
+                        topk_w=inp["topk_w"])
+    check_dispatch(recv, D, N)
+    assert ep.ep_check_errors(ws) == 0
+
+
 @pytest.mark.parametrize("segs", ["fp8+scales", "x", "scales", "meta", "fp8"])
 def test_dispatch_segment_subsets(segs):
     """Every payload piece is optional on its own; the metadata too."""
