@@ -343,6 +343,13 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(
                 const int kk = min(k, a.K - 1);
                 return a.y + (int64_t)(((um >> k) & 1) ? readlane(s, kk) : s_any) * a.stride;
             };
+            // A repeated row taken from `keep` is not read again; its load
+            // slot reads the workspace's first 256 bytes instead (the error
+            // words: in bounds and cached). Every step then issues the same
+            // loads whichever rows repeat, so the compiler waits for row k
+            // alone before summing it instead of for everything in flight
+            // (a request under a branch made it wait for all loads).
+            const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.err) + (lane & 15) * 16;
             {
                 const uint8_t* r0 = row_of(0);
 #pragma unroll
@@ -350,10 +357,11 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(
             }
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
-                if (k + 1 < KMAX && !((kept >> (k + 1)) & 1)) {
+                if (k + 1 < KMAX) {
+                    const bool again = (kept >> (k + 1)) & 1;
                     const uint8_t* rn = row_of(k + 1);
 #pragma unroll
-                    for (int j = 0; j < VPW; ++j) buf[(k + 1) & 1][j] = ld_row(rn + off[j]);
+                    for (int j = 0; j < VPW; ++j) buf[(k + 1) & 1][j] = ld_row(again ? spare : rn + off[j]);
                 }
                 const float wk = readlane_f(wt, min(k, a.K - 1));
                 const bool uk = (um >> k) & 1;

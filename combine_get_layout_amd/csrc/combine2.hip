@@ -328,28 +328,37 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_rows_kernel(Combi
                 for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
             int cur = __ffsll((unsigned long long)seq) - 1;
             uint64_t rest = seq & (seq - 1);
-            u32x4 vc[VPW], vn[VPW];
+            // Two register sets in turn (the loop is unrolled over the at
+            // most 8 usable lanes, so no set is copied into the other).
+            u32x4 vb[2][VPW];
             {
                 const uint8_t* r0 = a.y + (int64_t)readlane(s, cur & 7) * a.y_stride;
 #pragma unroll
-                for (int j = 0; j < VPW; ++j) vc[j] = ld16(r0 + off[j]);
+                for (int j = 0; j < VPW; ++j) vb[0][j] = ld16(r0 + off[j]);
             }
-            while (true) {
-                const int nxt = rest ? __ffsll((unsigned long long)rest) - 1 : -1;
-                if (nxt >= 0) {
-                    const uint8_t* rn = a.y + (int64_t)readlane(s, nxt & 7) * a.y_stride;
+            // The next row's burst is always requested; after the last row
+            // it reads the workspace's first 256 bytes (the error words: in
+            // bounds and cached). Every step then issues the same loads, so
+            // the compiler waits for the current row alone, not for the
+            // next one too (a request under a branch made it wait for all).
+            const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.err) + (lane & 15) * 16;
 #pragma unroll
-                    for (int j = 0; j < VPW; ++j) vn[j] = ld16(rn + off[j]);
+            for (int i = 0; i < KMAX; ++i) {
+                const int nxt = rest ? __ffsll((unsigned long long)rest) - 1 : -1;
+                {
+                    const uint8_t* rn = a.y + (int64_t)readlane(s, (nxt < 0 ? cur : nxt) & 7) * a.y_stride;
+#pragma unroll
+                    for (int j = 0; j < VPW; ++j) vb[(i + 1) & 1][j] = ld16(nxt >= 0 ? rn + off[j] : spare);
                 }
                 const int k = cur & 7, gi = cur >> 3;
                 const float wk = readlane_f(wt, k);
 #pragma unroll
                 for (int j = 0; j < VPW; ++j) {
-                    if (fl[j] && !flag_ok(vc[j], a.epoch)) bad |= 1u << k;
+                    if (fl[j] && !flag_ok(vb[i & 1][j], a.epoch)) bad |= 1u << k;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        acc[j][2 * q] = __builtin_fmaf(wk, bf16_lo(vc[j][q]), acc[j][2 * q]);
-                        acc[j][2 * q + 1] = __builtin_fmaf(wk, bf16_hi(vc[j][q]), acc[j][2 * q + 1]);
+                        acc[j][2 * q] = __builtin_fmaf(wk, bf16_lo(vb[i & 1][j][q]), acc[j][2 * q]);
+                        acc[j][2 * q + 1] = __builtin_fmaf(wk, bf16_hi(vb[i & 1][j][q]), acc[j][2 * q + 1]);
                     }
                 }
                 if (nxt < 0 || (nxt >> 3) != gi) {
@@ -361,8 +370,6 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_rows_kernel(Combi
                         for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
                 }
                 if (nxt < 0) break;
-#pragma unroll
-                for (int j = 0; j < VPW; ++j) vc[j] = vn[j];
                 cur = nxt;
                 rest &= rest - 1;
             }
@@ -560,7 +567,6 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combi
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
         if (posmask && live) {
-            u32x4 vc[VPW], vn[VPW];
             auto row_at = [&](int pos) {
                 int ln = 0;
 #pragma unroll
@@ -569,30 +575,34 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combi
             };
             int cur = __ffs(posmask) - 1;
             uint32_t rest = posmask & (posmask - 1);
+            // As in the group step: two register sets in turn, and the next
+            // burst always requested (the workspace's error words after the
+            // last row).
+            u32x4 vb[2][VPW];
             {
                 const uint8_t* r0 = row_at(cur);
 #pragma unroll
-                for (int j = 0; j < VPW; ++j) vc[j] = ld16(r0 + off[j]);
+                for (int j = 0; j < VPW; ++j) vb[0][j] = ld16(r0 + off[j]);
             }
-            while (true) {
-                const int nxt = rest ? __ffs(rest) - 1 : -1;
-                if (nxt >= 0) {
-                    const uint8_t* rn = row_at(nxt);
+            const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.err) + (lane & 15) * 16;
 #pragma unroll
-                    for (int j = 0; j < VPW; ++j) vn[j] = ld16(rn + off[j]);
+            for (int i = 0; i < GMAX; ++i) {
+                const int nxt = rest ? __ffs(rest) - 1 : -1;
+                {
+                    const uint8_t* rn = row_at(nxt < 0 ? cur : nxt);
+#pragma unroll
+                    for (int j = 0; j < VPW; ++j) vb[(i + 1) & 1][j] = ld16(nxt >= 0 ? rn + off[j] : spare);
                 }
 #pragma unroll
                 for (int j = 0; j < VPW; ++j) {
-                    if (fl[j] && !flag_ok(vc[j], a.epoch)) bad |= 1u << cur;
+                    if (fl[j] && !flag_ok(vb[i & 1][j], a.epoch)) bad |= 1u << cur;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        acc[j][2 * q] = acc[j][2 * q] + bf16_lo(vc[j][q]);
-                        acc[j][2 * q + 1] = acc[j][2 * q + 1] + bf16_hi(vc[j][q]);
+                        acc[j][2 * q] = acc[j][2 * q] + bf16_lo(vb[i & 1][j][q]);
+                        acc[j][2 * q + 1] = acc[j][2 * q + 1] + bf16_hi(vb[i & 1][j][q]);
                     }
                 }
                 if (nxt < 0) break;
-#pragma unroll
-                for (int j = 0; j < VPW; ++j) vc[j] = vn[j];
                 cur = nxt;
                 rest &= rest - 1;
             }
