@@ -357,6 +357,12 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
 // Counters and flags live in the workspace and are zeroed by a one-workgroup
 // kernel launched just before (stream ordered, no memset node).
 // ---------------------------------------------------------------------------
+#ifndef EP_FUSED_WPB
+#define EP_FUSED_WPB 8  // waves per workgroup of the workgroup-level fused kernel
+#endif
+constexpr int kFusedWaves = EP_FUSED_WPB;
+constexpr int kFusedThreads = kFusedWaves * kWave;
+
 struct FusedArgs {
     HierArgs h;
     int tile;               // tokens per batch
@@ -468,40 +474,15 @@ __global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) 
     }
 }
 #else
-__global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) {
+__global__ __launch_bounds__(kFusedThreads) void fused_hier_kernel(FusedArgs f) {
     const HierArgs& a = f.h;
     __shared__ int sh_job, sh_kind;  // kind: 0 produce, 1 forward (flag seen), 2 forward (wait), 3 done
     __shared__ int sh_ok;
     const int wave = wave_in_block();
-    const int lane = lane_id();
     for (;;) {
         if (threadIdx.x == 0) {
-            int kind = 3, job = 0;
-            // A published batch first, if one is waiting to be forwarded.
-            const uint32_t fb = flag_load(&f.ctr[1]);
-            if ((int)fb < f.nbatch && flag_load(&f.flags[fb]) == a.epoch) {
-                uint32_t want = fb;
-                if (__hip_atomic_compare_exchange_strong(&f.ctr[1], &want, fb + 1, __ATOMIC_RELAXED,
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-                    kind = 1;
-                    job = (int)fb;
-                }
-            }
-            if (kind == 3 && flag_load(&f.ctr[0]) < (uint32_t)f.nbatch) {
-                const uint32_t b = atomicAdd(&f.ctr[0], 1u);
-                if ((int)b < f.nbatch) {
-                    kind = 0;
-                    job = (int)b;
-                }
-            }
-            if (kind == 3 && flag_load(&f.ctr[0]) >= (uint32_t)f.nbatch) {
-                const uint32_t b = atomicAdd(&f.ctr[1], 1u);
-                if ((int)b < f.nbatch) {
-                    kind = 2;
-                    job = (int)b;
-                }
-            }
-            sh_kind = kind;
+            int job = 0;
+            sh_kind = take_job(f, job);
             sh_job = job;
         }
         __syncthreads();
@@ -510,10 +491,10 @@ __global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) 
         if (kind == 3) return;
         const int t0 = job * f.tile, t1 = min(a.T, t0 + f.tile);
         if (kind == 0) {
-            // Wave w writes whole records of tokens t0 + w, t0 + w + 4, ...
+            // Wave w writes whole records of tokens t0 + w, t0 + w + W, ... (W waves per workgroup)
             // (the kernel's register budget is set by the forward part, so a
             // wave holds a 32-block piece of the record at once).
-            for (int t = t0 + wave; t < t1; t += kWavesPerBlock)
+            for (int t = t0 + wave; t < t1; t += kFusedWaves)
                 scaleout_token<1, kPieceIters, EP_FUSED_COHERENT ? kStoreDevice : kStorePlain>(a, t, 0);
 #if EP_FUSED_COHERENT
             // Publish: the rows were stored with device scope; each wave waits
@@ -538,49 +519,19 @@ __global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) 
         // reads the batch's rows (with device-scope loads, or after an
         // agent-scope acquire fence).
         if (threadIdx.x == 0) {
-            int ok = 1;
-            if (kind == 2) {
-                const uint64_t start = (uint64_t)wall_clock64();
-                ok = 0;
-                for (;;) {
-                    if (flag_load(&f.flags[job]) == a.epoch) {
-                        ok = 1;
-                        break;
-                    }
-                    if ((uint64_t)wall_clock64() - start > f.timeout) break;
-                    __builtin_amdgcn_s_sleep(8);
-                }
-                if (!ok) report(a.err, EP_DEVERR_TIMEOUT);
-            }
+            const bool ok = kind == 1 || wait_batch(f, job);
 #if !EP_FUSED_COHERENT
             if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #endif
-            sh_ok = ok;
+            sh_ok = ok ? 1 : 0;
         }
         __syncthreads();
         const int ok = sh_ok;
         __syncthreads();
         if (!ok) continue;
         // Forward the group rows of the batch's tokens: wave w takes tokens
-        // t0 + w, t0 + w + 4, ..., and each of its groups in ascending lane
-        // order (the first lane of each group).
-        for (int t = t0 + wave; t < t1; t += kWavesPerBlock) {
-            int gs = -1, g = -1;
-            if (lane < a.K) {
-                gs = a.group_slot[(int64_t)t * a.K + lane];
-                const int64_t e = a.topk[(int64_t)t * a.K + lane];
-                if (gs >= 0 && expert_ok(e, a.E)) g = ((int)e / a.epr) / a.P;
-            }
-            bool first = gs >= 0 && g >= 0;
-            for (int j = 0; j < a.K; ++j) {
-                const int sj = readlane(gs, j);
-                if (j < lane && sj == gs) first = false;
-            }
-            for (uint64_t m = __ballot(first && gs < a.group_cap); m; m &= m - 1) {
-                const int k = __ffsll((unsigned long long)m) - 1;
-                forward_row<EP_FUSED_COHERENT != 0>(a, readlane(gs, k), readlane(g, k), t);
-            }
-        }
+        // t0 + w, t0 + w + W, ... (W waves per workgroup)
+        for (int t = t0 + wave; t < t1; t += kFusedWaves) forward_token<EP_FUSED_COHERENT != 0>(a, t);
     }
 }
 
@@ -652,7 +603,8 @@ static hipError_t fused_device_info(hipStream_t st, FusedDeviceInfo* out) {
             return e;
         if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
             return e;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu, fused_hier_kernel, kBlockThreads, 0)) !=
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu, fused_hier_kernel,
+                                                              EP_FUSED_WAVE ? kBlockThreads : kFusedThreads, 0)) !=
             hipSuccess)
             return e;
         info[dev] = d;
@@ -691,7 +643,8 @@ hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tok
     const int jobs_per_block = EP_FUSED_WAVE ? kWavesPerBlock : 1;
     const int blocks = std::min(resident, std::max(1, (2 * f.nbatch + jobs_per_block - 1) / jobs_per_block));
     hipLaunchKernelGGL(fused_reset_kernel, dim3(1), dim3(kBlockThreads), 0, st, f.ctr, f.flags, f.nbatch);
-    hipLaunchKernelGGL(fused_hier_kernel, dim3(blocks), dim3(kBlockThreads), 0, st, f);
+    hipLaunchKernelGGL(fused_hier_kernel, dim3(blocks), dim3(EP_FUSED_WAVE ? kBlockThreads : kFusedThreads), 0, st,
+                       f);
     return hipGetLastError();
 }
 

@@ -250,7 +250,7 @@ int ep_hierarchical_dispatch(const ep_shape *shape, const ep_layout *layout,
  * memset), so calls on one workspace must not overlap. opts may be NULL
  * (defaults); all-zero fields mean the defaults. */
 typedef struct ep_fused_opts {
-    int32_t tile_tokens;    /* tokens per batch, 1..64 (0: 16) */
+    int32_t tile_tokens;    /* tokens per batch, 1..64 (0: 8) */
     uint32_t timeout_us;    /* longest wait for one batch flag (0: 100000 us) */
     uint32_t test_flags;    /* EP_FUSED_WITHHOLD: batch `withhold_batch`'s flag is never
                                published, to test the bounded wait (its group rows are
