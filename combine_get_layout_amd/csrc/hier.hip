@@ -241,7 +241,7 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g,
             const int c = min(2 * j + c_half, nchunks - 1);
             const int64_t off = (int64_t)c * kChunkBytes + (int64_t)wv * 16;
             if constexpr (DEVICE_LOADS) v[j] = ld16_device(src_row, stride, off);
-            else v[j] = ld16(src_row + off);
+            else v[j] = ld16_stream(src_row + off);  // read once: non-temporal (-7 us per hier8x8 step)
         }
     }
     int32_t src, id, d_early = -1;
@@ -294,7 +294,7 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g,
                 const int c = 2 * (it0 + j) + c_half;
                 if (it0 + j < iters && c < nchunks)
                     v[j] = DEVICE_LOADS ? ld16_device(src_row, stride, chunk_lane_offset(it0 + j, lane))
-                                        : ld16(src_row + chunk_lane_offset(it0 + j, lane));
+                                        : ld16_stream(src_row + chunk_lane_offset(it0 + j, lane));
             }
         }
         for (uint64_t m = dest; m; m &= m - 1) {
