@@ -334,13 +334,15 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_rows_kernel(Combi
             {
                 const uint8_t* r0 = a.y + (int64_t)readlane(s, cur & 7) * a.y_stride;
 #pragma unroll
-                for (int j = 0; j < VPW; ++j) vb[0][j] = ld16(r0 + off[j]);
+                for (int j = 0; j < VPW; ++j) vb[0][j] = ld16_stream(r0 + off[j]);
             }
             // The next row's burst is always requested; after the last row
             // it reads the workspace's first 256 bytes (the error words: in
             // bounds and cached). Every step then issues the same loads, so
             // the compiler waits for the current row alone, not for the
             // next one too (a request under a branch made it wait for all).
+            // Rows are read once: non-temporal loads (the two-level combine
+            // at hier8x8: 915 -> 884 us).
             const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.err) + (lane & 15) * 16;
 #pragma unroll
             for (int i = 0; i < KMAX; ++i) {
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_rows_kernel(Combi
                 {
                     const uint8_t* rn = a.y + (int64_t)readlane(s, (nxt < 0 ? cur : nxt) & 7) * a.y_stride;
 #pragma unroll
-                    for (int j = 0; j < VPW; ++j) vb[(i + 1) & 1][j] = ld16(nxt >= 0 ? rn + off[j] : spare);
+                    for (int j = 0; j < VPW; ++j) vb[(i + 1) & 1][j] = ld16_stream(nxt >= 0 ? rn + off[j] : spare);
                 }
                 const int k = cur & 7, gi = cur >> 3;
                 const float wk = readlane_f(wt, k);
@@ -582,7 +584,7 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combi
             {
                 const uint8_t* r0 = row_at(cur);
 #pragma unroll
-                for (int j = 0; j < VPW; ++j) vb[0][j] = ld16(r0 + off[j]);
+                for (int j = 0; j < VPW; ++j) vb[0][j] = ld16_stream(r0 + off[j]);
             }
             const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.err) + (lane & 15) * 16;
 #pragma unroll
@@ -591,7 +593,7 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combi
                 {
                     const uint8_t* rn = row_at(nxt < 0 ? cur : nxt);
 #pragma unroll
-                    for (int j = 0; j < VPW; ++j) vb[(i + 1) & 1][j] = ld16(nxt >= 0 ? rn + off[j] : spare);
+                    for (int j = 0; j < VPW; ++j) vb[(i + 1) & 1][j] = ld16_stream(nxt >= 0 ? rn + off[j] : spare);
                 }
 #pragma unroll
                 for (int j = 0; j < VPW; ++j) {
