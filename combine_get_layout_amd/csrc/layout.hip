@@ -72,10 +72,14 @@ struct TokenIds {
     int64_t v[KMAX > 0 ? KMAX : 1];
     __device__ __forceinline__ void load(const int64_t* row, int K) {
         if constexpr (KMAX > 0) {
+            // Every load issued (lanes k >= K re-read lane K - 1; callers
+            // stop at K): loads under a branch were sunk past the LDS
+            // clearing and the barrier to their first use.
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k) v[k] = k < K ? row[k] : -1;
+            for (int k = 0; k < KMAX; ++k) v[k] = row[min(k, K - 1)];
         }
     }
+    // Callers ask for lanes k < K only.
     __device__ __forceinline__ int64_t get(const int64_t* row, int k) const {
         if constexpr (KMAX > 0) return v[k];
         else return row[k];
