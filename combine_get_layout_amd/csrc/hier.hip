@@ -387,7 +387,11 @@ __device__ __forceinline__ uint32_t flag_load(const uint32_t* p) {
 // forward, to be waited for. kind: 0 produce, 1 forward (flag seen), 2
 // forward (wait), 3 done. Called by one thread.
 __device__ __forceinline__ int take_job(const FusedArgs& f, int& job) {
+    // Both counters are read together (one round trip instead of two: a
+    // claim's device-scope accesses are its cost, several microseconds each
+    // under contention).
     const uint32_t fb = flag_load(&f.ctr[1]);
+    const uint32_t pb = flag_load(&f.ctr[0]);
     if ((int)fb < f.nbatch && flag_load(&f.flags[fb]) == f.h.epoch) {
         uint32_t want = fb;
         if (__hip_atomic_compare_exchange_strong(&f.ctr[1], &want, fb + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
@@ -396,7 +400,7 @@ __device__ __forceinline__ int take_job(const FusedArgs& f, int& job) {
             return 1;
         }
     }
-    if (flag_load(&f.ctr[0]) < (uint32_t)f.nbatch) {
+    if (pb < (uint32_t)f.nbatch) {
         const uint32_t b = atomicAdd(&f.ctr[0], 1u);
         if ((int)b < f.nbatch) {
             job = (int)b;
