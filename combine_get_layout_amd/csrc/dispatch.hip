@@ -137,7 +137,9 @@ __device__ __forceinline__ void fan_out_row(const uint8_t* src, int64_t row_byte
     }
 }
 
-template <int NV>
+// FP8: the launch moves an FP8 payload (its first pass is then loaded with
+// the bf16 one; without it the kernel holds no registers for it).
+template <int NV, bool FP8>
 __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(DispatchArgs a) {
     const int lane = lane_id();
     const int gw = blockIdx.x * kDspWaves + wave_in_block();
@@ -145,9 +147,9 @@ __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(Disp
     if (t >= a.T) return;
 
     // Lanes 0..K-1 hold this token's slots, ids and weights (the other lanes
-    // load lane 0's and drop them). The first pass of the bf16 slice is
-    // requested together with them, so the wave waits for one round trip,
-    // not two (measured 1-2 us at 4,096 tokens x 7,168).
+    // load lane 0's and drop them). The first pass of the bf16 (and FP8)
+    // slice is requested together with them, so the wave waits for one
+    // round trip, not two (measured 1-2 us at 4,096 tokens x 7,168).
     const int kl = lane < a.K ? lane : 0;
     int s = a.slot[(int64_t)t * a.K + kl];
     int64_t e = a.topk[(int64_t)t * a.K + kl];
@@ -157,8 +159,16 @@ __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(Disp
     const uint8_t* xsrc = bf16 ? a.x + (int64_t)t * xrow : nullptr;
     int xv0 = 0, xv1 = 0;
     slice_range((int)(xrow / 16), part, a.split, xv0, xv1);
-    u32x4 v[NV];
+    // The FP8 slice's first pass too, in registers of its own when that
+    // keeps the occupancy (up to 4 vectors per lane); wider slices load it
+    // into v after the bf16 stores.
+    constexpr bool kEarlyFp8 = FP8 && NV <= 4;
+    u32x4 v[NV], vf[kEarlyFp8 ? NV : 1];
     if (bf16) load_pass<NV>(xsrc, xv0, xv1, v);
+    const uint8_t* fsrc = FP8 ? a.x_fp8 + (int64_t)t * a.H : nullptr;
+    int fv0 = 0, fv1 = 0;
+    slice_range(a.H / 16, part, a.split, fv0, fv1);
+    if constexpr (kEarlyFp8) load_pass<NV>(fsrc, fv0, fv1, vf);
     if (lane >= a.K) {
         s = -1;
         e = -1;
@@ -178,10 +188,9 @@ __global__ __launch_bounds__(kDspThreads, EP_DSP_MINB) void dispatch_kernel(Disp
     if (!dest) return;
 
     if (bf16) fan_out_row<NV>(xsrc, xrow, a.rx, dest, s, xv0, xv1, v);
-    if (a.x_fp8 && a.rfp8) {
-        const uint8_t* fsrc = a.x_fp8 + (int64_t)t * a.H;
-        int fv0 = 0, fv1 = 0;
-        slice_range(a.H / 16, part, a.split, fv0, fv1);
+    if constexpr (kEarlyFp8) {
+        fan_out_row<NV>(fsrc, a.H, a.rfp8, dest, s, fv0, fv1, vf);
+    } else if constexpr (FP8) {
         load_pass<NV>(fsrc, fv0, fv1, v);
         fan_out_row<NV>(fsrc, a.H, a.rfp8, dest, s, fv0, fv1, v);
     }
@@ -409,6 +418,22 @@ __global__ __launch_bounds__(kDspThreads) void dispatch_persistent_kernel(Dispat
     }
 }
 
+// The instantiation holding enough vectors per lane for the widest slice.
+template <bool FP8>
+hipError_t launch_nv(int64_t per_lane, dim3 grid, dim3 block, const DispatchArgs& a, hipStream_t st) {
+    if (per_lane <= 1)
+        hipLaunchKernelGGL((dispatch_kernel<1, FP8>), grid, block, 0, st, a);
+    else if (per_lane <= 2)
+        hipLaunchKernelGGL((dispatch_kernel<2, FP8>), grid, block, 0, st, a);
+    else if (per_lane <= 4 || EP_DSP_NVMAX <= 4)
+        hipLaunchKernelGGL((dispatch_kernel<4, FP8>), grid, block, 0, st, a);
+    else if (per_lane <= 8 || EP_DSP_NVMAX <= 8)
+        hipLaunchKernelGGL((dispatch_kernel<8, FP8>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((dispatch_kernel<16, FP8>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
@@ -479,17 +504,8 @@ hipError_t launch_dispatch(const ep_shape& s, const ep_layout& L, const ep_token
         return hipGetLastError();
     }
 #endif
-    if (per_lane <= 1)
-        hipLaunchKernelGGL(dispatch_kernel<1>, grid, block, 0, st, a);
-    else if (per_lane <= 2)
-        hipLaunchKernelGGL(dispatch_kernel<2>, grid, block, 0, st, a);
-    else if (per_lane <= 4 || EP_DSP_NVMAX <= 4)
-        hipLaunchKernelGGL(dispatch_kernel<4>, grid, block, 0, st, a);
-    else if (per_lane <= 8 || EP_DSP_NVMAX <= 8)
-        hipLaunchKernelGGL(dispatch_kernel<8>, grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL(dispatch_kernel<16>, grid, block, 0, st, a);
-    return hipGetLastError();
+    if (a.x_fp8 && a.rfp8) return launch_nv<true>(per_lane, grid, block, a, st);
+    return launch_nv<false>(per_lane, grid, block, a, st);
 }
 
 }  // namespace ep
