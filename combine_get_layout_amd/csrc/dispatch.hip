@@ -12,12 +12,14 @@
 // Mapping on CDNA4: each source token's row is cut into `split` column
 // slices of whole 128-byte lines, one wave64 per slice, four waves per
 // workgroup (split = EP_DSP_SPLIT, 4, for rows of 2,048 bf16 values and
-// more; fewer for narrower rows, so that a slice fills a wave's 64 lanes). A wave loads its slice into VGPRs (up to 16 16-byte vectors per
-// lane per pass), then streams it to each destination row with non-temporal
-// 16-byte stores: one HBM read, D writes, no LDS round trip. Destinations
-// are the lanes k whose slot differs from every earlier lane's (the rank
+// more; fewer for narrower rows, so that a slice fills a wave's 64 lanes).
+// A wave loads its slice into VGPRs (up to 16 16-byte vectors per lane per
+// pass), then streams it to each destination row with non-temporal 16-byte
+// stores: one HBM read, D writes, no LDS round trip. Destinations are the
+// lanes k whose slot differs from every earlier lane's (the rank
 // deduplication), found with one ballot. The first slice's wave also writes
-// the scales and the metadata.
+// the scales and the metadata. Rows of at most 32 vectors with K <= 8 take
+// a second kernel that holds 2, 4 or 8 tokens per wave.
 #include <algorithm>
 
 #include "ep_device.h"
