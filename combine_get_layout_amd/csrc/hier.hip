@@ -91,37 +91,42 @@ struct HierArgs {
 };
 
 // Record vector q >= q_scales of token t (16 bytes): scales, expert ids,
-// weights, source index, or zero past the end of the record.
+// weights, source index, or zero past the end of the record. Every
+// candidate value is loaded (indices clamped into the token's arrays) and
+// the vector is then selected by q: loads under per-lane branches were
+// issued one round trip at a time.
 __device__ __forceinline__ u32x4 meta_vector(const HierArgs& a, int t, int q) {
     const RecordGeom& g = a.geom;
+    const int ns = a.H / 128;
+    const int i0 = max(0, (q - g.q_scales) * 4);
+    const int k0 = max(0, (q - g.q_idx) * 4), kw0 = max(0, (q - g.q_w) * 4);
+    float sc[4] = {0.f, 0.f, 0.f, 0.f}, wt[4];
+    int64_t e[4];
+    if (a.x_scales) {  // present whenever the record has scales (then ns >= 1)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[j] = a.x_scales[(int64_t)t * ns + min(i0 + j, ns - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        e[j] = a.topk[(int64_t)t * a.K + min(k0 + j, a.K - 1)];
+        wt[j] = a.topk_w[(int64_t)t * a.K + min(kw0 + j, a.K - 1)];
+    }
     u32x4 v = {0u, 0u, 0u, 0u};
     if (q < g.q_idx) {
-        const int ns = a.H / 128;
-        const int i0 = (q - g.q_scales) * 4;
-        const float* sc = a.x_scales + (int64_t)t * ns;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (i0 + j < ns) v[j] = __float_as_uint(sc[i0 + j]);
-        return v;
-    }
-    if (q < g.q_w) {
-        const int k0 = (q - g.q_idx) * 4;
+            if (i0 + j < ns) v[j] = __float_as_uint(sc[j]);
+    } else if (q < g.q_w) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (k0 + j < a.K) {
-                const int64_t e = a.topk[(int64_t)t * a.K + k0 + j];
-                v[j] = (uint32_t)(expert_ok(e, a.E) ? (int32_t)e : -1);
-            }
-        return v;
-    }
-    if (q < g.q_src) {
-        const int k0 = (q - g.q_w) * 4;
+            if (k0 + j < a.K) v[j] = (uint32_t)(expert_ok(e[j], a.E) ? (int32_t)e[j] : -1);
+    } else if (q < g.q_src) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (k0 + j < a.K) v[j] = __float_as_uint(a.topk_w[(int64_t)t * a.K + k0 + j]);
-        return v;
+            if (kw0 + j < a.K) v[j] = __float_as_uint(wt[j]);
+    } else if (q == g.q_src) {
+        v[0] = (uint32_t)t;
     }
-    if (q == g.q_src) v[0] = (uint32_t)t;
     return v;
 }
 
