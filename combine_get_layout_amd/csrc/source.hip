@@ -58,21 +58,48 @@ __device__ __forceinline__ void tile_range(const SourceArgs& a, int& t0, int& nt
     nt = max(0, min(kTile, end - t0));
 }
 
+// A token's expert ids: with K <= 8 all requested at once (lanes past K
+// re-read lane K - 1; callers stop at K), else read on use. A loop over a
+// run-time K issued one load per round trip.
+struct Ids {
+    int64_t v[8];
+    __device__ __forceinline__ void load(const int64_t* row, int K) {
+        if (K <= 8) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = row[min(k, K - 1)];
+        }
+    }
+    // f(k, id) for k = 0 .. K - 1.
+    template <typename F>
+    __device__ __forceinline__ void each(const int64_t* row, int K, F f) const {
+        if (K <= 8) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (k >= K) break;
+                f(k, v[k]);
+            }
+        } else {
+            for (int k = 0; k < K; ++k) f(k, row[k]);
+        }
+    }
+};
+
 // Bit (r, i) of the tile's matrix is set when token t0 + i sends to rank r.
-// Returns whether this thread's token holds an invalid id.
-__device__ bool tile_bits(const SourceArgs& a, int t0, int nt, uint32_t* bits) {
-    for (int i = threadIdx.x; i < a.R * kTileWords; i += kBlockThreads) bits[i] = 0u;
+// Returns whether this thread's token holds an invalid id. The caller has
+// requested the ids (ids.load) before, so they arrive while the matrix is
+// cleared.
+__device__ bool tile_bits(const SourceArgs& a, int t0, int nt, uint32_t* bits, const Ids& ids) {
+    const int i = threadIdx.x;
+    const int64_t* row = a.topk + (int64_t)(t0 + i) * a.K;
+    for (int j = threadIdx.x; j < a.R * kTileWords; j += kBlockThreads) bits[j] = 0u;
     __syncthreads();
     bool bad = false;
-    const int i = threadIdx.x;
     if (i < nt) {
-        const int64_t* row = a.topk + (int64_t)(t0 + i) * a.K;
         const uint32_t bit = 1u << (i & 31);
-        for (int k = 0; k < a.K; ++k) {
-            const int64_t e = row[k];
+        ids.each(row, a.K, [&](int, int64_t e) {
             bad |= expert_bad(e, a.E);
             if (expert_ok(e, a.E)) atomicOr(&bits[a.div_epr((int)e) * kTileWords + (i >> 5)], bit);
-        }
+        });
     }
     __syncthreads();
     return bad;
@@ -83,7 +110,9 @@ __global__ __launch_bounds__(kBlockThreads) void source_count_kernel(SourceArgs 
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.err = 0u;  // clean word
     int t0, nt;
     tile_range(a, t0, nt);
-    tile_bits(a, t0, nt, bits);
+    Ids ids;
+    if ((int)threadIdx.x < nt) ids.load(a.topk + (int64_t)(t0 + threadIdx.x) * a.K, a.K);
+    tile_bits(a, t0, nt, bits, ids);
     int32_t* part = a.part + ((int64_t)blockIdx.y * a.nbs + blockIdx.x) * a.R;
     for (int r = threadIdx.x; r < a.R; r += kBlockThreads) {
         int c = 0;
@@ -134,20 +163,33 @@ __global__ __launch_bounds__(kExchangeThreads) void source_exchange_kernel(Sourc
 
 __global__ __launch_bounds__(kBlockThreads) void source_assign_kernel(SourceArgs a) {
     extern __shared__ uint32_t bits[];
+    // The tile's per-rank prefixes go to LDS after the bit matrix; they are
+    // loaded while the matrix is cleared and read once the marking barrier
+    // has passed (one round trip instead of one per lane).
+    int32_t* base = reinterpret_cast<int32_t*>(bits + a.R * kTileWords);
+    const int s = blockIdx.y;
     int t0, nt;
     tile_range(a, t0, nt);
-    const bool bad = tile_bits(a, t0, nt, bits);
+    Ids ids;
+    if ((int)threadIdx.x < nt) ids.load(a.topk + (int64_t)(t0 + threadIdx.x) * a.K, a.K);
+    constexpr int kPrefixRounds = (EP_MAX_RANKS + kBlockThreads - 1) / kBlockThreads;
+    const int32_t* part = a.part + ((int64_t)s * a.nbs + blockIdx.x) * a.R;
+    int32_t pv[kPrefixRounds];
+#pragma unroll
+    for (int q = 0; q < kPrefixRounds; ++q) pv[q] = part[min((int)threadIdx.x + q * kBlockThreads, a.R - 1)];
+#pragma unroll
+    for (int q = 0; q < kPrefixRounds; ++q)
+        if ((int)threadIdx.x + q * kBlockThreads < a.R) base[threadIdx.x + q * kBlockThreads] = pv[q];
+    const bool bad = tile_bits(a, t0, nt, bits, ids);
     if (bad) report(a.err, EP_DEVERR_EXPERT_ID);
     const int i = threadIdx.x;
     if (i >= nt) return;
-    const int s = blockIdx.y;
     const int64_t t = t0 + i;
-    const int32_t* base = a.part + ((int64_t)s * a.nbs + blockIdx.x) * a.R;
     const int w = i >> 5;
     const uint32_t below = (1u << (i & 31)) - 1u;
     bool over = false;
-    for (int k = 0; k < a.K; ++k) {
-        const int64_t e = a.topk[t * a.K + k];
+    const int64_t* row = a.topk + t * a.K;
+    ids.each(row, a.K, [&](int k, int64_t e) {
         int32_t v = -1;
         if (expert_ok(e, a.E)) {
             const int r = a.div_epr((int)e);
@@ -157,7 +199,7 @@ __global__ __launch_bounds__(kBlockThreads) void source_assign_kernel(SourceArgs
             else over = true;
         }
         a.src_slot[t * a.K + k] = v;
-    }
+    });
     if (over) report(a.err, EP_DEVERR_CAPACITY);
 }
 
@@ -313,8 +355,9 @@ hipError_t launch_source_layout(const ep_shape& s, const int64_t* topk, const ep
     const dim3 grid(W.nbs, src.S), block(kBlockThreads);
     const size_t lds = sizeof(uint32_t) * (size_t)s.R * kTileWords;
     hipLaunchKernelGGL(source_count_kernel, grid, block, lds, st, a);
+    const size_t lds_assign = lds + sizeof(int32_t) * (size_t)s.R;  // + the tile's per-rank prefixes
     hipLaunchKernelGGL(source_exchange_kernel, dim3(1), dim3(kExchangeThreads), 0, st, a);
-    if (s.T > 0) hipLaunchKernelGGL(source_assign_kernel, grid, block, lds, st, a);
+    if (s.T > 0) hipLaunchKernelGGL(source_assign_kernel, grid, block, lds_assign, st, a);
     return hipGetLastError();
 }
 
