@@ -763,11 +763,16 @@ __global__ __launch_bounds__(kBlockThreads) void layout_expand_kernel(LayoutArgs
     const int tid = threadIdx.x;
     const int t0 = b * kLayoutTokens;
     const int t = t0 + tid;
+    // Every id load issued (token and lane clamped, the extra entries masked
+    // to key E afterwards): loads under a branch were issued one by one.
+    const int tc = min(t, a.T - 1);
+    int64_t raw[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) raw[k] = a.topk[(int64_t)tc * a.K + min(k, a.K - 1)];
     int keys[ITEMS];
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
-        int64_t e = -1;
-        if (t < a.T && k < a.K) e = a.topk[(int64_t)t * a.K + k];
+        const int64_t e = t < a.T && k < a.K ? raw[k] : -1;
         keys[k] = expert_ok(e, a.E) ? (int)e : a.E;  // no expert: key E
     }
     bool dup = false;
@@ -776,35 +781,38 @@ __global__ __launch_bounds__(kBlockThreads) void layout_expand_kernel(LayoutArgs
 #pragma unroll
         for (int j = 0; j < k; ++j) dup |= keys[k] < a.E && keys[k] == keys[j];
 
-    if (use_bits && !__syncthreads_or(dup)) {
-        uint32_t* bits = lds_x;  // [E][kWords]
-        for (int i = tid; i < a.E * kWords; i += kBlockThreads) bits[i] = 0u;
-        __syncthreads();
-        const int w = tid / 32;
-        const uint32_t bit = 1u << (tid & 31);
-#pragma unroll
-        for (int k = 0; k < ITEMS; ++k)
-            if (keys[k] < a.E) atomicOr(&bits[keys[k] * kWords + w], bit);
-        __syncthreads();
-        if (t >= a.T) return;
-        // Both global terms of every lane are loaded together (clamped ids).
+    if (use_bits) {
+        // Both global terms of every lane (clamped ids), requested before the
+        // bit matrix is built so that they arrive during it.
         int base[ITEMS];
 #pragma unroll
         for (int k = 0; k < ITEMS; ++k) {
             const int e = min(keys[k], a.E - 1);
             base[k] = a.out.expert_offsets[e] + a.part_expert[(int64_t)b * a.E + e];
         }
-        const uint32_t below = bit - 1u;
+        if (!__syncthreads_or(dup)) {
+            uint32_t* bits = lds_x;  // [E][kWords]
+            for (int i = tid; i < a.E * kWords; i += kBlockThreads) bits[i] = 0u;
+            __syncthreads();
+            const int w = tid / 32;
+            const uint32_t bit = 1u << (tid & 31);
 #pragma unroll
-        for (int k = 0; k < ITEMS; ++k) {
-            if (k >= a.K) break;
-            const int e = min(keys[k], a.E - 1);
-            int rank = __popc(bits[e * kWords + w] & below);
+            for (int k = 0; k < ITEMS; ++k)
+                if (keys[k] < a.E) atomicOr(&bits[keys[k] * kWords + w], bit);
+            __syncthreads();
+            if (t >= a.T) return;
+            const uint32_t below = bit - 1u;
 #pragma unroll
-            for (int j = 0; j < kWords; ++j) rank += j < w ? __popc(bits[e * kWords + j]) : 0;
-            a.out.expert_slot[(int64_t)t * a.K + k] = keys[k] < a.E ? base[k] + rank : -1;
+            for (int k = 0; k < ITEMS; ++k) {
+                if (k >= a.K) break;
+                const int e = min(keys[k], a.E - 1);
+                int rank = __popc(bits[e * kWords + w] & below);
+#pragma unroll
+                for (int j = 0; j < kWords; ++j) rank += j < w ? __popc(bits[e * kWords + j]) : 0;
+                a.out.expert_slot[(int64_t)t * a.K + k] = keys[k] < a.E ? base[k] + rank : -1;
+            }
+            return;
         }
-        return;
     }
 
     typename sort_t::storage_type& sort_st = *reinterpret_cast<typename sort_t::storage_type*>(lds_x);
@@ -814,6 +822,14 @@ __global__ __launch_bounds__(kBlockThreads) void layout_expand_kernel(LayoutArgs
     for (int k = 0; k < ITEMS; ++k) vals[k] = tid * ITEMS + k;
     sort_t().sort(keys, vals, sort_st, 0, key_bits);
     __syncthreads();
+    // The global terms of every sorted entry (clamped keys), requested
+    // together before the searches.
+    int sbase[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int e = min(keys[j], a.E - 1);
+        sbase[j] = a.out.expert_offsets[e] + a.part_expert[(int64_t)b * a.E + e];
+    }
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) sorted[tid * ITEMS + j] = keys[j];
     __syncthreads();
@@ -830,7 +846,7 @@ __global__ __launch_bounds__(kBlockThreads) void layout_expand_kernel(LayoutArgs
                 const int mid = (lo + hi) >> 1;
                 if (sorted[mid] < key) lo = mid + 1; else hi = mid;
             }
-            row = a.out.expert_offsets[key] + a.part_expert[(int64_t)b * a.E + key] + (pos - lo);
+            row = sbase[j] + (pos - lo);
         }
         a.out.expert_slot[(int64_t)(t0 + lt) * a.K + k] = row;
     }
