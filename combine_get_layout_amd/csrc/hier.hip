@@ -315,6 +315,8 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g,
     }
 }
 
+constexpr int kForwardMaxBlocks = 65536;  // workgroups of the forward launch at most
+
 // One wave per group-region row, grid-stride; the row count is read on the
 // device. The row's group is the number of groups g >= 1 whose region starts
 // at or before n (empty groups have equal starts).
@@ -582,8 +584,12 @@ hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& t
                            dim3((unsigned)(((int64_t)s.T * kSoSplit + kWavesPerBlock - 1) / kWavesPerBlock)), block, 0,
                            st, a);
     if ((steps & EP_HIER_FORWARD) && group_cap > 0) {
+        // One wave per row up to 262,144 rows (grid-stride beyond): one-shot
+        // waves beat a grid of 8,192 workgroups walking 2-3 rows per wave
+        // (hier8x8 forward 645 -> 600 us by rocprofv3). Waves past the row
+        // count read on the device exit at once.
         const int64_t want = (group_cap + kWavesPerBlock - 1) / kWavesPerBlock;
-        const int blocks = (int)(want < 8192 ? want : 8192);
+        const int blocks = (int)(want < kForwardMaxBlocks ? want : kForwardMaxBlocks);
         hipLaunchKernelGGL(forward_kernel, dim3(blocks), block, 0, st, a);
     }
     return hipGetLastError();
