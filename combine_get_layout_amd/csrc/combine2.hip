@@ -16,8 +16,11 @@
 //     partial rows in ascending g, from +0); a partial row whose flags are not
 //     all epoch is skipped.
 //
-// CDNA4 mapping: one wave64 per token for both steps. Both use the chunked
-// lane mapping (wave iteration i covers blocks 2i and 2i+1; lane L holds
+// CDNA4 mapping: with K <= 8 both steps cut a token into slices of 4
+// wave-iterations, one wave per slice (the slices of a token in one
+// workgroup), and stream its rows one burst at a time with the next burst
+// requested first; otherwise one wave64 per token. Both use the chunked lane
+// mapping (wave iteration i covers blocks 2i and 2i+1; lane L holds
 // hidden vector 30 * (2i + L/32) + L%32 when L%32 < 30, else a flag vector),
 // so a partial row is produced and consumed with whole-wave 1 KiB stores and
 // loads. The flags of every chunked row read are checked by the flag lanes of

@@ -15,12 +15,15 @@
 // 16-byte vector per lane covers exactly two blocks: lanes 0-29 carry payload
 // vectors of block 2i, lanes 30-31 its flag, lanes 32-61 and 62-63 the same
 // for block 2i+1. Record vector q sits in block q / 30, vector q % 30.
-//   step 1: one wave per token assembles its chunked record in VGPRs (pieces
-//           of 16 wave-iterations = 32 blocks = 16 KiB) and streams it once to
-//           each destination group's row.
-//   step 2: one wave per group-region row (grid-stride; the row count is read
-//           on the device): check every block's flag, read src and top-k ids
-//           from the record, then stream the row to each scale-up peer's row.
+//   step 1: four waves per token, each assembling a run of its chunked
+//           record's blocks in VGPRs, stream it once to each destination
+//           group's row.
+//   step 2: one wave per group-region row (the row count is read on the
+//           device; grid-stride past 262,144 rows): check every block's flag,
+//           read src and top-k ids from the record, then stream the row to
+//           each scale-up peer's row.
+//   fused : both steps in one persistent launch; workgroups take batches of
+//           tokens to produce or, once a batch's flag is out, to forward.
 // Step 1 also serves several source ranks on one GPU: given one staging row
 // per (token, destination rank) instead of per group, it is their send.
 #include <algorithm>
@@ -317,8 +320,8 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g,
 
 constexpr int kForwardMaxBlocks = 65536;  // workgroups of the forward launch at most
 
-// One wave per group-region row, grid-stride; the row count is read on the
-// device. The row's group is the number of groups g >= 1 whose region starts
+// One wave per group-region row (grid-stride when the grid is capped); the
+// row count is read on the device. The row's group is the number of groups g >= 1 whose region starts
 // at or before n (empty groups have equal starts).
 __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
     __shared__ int32_t goff[EP_MAX_GROUPS + 1];
