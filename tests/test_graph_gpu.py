@@ -358,3 +358,171 @@ def test_graph_cycle_full_size_hier8x8_against_oracle(fused):
         if i == len(inps) - 1:  # the buffers hold the last batch's dispatch
             np.testing.assert_array_equal(gbuf.cpu().numpy()[:Gs[i]], Hd["group_buf"])
             np.testing.assert_array_equal(pbuf.cpu().numpy()[:Ns[i]], Hd["peer_buf"])
+
+
+def _capture_twice(run):
+    """Run once eagerly, capture, replay twice; returns nothing (the outputs of
+    the last replay are in the caller's buffers)."""
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_graph_cycle_full_size_ep32_expand_against_oracle():
+    """ep32 with expand rows (one receive row per (token, lane), grouped by
+    expert) at full size, as `bench.py --workload ep32 --expand` times it: the
+    steps of two input batches in one graph, replayed twice, and every output
+    of the last replay compared with the CPU oracle."""
+    import oracle
+
+    oracle.build(force=False)
+    w = synth.workload("ep32")
+    print("graph cycle: ep32 expand", flush=True)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, 1)
+    ws = ep.alloc_workspace(shape)
+    inps = [synth.make_inputs(w, seed=synth.seed_of(w) + 1000 * i) for i in range(2)]
+    batches = [dict(x=dev(b["x"]), topk_idx=dev(b["topk_idx"]), topk_weights=dev(b["topk_w"])) for b in inps]
+    Ls = [ep.alloc_layout(shape, masks=True, groups=False, expand=True) for _ in batches]
+    cap = w.T * w.K
+    recv = ep.alloc_recv(shape, cap)
+    outs = [torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda") for _ in batches]
+
+    def run():
+        for i, tk in enumerate(batches):
+            ep.ep_get_layout(shape, tk["topk_idx"], Ls[i], ws)
+            ep.ep_dispatch_expand(shape, Ls[i], tk, recv, cap, ws)
+            ep.ep_combine_expand(shape, Ls[i], recv["x"], cap, 2 * w.H, ep.EP_FMT_PLAIN, 0,
+                                 tk["topk_weights"], outs[i], ws)
+
+    ep.ep_clear_errors(ws)
+    _capture_twice(run)
+    assert ep.ep_check_sticky_errors(ws) == 0
+    for i, b in enumerate(inps):
+        O = oracle.layout(b["topk_idx"], w.E, w.R, 1)
+        es = oracle.expert_slots(b["topk_idx"], w.E, O["expert_offsets"])
+        np.testing.assert_array_equal(Ls[i]["expert_slot"].cpu().numpy().reshape(w.T, w.K), es)
+        n_rows = int(O["expert_offsets"][-1])
+        D = oracle.dispatch_rows(b["topk_idx"], w.E, es, n_rows, x=b["x"], topk_w=b["topk_w"])
+        C = oracle.combine(es, b["topk_w"], D["recv_x"], w.H)
+        got = outs[i].view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, C["out"], err_msg=f"batch {i}")
+        if i == len(inps) - 1:
+            rx = recv["x"].view(torch.int16).cpu().numpy().view(np.uint16)[:n_rows]
+            np.testing.assert_array_equal(rx, D["recv_x"])
+            np.testing.assert_array_equal(recv["src_idx"].cpu().numpy()[:n_rows], D["recv_src"])
+            np.testing.assert_array_equal(recv["topk_idx"].cpu().numpy()[:n_rows], D["recv_topk_idx"])
+            np.testing.assert_array_equal(recv["topk_weights"].cpu().numpy()[:n_rows].view(np.uint32),
+                                          D["recv_topk_w"].view(np.uint32))
+
+
+def test_graph_cycle_full_size_hier8x8_two_level_combine_against_oracle():
+    """hier8x8 with the two-level combine at full size, as `bench.py
+    --workload hier8x8 --two-level-combine` times it: two batches in one graph,
+    replayed twice; the last replay's partial rows and outputs against the
+    oracle."""
+    import oracle
+
+    oracle.build(force=False)
+    w = synth.workload("hier8x8")
+    print("graph cycle: hier8x8 two-level combine", flush=True)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, w.G)
+    ws = ep.alloc_workspace(shape)
+    inps = [synth.make_inputs(w, seed=synth.seed_of(w) + 1000 * i) for i in range(2)]
+    batches = [dict(x=dev(b["x"]), topk_idx=dev(b["topk_idx"]), topk_weights=dev(b["topk_w"])) for b in inps]
+    Ls = [ep.alloc_layout(shape, masks=False, groups=True) for _ in batches]
+    Os = [oracle.layout(b["topk_idx"], w.E, w.R, w.G) for b in inps]
+    Ns = [int(O["rank_offsets"][-1]) for O in Os]
+    Gs = [int(O["group_offsets"][-1]) for O in Os]
+    stride = ep.ep_chunked_record_bytes(shape, ep.EP_SEG_BF16)
+    gbuf = torch.zeros((max(Gs), stride), dtype=torch.uint8, device="cuda")
+    pbuf = torch.zeros((max(Ns), stride), dtype=torch.uint8, device="cuda")
+    part = torch.zeros((max(Gs), ep.ep_partial_row_bytes(shape)), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda") for _ in batches]
+
+    def run():
+        for i, tk in enumerate(batches):
+            e = 60 + i
+            ep.ep_get_layout(shape, tk["topk_idx"], Ls[i], ws)
+            ep.ep_hierarchical_dispatch(shape, Ls[i], tk, e, 3, gbuf, Gs[i], pbuf, Ns[i], ws)
+            ep.ep_combine_two_level(shape, Ls[i], tk["topk_idx"], pbuf, Ns[i], stride, ep.EP_FMT_CHUNKED, e,
+                                    tk["topk_weights"], part, Gs[i], 3, outs[i], ws)
+
+    ep.ep_clear_errors(ws)
+    _capture_twice(run)
+    assert ep.ep_check_sticky_errors(ws) == 0
+    for i, b in enumerate(inps):
+        O = Os[i]
+        Hd = oracle.hier_dispatch(b["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_offsets"], 60 + i,
+                                  x=b["x"], topk_w=b["topk_w"])
+        C2 = oracle.combine_two_level(b["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_slot"], b["topk_w"],
+                                      Hd["peer_buf"], w.H, Gs[i], 60 + i, chunked=True)
+        assert C2["err"] == 0
+        got = outs[i].view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, C2["out"], err_msg=f"batch {i}")
+        if i == len(inps) - 1:
+            np.testing.assert_array_equal(part.cpu().numpy()[:Gs[i]], C2["group_buf"])
+
+
+def test_graph_cycle_full_size_ep32_sources_against_oracle():
+    """ep32 as 32 source ranks of 128 tokens at full size, as `bench.py
+    --workload ep32 --sources 32` times it: source layout, send into the
+    per-(rank, source) staging regions, copy epilogue and combine over the
+    staging rows, for two batches in one graph replayed twice; the last
+    replay's outputs against the oracle."""
+    import oracle
+
+    oracle.build(force=False)
+    w = synth.workload("ep32")
+    S = 32
+    print("graph cycle: ep32 32 sources", flush=True)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, 1)
+    ws = ep.alloc_source_workspace(shape, S)
+    inps = [synth.make_inputs(w, seed=synth.seed_of(w) + 1000 * i) for i in range(2)]
+    batches = [dict(x=dev(b["x"]), topk_idx=dev(b["topk_idx"]), topk_weights=dev(b["topk_w"])) for b in inps]
+    srcs = [ep.alloc_sources(shape, S, -(-w.T // S)) for _ in batches]
+    Xs = [oracle.source_counts(b["topk_idx"], w.E, w.R, S) for b in inps]
+    cap = max(int(X["counts"].max()) for X in Xs)
+    for src in srcs:
+        src["capacity"] = cap
+    Ns = [int(X["recv_offsets"][-1]) for X in Xs]
+    stride = ep.ep_chunked_record_bytes(shape, ep.EP_SEG_BF16)
+    staging = torch.zeros((w.R * S * cap, stride), dtype=torch.uint8, device="cuda")
+    recv = ep.alloc_recv(shape, max(Ns))
+    outs = [torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda") for _ in batches]
+
+    def run():
+        for i, tk in enumerate(batches):
+            e = 80 + i
+            ep.ep_source_layout(shape, tk["topk_idx"], srcs[i], ws)
+            ep.ep_source_dispatch(shape, srcs[i], tk, e, staging, ws)
+            ep.ep_copy_epilogue(shape, srcs[i], staging, e, ep.EP_SEG_BF16, recv, Ns[i], ws)
+            ep.ep_combine(shape, dict(slot=srcs[i]["src_slot"]), staging, staging.shape[0], stride,
+                          ep.EP_FMT_CHUNKED, e, tk["topk_weights"], outs[i], ws)
+
+    ep.ep_clear_errors(ws)
+    _capture_twice(run)
+    assert ep.ep_check_sticky_errors(ws) == 0
+    for i, b in enumerate(inps):
+        X = Xs[i]
+        np.testing.assert_array_equal(srcs[i]["counts"].cpu().numpy(), X["counts"])
+        np.testing.assert_array_equal(srcs[i]["recv_offsets"].cpu().numpy(), X["recv_offsets"])
+        sl = oracle.source_slots(b["topk_idx"], w.E, w.R, S, cap)["src_slot"]
+        np.testing.assert_array_equal(srcs[i]["src_slot"].cpu().numpy().reshape(w.T, w.K), sl)
+        Sd = oracle.source_dispatch(b["topk_idx"], w.E, w.R, S, cap, 80 + i, x=b["x"], topk_w=b["topk_w"])
+        C = oracle.combine(sl, b["topk_w"], Sd["staging"], w.H, chunked=True, epoch=80 + i)
+        got = outs[i].view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, C["out"], err_msg=f"batch {i}")
+        if i == len(inps) - 1:
+            Ep = oracle.copy_epilogue(X["recv_offsets"], Sd["staging"], w.H, w.K, w.R, S, cap, 80 + i)
+            n = Ns[i]
+            rx = recv["x"].view(torch.int16).cpu().numpy().view(np.uint16)[:n]
+            np.testing.assert_array_equal(rx, Ep["recv_x"])
+            np.testing.assert_array_equal(recv["src_idx"].cpu().numpy()[:n], Ep["recv_src"])
+            np.testing.assert_array_equal(recv["topk_idx"].cpu().numpy()[:n], Ep["recv_topk_idx"])
