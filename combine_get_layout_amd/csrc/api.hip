@@ -186,7 +186,7 @@ int ep_hierarchical_dispatch(const ep_shape* shape, const ep_layout* layout,
          (group_cap > 0 && !group_buf)))
         return EP_ERR_ARG;
     if ((steps & EP_HIER_FORWARD) &&
-        (!layout->group_offsets || !layout->slot || (group_cap > 0 && !group_buf) ||
+        (!layout->group_offsets || (shape->T > 0 && !layout->slot) || (group_cap > 0 && !group_buf) ||
          (peer_cap > 0 && !peer_buf)))
         return EP_ERR_ARG;
     if (tokens->x_fp8 && shape->H % 16 != 0) return EP_ERR_ARG;

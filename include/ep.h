@@ -28,6 +28,9 @@
  *     16-bit patterns (uint16_t), FP8 values as e4m3 bytes.
  *   - Alignment: hidden rows (bf16, FP8), receive rows and chunk buffers need
  *     16 B aligned base pointers; other arrays their element alignment.
+ *   - With T = 0 the per-token arrays (topk_idx, x, weights, slot, ...) and
+ *     buffers of zero capacity may be NULL; the layout calls then write zero
+ *     counts and offsets, and no call writes a row.
  *   - Return value: EP_OK, or a negative EP_ERR_* status. Nothing is enqueued
  *     when a host-side check fails. Problems only visible on the device set
  *     bits in the workspace's error words (read with ep_check_errors and

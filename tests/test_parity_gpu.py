@@ -311,6 +311,45 @@ def test_dispatch_zero_tokens():
     assert ep.ep_check_errors(ws) == 0
 
 
+def test_zero_tokens_every_other_path():
+    """No tokens through the two-level dispatch (two launches and fused), the
+    chunked and two-level combines and the expand rows: every call succeeds,
+    the offsets are all zero, no error bit is set and one-row sentinel
+    buffers handed in with zero capacity are left as they were."""
+    T, H, K, E, R, G = 0, 512, 4, 32, 8, 4
+    shape = ep.make_shape(T, H, K, E, R, G)
+    L = ep.alloc_layout(shape, masks=True, groups=True, expand=True)
+    ws = ep.alloc_workspace(shape)
+    tk = dict(x=torch.empty((0, H), dtype=torch.uint16, device="cuda"),
+              topk_idx=torch.empty((0, K), dtype=torch.int64, device="cuda"),
+              topk_weights=torch.empty((0, K), dtype=torch.float32, device="cuda"))
+    ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+    torch.cuda.synchronize()
+    for k in ("rank_offsets", "group_offsets", "expert_offsets", "tokens_per_rank",
+              "tokens_per_group", "tokens_per_expert"):
+        assert (host(L[k]) == 0).all(), k
+    stride = ep.ep_chunked_record_bytes(shape, ep.EP_SEG_BF16)
+    gb = poison(torch.empty((1, stride), dtype=torch.uint8, device="cuda"), 0xA5)
+    pb = poison(torch.empty((1, stride), dtype=torch.uint8, device="cuda"), 0xA5)
+    ep.ep_hierarchical_dispatch(shape, L, tk, 3, 3, gb, 0, pb, 0, ws)
+    ep.ep_hierarchical_dispatch_fused(shape, L, tk, 4, gb, 0, pb, 0, ws)
+    out = poison(torch.empty((1, H), dtype=torch.uint16, device="cuda"), 0xA5)
+    ep.ep_combine(shape, L, pb, 0, stride, ep.EP_FMT_CHUNKED, 4, tk["topk_weights"], out, ws)
+    part = poison(torch.empty((1, ep.ep_partial_row_bytes(shape)), dtype=torch.uint8, device="cuda"), 0xA5)
+    ep.ep_combine_two_level(shape, L, tk["topk_idx"], pb, 0, stride, ep.EP_FMT_CHUNKED, 4,
+                            tk["topk_weights"], part, 0, 3, out, ws)
+    recv = ep.alloc_recv(shape, 1)
+    for t in recv.values():
+        poison(t, 0xA5)
+    ep.ep_dispatch_expand(shape, L, tk, recv, 0, ws)
+    ep.ep_combine_expand(shape, L, recv["x"], 0, 2 * H, ep.EP_FMT_PLAIN, 0, tk["topk_weights"], out, ws)
+    torch.cuda.synchronize()
+    for name, t in [("group_buf", gb), ("peer_buf", pb), ("out", out), ("partials", part)] + \
+            [("recv " + k, v) for k, v in recv.items()]:
+        assert (t.view(torch.uint8) == 0xA5).all(), name
+    assert ep.ep_check_errors(ws) == 0
+
+
 # --------------------------------------------------------------------------
 # Combine
 # --------------------------------------------------------------------------
