@@ -4,8 +4,10 @@
 A step is one pass of the whole path over one batch of synthetic tokens:
   flat workloads   : ep_get_layout -> ep_dispatch -> ep_combine (identity expert:
                      the combine gathers the dispatched rows back)
-  two-level (hier) : ep_get_layout -> ep_hierarchical_dispatch (both steps) ->
-                     ep_combine on the chunked scale-up rows
+  two-level (hier) : ep_get_layout -> ep_hierarchical_dispatch_fused (both
+                     steps in one launch; --two-launch: ep_hierarchical_dispatch,
+                     the two steps as two launches) -> ep_combine on the
+                     chunked scale-up rows
   --sources S      : S source ranks (default R) on the flat workloads:
                      ep_source_layout -> ep_source_dispatch into per-(rank,
                      source) staging regions -> ep_copy_epilogue into dense
@@ -58,8 +60,12 @@ def parse():
     p.add_argument("--fp8", action="store_true", help="also move the FP8 payload + scales")
     p.add_argument("--fused", action="store_true",
                    help="two-level workloads: both dispatch steps in one persistent launch with "
-                        "per-batch flags (ep_hierarchical_dispatch_fused)")
-    p.add_argument("--fused-tile", type=int, default=0, help="tokens per batch of --fused (0: default)")
+                        "per-batch flags (ep_hierarchical_dispatch_fused; the default)")
+    p.add_argument("--two-launch", action="store_true",
+                   help="two-level workloads: the two dispatch steps as two launches "
+                        "(ep_hierarchical_dispatch)")
+    p.add_argument("--fused-tile", type=int, default=0,
+                   help="tokens per batch of the fused two-level dispatch (0: default)")
     p.add_argument("--two-level-combine", action="store_true",
                    help="two-level workloads: combine through per-group partial rows")
     p.add_argument("--expand", action="store_true",
@@ -197,7 +203,8 @@ def main():
         return
     ep.lib()
     torch.cuda.set_device(0)
-    variants = args.fp8 or args.expand or args.two_level_combine or args.fused or args.sources is not None
+    variants = (args.fp8 or args.expand or args.two_level_combine or args.fused or args.two_launch or
+                args.fused_tile or args.sources is not None)
     if args.workload is None and not variants:
         runs = [(label, "ep32" if label.startswith("ep32") else label, kw) for label, kw in TARGET_CONFIGS]
     else:
@@ -238,10 +245,13 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
     hier = w.G > 1
     expand = bool(args.expand)
     two_level = bool(args.two_level_combine)
-    fused = bool(args.fused)
-    if fused and not hier:
-        print("--fused applies to the two-level workloads", file=sys.stderr)
+    if args.fused and args.two_launch:
+        print("--fused and --two-launch exclude each other", file=sys.stderr)
         sys.exit(2)
+    if (args.fused or args.two_launch or args.fused_tile) and not hier:
+        print("--fused, --two-launch and --fused-tile apply to the two-level workloads", file=sys.stderr)
+        sys.exit(2)
+    fused = hier and not args.two_launch
     if two_level and not hier:
         print("--two-level-combine applies to the two-level workloads", file=sys.stderr)
         sys.exit(2)
@@ -513,7 +523,7 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
     dom = max(names[1:], key=lambda n: avg_ms[n])
     achieved = by[dom] / (avg_ms[dom] * 1e-3) / 1e9
     label = w.name + ("_fp8" if fp8 else "") + ("_expand" if expand else "") + \
-        ("_fused" if fused else "") + ("_2lc" if two_level else "") + (f"_s{S}" if multi else "")
+        ("_2launch" if hier and not fused else "") + ("_2lc" if two_level else "") + (f"_s{S}" if multi else "")
     traffic = committed_traffic(label, kernel_of[dom])
 
     if args.copy_calibration:

@@ -52,6 +52,9 @@
 #ifndef EP_CMB_DUP
 #define EP_CMB_DUP 1        // row-streaming kernel: keep one repeated row in VGPRs instead of re-reading it
 #endif
+#ifndef EP_CMB_NTSTORE
+#define EP_CMB_NTSTORE 1    // non-temporal stores of the output rows
+#endif
 
 namespace ep {
 namespace {
@@ -64,6 +67,13 @@ __device__ __forceinline__ u32x4 ld_row(const void* p) {
     return ld16_stream(p);
 #else
     return ld16(p);
+#endif
+}
+__device__ __forceinline__ void st_out(void* p, u32x4 v) {
+#if EP_CMB_NTSTORE
+    st16_stream(p, v);
+#else
+    st16(p, v);
 #endif
 }
 
@@ -169,7 +179,7 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_kernel(Combi
                 const float wk = readlane_f(wt, k);
                 if (valid) fma8(acc, wk, ld_row(a.y + (int64_t)sk * a.stride + off));
             }
-            if (valid) st16_stream(out_row + (int64_t)p * 16, pack8(acc));
+            if (valid) st_out(out_row + (int64_t)p * 16, pack8(acc));
         }
     } else {
         // One uniform row pointer per lane k. Lanes that do not contribute
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_kernel(Combi
                     int p;
                     int64_t off;
                     if (lane_vector<CHUNKED>(it, lane, nvh, p, off))
-                        st16_stream(out_row + (int64_t)p * 16, u32x4{0u, 0u, 0u, 0u});
+                        st_out(out_row + (int64_t)p * 16, u32x4{0u, 0u, 0u, 0u});
                 }
                 return;
             }
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_kernel(Combi
 #pragma unroll
                     for (int k = 0; k < KMAX; ++k)
                         if ((um >> k) & 1) fma8(acc, wk[k], v[k][j]);
-                    if (valid[j]) st16_stream(out_row + (int64_t)p[j] * 16, pack8(acc));
+                    if (valid[j]) st_out(out_row + (int64_t)p[j] * 16, pack8(acc));
                 }
             }
             if (!CHUNKED) return;
@@ -306,7 +316,7 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(
         if (!um) {
 #pragma unroll
             for (int j = 0; j < VPW; ++j)
-                if (valid[j]) st16_stream(out_row + (int64_t)p[j] * 16, u32x4{0u, 0u, 0u, 0u});
+                if (valid[j]) st_out(out_row + (int64_t)p[j] * 16, u32x4{0u, 0u, 0u, 0u});
         } else {
             const int s_any = readlane(s, __ffsll((unsigned long long)um) - 1);
             // A rank reached by two lanes of the token shares one row. The
@@ -388,7 +398,7 @@ __global__ __launch_bounds__(kCmbThreads, EP_CMB_MINB) void combine_rows_kernel(
             }
 #pragma unroll
             for (int j = 0; j < VPW; ++j)
-                if (valid[j]) st16_stream(out_row + (int64_t)p[j] * 16, pack8(acc[j]));
+                if (valid[j]) st_out(out_row + (int64_t)p[j] * 16, pack8(acc[j]));
         }
         if (!CHUNKED || pass == 1) return;
         // The rows whose flags failed in this slice's blocks, then in any
@@ -464,7 +474,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_narrow_kernel(CombineArgs
         for (int k = 0; k < 8; ++k)
             if (s[k] >= 0) fma8(acc, wk[k], y[k]);
     }
-    if (v < nvh) st16_stream(reinterpret_cast<uint8_t*>(a.out) + ((int64_t)t * nvh + v) * 16, pack8(acc));
+    if (v < nvh) st_out(reinterpret_cast<uint8_t*>(a.out) + ((int64_t)t * nvh + v) * 16, pack8(acc));
 }
 
 template <bool CHUNKED>

@@ -14,7 +14,7 @@ namespace ep {
 constexpr int kLayoutTokens = 256;  // tokens per layout workgroup (one per thread)
 constexpr int kFusedMinTile = 1;    // smallest batch of the fused two-level dispatch (tokens)
 constexpr int kFusedMaxTile = 64;   // largest batch
-constexpr int kFusedDefaultTile = 8;
+constexpr int kFusedDefaultTile = 2;  // one token per wave of a 2-wave workgroup (measured best of 1-16)
 constexpr int kFusedCounters = 64;  // u32 words before the batch flags (two used)
 
 // Workspace carve-up (byte offsets from the workspace base).

@@ -41,6 +41,12 @@ constexpr int kPieceIters = 16;  // wave iterations (2 blocks each) held in VGPR
 #define EP_SO_SPLIT 4  // scale-out: waves per token, each writing a run of the record's blocks (measured best of 1, 2, 4)
 #endif
 constexpr int kSoSplit = EP_SO_SPLIT;
+#ifndef EP_SO_NTSTORE
+#define EP_SO_NTSTORE 1  // scale-out: non-temporal stores of the group rows (else plain stores)
+#endif
+#ifndef EP_FWD_NTSTORE
+#define EP_FWD_NTSTORE 1  // forward: non-temporal stores of the peer rows (else plain stores)
+#endif
 #ifndef EP_FUSED_WAVE
 #define EP_FUSED_WAVE 0  // fused kernel: each wave takes its own batches (else each workgroup;
                          // measured slower: the counters' atomics serialise at small batches)
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(kBlockThreads) void scaleout_kernel(HierArgs a) {
     const int gw = blockIdx.x * kWavesPerBlock + wave_in_block();
     const int t = gw / kSoSplit, part = gw % kSoSplit;
     if (t >= a.T) return;
-    scaleout_token<kSoSplit, kSoPiece>(a, t, part);
+    scaleout_token<kSoSplit, kSoPiece, EP_SO_NTSTORE ? kStoreStream : kStorePlain>(a, t, part);
 }
 
 // Address of record byte b (4-byte aligned, never straddling a block) in a
@@ -311,8 +317,10 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g,
 #pragma unroll
             for (int j = 0; j < kPieceIters; ++j) {
                 const int c = 2 * (it0 + j) + c_half;
-                if (it0 + j < iters && c < nchunks)
-                    st16_stream(row + chunk_lane_offset(it0 + j, lane), v[j]);
+                if (it0 + j < iters && c < nchunks) {
+                    if constexpr (EP_FWD_NTSTORE) st16_stream(row + chunk_lane_offset(it0 + j, lane), v[j]);
+                    else st16(row + chunk_lane_offset(it0 + j, lane), v[j]);
+                }
             }
         }
     }
@@ -348,27 +356,40 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
 // hierarchical path the same; "07: DeepEP Intra/Inter-node 协调": forward
 // warps take records from the scale-out buffer as they arrive, waiting with
 // a time limit). Batch b = tokens [b*tile, (b+1)*tile).
-//   * Production: a workgroup takes the next batch from a counter, writes the
-//     scale-out records of its tokens (plain stores), then every wave makes
-//     them visible device-wide (release fence: L2 write-back, wait for the
-//     stores), and after a barrier one thread stores the batch's flag = epoch.
-//   * Forwarding: a workgroup takes the next batch to forward from a second
-//     counter, in batch order. While batches remain to be produced it takes
-//     one only if its flag is already published; once production is all
-//     handed out it takes the next one and waits for its flag (one thread
-//     polls; bounded by `timeout` clock ticks, after which the batch is
-//     skipped with EP_DEVERR_TIMEOUT). After the flag, every wave makes
-//     later loads see memory (acquire fence: L2 invalidate), and the group
-//     rows of the batch's tokens are forwarded as in step 2 (block flags
-//     checked, record's src and ids, the layout's slots).
-// A workgroup waits only for batches whose production another running
-// workgroup has already taken on, and production never waits, so every wait
-// ends even if the grid is not co-resident; the time limit covers the rest.
-// Counters and flags live in the workspace and are zeroed by a one-workgroup
-// kernel launched just before (stream ordered, no memset node).
+//   * Production of batch b: its tokens' scale-out records are written with
+//     device-scope stores (through the XCD's L2 to the device's coherence
+//     point); each wave waits until its stores are acknowledged, and after a
+//     barrier one thread stores the batch's flag = epoch (device scope).
+//   * Forwarding of batch b: one thread waits for the flag (device-scope
+//     polls, bounded by `timeout` clock ticks, after which the batch is
+//     skipped with EP_DEVERR_TIMEOUT); after a barrier the group rows of the
+//     batch's tokens are read with device-scope loads and forwarded as in
+//     step 2 (block flags checked, record's src and ids, the layout's
+//     slots).
+// Default schedule (EP_FUSED_LAG > 0), a fixed lag: one counter hands out
+// jobs 0 .. nbatch + lag - 1 in order, and job i produces batch i, then
+// forwards batch i - lag. A group row is therefore read back a bounded
+// number of batches after it was written, while it is still in the
+// memory-side cache (the 256 MB MALL) instead of being fetched from HBM;
+// with the grid held to about four busy waves per CU, the records in flight
+// stay well inside that cache. The other schedule (EP_FUSED_LAG = 0) hands
+// out forwarding as soon as a flag is seen and otherwise production, from
+// two counters; production then runs far ahead of forwarding and the rows
+// come back from HBM.
+// Either way a workgroup waits only for a batch whose production another
+// running workgroup has already taken on, and production never waits, so
+// every wait ends even if the grid is not co-resident; the time limit covers
+// the rest. Counters and flags live in the workspace and are zeroed by a
+// one-workgroup kernel launched just before (stream ordered, no memset node).
 // ---------------------------------------------------------------------------
 #ifndef EP_FUSED_WPB
-#define EP_FUSED_WPB 8  // waves per workgroup of the workgroup-level fused kernel
+#define EP_FUSED_WPB 2  // waves per workgroup of the workgroup-level fused kernel
+#endif
+#ifndef EP_FUSED_WG_PER_CU
+#define EP_FUSED_WG_PER_CU 2  // > 0: at most this many fused workgroups per CU (0: all resident)
+#endif
+#ifndef EP_FUSED_LAG
+#define EP_FUSED_LAG 64  // > 0: job i produces batch i, then forwards batch i - EP_FUSED_LAG
 #endif
 constexpr int kFusedWaves = EP_FUSED_WPB;
 constexpr int kFusedThreads = kFusedWaves * kWave;
@@ -378,6 +399,7 @@ struct FusedArgs {
     int tile;               // tokens per batch
     int nbatch;             // ceil(T / tile)
     int withhold;           // batch whose flag is never published (-1: none)
+    int lag;                // fixed-lag schedule: batches between production and forwarding
     uint64_t timeout;       // wall-clock ticks a batch wait may last
     uint32_t* ctr;          // [0] next batch to produce, [1] next batch to forward
     uint32_t* flags;        // [nbatch] epoch once batch b is written
@@ -485,6 +507,44 @@ __global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) 
         if (kind == 2 && lane == 0) ok = wait_batch(f, job) ? 1 : 0;
         if (!readlane(ok, 0)) continue;
         for (int t = t0; t < t1; ++t) forward_token<true>(a, t);
+    }
+}
+#elif EP_FUSED_LAG > 0
+// Fixed-lag schedule: one counter hands out jobs 0 .. nbatch + lag - 1 in
+// order; job i writes batch i (if i < nbatch) and publishes its flag, then
+// forwards batch i - lag (if i >= lag), waiting for its flag. Batch i - lag
+// was handed out before job i to a running workgroup that writes it before
+// it waits for anything, so every wait ends; a group row is read about `lag`
+// jobs after it was written.
+__global__ __launch_bounds__(kFusedThreads) void fused_hier_kernel(FusedArgs f) {
+    const HierArgs& a = f.h;
+    __shared__ int sh_job, sh_ok;
+    const int wave = wave_in_block();
+    const int njobs = f.nbatch + f.lag;
+    for (;;) {
+        if (threadIdx.x == 0) sh_job = (int)atomicAdd(&f.ctr[0], 1u);
+        __syncthreads();
+        const int job = sh_job;
+        __syncthreads();
+        if (job >= njobs) return;
+        if (job < f.nbatch) {
+            const int t0 = job * f.tile, t1 = min(a.T, t0 + f.tile);
+            for (int t = t0 + wave; t < t1; t += kFusedWaves)
+                scaleout_token<1, kPieceIters, kStoreDevice>(a, t, 0);
+            wait_vmem();
+            __syncthreads();
+            if (threadIdx.x == 0 && job != f.withhold)
+                __hip_atomic_store(&f.flags[job], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const int fb = job - f.lag;
+        if (fb < 0) continue;
+        if (threadIdx.x == 0) sh_ok = wait_batch(f, fb) ? 1 : 0;
+        __syncthreads();
+        const int ok = sh_ok;
+        __syncthreads();
+        if (!ok) continue;
+        const int t0 = fb * f.tile, t1 = min(a.T, t0 + f.tile);
+        for (int t = t0 + wave; t < t1; t += kFusedWaves) forward_token<true>(a, t);
     }
 }
 #else
@@ -650,14 +710,20 @@ hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tok
     f.tile = tile;
     f.nbatch = (s.T + tile - 1) / tile;
     f.withhold = withhold;
+    f.lag = EP_FUSED_LAG;
     f.ctr = reinterpret_cast<uint32_t*>(ws + W.fused);
     f.flags = f.ctr + kFusedCounters;
     FusedDeviceInfo d;
     const hipError_t e = fused_device_info(st, &d);
     if (e != hipSuccess) return e;
     f.timeout = (uint64_t)timeout_us * (uint64_t)(d.rate_khz > 0 ? d.rate_khz : 100000) / 1000u;
-    // No more workgroups than are resident at once (more would find no work).
-    const int resident = std::max(1, d.cus * std::max(1, d.per_cu));
+    // No more workgroups than are resident at once (more would find no work),
+    // and at most EP_FUSED_WG_PER_CU per CU: at hier8x8's shapes about four
+    // busy waves per CU keep the records between a batch's production and
+    // its forwarding in the MALL (698.6 us for the launch with 2 workgroups
+    // of 2 waves per CU, 1,003 us with 1, 786 us with 1.5).
+    const int per_cu = EP_FUSED_WG_PER_CU > 0 ? std::min(d.per_cu, EP_FUSED_WG_PER_CU) : d.per_cu;
+    const int resident = std::max(1, d.cus * std::max(1, per_cu));
     const int jobs_per_block = EP_FUSED_WAVE ? kWavesPerBlock : 1;
     const int blocks = std::min(resident, std::max(1, (2 * f.nbatch + jobs_per_block - 1) / jobs_per_block));
     hipLaunchKernelGGL(fused_reset_kernel, dim3(1), dim3(kBlockThreads), 0, st, f.ctr, f.flags, f.nbatch);

@@ -205,8 +205,11 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 //   * column q*256 + thread of this workgroup's slice of experts.
 constexpr int kVecRounds = (2 * EP_MAX_RANKS + EP_MAX_GROUPS + 4 * kBlockThreads - 1) / (4 * kBlockThreads);
 constexpr int kSliceRounds = EP_MAX_EXPERTS / kBlockThreads;
-constexpr int kRowBatch = 8;
-constexpr int kSpreadStride = 17;  // ints per (thread group, column) partial: 2 x (4 + 4) + 1  // table rows (workgroups) loaded per batch (measured best of 8, 16, 32)
+#ifndef EP_LAYOUT_ROWBATCH
+#define EP_LAYOUT_ROWBATCH 8  // table rows (workgroups) loaded per batch
+#endif
+constexpr int kRowBatch = EP_LAYOUT_ROWBATCH;
+constexpr int kSpreadStride = 17;  // ints per (thread group, column) partial: 2 x (4 + 4) + 1
 // Scan slots of the LDS scratch, one int per wave each.
 constexpr int kScRank = 0;                          // rank totals, per vector round
 constexpr int kScLane = kScRank + kVecRounds;       // lane totals, per vector round

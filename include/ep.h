@@ -234,26 +234,26 @@ int ep_hierarchical_dispatch(const ep_shape *shape, const ep_layout *layout,
                              int64_t peer_cap, void *ws, size_t ws_bytes, void *stream);
 
 /* Both two-level steps in one persistent launch, forwarders consuming each
- * batch of records as soon as its flag is published ([ASC] 方案一 and the
+ * batch of records once its flag is published ([ASC] 方案一 and the
  * hierarchical Stage1: the batch's payload written without ordering, then
  * one ordered flag per batch; [PIPE] forward warps: records taken from the
  * scale-out buffer as they arrive, each wait bounded by a time limit).
  * Batch b = tokens [b * tile, (b+1) * tile). A workgroup writing batch b's
- * group rows (as step EP_HIER_SCALEOUT) makes them visible device-wide (a
- * release fence per wave), then stores flag b = epoch; a workgroup
+ * group rows (as step EP_HIER_SCALEOUT) stores them with device scope, waits
+ * until they are acknowledged, then stores flag b = epoch; a workgroup
  * forwarding batch b waits for that flag (at most timeout_us; then the
- * batch's rows are not forwarded and EP_DEVERR_TIMEOUT is set), acquires,
- * and forwards the group rows of the batch's tokens (as step
- * EP_HIER_FORWARD, block flags checked). Batches are forwarded in order,
- * each as soon as it is published while production is still running. The
- * results are those of ep_hierarchical_dispatch with both steps, byte for
- * byte. Same arguments and requirements as ep_hierarchical_dispatch with
- * steps = 3; the workspace (ep_workspace_bytes) also holds the batch flags
- * and work counters, which the call zeroes first with a small kernel (no
- * memset), so calls on one workspace must not overlap. opts may be NULL
- * (defaults); all-zero fields mean the defaults. */
+ * batch's rows are not forwarded and EP_DEVERR_TIMEOUT is set) and forwards
+ * the group rows of the batch's tokens (as step EP_HIER_FORWARD, block flags
+ * checked). Jobs are handed out in order and job i writes batch i, then
+ * forwards batch i - 64, so each group row is read back shortly after it was
+ * written. The results are those of ep_hierarchical_dispatch with both
+ * steps, byte for byte. Same arguments and requirements as
+ * ep_hierarchical_dispatch with steps = 3; the workspace (ep_workspace_bytes)
+ * also holds the batch flags and work counters, which the call zeroes first
+ * with a small kernel (no memset), so calls on one workspace must not
+ * overlap. opts may be NULL (defaults); all-zero fields mean the defaults. */
 typedef struct ep_fused_opts {
-    int32_t tile_tokens;    /* tokens per batch, 1..64 (0: 8) */
+    int32_t tile_tokens;    /* tokens per batch, 1..64 (0: 2) */
     uint32_t timeout_us;    /* longest wait for one batch flag (0: 100000 us) */
     uint32_t test_flags;    /* EP_FUSED_WITHHOLD: batch `withhold_batch`'s flag is never
                                published, to test the bounded wait (its group rows are
