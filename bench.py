@@ -139,6 +139,7 @@ KERNEL_FILES = {
     "scaleout_kernel": ["hier.hip"],
     "copy_epilogue_kernel": ["source.hip"],
     "combine_group_kernel+combine_cross_kernel": ["combine2.hip"],
+    "combine_two_level_fused_kernel": ["combine2.hip"],
 }
 COMMON_FILES = ["ep_device.h", "ep_internal.h", "api.hip"]
 
@@ -152,6 +153,16 @@ def kernel_source_hash(kernel: str) -> str:
         h.update(open(os.path.join(csrc, f), "rb").read())
     h.update(open(os.path.join(ROOT, "include", "ep.h"), "rb").read())
     return h.hexdigest()[:16]
+
+
+def two_level_combine_kernel(H: int, K: int) -> str:
+    """The launch ep_combine_two_level makes with both steps: one fused kernel
+    when K <= 8 and a token's slices of 4 wave-iterations fill a 4-wave
+    workgroup evenly, else the group and cross kernels."""
+    blocks = (2 * H + 479) // 480
+    slices = ((blocks + 1) // 2 + 3) // 4
+    return "combine_two_level_fused_kernel" if K <= 8 and 4 % slices == 0 else \
+        "combine_group_kernel+combine_cross_kernel"
 
 
 def committed_traffic(workload: str, kernel: str):
@@ -519,7 +530,7 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
     kernel_of = {"layout": "layout_*", "dispatch": "dispatch_kernel", "send": "scaleout_kernel",
                  "epilogue": "copy_epilogue_kernel",
                  "hier": "fused_hier_kernel" if fused else "scaleout_kernel+forward_kernel",
-                 "combine": "combine_group_kernel+combine_cross_kernel" if two_level else "combine_kernel"}
+                 "combine": (two_level_combine_kernel(w.H, w.K) if two_level else "combine_kernel")}
     dom = max(names[1:], key=lambda n: avg_ms[n])
     achieved = by[dom] / (avg_ms[dom] * 1e-3) / 1e9
     label = w.name + ("_fp8" if fp8 else "") + ("_expand" if expand else "") + \

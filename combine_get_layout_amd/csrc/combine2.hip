@@ -28,11 +28,29 @@
 // token run a second pass without it (error path only). Past 16 top-k lanes,
 // any-K kernels check each row's flags in a short pass before its values are
 // used and take the token's groups one at a time.
+#include <algorithm>
+#include <mutex>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 
 #ifndef EP_C2_ROWS
 #define EP_C2_ROWS 1  // both steps: row-streaming kernels when K <= 8 (0 = one wave per token)
+#endif
+#ifndef EP_C2_FUSED
+#define EP_C2_FUSED 1  // both steps asked for, row-streaming shapes: one persistent launch (fixed lag)
+#endif
+#ifndef EP_C2F_TILE
+#define EP_C2F_TILE 1  // fused launch: tokens per batch
+#endif
+#ifndef EP_C2F_LAG
+#define EP_C2F_LAG 128  // fused launch: job i reduces batch i's groups, then batch i - EP_C2F_LAG across groups
+#endif
+#ifndef EP_C2F_MINW
+#define EP_C2F_MINW 1  // fused launch: minimum waves per SIMD the compiler must allow (launch bound)
+#endif
+#ifndef EP_C2F_WG_PER_CU
+#define EP_C2F_WG_PER_CU 0  // fused launch: at most this many workgroups per CU (0: all resident)
 #endif
 
 namespace ep {
@@ -224,14 +242,24 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_kernel(Combine2Ar
 // flags failed to LDS and meet at one barrier (reached once by every wave of
 // the workgroup), and a token with a dropped row is computed again without
 // it (error path only; the second pass rewrites the partial slices).
-template <int VPW>
-__global__ __launch_bounds__(kBlockThreads) void combine_group_rows_kernel(Combine2Args a, int slices) {
+// Device-scope 16-byte store / load at byte `off` of a row of `bytes` bytes
+// (a buffer resource over the row; cache-policy 16 is the device-scope bit,
+// sc1): stores go through the XCD's L2 to the device's coherence point, and
+// loads do not hit stale lines of another XCD's writes.
+constexpr int kC2DeviceScope = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t c2_rsrc(const void* row, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, (int)bytes, 0x00020000);
+}
+
+// One token's group step, slice `part` of `slices` (the slices of a token are
+// consecutive waves of one workgroup). DEV: the partial rows are stored with
+// device scope (the fused launch reads them back in the same kernel);
+// otherwise non-temporal stores.
+template <int VPW, bool DEV>
+__device__ __forceinline__ void group_rows_token(const Combine2Args& a, int t, int part, int slices, bool live,
+                                                 uint32_t* drop_lds) {
     constexpr int KMAX = 8;
-    __shared__ uint32_t drop_lds[kWavesPerBlock];
     const int lane = lane_id(), wave = wave_in_block();
-    const int gw = blockIdx.x * kWavesPerBlock + wave;
-    const int t = gw / slices, part = gw % slices;
-    const bool live = t < a.T;
     int s = -1, g = -1, gs = -1;
     float wt = 0.f;
     if (live && lane < a.K) {
@@ -312,7 +340,9 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_rows_kernel(Combi
             u32x4 o = {0u, 0u, 0u, 0u};
             if (hv[j] && !zero) o = pack8(acc[j]);
             if (fw[j]) o = flagv;
-            st16_stream(prow + o_off[j], o);
+            if constexpr (DEV) __builtin_amdgcn_raw_buffer_store_b128(o, c2_rsrc(prow, a.pstride), (int)o_off[j], 0,
+                                                                      kC2DeviceScope);
+            else st16_stream(prow + o_off[j], o);
         }
     };
     for (int pass = 0; pass < 2; ++pass) {
@@ -399,6 +429,14 @@ __global__ __launch_bounds__(kBlockThreads) void combine_group_rows_kernel(Combi
             if ((drop >> k) & 1) drop |= (uint32_t)__ballot(use && s == readlane(s, min(k, a.K - 1)));
         um &= ~(uint64_t)drop;
     }
+}
+
+template <int VPW>
+__global__ __launch_bounds__(kBlockThreads) void combine_group_rows_kernel(Combine2Args a, int slices) {
+    __shared__ uint32_t drop_lds[kWavesPerBlock];
+    const int gw = blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int t = gw / slices;
+    group_rows_token<VPW, false>(a, t, gw % slices, slices, t < a.T, drop_lds);
 }
 
 template <int GMAX>
@@ -508,14 +546,14 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_kernel(Combine2Ar
 // requested first, and summed in fp32; flags are checked by the flag lanes of
 // the same loads and exchanged between the slices through LDS at one barrier,
 // as in the group step.
-template <int VPW>
-__global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combine2Args a, int slices) {
+// One token's cross step, slice `part` of `slices`. DEV: the partial rows are
+// read with device scope (written by other workgroups of the same launch);
+// otherwise non-temporal loads.
+template <int VPW, bool DEV>
+__device__ __forceinline__ void cross_rows_token(const Combine2Args& a, int t, int part, int slices, bool live,
+                                                 uint32_t* drop_lds) {
     constexpr int GMAX = 8;
-    __shared__ uint32_t drop_lds[kWavesPerBlock];
     const int lane = lane_id(), wave = wave_in_block();
-    const int gw = blockIdx.x * kWavesPerBlock + wave;
-    const int t = gw / slices, part = gw % slices;
-    const bool live = t < a.T;
     int g = -1, gs = -1;
     if (live && lane < a.K) {
         const int64_t e = a.topk[(int64_t)t * a.K + lane];
@@ -587,7 +625,11 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combi
             {
                 const uint8_t* r0 = row_at(cur);
 #pragma unroll
-                for (int j = 0; j < VPW; ++j) vb[0][j] = ld16_stream(r0 + off[j]);
+                for (int j = 0; j < VPW; ++j) {
+                    if constexpr (DEV) vb[0][j] = __builtin_amdgcn_raw_buffer_load_b128(c2_rsrc(r0, a.pstride), (int)off[j], 0,
+                                                                                        kC2DeviceScope);
+                    else vb[0][j] = ld16_stream(r0 + off[j]);
+                }
             }
             const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.err) + (lane & 15) * 16;
 #pragma unroll
@@ -595,8 +637,20 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combi
                 const int nxt = rest ? __ffs(rest) - 1 : -1;
                 {
                     const uint8_t* rn = row_at(nxt < 0 ? cur : nxt);
+                    if constexpr (DEV) {
+                        // After the last row the request reads the workspace's
+                        // error words (in bounds; the values are not used).
+                        const __amdgpu_buffer_rsrc_t rs =
+                            c2_rsrc(nxt >= 0 ? static_cast<const void*>(rn) : static_cast<const void*>(a.err),
+                                    nxt >= 0 ? a.pstride : 256);
 #pragma unroll
-                    for (int j = 0; j < VPW; ++j) vb[(i + 1) & 1][j] = ld16_stream(nxt >= 0 ? rn + off[j] : spare);
+                        for (int j = 0; j < VPW; ++j)
+                            vb[(i + 1) & 1][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                                rs, nxt >= 0 ? (int)off[j] : (lane & 15) * 16, 0, kC2DeviceScope);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < VPW; ++j) vb[(i + 1) & 1][j] = ld16_stream(nxt >= 0 ? rn + off[j] : spare);
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < VPW; ++j) {
@@ -629,6 +683,99 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combi
         if (!drop || !live) return;
         if (lane == 0 && part == 0) report(a.err, EP_DEVERR_FLAG);
         fm &= ~(uint64_t)drop;
+    }
+}
+
+template <int VPW>
+__global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combine2Args a, int slices) {
+    __shared__ uint32_t drop_lds[kWavesPerBlock];
+    const int gw = blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int t = gw / slices;
+    cross_rows_token<VPW, false>(a, t, gw % slices, slices, t < a.T, drop_lds);
+}
+
+// ---------------------------------------------------------------------------
+// Both steps in one persistent launch, with one flag per batch of tokens (the
+// per-batch publication of "Ascend Send Ordering", 方案一, applied to the
+// partial rows). One counter hands out jobs 0 .. nbatch + lag - 1 in order;
+// job i runs the group step for the tokens of batch i (partial rows stored
+// with device scope), waits until its stores are acknowledged and publishes
+// flag i = epoch, then runs the cross step for batch i - lag (waiting for its
+// flag, bounded by `timeout` clock ticks; on expiry EP_DEVERR_TIMEOUT and the
+// batch's outputs are not written), reading the partial rows with device
+// scope. A partial row is read back shortly after it was written, while it is
+// still in the memory-side cache (the MALL) rather than in HBM alone. Unlike
+// the fused dispatch, whose waves each hold a whole record in flight, a
+// combine wave streams one or two rows at a time, so this launch wants every
+// resident workgroup (3 per CU at its register count) and one-token batches:
+// at hier8x8 746 us against 889 us for the two launches (tile 2: 783 us,
+// tile 8: 1,036 us; one workgroup per CU: 1,281 us). Batch i
+// - lag was handed out before job i to a running workgroup that writes it
+// before it waits for anything, so every wait ends, co-resident or not. The
+// arithmetic is that of the two launches, so the results are identical.
+// ---------------------------------------------------------------------------
+struct C2Fused {
+    int tile, nbatch, lag;
+    uint64_t timeout;       // wall-clock ticks a batch wait may last
+    uint32_t* ctr;          // [0] next job
+    uint32_t* flags;        // [nbatch] epoch once batch b's partial rows are written
+};
+
+__global__ void c2_reset_kernel(uint32_t* words, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) words[i] = 0u;
+}
+
+__device__ __forceinline__ bool c2_wait_flag(const uint32_t* flag, uint32_t epoch, uint64_t timeout) {
+    const uint64_t start = (uint64_t)wall_clock64();
+    for (;;) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) return true;
+        if ((uint64_t)wall_clock64() - start > timeout) return false;
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
+template <int VPW>
+__global__ __launch_bounds__(kBlockThreads, EP_C2F_MINW) void combine_two_level_fused_kernel(Combine2Args a, int slices, C2Fused f) {
+    __shared__ uint32_t drop_lds[kWavesPerBlock];
+    __shared__ int sh_job, sh_ok;
+    const int wave = wave_in_block();
+    const int per = kWavesPerBlock / slices;  // tokens per pass of the workgroup
+    const int sub = wave / slices, part = wave % slices;
+    const int njobs = f.nbatch + f.lag;
+    for (;;) {
+        if (threadIdx.x == 0) sh_job = (int)atomicAdd(&f.ctr[0], 1u);
+        __syncthreads();
+        const int job = sh_job;
+        __syncthreads();
+        if (job >= njobs) return;
+        if (job < f.nbatch) {
+            const int t0 = job * f.tile, t1 = min(a.T, t0 + f.tile);
+            for (int tb = t0; tb < t1; tb += per) {
+                group_rows_token<VPW, true>(a, tb + sub, part, slices, tb + sub < t1, drop_lds);
+                __syncthreads();  // drop_lds is reused by the next token
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are acknowledged
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&f.flags[job], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const int fb = job - f.lag;
+        if (fb < 0) continue;
+        if (threadIdx.x == 0) {
+            const bool ok = c2_wait_flag(&f.flags[fb], a.epoch, f.timeout);
+            if (!ok) report(a.err, EP_DEVERR_TIMEOUT);
+            sh_ok = ok ? 1 : 0;
+        }
+        __syncthreads();
+        const int ok = sh_ok;
+        __syncthreads();
+        if (!ok) continue;
+        const int t0 = fb * f.tile, t1 = min(a.T, t0 + f.tile);
+        for (int tb = t0; tb < t1; tb += per) {
+            cross_rows_token<VPW, true>(a, tb + sub, part, slices, tb + sub < t1, drop_lds);
+            __syncthreads();
+        }
     }
 }
 
@@ -810,6 +957,39 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_any_kernel(Combin
 
 }  // namespace
 
+// Per-device launch facts of the fused two-level combine (wall-clock rate in
+// kHz, CUs, resident workgroups per CU), queried on the first call on each
+// device and kept, so that later calls (also under stream capture) make no
+// queries.
+struct C2DeviceInfo {
+    int rate_khz, cus, per_cu;
+};
+constexpr uint32_t kC2FusedTimeoutUs = 100000;  // longest wait for one batch flag
+
+static hipError_t c2_device_info(hipStream_t st, C2DeviceInfo* out) {
+    constexpr int kMaxDev = 64;
+    static C2DeviceInfo info[kMaxDev];
+    static bool known[kMaxDev];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!known[dev]) {
+        C2DeviceInfo d = {0, 0, 0};
+        if ((e = hipDeviceGetAttribute(&d.rate_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
+        if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu, combine_two_level_fused_kernel<4>,
+                                                              kBlockThreads, 0)) != hipSuccess)
+            return e;
+        info[dev] = d;
+        known[dev] = true;
+    }
+    *out = info[dev];
+    return hipSuccess;
+}
+
 hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const int64_t* topk,
                                     const void* y, int64_t y_rows, int64_t y_stride, int fmt,
                                     uint32_t epoch, const float* w, void* group_buf,
@@ -839,6 +1019,25 @@ hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const
     const int iters = (nblk + 1) / 2;
     constexpr int kGroupVpw = 4;
     const int slices = (iters + kGroupVpw - 1) / kGroupVpw;
+    if (steps == 3 && EP_C2_FUSED && s.K <= 8 && EP_C2_ROWS && kWavesPerBlock % slices == 0) {
+        C2DeviceInfo d;
+        const hipError_t e = c2_device_info(st, &d);
+        if (e != hipSuccess) return e;
+        C2Fused f;
+        f.tile = EP_C2F_TILE;
+        f.nbatch = (s.T + f.tile - 1) / f.tile;
+        f.lag = EP_C2F_LAG;
+        f.timeout = (uint64_t)kC2FusedTimeoutUs * (uint64_t)(d.rate_khz > 0 ? d.rate_khz : 100000) / 1000u;
+        f.ctr = reinterpret_cast<uint32_t*>(ws + W.fused);
+        f.flags = f.ctr + kFusedCounters;
+        const int per_cu = EP_C2F_WG_PER_CU > 0 ? std::min(d.per_cu, EP_C2F_WG_PER_CU) : d.per_cu;
+        const int blocks = std::min(std::max(1, d.cus * std::max(1, per_cu)), std::max(1, 2 * f.nbatch));
+        const int words = kFusedCounters + f.nbatch;  // f.flags follows the counter words
+        hipLaunchKernelGGL(c2_reset_kernel, dim3((words + kBlockThreads - 1) / kBlockThreads), block, 0, st,
+                           f.ctr, words);
+        hipLaunchKernelGGL(combine_two_level_fused_kernel<kGroupVpw>, dim3(blocks), block, 0, st, a, slices, f);
+        return hipGetLastError();
+    }
     if ((steps & 1) && s.K <= 8 && EP_C2_ROWS && (!a.y_chunked || kWavesPerBlock % slices == 0)) {
         const dim3 g2((unsigned)(((int64_t)s.T * slices + kWavesPerBlock - 1) / kWavesPerBlock));
         hipLaunchKernelGGL(combine_group_rows_kernel<kGroupVpw>, g2, block, 0, st, a, slices);

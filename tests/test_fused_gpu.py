@@ -86,6 +86,7 @@ def test_fused_small_first():
 @pytest.mark.parametrize("T,H,K,E,R,G,tile,fp8", [
     (1000, 512, 6, 64, 16, 4, 64, False),     # ragged last batch
     (1000, 512, 6, 64, 16, 4, 4, False),      # small batches
+    (1000, 512, 6, 64, 16, 4, 2, False),      # the default batch: 500 batches, many more than the lag
     (300, 256, 4, 32, 8, 4, 1, False),        # one token per batch
     (50, 512, 6, 64, 16, 4, 64, False),       # one batch holds every token
     (777, 1024, 8, 128, 32, 8, 16, True),     # FP8 + scales, many small batches
@@ -124,6 +125,31 @@ def test_fused_repeated_calls_new_epochs():
         ep.ep_hierarchical_dispatch_fused(shape, L, tk, epoch, gb, cap, pb, cap, ws, tile=32)
         torch.cuda.synchronize()
         O, Hd = expected(w, inp, epoch)
+        GR, N = Hd["group_buf"].shape[0], Hd["peer_buf"].shape[0]
+        np.testing.assert_array_equal(host(gb)[:GR], Hd["group_buf"], err_msg=f"call {call}")
+        np.testing.assert_array_equal(host(pb)[:N], Hd["peer_buf"], err_msg=f"call {call}")
+        assert ep.ep_check_errors(ws) == 0
+
+
+def test_fused_same_epoch_twice():
+    """Two calls with the same epoch on one workspace and new tokens: the
+    call's reset kernel clears the previous call's flags, so no batch of the
+    second call is forwarded before it is written."""
+    w = synth.Workload("fz_same", 1200, 512, 64, 16, 4, 6, "uniform")
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, w.G)
+    ws = ep.alloc_workspace(shape)
+    stride = ep.ep_chunked_record_bytes(shape, ep.EP_SEG_BF16)
+    cap = w.T * min(w.K, w.R)
+    gb = torch.zeros((cap, stride), dtype=torch.uint8, device="cuda")
+    pb = torch.zeros((cap, stride), dtype=torch.uint8, device="cuda")
+    L = ep.alloc_layout(shape, masks=False, groups=True)
+    for call in range(2):
+        inp = synth.make_inputs(w, seed=60 + call)
+        tk = dict(x=dev(inp["x"]), topk_idx=dev(inp["topk_idx"]), topk_weights=dev(inp["topk_w"]))
+        ep.ep_get_layout(shape, tk["topk_idx"], L, ws)
+        ep.ep_hierarchical_dispatch_fused(shape, L, tk, 7, gb, cap, pb, cap, ws)
+        torch.cuda.synchronize()
+        O, Hd = expected(w, inp, 7)
         GR, N = Hd["group_buf"].shape[0], Hd["peer_buf"].shape[0]
         np.testing.assert_array_equal(host(gb)[:GR], Hd["group_buf"], err_msg=f"call {call}")
         np.testing.assert_array_equal(host(pb)[:N], Hd["peer_buf"], err_msg=f"call {call}")

@@ -867,7 +867,10 @@ def test_two_level_combine_chunked(name):
                                          (300, 1032, 24, 64, 16, 4), (150, 264, 40, 128, 64, 64),
                                          (77, 4608, 64, 128, 32, 8), (50, 520, 17, 34, 17, 1),
                                          (40, 16384, 8, 64, 16, 4), (30, 16384, 24, 64, 16, 4),
-                                         (100, 1024, 64, 1024, 512, 256)])
+                                         (100, 1024, 64, 1024, 512, 256),
+                                         # one launch with rows of 2 and 4 slices of 8 blocks
+                                         (200, 2048, 8, 64, 16, 4), (96, 3840, 5, 40, 8, 2),
+                                         (60, 5768, 8, 64, 16, 4)])
 def test_two_level_combine_plain(T, H, K, E, R, G):
     w = synth.Workload("edge", T, H, E, R, G, K, "uniform")
     rng = np.random.default_rng(T + H + K)
