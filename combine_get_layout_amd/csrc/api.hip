@@ -2,6 +2,8 @@
 // and record sizing, and the kernel launches (declared in include/ep.h).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "ep.h"
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -31,6 +33,37 @@ WsLayout ws_layout(const ep_shape& s) {
 }
 
 static int pad16_vecs(int64_t bytes) { return (int)((bytes + 15) / 16); }
+
+hipError_t launch_info(hipStream_t st, const void* kernel, int block_threads, LaunchInfo* out) {
+    struct Entry {
+        int dev;
+        const void* kernel;
+        int threads;
+        LaunchInfo info;
+    };
+    constexpr int kMaxEntries = 256;  // (device, kernel) pairs: a few kernels on up to 64 devices
+    static Entry cache[kMaxEntries];
+    static int n_cache = 0;
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_cache; ++i) {
+        if (cache[i].dev == dev && cache[i].kernel == kernel && cache[i].threads == block_threads) {
+            *out = cache[i].info;
+            return hipSuccess;
+        }
+    }
+    LaunchInfo d = {0, 0, 0};
+    if ((e = hipDeviceGetAttribute(&d.rate_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu, kernel, block_threads, 0)) != hipSuccess)
+        return e;
+    if (n_cache < kMaxEntries) cache[n_cache++] = {dev, kernel, block_threads, d};
+    *out = d;
+    return hipSuccess;
+}
 
 RecordGeom record_geom(const ep_shape& s, int seg) {
     RecordGeom g;

@@ -29,7 +29,6 @@
 // any-K kernels check each row's flags in a short pass before its values are
 // used and take the token's groups one at a time.
 #include <algorithm>
-#include <mutex>
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -957,38 +956,7 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_any_kernel(Combin
 
 }  // namespace
 
-// Per-device launch facts of the fused two-level combine (wall-clock rate in
-// kHz, CUs, resident workgroups per CU), queried on the first call on each
-// device and kept, so that later calls (also under stream capture) make no
-// queries.
-struct C2DeviceInfo {
-    int rate_khz, cus, per_cu;
-};
 constexpr uint32_t kC2FusedTimeoutUs = 100000;  // longest wait for one batch flag
-
-static hipError_t c2_device_info(hipStream_t st, C2DeviceInfo* out) {
-    constexpr int kMaxDev = 64;
-    static C2DeviceInfo info[kMaxDev];
-    static bool known[kMaxDev];
-    static std::mutex mu;
-    int dev = 0;
-    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!known[dev]) {
-        C2DeviceInfo d = {0, 0, 0};
-        if ((e = hipDeviceGetAttribute(&d.rate_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
-        if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu, combine_two_level_fused_kernel<4>,
-                                                              kBlockThreads, 0)) != hipSuccess)
-            return e;
-        info[dev] = d;
-        known[dev] = true;
-    }
-    *out = info[dev];
-    return hipSuccess;
-}
 
 hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const int64_t* topk,
                                     const void* y, int64_t y_rows, int64_t y_stride, int fmt,
@@ -1020,8 +988,9 @@ hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const
     constexpr int kGroupVpw = 4;
     const int slices = (iters + kGroupVpw - 1) / kGroupVpw;
     if (steps == 3 && EP_C2_FUSED && s.K <= 8 && EP_C2_ROWS && kWavesPerBlock % slices == 0) {
-        C2DeviceInfo d;
-        const hipError_t e = c2_device_info(st, &d);
+        LaunchInfo d;
+        const hipError_t e = launch_info(st, reinterpret_cast<const void*>(&combine_two_level_fused_kernel<kGroupVpw>),
+                                         kBlockThreads, &d);
         if (e != hipSuccess) return e;
         C2Fused f;
         f.tile = EP_C2F_TILE;

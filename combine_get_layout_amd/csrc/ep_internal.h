@@ -57,6 +57,16 @@ struct RecordGeom {
 };
 RecordGeom record_geom(const ep_shape& s, int seg_flags);
 
+// Launch facts of a persistent kernel on the device of stream `st`: the
+// wall-clock rate (kHz, for bounded waits), the CU count and how many
+// workgroups of `block_threads` threads of `kernel` one CU holds at once.
+// Queried on the first call for each (device, kernel) and kept, so later calls
+// (also under stream capture) make no queries.
+struct LaunchInfo {
+    int rate_khz, cus, per_cu;
+};
+hipError_t launch_info(hipStream_t st, const void* kernel, int block_threads, LaunchInfo* out);
+
 hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout& L, char* ws,
                          hipStream_t st);
 // The allocation-free variant: count tables in the library's per-device

@@ -22,12 +22,12 @@
 //           device; grid-stride past 262,144 rows): check every block's flag,
 //           read src and top-k ids from the record, then stream the row to
 //           each scale-up peer's row.
-//   fused : both steps in one persistent launch; workgroups take batches of
-//           tokens to produce or, once a batch's flag is out, to forward.
+//   fused : both steps in one persistent launch; job i writes batch i of the
+//           tokens' records and publishes its flag, then forwards batch
+//           i - lag, whose records are then still in the MALL.
 // Step 1 also serves several source ranks on one GPU: given one staging row
 // per (token, destination rank) instead of per group, it is their send.
 #include <algorithm>
-#include <mutex>
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -660,40 +660,6 @@ hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& t
     return hipGetLastError();
 }
 
-// Per-device launch facts of the fused kernel (wall-clock rate in kHz, CUs,
-// resident workgroups per CU), queried on the first call on each device and
-// kept, so that later calls (also under stream capture) make no queries.
-struct FusedDeviceInfo {
-    int rate_khz, cus, per_cu;
-};
-
-static hipError_t fused_device_info(hipStream_t st, FusedDeviceInfo* out) {
-    constexpr int kMaxDev = 64;
-    static FusedDeviceInfo info[kMaxDev];
-    static bool known[kMaxDev];
-    static std::mutex mu;
-    int dev = 0;
-    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!known[dev]) {
-        FusedDeviceInfo d = {0, 0, 0};
-        if ((e = hipDeviceGetAttribute(&d.rate_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
-            return e;
-        if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-            return e;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu, fused_hier_kernel,
-                                                              EP_FUSED_WAVE ? kBlockThreads : kFusedThreads, 0)) !=
-            hipSuccess)
-            return e;
-        info[dev] = d;
-        known[dev] = true;
-    }
-    *out = info[dev];
-    return hipSuccess;
-}
-
 hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
                              uint32_t epoch, void* group_buf, int64_t group_cap, void* peer_buf,
                              int64_t peer_cap, int tile, uint32_t timeout_us, int withhold, char* ws,
@@ -715,8 +681,9 @@ hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tok
     f.lag = EP_FUSED_LAG;
     f.ctr = reinterpret_cast<uint32_t*>(ws + W.fused);
     f.flags = f.ctr + kFusedCounters;
-    FusedDeviceInfo d;
-    const hipError_t e = fused_device_info(st, &d);
+    LaunchInfo d;
+    const hipError_t e = launch_info(st, reinterpret_cast<const void*>(&fused_hier_kernel),
+                                     EP_FUSED_WAVE ? kBlockThreads : kFusedThreads, &d);
     if (e != hipSuccess) return e;
     f.timeout = (uint64_t)timeout_us * (uint64_t)(d.rate_khz > 0 ? d.rate_khz : 100000) / 1000u;
     // No more workgroups than are resident at once (more would find no work),
