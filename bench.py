@@ -9,9 +9,11 @@ A step is one pass of the whole path over one batch of synthetic tokens:
                      the two steps as two launches) -> ep_combine on the
                      chunked scale-up rows
   --sources S      : S source ranks (default R) on the flat workloads:
-                     ep_source_layout -> ep_source_dispatch into per-(rank,
-                     source) staging regions -> ep_copy_epilogue into dense
-                     receive rows -> ep_combine over the staging rows
+                     ep_source_layout -> ep_source_dispatch_fused (send into
+                     per-(rank, source) staging regions and copy epilogue into
+                     dense receive rows in one launch; --two-launch:
+                     ep_source_dispatch, then ep_copy_epilogue) -> ep_combine
+                     over the staging rows
 With no --workload the run times every target configuration in turn (ep32,
 ep32 with the FP8 + scales payload, ep256, zipf, hier8x8); the headline
 fields are ep32's and `per_config` holds one entry per configuration. With
@@ -59,11 +61,12 @@ def parse():
                    help="time only this workload (default: every target configuration, ep32 first)")
     p.add_argument("--fp8", action="store_true", help="also move the FP8 payload + scales")
     p.add_argument("--fused", action="store_true",
-                   help="two-level workloads: both dispatch steps in one persistent launch with "
-                        "per-batch flags (ep_hierarchical_dispatch_fused; the default)")
+                   help="two-level workloads and --sources: the one-launch forms with per-batch flags "
+                        "(ep_hierarchical_dispatch_fused, ep_source_dispatch_fused; the default)")
     p.add_argument("--two-launch", action="store_true",
                    help="two-level workloads: the two dispatch steps as two launches "
-                        "(ep_hierarchical_dispatch)")
+                        "(ep_hierarchical_dispatch); --sources: the send and the copy epilogue as "
+                        "two calls")
     p.add_argument("--fused-tile", type=int, default=0,
                    help="tokens per batch of the fused two-level dispatch (0: default)")
     p.add_argument("--two-level-combine", action="store_true",
@@ -137,7 +140,8 @@ KERNEL_FILES = {
     "scaleout_kernel+forward_kernel": ["hier.hip"],
     "fused_hier_kernel": ["hier.hip"],
     "scaleout_kernel": ["hier.hip"],
-    "copy_epilogue_kernel": ["source.hip"],
+    "copy_epilogue_kernel": ["source.hip", "ep_epilogue.h"],
+    "source_fused_kernel": ["hier.hip", "ep_epilogue.h"],
     "combine_group_kernel+combine_cross_kernel": ["combine2.hip"],
     "combine_two_level_fused_kernel": ["combine2.hip"],
 }
@@ -259,17 +263,20 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
     if args.fused and args.two_launch:
         print("--fused and --two-launch exclude each other", file=sys.stderr)
         sys.exit(2)
-    if (args.fused or args.two_launch or args.fused_tile) and not hier:
-        print("--fused, --two-launch and --fused-tile apply to the two-level workloads", file=sys.stderr)
+    multi = args.sources is not None
+    if (args.fused or args.two_launch) and not (hier or multi):
+        print("--fused and --two-launch apply to the two-level workloads and to --sources", file=sys.stderr)
         sys.exit(2)
-    fused = hier and not args.two_launch
+    if args.fused_tile and not hier:
+        print("--fused-tile applies to the two-level workloads", file=sys.stderr)
+        sys.exit(2)
+    fused = (hier or multi) and not args.two_launch
     if two_level and not hier:
         print("--two-level-combine applies to the two-level workloads", file=sys.stderr)
         sys.exit(2)
     if expand and hier:
         print("--expand applies to the flat workloads", file=sys.stderr)
         sys.exit(2)
-    multi = args.sources is not None
     S = (args.sources or w.R) if multi else 1
     if multi and (hier or expand or two_level):
         print("--sources applies to the flat workloads without --expand", file=sys.stderr)
@@ -342,8 +349,8 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
 
     epoch = [0]
     stream = torch.cuda.current_stream()
-    names = (["layout", "send", "epilogue", "combine"] if multi else
-             ["layout", "hier" if hier else "dispatch", "combine"])
+    names = ((["layout", "send+epilogue", "combine"] if fused else ["layout", "send", "epilogue", "combine"])
+             if multi else ["layout", "hier" if hier else "dispatch", "combine"])
     ev = {n: [] for n in names}
     used = []
 
@@ -362,9 +369,13 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
         tokens, N, G_rows = batches[i], Ns[i], Gs[i]
         if multi:
             timed("layout", lambda: ep.ep_source_layout(shape, tokens["topk_idx"], src, ws), record)
-            timed("send", lambda: ep.ep_source_dispatch(shape, src, tokens, e, staging, ws), record)
-            timed("epilogue", lambda: ep.ep_copy_epilogue(shape, src, staging, e, seg, recv, N, ws),
-                  record)
+            if fused:
+                timed("send+epilogue", lambda: ep.ep_source_dispatch_fused(shape, src, tokens, e, staging,
+                                                                           recv, N, ws), record)
+            else:
+                timed("send", lambda: ep.ep_source_dispatch(shape, src, tokens, e, staging, ws), record)
+                timed("epilogue", lambda: ep.ep_copy_epilogue(shape, src, staging, e, seg, recv, N, ws),
+                      record)
             timed("combine", lambda: ep.ep_combine(shape, y_src, staging, staging.shape[0], stride,
                                                    ep.EP_FMT_CHUNKED, e, tokens["topk_weights"],
                                                    out, ws), record)
@@ -514,6 +525,8 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
               "send": T * row + route + N * rec_b,
               "epilogue": N * rec_b + N * (row + meta),
               "combine": N * hid + T * 2 * H + T * K * 8}
+        if fused:
+            by["send+epilogue"] = by.pop("send") + by.pop("epilogue")
     elif hier:
         rec_b = ep.ep_chunked_record_bytes(shape, seg)
         hid = 512 * ((2 * H + 479) // 480)
@@ -528,13 +541,13 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
         by = {"layout": bytes_layout, names[1]: bytes_main, "combine": bytes_combine}
     step_bytes = sum(by.values())
     kernel_of = {"layout": "layout_*", "dispatch": "dispatch_kernel", "send": "scaleout_kernel",
-                 "epilogue": "copy_epilogue_kernel",
+                 "epilogue": "copy_epilogue_kernel", "send+epilogue": "source_fused_kernel",
                  "hier": "fused_hier_kernel" if fused else "scaleout_kernel+forward_kernel",
                  "combine": (two_level_combine_kernel(w.H, w.K) if two_level else "combine_kernel")}
     dom = max(names[1:], key=lambda n: avg_ms[n])
     achieved = by[dom] / (avg_ms[dom] * 1e-3) / 1e9
     label = w.name + ("_fp8" if fp8 else "") + ("_expand" if expand else "") + \
-        ("_2launch" if hier and not fused else "") + ("_2lc" if two_level else "") + (f"_s{S}" if multi else "")
+        ("_2lc" if two_level else "") + (f"_s{S}" if multi else "") + ("_2launch" if (hier or multi) and not fused else "")
     traffic = committed_traffic(label, kernel_of[dom])
 
     if args.copy_calibration:

@@ -400,6 +400,29 @@ int ep_copy_epilogue(const ep_shape* shape, const ep_sources* sources, const voi
                                            static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
 }
 
+int ep_source_dispatch_fused(const ep_shape* shape, const ep_sources* sources, const ep_tokens* tokens,
+                             uint32_t epoch, void* staging, const ep_recv* recv, void* ws, size_t ws_bytes,
+                             void* stream) {
+    int rc = check_sources(shape, sources, ws, ws_bytes);
+    if (rc != EP_OK) return rc;
+    if (!tokens || !recv || recv->capacity < 0 || epoch == 0 || !sources->recv_offsets) return EP_ERR_ARG;
+    const int64_t rows = (int64_t)shape->R * sources->S * sources->capacity;
+    if (shape->T > 0 && (!tokens->x || !tokens->topk_idx || !tokens->topk_weights ||
+                         !sources->src_slot || (rows > 0 && !staging)))
+        return EP_ERR_ARG;
+    if (tokens->x_fp8 && shape->H % 16 != 0) return EP_ERR_ARG;
+    if (tokens->x_scales && shape->H % 128 != 0) return EP_ERR_ARG;
+    if ((recv->x_fp8 && !tokens->x_fp8) || (recv->x_scales && !tokens->x_scales)) return EP_ERR_ARG;
+    if (!aligned(tokens->x, 16) || !aligned(tokens->x_fp8, 16) || !aligned(tokens->x_scales, 4) ||
+        !aligned(tokens->topk_idx, 8) || !aligned(tokens->topk_weights, 4) || !aligned(staging, 16) ||
+        !aligned(sources->src_slot, 4) || !aligned(recv->x, 16) || !aligned(recv->x_fp8, 16) ||
+        !aligned(recv->x_scales, 4) || !aligned(recv->src_idx, 4) || !aligned(recv->topk_idx, 4) ||
+        !aligned(recv->topk_weights, 4) || !aligned(sources->recv_offsets, 4))
+        return EP_ERR_ARG;
+    return hip_status(launch_source_fused(*shape, *sources, *tokens, epoch, staging, *recv,
+                                          static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+}
+
 int ep_clear_errors(void* ws, void* stream) {
     if (!ws || !aligned(ws, 256)) return EP_ERR_ARG;
     hipLaunchKernelGGL(clear_error_kernel, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream),

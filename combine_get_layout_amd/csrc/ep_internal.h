@@ -98,5 +98,9 @@ hipError_t launch_source_layout(const ep_shape& s, const int64_t* topk, const ep
 hipError_t launch_copy_epilogue(const ep_shape& s, const ep_sources& src, const void* staging,
                                 uint32_t epoch, int seg, const ep_recv& rv, char* ws,
                                 hipStream_t st);
+// Send and copy epilogue in one launch (records' pieces as in tokens).
+hipError_t launch_source_fused(const ep_shape& s, const ep_sources& src, const ep_tokens& tk,
+                               uint32_t epoch, void* staging, const ep_recv& rv, char* ws, hipStream_t st);
+constexpr uint32_t kSourceFusedTimeoutUs = 100000;  // longest wait for one batch flag of that launch
 
 }  // namespace ep

@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "ep_device.h"
+#include "ep_epilogue.h"
 #include "ep_internal.h"
 
 namespace ep {
@@ -613,6 +614,121 @@ __global__ __launch_bounds__(kFusedThreads) void fused_hier_kernel(FusedArgs f) 
 
 #endif  // EP_FUSED_WAVE
 
+// ---------------------------------------------------------------------------
+// Several sources, send and copy epilogue in one persistent launch: the
+// receivers take each batch of records as soon as its flag is out ("DeepEP V2
+// 深度深潜", §3.3 阶段2 and 阶段3; "Ascend Send Ordering", 方案一: the batch's
+// records written without ordering, then one flag). The same fixed-lag
+// schedule as the fused two-level dispatch: job i sends batch i's records to
+// their staging rows (device-scope stores, then the batch's flag), then
+// unpacks the staging rows of batch i - lag into their dense receive rows
+// (device-scope loads), shortly after they were written, so they come from
+// the MALL. The staging row (r*S + s)*capacity + j of (t, r) holds dense row
+// recv_offsets[r*S + s] + j, which is the copy epilogue's row; every dense row
+// of a region below its capacity is some (t, r)'s, so the receive rows equal
+// those of the send followed by the copy epilogue. A batch's records are
+// written one token per wave; its staging rows (about D per token) are then
+// listed in LDS and spread over all the workgroup's waves, so that each wave
+// unpacks one or two rows, not a token's D rows one after another: at ep32
+// with 32 sources 251 us against 264 us for the two launches (one token per
+// wave for the unpacking as well: 270-323 us).
+// ---------------------------------------------------------------------------
+#ifndef EP_SRCF_WPB
+#define EP_SRCF_WPB 8  // waves per workgroup
+#endif
+#ifndef EP_SRCF_WG_PER_CU
+#define EP_SRCF_WG_PER_CU 0  // at most this many workgroups per CU (0: all resident, 1 at 162 VGPRs)
+#endif
+#ifndef EP_SRCF_LAG
+#define EP_SRCF_LAG 64  // job i sends batch i, then unpacks batch i - EP_SRCF_LAG
+#endif
+#ifndef EP_SRCF_TILE
+#define EP_SRCF_TILE 4  // tokens per batch (at most EP_SRCF_WPB: one listing wave per token)
+#endif
+constexpr int kSrcFusedWaves = EP_SRCF_WPB;
+static_assert(EP_SRCF_TILE <= EP_SRCF_WPB, "one listing wave per token of a batch");
+
+struct SourceFusedArgs {
+    HierArgs h;        // send: group_slot = src_slot, group_buf = staging, group_cap = its rows
+    EpilogueArgs e;    // unpack into the receive arrays
+    int tile, nbatch, lag;
+    uint64_t timeout;  // wall-clock ticks a batch wait may last
+    uint32_t* ctr;     // [0] next job
+    uint32_t* flags;   // [nbatch] epoch once batch b's records are written
+};
+
+__global__ __launch_bounds__(kSrcFusedWaves * kWave) void source_fused_kernel(SourceFusedArgs f) {
+    const HierArgs& a = f.h;
+    __shared__ int sh_job, sh_ok;
+    const int wave = wave_in_block(), lane = lane_id();
+    const int njobs = f.nbatch + f.lag;
+    for (;;) {
+        if (threadIdx.x == 0) sh_job = (int)atomicAdd(&f.ctr[0], 1u);
+        __syncthreads();
+        const int job = sh_job;
+        __syncthreads();
+        if (job >= njobs) return;
+        if (job < f.nbatch) {
+            const int t0 = job * f.tile, t1 = min(a.T, t0 + f.tile);
+            for (int t = t0 + wave; t < t1; t += kSrcFusedWaves)
+                scaleout_token<1, kPieceIters, kStoreDevice>(a, t, 0);
+            wait_vmem();
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&f.flags[job], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const int fb = job - f.lag;
+        if (fb < 0) continue;
+        if (threadIdx.x == 0) {
+            const uint64_t start = (uint64_t)wall_clock64();
+            bool ok = false;
+            for (;;) {
+                if (flag_load(&f.flags[fb]) == a.epoch) { ok = true; break; }
+                if ((uint64_t)wall_clock64() - start > f.timeout) break;
+                __builtin_amdgcn_s_sleep(8);
+            }
+            if (!ok) report(a.err, EP_DEVERR_TIMEOUT);
+            sh_ok = ok ? 1 : 0;
+        }
+        __syncthreads();
+        const int ok = sh_ok;
+        __syncthreads();
+        if (!ok) continue;
+        const int t0 = fb * f.tile, t1 = min(a.T, t0 + f.tile);
+        // The batch's distinct staging rows go to an LDS list (wave w lists
+        // token t0 + w's, at most K each); then every wave takes rows w, w + W, ...
+        __shared__ int64_t sh_rows[kSrcFusedWaves][EP_MAX_TOPK];
+        __shared__ int sh_n[kSrcFusedWaves];
+        {
+            const int t = t0 + wave;
+            int sr = -1;
+            if (t < t1 && lane < a.K) sr = a.group_slot[(int64_t)t * a.K + lane];
+            bool first = sr >= 0 && sr < a.group_cap;
+            for (int j = 0; j < a.K; ++j)
+                if (j < lane && readlane(sr, j) == sr) first = false;
+            const uint64_t m = __ballot(first);
+            if (first) sh_rows[wave][__popcll(m & ((1ull << lane) - 1))] = sr;
+            if (lane == 0) sh_n[wave] = __popcll(m);
+        }
+        __syncthreads();
+        int total = 0;
+        for (int w = 0; w < kSrcFusedWaves; ++w) total += sh_n[w];
+        for (int e = wave; e < total; e += kSrcFusedWaves) {
+            int w = 0, k = e;
+            while (k >= sh_n[w]) k -= sh_n[w++];
+            const int64_t row = sh_rows[w][k];
+            const int64_t q = row / f.e.cap, j = row - q * f.e.cap;
+            const int64_t i = (int64_t)f.e.offs[q] + j;
+            if (i >= f.e.rcap) {
+                if (lane == 0) report(a.err, EP_DEVERR_CAPACITY);
+                continue;
+            }
+            epilogue_row<true>(f.e, i, a.group_buf + row * a.geom.stride);
+        }
+        __syncthreads();  // the list is rebuilt by the next job
+    }
+}
+
 HierArgs hier_args(const ep_shape& s, const ep_tokens& tk, uint32_t epoch, char* ws) {
     const WsLayout W = ws_layout(s);
     int seg = EP_SEG_BF16 | (tk.x_fp8 ? EP_SEG_FP8 : 0) | (tk.x_scales ? EP_SEG_SCALES : 0);
@@ -713,6 +829,49 @@ hipError_t launch_send_rows(const ep_shape& s, const ep_tokens& tk, const int32_
     hipLaunchKernelGGL(scaleout_kernel,
                        dim3((unsigned)(((int64_t)s.T * kSoSplit + kWavesPerBlock - 1) / kWavesPerBlock)),
                        dim3(kBlockThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_source_fused(const ep_shape& s, const ep_sources& src, const ep_tokens& tk,
+                               uint32_t epoch, void* staging, const ep_recv& rv, char* ws, hipStream_t st) {
+    if (s.T == 0) return hipSuccess;
+    const int seg = EP_SEG_BF16 | (tk.x_fp8 ? EP_SEG_FP8 : 0) | (tk.x_scales ? EP_SEG_SCALES : 0);
+    SourceFusedArgs f;
+    f.h = hier_args(s, tk, epoch, ws);
+    f.h.group_slot = src.src_slot;
+    f.h.group_buf = reinterpret_cast<uint8_t*>(staging);
+    f.h.group_cap = (int64_t)s.R * src.S * src.capacity;
+    EpilogueArgs& e = f.e;
+    e.H = s.H; e.K = s.K; e.RS = s.R * src.S;
+    e.cap = src.capacity;
+    e.geom = record_geom(s, seg);
+    e.offs = src.recv_offsets;
+    e.staging = reinterpret_cast<const uint8_t*>(staging);
+    e.rx = reinterpret_cast<uint8_t*>(rv.x);
+    e.rfp8 = rv.x_fp8;
+    e.rscales = rv.x_scales;
+    e.rsrc = rv.src_idx;
+    e.ridx = rv.topk_idx;
+    e.rw = rv.topk_weights;
+    e.rcap = rv.capacity;
+    e.epoch = epoch;
+    e.err = f.h.err;
+    f.tile = EP_SRCF_TILE;
+    f.nbatch = (s.T + f.tile - 1) / f.tile;
+    f.lag = EP_SRCF_LAG;
+    f.ctr = reinterpret_cast<uint32_t*>(ws + ws_layout(s).fused);
+    f.flags = f.ctr + kFusedCounters;
+    LaunchInfo d;
+    const hipError_t err = launch_info(st, reinterpret_cast<const void*>(&source_fused_kernel),
+                                       kSrcFusedWaves * kWave, &d);
+    if (err != hipSuccess) return err;
+    f.timeout = (uint64_t)kSourceFusedTimeoutUs * (uint64_t)(d.rate_khz > 0 ? d.rate_khz : 100000) / 1000u;
+    const int per_cu = EP_SRCF_WG_PER_CU > 0 ? std::min(d.per_cu, EP_SRCF_WG_PER_CU) : d.per_cu;
+    const int blocks = std::min(std::max(1, d.cus * std::max(1, per_cu)), std::max(1, 2 * f.nbatch));
+    const int words = kFusedCounters + f.nbatch;  // f.flags follows the counter words
+    hipLaunchKernelGGL(fused_reset_kernel, dim3((words + kBlockThreads - 1) / kBlockThreads), dim3(kBlockThreads), 0,
+                       st, f.ctr, words);
+    hipLaunchKernelGGL(source_fused_kernel, dim3(blocks), dim3(kSrcFusedWaves * kWave), 0, st, f);
     return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@
 //                 chunked record (its flag lanes load the flags), checks them
 //                 and stores every field to row i of the receive arrays.
 #include "ep_device.h"
+#include "ep_epilogue.h"
 #include "ep_internal.h"
 
 namespace ep {
@@ -35,7 +36,6 @@ namespace {
 constexpr int kTile = kLayoutTokens;
 constexpr int kTileWords = kTile / 32;
 constexpr int kExchangeThreads = 1024;
-constexpr int kEpiloguePieceIters = 16;  // wave iterations (2 blocks each) held in VGPRs
 
 struct SourceArgs {
     int T, K, E, R, S, Ts, nbs, epr;
@@ -203,23 +203,6 @@ __global__ __launch_bounds__(kBlockThreads) void source_assign_kernel(SourceArgs
     if (over) report(a.err, EP_DEVERR_CAPACITY);
 }
 
-struct EpilogueArgs {
-    int H, K, RS;
-    int64_t cap;
-    RecordGeom geom;
-    const int32_t* offs;
-    const uint8_t* staging;
-    uint8_t* rx;
-    uint8_t* rfp8;
-    float* rscales;
-    int32_t* rsrc;
-    int32_t* ridx;
-    float* rw;
-    int64_t rcap;
-    uint32_t epoch;
-    uint32_t* err;
-};
-
 // Region of dense row i: the largest p < RS with offs[p] <= i (offsets are
 // non-decreasing and offs[0] = 0). Each round probes 64 evenly spaced
 // entries, one per lane, and keeps the interval after the last probe <= i.
@@ -237,47 +220,10 @@ __device__ __forceinline__ int find_region(const int32_t* offs, int RS, int64_t 
     return lo;
 }
 
-// Record vector q of a row, to the receive arrays' row `row`.
-__device__ __forceinline__ void put_vector(const EpilogueArgs& a, int64_t row, int q, u32x4 v) {
-    const RecordGeom& g = a.geom;
-    if (q < g.q_fp8) {
-        if (a.rx) st16_stream(a.rx + row * 2 * a.H + (int64_t)q * 16, v);
-    } else if (q < g.q_scales) {
-        if (a.rfp8) st16_stream(a.rfp8 + row * a.H + (int64_t)(q - g.q_fp8) * 16, v);
-    } else if (q < g.q_idx) {
-        const int ns = a.H / 128, i0 = (q - g.q_scales) * 4;
-        if (a.rscales)
-            for (int m = 0; m < 4; ++m)
-                if (i0 + m < ns) a.rscales[row * ns + i0 + m] = __uint_as_float(v[m]);
-    } else if (q < g.q_w) {
-        const int k0 = (q - g.q_idx) * 4;
-        if (a.ridx)
-            for (int m = 0; m < 4; ++m)
-                if (k0 + m < a.K) a.ridx[row * a.K + k0 + m] = (int32_t)v[m];
-    } else if (q < g.q_src) {
-        const int k0 = (q - g.q_w) * 4;
-        if (a.rw)
-            for (int m = 0; m < 4; ++m)
-                if (k0 + m < a.K) a.rw[row * a.K + k0 + m] = __uint_as_float(v[m]);
-    } else if (q == g.q_src) {
-        if (a.rsrc) a.rsrc[row] = (int32_t)v[0];
-    }
-}
-
-__device__ __forceinline__ bool flag_ok(u32x4 f, uint32_t epoch) {
-    return f[0] == epoch && f[1] == epoch && f[2] == epoch && f[3] == epoch;
-}
-
 __global__ __launch_bounds__(kBlockThreads) void copy_epilogue_kernel(EpilogueArgs a) {
     const int lane = lane_id();
     const int64_t n_rows = a.offs[a.RS];
-    const int nchunks = a.geom.nchunks;
-    const int iters = (nchunks + 1) / 2;
-    const int64_t stride = a.geom.stride;
-    const int c_half = lane >> 5, wv = lane & 31;
-    const bool one_piece = iters <= kEpiloguePieceIters;
     const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerBlock;
-
     for (int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block(); i < n_rows;
          i += wave_stride) {
         const int reg = find_region(a.offs, a.RS, i);
@@ -286,43 +232,7 @@ __global__ __launch_bounds__(kBlockThreads) void copy_epilogue_kernel(EpilogueAr
             if (lane == 0) report(a.err, EP_DEVERR_CAPACITY);
             continue;
         }
-        const uint8_t* src_row = a.staging + ((int64_t)reg * a.cap + j) * stride;
-        u32x4 v[kEpiloguePieceIters];
-        bool ok = true;
-        if (one_piece) {
-            // The whole row at once; lanes past the last block reload it.
-#pragma unroll
-            for (int it = 0; it < kEpiloguePieceIters; ++it) {
-                const int c = min(2 * it + c_half, nchunks - 1);
-                v[it] = ld16_stream(src_row + (int64_t)c * kChunkBytes + (int64_t)wv * 16);
-            }
-#pragma unroll
-            for (int it = 0; it < kEpiloguePieceIters; ++it)
-                ok &= wv < kChunkPayloadVecs || flag_ok(v[it], a.epoch);
-        } else {
-            for (int f = lane; f < 2 * nchunks; f += kWave)
-                ok &= flag_ok(ld16(src_row + (int64_t)(f >> 1) * kChunkBytes + kChunkPayload + (f & 1) * 16),
-                              a.epoch);
-        }
-        if (__ballot(!ok)) {
-            if (lane == 0) report(a.err, EP_DEVERR_FLAG);
-            continue;
-        }
-        for (int it0 = 0; it0 < iters; it0 += kEpiloguePieceIters) {
-            if (!one_piece) {
-#pragma unroll
-                for (int jj = 0; jj < kEpiloguePieceIters; ++jj) {
-                    const int c = min(2 * (it0 + jj) + c_half, nchunks - 1);
-                    v[jj] = ld16_stream(src_row + (int64_t)c * kChunkBytes + (int64_t)wv * 16);
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < kEpiloguePieceIters; ++jj) {
-                const int c = 2 * (it0 + jj) + c_half;
-                if (it0 + jj < iters && c < nchunks && wv < kChunkPayloadVecs)
-                    put_vector(a, i, c * kChunkPayloadVecs + wv, v[jj]);
-            }
-        }
+        epilogue_row<false>(a, i, a.staging + ((int64_t)reg * a.cap + j) * a.geom.stride);
     }
 }
 

@@ -67,7 +67,8 @@ EXPORTS = ("ep_workspace_bytes", "ep_record_bytes", "ep_chunked_record_bytes", "
            "ep_hierarchical_dispatch_fused", "ep_combine",
            "ep_combine_expand", "ep_partial_row_bytes", "ep_combine_two_level",
            "ep_source_workspace_bytes", "ep_source_layout", "ep_source_dispatch",
-           "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors", "ep_check_sticky_errors",
+           "ep_copy_epilogue", "ep_source_dispatch_fused", "ep_clear_errors", "ep_check_errors",
+           "ep_check_sticky_errors",
            "ep_status_string")
 
 _lib = None
@@ -111,6 +112,8 @@ def lib() -> ctypes.CDLL:
     L.ep_source_dispatch.argtypes = [sp, xp, ctypes.POINTER(ep_tokens), u32, _P, _P, sz, _P]
     L.ep_copy_epilogue.argtypes = [sp, xp, _P, u32, ctypes.c_int, ctypes.POINTER(ep_recv), _P, sz,
                                    _P]
+    L.ep_source_dispatch_fused.argtypes = [sp, xp, ctypes.POINTER(ep_tokens), u32, _P,
+                                           ctypes.POINTER(ep_recv), _P, sz, _P]
     L.ep_clear_errors.argtypes = [_P, _P]
     L.ep_check_errors.argtypes = [_P, _P, ctypes.POINTER(u32)]
     L.ep_check_sticky_errors.argtypes = [_P, _P, ctypes.POINTER(u32)]
@@ -119,7 +122,8 @@ def lib() -> ctypes.CDLL:
     for f in ("ep_get_layout", "ep_get_layout_noalloc", "ep_dispatch", "ep_dispatch_expand",
               "ep_hierarchical_dispatch", "ep_hierarchical_dispatch_fused",
               "ep_combine", "ep_combine_expand", "ep_combine_two_level", "ep_source_layout",
-              "ep_source_dispatch", "ep_copy_epilogue", "ep_clear_errors", "ep_check_errors",
+              "ep_source_dispatch", "ep_copy_epilogue", "ep_source_dispatch_fused", "ep_clear_errors",
+              "ep_check_errors",
               "ep_check_sticky_errors"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -355,6 +359,19 @@ def ep_copy_epilogue(shape, sources: dict, staging, epoch: int, seg_flags: int, 
                                   _ptr(staging, "staging", _staging_bytes(shape, sources, int(seg_flags))),
                                   int(epoch), int(seg_flags), ctypes.byref(rv), *_ws(ws),
                                   _stream(stream)), "ep_copy_epilogue")
+
+
+def ep_source_dispatch_fused(shape, sources: dict, tokens: dict, epoch: int, staging, recv: dict,
+                             capacity: int, ws, stream=None):
+    """ep_source_dispatch and ep_copy_epilogue in one launch (the record's
+    pieces are those of `tokens`)."""
+    X = _sources_struct(shape, sources)
+    tk = _tokens_struct(shape, tokens)
+    rv = _recv_struct(shape, recv, capacity)
+    _check(lib().ep_source_dispatch_fused(
+        ctypes.byref(shape), ctypes.byref(X), ctypes.byref(tk), int(epoch),
+        _ptr(staging, "staging", _staging_bytes(shape, sources, _seg_of(tokens))), ctypes.byref(rv),
+        *_ws(ws), _stream(stream)), "ep_source_dispatch_fused")
 
 
 def ep_clear_errors(ws, stream=None):

@@ -378,6 +378,25 @@ int ep_copy_epilogue(const ep_shape *shape, const ep_sources *sources, const voi
                      uint32_t epoch, int seg_flags, const ep_recv *recv, void *ws,
                      size_t ws_bytes, void *stream);
 
+/* Send and copy epilogue in one persistent launch: the same staging rows and
+ * receive rows as ep_source_dispatch followed by ep_copy_epilogue with the
+ * pieces of `tokens` (EP_SEG_BF16, plus EP_SEG_FP8 / EP_SEG_SCALES when
+ * tokens carry them), with the destinations consuming each batch of records
+ * once its flag is published ([V2] §3.3 阶段2 and 阶段3; [ASC] 方案一: a
+ * batch's records written without ordering, then one ordered flag). Jobs are
+ * handed out in order: job i sends the records of tokens [4i, 4i+4) and
+ * publishes the batch, then unpacks the staging rows of batch i - 64 into
+ * their dense rows recv_offsets[r*S+s] + j, while those rows are still in the
+ * MALL. A batch whose flag does not come within 100 ms is not unpacked
+ * (EP_DEVERR_TIMEOUT); rows >= recv->capacity are skipped
+ * (EP_DEVERR_CAPACITY). Needs the arguments of both calls; the workspace
+ * (ep_source_workspace_bytes) also holds the batch flags, which the call
+ * zeroes first with a small kernel, so calls on one workspace must not
+ * overlap. */
+int ep_source_dispatch_fused(const ep_shape *shape, const ep_sources *sources, const ep_tokens *tokens,
+                             uint32_t epoch, void *staging, const ep_recv *recv, void *ws,
+                             size_t ws_bytes, void *stream);
+
 /* Clear both workspace error words (a stream-ordered kernel, no memset
  * node). */
 int ep_clear_errors(void *ws, void *stream);
