@@ -3,7 +3,8 @@ oracle: layout (all outputs, groups and expand rows; also through the
 allocation-free entry point), dispatch with a random subset of payload
 pieces, combine, the two-level chunked dispatch (two launches, and the fused
 one-launch form with a random batch size) with the flat and the two-level
-combine, and expand-mode dispatch and combine.
+combine, expand-mode dispatch and combine, and the several-source send and
+copy epilogue in one launch with a random source count.
 
 The shapes are drawn from a fixed seed list (200 seeds; EP_FUZZ_SEEDS sets
 another count), so a failure names a case that
@@ -200,3 +201,27 @@ def test_fuzz_all_entry_points(seed):
     ep.ep_combine_expand(shape, L, dev(yx), n_rows, 2 * H, ep.EP_FMT_PLAIN, 0, wd, out, ws)
     np.testing.assert_array_equal(host(out), oracle.combine(es, w, yx[:n_rows], H)["out"])
     assert ep.ep_check_errors(ws) == 0
+
+    # several sources: send and copy epilogue in one launch
+    S = int(rng.choice([1, 2, 3, 5, 8]))
+    s1 = ep.make_shape(T, H, K, E, R, 1)
+    X = oracle.source_counts(topk, E, R, S)
+    cap = max(int(X["counts"].max(initial=0)), 1)
+    src = ep.alloc_sources(s1, S, cap)
+    wss = ep.alloc_source_workspace(s1, S)
+    ep.ep_source_layout(s1, tk, src, wss)
+    staging = torch.zeros((R * S * cap, ep.ep_chunked_record_bytes(s1, ep.EP_SEG_BF16)), dtype=torch.uint8,
+                          device="cuda")
+    n_src = int(X["recv_offsets"][-1])
+    rs = ep.alloc_recv(s1, max(n_src, 1), meta=True)
+    for t in rs.values():
+        poison(t)
+    ep.ep_source_dispatch_fused(s1, src, htok, epoch + 2000, staging, rs, n_src, wss)
+    Sd = oracle.source_dispatch(topk, E, R, S, cap, epoch + 2000, x=x, topk_w=w)
+    np.testing.assert_array_equal(host(staging), Sd["staging"], err_msg=f"sources {S}")
+    Ds = oracle.dispatch(topk, E, R, O["rank_offsets"], x=x, topk_w=w)
+    for g, o in [("x", "recv_x"), ("src_idx", "recv_src"), ("topk_idx", "recv_topk_idx"),
+                 ("topk_weights", "recv_topk_w")]:
+        np.testing.assert_array_equal(host(rs[g])[:n_src].view(np.uint8), Ds[o][:n_src].view(np.uint8),
+                                      err_msg=f"sources {S} " + g)
+    assert ep.ep_check_errors(wss) == 0
