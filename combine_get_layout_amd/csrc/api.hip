@@ -91,6 +91,13 @@ __global__ void clear_error_kernel(uint32_t* err) {
     err[1] = 0u;  // since the last clear
 }
 
+// One thread per word (a single workgroup looping over 8,192 batch flags took
+// 4.5 us).
+__global__ void zero_words_kernel(uint32_t* words, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) words[i] = 0u;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Shape check shared by all entry points.
@@ -114,6 +121,13 @@ int check_ws(const ep_shape* s, void* ws, size_t ws_bytes) {
 int hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
 
 }  // namespace
+
+hipError_t launch_zero_words(uint32_t* words, int n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + kBlockThreads - 1) / kBlockThreads), dim3(kBlockThreads), 0, st,
+                       words, n);
+    return hipSuccess;
+}
 }  // namespace ep
 
 using namespace ep;

@@ -720,19 +720,6 @@ struct C2Fused {
     uint32_t* flags;        // [nbatch] epoch once batch b's partial rows are written
 };
 
-__global__ void c2_reset_kernel(uint32_t* words, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) words[i] = 0u;
-}
-
-__device__ __forceinline__ bool c2_wait_flag(const uint32_t* flag, uint32_t epoch, uint64_t timeout) {
-    const uint64_t start = (uint64_t)wall_clock64();
-    for (;;) {
-        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) return true;
-        if ((uint64_t)wall_clock64() - start > timeout) return false;
-        __builtin_amdgcn_s_sleep(8);
-    }
-}
 
 template <int VPW>
 __global__ __launch_bounds__(kBlockThreads, EP_C2F_MINW) void combine_two_level_fused_kernel(Combine2Args a, int slices, C2Fused f) {
@@ -762,7 +749,7 @@ __global__ __launch_bounds__(kBlockThreads, EP_C2F_MINW) void combine_two_level_
         const int fb = job - f.lag;
         if (fb < 0) continue;
         if (threadIdx.x == 0) {
-            const bool ok = c2_wait_flag(&f.flags[fb], a.epoch, f.timeout);
+            const bool ok = wait_flag_bounded(&f.flags[fb], a.epoch, f.timeout);
             if (!ok) report(a.err, EP_DEVERR_TIMEOUT);
             sh_ok = ok ? 1 : 0;
         }
@@ -1001,9 +988,7 @@ hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const
         f.flags = f.ctr + kFusedCounters;
         const int per_cu = EP_C2F_WG_PER_CU > 0 ? std::min(d.per_cu, EP_C2F_WG_PER_CU) : d.per_cu;
         const int blocks = std::min(std::max(1, d.cus * std::max(1, per_cu)), std::max(1, 2 * f.nbatch));
-        const int words = kFusedCounters + f.nbatch;  // f.flags follows the counter words
-        hipLaunchKernelGGL(c2_reset_kernel, dim3((words + kBlockThreads - 1) / kBlockThreads), block, 0, st,
-                           f.ctr, words);
+        launch_zero_words(f.ctr, kFusedCounters + f.nbatch, st);  // f.flags follows the counter words
         hipLaunchKernelGGL(combine_two_level_fused_kernel<kGroupVpw>, dim3(blocks), block, 0, st, a, slices, f);
         return hipGetLastError();
     }

@@ -63,6 +63,19 @@ __device__ __forceinline__ void report(uint32_t* err, uint32_t bits) {
     atomicOr(reinterpret_cast<unsigned int*>(err) + 1, bits);
 }
 
+// Wait (one thread) until the device-scope word *flag equals `value`, at most
+// `timeout` wall-clock ticks (the device's wall-clock rate, kHz / 1000 per us),
+// sleeping between polls; false if it never did. Used by the persistent
+// launches for their per-batch flags.
+__device__ __forceinline__ bool wait_flag_bounded(const uint32_t* flag, uint32_t value, uint64_t timeout) {
+    const uint64_t start = (uint64_t)wall_clock64();
+    for (;;) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == value) return true;
+        if ((uint64_t)wall_clock64() - start > timeout) return false;
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
 // bf16 bit pattern -> float (bf16 is the upper half of a binary32).
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }

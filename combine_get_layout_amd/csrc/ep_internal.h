@@ -66,6 +66,10 @@ struct LaunchInfo {
     int rate_khz, cus, per_cu;
 };
 hipError_t launch_info(hipStream_t st, const void* kernel, int block_threads, LaunchInfo* out);
+// Zero n consecutive u32 words with a small kernel on `st` (the persistent
+// launches' counters and batch flags: a kernel, not a memset, so that the
+// call can be captured into a graph).
+hipError_t launch_zero_words(uint32_t* words, int n, hipStream_t st);
 
 hipError_t launch_layout(const ep_shape& s, const int64_t* topk, const ep_layout& L, char* ws,
                          hipStream_t st);

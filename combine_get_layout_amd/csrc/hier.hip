@@ -406,12 +406,6 @@ struct FusedArgs {
     uint32_t* flags;        // [nbatch] epoch once batch b is written
 };
 
-// Zeroes the n words of the work counters and batch flags (contiguous), one
-// thread per word: a single workgroup looping over 8,192 flags took 4.5 us.
-__global__ void fused_reset_kernel(uint32_t* words, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) words[i] = 0u;
-}
 
 __device__ __forceinline__ uint32_t flag_load(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -453,12 +447,7 @@ __device__ __forceinline__ int take_job(const FusedArgs& f, int& job) {
 // Wait (one thread) until batch `job`'s flag is out, at most f.timeout
 // wall-clock ticks; false (and EP_DEVERR_TIMEOUT) if it never comes.
 __device__ __forceinline__ bool wait_batch(const FusedArgs& f, int job) {
-    const uint64_t start = (uint64_t)wall_clock64();
-    for (;;) {
-        if (flag_load(&f.flags[job]) == f.h.epoch) return true;
-        if ((uint64_t)wall_clock64() - start > f.timeout) break;
-        __builtin_amdgcn_s_sleep(8);
-    }
+    if (wait_flag_bounded(&f.flags[job], f.h.epoch, f.timeout)) return true;
     report(f.h.err, EP_DEVERR_TIMEOUT);
     return false;
 }
@@ -680,13 +669,7 @@ __global__ __launch_bounds__(kSrcFusedWaves * kWave) void source_fused_kernel(So
         const int fb = job - f.lag;
         if (fb < 0) continue;
         if (threadIdx.x == 0) {
-            const uint64_t start = (uint64_t)wall_clock64();
-            bool ok = false;
-            for (;;) {
-                if (flag_load(&f.flags[fb]) == a.epoch) { ok = true; break; }
-                if ((uint64_t)wall_clock64() - start > f.timeout) break;
-                __builtin_amdgcn_s_sleep(8);
-            }
+            const bool ok = wait_flag_bounded(&f.flags[fb], a.epoch, f.timeout);
             if (!ok) report(a.err, EP_DEVERR_TIMEOUT);
             sh_ok = ok ? 1 : 0;
         }
@@ -811,9 +794,7 @@ hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tok
     const int resident = std::max(1, d.cus * std::max(1, per_cu));
     const int jobs_per_block = EP_FUSED_WAVE ? kWavesPerBlock : 1;
     const int blocks = std::min(resident, std::max(1, (2 * f.nbatch + jobs_per_block - 1) / jobs_per_block));
-    const int reset_words = kFusedCounters + f.nbatch;  // f.flags follows the counters
-    hipLaunchKernelGGL(fused_reset_kernel, dim3((reset_words + kBlockThreads - 1) / kBlockThreads),
-                       dim3(kBlockThreads), 0, st, f.ctr, reset_words);
+    launch_zero_words(f.ctr, kFusedCounters + f.nbatch, st);  // f.flags follows the counters
     hipLaunchKernelGGL(fused_hier_kernel, dim3(blocks), dim3(EP_FUSED_WAVE ? kBlockThreads : kFusedThreads), 0, st,
                        f);
     return hipGetLastError();
@@ -868,9 +849,7 @@ hipError_t launch_source_fused(const ep_shape& s, const ep_sources& src, const e
     f.timeout = (uint64_t)kSourceFusedTimeoutUs * (uint64_t)(d.rate_khz > 0 ? d.rate_khz : 100000) / 1000u;
     const int per_cu = EP_SRCF_WG_PER_CU > 0 ? std::min(d.per_cu, EP_SRCF_WG_PER_CU) : d.per_cu;
     const int blocks = std::min(std::max(1, d.cus * std::max(1, per_cu)), std::max(1, 2 * f.nbatch));
-    const int words = kFusedCounters + f.nbatch;  // f.flags follows the counter words
-    hipLaunchKernelGGL(fused_reset_kernel, dim3((words + kBlockThreads - 1) / kBlockThreads), dim3(kBlockThreads), 0,
-                       st, f.ctr, words);
+    launch_zero_words(f.ctr, kFusedCounters + f.nbatch, st);  // f.flags follows the counter words
     hipLaunchKernelGGL(source_fused_kernel, dim3(blocks), dim3(kSrcFusedWaves * kWave), 0, st, f);
     return hipGetLastError();
 }
