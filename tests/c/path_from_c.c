@@ -5,7 +5,10 @@
  *   two-level (2 groups of 4 ranks): ep_get_layout with groups ->
  *         ep_hierarchical_dispatch (both steps) -> ep_combine on the chunked
  *         rows and ep_combine_two_level; the fused one-launch two-level
- *         dispatch; the allocation-free layout.
+ *         dispatch; the allocation-free layout;
+ *   several sources: ep_source_layout -> ep_source_dispatch_fused (send and
+ *         copy epilogue in one launch), whose dense rows equal the flat
+ *         dispatch's.
  * The results are compared bit for bit with the CPU oracle (liboracle.so,
  * test infrastructure), called from the same program. Inputs come from a fixed xorshift generator: ids in [-1, E) with
  * repeats, bf16 rows in [-2, 2), weights in [0, 1).
@@ -36,6 +39,8 @@ int oracle_hier_dispatch(int T, int H, int K, int E, int R, int G, const int64_t
                          const float *x_scales, const int32_t *slot, const int32_t *group_offsets,
                          uint32_t epoch, uint8_t *group_buf, int64_t group_cap, uint8_t *peer_buf,
                          int64_t peer_cap, int steps, uint32_t *err);
+int oracle_source_counts(int T, int K, int E, int R, int S, const int64_t *topk_idx, int32_t *counts,
+                         int32_t *recv_offsets);
 void oracle_combine_two_level(int T, int H, int K, int E, int R, int G, const int64_t *topk_idx,
                               const int32_t *slot, const int32_t *group_slot, const float *topk_w,
                               const uint8_t *y, int64_t y_rows, int64_t row_stride, int chunked,
@@ -258,6 +263,52 @@ int main(void) {
         ok &= same("noalloc rank_offsets", n_ro, o_ro, sizeof o_ro);
         ok &= same("noalloc slot", n_slot, o_slot, sizeof o_slot);
         ok &= bn == 0;
+    }
+    /* several sources (S3 source ranks): source layout, then the send and the
+     * copy epilogue in one launch; the dense rows equal the flat dispatch's */
+    {
+        enum { S3 = 3 };
+        static int32_t c_counts[S3 * R], c_offs[R * S3 + 1];
+        if (oracle_source_counts(T, K, E, R, S3, ids, c_counts, c_offs) != 0) {
+            printf("FAIL oracle_source_counts\n");
+            return 1;
+        }
+        int cap = 1;
+        for (int i = 0; i < S3 * R; i++) cap = c_counts[i] > cap ? c_counts[i] : cap;
+        size_t ws3_bytes = ep_source_workspace_bytes(&s, S3);
+        const int64_t stride3 = ep_chunked_record_bytes(&s, EP_SEG_BF16);
+        void *ws3;
+        int32_t *d3_counts, *d3_offs, *d3_sslot, *d3_src, *d3_ridx;
+        uint8_t *d3_staging;
+        uint16_t *d3_recv;
+        float *d3_rw;
+        HIP_OK(hipMalloc(&ws3, ws3_bytes));
+        HIP_OK(hipMalloc((void **)&d3_counts, sizeof c_counts));
+        HIP_OK(hipMalloc((void **)&d3_offs, sizeof c_offs));
+        HIP_OK(hipMalloc((void **)&d3_sslot, sizeof(int32_t) * T * K));
+        HIP_OK(hipMalloc((void **)&d3_staging, (size_t)R * S3 * cap * stride3));
+        HIP_OK(hipMalloc((void **)&d3_recv, sizeof(uint16_t) * (size_t)N * H));
+        HIP_OK(hipMalloc((void **)&d3_src, sizeof(int32_t) * (size_t)N));
+        HIP_OK(hipMalloc((void **)&d3_ridx, sizeof(int32_t) * (size_t)N * K));
+        HIP_OK(hipMalloc((void **)&d3_rw, sizeof(float) * (size_t)N * K));
+        ep_sources src3 = {S3, cap, d3_counts, d3_offs, d3_sslot};
+        ep_recv rv3 = {d3_recv, NULL, NULL, d3_src, d3_ridx, d3_rw, N};
+        EP_OK_(ep_source_layout(&s, d_ids, &src3, ws3, ws3_bytes, st));
+        EP_OK_(ep_source_dispatch_fused(&s, &src3, &tk, EPOCH, d3_staging, &rv3, ws3, ws3_bytes, st));
+        uint32_t b3 = 99;
+        EP_OK_(ep_check_errors(ws3, st, &b3));
+        static int32_t g3_offs[R * S3 + 1];
+        HIP_OK(hipMemcpy(g3_offs, d3_offs, sizeof g3_offs, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_recv, d3_recv, sizeof(uint16_t) * (size_t)N * H, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_src, d3_src, sizeof(int32_t) * (size_t)N, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_ridx, d3_ridx, sizeof(int32_t) * (size_t)N * K, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_rw, d3_rw, sizeof(float) * (size_t)N * K, hipMemcpyDeviceToHost));
+        ok &= same("sources: recv_offsets", g3_offs, c_offs, sizeof c_offs);
+        ok &= same("sources, one launch: recv_x", g_recv, o_recv, sizeof(uint16_t) * (size_t)N * H);
+        ok &= same("sources, one launch: recv_src", g_src, o_src, sizeof(int32_t) * (size_t)N);
+        ok &= same("sources, one launch: recv_topk_idx", g_ridx, o_ridx, sizeof(int32_t) * (size_t)N * K);
+        ok &= same("sources, one launch: recv_topk_weights", g_rw, o_rw, sizeof(float) * (size_t)N * K);
+        ok &= b3 == 0;
     }
     /* two-level path on the same tokens, R ranks in G2 groups */
     {

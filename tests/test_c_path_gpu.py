@@ -2,6 +2,7 @@
 buffers from the HIP runtime's C API, one caller-created stream; the flat path
 (ep_get_layout -> ep_dispatch -> ep_combine) and the two-level one
 (ep_hierarchical_dispatch -> ep_combine on chunked rows, ep_combine_two_level)
+and the several-source one (ep_source_layout -> ep_source_dispatch_fused)
 through libep.so, every output compared bit for bit with the CPU oracle inside
 the same program."""
 import os
