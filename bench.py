@@ -37,6 +37,7 @@ bounded sample.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -59,6 +60,8 @@ def parse():
     p.add_argument("--workload", default=None,
                    choices=["tiny", "ep32", "ep256", "zipf", "hier8x8", "many"],
                    help="time only this workload (default: every target configuration, ep32 first)")
+    p.add_argument("--hidden", type=int, default=0,
+                   help="with --workload: this hidden size instead of the workload's (labelled _h<H>)")
     p.add_argument("--fp8", action="store_true", help="also move the FP8 payload + scales")
     p.add_argument("--fused", action="store_true",
                    help="two-level workloads and --sources: the one-launch forms with per-batch flags "
@@ -219,7 +222,7 @@ def main():
     ep.lib()
     torch.cuda.set_device(0)
     variants = (args.fp8 or args.expand or args.two_level_combine or args.fused or args.two_launch or
-                args.fused_tile or args.sources is not None)
+                args.fused_tile or args.hidden or args.sources is not None)
     if args.workload is None and not variants:
         runs = [(label, "ep32" if label.startswith("ep32") else label, kw) for label, kw in TARGET_CONFIGS]
     else:
@@ -257,6 +260,11 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
     from combine_get_layout_amd import ep
 
     w = synth.workload(wname)
+    if args.hidden:
+        if args.hidden % 8 or (fp8 and args.hidden % 128):
+            print("--hidden must be a multiple of 8 (of 128 with --fp8)", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, name=f"{w.name}_h{args.hidden}", H=args.hidden)
     hier = w.G > 1
     expand = bool(args.expand)
     two_level = bool(args.two_level_combine)

@@ -387,7 +387,10 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
 #define EP_FUSED_WPB 2  // waves per workgroup of the workgroup-level fused kernel
 #endif
 #ifndef EP_FUSED_WG_PER_CU
-#define EP_FUSED_WG_PER_CU 2  // > 0: at most this many fused workgroups per CU (0: all resident)
+#define EP_FUSED_WG_PER_CU 0  // > 0: at most this many fused workgroups per CU (0: from the record size)
+#endif
+#ifndef EP_FUSED_INFLIGHT_BYTES
+#define EP_FUSED_INFLIGHT_BYTES (20ll << 20)  // records the fused grid's waves hold at once (about)
 #endif
 #ifndef EP_FUSED_LAG
 #define EP_FUSED_LAG 64  // > 0: job i produces batch i, then forwards batch i - EP_FUSED_LAG
@@ -786,11 +789,23 @@ hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tok
     if (e != hipSuccess) return e;
     f.timeout = (uint64_t)timeout_us * (uint64_t)(d.rate_khz > 0 ? d.rate_khz : 100000) / 1000u;
     // No more workgroups than are resident at once (more would find no work),
-    // and at most EP_FUSED_WG_PER_CU per CU: at hier8x8's shapes about four
-    // busy waves per CU keep the records between a batch's production and
-    // its forwarding in the MALL (698.6 us for the launch with 2 workgroups
-    // of 2 waves per CU, 1,003 us with 1, 786 us with 1.5).
-    const int per_cu = EP_FUSED_WG_PER_CU > 0 ? std::min(d.per_cu, EP_FUSED_WG_PER_CU) : d.per_cu;
+    // and per CU only as many as keep about EP_FUSED_INFLIGHT_BYTES of records
+    // in the waves at once (but at least 2): with more, the rows written
+    // between a batch's production and its forwarding push it out of the
+    // MALL; with fewer, HBM idles. At hier8x8 (15,872-byte records) that is 2
+    // workgroups of 2 waves per CU: 699 us for the launch, against 1,003 us
+    // with 1 and 764 us with all 4 resident; with 9,216-byte records
+    // (H = 4,096) all 4: 445 against 574 us with 2; with 35,328-byte records
+    // (H = 16,384) 2: 1,932 against 2,492 us with 1.
+    const int waves_per_wg = EP_FUSED_WAVE ? kWavesPerBlock : kFusedWaves;
+    int per_cu = d.per_cu;
+    if (EP_FUSED_WG_PER_CU > 0) {
+        per_cu = std::min(per_cu, EP_FUSED_WG_PER_CU);
+    } else {
+        const int64_t fit = (int64_t)EP_FUSED_INFLIGHT_BYTES /
+                            ((int64_t)waves_per_wg * std::max(1, d.cus) * std::max<int64_t>(1, f.h.geom.stride));
+        per_cu = (int)std::min<int64_t>(per_cu, std::max<int64_t>(2, fit));
+    }
     const int resident = std::max(1, d.cus * std::max(1, per_cu));
     const int jobs_per_block = EP_FUSED_WAVE ? kWavesPerBlock : 1;
     const int blocks = std::min(resident, std::max(1, (2 * f.nbatch + jobs_per_block - 1) / jobs_per_block));
