@@ -162,13 +162,15 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def two_level_combine_kernel(H: int, K: int) -> str:
+def two_level_combine_kernel(H: int, K: int, group_cap: int) -> str:
     """The launch ep_combine_two_level makes with both steps: one fused kernel
-    when K <= 8 and a token's slices of 4 wave-iterations fill a 4-wave
-    workgroup evenly, else the group and cross kernels."""
+    when K <= 8, a token's slices of 4 wave-iterations fill a 4-wave
+    workgroup evenly and the partial rows (group_cap of them) take at least
+    512 MB, else the group and cross kernels."""
     blocks = (2 * H + 479) // 480
     slices = ((blocks + 1) // 2 + 3) // 4
-    return "combine_two_level_fused_kernel" if K <= 8 and 4 % slices == 0 else \
+    big = group_cap * 512 * blocks >= 512 << 20
+    return "combine_two_level_fused_kernel" if K <= 8 and 4 % slices == 0 and big else \
         "combine_group_kernel+combine_cross_kernel"
 
 
@@ -551,7 +553,7 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
     kernel_of = {"layout": "layout_*", "dispatch": "dispatch_kernel", "send": "scaleout_kernel",
                  "epilogue": "copy_epilogue_kernel", "send+epilogue": "source_fused_kernel",
                  "hier": "fused_hier_kernel" if fused else "scaleout_kernel+forward_kernel",
-                 "combine": (two_level_combine_kernel(w.H, w.K) if two_level else "combine_kernel")}
+                 "combine": (two_level_combine_kernel(w.H, w.K, int(G_rows)) if two_level else "combine_kernel")}
     dom = max(names[1:], key=lambda n: avg_ms[n])
     achieved = by[dom] / (avg_ms[dom] * 1e-3) / 1e9
     label = w.name + ("_fp8" if fp8 else "") + ("_expand" if expand else "") + \

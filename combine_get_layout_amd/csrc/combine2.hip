@@ -944,6 +944,10 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_any_kernel(Combin
 }  // namespace
 
 constexpr uint32_t kC2FusedTimeoutUs = 100000;  // longest wait for one batch flag
+#ifndef EP_C2F_MIN_PARTIAL_BYTES
+#define EP_C2F_MIN_PARTIAL_BYTES (512ll << 20)  // one launch from this many bytes of partial rows
+#endif
+constexpr int64_t kC2FusedMinPartialBytes = EP_C2F_MIN_PARTIAL_BYTES;
 
 hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const int64_t* topk,
                                     const void* y, int64_t y_rows, int64_t y_stride, int fmt,
@@ -974,13 +978,19 @@ hipError_t launch_combine_two_level(const ep_shape& s, const ep_layout& L, const
     const int iters = (nblk + 1) / 2;
     constexpr int kGroupVpw = 4;
     const int slices = (iters + kGroupVpw - 1) / kGroupVpw;
-    if (steps == 3 && EP_C2_FUSED && s.K <= 8 && EP_C2_ROWS && kWavesPerBlock % slices == 0) {
+    // One launch pays off only when the partial rows are well past the MALL:
+    // smaller ones are still cached when the cross launch reads them
+    // (hier8x8 shapes, T = 16,384, bench.py --hidden: fused / two launches
+    // 752 / 885 us at H = 7,168, 421 / 480 us at 3,840 (710 MB of partial
+    // rows), 317 / 281 us at 2,048 (400 MB), 168 / 153 us at 1,024).
+    const bool big = (int64_t)group_cap * a.pstride >= kC2FusedMinPartialBytes;
+    if (steps == 3 && EP_C2_FUSED && big && s.K <= 8 && EP_C2_ROWS && kWavesPerBlock % slices == 0) {
         LaunchInfo d;
         const hipError_t e = launch_info(st, reinterpret_cast<const void*>(&combine_two_level_fused_kernel<kGroupVpw>),
                                          kBlockThreads, &d);
         if (e != hipSuccess) return e;
         C2Fused f;
-        f.tile = EP_C2F_TILE;
+        f.tile = EP_C2F_TILE * (kWavesPerBlock / slices);  // every wave of a workgroup pass busy
         f.nbatch = (s.T + f.tile - 1) / f.tile;
         f.lag = EP_C2F_LAG;
         f.timeout = (uint64_t)kC2FusedTimeoutUs * (uint64_t)(d.rate_khz > 0 ? d.rate_khz : 100000) / 1000u;

@@ -310,13 +310,15 @@ int64_t ep_partial_row_bytes(const ep_shape *shape);
  *    partial row with a flag != epoch is skipped (EP_DEVERR_FLAG).
  * Needs layout->slot, layout->group_slot, tokens' topk_idx; epoch >= 1.
  * Usable lanes are as in ep_combine. With G = 1 the result equals
- * ep_combine bit for bit. With steps = 3, K <= 8 and H <= 3,840 or
+ * ep_combine bit for bit. With steps = 3, K <= 8, H <= 3,840 or
  * 5,760 < H <= 7,680 (a row's 512 B blocks cut into 1, 2 or 4 slices of 8
- * blocks), both steps run as one persistent launch with one flag per
- * one-token batch in the workspace (as for ep_hierarchical_dispatch_fused;
- * calls on one workspace must not overlap): job i reduces token i's groups,
- * publishes it, then sums token i - 128 across groups, so the partial rows are
- * read back shortly after they were written. A batch whose flag does not come
+ * blocks) and group_cap partial rows of at least 512 MB (smaller ones stay
+ * in the MALL between two launches anyway), both steps run as one persistent
+ * launch with one flag per batch of tokens in the workspace (as for
+ * ep_hierarchical_dispatch_fused; calls on one workspace must not overlap):
+ * job i reduces batch i's groups, publishes it, then sums batch i - 128
+ * across groups, so the partial rows are read back shortly after they were
+ * written. A batch whose flag does not come
  * within 100 ms is not summed (EP_DEVERR_TIMEOUT). The results equal the two
  * launches' bit for bit. */
 int ep_combine_two_level(const ep_shape *shape, const ep_layout *layout, const int64_t *topk_idx,

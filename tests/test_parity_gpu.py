@@ -813,13 +813,17 @@ def test_other_shapes_end_to_end(name, w, fp8):
     assert ep.ep_check_errors(ws) == 0
 
 
-def run_two_level(shape, L, tk, y, y_rows, y_stride, fmt, epoch, w_dev, steps=3, group_buf=None):
+def run_two_level(shape, L, tk, y, y_rows, y_stride, fmt, epoch, w_dev, steps=3, group_buf=None,
+                  min_buf_bytes=0):
+    """min_buf_bytes: pass a partial-row buffer (and capacity) of at least this
+    many bytes; from 512 MB the library runs both steps as one launch."""
     gcap = int(host(L["group_offsets"])[-1])
     pstride = ep.ep_partial_row_bytes(shape)
+    cap = max(gcap, -(-min_buf_bytes // pstride))
     if group_buf is None:
-        group_buf = torch.zeros((max(gcap, 1), pstride), dtype=torch.uint8, device="cuda")
+        group_buf = torch.zeros((max(cap, 1), pstride), dtype=torch.uint8, device="cuda")
     out = poison(torch.empty((shape.T, shape.H), dtype=torch.uint16, device="cuda"))
-    ep.ep_combine_two_level(shape, L, tk, y, y_rows, y_stride, fmt, epoch, w_dev, group_buf, gcap,
+    ep.ep_combine_two_level(shape, L, tk, y, y_rows, y_stride, fmt, epoch, w_dev, group_buf, cap,
                             steps, out, ws=L["_ws"])
     torch.cuda.synchronize()
     return group_buf, out, gcap
@@ -868,7 +872,6 @@ def test_two_level_combine_chunked(name):
                                          (77, 4608, 64, 128, 32, 8), (50, 520, 17, 34, 17, 1),
                                          (40, 16384, 8, 64, 16, 4), (30, 16384, 24, 64, 16, 4),
                                          (100, 1024, 64, 1024, 512, 256),
-                                         # one launch with rows of 2 and 4 slices of 8 blocks
                                          (200, 2048, 8, 64, 16, 4), (96, 3840, 5, 40, 8, 2),
                                          (60, 5768, 8, 64, 16, 4)])
 def test_two_level_combine_plain(T, H, K, E, R, G):
@@ -889,6 +892,34 @@ def test_two_level_combine_plain(T, H, K, E, R, G):
         flat = poison(torch.empty((T, H), dtype=torch.uint16, device="cuda"))
         ep.ep_combine(shape, L, dev(y), N, 2 * H, ep.EP_FMT_PLAIN, 0, dev(wts), flat, ws)
         np.testing.assert_array_equal(host(flat), host(out))
+    assert ep.ep_check_errors(ws) == 0
+
+
+@pytest.mark.parametrize("T,H,K,E,R,G", [(300, 512, 3, 24, 8, 4), (500, 2048, 8, 64, 16, 4),
+                                         (257, 3840, 5, 40, 8, 2), (120, 7168, 8, 256, 64, 8),
+                                         (64, 5768, 8, 64, 16, 4)])
+def test_two_level_combine_one_launch(T, H, K, E, R, G):
+    """Small shapes through the one-launch two-level combine (a partial-row
+    capacity of 512 MB selects it), rows of 1, 2 and 4 slices: partial rows and
+    outputs against the oracle and against the two launches (steps 1, then 2)."""
+    w = synth.Workload("edge", T, H, E, R, G, K, "uniform")
+    rng = np.random.default_rng(T + 7 * H + K)
+    topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
+    wts = rng.standard_normal((T, K)).astype(np.float32)
+    shape, L, ws, tk = run_layout(w, topk)
+    L["_ws"] = ws
+    N = int(host(L["rank_offsets"])[-1])
+    y = synth.random_bf16_rows(max(N, 1), H, seed=T + H)
+    gbuf, out, gcap = run_two_level(shape, L, tk, dev(y), N, 2 * H, ep.EP_FMT_PLAIN, 9, dev(wts),
+                                    min_buf_bytes=512 << 20)
+    O = oracle.layout(topk, E, R, G)
+    C = oracle.combine_two_level(topk, E, R, G, O["slot"], O["group_slot"], wts, y[:N], H, gcap, 9)
+    np.testing.assert_array_equal(host(gbuf[:gcap]), C["group_buf"])
+    np.testing.assert_array_equal(host(out), C["out"])
+    g1, _, _ = run_two_level(shape, L, tk, dev(y), N, 2 * H, ep.EP_FMT_PLAIN, 9, dev(wts), steps=1)
+    _, out2, _ = run_two_level(shape, L, tk, dev(y), N, 2 * H, ep.EP_FMT_PLAIN, 9, dev(wts), steps=2,
+                               group_buf=g1)
+    np.testing.assert_array_equal(host(out2), host(out))
     assert ep.ep_check_errors(ws) == 0
 
 
