@@ -372,8 +372,8 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
 // forwards batch i - lag. A group row is therefore read back a bounded
 // number of batches after it was written, while it is still in the
 // memory-side cache (the 256 MB MALL) instead of being fetched from HBM;
-// with the grid held to about four busy waves per CU, the records in flight
-// stay well inside that cache. The other schedule (EP_FUSED_LAG = 0) hands
+// with the grid sized to hold about 20 MB of records at once, the records
+// in flight stay well inside that cache. The other schedule (EP_FUSED_LAG = 0) hands
 // out forwarding as soon as a flag is seen and otherwise production, from
 // two counters; production then runs far ahead of forwarding and the rows
 // come back from HBM.
