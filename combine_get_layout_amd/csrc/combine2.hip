@@ -706,9 +706,12 @@ __global__ __launch_bounds__(kBlockThreads) void combine_cross_rows_kernel(Combi
 // still in the memory-side cache (the MALL) rather than in HBM alone. Unlike
 // the fused dispatch, whose waves each hold a whole record in flight, a
 // combine wave streams one or two rows at a time, so this launch wants every
-// resident workgroup (3 per CU at its register count) and one-token batches:
-// at hier8x8 746 us against 889 us for the two launches (tile 2: 783 us,
-// tile 8: 1,036 us; one workgroup per CU: 1,281 us). Batch i
+// resident workgroup (3 per CU at its register count) and batches of one
+// token per workgroup pass (4 / slices tokens, so that rows of 1 or 2
+// slices still keep every wave busy): at hier8x8 746 us against 889 us for
+// the two launches (2-token batches: 783 us, 8-token: 1,036 us; one
+// workgroup per CU: 1,281 us). The launcher takes this form only for
+// partial rows well past the MALL (see kC2FusedMinPartialBytes). Batch i
 // - lag was handed out before job i to a running workgroup that writes it
 // before it waits for anything, so every wait ends, co-resident or not. The
 // arithmetic is that of the two launches, so the results are identical.
@@ -719,7 +722,6 @@ struct C2Fused {
     uint32_t* ctr;          // [0] next job
     uint32_t* flags;        // [nbatch] epoch once batch b's partial rows are written
 };
-
 
 template <int VPW>
 __global__ __launch_bounds__(kBlockThreads, EP_C2F_MINW) void combine_two_level_fused_kernel(Combine2Args a, int slices, C2Fused f) {
