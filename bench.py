@@ -72,6 +72,9 @@ def parse():
                         "two calls")
     p.add_argument("--fused-tile", type=int, default=0,
                    help="tokens per batch of the fused two-level dispatch (0: default)")
+    p.add_argument("--ring", type=int, default=0,
+                   help="fused two-level dispatch: group rows through a ring of this many batches "
+                        "(> 64; 0: at their group-region rows; labelled _ring<N>)")
     p.add_argument("--two-level-combine", action="store_true",
                    help="two-level workloads: combine through per-group partial rows")
     p.add_argument("--expand", action="store_true",
@@ -224,7 +227,7 @@ def main():
     ep.lib()
     torch.cuda.set_device(0)
     variants = (args.fp8 or args.expand or args.two_level_combine or args.fused or args.two_launch or
-                args.fused_tile or args.hidden or args.sources is not None)
+                args.fused_tile or args.hidden or args.ring or args.sources is not None)
     if args.workload is None and not variants:
         runs = [(label, "ep32" if label.startswith("ep32") else label, kw) for label, kw in TARGET_CONFIGS]
     else:
@@ -277,10 +280,13 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
     if (args.fused or args.two_launch) and not (hier or multi):
         print("--fused and --two-launch apply to the two-level workloads and to --sources", file=sys.stderr)
         sys.exit(2)
-    if args.fused_tile and not hier:
-        print("--fused-tile applies to the two-level workloads", file=sys.stderr)
+    if (args.fused_tile or args.ring) and not hier:
+        print("--fused-tile and --ring apply to the two-level workloads", file=sys.stderr)
         sys.exit(2)
     fused = (hier or multi) and not args.two_launch
+    if args.ring and not fused:
+        print("--ring applies to the fused two-level dispatch", file=sys.stderr)
+        sys.exit(2)
     if two_level and not hier:
         print("--two-level-combine applies to the two-level workloads", file=sys.stderr)
         sys.exit(2)
@@ -393,7 +399,8 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
         timed("layout", lambda: ep.ep_get_layout(shape, tokens["topk_idx"], L, ws), record)
         if hier and fused:
             timed("hier", lambda: ep.ep_hierarchical_dispatch_fused(
-                shape, L, tokens, e, group_buf, G_rows, peer_buf, N, ws, tile=args.fused_tile), record)
+                shape, L, tokens, e, group_buf, G_rows, peer_buf, N, ws, tile=args.fused_tile, ring=args.ring),
+                record)
         if hier and not fused:
             timed("hier", lambda: ep.ep_hierarchical_dispatch(
                 shape, L, tokens, e, ep.EP_HIER_SCALEOUT | ep.EP_HIER_FORWARD,
@@ -557,7 +564,8 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
     dom = max(names[1:], key=lambda n: avg_ms[n])
     achieved = by[dom] / (avg_ms[dom] * 1e-3) / 1e9
     label = w.name + ("_fp8" if fp8 else "") + ("_expand" if expand else "") + \
-        ("_2lc" if two_level else "") + (f"_s{S}" if multi else "") + ("_2launch" if (hier or multi) and not fused else "")
+        ("_2lc" if two_level else "") + (f"_s{S}" if multi else "") + ("_2launch" if (hier or multi) and not fused else "") + \
+        (f"_ring{args.ring}" if args.ring else "")
     traffic = committed_traffic(label, kernel_of[dom])
 
     if args.copy_calibration:
@@ -588,6 +596,7 @@ def run_config(args, wname: str, fp8: bool, cpu_seconds: float) -> dict:
                    "ranks": R, "groups": w.G, "topk": K, "routing": w.routing,
                    "receive_rows": N, "fp8_payload": fp8, "expand_rows": expand,
                    "two_level_combine": two_level, "fused_two_level_dispatch": fused,
+                   "ring_batches": args.ring or None,
                    "sources": S if multi else None,
                    "region_capacity": cap if multi else None,
                    "input_batches": n_batches,

@@ -27,7 +27,7 @@ WsLayout ws_layout(const ep_shape& s) {
     off += align256(sizeof(int32_t) * (size_t)(w.nb + 1) * s.E);
     w.tables_end = off;
     w.fused = off;
-    off += align256(sizeof(uint32_t) * (kFusedCounters + (size_t)(s.T + kFusedMinTile - 1) / kFusedMinTile));
+    off += align256(sizeof(uint32_t) * (kFusedCounters + 2 * ((size_t)(s.T + kFusedMinTile - 1) / kFusedMinTile)));
     w.total = off;
     return w;
 }
@@ -266,15 +266,21 @@ int ep_hierarchical_dispatch_fused(const ep_shape* shape, const ep_layout* layou
         !aligned(group_buf, 16) || !aligned(peer_buf, 16) || !aligned(layout->slot, 4) ||
         !aligned(layout->group_slot, 4))
         return EP_ERR_ARG;
-    ep_fused_opts o = {0, 0, 0, 0};
+    ep_fused_opts o = {0, 0, 0, 0, 0};
     if (opts) o = *opts;
     const int tile = o.tile_tokens ? o.tile_tokens : kFusedDefaultTile;
     if (tile < kFusedMinTile || tile > kFusedMaxTile || (o.test_flags & ~EP_FUSED_WITHHOLD)) return EP_ERR_ARG;
+    // Ring mode: more batches than the fixed lag (the producer of batch b
+    // waits for the forwarding of batch b - ring), and room for all of them.
+    if (o.ring_batches < 0 || (o.ring_batches > 0 && o.ring_batches <= kFusedLag)) return EP_ERR_ARG;
+    if (o.ring_batches > 0 &&
+        group_cap < (int64_t)o.ring_batches * tile * std::min(shape->K, shape->G))
+        return EP_ERR_ARG;
     const uint32_t timeout = o.timeout_us ? o.timeout_us : 100000u;
     const int withhold = (o.test_flags & EP_FUSED_WITHHOLD) ? o.withhold_batch : -1;
     return hip_status(launch_hier_fused(*shape, *layout, *tokens, epoch, group_buf, group_cap, peer_buf,
-                                        peer_cap, tile, timeout, withhold, static_cast<char*>(ws),
-                                        static_cast<hipStream_t>(stream)));
+                                        peer_cap, tile, timeout, withhold, o.ring_batches,
+                                        static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
 }
 
 int ep_combine(const ep_shape* shape, const ep_layout* layout, const void* y, int64_t y_rows,

@@ -14,6 +14,7 @@ namespace ep {
 constexpr int kLayoutTokens = 256;  // tokens per layout workgroup (one per thread)
 constexpr int kFusedMinTile = 1;    // smallest batch of the fused two-level dispatch (tokens)
 constexpr int kFusedMaxTile = 64;   // largest batch
+constexpr int kFusedLag = 64;       // fixed lag of the fused two-level dispatch (batches)
 constexpr int kFusedDefaultTile = 2;  // one token per wave of a 2-wave workgroup (measured best of 1-16)
 constexpr int kFusedCounters = 64;  // u32 words before the batch flags (two used)
 
@@ -31,7 +32,8 @@ struct WsLayout {
     size_t part_expert;     // int32 [nb + 1][E] lanes per expert
     size_t tables_end;      // end of the count tables (all the layout kernels use)
     size_t fused;           // fused two-level dispatch: u32 [kFusedCounters] work counters,
-                            // then u32 [ceil(T / kFusedMinTile)] batch flags
+                            // then u32 [ceil(T / kFusedMinTile)] batch flags, then as
+                            // many batch-freed words (ring mode)
     size_t total;
 };
 WsLayout ws_layout(const ep_shape& s);
@@ -85,8 +87,8 @@ hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& t
                        void* peer_buf, int64_t peer_cap, char* ws, hipStream_t st);
 hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
                              uint32_t epoch, void* group_buf, int64_t group_cap, void* peer_buf,
-                             int64_t peer_cap, int tile, uint32_t timeout_us, int withhold, char* ws,
-                             hipStream_t st);
+                             int64_t peer_cap, int tile, uint32_t timeout_us, int withhold, int ring,
+                             char* ws, hipStream_t st);
 hipError_t launch_combine(const ep_shape& s, const ep_layout& L, const void* y, int64_t y_rows,
                           int64_t y_stride, int fmt, uint32_t epoch, const float* w,
                           uint16_t* out, char* ws, hipStream_t st);

@@ -395,6 +395,9 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
 #ifndef EP_FUSED_LAG
 #define EP_FUSED_LAG 64  // > 0: job i produces batch i, then forwards batch i - EP_FUSED_LAG
 #endif
+// The host accepts ring sizes above kFusedLag; the ring's waits point at
+// earlier jobs only while the ring is longer than the lag.
+static_assert(EP_FUSED_LAG <= kFusedLag, "ring sizes are checked against kFusedLag");
 constexpr int kFusedWaves = EP_FUSED_WPB;
 constexpr int kFusedThreads = kFusedWaves * kWave;
 
@@ -404,6 +407,9 @@ struct FusedArgs {
     int nbatch;             // ceil(T / tile)
     int withhold;           // batch whose flag is never published (-1: none)
     int lag;                // fixed-lag schedule: batches between production and forwarding
+    int ring;               // > 0: group rows in a ring of this many batches (released by forwarding)
+    int gmax;               // ring rows per token: min(K, G)
+    uint32_t* freed;        // [nbatch] epoch once batch b's ring rows are read (ring mode)
     uint64_t timeout;       // wall-clock ticks a batch wait may last
     uint32_t* ctr;          // [0] next batch to produce, [1] next batch to forward
     uint32_t* flags;        // [nbatch] epoch once batch b is written
@@ -449,8 +455,8 @@ __device__ __forceinline__ int take_job(const FusedArgs& f, int& job) {
 
 // Wait (one thread) until batch `job`'s flag is out, at most f.timeout
 // wall-clock ticks; false (and EP_DEVERR_TIMEOUT) if it never comes.
-__device__ __forceinline__ bool wait_batch(const FusedArgs& f, int job) {
-    if (wait_flag_bounded(&f.flags[job], f.h.epoch, f.timeout)) return true;
+__device__ __forceinline__ bool wait_batch(const FusedArgs& f, int job, uint64_t limit = 0) {
+    if (wait_flag_bounded(&f.flags[job], f.h.epoch, limit ? limit : f.timeout)) return true;
     report(f.h.err, EP_DEVERR_TIMEOUT);
     return false;
 }
@@ -511,10 +517,52 @@ __global__ __launch_bounds__(kBlockThreads) void fused_hier_kernel(FusedArgs f) 
 // was handed out before job i to a running workgroup that writes it before
 // it waits for anything, so every wait ends; a group row is read about `lag`
 // jobs after it was written.
+//
+// Ring mode (ring > 0): the group rows are not kept at their group-region
+// rows but pass through a ring of `ring` batches, the scale-out receive
+// buffer with flow control of "07: DeepEP Intra/Inter-node 协调" (the RDMA
+// sender waits until the receiver's ring has free slots; the forwarder
+// releases them). The j-th distinct group of the i-th token of batch b goes
+// to ring row (b mod ring) * tile * gmax + i * gmax + j. Before writing batch
+// b >= ring, the producer waits until batch b - ring's rows were read
+// (`freed`); a forwarder marks its batch freed once its loads are done, also
+// after a timed-out wait. Batch b - ring was forwarded by job
+// b - ring + lag < b (ring > lag), handed out earlier, so every wait still
+// points at an earlier job. The rows then stay in a few hundred MB that the
+// MALL can hold instead of all G_rows.
+// The waits of one slot chain through the generations n = b / ring: the
+// producer of batch b waits for the forwarder of b - ring, which waits for
+// its producer, and so on. Since every wait may start at about the same
+// time, each limit grows with n: a forwarder waits at most (n + 1) * timeout,
+// a producer at most (n + 1/2) * timeout. A flag lost in generation n then
+// stops only its own batch: its forwarder gives up at (n + 1) * timeout,
+// before the next producer's limit, whose flag comes before its forwarder's.
+__device__ __forceinline__ int ring_row(const FusedArgs& f, int batch, int i, uint64_t firsts, int lane) {
+    const int base = (batch % f.ring) * f.tile * f.gmax + i * f.gmax;
+    return base + __popcll(firsts & ((1ull << lane) - 1));
+}
+
+// The distinct groups of token t (first lane of each, as in scaleout_token
+// and forward_token): group slot, group and the mask of first lanes.
+__device__ __forceinline__ uint64_t token_groups(const HierArgs& a, int t, int& gs, int& g) {
+    const int lane = lane_id();
+    gs = -1;
+    g = -1;
+    if (lane < a.K) {
+        gs = a.group_slot[(int64_t)t * a.K + lane];
+        const int64_t e = a.topk[(int64_t)t * a.K + lane];
+        if (gs >= 0 && expert_ok(e, a.E)) g = ((int)e / a.epr) / a.P;
+    }
+    bool first = gs >= 0 && g >= 0;
+    for (int j = 0; j < a.K; ++j)
+        if (j < lane && readlane(gs, j) == gs) first = false;
+    return __ballot(first);
+}
+
 __global__ __launch_bounds__(kFusedThreads) void fused_hier_kernel(FusedArgs f) {
     const HierArgs& a = f.h;
     __shared__ int sh_job, sh_ok;
-    const int wave = wave_in_block();
+    const int wave = wave_in_block(), lane = lane_id();
     const int njobs = f.nbatch + f.lag;
     for (;;) {
         if (threadIdx.x == 0) sh_job = (int)atomicAdd(&f.ctr[0], 1u);
@@ -524,8 +572,21 @@ __global__ __launch_bounds__(kFusedThreads) void fused_hier_kernel(FusedArgs f) 
         if (job >= njobs) return;
         if (job < f.nbatch) {
             const int t0 = job * f.tile, t1 = min(a.T, t0 + f.tile);
-            for (int t = t0 + wave; t < t1; t += kFusedWaves)
-                scaleout_token<1, kPieceIters, kStoreDevice>(a, t, 0);
+            if (f.ring > 0) {
+                if (job >= f.ring && threadIdx.x == 0 &&
+                    !wait_flag_bounded(&f.freed[job - f.ring], a.epoch,
+                                       (uint64_t)(job / f.ring) * f.timeout + f.timeout / 2))
+                    report(a.err, EP_DEVERR_TIMEOUT);
+                __syncthreads();
+                for (int t = t0 + wave; t < t1; t += kFusedWaves) {
+                    int gs, g;
+                    const uint64_t fm = token_groups(a, t, gs, g);
+                    write_record<1, kPieceIters, kStoreDevice>(a, t, 0, fm, ring_row(f, job, t - t0, fm, lane));
+                }
+            } else {
+                for (int t = t0 + wave; t < t1; t += kFusedWaves)
+                    scaleout_token<1, kPieceIters, kStoreDevice>(a, t, 0);
+            }
             wait_vmem();
             __syncthreads();
             if (threadIdx.x == 0 && job != f.withhold)
@@ -533,13 +594,33 @@ __global__ __launch_bounds__(kFusedThreads) void fused_hier_kernel(FusedArgs f) 
         }
         const int fb = job - f.lag;
         if (fb < 0) continue;
-        if (threadIdx.x == 0) sh_ok = wait_batch(f, fb) ? 1 : 0;
+        if (threadIdx.x == 0)
+            sh_ok = wait_batch(f, fb, f.ring > 0 ? (uint64_t)(fb / f.ring + 1) * f.timeout : 0) ? 1 : 0;
         __syncthreads();
         const int ok = sh_ok;
         __syncthreads();
-        if (!ok) continue;
         const int t0 = fb * f.tile, t1 = min(a.T, t0 + f.tile);
-        for (int t = t0 + wave; t < t1; t += kFusedWaves) forward_token<true>(a, t);
+        if (ok) {
+            for (int t = t0 + wave; t < t1; t += kFusedWaves) {
+                if (f.ring > 0) {
+                    int gs, g;
+                    const uint64_t fm = token_groups(a, t, gs, g);
+                    const int rr = ring_row(f, fb, t - t0, fm, lane);
+                    for (uint64_t m = fm; m; m &= m - 1) {
+                        const int k = __ffsll((unsigned long long)m) - 1;
+                        forward_row<true>(a, readlane(rr, k), readlane(g, k), t);
+                    }
+                } else {
+                    forward_token<true>(a, t);
+                }
+            }
+        }
+        if (f.ring > 0) {  // release the batch's ring rows (its loads are done)
+            wait_vmem();
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&f.freed[fb], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 #else
@@ -764,9 +845,10 @@ hipError_t launch_hier(const ep_shape& s, const ep_layout& L, const ep_tokens& t
 
 hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tokens& tk,
                              uint32_t epoch, void* group_buf, int64_t group_cap, void* peer_buf,
-                             int64_t peer_cap, int tile, uint32_t timeout_us, int withhold, char* ws,
-                             hipStream_t st) {
+                             int64_t peer_cap, int tile, uint32_t timeout_us, int withhold, int ring,
+                             char* ws, hipStream_t st) {
     if (s.T == 0) return hipSuccess;
+    if (ring > 0 && (EP_FUSED_WAVE || EP_FUSED_LAG == 0)) return hipErrorNotSupported;  // lag kernel only
     const WsLayout W = ws_layout(s);
     FusedArgs f;
     f.h = hier_args(s, tk, epoch, ws);
@@ -781,8 +863,11 @@ hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tok
     f.nbatch = (s.T + tile - 1) / tile;
     f.withhold = withhold;
     f.lag = EP_FUSED_LAG;
+    f.ring = ring;
+    f.gmax = std::min(s.K, s.G);
     f.ctr = reinterpret_cast<uint32_t*>(ws + W.fused);
     f.flags = f.ctr + kFusedCounters;
+    f.freed = f.flags + f.nbatch;
     LaunchInfo d;
     const hipError_t e = launch_info(st, reinterpret_cast<const void*>(&fused_hier_kernel),
                                      EP_FUSED_WAVE ? kBlockThreads : kFusedThreads, &d);
@@ -809,7 +894,7 @@ hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tok
     const int resident = std::max(1, d.cus * std::max(1, per_cu));
     const int jobs_per_block = EP_FUSED_WAVE ? kWavesPerBlock : 1;
     const int blocks = std::min(resident, std::max(1, (2 * f.nbatch + jobs_per_block - 1) / jobs_per_block));
-    launch_zero_words(f.ctr, kFusedCounters + f.nbatch, st);  // f.flags follows the counters
+    launch_zero_words(f.ctr, kFusedCounters + 2 * f.nbatch, st);  // then f.flags, then f.freed
     hipLaunchKernelGGL(fused_hier_kernel, dim3(blocks), dim3(EP_FUSED_WAVE ? kBlockThreads : kFusedThreads), 0, st,
                        f);
     return hipGetLastError();

@@ -53,7 +53,8 @@ class ep_recv(ctypes.Structure):
 
 class ep_fused_opts(ctypes.Structure):
     _fields_ = [("tile_tokens", ctypes.c_int32), ("timeout_us", ctypes.c_uint32),
-                ("test_flags", ctypes.c_uint32), ("withhold_batch", ctypes.c_int32)]
+                ("test_flags", ctypes.c_uint32), ("withhold_batch", ctypes.c_int32),
+                ("ring_batches", ctypes.c_int32)]
 
 
 class ep_sources(ctypes.Structure):
@@ -265,12 +266,13 @@ def ep_hierarchical_dispatch(shape, layout: dict, tokens: dict, epoch: int, step
 
 def ep_hierarchical_dispatch_fused(shape, layout: dict, tokens: dict, epoch: int, group_buf,
                                    group_cap: int, peer_buf, peer_cap: int, ws, tile: int = 0,
-                                   timeout_us: int = 0, withhold: int | None = None, stream=None):
+                                   timeout_us: int = 0, withhold: int | None = None, ring: int = 0,
+                                   stream=None):
     L = _layout_struct(shape, layout)
     tk = _tokens_struct(shape, tokens)
     stride = max(ep_chunked_record_bytes(shape, _seg_of(tokens) or EP_SEG_BF16), 0)
     opts = ep_fused_opts(int(tile), int(timeout_us), EP_FUSED_WITHHOLD if withhold is not None else 0,
-                         int(withhold) if withhold is not None else 0)
+                         int(withhold) if withhold is not None else 0, int(ring))
     _check(lib().ep_hierarchical_dispatch_fused(
         ctypes.byref(shape), ctypes.byref(L), ctypes.byref(tk), int(epoch),
         _ptr(group_buf, "group_buf", max(int(group_cap), 0) * stride), int(group_cap),

@@ -254,11 +254,30 @@ int ep_hierarchical_dispatch(const ep_shape *shape, const ep_layout *layout,
  * overlap. opts may be NULL (defaults); all-zero fields mean the defaults. */
 typedef struct ep_fused_opts {
     int32_t tile_tokens;    /* tokens per batch, 1..64 (0: 2) */
-    uint32_t timeout_us;    /* longest wait for one batch flag (0: 100000 us) */
+    uint32_t timeout_us;    /* longest wait for one batch flag (0: 100000 us; in ring
+                               mode scaled by the batch's generation, below) */
     uint32_t test_flags;    /* EP_FUSED_WITHHOLD: batch `withhold_batch`'s flag is never
                                published, to test the bounded wait (its group rows are
                                still written; it is not forwarded; EP_DEVERR_TIMEOUT) */
     int32_t withhold_batch;
+    int32_t ring_batches;   /* 0: group rows at their group-region rows (group_slot), as
+                               ep_hierarchical_dispatch writes them. > 64: group_buf is a
+                               ring of this many batches instead ([PIPE] the scale-out
+                               receive buffer with flow control: a sender waits until the
+                               forwarder has freed the slots it reuses). Token i of batch b
+                               puts its j-th distinct group's record at row
+                               ((b mod ring) * tile + i) * min(K, G) + j; the producer of
+                               batch b waits until batch b - ring was forwarded. With
+                               n = b / ring, the producer waits at most (n + 1/2) *
+                               timeout_us (then writes anyway and sets
+                               EP_DEVERR_TIMEOUT) and the forwarder (n + 1) * timeout_us,
+                               so a lost flag stops only its own batch, and a broken run
+                               lasts at most about (nbatch / ring + 1) * timeout_us.
+                               Needs group_cap >= ring * tile * min(K, G); the
+                               peer rows are those of ring 0, byte for byte; group_buf's
+                               contents afterwards are unspecified (the last pass over the
+                               ring), and group_slot's capacity check does not apply.
+                               Other values: EP_ERR_ARG. */
 } ep_fused_opts;
 #define EP_FUSED_WITHHOLD 1u
 int ep_hierarchical_dispatch_fused(const ep_shape *shape, const ep_layout *layout,

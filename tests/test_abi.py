@@ -98,7 +98,8 @@ def test_null_and_misaligned_arguments_rejected_before_launch(lib):
 
 def test_fused_options_checked_before_launch(lib):
     """The fused two-level dispatch refuses batch sizes outside 1..64, unknown
-    test flags and epoch 0 on the host; with T = 0 it enqueues nothing."""
+    test flags, ring sizes of 64 batches or fewer (or more than group_cap rows)
+    and epoch 0 on the host; with T = 0 it enqueues nothing."""
     s = ep.make_shape(128, 256, 4, 32, 8, 4)
     n = ep.ep_workspace_bytes(s)
     ws = 0x100000
@@ -112,6 +113,9 @@ def test_fused_options_checked_before_launch(lib):
     assert call(ctypes.byref(ep.ep_fused_opts(65, 0, 0, 0))) == ep.EP_ERR_ARG
     assert call(ctypes.byref(ep.ep_fused_opts(-1, 0, 0, 0))) == ep.EP_ERR_ARG
     assert call(ctypes.byref(ep.ep_fused_opts(16, 0, 2, 0))) == ep.EP_ERR_ARG  # unknown test flag
+    assert call(ctypes.byref(ep.ep_fused_opts(1, 0, 0, 0, 64))) == ep.EP_ERR_ARG  # ring not above the lag
+    assert call(ctypes.byref(ep.ep_fused_opts(1, 0, 0, 0, -1))) == ep.EP_ERR_ARG
+    assert call(ctypes.byref(ep.ep_fused_opts(1, 0, 0, 0, 65))) == ep.EP_ERR_ARG  # 260 ring rows > group_cap 10
     assert call(None, epoch=0) == ep.EP_ERR_ARG
     z = ep.make_shape(0, 256, 4, 32, 8, 4)
     assert lib.ep_hierarchical_dispatch_fused(ctypes.byref(z), ctypes.byref(L), ctypes.byref(tk), 3, None, 0,

@@ -5,7 +5,9 @@ rows and scale-up rows byte for byte. Also: ragged batches and several batch
 sizes, the FP8 + scales payload, repeated calls on the same buffers with new
 epochs, the full hier8x8 workload, and the bounded wait: with one batch's
 flag withheld by the host the wait gives up, the error bit is set, every
-other row is still right and the launch ends."""
+other row is still right and the launch ends. Ring mode (group rows through
+a ring of batches that the forwarders free): the scale-up rows byte for byte,
+at several ring sizes, with a withheld flag, and at full size."""
 import numpy as np
 import pytest
 import torch
@@ -207,4 +209,81 @@ def test_fused_full_hier8x8():
     assert ep.ep_check_errors(ws) == 0
     O, Hd = expected(w, inp, 7)
     np.testing.assert_array_equal(host(gb)[:GR], Hd["group_buf"])
+    np.testing.assert_array_equal(host(pb)[:N], Hd["peer_buf"])
+
+
+def run_ring(w, inp, tile, ring, epoch=9, fp8=False, withhold=None, timeout_us=0, calls=1):
+    """Fused call(s) in ring mode; group_buf holds only the ring."""
+    print(f"fused ring: T={w.T} H={w.H} K={w.K} E={w.E} R={w.R} G={w.G} tile={tile} ring={ring} "
+          f"fp8={fp8} withhold={withhold}", flush=True)
+    shape, L, ws, tk, _, pb, GR, N = setup(w, inp, fp8)
+    stride = pb.shape[1]
+    ring_rows = ring * tile * min(w.K, w.G)
+    gb = torch.full((ring_rows, stride), 0xA5, dtype=torch.uint8, device="cuda")
+    for _ in range(calls):
+        pb.fill_(0xA5)
+        ep.ep_hierarchical_dispatch_fused(shape, L, tk, epoch, gb, ring_rows, pb, N, ws, tile=tile, ring=ring,
+                                          withhold=withhold, timeout_us=timeout_us)
+        torch.cuda.synchronize()
+    return ws, pb, N
+
+
+@pytest.mark.parametrize("T,H,K,E,R,G,tile,ring,fp8", [
+    (1000, 512, 6, 64, 16, 4, 2, 65, False),      # smallest ring: 500 batches through 65
+    (1000, 512, 6, 64, 16, 4, 2, 100, False),
+    (1000, 512, 6, 64, 16, 4, 4, 300, False),     # ring longer than the batch count
+    (777, 1024, 8, 128, 32, 8, 16, 70, True),     # FP8 + scales
+    (129, 1032, 12, 48, 16, 4, 1, 65, False),     # K > G: min(K, G) rows per token
+    (200, 256, 64, 1024, 256, 256, 1, 65, False),  # 64 groups per token at most
+    (40, 16384, 8, 64, 16, 4, 1, 65, False),      # records of several 32-block pieces
+])
+def test_fused_ring_shapes(T, H, K, E, R, G, tile, ring, fp8):
+    w = synth.Workload("fz_ring", T, H, E, R, G, K, "uniform")
+    inp = synth.make_inputs(w, seed=T + ring, with_fp8=fp8)
+    ws, pb, N = run_ring(w, inp, tile, ring, fp8=fp8)
+    assert ep.ep_check_errors(ws) == 0
+    _, Hd = expected(w, inp, 9, fp8)
+    np.testing.assert_array_equal(host(pb)[:N], Hd["peer_buf"])
+
+
+def test_fused_ring_skipped_lanes_and_repeats():
+    """-1 and repeated experts, and two calls on one workspace with the same
+    epoch (the freed words of the first call are cleared for the second)."""
+    w = synth.Workload("fz_ring_rand", 600, 256, 20, 10, 5, 5, "uniform")
+    inp = synth.make_inputs(w, seed=3)
+    inp["topk_idx"] = np.random.default_rng(6).integers(-1, w.E, size=(w.T, w.K)).astype(np.int64)
+    ws, pb, N = run_ring(w, inp, 1, 80, calls=2)
+    assert ep.ep_check_errors(ws) == 0
+    _, Hd = expected(w, inp, 9)
+    np.testing.assert_array_equal(host(pb)[:N], Hd["peer_buf"])
+
+
+@pytest.mark.parametrize("held", [5, 150])
+def test_fused_ring_withheld_flag(held):
+    """One batch's flag withheld in ring mode (in the ring's first pass, and
+    in its third): its forwarder gives up and still frees the batch's ring
+    rows; the producer that reuses them and every later wait of that slot
+    have longer limits, so only the withheld batch is lost: every other
+    scale-up row is the oracle's."""
+    w = synth.Workload("fz_ring_hold", 1000, 512, 64, 16, 4, 6, "uniform")
+    inp = synth.make_inputs(w, seed=18)
+    tile = 2
+    ws, pb, N = run_ring(w, inp, tile, 70, withhold=held, timeout_us=2000)
+    assert ep.ep_check_errors(ws) == ep.EP_DEVERR_TIMEOUT
+    O, Hd = expected(w, inp, 9)
+    sl = O["slot"][held * tile:(held + 1) * tile]
+    held_rows = np.unique(sl[sl >= 0])
+    keep = np.setdiff1d(np.arange(N), held_rows)
+    got = host(pb)[:N]
+    np.testing.assert_array_equal(got[keep], Hd["peer_buf"][keep])
+    assert (got[held_rows] == 0xA5).all()
+
+
+@pytest.mark.parametrize("ring", [128, 512])
+def test_fused_ring_full_hier8x8(ring):
+    w = synth.workload("hier8x8")
+    inp = synth.make_inputs(w)
+    ws, pb, N = run_ring(w, inp, 2, ring)
+    assert ep.ep_check_errors(ws) == 0
+    _, Hd = expected(w, inp, 9)
     np.testing.assert_array_equal(host(pb)[:N], Hd["peer_buf"])
