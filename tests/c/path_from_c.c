@@ -408,6 +408,21 @@ int main(void) {
             ok &= same("fused group rows", g_gbuf, o_gbuf2, (size_t)GR * stride);
             ok &= same("fused peer rows", g_pbuf, o_pbuf2, (size_t)N2 * stride);
             ok &= fb == 0 && f_err == 0;
+            /* ring mode: one-token batches, group rows through a ring of 65 batches */
+            f_err = 0;
+            oracle_hier_dispatch(T, H, K, E, R, G2, ids, w, x, NULL, NULL, p_slot, p_go, EPOCH + 2, o_gbuf2, GR,
+                                 o_pbuf2, N2, 3, &f_err);
+            HIP_OK(hipMemset(d2_pbuf, 0, (size_t)N2 * stride));
+            memset(&fo, 0, sizeof fo);
+            fo.tile_tokens = 1;
+            fo.ring_batches = 65;
+            EP_OK_(ep_hierarchical_dispatch_fused(&s2, &L2, &tk, EPOCH + 2, d2_gbuf, GR, d2_pbuf, N2, &fo, ws2,
+                                                  ws2_bytes, st));
+            fb = 99;
+            EP_OK_(ep_check_errors(ws2, st, &fb));
+            HIP_OK(hipMemcpy(g_pbuf, d2_pbuf, (size_t)N2 * stride, hipMemcpyDeviceToHost));
+            ok &= same("fused peer rows, ring of 65 batches", g_pbuf, o_pbuf2, (size_t)N2 * stride);
+            ok &= fb == 0 && f_err == 0;
         }
         if (bits2 != p_err) {
             printf("FAIL two-level error bits %u != %u\n", bits2, p_err);

@@ -299,18 +299,20 @@ def test_graph_cycle_full_size_against_oracle(name, fp8):
                                               D["recv_scales"].view(np.uint32))
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_graph_cycle_full_size_hier8x8_against_oracle(fused):
+@pytest.mark.parametrize("fused,ring", [pytest.param(False, 0, id="False"), pytest.param(True, 0, id="True"),
+                                        pytest.param(True, 1024, id="ring1024")])
+def test_graph_cycle_full_size_hier8x8_against_oracle(fused, ring):
     """hier8x8 at full size as the benchmark times it: the steps of two input
-    batches (layout, two-level dispatch (two launches, or the fused one),
+    batches (layout, two-level dispatch (two launches, or the fused one, or
+    the fused one with its group rows through a ring of 1,024 batches),
     combine on the chunked scale-up rows) in one graph, replayed twice, and
-    the last replay's group rows, scale-up rows and combine outputs compared
-    with the CPU oracle."""
+    the last replay's group rows (not in ring mode), scale-up rows and
+    combine outputs compared with the CPU oracle."""
     import oracle
 
     oracle.build(force=False)
     w = synth.workload("hier8x8")
-    print(f"graph cycle: hier8x8 fused={fused}", flush=True)
+    print(f"graph cycle: hier8x8 fused={fused} ring={ring}", flush=True)
     shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, w.G)
     ws = ep.alloc_workspace(shape)
     inps = [synth.make_inputs(w, seed=synth.seed_of(w) + 1000 * i) for i in range(2)]
@@ -320,6 +322,9 @@ def test_graph_cycle_full_size_hier8x8_against_oracle(fused):
     Ns = [int(O["rank_offsets"][-1]) for O in Os]
     Gs = [int(O["group_offsets"][-1]) for O in Os]
     stride = ep.ep_chunked_record_bytes(shape, ep.EP_SEG_BF16)
+    ring_rows = ring * 2 * min(w.K, w.G)  # the default batch is 2 tokens
+    if ring:
+        Gs = [ring_rows] * len(Gs)
     gbuf = torch.zeros((max(Gs), stride), dtype=torch.uint8, device="cuda")
     pbuf = torch.zeros((max(Ns), stride), dtype=torch.uint8, device="cuda")
     outs = [torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda") for _ in batches]
@@ -329,7 +334,7 @@ def test_graph_cycle_full_size_hier8x8_against_oracle(fused):
             e = 40 + i
             ep.ep_get_layout(shape, tk["topk_idx"], Ls[i], ws)
             if fused:
-                ep.ep_hierarchical_dispatch_fused(shape, Ls[i], tk, e, gbuf, Gs[i], pbuf, Ns[i], ws)
+                ep.ep_hierarchical_dispatch_fused(shape, Ls[i], tk, e, gbuf, Gs[i], pbuf, Ns[i], ws, ring=ring)
             else:
                 ep.ep_hierarchical_dispatch(shape, Ls[i], tk, e, 3, gbuf, Gs[i], pbuf, Ns[i], ws)
             ep.ep_combine(shape, Ls[i], pbuf, Ns[i], stride, ep.EP_FMT_CHUNKED, e, tk["topk_weights"], outs[i], ws)
@@ -356,7 +361,8 @@ def test_graph_cycle_full_size_hier8x8_against_oracle(fused):
         got = outs[i].view(torch.int16).cpu().numpy().view(np.uint16)
         np.testing.assert_array_equal(got, C["out"], err_msg=f"batch {i}")
         if i == len(inps) - 1:  # the buffers hold the last batch's dispatch
-            np.testing.assert_array_equal(gbuf.cpu().numpy()[:Gs[i]], Hd["group_buf"])
+            if not ring:
+                np.testing.assert_array_equal(gbuf.cpu().numpy()[:Gs[i]], Hd["group_buf"])
             np.testing.assert_array_equal(pbuf.cpu().numpy()[:Ns[i]], Hd["peer_buf"])
 
 
