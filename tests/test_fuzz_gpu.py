@@ -2,7 +2,8 @@
 oracle: layout (all outputs, groups and expand rows; also through the
 allocation-free entry point), dispatch with a random subset of payload
 pieces, combine, the two-level chunked dispatch (two launches, and the fused
-one-launch form with a random batch size) with the flat and the two-level
+one-launch form with a random batch size, also with its group rows through a
+ring of a random number of batches) with the flat and the two-level
 combine, expand-mode dispatch and combine, and the several-source send and
 copy epilogue in one launch with a random source count.
 
@@ -173,6 +174,17 @@ def test_fuzz_all_entry_points(seed):
     np.testing.assert_array_equal(host(gbf)[:G_rows], Hf["group_buf"], err_msg=f"fused tile {tile}")
     np.testing.assert_array_equal(host(pbf)[:N], Hf["peer_buf"], err_msg=f"fused tile {tile}")
     assert ep.ep_check_errors(ws) == 0
+    # ring mode (its own generator, so the draws above and below stay those of the seed)
+    rr = np.random.default_rng(20_000 + seed)
+    rtile, ring = int(rr.choice([1, 2, 3])), int(rr.choice([65, 80, 129]))
+    ring_rows = ring * rtile * min(K, G)
+    gbr = torch.empty((ring_rows, stride), dtype=torch.uint8, device="cuda")
+    pbr = poison(torch.empty_like(pb))
+    ep.ep_hierarchical_dispatch_fused(shape, L, htok, epoch + 1000, gbr, ring_rows, pbr, N, ws, tile=rtile,
+                                      ring=ring)
+    np.testing.assert_array_equal(host(pbr)[:N], Hf["peer_buf"], err_msg=f"ring {ring} tile {rtile}")
+    assert ep.ep_check_errors(ws) == 0
+    del gbr, pbr
     ep.ep_combine(shape, L, pb, N, stride, ep.EP_FMT_CHUNKED, epoch, wd, out, ws)
     C = oracle.combine(O["slot"], w, Hd["peer_buf"], H, chunked=True, epoch=epoch)
     np.testing.assert_array_equal(host(out), C["out"])
