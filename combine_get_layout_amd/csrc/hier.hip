@@ -247,10 +247,18 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g,
     const int64_t off_idx = (int64_t)a.geom.q_idx * 16;
     const int64_t off_src = (int64_t)a.geom.q_src * 16;
     const int c_half = lane >> 5, wv = lane & 31;
-    const bool one_piece = iters <= kPieceIters;
     const uint8_t* src_row = a.group_buf + n * stride;
+    // The first piece (the whole record when it fits) is requested at once,
+    // together with the metadata. In the fused launch (device-scope loads)
+    // also for longer records, with the flags of the later pieces: one round
+    // trip before the flag check instead of two (the fused launch at H = 8,192
+    // 1,094 -> 976 us, at 16,384 1,929 -> 1,829 us). The forward launch keeps
+    // a flag pre-pass for those: there the change took its registers from 193
+    // to 166, and the forward of one-piece records (hier8x8) got 34 us slower.
+    const bool one_piece = iters <= kPieceIters;
+    const bool hold_first = DEVICE_LOADS || one_piece;
     u32x4 v[kPieceIters];
-    if (one_piece) {
+    if (hold_first) {
 #pragma unroll
         for (int j = 0; j < kPieceIters; ++j) {
             const int c = min(2 * j + c_half, nchunks - 1);
@@ -269,7 +277,15 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g,
         id = *reinterpret_cast<const int32_t*>(record_byte(src_row, off_idx + 4 * min(lane, a.K - 1)));
     }
     bool ok = true;
-    if (one_piece) {
+    if (hold_first) {
+        if constexpr (DEVICE_LOADS) {
+            // Flags of the blocks past the first piece (flag vector i: block i / 2).
+            for (int i = 4 * kPieceIters + lane; i < 2 * nchunks; i += kWave) {
+                const int64_t off = (int64_t)(i >> 1) * kChunkBytes + kChunkPayload + (i & 1) * 16;
+                const u32x4 f = ld16_device(src_row, stride, off);
+                ok &= f[0] == a.epoch && f[1] == a.epoch && f[2] == a.epoch && f[3] == a.epoch;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < kPieceIters; ++j) {
             const bool is_flag = wv >= kChunkPayloadVecs && j < iters && 2 * j + c_half < nchunks;
@@ -303,7 +319,7 @@ __device__ __forceinline__ void forward_row(const HierArgs& a, int64_t n, int g,
     if (!dest) return;
 
     for (int it0 = 0; it0 < iters; it0 += kPieceIters) {
-        if (!one_piece) {
+        if (DEVICE_LOADS ? it0 > 0 : !one_piece) {  // else this piece is already held
 #pragma unroll
             for (int j = 0; j < kPieceIters; ++j) {
                 const int c = 2 * (it0 + j) + c_half;
