@@ -907,7 +907,11 @@ hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tok
                             ((int64_t)waves_per_wg * std::max(1, d.cus) * std::max<int64_t>(1, f.h.geom.stride));
         per_cu = (int)std::min<int64_t>(per_cu, std::max<int64_t>(2, fit));
     }
-    const int resident = std::max(1, d.cus * std::max(1, per_cu));
+    int resident = std::max(1, d.cus * std::max(1, per_cu));
+    // Ring mode: a workgroup holds one job at a time, so about `blocks` jobs
+    // are in flight; the producer of batch b waits for job b - ring + lag,
+    // which is then done only if ring - lag >= blocks.
+    if (ring > 0) resident = std::min(resident, std::max(1, ring - f.lag));
     const int jobs_per_block = EP_FUSED_WAVE ? kWavesPerBlock : 1;
     const int blocks = std::min(resident, std::max(1, (2 * f.nbatch + jobs_per_block - 1) / jobs_per_block));
     launch_zero_words(f.ctr, kFusedCounters + 2 * f.nbatch, st);  // then f.flags, then f.freed
