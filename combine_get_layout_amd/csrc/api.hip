@@ -273,9 +273,9 @@ int ep_hierarchical_dispatch_fused(const ep_shape* shape, const ep_layout* layou
     // Ring mode: more batches than the fixed lag (the producer of batch b
     // waits for the forwarding of batch b - ring), and room for all of them.
     if (o.ring_batches < 0 || (o.ring_batches > 0 && o.ring_batches <= kFusedLag)) return EP_ERR_ARG;
-    if (o.ring_batches > 0 &&
-        group_cap < (int64_t)o.ring_batches * tile * std::min(shape->K, shape->G))
-        return EP_ERR_ARG;
+    // Ring rows are 32-bit indices on the device.
+    const int64_t ring_rows = (int64_t)o.ring_batches * tile * std::min(shape->K, shape->G);
+    if (o.ring_batches > 0 && (group_cap < ring_rows || ring_rows > INT32_MAX)) return EP_ERR_ARG;
     const uint32_t timeout = o.timeout_us ? o.timeout_us : 100000u;
     const int withhold = (o.test_flags & EP_FUSED_WITHHOLD) ? o.withhold_batch : -1;
     return hip_status(launch_hier_fused(*shape, *layout, *tokens, epoch, group_buf, group_cap, peer_buf,

@@ -273,7 +273,7 @@ typedef struct ep_fused_opts {
                                EP_DEVERR_TIMEOUT) and the forwarder (n + 1) * timeout_us,
                                so a lost flag stops only its own batch, and a broken run
                                lasts at most about (nbatch / ring + 1) * timeout_us.
-                               Needs group_cap >= ring * tile * min(K, G); the
+                               Needs group_cap >= ring * tile * min(K, G) (< 2^31); the
                                peer rows are those of ring 0, byte for byte; group_buf's
                                contents afterwards are unspecified (the last pass over the
                                ring), and group_slot's capacity check does not apply.

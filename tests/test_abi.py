@@ -116,6 +116,10 @@ def test_fused_options_checked_before_launch(lib):
     assert call(ctypes.byref(ep.ep_fused_opts(1, 0, 0, 0, 64))) == ep.EP_ERR_ARG  # ring not above the lag
     assert call(ctypes.byref(ep.ep_fused_opts(1, 0, 0, 0, -1))) == ep.EP_ERR_ARG
     assert call(ctypes.byref(ep.ep_fused_opts(1, 0, 0, 0, 65))) == ep.EP_ERR_ARG  # 260 ring rows > group_cap 10
+    big = lib.ep_hierarchical_dispatch_fused(ctypes.byref(s), ctypes.byref(L), ctypes.byref(tk), 3, 0x10000,
+                                             1 << 40, 0x20000, 10, ctypes.byref(ep.ep_fused_opts(64, 0, 0, 0, 1 << 24)),
+                                             ws, n, None)
+    assert big == ep.EP_ERR_ARG  # 2^24 * 64 * 4 ring rows: past 32-bit row indices
     assert call(None, epoch=0) == ep.EP_ERR_ARG
     z = ep.make_shape(0, 256, 4, 32, 8, 4)
     assert lib.ep_hierarchical_dispatch_fused(ctypes.byref(z), ctypes.byref(L), ctypes.byref(tk), 3, None, 0,
