@@ -5,7 +5,8 @@ produce, so they need no co-residency: with a memory-bound kernel of another
 stream holding the CUs, their workgroups start a few at a time, and every
 call must still end with the oracle's rows and no error bit (a wait that
 gave up would set EP_DEVERR_TIMEOUT). Covered: the fused two-level dispatch,
-also in ring mode, and the several-source send with its copy epilogue.
+also in ring mode, the several-source send with its copy epilogue, and the
+one-launch two-level combine.
 """
 import numpy as np
 import pytest
@@ -132,3 +133,43 @@ def test_source_fused_beside_a_busy_stream():
     D = oracle.dispatch(inp["topk_idx"], w.E, w.R, O["rank_offsets"], x=inp["x"], topk_w=inp["topk_w"])
     np.testing.assert_array_equal(host(recv["x"])[:N], D["recv_x"][:N])
     np.testing.assert_array_equal(host(recv["src_idx"])[:N], D["recv_src"][:N])
+
+
+def test_two_level_combine_one_launch_beside_a_busy_stream():
+    """The one-launch two-level combine (a partial-row capacity of 512 MB
+    selects it) while the side stream holds the CUs: partial rows and outputs
+    against the oracle."""
+    w = synth.Workload("busy_c2", 3000, 2048, 128, 32, 8, 8, "uniform")
+    inp = synth.make_inputs(w, seed=33)
+    print("two-level combine beside a busy stream", flush=True)
+    shape = ep.make_shape(w.T, w.H, w.K, w.E, w.R, w.G)
+    L = ep.alloc_layout(shape, masks=False, groups=True)
+    ws = ep.alloc_workspace(shape)
+    tk = dev(inp["topk_idx"])
+    wd = dev(inp["topk_w"])
+    ep.ep_get_layout(shape, tk, L, ws)
+    torch.cuda.synchronize()
+    N = int(L["rank_offsets"][-1].item())
+    GR = int(L["group_offsets"][-1].item())
+    y = synth.random_bf16_rows(N, w.H, seed=34)
+    pstride = ep.ep_partial_row_bytes(shape)
+    gcap = max(GR, -(-(512 << 20) // pstride))
+    part = torch.empty((gcap, pstride), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.T, w.H), dtype=torch.uint16, device="cuda")
+    busy = torch.ones(BUSY_ELEMS, dtype=torch.float32, device="cuda")
+    yd = dev(y)
+    torch.cuda.synchronize()
+    side, side_end = keep_busy(busy)
+    start, done = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    ep.ep_combine_two_level(shape, L, tk, yd, N, 2 * w.H, ep.EP_FMT_PLAIN, 9, wd, part, gcap, 3, out, ws)
+    done.record()
+    torch.cuda.synchronize()
+    side.synchronize()
+    report_overlap(start, done, side_end)
+    assert ep.ep_check_errors(ws) == 0
+    O = oracle.layout(inp["topk_idx"], w.E, w.R, w.G)
+    C = oracle.combine_two_level(inp["topk_idx"], w.E, w.R, w.G, O["slot"], O["group_slot"], inp["topk_w"], y,
+                                 w.H, gcap, 9)
+    np.testing.assert_array_equal(host(part)[:GR], C["group_buf"][:GR])
+    np.testing.assert_array_equal(host(out), C["out"])
