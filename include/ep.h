@@ -249,7 +249,8 @@ int ep_hierarchical_dispatch(const ep_shape *shape, const ep_layout *layout,
  * written. The results are those of ep_hierarchical_dispatch with both
  * steps, byte for byte. Same arguments and requirements as
  * ep_hierarchical_dispatch with steps = 3; the workspace (ep_workspace_bytes)
- * also holds the batch flags and work counters, which the call zeroes first
+ * also holds the batch flags, the ring's batch-freed words and the work
+ * counters, which the call zeroes first
  * with a small kernel (no memset), so calls on one workspace must not
  * overlap. opts may be NULL (defaults); all-zero fields mean the defaults. */
 typedef struct ep_fused_opts {
