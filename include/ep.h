@@ -250,9 +250,9 @@ int ep_hierarchical_dispatch(const ep_shape *shape, const ep_layout *layout,
  * steps, byte for byte. Same arguments and requirements as
  * ep_hierarchical_dispatch with steps = 3; the workspace (ep_workspace_bytes)
  * also holds the batch flags, the ring's batch-freed words and the work
- * counters, which the call zeroes first
- * with a small kernel (no memset), so calls on one workspace must not
- * overlap. opts may be NULL (defaults); all-zero fields mean the defaults. */
+ * counters, which the call zeroes first with a small kernel (no memset), so
+ * calls on one workspace must not overlap. opts may be NULL (defaults);
+ * all-zero fields mean the defaults. */
 typedef struct ep_fused_opts {
     int32_t tile_tokens;    /* tokens per batch, 1..64 (0: 2) */
     uint32_t timeout_us;    /* longest wait for one batch flag (0: 100000 us; in ring
