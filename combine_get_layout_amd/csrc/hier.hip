@@ -411,6 +411,7 @@ __global__ __launch_bounds__(kBlockThreads) void forward_kernel(HierArgs a) {
 #ifndef EP_FUSED_LAG
 #define EP_FUSED_LAG 64  // > 0: job i produces batch i, then forwards batch i - EP_FUSED_LAG
 #endif
+constexpr int kRingMinLag = 16;  // shortest lag the ring mode takes (batches)
 // The host accepts ring sizes above kFusedLag; the ring's waits point at
 // earlier jobs only while the ring is longer than the lag.
 static_assert(EP_FUSED_LAG <= kFusedLag, "ring sizes are checked against kFusedLag");
@@ -910,8 +911,17 @@ hipError_t launch_hier_fused(const ep_shape& s, const ep_layout& L, const ep_tok
     int resident = std::max(1, d.cus * std::max(1, per_cu));
     // Ring mode: a workgroup holds one job at a time, so about `blocks` jobs
     // are in flight; the producer of batch b waits for job b - ring + lag,
-    // which is then done only if ring - lag >= blocks.
-    if (ring > 0) resident = std::min(resident, std::max(1, ring - f.lag));
+    // which is then done only if ring - lag >= blocks. A ring with room for
+    // the whole grid keeps the lag of 64; a shorter one takes a lag down to
+    // 16, leaving more of the ring to jobs in flight, and caps the grid at
+    // ring - lag. At hier8x8 (512 workgroups) that gave 2,088 / 1,085 / 893 /
+    // 770 us for rings of 128 / 256 / 384 / 512 batches, against 3,555 /
+    // 1,281 / 937 / 783 us with the lag of 64; with 768 batches the lag of
+    // 64 is best (695 against 719 us with 16).
+    if (ring > 0) {
+        f.lag = std::min(EP_FUSED_LAG, std::max(kRingMinLag, ring - resident));
+        resident = std::min(resident, std::max(1, ring - f.lag));
+    }
     const int jobs_per_block = EP_FUSED_WAVE ? kWavesPerBlock : 1;
     const int blocks = std::min(resident, std::max(1, (2 * f.nbatch + jobs_per_block - 1) / jobs_per_block));
     launch_zero_words(f.ctr, kFusedCounters + 2 * f.nbatch, st);  // then f.flags, then f.freed

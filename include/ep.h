@@ -278,9 +278,10 @@ typedef struct ep_fused_opts {
                                peer rows are those of ring 0, byte for byte; group_buf's
                                contents afterwards are unspecified (the last pass over the
                                ring), and group_slot's capacity check does not apply.
-                               The launch keeps at most ring - 64 workgroups, so a short
-                               ring also bounds the work in flight (slower). Other
-                               values: EP_ERR_ARG. */
+                               A ring too short for the whole grid runs with a shorter
+                               lag (down to 16 batches) and at most ring - lag
+                               workgroups, so it also bounds the work in flight (slower).
+                               Other values: EP_ERR_ARG. */
 } ep_fused_opts;
 #define EP_FUSED_WITHHOLD 1u
 int ep_hierarchical_dispatch_fused(const ep_shape *shape, const ep_layout *layout,
